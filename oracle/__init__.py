@@ -1,0 +1,182 @@
+"""CPU oracle for the MoE expert-parallel dispatch layout, dispatch pack and combine.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The GPU library
+(``combine_ep_layout_02_amd``) never imports it and shares no code with it.
+
+The arithmetic lives in ``ep_oracle.c`` (plain single-threaded C, gcc -O2, no
+fast-math, no FP contraction).  This module only marshals numpy arrays into
+that library through ctypes.  Each function's docstring names the passage of
+the DeepEP pages it follows; the C source restates the definition.
+
+Pins (what ties the oracle to something other than itself) are in
+``tests/pins.py``; every function here is pinned, none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "ep_oracle.c")
+LIBRARY = os.path.join(_HERE, "libep_oracle.so")
+
+# gcc flags: IEEE binary32 arithmetic in source order, no fused contraction.
+CFLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+STATUS_OK = 0
+STATUS_BAD_EXPERT_ID = 1
+STATUS_BAD_SLOT = 2
+STATUS_BAD_ARGS = 4
+
+
+def build(source: str = SOURCE, output: str = LIBRARY) -> str:
+    """Compile the oracle with gcc into a shared library and return its path."""
+    subprocess.check_call(["gcc", *CFLAGS, "-o", output, source, "-lm"])
+    return output
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Oracle:
+    """ctypes handle on one build of ``ep_oracle.c`` (the default build, or a
+    planted-mistake variant built by the mutation tests)."""
+
+    def __init__(self, path: str = LIBRARY):
+        self.path = path
+        lib = ctypes.CDLL(path)
+        i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+        lib.oracle_layout.argtypes = [i32, i32, i32, i32] + [vp] * 7
+        lib.oracle_layout.restype = ctypes.c_int
+        lib.oracle_pack.argtypes = [i32] * 6 + [vp] * 6
+        lib.oracle_pack.restype = ctypes.c_int
+        lib.oracle_combine.argtypes = [i32] * 5 + [vp] * 5
+        lib.oracle_combine.restype = ctypes.c_int
+        lib.oracle_e4m3fn_encode_array.argtypes = [i64, vp, vp]
+        lib.oracle_e4m3fn_decode_array.argtypes = [i64, vp, vp]
+        lib.oracle_bf16_rne_array.argtypes = [i64, vp, vp]
+        lib.oracle_quantize_rows.argtypes = [i32, i32, vp, vp, vp]
+        lib.oracle_dequant_rows.argtypes = [i32, i32, vp, vp, vp]
+        self.lib = lib
+
+    # ------------------------------------------------------------- layout
+    def layout(self, topk_idx: np.ndarray, num_experts: int, num_ranks: int) -> dict:
+        """Dispatch layout (DeepEP V1 Legacy guide §5.2(1); Ascend deep dive,
+        "Dispatch's Three Phases", phase 2).  ``topk_idx`` int64 [N, K] with -1
+        for masked entries.  Returns counts, mask, slots, offsets, status."""
+        idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
+        n, k = idx.shape
+        e, r = int(num_experts), int(num_ranks)
+        out = {
+            "num_tokens_per_rank": np.empty(r, np.int32),
+            "num_tokens_per_expert": np.empty(e, np.int32),
+            "is_token_in_rank": np.empty((n, r), np.uint8),
+            "expert_slot": np.empty((n, k), np.int32),
+            "rank_slot": np.empty((n, r), np.int32),
+            "expert_offset": np.empty(e + 1, np.int32),
+        }
+        st = self.lib.oracle_layout(
+            n, k, e, r, _ptr(idx), _ptr(out["num_tokens_per_rank"]),
+            _ptr(out["num_tokens_per_expert"]), _ptr(out["is_token_in_rank"]),
+            _ptr(out["expert_slot"]), _ptr(out["rank_slot"]), _ptr(out["expert_offset"]))
+        out["status"] = int(st)
+        return out
+
+    # --------------------------------------------------------------- pack
+    def pack(self, x_bits: np.ndarray, topk_idx: np.ndarray, expert_slot: np.ndarray,
+             num_experts: int, capacity: int, use_fp8: bool, fill: int = 0):
+        """Dispatch pack (Lesson 14 §3 receive shape; DeepEP V1 Legacy guide
+        §5.2(6) and §6.3 FP8 with one scale per 128 channels).  ``x_bits`` is
+        the bf16 bit pattern, uint16 [N, H].  Returns (recv_x, recv_scales,
+        recv_src_idx, status) with recv_x uint8 [E, S, H] (FP8) or uint16
+        [E, S, H] (BF16); rows never written keep ``fill``."""
+        x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
+        slot = np.ascontiguousarray(expert_slot, dtype=np.int32)
+        n, h = x.shape
+        k = idx.shape[1]
+        e, s = int(num_experts), int(capacity)
+        if use_fp8:
+            recv_x = np.full((e, s, h), fill & 0xFF, np.uint8)
+            recv_scales = np.full((e, s, h // 128), np.nan, np.float32)
+        else:
+            recv_x = np.full((e, s, h), fill & 0xFFFF, np.uint16)
+            recv_scales = None
+        recv_src = np.full((e, s), -2, np.int32)
+        st = self.lib.oracle_pack(n, h, k, e, s, int(bool(use_fp8)), _ptr(x), _ptr(idx),
+                                  _ptr(slot), _ptr(recv_x), _ptr(recv_scales), _ptr(recv_src))
+        return recv_x, recv_scales, recv_src, int(st)
+
+    # ------------------------------------------------------------ combine
+    def combine(self, y_bits: np.ndarray, topk_idx: np.ndarray, topk_weights: np.ndarray,
+                expert_slot: np.ndarray, num_experts: int, capacity: int):
+        """Combine (Ascend deep dive, "Two Transfers" and "Combine: More
+        Output, Same Cost"; Lesson 14 exercise; DeepEP V1 Legacy guide
+        §5.2(6)).  ``y_bits`` uint16 [E, S, H] bf16 expert outputs.  Returns
+        (combined bf16 bits uint16 [N, H], status)."""
+        y = np.ascontiguousarray(y_bits, dtype=np.uint16)
+        idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
+        w = np.ascontiguousarray(topk_weights, dtype=np.float32)
+        slot = np.ascontiguousarray(expert_slot, dtype=np.int32)
+        n, k = idx.shape
+        h = y.shape[-1]
+        out = np.empty((n, h), np.uint16)
+        st = self.lib.oracle_combine(n, h, k, int(num_experts), int(capacity), _ptr(y),
+                                     _ptr(idx), _ptr(w), _ptr(slot), _ptr(out))
+        return out, int(st)
+
+    # ------------------------------------------------------------ formats
+    def e4m3fn_encode(self, v: np.ndarray) -> np.ndarray:
+        a = np.ascontiguousarray(v, dtype=np.float32).ravel()
+        out = np.empty(a.size, np.uint8)
+        self.lib.oracle_e4m3fn_encode_array(a.size, _ptr(a), _ptr(out))
+        return out.reshape(np.shape(v))
+
+    def e4m3fn_decode(self, c: np.ndarray) -> np.ndarray:
+        a = np.ascontiguousarray(c, dtype=np.uint8).ravel()
+        out = np.empty(a.size, np.float64)
+        self.lib.oracle_e4m3fn_decode_array(a.size, _ptr(a), _ptr(out))
+        return out.reshape(np.shape(c))
+
+    def bf16_rne(self, v: np.ndarray) -> np.ndarray:
+        a = np.ascontiguousarray(v, dtype=np.float32).ravel()
+        out = np.empty(a.size, np.uint16)
+        self.lib.oracle_bf16_rne_array(a.size, _ptr(a), _ptr(out))
+        return out.reshape(np.shape(v))
+
+    def quantize_rows(self, x_bits: np.ndarray):
+        """FP8 payload of each row: (q uint8 [N, H], scales float32 [N, H/128])."""
+        x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        n, h = x.shape
+        q = np.empty((n, h), np.uint8)
+        sc = np.empty((n, h // 128), np.float32)
+        self.lib.oracle_quantize_rows(n, h, _ptr(x), _ptr(q), _ptr(sc))
+        return q, sc
+
+    def dequant_rows(self, q: np.ndarray, scales: np.ndarray) -> np.ndarray:
+        """Identity-expert output of FP8 rows: bf16 bits uint16 [N, H]."""
+        qq = np.ascontiguousarray(q, dtype=np.uint8)
+        sc = np.ascontiguousarray(scales, dtype=np.float32)
+        n, h = qq.shape
+        y = np.empty((n, h), np.uint16)
+        self.lib.oracle_dequant_rows(n, h, _ptr(qq), _ptr(sc), _ptr(y))
+        return y
+
+
+_DEFAULT: Oracle | None = None
+
+
+def get() -> Oracle:
+    """The oracle built from ``ep_oracle.c`` (built with gcc on first use if
+    no library is present)."""
+    global _DEFAULT
+    if _DEFAULT is None:
+        if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
+            build()
+        _DEFAULT = Oracle(LIBRARY)
+    return _DEFAULT

@@ -1,0 +1,388 @@
+/*
+ * ep_oracle.c -- plain, slow, single-threaded CPU oracle for the MoE
+ * expert-parallel dispatch layout, dispatch pack and combine.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the package smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU library never
+ * calls it, and the two share no source, header, table or helper.
+ *
+ * Every function is written for a reader to check by eye against the pages it
+ * follows (web pages on DeepSeek's DeepEP):
+ *   [V1]  "DeepEP V1 Legacy guide" (zskr.cn): §5.1 (normal-mode example:
+ *         get_dispatch_layout, dispatch, combine), §5.2(1) (the four layout
+ *         outputs), §5.2(6) (FP8 input with one float scale per 128 channels,
+ *         BF16 weighted reduction in combine), §6.1 (experts split evenly over
+ *         ranks), §6.3 (use_fp8 receive shape; -1 in topk_idx is legal).
+ *   [ASC] "DeepEP Ascend Deep Dive" (kongchang.com): "Two Transfers: Dispatch
+ *         and Combine" (one copy per destination card; weighted sum at the
+ *         origin), "Dispatch's Three Phases and FP8 Compression" (count per
+ *         expert and per card; receive-source map; amax -> ratio -> multiply
+ *         -> convert).
+ *   [L14] "Lesson 14: DeepSeek DeepEP" (hpc.payai.win): §3 (low-latency call
+ *         sketch: fixed-shape receive buffer [local experts, M * ranks,
+ *         hidden] and a per-expert count), and the dispatch/combine simulator
+ *         exercise (append per (token, k); weighted sum per token).
+ *
+ * Conventions the pages leave open are fixed here: receive slots follow
+ * (token, k) order, so exactly one slot assignment is correct; experts sit on
+ * ranks in contiguous blocks (the only placement the pages show); FP8 is
+ * E4M3FN rounded to nearest-even after clamping to +-448; the block amax has a
+ * 1e-4 floor so an all-zero block never divides by zero; the combine adds in
+ * ascending k with fp32 fused multiply-add and rounds to bf16 once.
+ *
+ * Build: gcc -O2 -std=c99 -ffp-contract=off -fPIC -shared (no fast-math), so
+ * every float operation below is one IEEE binary32 operation in the order
+ * written.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_EXPERT_ID 1 /* an id >= E or < -1 was seen (treated as -1) */
+#define ORACLE_BAD_SLOT 2      /* an expert_slot outside [0, S) was seen      */
+#define ORACLE_BAD_ARGS 4      /* shapes that make no sense                   */
+
+/* ---------------------------------------------------------------- formats */
+
+/* bf16 is the upper half of a binary32; widening is exact. */
+float oracle_bf16_to_f32(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Round a binary32 to bf16, to nearest, ties to even: keep the upper 16 bits
+ * and add one unit in their last place when the dropped 16 bits are above
+ * half, or exactly half with an odd kept part.  NaN stays a (quiet) NaN. */
+uint16_t oracle_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if (isnan(f))
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t kept = u >> 16;
+    uint32_t dropped = u & 0xFFFFu;
+    if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u)))
+        kept += 1u;
+    return (uint16_t)kept;
+}
+
+/* OCP FP8 E4M3FN ([V1] §5.2(6) names torch's float8_e4m3fn): 1 sign bit,
+ * 4 exponent bits with bias 7, 3 mantissa bits; no infinity; S.1111.111 is
+ * NaN; largest finite magnitude 448 (code 0x7E).  Normal codes hold
+ * (1 + m/8) * 2^(E-7) for E = 1..15, subnormal codes m * 2^-9. */
+double oracle_e4m3fn_decode(uint8_t c)
+{
+    int s = c >> 7;
+    int E = (c >> 3) & 15;
+    int m = c & 7;
+    if (E == 15 && m == 7)
+        return NAN;
+    double v = (E == 0) ? ldexp((double)m, -9) : ldexp((double)(8 + m), E - 10);
+    return s ? -v : v;
+}
+
+/* Encode a finite binary32 with |v| <= 448 to E4M3FN, rounding to nearest
+ * with ties to an even mantissa.  The sign is kept (so -tiny -> 0x80).
+ * All double arithmetic below is exact: v has 24 significant bits. */
+uint8_t oracle_e4m3fn_encode(float v)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (a < 0x1p-6) {
+        /* subnormal range: a = q * 2^-9 with q in [0, 8); q rounds to
+         * m in 0..8, and m = 8 is exactly code 0x08 = 2^-6. */
+        double m = nearbyint(a * 0x1p9);
+        return (uint8_t)(sign | (uint8_t)m);
+    }
+    int ex;
+    frexp(a, &ex);  /* a = f * 2^ex, f in [0.5, 1) */
+    int e = ex - 1; /* a in [2^e, 2^(e+1)), e in [-6, 8] */
+    double m = nearbyint((ldexp(a, -e) - 1.0) * 8.0);
+    if (m == 8.0) { /* mantissa rounded up into the next binade */
+        e += 1;
+        m = 0.0;
+    }
+    return (uint8_t)(sign | (uint8_t)(((e + 7) << 3) | (int)m));
+}
+
+/* ---------------------------------------------------------------- routing */
+
+/* [V1] §6.3: -1 means "no expert at this position" and is legal input.  Any
+ * other id outside [0, E) is treated the same way and reported. */
+static int32_t routed_expert(int64_t id, int32_t E, int *status)
+{
+    if (id == -1)
+        return -1;
+    if (id < 0 || id >= (int64_t)E) {
+        *status |= ORACLE_BAD_EXPERT_ID;
+        return -1;
+    }
+    return (int32_t)id;
+}
+
+/* [V1] §6.1 (E % R == 0, E / R local experts per rank) and [ASC] "Why MoE
+ * Needs a Dedicated Communication Library" (256 experts over 8 cards, 32
+ * each): expert e lives on rank e / L in a contiguous block, L = E / R. */
+static int32_t rank_of(int32_t e, int32_t E, int32_t R)
+{
+    return e / (E / R);
+}
+
+/* ----------------------------------------------------------------- layout */
+
+/* Dispatch layout ([V1] §5.2(1); [ASC] "Dispatch's Three Phases", phase 2:
+ * count per expert and per destination card; [ASC] "Two Transfers": a card
+ * receives one copy of a token however many of its experts live there).
+ *
+ * Walk the entries in (t, k) order:
+ *   valid entry, expert e:  expert_slot[t,k] = running count of e, then +1;
+ *                           mark rank(e) in the token's rank set;
+ *   masked entry:           expert_slot[t,k] = -1.
+ * Then for each rank r of the token's set (r ascending):
+ *   is_token_in_rank[t,r] = 1, rank_slot[t,r] = running count of r, then +1;
+ * and 0 / -1 for ranks outside the set.
+ * Outputs: num_tokens_per_expert (counts with multiplicity),
+ * num_tokens_per_rank (each token at most once per rank), expert_offset =
+ * exclusive prefix of num_tokens_per_expert with expert_offset[E] = number of
+ * valid entries (nullable). */
+int oracle_layout(int32_t N, int32_t K, int32_t E, int32_t R, const int64_t *topk_idx,
+                  int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+                  uint8_t *is_token_in_rank, int32_t *expert_slot, int32_t *rank_slot,
+                  int32_t *expert_offset)
+{
+    if (N < 0 || K < 1 || E < 1 || R < 1 || E % R != 0)
+        return ORACLE_BAD_ARGS;
+    int status = ORACLE_OK;
+    uint8_t *in_set = (uint8_t *)calloc((size_t)R, 1);
+    if (!in_set)
+        return ORACLE_BAD_ARGS;
+    for (int32_t e = 0; e < E; ++e)
+        num_tokens_per_expert[e] = 0;
+    for (int32_t r = 0; r < R; ++r)
+        num_tokens_per_rank[r] = 0;
+
+    for (int32_t t = 0; t < N; ++t) {
+        memset(in_set, 0, (size_t)R);
+        for (int32_t k = 0; k < K; ++k) {
+            size_t i = (size_t)t * K + k;
+            int32_t e = routed_expert(topk_idx[i], E, &status);
+            if (e < 0) {
+                expert_slot[i] = -1;
+                continue;
+            }
+            expert_slot[i] = num_tokens_per_expert[e];
+            num_tokens_per_expert[e] += 1;
+            in_set[rank_of(e, E, R)] = 1;
+        }
+        for (int32_t r = 0; r < R; ++r) {
+            size_t i = (size_t)t * R + r;
+            if (in_set[r]) {
+                is_token_in_rank[i] = 1;
+                rank_slot[i] = num_tokens_per_rank[r];
+                num_tokens_per_rank[r] += 1;
+            } else {
+                is_token_in_rank[i] = 0;
+                rank_slot[i] = -1;
+            }
+        }
+    }
+    if (expert_offset) {
+        int32_t run = 0;
+        for (int32_t e = 0; e < E; ++e) {
+            expert_offset[e] = run;
+            run += num_tokens_per_expert[e];
+        }
+        expert_offset[E] = run;
+    }
+    free(in_set);
+    return status;
+}
+
+/* ------------------------------------------------------------ FP8 payload */
+
+/* One token row to FP8 with one fp32 scale per 128 channels ([V1] §5.2(6):
+ * scales of shape [tokens, hidden / 128]; [ASC] "Dispatch's Three Phases and
+ * FP8 Compression": find the max magnitude, form the ratio, multiply, convert,
+ * and ship the scale so the receiver can undo it).  For block b:
+ *   a     = max |x|           over the 128 channels (exact)
+ *   a'    = max(a, 1e-4)      floor so an all-zero block divides safely
+ *   inv   = 448 / a'          (one rounded fp32 division)
+ *   scale = a' / 448          (one rounded fp32 division; what ships)
+ *   q     = E4M3FN_RNE(clamp(x * inv, -448, 448))
+ * The receiver reconstructs x ~ q * scale. */
+void oracle_quantize_row(int32_t H, const uint16_t *x_row, uint8_t *q_row, float *scales)
+{
+    for (int32_t b = 0; b < H / 128; ++b) {
+        const uint16_t *xb = x_row + (size_t)b * 128;
+        float a = 0.0f;
+        for (int c = 0; c < 128; ++c) {
+            float m = fabsf(oracle_bf16_to_f32(xb[c]));
+            if (m > a)
+                a = m;
+        }
+        float ap = (a > 1e-4f) ? a : 1e-4f;
+        float inv = 448.0f / ap;
+        float scale = ap / 448.0f;
+        scales[b] = scale;
+        for (int c = 0; c < 128; ++c) {
+            float v = oracle_bf16_to_f32(xb[c]) * inv;
+            if (v > 448.0f)
+                v = 448.0f;
+            if (v < -448.0f)
+                v = -448.0f;
+            q_row[(size_t)b * 128 + c] = oracle_e4m3fn_encode(v);
+        }
+    }
+}
+
+/* What an identity expert returns for an FP8 row: bf16_RNE(float(q) * scale),
+ * one rounded fp32 product per channel (float(q) is exact). */
+void oracle_dequant_row(int32_t H, const uint8_t *q_row, const float *scales, uint16_t *y_row)
+{
+    for (int32_t c = 0; c < H; ++c) {
+        float qv = (float)oracle_e4m3fn_decode(q_row[c]);
+        float v = qv * scales[c / 128];
+        y_row[c] = oracle_bf16_rne(v);
+    }
+}
+
+/* ------------------------------------------------------------------- pack */
+
+/* Dispatch pack into fixed-shape per-expert receive buffers ([L14] §3: data
+ * [local experts, M * ranks, hidden] plus a count per local expert; [V1] §6.3
+ * the same shape for use_fp8; [ASC] phase 3: a map of which slot holds which
+ * token).  Global layout here: recv_x[e][j] with e the global expert id
+ * (rank r owns e in [r*L, (r+1)*L)) and j < S.
+ *
+ * For each token t (in order) the payload is formed once: the bf16 row, or
+ * the FP8 row and its scales.  Then for each valid (t,k), e = topk_idx[t,k],
+ * j = expert_slot[t,k]:
+ *   recv_x[e][j] = payload, recv_scales[e][j][:] = scales (FP8 only),
+ *   recv_src_idx[e][j] = t.
+ * Rows j >= count_e are not written. */
+int oracle_pack(int32_t N, int32_t H, int32_t K, int32_t E, int32_t S, int32_t use_fp8,
+                const uint16_t *x, const int64_t *topk_idx, const int32_t *expert_slot,
+                void *recv_x, float *recv_scales, int32_t *recv_src_idx)
+{
+    if (N < 0 || H < 1 || K < 1 || E < 1 || S < 0 || (use_fp8 && H % 128 != 0))
+        return ORACLE_BAD_ARGS;
+    int status = ORACLE_OK;
+    int32_t G = H / 128;
+    uint8_t *q = (uint8_t *)malloc((size_t)H);
+    float *sc = (float *)malloc(sizeof(float) * (size_t)(G > 0 ? G : 1));
+    if (!q || !sc) {
+        free(q);
+        free(sc);
+        return ORACLE_BAD_ARGS;
+    }
+    for (int32_t t = 0; t < N; ++t) {
+        const uint16_t *xt = x + (size_t)t * H;
+        if (use_fp8)
+            oracle_quantize_row(H, xt, q, sc);
+        for (int32_t k = 0; k < K; ++k) {
+            size_t i = (size_t)t * K + k;
+            int32_t e = routed_expert(topk_idx[i], E, &status);
+            if (e < 0)
+                continue;
+            int32_t j = expert_slot[i];
+            if (j < 0 || j >= S) {
+                status |= ORACLE_BAD_SLOT;
+                continue;
+            }
+            size_t row = (size_t)e * S + j;
+            if (use_fp8) {
+                memcpy((uint8_t *)recv_x + row * H, q, (size_t)H);
+                memcpy(recv_scales + row * G, sc, sizeof(float) * (size_t)G);
+            } else {
+                memcpy((uint16_t *)recv_x + row * H, xt, sizeof(uint16_t) * (size_t)H);
+            }
+            recv_src_idx[row] = t;
+        }
+    }
+    free(q);
+    free(sc);
+    return status;
+}
+
+/* ---------------------------------------------------------------- combine */
+
+/* Combine ([ASC] "Two Transfers" and "Combine: More Output, Same Cost":
+ * results come back to the origin, are weighted by the router scores and
+ * summed; [V1] §5.2(6): the reduction is BF16 in, BF16 out; [L14] exercise:
+ * combined[i] += w[i,k] * out(i, e)).  Per token t and channel c:
+ *   acc = +0
+ *   for k = 0..K-1 with a valid expert e and slot j:
+ *       acc = fmaf(w[t,k], float(y[e][j][c]), acc)
+ *   out[t,c] = bf16_RNE(acc)
+ * A token with every entry masked gets +0. */
+int oracle_combine(int32_t N, int32_t H, int32_t K, int32_t E, int32_t S, const uint16_t *y,
+                   const int64_t *topk_idx, const float *topk_weights,
+                   const int32_t *expert_slot, uint16_t *combined_x)
+{
+    if (N < 0 || H < 1 || K < 1 || E < 1 || S < 0)
+        return ORACLE_BAD_ARGS;
+    int status = ORACLE_OK;
+    float *acc = (float *)malloc(sizeof(float) * (size_t)H);
+    if (!acc)
+        return ORACLE_BAD_ARGS;
+    for (int32_t t = 0; t < N; ++t) {
+        for (int32_t c = 0; c < H; ++c)
+            acc[c] = 0.0f;
+        for (int32_t k = 0; k < K; ++k) {
+            size_t i = (size_t)t * K + k;
+            int32_t e = routed_expert(topk_idx[i], E, &status);
+            if (e < 0)
+                continue;
+            int32_t j = expert_slot[i];
+            if (j < 0 || j >= S) {
+                status |= ORACLE_BAD_SLOT;
+                continue;
+            }
+            const uint16_t *yr = y + ((size_t)e * S + j) * H;
+            float w = topk_weights[i];
+            for (int32_t c = 0; c < H; ++c)
+                acc[c] = fmaf(w, oracle_bf16_to_f32(yr[c]), acc[c]);
+        }
+        for (int32_t c = 0; c < H; ++c)
+            combined_x[(size_t)t * H + c] = oracle_bf16_rne(acc[c]);
+    }
+    free(acc);
+    return status;
+}
+
+/* ------------------------------------------------- array forms for pinning */
+
+void oracle_e4m3fn_encode_array(int64_t n, const float *v, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_e4m3fn_encode(v[i]);
+}
+
+void oracle_e4m3fn_decode_array(int64_t n, const uint8_t *c, double *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_e4m3fn_decode(c[i]);
+}
+
+void oracle_bf16_rne_array(int64_t n, const float *v, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_bf16_rne(v[i]);
+}
+
+void oracle_quantize_rows(int32_t N, int32_t H, const uint16_t *x, uint8_t *q, float *scales)
+{
+    for (int32_t t = 0; t < N; ++t)
+        oracle_quantize_row(H, x + (size_t)t * H, q + (size_t)t * H, scales + (size_t)t * (H / 128));
+}
+
+void oracle_dequant_rows(int32_t N, int32_t H, const uint8_t *q, const float *scales, uint16_t *y)
+{
+    for (int32_t t = 0; t < N; ++t)
+        oracle_dequant_row(H, q + (size_t)t * H, scales + (size_t)t * (H / 128), y + (size_t)t * H);
+}

@@ -1,0 +1,513 @@
+"""Pins that tie the CPU oracle to something other than itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` handle and raises
+``AssertionError`` when the oracle disagrees with what the DeepEP pages or the
+mathematics fix: a worked example built on the pages' own routing table,
+brute-force enumeration of the layout definition, format facts checked against
+torch's CPU casts and an independent nearest-value search, closed forms,
+special cases and error bounds.  The same functions run against planted-
+mistake builds of the oracle (``test_oracle_mutants.py``), where at least one
+of them must fail.
+
+Nothing here imports the GPU library.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ------------------------------------------------------------------ helpers
+
+def set_builder_layout(topk_idx: np.ndarray, E: int, R: int) -> dict:
+    """The layout written as set definitions, vectorised over a batch of
+    routings [C, N, K] (brute force, independent of the oracle's running
+    counters):
+
+    count_e          = |{(t,k) : idx[t,k] = e}|
+    expert_slot(t,k) = |{(t',k') <lex (t,k) : idx[t',k'] = idx[t,k]}|  (-1 if masked)
+    ranks(t)         = {idx[t,k] // (E/R) : idx[t,k] valid}
+    rank_slot(t,r)   = |{t' < t : r in ranks(t')}| if r in ranks(t) else -1
+    """
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    C, N, K = idx.shape
+    L = E // R
+    flat = idx.reshape(C, N * K)
+    valid = (flat >= 0) & (flat < E)
+    same = (flat[:, :, None] == flat[:, None, :]) & valid[:, :, None] & valid[:, None, :]
+    earlier = np.tril(np.ones((N * K, N * K), dtype=bool), k=-1)  # [j, j'] : j' < j
+    slot = (same & earlier[None]).sum(axis=2)
+    slot = np.where(valid, slot, -1).reshape(C, N, K)
+    counts = np.stack([(valid & (flat == e)).sum(axis=1) for e in range(E)], axis=1)
+    rank_of = np.where(valid, flat // L, -1).reshape(C, N, K)
+    in_rank = np.stack([(rank_of == r).any(axis=2) for r in range(R)], axis=2)  # [C, N, R]
+    before = np.cumsum(in_rank, axis=1) - in_rank
+    rank_slot = np.where(in_rank, before, -1)
+    offsets = np.concatenate([np.zeros((C, 1), np.int64), np.cumsum(counts, axis=1)], axis=1)
+    return {
+        "num_tokens_per_expert": counts,
+        "num_tokens_per_rank": in_rank.sum(axis=1),
+        "is_token_in_rank": in_rank.astype(np.uint8),
+        "expert_slot": slot,
+        "rank_slot": rank_slot,
+        "expert_offset": offsets,
+    }
+
+
+def fp8_table() -> np.ndarray:
+    """Values of all 256 E4M3FN codes from torch's float8_e4m3fn (library)."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def nearest_e4m3fn(v: np.ndarray) -> np.ndarray:
+    """Encode by nearest-value search over the 127 finite non-negative codes
+    (values from torch's table), ties to the even code; sign bit copied."""
+    table = fp8_table()[:127]  # codes 0x00..0x7E, increasing
+    a = np.abs(v.astype(np.float64))
+    hi = np.searchsorted(table, a, side="left").clip(1, 126)
+    lo = hi - 1
+    dlo = a - table[lo]
+    dhi = table[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a <= table[0], 0, code)
+    code = np.where(a >= table[126], 126, code)
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def ulp_bf16(v: np.ndarray) -> np.ndarray:
+    """Unit in the last place of bf16 at |v|: 2^(floor(log2|v|) - 7), with
+    2^-133 for zero and subnormal magnitudes."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    u = np.exp2(e - 7)
+    return np.where(a < 2.0 ** -126, 2.0 ** -133, u)
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def assert_combine_close(got_bits: np.ndarray, ref: np.ndarray, what: str = "combine",
+                         abs_slack=0.0):
+    """The combine acceptance bar: within 1 bf16 ulp of the reference, or
+    within 8e-3 relative.  ``abs_slack`` adds an absolute allowance when the
+    reference is exact (float64) rather than the same fp32 evaluation: a sum
+    of K products in fp32 with FMA is off by at most K 2^-24 sum|w y| (the
+    textbook forward bound), which matters where the terms cancel."""
+    got = bf16_to_f64(got_bits)
+    err = np.abs(got - ref)
+    ok = (err <= ulp_bf16(ref) + abs_slack) | (err <= 8e-3 * np.abs(ref) + abs_slack)
+    assert ok.all(), f"{what}: {int((~ok).sum())} elements outside tolerance, worst {err.max():.3e}"
+
+
+def place_rows(rows: np.ndarray, topk_idx: np.ndarray, expert_slot: np.ndarray, E: int, S: int,
+               fill=0) -> np.ndarray:
+    """Scatter one row per valid (t, k) entry (in (t, k) order) to y[e][slot]."""
+    H = rows.shape[1]
+    y = np.full((E, S, H), fill, dtype=rows.dtype)
+    flat_idx = topk_idx.reshape(-1)
+    flat_slot = expert_slot.reshape(-1)
+    valid = flat_idx >= 0
+    y[flat_idx[valid], flat_slot[valid]] = rows
+    return y
+
+
+# --------------------------------------------------------------------- pins
+
+def pin_lesson_example(o):
+    """Worked example on the routing table printed in the Lesson 14 dispatch /
+    combine exercise (4 tokens, 4 experts, top-2), layouts derived by hand
+    for 1, 2 and 4 ranks (tests/golden/lesson14_layout.json)."""
+    with open(os.path.join(GOLDEN, "lesson14_layout.json")) as f:
+        g = json.load(f)
+    idx = np.array(g["topk_idx"], dtype=np.int64)
+    for case in g["cases"]:
+        got = o.layout(idx, g["num_experts"], case["num_ranks"])
+        assert got["status"] == 0
+        for key, want in case["expected"].items():
+            assert np.array_equal(got[key], np.array(want)), (case["num_ranks"], key, got[key], want)
+
+
+def _enumerate_cases(N, K, E):
+    vals = range(-1, E)
+    return np.array(list(itertools.product(vals, repeat=N * K)), dtype=np.int64).reshape(-1, N, K)
+
+
+def pin_layout_bruteforce(o, shapes=((3, 2, 4, 2), (2, 3, 4, 4), (4, 2, 3, 3), (3, 2, 4, 1))):
+    """Every routing in {-1..E-1}^(N x K) for small shapes against the set-
+    builder definition."""
+    for (N, K, E, R) in shapes:
+        cases = _enumerate_cases(N, K, E)
+        want = set_builder_layout(cases, E, R)
+        for c in range(cases.shape[0]):
+            got = o.layout(cases[c], E, R)
+            assert got["status"] == 0
+            for key in want:
+                if not np.array_equal(got[key], want[key][c]):
+                    raise AssertionError(f"layout {key} differs for N,K,E,R={N, K, E, R} "
+                                         f"routing {cases[c].tolist()}: {got[key]} vs {want[key][c]}")
+
+
+def pin_layout_bad_ids(o):
+    """Ids >= E or < -1 behave like -1 and raise the bad-id status bit."""
+    rng = np.random.default_rng(7)
+    E, R = 6, 3
+    idx = rng.integers(-1, E, size=(40, 3))
+    bad = idx.copy()
+    pos = rng.permutation(bad.size)[:15]
+    bad.reshape(-1)[pos] = rng.choice([-5, -2, E, E + 3, 1 << 40], size=15)
+    masked = bad.copy()
+    masked[(masked < -1) | (masked >= E)] = -1
+    got_bad = o.layout(bad, E, R)
+    got_masked = o.layout(masked, E, R)
+    assert got_bad["status"] & 1 and got_masked["status"] == 0
+    for key in ("num_tokens_per_expert", "num_tokens_per_rank", "is_token_in_rank", "expert_slot",
+                "rank_slot", "expert_offset"):
+        assert np.array_equal(got_bad[key], got_masked[key]), key
+
+
+def check_layout_invariants(lay: dict, topk_idx: np.ndarray, E: int, R: int):
+    """Invariants that hold for every routing: counts sum to the number of
+    valid entries; per expert the slots are a permutation of [0, count); per
+    rank the rank slots are a permutation of [0, count), so each token is
+    counted at most once per rank; offsets are the exclusive prefix."""
+    idx = np.asarray(topk_idx)
+    N, K = idx.shape
+    L = E // R
+    valid = idx >= 0
+    P = int(valid.sum())
+    cnt_e = lay["num_tokens_per_expert"].astype(np.int64)
+    cnt_r = lay["num_tokens_per_rank"].astype(np.int64)
+    assert cnt_e.sum() == P
+    assert lay["expert_offset"][E] == P
+    assert np.array_equal(lay["expert_offset"][:-1], np.concatenate([[0], np.cumsum(cnt_e)[:-1]]))
+    slot = lay["expert_slot"]
+    assert np.all(slot[~valid] == -1)
+    for e in range(E):
+        s = np.sort(slot[idx == e])
+        assert np.array_equal(s, np.arange(cnt_e[e])), f"expert {e} slots not a permutation"
+    mask = lay["is_token_in_rank"].astype(bool)
+    rs = lay["rank_slot"]
+    assert np.all(rs[~mask] == -1)
+    for r in range(R):
+        s = np.sort(rs[mask[:, r], r])
+        assert np.array_equal(s, np.arange(cnt_r[r])), f"rank {r} slots not a permutation"
+    assert np.all(cnt_r <= N)
+    # the mask is exactly the set of ranks holding a valid expert of the token
+    want_mask = np.zeros((N, R), dtype=bool)
+    rows = np.repeat(np.arange(N), K)
+    fv = valid.reshape(-1)
+    want_mask[rows[fv], idx.reshape(-1)[fv] // L] = True
+    assert np.array_equal(mask, want_mask)
+    assert cnt_r.sum() == want_mask.sum() <= P
+
+
+def pin_layout_invariants(o, inputs_list):
+    for (inp, E, R) in inputs_list:
+        lay = o.layout(inp["topk_idx"], E, R)
+        assert lay["status"] == 0
+        check_layout_invariants(lay, inp["topk_idx"], E, R)
+
+
+def fp8_probe_values() -> np.ndarray:
+    """float32 values around every E4M3FN code and every midpoint between
+    neighbouring codes (+-16 ulps), special values, both signs, plus a
+    random sample of [0, 448]."""
+    table = fp8_table()[:127].astype(np.float32)
+    mids = ((table[:-1].astype(np.float64) + table[1:]) / 2).astype(np.float32)
+    centres = np.concatenate([table, mids]).view(np.uint32).astype(np.int64)
+    offs = np.arange(-16, 17, dtype=np.int64)
+    pts = (centres[:, None] + offs[None, :]).reshape(-1)
+    pts = pts[(pts >= 0) & (pts <= 0x43E00000)].astype(np.uint32)
+    rng = np.random.default_rng(11)
+    rnd = rng.integers(0, 0x43E00000 + 1, size=1 << 20, dtype=np.int64).astype(np.uint32)
+    tiny = np.arange(0, 4096, dtype=np.uint32)  # fp32 subnormals and zero
+    allb = np.unique(np.concatenate([pts, rnd, tiny]))
+    pos = allb.view(np.float32)
+    return np.concatenate([pos, -pos])
+
+
+def pin_e4m3fn(o, values: np.ndarray | None = None):
+    """Encoder against nearest-value search and torch's float8_e4m3fn cast;
+    decoder against torch's table for all 256 codes."""
+    table = fp8_table()
+    dec = o.e4m3fn_decode(np.arange(256, dtype=np.uint8))
+    both_nan = np.isnan(dec) & np.isnan(table)
+    assert np.all(both_nan | (dec == table)), "decode differs from torch's table"
+    assert np.array_equal(np.isnan(dec), np.isnan(table))
+    v = fp8_probe_values() if values is None else values
+    got = o.e4m3fn_encode(v)
+    ref_search = nearest_e4m3fn(v)
+    ref_torch = torch.from_numpy(np.ascontiguousarray(v)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    bad = np.nonzero(got != ref_search)[0]
+    assert bad.size == 0, f"encode vs nearest search: {bad.size} differ, e.g. {v[bad[:4]]} -> {got[bad[:4]]} vs {ref_search[bad[:4]]}"
+    bad = np.nonzero(got != ref_torch)[0]
+    assert bad.size == 0, f"encode vs torch cast: {bad.size} differ, e.g. {v[bad[:4]]}"
+
+
+def pin_e4m3fn_exhaustive_positive(o, chunk_bits: int = 26):
+    """Every non-negative binary32 up to 448 (about 1.14e9 values) against
+    torch's float8_e4m3fn cast."""
+    top = 0x43E00000
+    step = 1 << chunk_bits
+    for start in range(0, top + 1, step):
+        stop = min(start + step, top + 1)
+        v = np.arange(start, stop, dtype=np.uint32).view(np.float32)
+        got = o.e4m3fn_encode(v)
+        ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        bad = np.nonzero(got != ref)[0]
+        assert bad.size == 0, f"encode vs torch at {v[bad[:4]]}: {got[bad[:4]]} vs {ref[bad[:4]]}"
+
+
+def pin_bf16(o):
+    """bf16 round-to-nearest-even against torch's CPU cast: every high half
+    combined with the low halves that decide rounding, plus random patterns."""
+    hi = np.arange(0, 1 << 16, dtype=np.uint32)
+    hi = hi[((hi >> 7) & 0xFF) != 0xFF]  # finite patterns (NaN payloads aside)
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x4000, 0xC000], dtype=np.uint32)
+    bits = ((hi[:, None] << 16) | lows[None, :]).reshape(-1)
+    rng = np.random.default_rng(5)
+    bits = np.concatenate([bits, rng.integers(0, 1 << 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)])
+    v = bits.view(np.float32)
+    v = v[np.isfinite(v)]
+    got = o.bf16_rne(v)
+    ref = torch.from_numpy(np.ascontiguousarray(v)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, f"bf16 RNE differs at {v[bad[:4]]}: {got[bad[:4]]} vs {ref[bad[:4]]}"
+
+
+def _rows_with_amax(amax_bits: np.ndarray) -> np.ndarray:
+    """One 128-channel block per value: the value, its negation, zeros and
+    a few smaller entries, so the block amax is exactly that value."""
+    n = amax_bits.size
+    rows = np.zeros((n, 128), dtype=np.uint16)
+    rows[:, 0] = amax_bits
+    rows[:, 1] = amax_bits | 0x8000
+    rows[:, 2] = amax_bits >> 1  # smaller magnitude (finite, non-negative)
+    return rows
+
+
+def pin_scales_closed_form(o):
+    """For every finite bf16 magnitude as the block amax, the shipped scale
+    is RN_f32(max(amax, 1e-4) / 448), computed here in float64 and rounded
+    once (double rounding is harmless for a quotient), and the element equal
+    to the amax encodes to the largest code +-448 when amax >= 1e-4."""
+    mags = np.arange(0, 0x7F80, dtype=np.uint32).astype(np.uint16)  # +0 .. largest finite
+    rows = _rows_with_amax(mags)
+    q, sc = o.quantize_rows(rows)
+    a = bf16_to_f64(mags)
+    floor = float(np.float32(1e-4))
+    ap = np.maximum(a, floor)
+    want_scale = (ap / 448.0).astype(np.float32)
+    assert np.array_equal(sc[:, 0], want_scale), "scale is not RN(max(amax, 1e-4) / 448)"
+    big = a >= floor
+    assert np.all(q[big, 0] == 0x7E) and np.all(q[big, 1] == 0xFE)
+    # the encoded values are the nearest codes to RN(x * RN(448 / a'))
+    inv = (448.0 / ap).astype(np.float32)
+    v = (bf16_to_f64(rows).astype(np.float32) * inv[:, None]).astype(np.float32)
+    v = np.clip(v, -448.0, 448.0).astype(np.float32)
+    assert np.array_equal(q, nearest_e4m3fn(v))
+
+
+def pin_dequant_bound(o):
+    """Quantise-then-dequantise error bound: |y - x| <= 2^-4 |x| (normal FP8
+    range, half an ulp of a 3-bit mantissa) + 2^-10 scale (subnormal FP8
+    range) + half a bf16 ulp of y, on rows of widely varying magnitude."""
+    rng = np.random.default_rng(3)
+    n, h = 64, 512
+    base = rng.standard_normal((n, h)).astype(np.float32)
+    mag = np.exp2(rng.uniform(-20, 20, size=(n, h // 128, 1))).astype(np.float32)
+    x = (base.reshape(n, h // 128, 128) * mag).reshape(n, h)
+    x[0, :128] = 0.0                                  # all-zero block
+    x[1, 128:256] = 0.0
+    x[1, 130] = 3.0                                   # one non-zero in a block
+    x[2, :128] = np.float32(1e-6)                     # below the amax floor
+    xb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    q, sc = o.quantize_rows(xb)
+    y = bf16_to_f64(o.dequant_rows(q, sc))
+    xv = bf16_to_f64(xb)
+    s = np.repeat(sc.astype(np.float64), 128, axis=1)
+    bound = 2.0 ** -4 * np.abs(xv) * (1 + 2.0 ** -20) + 2.0 ** -10 * s * (1 + 2.0 ** -20) + 0.5 * ulp_bf16(y)
+    err = np.abs(y - xv)
+    assert np.all(err <= bound), f"dequant error {err.max()} above bound at {np.argmax(err - bound)}"
+    assert np.all(y[0, :128] == 0) and np.all(q[0, :128] == 0)
+
+
+def _layout_and_pack(o, inp, E, R, S, use_fp8):
+    lay = o.layout(inp["topk_idx"], E, R)
+    recv_x, recv_sc, recv_src, st = o.pack(inp["x_bits"], inp["topk_idx"], lay["expert_slot"], E, S,
+                                           use_fp8, fill=0xA5A5)
+    assert st == 0
+    return lay, recv_x, recv_sc, recv_src
+
+
+def check_pack(o, inp, lay, recv_x, recv_sc, recv_src, E, S, use_fp8, fill=0xA5A5):
+    """Each valid (t, k) row holds token t's payload (bit copy, or the FP8
+    row and scales of token t); recv_src_idx names t; rows past the count
+    keep the fill; exactly one row is written per valid entry (the Lesson 14
+    exercise's conservation check, with masked entries removed)."""
+    idx = inp["topk_idx"]
+    x = inp["x_bits"]
+    cnt = lay["num_tokens_per_expert"]
+    written = np.zeros(recv_src.shape, dtype=bool)
+    for e in range(E):
+        written[e, :cnt[e]] = True
+    assert np.all(recv_src[written] >= 0)
+    assert np.all(recv_src[~written] == -2)
+    assert int(written.sum()) == int((idx >= 0).sum())
+    if use_fp8:
+        q, sc = o.quantize_rows(x)
+    t_of = recv_src[written]
+    if use_fp8:
+        assert np.array_equal(recv_x[written], q[t_of])
+        assert np.array_equal(recv_sc[written], sc[t_of])
+        assert np.all(recv_x[~written] == (fill & 0xFF))
+    else:
+        assert np.array_equal(recv_x[written], x[t_of])
+        assert np.all(recv_x[~written] == fill)
+    tt, kk = np.nonzero(idx >= 0)
+    assert np.array_equal(recv_src[idx[tt, kk], lay["expert_slot"][tt, kk]], tt)
+
+
+def pin_pack(o, cases):
+    for (inp, E, R, S, use_fp8) in cases:
+        lay, rx, rs, src = _layout_and_pack(o, inp, E, R, S, use_fp8)
+        check_pack(o, inp, lay, rx, rs, src, E, S, use_fp8)
+
+
+def pin_pack_fp8_is_row_quantiser(o):
+    """The pack's FP8 rows equal the per-token quantiser's rows: a token
+    routed to several experts gets the same bytes everywhere, computed once."""
+    rng = np.random.default_rng(9)
+    x = torch.from_numpy(rng.standard_normal((5, 256)).astype(np.float32)).to(torch.bfloat16)
+    xb = x.view(torch.int16).numpy().view(np.uint16)
+    idx = np.array([[0, 1], [1, 2], [2, 3], [3, 0], [0, 2]], dtype=np.int64)
+    lay = o.layout(idx, 4, 2)
+    rx, rs, src, st = o.pack(xb, idx, lay["expert_slot"], 4, 8, True)
+    q, sc = o.quantize_rows(xb)
+    for t in range(5):
+        for k in range(2):
+            e, j = idx[t, k], lay["expert_slot"][t, k]
+            assert np.array_equal(rx[e, j], q[t]) and np.array_equal(rs[e, j], sc[t])
+
+
+def pin_combine_scalar_experts(o, cases):
+    """Closed form: expert e returns bf16(c_e x) with c_e = 2^((e mod 5) - 2),
+    exact in bf16, so out = (sum_k w_k c_{e_k}) x, computed here in float64,
+    within the combine tolerance.  A wrong slot, expert or weight index
+    changes the result."""
+    for (inp, E, R, S) in cases:
+        idx, w, x = inp["topk_idx"], inp["topk_weights"], inp["x_bits"]
+        lay = o.layout(idx, E, R)
+        c = np.exp2((np.arange(E) % 5) - 2.0)
+        tt, kk = np.nonzero(idx >= 0)
+        rows = (bf16_to_f64(x[tt]) * c[idx[tt, kk]][:, None]).astype(np.float32)
+        rows = rows.view(np.uint32)
+        assert np.all((rows & 0xFFFF) == 0)  # exact in bf16
+        y = place_rows((rows >> 16).astype(np.uint16), idx, lay["expert_slot"], E, S)
+        out, st = o.combine(y, idx, w, lay["expert_slot"], E, S)
+        assert st == 0
+        coef = np.where(idx >= 0, w.astype(np.float64) * c[np.where(idx >= 0, idx, 0)], 0.0).sum(axis=1)
+        assert_combine_close(out, coef[:, None] * bf16_to_f64(x), "scalar-expert combine")
+
+
+def _renormalised(w, idx):
+    wv = np.where(idx >= 0, w, 0.0).astype(np.float32)
+    s = wv.sum(axis=1, keepdims=True, dtype=np.float32)
+    return np.where(s > 0, wv / np.where(s > 0, s, 1), 0.0).astype(np.float32)
+
+
+def pin_identity_expert(o, cases):
+    """Identity expert with weights summing to 1 over the valid entries
+    reproduces the token exactly: x itself for BF16 dispatch, the dequantised
+    FP8 row for FP8 dispatch (as values: -0 comes back as +0).  Tokens with
+    every entry masked give +0."""
+    for (inp, E, R, S, use_fp8) in cases:
+        idx = inp["topk_idx"]
+        w = _renormalised(inp["topk_weights"], idx)
+        lay, rx, rs, src = _layout_and_pack(o, inp, E, R, S, use_fp8)
+        if use_fp8:
+            H = rx.shape[-1]
+            y = o.dequant_rows(rx.reshape(-1, H), rs.reshape(-1, H // 128)).reshape(rx.shape)
+            q, sc = o.quantize_rows(inp["x_bits"])
+            want = o.dequant_rows(q, sc)
+        else:
+            y = rx
+            want = inp["x_bits"]
+        out, st = o.combine(y, idx, w, lay["expert_slot"], E, S)
+        assert st == 0
+        alive = (idx >= 0).any(axis=1)
+        # compared as values: the sum starts at +0, so a -0 channel comes back as +0
+        assert np.array_equal(bf16_to_f64(out[alive]), bf16_to_f64(want[alive])), \
+            "identity expert did not reproduce the token"
+        assert np.all(out[~alive] == 0)
+
+
+def pin_lesson_dense(o, H: int = 4, seed: int = 42):
+    """The Lesson 14 exercise's end-to-end check: dispatch, per-expert linear
+    map y = x W_e, combine, against the dense sum_k w_k (x W_{e_k}).  Here
+    the expert outputs are rounded to bf16 (the combine's input type), so the
+    reference uses the same rounded rows and the combine tolerance; the
+    unrounded dense value is within a few bf16 ulps."""
+    rng = np.random.default_rng(seed)
+    N, K, E = 4, 2, 4
+    idx = np.array([[0, 2], [1, 3], [0, 3], [1, 2]], dtype=np.int64)
+    x = torch.from_numpy(rng.standard_normal((N, H)).astype(np.float32)).to(torch.bfloat16)
+    xb = x.view(torch.int16).numpy().view(np.uint16)
+    raw = rng.uniform(0.1, 1.0, size=(N, K))
+    w = (raw / raw.sum(axis=1, keepdims=True)).astype(np.float32)
+    W = rng.standard_normal((E, H, H))
+    lay = o.layout(idx, E, 2)
+    rx, _, _, st = o.pack(xb, idx, lay["expert_slot"], E, N, False)
+    y = np.zeros_like(rx)
+    xs = bf16_to_f64(rx)
+    for e in range(E):
+        ye = (xs[e] @ W[e]).astype(np.float32)
+        y[e] = torch.from_numpy(ye).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    out, st = o.combine(y, idx, w, lay["expert_slot"], E, N)
+    xf = bf16_to_f64(xb)
+    dense_rounded = np.zeros((N, H))
+    dense = np.zeros((N, H))
+    for t in range(N):
+        for k in range(K):
+            e = idx[t, k]
+            yr = torch.from_numpy((xf[t] @ W[e]).astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+            dense_rounded[t] += float(w[t, k]) * yr
+            dense[t] += float(w[t, k]) * (xf[t] @ W[e])
+    assert_combine_close(out, dense_rounded, "lesson dense equivalence")
+    scale = np.abs(dense).max()
+    assert np.all(np.abs(bf16_to_f64(out) - dense) <= 2.0 ** -6 * scale)
+
+
+def pin_pages_pass_bytes(o):
+    """Ascend deep dive, "Two Transfers": 16,384 tokens x 7,168 values x 2 B
+    x 6 copies is about 1.4 GB per dispatch pass.  The BF16 pack writes one
+    row per (token, expert) entry: 98,304 rows at that shape (H is shrunk to
+    8 here; the row count does not depend on H)."""
+    with open(os.path.join(GOLDEN, "pages_figures.json")) as f:
+        g = json.load(f)["ascend_dispatch_pass"]
+    N, K, E, R, H = g["tokens"], g["topk"], g["experts"], g["ranks"], 8
+    rng = np.random.default_rng(17)
+    idx = np.argsort(rng.random((N, E)), axis=1)[:, :K].astype(np.int64)
+    x = rng.integers(0, 0x3F80, size=(N, H)).astype(np.uint16)
+    lay = o.layout(idx, E, R)
+    S = int(lay["num_tokens_per_expert"].max())
+    rx, _, src, st = o.pack(x, idx, lay["expert_slot"], E, S, False)
+    rows = int((src >= 0).sum())
+    assert rows == N * K
+    total = rows * g["hidden"] * g["bytes_per_value"]
+    assert abs(total - g["bytes_approx"]) / g["bytes_approx"] < 0.01, total
+
+
+CHEAP_PINS = ("pin_lesson_example", "pin_bf16", "pin_e4m3fn", "pin_scales_closed_form",
+              "pin_dequant_bound", "pin_pack_fp8_is_row_quantiser", "pin_lesson_dense",
+              "pin_layout_bad_ids")
