@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE expert-parallel dispatch layout + dispatch pack +
+combine on one MI355X.
+
+A step is one pass of the whole path (ep_layout, ep_dispatch, ep_combine)
+over one batch: the prefill workload, 4,096 tokens x hidden 7,168, 256 experts
+in 8 groups over 8 logical ranks, top-4 groups then top-8 experts, FP8
+dispatch with one scale per 128 channels, BF16 combine (the DeepEP V1 Legacy
+guide's §2.1 normal-kernel benchmark shape).  The decode workload (128 tokens,
+top-8, FP8; §2.2's low-latency shape) is timed the same way and reported in
+the same JSON line.
+
+Inputs are seeded synthetic data resident in HBM before timing starts.  Each
+timed step is bracketed by HIP events on the stream the kernels run on, with
+an event between phases; before each step an untimed 1 GiB write evicts the
+256 MB Infinity Cache, so the figures are cold-HBM figures ("warm" figures,
+without the eviction, are reported beside them).  Throughput counts the
+algorithmic bytes of the method (reads + writes it must do), not allocation,
+poisoning or the expert output generation.
+
+Prints ONE JSON line.  With --gpus > 1 it exits: the path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak, AMD's published figure
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def algorithmic_bytes(n, h, k, e, r, p, use_fp8):
+    """Bytes the method must move per call, by phase.
+
+    layout : read topk_idx (8 B per entry); write expert_slot (4 B per entry),
+             rank_slot (4 B) and the u8 mask per (token, rank), the two count
+             arrays and the offsets.
+    pack   : read x once per token, topk_idx + expert_slot per entry; write
+             per valid entry one row (H bytes FP8 or 2H bytes BF16), its
+             source index (4 B) and, for FP8, H/128 fp32 scales.
+    combine: read one bf16 expert row per valid entry and idx + slot + weight
+             per entry; write one bf16 output row per token."""
+    b = 1 if use_fp8 else 2
+    layout = 12 * n * k + 5 * n * r + 4 * (2 * e + r + 1)
+    pack = 2 * n * h + 12 * n * k + p * (b * h + 4 + (4 * (h // 128) if use_fp8 else 0))
+    combine = 2 * p * h + 16 * n * k + 2 * n * h
+    return {"layout": layout, "dispatch": pack, "combine": combine,
+            "total": layout + pack + combine}
+
+
+def kernel_source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "combine_ep_layout_02_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload_name, kernel, digest):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload_name}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_digest:\s*(\w+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != digest:
+        return None
+    return float(t.group(1))
+
+
+def percentile(xs, q):
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
+
+
+def run_workload(wid, steps, warmup, scrub_bytes, say):
+    import torch
+    from combine_ep_layout_02_amd import ep
+    from combine_ep_layout_02_amd import workloads as W
+
+    w = W.WORKLOADS[wid]
+    shape = ep.shape_of(w)
+    say(f"workload {w.name}: generating inputs")
+    inp = W.make_inputs(w)
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    topk_idx = torch.from_numpy(inp["topk_idx"]).to(dev)
+    topk_weights = torch.from_numpy(inp["topk_weights"]).to(dev)
+    x = torch.from_numpy(inp["x_bits"].view(np.int16)).to(dev)
+    buf = ep.allocate(shape, dev, parts=("layout", "dispatch", "combine"))
+    g = torch.Generator(device=dev)
+    g.manual_seed(2000 + wid)
+    # expert outputs: bf16 N(0, 1) in every row (rows past a count are never read)
+    y = torch.randn((w.num_experts, w.expert_capacity, w.hidden), dtype=torch.bfloat16,
+                    device=dev, generator=g).view(torch.int16)
+    scrub = torch.empty(scrub_bytes // 4, dtype=torch.int32, device=dev) if scrub_bytes else None
+    P = inp["num_valid"]
+    nbytes = algorithmic_bytes(w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks, P,
+                               w.use_fp8)
+
+    def step(ev):
+        """One pass of the path; ev[0..3] bracket layout, dispatch, combine."""
+        ev[0].record(stream)
+        ep.ep_layout(shape, topk_idx, buf["num_tokens_per_rank"], buf["num_tokens_per_expert"],
+                     buf["is_token_in_rank"], buf["expert_slot"], buf["rank_slot"],
+                     buf["expert_offset"], buf["workspace"], buf["status"], stream)
+        ev[1].record(stream)
+        ep.ep_dispatch(shape, x, topk_idx, buf["expert_slot"], buf["recv_x"], buf["recv_scales"],
+                       buf["recv_src_idx"], buf["status"], stream)
+        ev[2].record(stream)
+        ep.ep_combine(shape, y, topk_idx, topk_weights, buf["expert_slot"], buf["combined_x"],
+                      buf["status"], stream)
+        ev[3].record(stream)
+
+    say(f"workload {w.name}: {warmup} warmup steps")
+    for _ in range(warmup):
+        step([torch.cuda.Event(enable_timing=True) for _ in range(4)])
+    torch.cuda.synchronize()
+    if int(buf["status"].item()) != 0:
+        raise RuntimeError(f"device status {int(buf['status'].item())} during warmup")
+
+    def timed(n, with_scrub):
+        phases = {"layout": [], "dispatch": [], "combine": [], "total": []}
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            if with_scrub:
+                scrub.fill_(i)
+            step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        for e4 in evs:
+            phases["layout"].append(e4[0].elapsed_time(e4[1]) * 1e3)
+            phases["dispatch"].append(e4[1].elapsed_time(e4[2]) * 1e3)
+            phases["combine"].append(e4[2].elapsed_time(e4[3]) * 1e3)
+            phases["total"].append(e4[0].elapsed_time(e4[3]) * 1e3)
+        return phases, wall
+
+    say(f"workload {w.name}: {steps} timed steps (cache scrubbed before each)")
+    cold, wall_cold = timed(steps, scrub is not None)
+    say(f"workload {w.name}: {steps} timed steps back to back (warm)")
+    warm, wall_warm = timed(steps, False)
+    # a plain copy of known size, for scaling the counter readings of a profile run
+    if scrub is not None:
+        half = scrub.numel() // 2
+        scrub[half:].copy_(scrub[:half])
+    torch.cuda.synchronize()
+
+    def summarize(ph):
+        out = {}
+        for k, v in ph.items():
+            med = statistics.median(v)
+            out[k] = {"us_median": round(med, 2), "us_mean": round(statistics.fmean(v), 2),
+                      "us_p10": round(percentile(v, 10), 2), "us_p90": round(percentile(v, 90), 2),
+                      "gbps_median": round(nbytes[k] / (med * 1e-6) / 1e9, 1)}
+        return out
+
+    return {
+        "workload": w, "bytes": nbytes, "num_valid": P,
+        "cold": summarize(cold), "warm": summarize(warm),
+        "cold_raw": cold, "wall_cold_s": wall_cold, "wall_warm_s": wall_warm,
+        "inputs": inp,
+    }
+
+
+def cpu_baseline(inp, w, reps, say):
+    """The CPU oracle as it stands (single-threaded C through its ctypes
+    wrapper, allocation of its output arrays included) on the same inputs."""
+    import oracle
+
+    o = oracle.get()
+    P = inp["num_valid"]
+    nbytes = algorithmic_bytes(w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks, P,
+                               w.use_fp8)["total"]
+    rng = np.random.default_rng(3000)
+    times = []
+    rows = None
+    for r in range(reps):
+        say(f"cpu oracle step {r + 1}/{reps}")
+        t0 = time.perf_counter()
+        lay = o.layout(inp["topk_idx"], w.num_experts, w.num_ranks)
+        s_or = max(1, int(lay["num_tokens_per_expert"].max()))
+        o.pack(inp["x_bits"], inp["topk_idx"], lay["expert_slot"], w.num_experts, s_or, w.use_fp8)
+        t1 = time.perf_counter()
+        if rows is None:  # expert outputs (input generation, not timed)
+            from combine_ep_layout_02_amd import workloads as W
+            rows = W.bf16_bits(rng.standard_normal((P, w.hidden), dtype=np.float32))
+            yv = np.zeros((w.num_experts, s_or, w.hidden), np.uint16)
+            valid = inp["topk_idx"] >= 0
+            yv[inp["topk_idx"][valid], lay["expert_slot"][valid]] = rows
+        t2 = time.perf_counter()
+        o.combine(yv, inp["topk_idx"], inp["topk_weights"], lay["expert_slot"], w.num_experts, s_or)
+        t3 = time.perf_counter()
+        times.append((t1 - t0) + (t3 - t2))
+    med = statistics.median(times)
+    return {"value": round(nbytes / med / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} full steps of {w.name} (layout + pack + combine, {w.num_tokens} tokens), "
+                      f"median {med * 1e3:.0f} ms per step, single-threaded C, "
+                      f"host has {os.cpu_count()} logical CPUs"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--scrub-mib", type=int, default=1024)
+    ap.add_argument("--cpu-reps", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--quiet", action="store_true")
+    args = ap.parse_args()
+
+    def say(msg):
+        if not args.quiet:
+            print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if args.gpus != 1:
+        print(f"bench.py runs the path on one GPU; --gpus {args.gpus} is not supported "
+              "(the logical EP ranks are regions of one GPU's HBM).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (MI355X)", file=sys.stderr)
+        sys.exit(2)
+    from combine_ep_layout_02_amd import ep
+
+    ep.lib()  # fail loudly if the HIP library is missing
+    scrub_bytes = args.scrub_mib << 20
+    prefill = run_workload(3, args.steps, args.warmup, scrub_bytes, say)
+    decode = None if args.no_decode else run_workload(2, args.steps, args.warmup, scrub_bytes, say)
+
+    w = prefill["workload"]
+    cold = prefill["cold"]
+    total_us = cold["total"]["us_mean"]
+    value = prefill["bytes"]["total"] / (total_us * 1e-6) / 1e9
+    comb_us = cold["combine"]["us_mean"]
+    digest = kernel_source_digest(["combine.hip", "ep_device.h"])
+    roofline = {
+        "bound": "hbm",
+        "kernel": "combine_kernel (ep_combine)",
+        "achieved": round(prefill["bytes"]["combine"] / (comb_us * 1e-6) / 1e9, 1),
+        "peak": PEAK_HBM_GBPS,
+        "unit": "GB/s",
+        "frac": round(prefill["bytes"]["combine"] / (comb_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+        "traffic": committed_traffic(w.name, "combine", digest),
+        "algorithmic_bytes_per_launch": prefill["bytes"]["combine"],
+        "avg_launch_us": round(comb_us, 2),
+    }
+    pack_us = cold["dispatch"]["us_mean"]
+    extra = {
+        "phases_us_cold": {k: v for k, v in cold.items()},
+        "phases_us_warm": prefill["warm"],
+        "bytes_per_step": prefill["bytes"],
+        "dispatch_frac_of_peak": round(prefill["bytes"]["dispatch"] / (pack_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+        "gate_60pct_of_peak_us": round(prefill["bytes"]["total"] / (0.6 * PEAK_HBM_GBPS * 1e9) * 1e6, 1),
+        "wall_s_incl_scrub": round(prefill["wall_cold_s"], 4),
+        "wall_s_warm": round(prefill["wall_warm_s"], 4),
+    }
+    if decode is not None:
+        extra["decode_128x7168"] = {
+            "phases_us_cold": decode["cold"], "phases_us_warm": decode["warm"],
+            "bytes_per_step": decode["bytes"],
+        }
+    line = {
+        "metric": "dispatch+combine achieved HBM GB/s (4096 tok x hidden 7168, FP8 dispatch, BF16 combine)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_us / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32 (FP8 E4M3FN / BF16 storage)",
+        "data": "synthetic (seeded numpy inputs; expert outputs bf16 N(0,1) from a seeded torch generator)",
+        "config": {"workload": w.name, "num_tokens": w.num_tokens, "hidden": w.hidden,
+                   "num_topk": w.num_topk, "num_experts": w.num_experts, "num_ranks": w.num_ranks,
+                   "routing": "group-limited top-4 of 8 groups, top-8 experts",
+                   "num_max_dispatch_tokens_per_rank": w.num_max_dispatch_tokens_per_rank,
+                   "expert_capacity": w.expert_capacity, "dispatch": "fp8_e4m3fn, 1 scale / 128 ch",
+                   "combine": "bf16, fp32 accumulate", "parallelism": "1 GPU, 8 logical EP ranks"},
+        "roofline": roofline,
+        "cpu_baseline": None,
+        "extra": extra,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(prefill["inputs"], w, args.cpu_reps, say)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

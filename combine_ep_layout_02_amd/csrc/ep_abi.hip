@@ -1,0 +1,168 @@
+// ep_abi.hip -- the C ABI declared in include/ep.h: host-side validation,
+// buffer sizes and launches on the caller's stream.  Every static check runs
+// before anything is enqueued; no entry point allocates or synchronises.
+#include <stdint.h>
+
+#include "ep_internal.h"
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_shape(const ep_shape *s)
+{
+    if (!s)
+        return EP_ERR_NULL;
+    const int64_t N = s->num_tokens, H = s->hidden, K = s->num_topk, E = s->num_experts,
+                  R = s->num_ranks, M = s->num_max_dispatch_tokens_per_rank,
+                  S = s->expert_capacity;
+    if (N < 0 || H < 8 || H % 8 != 0 || K < 1 || E < 1 || R < 1 || E % R != 0)
+        return EP_ERR_SHAPE;
+    if (s->use_fp8 != 0 && s->use_fp8 != 1)
+        return EP_ERR_SHAPE;
+    if (s->use_fp8 && H % 128 != 0)
+        return EP_ERR_SHAPE;
+    if (K > EP_MAX_TOPK || E > EP_MAX_EXPERTS || R > EP_MAX_RANKS)
+        return EP_ERR_UNSUPPORTED;
+    if (M < 1 || N > M || S < M)
+        return EP_ERR_CAPACITY;
+    // indices stay within int32 where the kernels keep them in 32 bits, and
+    // byte offsets within int64
+    if (N * K > INT32_MAX || N * R > INT32_MAX || E * S > INT32_MAX)
+        return EP_ERR_UNSUPPORTED;
+    if (E * S > INT64_MAX / (H * 2))
+        return EP_ERR_UNSUPPORTED;
+    ep::LayoutPlan plan;
+    if (!ep::plan_layout(*s, &plan))
+        return EP_ERR_UNSUPPORTED;
+    return EP_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *ep_strerror(int code)
+{
+    switch (code) {
+    case EP_OK:
+        return "EP_OK";
+    case EP_ERR_NULL:
+        return "EP_ERR_NULL: a required pointer is NULL";
+    case EP_ERR_SHAPE:
+        return "EP_ERR_SHAPE: invalid shape";
+    case EP_ERR_CAPACITY:
+        return "EP_ERR_CAPACITY: num_tokens > num_max_dispatch_tokens_per_rank or "
+               "expert_capacity < num_max_dispatch_tokens_per_rank";
+    case EP_ERR_ALIGN:
+        return "EP_ERR_ALIGN: misaligned pointer";
+    case EP_ERR_UNSUPPORTED:
+        return "EP_ERR_UNSUPPORTED: size outside this build's limits";
+    case EP_ERR_HIP:
+        return "EP_ERR_HIP: kernel launch failed";
+    case EP_ERR_WORKSPACE:
+        return "EP_ERR_WORKSPACE: layout workspace missing or too small";
+    default:
+        return "unknown ep status code";
+    }
+}
+
+int ep_query_sizes(const ep_shape *s, ep_sizes *out)
+{
+    if (!out)
+        return EP_ERR_NULL;
+    const int rc = check_shape(s);
+    if (rc != EP_OK)
+        return rc;
+    const size_t N = s->num_tokens, H = s->hidden, K = s->num_topk, E = s->num_experts,
+                 R = s->num_ranks, S = s->expert_capacity;
+    const size_t rows = E * S;
+    out->recv_x = rows * H * (s->use_fp8 ? 1 : 2);
+    out->recv_scales = s->use_fp8 ? rows * (H / 128) * sizeof(float) : 0;
+    out->recv_src_idx = rows * sizeof(int32_t);
+    out->expert_out = rows * H * 2;
+    out->combined_x = N * H * 2;
+    out->num_tokens_per_rank = R * sizeof(int32_t);
+    out->num_tokens_per_expert = E * sizeof(int32_t);
+    out->is_token_in_rank = N * R;
+    out->expert_slot = N * K * sizeof(int32_t);
+    out->rank_slot = N * R * sizeof(int32_t);
+    out->expert_offset = (E + 1) * sizeof(int32_t);
+    ep::LayoutPlan plan;
+    ep::plan_layout(*s, &plan);
+    out->layout_workspace = plan.workspace_bytes;
+    return EP_OK;
+}
+
+int ep_layout(const ep_shape *s, const int64_t *topk_idx, int32_t *num_tokens_per_rank,
+              int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank, int32_t *expert_slot,
+              int32_t *rank_slot, int32_t *expert_offset, void *workspace, size_t workspace_bytes,
+              uint32_t *status, void *stream)
+{
+    const int rc = check_shape(s);
+    if (rc != EP_OK)
+        return rc;
+    const bool has_tokens = s->num_tokens > 0;
+    if (!num_tokens_per_rank || !num_tokens_per_expert)
+        return EP_ERR_NULL;
+    if (has_tokens && (!topk_idx || !is_token_in_rank || !expert_slot || !rank_slot))
+        return EP_ERR_NULL;
+    if (!aligned(topk_idx, 8) || !aligned(num_tokens_per_rank, 4) ||
+        !aligned(num_tokens_per_expert, 4) || !aligned(expert_slot, 4) || !aligned(rank_slot, 4) ||
+        !aligned(expert_offset, 4) || !aligned(status, 4) || !aligned(workspace, 16))
+        return EP_ERR_ALIGN;
+    ep::LayoutPlan plan;
+    ep::plan_layout(*s, &plan);
+    if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+        return EP_ERR_WORKSPACE;
+    const hipError_t err = ep::launch_layout(
+        *s, plan, topk_idx, num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank,
+        expert_slot, rank_slot, expert_offset, static_cast<int32_t *>(workspace), status,
+        static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+int ep_dispatch(const ep_shape *s, const uint16_t *x, const int64_t *topk_idx,
+                const int32_t *expert_slot, void *recv_x, float *recv_scales,
+                int32_t *recv_src_idx, uint32_t *status, void *stream)
+{
+    const int rc = check_shape(s);
+    if (rc != EP_OK)
+        return rc;
+    if (s->num_tokens == 0)
+        return EP_OK;
+    if (!x || !topk_idx || !expert_slot || !recv_x || !recv_src_idx)
+        return EP_ERR_NULL;
+    if (s->use_fp8 && !recv_scales)
+        return EP_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(topk_idx, 8) ||
+        !aligned(expert_slot, 4) || !aligned(recv_scales, 4) || !aligned(recv_src_idx, 4) ||
+        !aligned(status, 4))
+        return EP_ERR_ALIGN;
+    const hipError_t err =
+        ep::launch_dispatch(*s, x, topk_idx, expert_slot, recv_x, recv_scales, recv_src_idx,
+                            status, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+int ep_combine(const ep_shape *s, const uint16_t *expert_out, const int64_t *topk_idx,
+               const float *topk_weights, const int32_t *expert_slot, uint16_t *combined_x,
+               uint32_t *status, void *stream)
+{
+    const int rc = check_shape(s);
+    if (rc != EP_OK)
+        return rc;
+    if (s->num_tokens == 0)
+        return EP_OK;
+    if (!expert_out || !topk_idx || !topk_weights || !expert_slot || !combined_x)
+        return EP_ERR_NULL;
+    if (!aligned(expert_out, 16) || !aligned(combined_x, 16) || !aligned(topk_idx, 8) ||
+        !aligned(topk_weights, 4) || !aligned(expert_slot, 4) || !aligned(status, 4))
+        return EP_ERR_ALIGN;
+    const hipError_t err =
+        ep::launch_combine(*s, expert_out, topk_idx, topk_weights, expert_slot, combined_x, status,
+                           static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+} // extern "C"

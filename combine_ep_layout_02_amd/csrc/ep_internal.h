@@ -1,0 +1,46 @@
+// ep_internal.h -- launchers shared between the C-ABI host code and the
+// kernel translation units of libep_mi355x.so.  Host code validates every
+// argument before it calls a launcher; launchers only size grids and enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ep.h"
+
+namespace ep {
+
+// ---- dispatch layout ---------------------------------------------------
+// The layout splits tokens into blocks of `tokens_per_block` (64, 128 or 256,
+// the largest whose LDS footprint fits) and runs two kernels: a per-block
+// histogram (skipped when one block covers every token) and a pass that adds
+// the histograms of earlier blocks to each block's local ranking.
+struct LayoutPlan {
+    int tokens_per_block;   // T
+    int num_blocks;         // B = ceil(N / T), at least 1
+    int hist_stride;        // ints per histogram row: round_up(E + R, 4)
+    size_t lds_bytes;       // dynamic LDS of the assign kernel
+    size_t workspace_bytes; // B * hist_stride * 4 when B > 1, else 0
+};
+
+// Returns false when no tokens_per_block fits the LDS budget.
+bool plan_layout(const ep_shape &s, LayoutPlan *plan);
+
+hipError_t launch_layout(const ep_shape &s, const LayoutPlan &plan, const int64_t *topk_idx,
+                         int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+                         uint8_t *is_token_in_rank, int32_t *expert_slot, int32_t *rank_slot,
+                         int32_t *expert_offset, int32_t *workspace, uint32_t *status,
+                         hipStream_t stream);
+
+// ---- dispatch pack -------------------------------------------------------
+hipError_t launch_dispatch(const ep_shape &s, const uint16_t *x, const int64_t *topk_idx,
+                           const int32_t *expert_slot, void *recv_x, float *recv_scales,
+                           int32_t *recv_src_idx, uint32_t *status, hipStream_t stream);
+
+// ---- combine ---------------------------------------------------------------
+hipError_t launch_combine(const ep_shape &s, const uint16_t *expert_out, const int64_t *topk_idx,
+                          const float *topk_weights, const int32_t *expert_slot,
+                          uint16_t *combined_x, uint32_t *status, hipStream_t stream);
+
+} // namespace ep

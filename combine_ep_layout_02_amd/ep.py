@@ -1,0 +1,237 @@
+"""Thin ctypes binding of libep_mi355x.so (declared in include/ep.h).
+
+Same entry points as the C ABI: ``ep_query_sizes``, ``ep_layout``,
+``ep_dispatch``, ``ep_combine``, ``ep_strerror`` (plus ``ep_probe_e4m3fn``
+from include/ep_probe.h).  Functions take torch tensors that already live on
+the GPU, check dtype / device / contiguity, and pass ``data_ptr()`` and the
+current HIP stream to the library.  Every step of the path runs in the HIP
+kernels; this module only marshals arguments and allocates buffers with torch
+on request.  There is no fallback: without the built library every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libep_mi355x.so")
+
+EP_OK = 0
+EP_ERR_NULL = 1
+EP_ERR_SHAPE = 2
+EP_ERR_CAPACITY = 3
+EP_ERR_ALIGN = 4
+EP_ERR_UNSUPPORTED = 5
+EP_ERR_HIP = 6
+EP_ERR_WORKSPACE = 7
+EP_STATUS_BAD_EXPERT_ID = 1
+EP_STATUS_BAD_SLOT = 2
+
+SHAPE_FIELDS = ("num_tokens", "hidden", "num_topk", "num_experts", "num_ranks",
+                "num_max_dispatch_tokens_per_rank", "expert_capacity", "use_fp8")
+SIZE_FIELDS = ("recv_x", "recv_scales", "recv_src_idx", "expert_out", "combined_x",
+               "num_tokens_per_rank", "num_tokens_per_expert", "is_token_in_rank",
+               "expert_slot", "rank_slot", "expert_offset", "layout_workspace")
+EXPORTED = ("ep_query_sizes", "ep_layout", "ep_dispatch", "ep_combine", "ep_strerror",
+            "ep_probe_e4m3fn")
+
+
+class ep_shape(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int32) for f in SHAPE_FIELDS]
+
+
+class ep_sizes(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_size_t) for f in SIZE_FIELDS]
+
+
+class EpError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {ep_strerror(code)} (code {code})")
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError(f"{LIBRARY} is not built: run `python -m combine_ep_layout_02_amd.build`."
+                               " The GPU path has no fallback.")
+        L = ctypes.CDLL(LIBRARY)
+        vp, sz, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64
+        sp = ctypes.POINTER(ep_shape)
+        L.ep_query_sizes.argtypes = [sp, ctypes.POINTER(ep_sizes)]
+        L.ep_layout.argtypes = [sp] + [vp] * 8 + [sz, vp, vp]
+        L.ep_dispatch.argtypes = [sp] + [vp] * 8
+        L.ep_combine.argtypes = [sp] + [vp] * 7
+        L.ep_probe_e4m3fn.argtypes = [vp, vp, vp, i64, vp]
+        L.ep_strerror.argtypes = [ctypes.c_int]
+        L.ep_strerror.restype = ctypes.c_char_p
+        for name in ("ep_query_sizes", "ep_layout", "ep_dispatch", "ep_combine", "ep_probe_e4m3fn"):
+            getattr(L, name).restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def make_shape(num_tokens: int, hidden: int, num_topk: int, num_experts: int, num_ranks: int,
+               num_max_dispatch_tokens_per_rank: int, expert_capacity: int,
+               use_fp8: bool) -> ep_shape:
+    return ep_shape(int(num_tokens), int(hidden), int(num_topk), int(num_experts), int(num_ranks),
+                    int(num_max_dispatch_tokens_per_rank), int(expert_capacity), int(bool(use_fp8)))
+
+
+def shape_of(workload) -> ep_shape:
+    """ep_shape of a ``workloads.Workload``."""
+    w = workload
+    return make_shape(w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks,
+                      w.num_max_dispatch_tokens_per_rank, w.expert_capacity, w.use_fp8)
+
+
+def ep_strerror(code: int) -> str:
+    return lib().ep_strerror(int(code)).decode()
+
+
+def ep_query_sizes(shape: ep_shape) -> dict:
+    out = ep_sizes()
+    rc = lib().ep_query_sizes(ctypes.byref(shape), ctypes.byref(out))
+    if rc != EP_OK:
+        raise EpError(rc, "ep_query_sizes")
+    return {f: int(getattr(out, f)) for f in SIZE_FIELDS}
+
+
+def _stream(stream, ref: torch.Tensor):
+    if stream is None:
+        stream = torch.cuda.current_stream(ref.device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtypes, numel: Optional[int] = None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs at least {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_I64 = (torch.int64,)
+_I32 = (torch.int32,)
+_U8 = (torch.uint8, torch.bool)
+_F32 = (torch.float32,)
+_STATUS = (torch.int32, torch.uint32)
+_FP8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def ep_layout(shape: ep_shape, topk_idx: torch.Tensor, num_tokens_per_rank: torch.Tensor,
+              num_tokens_per_expert: torch.Tensor, is_token_in_rank: torch.Tensor,
+              expert_slot: torch.Tensor, rank_slot: torch.Tensor,
+              expert_offset: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+              status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Dispatch layout; see ``ep_layout`` in include/ep.h."""
+    N, K, E, R = shape.num_tokens, shape.num_topk, shape.num_experts, shape.num_ranks
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().ep_layout(
+        ctypes.byref(shape), _ptr(topk_idx, "topk_idx", _I64, N * K),
+        _ptr(num_tokens_per_rank, "num_tokens_per_rank", _I32, R),
+        _ptr(num_tokens_per_expert, "num_tokens_per_expert", _I32, E),
+        _ptr(is_token_in_rank, "is_token_in_rank", _U8, N * R),
+        _ptr(expert_slot, "expert_slot", _I32, N * K), _ptr(rank_slot, "rank_slot", _I32, N * R),
+        _ptr(expert_offset, "expert_offset", _I32, E + 1),
+        _ptr(workspace, "workspace", (torch.uint8, torch.int32)), ctypes.c_size_t(ws_bytes),
+        _ptr(status, "status", _STATUS, 1), _stream(stream, num_tokens_per_expert))
+    if rc != EP_OK:
+        raise EpError(rc, "ep_layout")
+
+
+def ep_dispatch(shape: ep_shape, x: torch.Tensor, topk_idx: torch.Tensor, expert_slot: torch.Tensor,
+                recv_x: torch.Tensor, recv_scales: Optional[torch.Tensor],
+                recv_src_idx: torch.Tensor, status: Optional[torch.Tensor] = None,
+                stream=None) -> None:
+    """Dispatch pack; see ``ep_dispatch`` in include/ep.h."""
+    N, H, K, E, S = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts, \
+        shape.expert_capacity
+    rows = E * S
+    rx_types = _FP8 if shape.use_fp8 else _BF16
+    rc = lib().ep_dispatch(
+        ctypes.byref(shape), _ptr(x, "x", _BF16, N * H), _ptr(topk_idx, "topk_idx", _I64, N * K),
+        _ptr(expert_slot, "expert_slot", _I32, N * K), _ptr(recv_x, "recv_x", rx_types, rows * H),
+        _ptr(recv_scales, "recv_scales", _F32, rows * (H // 128)) if shape.use_fp8 else None,
+        _ptr(recv_src_idx, "recv_src_idx", _I32, rows), _ptr(status, "status", _STATUS, 1),
+        _stream(stream, recv_x))
+    if rc != EP_OK:
+        raise EpError(rc, "ep_dispatch")
+
+
+def ep_combine(shape: ep_shape, expert_out: torch.Tensor, topk_idx: torch.Tensor,
+               topk_weights: torch.Tensor, expert_slot: torch.Tensor, combined_x: torch.Tensor,
+               status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Combine; see ``ep_combine`` in include/ep.h."""
+    N, H, K, E, S = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts, \
+        shape.expert_capacity
+    rc = lib().ep_combine(
+        ctypes.byref(shape), _ptr(expert_out, "expert_out", _BF16, E * S * H),
+        _ptr(topk_idx, "topk_idx", _I64, N * K), _ptr(topk_weights, "topk_weights", _F32, N * K),
+        _ptr(expert_slot, "expert_slot", _I32, N * K),
+        _ptr(combined_x, "combined_x", _BF16, N * H), _ptr(status, "status", _STATUS, 1),
+        _stream(stream, combined_x))
+    if rc != EP_OK:
+        raise EpError(rc, "ep_combine")
+
+
+def ep_probe_e4m3fn(values: torch.Tensor, out_hw: Optional[torch.Tensor],
+                    out_sw: Optional[torch.Tensor], stream=None) -> None:
+    """The pack's clamp + FP8 conversion over an array; see include/ep_probe.h."""
+    n = values.numel()
+    rc = lib().ep_probe_e4m3fn(_ptr(values, "values", _F32), _ptr(out_hw, "out_hw", _U8, n),
+                               _ptr(out_sw, "out_sw", _U8, n), ctypes.c_int64(n),
+                               _stream(stream, values))
+    if rc != EP_OK:
+        raise EpError(rc, "ep_probe_e4m3fn")
+
+
+def allocate(shape: ep_shape, device="cuda", parts=("layout", "dispatch", "combine")) -> dict:
+    """torch.empty buffers for the outputs of the requested parts of the path
+    ("layout", "dispatch", "combine", "expert_out"), sized as ep_query_sizes
+    says.  Contents are uninitialised except ``status`` (zero)."""
+    sz = ep_query_sizes(shape)
+    N, H, K, E, R, S = (shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts,
+                        shape.num_ranks, shape.expert_capacity)
+    dev = torch.device(device)
+    out = {"status": torch.zeros(1, dtype=torch.int32, device=dev)}
+    if "layout" in parts:
+        out.update({
+            "num_tokens_per_rank": torch.empty(R, dtype=torch.int32, device=dev),
+            "num_tokens_per_expert": torch.empty(E, dtype=torch.int32, device=dev),
+            "is_token_in_rank": torch.empty((N, R), dtype=torch.uint8, device=dev),
+            "expert_slot": torch.empty((N, K), dtype=torch.int32, device=dev),
+            "rank_slot": torch.empty((N, R), dtype=torch.int32, device=dev),
+            "expert_offset": torch.empty(E + 1, dtype=torch.int32, device=dev),
+            "workspace": (torch.empty(sz["layout_workspace"], dtype=torch.uint8, device=dev)
+                          if sz["layout_workspace"] else None),
+        })
+    if "dispatch" in parts:
+        out.update({
+            "recv_x": torch.empty((E, S, H), dtype=torch.uint8 if shape.use_fp8 else torch.int16,
+                                  device=dev),
+            "recv_scales": (torch.empty((E, S, H // 128), dtype=torch.float32, device=dev)
+                            if shape.use_fp8 else None),
+            "recv_src_idx": torch.empty((E, S), dtype=torch.int32, device=dev),
+        })
+    if "combine" in parts:
+        out["combined_x"] = torch.empty((N, H), dtype=torch.int16, device=dev)
+    if "expert_out" in parts:
+        out["expert_out"] = torch.empty((E, S, H), dtype=torch.int16, device=dev)
+    return out

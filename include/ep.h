@@ -1,0 +1,190 @@
+/*
+ * ep.h -- C ABI of the MI355X (gfx950) MoE expert-parallel dispatch layout,
+ * dispatch pack and combine library (libep_mi355x.so).
+ *
+ * The operations and their arguments follow DeepSeek's DeepEP as described on
+ * these pages:
+ *   [V1]  "DeepEP V1 Legacy guide" (zskr.cn): §5.1 (get_dispatch_layout,
+ *         dispatch and combine of the normal kernels), §5.2(1) (the layout's
+ *         outputs), §5.2(6) (FP8 tokens with one float scale per 128 channels;
+ *         BF16 weighted reduction), §6.1 and §6.3 (low-latency dispatch:
+ *         num_max_dispatch_tokens_per_rank, experts split evenly over ranks,
+ *         receive data [local experts, M * ranks, hidden], -1 in topk_idx is
+ *         legal), §8.2 (fixed-size buffers at maximum capacity);
+ *   [ASC] "DeepEP Ascend Deep Dive" (kongchang.com): "Two Transfers: Dispatch
+ *         and Combine" (one copy per destination card; weighted sum at the
+ *         origin), "Dispatch's Three Phases and FP8 Compression" (counts per
+ *         expert and per card; the receive-source map);
+ *   [L14] "Lesson 14: DeepSeek DeepEP" (hpc.payai.win): §3 (low-latency call
+ *         sequence: x [tokens, hidden] bf16, topk_idx [tokens, topk] global
+ *         expert ids, receive data plus a count per local expert, combine
+ *         with topk_weights and the handle).
+ *
+ * One GPU plays every logical EP rank: rank r owns experts [r*L, (r+1)*L),
+ * L = E / R, and its receive buffer is the slice recv_x[r*L : (r+1)*L] of one
+ * [E, S, H] buffer in this GPU's HBM; its per-expert counts are the slice
+ * num_tokens_per_expert[r*L : (r+1)*L].
+ *
+ * Conventions of every entry point:
+ *  - Pointers are DEVICE pointers unless the comment says "host".  The caller
+ *    allocates and frees every buffer; each must stay valid until the stream
+ *    work completes.  The library never allocates, never synchronises the
+ *    host and keeps no mutable global state, so calls are reentrant and may be
+ *    captured into a HIP graph.
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *    null stream).  Entry points return EP_OK once the work is enqueued.
+ *  - Static errors (bad shape, capacity, null or misaligned pointer, too small
+ *    a workspace) are found on the host BEFORE anything is enqueued, and the
+ *    call returns their code.  A failed launch returns EP_ERR_HIP.
+ *  - Data-dependent problems are reported through the optional device word
+ *    `status` (nullable) by atomic OR of EP_STATUS_* bits; the library never
+ *    clears it.  An expert id >= E or < -1 is treated like -1 (masked) and
+ *    sets EP_STATUS_BAD_EXPERT_ID; an expert_slot outside [0, S) for a routed
+ *    entry is skipped and sets EP_STATUS_BAD_SLOT.
+ *  - Arrays are dense row-major.  Token rows (x, recv_x, expert_out,
+ *    combined_x) must be 16-byte aligned; every other array must be aligned to
+ *    its element size.
+ *  - Inputs must hold finite values; the FP8 bytes of a non-finite input are
+ *    unspecified (but every write stays inside its row).
+ */
+#ifndef EP_MI355X_H
+#define EP_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define EP_OK 0
+#define EP_ERR_NULL 1        /* a required pointer is NULL                            */
+#define EP_ERR_SHAPE 2       /* N < 0, H, K, E or R out of range, E % R != 0, FP8 with
+                                H % 128 != 0, BF16 with H % 8 != 0                    */
+#define EP_ERR_CAPACITY 3    /* N > M or S < M: the fixed upper bounds are never grown
+                                ([V1] §6.1 and §8.4; [L14] capacity discussion)       */
+#define EP_ERR_ALIGN 4       /* a pointer is not aligned as required                  */
+#define EP_ERR_UNSUPPORTED 5 /* a size this build does not support (see limits)       */
+#define EP_ERR_HIP 6         /* a HIP launch failed                                   */
+#define EP_ERR_WORKSPACE 7   /* workspace NULL or smaller than ep_query_sizes says    */
+
+/* Bits OR-ed into the optional device status word. */
+#define EP_STATUS_BAD_EXPERT_ID 1u
+#define EP_STATUS_BAD_SLOT 2u
+
+/* Limits of this build. */
+#define EP_MAX_EXPERTS 1024 /* E */
+#define EP_MAX_RANKS 64     /* R: a token's rank set is one 64-bit mask          */
+#define EP_MAX_TOPK 32      /* K */
+
+/* The problem's shape ([V1] §5.1 and §6.1; [L14] §3).  Passed by host pointer. */
+typedef struct {
+    int32_t num_tokens;  /* N >= 0: tokens on this (source) rank                      */
+    int32_t hidden;      /* H >= 8, H % 8 == 0; H % 128 == 0 when use_fp8           */
+    int32_t num_topk;    /* K in [1, EP_MAX_TOPK]: routing entries per token         */
+    int32_t num_experts; /* E in [1, EP_MAX_EXPERTS]                                  */
+    int32_t num_ranks;   /* R in [1, EP_MAX_RANKS], E % R == 0: logical EP ranks      */
+    int32_t num_max_dispatch_tokens_per_rank; /* M >= max(N, 1): fixed token bound   */
+    int32_t expert_capacity; /* S >= M: rows per expert receive buffer (the pages'
+                                low-latency shape uses S = R * M)                    */
+    int32_t use_fp8;     /* 0: BF16 rows; 1: E4M3FN rows + fp32 scale per 128 ch     */
+} ep_shape;
+
+/* Bytes of every buffer for a shape (0 for a buffer the shape does not use). */
+typedef struct {
+    size_t recv_x;                /* E*S*H (FP8) or E*S*H*2 (BF16)                    */
+    size_t recv_scales;           /* E*S*(H/128)*4 (FP8), else 0                      */
+    size_t recv_src_idx;          /* E*S*4                                            */
+    size_t expert_out;            /* E*S*H*2: bf16 expert outputs read by combine     */
+    size_t combined_x;            /* N*H*2                                            */
+    size_t num_tokens_per_rank;   /* R*4                                              */
+    size_t num_tokens_per_expert; /* E*4                                              */
+    size_t is_token_in_rank;      /* N*R                                              */
+    size_t expert_slot;           /* N*K*4                                            */
+    size_t rank_slot;             /* N*R*4                                            */
+    size_t expert_offset;         /* (E+1)*4                                          */
+    size_t layout_workspace;      /* scratch for ep_layout (0: none needed)           */
+} ep_sizes;
+
+/* Host only.  Fills `out` (host) with the byte size of every buffer for
+ * `shape` (host).  Returns EP_OK, EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_CAPACITY or
+ * EP_ERR_UNSUPPORTED. */
+int ep_query_sizes(const ep_shape *shape, ep_sizes *out);
+
+/* Dispatch layout ([V1] §5.2(1): tokens per rank, tokens per expert and the
+ * is_token_in_rank mask computed from topk_idx before any data moves; [ASC]
+ * phase 2: count per expert and per destination card; [ASC] "Two Transfers":
+ * a card receives a token once however many of its experts live there).
+ *
+ * In:  topk_idx [N, K] int64, global expert ids, -1 = no expert ([V1] §6.3).
+ * Out (all written in full, no pre-zeroing needed):
+ *   num_tokens_per_expert [E] int32  valid entries per expert (with multiplicity);
+ *   num_tokens_per_rank   [R] int32  tokens with >= 1 valid entry on rank r;
+ *   is_token_in_rank   [N, R] uint8  1 iff token t has a valid entry on rank r;
+ *   expert_slot        [N, K] int32  receive row of entry (t, k) in its expert's
+ *       buffer: the number of entries (t', k') before (t, k) in (token, k)
+ *       order with the same expert; -1 for masked entries;
+ *   rank_slot          [N, R] int32  the number of tokens t' < t in rank r's set,
+ *       -1 where token t is not in the set (each token appears at most once per
+ *       rank; this is the one row per (token, rank) a link would carry);
+ *   expert_offset      [E+1]  int32  exclusive prefix of num_tokens_per_expert,
+ *       expert_offset[E] = number of valid entries.  Nullable.
+ * expert_slot is the handle that ep_dispatch and ep_combine take ([V1] §5.2(4):
+ * the handle holds the routing metadata and can be reused while the routing is
+ * unchanged).
+ * workspace: device scratch of at least ep_sizes.layout_workspace bytes,
+ *   16-byte aligned, owned by the caller, contents irrelevant on entry and
+ *   meaningless after; NULL allowed when that size is 0.  Calls sharing one
+ *   workspace must be ordered on one stream.
+ * status: nullable device word (see conventions). */
+int ep_layout(const ep_shape *shape, const int64_t *topk_idx, int32_t *num_tokens_per_rank,
+              int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank, int32_t *expert_slot,
+              int32_t *rank_slot, int32_t *expert_offset, void *workspace, size_t workspace_bytes,
+              uint32_t *status, void *stream);
+
+/* Dispatch pack into the fixed-shape per-expert receive buffers ([L14] §3 and
+ * [V1] §6.3: data [local experts, M * ranks, hidden] with a count per local
+ * expert; [V1] §5.2(6): FP8 E4M3FN with one fp32 scale per 128 channels;
+ * [ASC] "Dispatch's Three Phases and FP8 Compression": amax, ratio, multiply,
+ * convert; the scale travels with the token).
+ *
+ * In:  x [N, H] bf16 bits; topk_idx [N, K]; expert_slot [N, K] from ep_layout.
+ * Out: recv_x [E, S, H]: row expert_slot[t,k] of expert topk_idx[t,k] receives
+ *        token t (BF16: a bit copy; FP8: per 128-channel block b, with
+ *        a = max|x|, a' = max(a, 1e-4), inv = RN(448 / a'):
+ *        q = E4M3FN_RNE(clamp(RN(x * inv), -448, 448)));
+ *      recv_scales [E, S, H/128] fp32: scale = RN(a' / 448) per block (FP8 only;
+ *        NULL when use_fp8 == 0);
+ *      recv_src_idx [E, S] int32: the source token t of each written row.
+ * Each token is read and quantised once and written once per valid entry.
+ * Rows at or beyond num_tokens_per_expert[e] are never written. */
+int ep_dispatch(const ep_shape *shape, const uint16_t *x, const int64_t *topk_idx,
+                const int32_t *expert_slot, void *recv_x, float *recv_scales,
+                int32_t *recv_src_idx, uint32_t *status, void *stream);
+
+/* Combine: top-k weighted gather-reduce back into token order ([ASC] "Two
+ * Transfers" and "Combine: More Output, Same Cost": outputs return to the
+ * origin and are summed with the router weights; [V1] §5.2(6): BF16 in and
+ * out; [L14] §3: combine takes expert_out, topk_idx, topk_weights and the
+ * handle).
+ *
+ * In:  expert_out [E, S, H] bf16 bits (rows < count are read); topk_idx
+ *      [N, K]; topk_weights [N, K] fp32; expert_slot [N, K] from ep_layout.
+ * Out: combined_x [N, H] bf16 bits:
+ *        acc = +0; for k = 0..K-1 with a valid expert e:
+ *            acc = fmaf(topk_weights[t,k], float(expert_out[e][slot][c]), acc);
+ *        combined_x[t,c] = bf16 round-to-nearest-even(acc).
+ *      A token whose entries are all masked gets +0. */
+int ep_combine(const ep_shape *shape, const uint16_t *expert_out, const int64_t *topk_idx,
+               const float *topk_weights, const int32_t *expert_slot, uint16_t *combined_x,
+               uint32_t *status, void *stream);
+
+/* Host only.  A static string naming a return code. */
+const char *ep_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_MI355X_H */

@@ -1,0 +1,320 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Bar: layout outputs, FP8 bytes, fp32 scales, BF16 rows and recv_src_idx are
+bit-exact; the combine is within 1 bf16 ulp or 8e-3 relative of the oracle
+(and is expected to be bit-identical, since both sides run the same k-ordered
+fp32 FMA chain; that is asserted separately).  Outputs start poisoned, so an
+element the kernels fail to write is caught, and receive rows past each
+expert's count must still hold the poison afterwards.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pins
+from cases import small_cases
+from combine_ep_layout_02_amd import ep
+from combine_ep_layout_02_amd import workloads as W
+from gpu_helpers import (POISON_SCALE_BITS, POISON_SRC, POISON_X8, POISON_X16, DispatchRun,
+                         LayoutRun, dev, gather_rows, place_expert_rows, run_combine, say,
+                         unwritten_rows_intact, written_rows)
+
+pytestmark = pytest.mark.gpu
+
+LAYOUT_KEYS = ("num_tokens_per_rank", "num_tokens_per_expert", "is_token_in_rank", "expert_slot",
+               "rank_slot", "expert_offset")
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.get()
+
+
+def first_diff(a, b):
+    d = np.argwhere(np.asarray(a) != np.asarray(b))
+    return None if d.size == 0 else (tuple(d[0]), np.asarray(a)[tuple(d[0])], np.asarray(b)[tuple(d[0])])
+
+
+def check_layout(o, shape, topk_idx, name):
+    say(f"ep_layout {name} N={shape.num_tokens} K={shape.num_topk} E={shape.num_experts} R={shape.num_ranks}")
+    run = LayoutRun(shape, topk_idx)
+    got = run.numpy()
+    want = o.layout(topk_idx, shape.num_experts, shape.num_ranks)
+    for key in LAYOUT_KEYS:
+        assert np.array_equal(got[key], want[key]), (name, key, first_diff(got[key], want[key]))
+    want_status = want["status"]  # oracle reports the bad-id bit the same way
+    assert got["status"] == want_status, (name, got["status"], want_status)
+    return run, want
+
+
+def check_dispatch(o, shape, inp, run, lay, name):
+    E, S, H = shape.num_experts, shape.expert_capacity, shape.hidden
+    say(f"ep_dispatch {name} fp8={shape.use_fp8} S={S} H={H}")
+    d = DispatchRun(shape, inp["x_bits"], run.topk_idx, run.expert_slot)
+    torch.cuda.synchronize()
+    counts = lay["num_tokens_per_expert"]
+    s_or = max(1, int(counts.max()) if counts.size else 1)
+    rx, rs, src, st = o.pack(inp["x_bits"], inp["topk_idx"], lay["expert_slot"], E, s_or,
+                             bool(shape.use_fp8))
+    rows_gpu = written_rows(counts, S)
+    rows_or = written_rows(counts, s_or)
+    got_x = gather_rows(d.recv_x, rows_gpu)
+    want_x = rx.reshape(E * s_or, H)[rows_or]
+    assert np.array_equal(got_x, want_x), (name, "recv_x", first_diff(got_x, want_x))
+    got_src = gather_rows(d.recv_src_idx, rows_gpu)
+    assert np.array_equal(got_src, src.reshape(-1)[rows_or]), (name, "recv_src_idx")
+    if shape.use_fp8:
+        got_sc = gather_rows(d.recv_scales.view(torch.int32), rows_gpu)
+        want_sc = rs.reshape(E * s_or, H // 128)[rows_or].view(np.int32)
+        assert np.array_equal(got_sc, want_sc), (name, "recv_scales", first_diff(got_sc, want_sc))
+        assert unwritten_rows_intact(d.recv_x, counts, POISON_X8)
+        assert unwritten_rows_intact(d.recv_scales.view(torch.int32), counts, POISON_SCALE_BITS)
+    else:
+        assert unwritten_rows_intact(d.recv_x, counts, int(POISON_X16))
+    assert unwritten_rows_intact(d.recv_src_idx, counts, POISON_SRC)
+    status = int(d.status.item()) & 0xFFFFFFFF
+    assert status == (st & ep.EP_STATUS_BAD_EXPERT_ID), (name, status, st)
+    return d, rx, s_or
+
+
+def check_combine(o, shape, inp, run, lay, y_dev, y_or, s_or, name, weights=None, token_sample=None):
+    """Combine on device rows y_dev [E, S, H] against the oracle on y_or
+    [E, s_or, H] holding the same rows."""
+    E = shape.num_experts
+    w = inp["topk_weights"] if weights is None else weights
+    say(f"ep_combine {name}")
+    got, st = run_combine(shape, y_dev, run.topk_idx, w, run.expert_slot)
+    idx, slot = inp["topk_idx"], lay["expert_slot"]
+    if token_sample is not None:
+        got, idx, slot, w = got[token_sample], idx[token_sample], slot[token_sample], w[token_sample]
+    want, _ = o.combine(y_or, idx, w, slot, E, s_or)
+    pins.assert_combine_close(got, pins.bf16_to_f64(want), f"{name} combine vs oracle")
+    ndiff = int((got != want).sum())
+    say(f"  combine elements not bit-identical to the oracle: {ndiff} of {got.size}")
+    assert ndiff == 0, f"{name}: within tolerance but {ndiff} elements not bit-identical"
+    return got
+
+
+def check_path(o, w, inp, name):
+    shape = ep.shape_of(w)
+    run, lay = check_layout(o, shape, inp["topk_idx"], name)
+    check_dispatch(o, shape, inp, run, lay, name)
+    E, S, H = w.num_experts, w.expert_capacity, w.hidden
+    y = place_expert_rows(inp["expert_rows"], inp["topk_idx"], lay["expert_slot"], E, S, H)
+    s_or = max(1, int(lay["num_tokens_per_expert"].max()))
+    y_or = pins.place_rows(inp["expert_rows"], inp["topk_idx"], lay["expert_slot"], E, s_or)
+    check_combine(o, shape, inp, run, lay, y, y_or, s_or, name)
+
+
+# ------------------------------------------------------------------ FP8 step
+
+def test_fp8_conversion_exhaustive(o):
+    """The pack's clamp + E4M3FN conversion (gfx950 instruction and the
+    bitwise formulation) against the oracle's encoder for every binary32 in
+    [0, 448], and sign symmetry for every negative counterpart; plus the
+    structured probe set (codes, midpoints, subnormals, both signs)."""
+    top = 0x43E00000
+    step = 1 << 26
+    for start in range(0, top + 1, step):
+        stop = min(start + step, top + 1)
+        say(f"ep_probe_e4m3fn bits [{start:#x}, {stop:#x})")
+        n = stop - start
+        n4 = -(-n // 4) * 4
+        bits = torch.arange(start, start + n4, dtype=torch.int64, device="cuda").clamp_(max=top)
+        v = bits.to(torch.int32).view(torch.float32)
+        hw = torch.empty(n4, dtype=torch.uint8, device="cuda")
+        sw = torch.empty(n4, dtype=torch.uint8, device="cuda")
+        ep.ep_probe_e4m3fn(v, hw, sw)
+        hw_neg = torch.empty_like(hw)
+        ep.ep_probe_e4m3fn(-v, hw_neg, None)
+        assert torch.equal(hw, sw), "hardware and bitwise conversions differ"
+        assert torch.equal(hw_neg, hw | 0x80), "negative inputs are not sign-symmetric"
+        want = o.e4m3fn_encode(v.cpu().numpy())
+        got = hw.cpu().numpy()
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, f"conversion differs from the oracle at {v.cpu().numpy()[bad[:4]]}"
+    vals = pins.fp8_probe_values()
+    vals = np.concatenate([vals, np.zeros((-vals.size) % 4, np.float32)])
+    d = dev(vals)
+    hw = torch.empty(vals.size, dtype=torch.uint8, device="cuda")
+    sw = torch.empty_like(hw)
+    ep.ep_probe_e4m3fn(d, hw, sw)
+    assert np.array_equal(hw.cpu().numpy(), o.e4m3fn_encode(vals))
+    assert np.array_equal(sw.cpu().numpy(), o.e4m3fn_encode(vals))
+
+
+# -------------------------------------------------------------- the workloads
+
+def test_layout_full_size_all_workloads(o):
+    for wid, w in W.WORKLOADS.items():
+        inp = W.make_inputs(w.scaled(w.num_tokens, 128))  # routing recipe at full N
+        check_layout(o, ep.shape_of(w), inp["topk_idx"], w.name)
+
+
+@pytest.mark.parametrize("case", range(5))
+def test_path_small(o, case):
+    w, inp = small_cases()[case]
+    check_path(o, w, inp, f"small {w.name} N={w.num_tokens} H={w.hidden}")
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 5])
+def test_path_full_size(o, wid):
+    w = W.WORKLOADS[wid]
+    inp = W.make_inputs(w, with_expert_rows=True)
+    check_path(o, w, inp, f"full {w.name}")
+
+
+def test_path_full_size_large_bf16(o):
+    """16,384 x 7,168 BF16, top-6 (the Ascend page's 1.4 GB pass): layout and
+    pack bit-exact; the combine with the identity expert (the receive buffer
+    itself as expert output) matches the oracle and reproduces x exactly."""
+    w = W.WORKLOADS[4]
+    inp = W.make_inputs(w)
+    shape = ep.shape_of(w)
+    run, lay = check_layout(o, shape, inp["topk_idx"], w.name)
+    d, rx, s_or = check_dispatch(o, shape, inp, run, lay, w.name)
+    rows = int((inp["topk_idx"] >= 0).sum())
+    assert rows * w.hidden * 2 == 1_409_286_144
+    got = check_combine(o, shape, inp, run, lay, d.recv_x, rx, s_or, w.name + " identity")
+    assert np.array_equal(pins.bf16_to_f64(got), pins.bf16_to_f64(inp["x_bits"]))
+
+
+# ------------------------------------------------------------------ edge cases
+
+def _edge(o, name, N, H, K, E, R, use_fp8, topk_idx=None, M=None, S=None, seed=0, mask=0.0):
+    rng = np.random.default_rng(seed)
+    if topk_idx is None:
+        topk_idx = np.argsort(rng.random((N, E)), axis=1)[:, :K].astype(np.int64) if K <= E else \
+            rng.integers(0, E, size=(N, K))
+        if mask:
+            topk_idx[rng.random((N, K)) < mask] = -1
+    M = max(N, 1) if M is None else M
+    S = M if S is None else S
+    w = W.Workload(0, name, N, H, K, E, R, M, S, use_fp8, "uniform")
+    x = W.bf16_bits(rng.standard_normal((N, H), dtype=np.float32))
+    wts = rng.random((N, K)).astype(np.float32)
+    P = int((topk_idx >= 0).sum())
+    rows = W.bf16_bits(rng.standard_normal((P, H), dtype=np.float32))
+    inp = {"x_bits": x, "topk_idx": topk_idx, "topk_weights": wts, "expert_rows": rows}
+    check_path(o, w, inp, name)
+
+
+EDGE = [
+    ("N=0", dict(N=0, H=256, K=4, E=16, R=4, use_fp8=True)),
+    ("N=1 K=1", dict(N=1, H=128, K=1, E=8, R=2, use_fp8=True)),
+    ("N=1 bf16 H=8", dict(N=1, H=8, K=2, E=4, R=2, use_fp8=False)),
+    ("all masked", dict(N=70, H=256, K=3, E=8, R=4, use_fp8=True,
+                        topk_idx=-np.ones((70, 3), np.int64))),
+    ("R=1", dict(N=300, H=128, K=4, E=16, R=1, use_fp8=True)),
+    ("R=E=64", dict(N=300, H=256, K=6, E=64, R=64, use_fp8=True, mask=0.2)),
+    ("ragged N=257 bf16 H=520", dict(N=257, H=520, K=5, E=32, R=8, use_fp8=False, mask=0.05)),
+    ("N=1000 fp8 H=1152", dict(N=1000, H=1152, K=8, E=256, R=8, use_fp8=True)),
+    ("N<M, S=R*M", dict(N=50, H=256, K=8, E=64, R=8, use_fp8=True, M=64, S=512)),
+    ("K=32 (128-token blocks)", dict(N=333, H=128, K=32, E=256, R=16, use_fp8=True)),
+    ("E=1024", dict(N=600, H=128, K=8, E=1024, R=64, use_fp8=True)),
+    ("K=32 E=1024 R=64", dict(N=300, H=128, K=32, E=1024, R=64, use_fp8=False, mask=0.1)),
+    ("K>E repeats", dict(N=200, H=128, K=12, E=8, R=4, use_fp8=True)),
+]
+
+
+@pytest.mark.parametrize("name,kw", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_shapes(o, name, kw):
+    _edge(o, name, **kw)
+
+
+def test_duplicate_experts_in_a_token(o):
+    rng = np.random.default_rng(4)
+    idx = rng.integers(-1, 6, size=(400, 5)).astype(np.int64)
+    idx[::3, 1] = idx[::3, 0]  # force repeats
+    _edge(o, "duplicates", N=400, H=256, K=5, E=6, R=3, use_fp8=True, topk_idx=idx)
+
+
+def test_bad_expert_ids_are_masked_and_reported(o):
+    rng = np.random.default_rng(5)
+    E, R, N, K = 32, 4, 500, 4
+    idx = np.argsort(rng.random((N, E)), axis=1)[:, :K].astype(np.int64)
+    bad = idx.copy()
+    pos = rng.permutation(N * K)[:97]
+    bad.reshape(-1)[pos] = rng.choice([-7, -2, E, E + 100, 1 << 40], size=97)
+    shape = ep.make_shape(N, 256, K, E, R, N, N, True)
+    run, lay = check_layout(o, shape, bad, "bad ids")
+    assert lay["status"] & ep.EP_STATUS_BAD_EXPERT_ID
+    masked = bad.copy()
+    masked[(masked < -1) | (masked >= E)] = -1
+    run2, lay2 = check_layout(o, shape, masked, "bad ids masked")
+    for key in LAYOUT_KEYS:
+        assert np.array_equal(run.numpy()[key], run2.numpy()[key])
+    x = W.bf16_bits(rng.standard_normal((N, 256), dtype=np.float32))
+    inp = {"x_bits": x, "topk_idx": bad}
+    check_dispatch(o, shape, inp, run, lay, "bad ids")
+
+
+def test_rank_down_emulation(o):
+    """A logical rank that drops out (DeepEP V1 Legacy guide §6.4, shrink
+    mode masks a rank's traffic): every entry routed to rank 3 is rewritten to
+    -1 on the host.  Rank 3 then receives nothing, its region stays
+    untouched, and the combine sums the surviving experts only."""
+    w = W.WORKLOADS[2]
+    inp = W.make_inputs(w)
+    L = w.num_experts // w.num_ranks
+    idx = inp["topk_idx"].copy()
+    idx[(idx // L) == 3] = -1
+    rng = np.random.default_rng(6)
+    inp = dict(inp, topk_idx=idx)
+    inp["expert_rows"] = W.bf16_bits(rng.standard_normal((int((idx >= 0).sum()), w.hidden),
+                                                         dtype=np.float32))
+    shape = ep.shape_of(w)
+    run, lay = check_layout(o, shape, idx, "rank 3 down")
+    assert lay["num_tokens_per_rank"][3] == 0
+    assert np.all(lay["num_tokens_per_expert"][3 * L:4 * L] == 0)
+    check_path(o, w, inp, "rank 3 down")
+
+
+def test_two_runs_are_bit_identical():
+    """Determinism: the whole path twice on the prefill workload gives the
+    same bytes (slots come from prefix sums, never from atomics)."""
+    w = W.WORKLOADS[3]
+    inp = W.make_inputs(w)
+    shape = ep.shape_of(w)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    y = torch.randn((w.num_experts, w.expert_capacity, w.hidden), dtype=torch.bfloat16,
+                    device="cuda", generator=g).view(torch.int16)
+    outs = []
+    for rep in range(2):
+        say(f"determinism run {rep}")
+        run = LayoutRun(shape, inp["topk_idx"])
+        d = DispatchRun(shape, inp["x_bits"], run.topk_idx, run.expert_slot)
+        got, _ = run_combine(shape, y, run.topk_idx, inp["topk_weights"], run.expert_slot)
+        r = run.numpy()
+        outs.append((r, d.recv_x.cpu(), d.recv_scales.cpu(), d.recv_src_idx.cpu(), got))
+        del d
+        torch.cuda.empty_cache()
+    a, b = outs
+    for key in LAYOUT_KEYS:
+        assert np.array_equal(a[0][key], b[0][key])
+    for i in (1, 2, 3):
+        assert torch.equal(a[i].view(torch.uint8) if a[i].dtype == torch.float32 else a[i],
+                           b[i].view(torch.uint8) if b[i].dtype == torch.float32 else b[i])
+    assert np.array_equal(a[4], b[4])
+
+
+def test_side_stream_and_handle_reuse(o):
+    """Work enqueued on a non-default stream; the layout's expert_slot is
+    reused as the handle for a second dispatch (DeepEP V1 Legacy guide
+    §5.2(4): the cached handle skips the layout while routing is unchanged)."""
+    w = W.WORKLOADS[2]
+    inp = W.make_inputs(w, with_expert_rows=True)
+    shape = ep.shape_of(w)
+    lay = o.layout(inp["topk_idx"], w.num_experts, w.num_ranks)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        say("ep_layout on a side stream")
+        run = LayoutRun(shape, inp["topk_idx"], stream=s)
+        d1 = DispatchRun(shape, inp["x_bits"], run.topk_idx, run.expert_slot, stream=s)
+        d2 = DispatchRun(shape, inp["x_bits"], run.topk_idx, run.expert_slot, stream=s)
+    s.synchronize()
+    for key in LAYOUT_KEYS:
+        assert np.array_equal(run.numpy()[key], lay[key])
+    assert torch.equal(d1.recv_x, d2.recv_x) and torch.equal(d1.recv_src_idx, d2.recv_src_idx)
