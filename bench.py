@@ -11,12 +11,12 @@ top-8, FP8; §2.2's low-latency shape) is timed the same way and reported in
 the same JSON line.
 
 Inputs are seeded synthetic data resident in HBM before timing starts.  Each
-timed step is bracketed by HIP events on the stream the kernels run on, with
-an event between phases; before each step an untimed 1 GiB write evicts the
-256 MB Infinity Cache, so the figures are cold-HBM figures ("warm" figures,
-without the eviction, are reported beside them).  Throughput counts the
-algorithmic bytes of the method (reads + writes it must do), not allocation,
-poisoning or the expert output generation.
+timed step is bracketed by two HIP events on the stream the kernels run on;
+before each step an untimed read of 1 GiB evicts the 256 MB Infinity Cache,
+so the figures are cold-HBM figures ("warm" figures, without the eviction,
+are reported beside them).  Throughput counts the algorithmic bytes of the
+method (reads + writes it must do), not allocation, poisoning or the expert
+output generation.
 
 Prints ONE JSON line.  With --gpus > 1 it exits: the path runs on one GPU.
 """
@@ -28,7 +28,6 @@ import json
 import os
 import re
 import statistics
-import subprocess
 import sys
 import time
 
@@ -86,7 +85,21 @@ def percentile(xs, q):
     return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
 
 
-def run_workload(wid, steps, warmup, scrub_bytes, say):
+def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
+    """Times the path on workload ``wid``.  Passes (each of ``steps``
+    iterations, an untimed cache eviction before each iteration):
+
+    cold    : events only before ep_layout and after ep_combine -> the value;
+    phases  : an event between phases as well (each event record delays the
+              next launch by a few us, so these phase times are upper bounds);
+    kernels : ``batch`` back-to-back launches of one entry point between two
+              events -> average launch duration per entry point (the roofline);
+    warm    : ``steps`` steps back to back, no eviction, two events overall.
+
+    The eviction reads a buffer larger than the 256 MB Infinity Cache, so the
+    cache holds clean unrelated lines and every input is in HBM (evicting by
+    writing would leave dirty lines whose write-back lands in the next
+    kernel)."""
     import torch
     from combine_ep_layout_02_amd import ep
     from combine_ep_layout_02_amd import workloads as W
@@ -106,73 +119,117 @@ def run_workload(wid, steps, warmup, scrub_bytes, say):
     # expert outputs: bf16 N(0, 1) in every row (rows past a count are never read)
     y = torch.randn((w.num_experts, w.expert_capacity, w.hidden), dtype=torch.bfloat16,
                     device=dev, generator=g).view(torch.int16)
-    scrub = torch.empty(scrub_bytes // 4, dtype=torch.int32, device=dev) if scrub_bytes else None
+    scrub = torch.ones(scrub_bytes // 4, dtype=torch.int32, device=dev) if scrub_bytes else None
+    scrub_out = torch.zeros((), dtype=torch.int64, device=dev)
     P = inp["num_valid"]
     nbytes = algorithmic_bytes(w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks, P,
                                w.use_fp8)
 
-    def step(ev):
-        """One pass of the path; ev[0..3] bracket layout, dispatch, combine."""
-        ev[0].record(stream)
+    def layout():
         ep.ep_layout(shape, topk_idx, buf["num_tokens_per_rank"], buf["num_tokens_per_expert"],
                      buf["is_token_in_rank"], buf["expert_slot"], buf["rank_slot"],
                      buf["expert_offset"], buf["workspace"], buf["status"], stream)
-        ev[1].record(stream)
+
+    def dispatch():
         ep.ep_dispatch(shape, x, topk_idx, buf["expert_slot"], buf["recv_x"], buf["recv_scales"],
                        buf["recv_src_idx"], buf["status"], stream)
-        ev[2].record(stream)
+
+    def combine():
         ep.ep_combine(shape, y, topk_idx, topk_weights, buf["expert_slot"], buf["combined_x"],
                       buf["status"], stream)
-        ev[3].record(stream)
+
+    def evict():
+        if scrub is not None:
+            torch.sum(scrub, dim=0, dtype=torch.int64, out=scrub_out)
+
+    def new_events(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
     say(f"workload {w.name}: {warmup} warmup steps")
     for _ in range(warmup):
-        step([torch.cuda.Event(enable_timing=True) for _ in range(4)])
+        layout()
+        dispatch()
+        combine()
+        evict()
     torch.cuda.synchronize()
     if int(buf["status"].item()) != 0:
         raise RuntimeError(f"device status {int(buf['status'].item())} during warmup")
 
-    def timed(n, with_scrub):
-        phases = {"layout": [], "dispatch": [], "combine": [], "total": []}
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(n):
-            if with_scrub:
-                scrub.fill_(i)
-            step(evs[i])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        for e4 in evs:
-            phases["layout"].append(e4[0].elapsed_time(e4[1]) * 1e3)
-            phases["dispatch"].append(e4[1].elapsed_time(e4[2]) * 1e3)
-            phases["combine"].append(e4[2].elapsed_time(e4[3]) * 1e3)
-            phases["total"].append(e4[0].elapsed_time(e4[3]) * 1e3)
-        return phases, wall
+    say(f"workload {w.name}: {steps} timed steps, cache evicted before each")
+    evs = [new_events(2) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        evict()
+        e[0].record(stream)
+        layout()
+        dispatch()
+        combine()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    wall_cold = time.perf_counter() - t0
+    cold = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
 
-    say(f"workload {w.name}: {steps} timed steps (cache scrubbed before each)")
-    cold, wall_cold = timed(steps, scrub is not None)
-    say(f"workload {w.name}: {steps} timed steps back to back (warm)")
-    warm, wall_warm = timed(steps, False)
-    # a plain copy of known size, for scaling the counter readings of a profile run
+    say(f"workload {w.name}: {steps} steps with an event between phases")
+    evs = [new_events(4) for _ in range(steps)]
+    for e in evs:
+        evict()
+        e[0].record(stream)
+        layout()
+        e[1].record(stream)
+        dispatch()
+        e[2].record(stream)
+        combine()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    phases = {"layout": [e[0].elapsed_time(e[1]) * 1e3 for e in evs],
+              "dispatch": [e[1].elapsed_time(e[2]) * 1e3 for e in evs],
+              "combine": [e[2].elapsed_time(e[3]) * 1e3 for e in evs]}
+
+    say(f"workload {w.name}: {batch} back-to-back launches per entry point, {steps} times")
+    kernels = {}
+    for name, fn in (("layout", layout), ("dispatch", dispatch), ("combine", combine)):
+        evs = [new_events(2) for _ in range(steps)]
+        for e in evs:
+            evict()
+            e[0].record(stream)
+            for _ in range(batch):
+                fn()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        kernels[name] = [e[0].elapsed_time(e[1]) * 1e3 / batch for e in evs]
+
+    say(f"workload {w.name}: {steps} steps back to back (warm)")
+    e = new_events(2)
+    e[0].record(stream)
+    for _ in range(steps):
+        layout()
+        dispatch()
+        combine()
+    e[1].record(stream)
+    torch.cuda.synchronize()
+    warm_us = e[0].elapsed_time(e[1]) * 1e3 / steps
+    # a plain copy of known size, for scaling counter readings of a profile run
     if scrub is not None:
         half = scrub.numel() // 2
         scrub[half:].copy_(scrub[:half])
     torch.cuda.synchronize()
+    if int(buf["status"].item()) != 0:
+        raise RuntimeError(f"device status {int(buf['status'].item())}")
 
-    def summarize(ph):
-        out = {}
-        for k, v in ph.items():
-            med = statistics.median(v)
-            out[k] = {"us_median": round(med, 2), "us_mean": round(statistics.fmean(v), 2),
-                      "us_p10": round(percentile(v, 10), 2), "us_p90": round(percentile(v, 90), 2),
-                      "gbps_median": round(nbytes[k] / (med * 1e-6) / 1e9, 1)}
-        return out
+    def stats(v, b):
+        med = statistics.median(v)
+        return {"us_median": round(med, 2), "us_mean": round(statistics.fmean(v), 2),
+                "us_p10": round(percentile(v, 10), 2), "us_p90": round(percentile(v, 90), 2),
+                "gbps_median": round(b / (med * 1e-6) / 1e9, 1)}
 
     return {
         "workload": w, "bytes": nbytes, "num_valid": P,
-        "cold": summarize(cold), "warm": summarize(warm),
-        "cold_raw": cold, "wall_cold_s": wall_cold, "wall_warm_s": wall_warm,
+        "cold": stats(cold, nbytes["total"]),
+        "phases": {k: stats(v, nbytes[k]) for k, v in phases.items()},
+        "kernels": {k: stats(v, nbytes[k]) for k, v in kernels.items()},
+        "warm_us_per_step": round(warm_us, 2),
+        "wall_cold_s": wall_cold,
         "inputs": inp,
     }
 
@@ -247,10 +304,9 @@ def main():
     decode = None if args.no_decode else run_workload(2, args.steps, args.warmup, scrub_bytes, say)
 
     w = prefill["workload"]
-    cold = prefill["cold"]
-    total_us = cold["total"]["us_mean"]
+    total_us = prefill["cold"]["us_mean"]
     value = prefill["bytes"]["total"] / (total_us * 1e-6) / 1e9
-    comb_us = cold["combine"]["us_mean"]
+    comb_us = prefill["kernels"]["combine"]["us_mean"]
     digest = kernel_source_digest(["combine.hip", "ep_device.h"])
     roofline = {
         "bound": "hbm",
@@ -262,21 +318,25 @@ def main():
         "traffic": committed_traffic(w.name, "combine", digest),
         "algorithmic_bytes_per_launch": prefill["bytes"]["combine"],
         "avg_launch_us": round(comb_us, 2),
+        "kernel_source_digest": digest,
     }
-    pack_us = cold["dispatch"]["us_mean"]
+    pack_us = prefill["kernels"]["dispatch"]["us_mean"]
     extra = {
-        "phases_us_cold": {k: v for k, v in cold.items()},
-        "phases_us_warm": prefill["warm"],
+        "step_us_cold": prefill["cold"],
+        "phases_us_with_events_between": prefill["phases"],
+        "kernel_avg_us_back_to_back": prefill["kernels"],
+        "step_us_warm": prefill["warm_us_per_step"],
         "bytes_per_step": prefill["bytes"],
         "dispatch_frac_of_peak": round(prefill["bytes"]["dispatch"] / (pack_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
         "gate_60pct_of_peak_us": round(prefill["bytes"]["total"] / (0.6 * PEAK_HBM_GBPS * 1e9) * 1e6, 1),
-        "wall_s_incl_scrub": round(prefill["wall_cold_s"], 4),
-        "wall_s_warm": round(prefill["wall_warm_s"], 4),
+        "frac_of_peak_whole_step": round(value / PEAK_HBM_GBPS, 4),
+        "wall_s_incl_eviction": round(prefill["wall_cold_s"], 4),
     }
     if decode is not None:
         extra["decode_128x7168"] = {
-            "phases_us_cold": decode["cold"], "phases_us_warm": decode["warm"],
-            "bytes_per_step": decode["bytes"],
+            "step_us_cold": decode["cold"], "phases_us_with_events_between": decode["phases"],
+            "kernel_avg_us_back_to_back": decode["kernels"],
+            "step_us_warm": decode["warm_us_per_step"], "bytes_per_step": decode["bytes"],
         }
     line = {
         "metric": "dispatch+combine achieved HBM GB/s (4096 tok x hidden 7168, FP8 dispatch, BF16 combine)",

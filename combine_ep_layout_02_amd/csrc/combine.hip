@@ -11,9 +11,12 @@
 //
 // Work item = one wave on one (token, 1024-channel chunk); each lane owns two
 // 8-channel units (16-byte loads, so every load instruction reads 1 KiB
-// contiguous of one expert row).  Rows are fetched eight entries at a time,
-// all loads issued before the first FMA, and the FMAs run in ascending k so
-// the fp32 sum is the same chain on every run (deterministic, no atomics).
+// contiguous of one expert row), marked non-temporal since every expert row
+// is read exactly once.  Entries are taken KB at a time: the KB
+// (expert id, slot, weight) triples arrive together (one vector load per lane,
+// broadcast with readlane), then every row load of the batch is issued before
+// the first FMA.  The FMAs run in ascending k, so the fp32 sum is the same
+// chain on every run (deterministic, no atomics).
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -23,7 +26,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kChunk = 1024; // channels per work item
-constexpr int kBatch = 8;    // rows in flight per lane pair of units
 
 __device__ __forceinline__ void fma_unit(float (&acc)[8], float w, const uint4 &v)
 {
@@ -43,6 +45,7 @@ __device__ __forceinline__ uint4 to_bf16_unit(const float (&acc)[8])
                       pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
 }
 
+template <int KB>
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     int32_t N, int32_t H, int32_t K, int32_t E, int32_t S, int32_t nchunks,
     const uint16_t *__restrict__ y, const int64_t *__restrict__ topk_idx,
@@ -50,16 +53,19 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     uint16_t *__restrict__ out, uint32_t *status)
 {
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t item = (int64_t)blockIdx.x * kWaves + wave;
-    if (item >= (int64_t)N * nchunks)
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t item = blockIdx.x * kWaves + wave; // host keeps N * nchunks < 2^31
+    if (item >= (uint32_t)N * (uint32_t)nchunks)
         return;
-    const int32_t t = (int32_t)(item / nchunks);
-    const int32_t chunk = (int32_t)(item - (int64_t)t * nchunks);
+    const uint32_t t = item / (uint32_t)nchunks;
+    const uint32_t chunk = item - t * (uint32_t)nchunks;
     const int32_t units = H / 8;
-    const int32_t u0 = chunk * (kChunk / 8) + lane;
+    const int32_t u0 = (int32_t)chunk * (kChunk / 8) + lane;
     const int32_t u1 = u0 + 64;
     const bool has0 = u0 < units, has1 = u1 < units;
+    // lanes past the row end load the row's last unit (in bounds, unused), so
+    // the loads need no per-lane branch
+    const int32_t l0 = min(u0, units - 1), l1 = min(u1, units - 1);
 
     float acc0[8], acc1[8];
 #pragma unroll
@@ -71,41 +77,22 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     const int64_t *idx_t = topk_idx + (size_t)t * K;
     const int32_t *slot_t = expert_slot + (size_t)t * K;
     const float *w_t = topk_weights + (size_t)t * K;
-    for (int k0 = 0; k0 < K; k0 += kBatch) {
-        uint4 v0[kBatch], v1[kBatch];
-        float wk[kBatch];
-        bool ok[kBatch];
+    for (int k0 = 0; k0 < K; k0 += KB) {
+        int64_t row[KB];
+        float wk[KB];
+        fetch_entries<KB>(idx_t, slot_t, w_t, k0, K, E, S, lane, row, wk, flags);
+        // every row load of the batch is issued before the first FMA; an
+        // entry without a row reads row 0 (in bounds) and is not accumulated
+        uint4 v0[KB], v1[KB];
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            const int k = k0 + b;
-            ok[b] = false;
-            wk[b] = 0.0f;
-            v0[b] = make_uint4(0, 0, 0, 0);
-            v1[b] = make_uint4(0, 0, 0, 0);
-            if (k < K) {
-                const int64_t id = idx_t[k];
-                if (id >= 0 && id < (int64_t)E) {
-                    const int32_t j = slot_t[k];
-                    if (j >= 0 && j < S) {
-                        ok[b] = true;
-                        wk[b] = w_t[k];
-                        const uint4 *row =
-                            reinterpret_cast<const uint4 *>(y + ((size_t)id * S + j) * H);
-                        if (has0)
-                            v0[b] = row[u0];
-                        if (has1)
-                            v1[b] = row[u1];
-                    } else {
-                        flags |= EP_STATUS_BAD_SLOT;
-                    }
-                } else if (id != -1) {
-                    flags |= EP_STATUS_BAD_EXPERT_ID;
-                }
-            }
+        for (int b = 0; b < KB; ++b) {
+            const uint4 *r = reinterpret_cast<const uint4 *>(y + (size_t)max(row[b], (int64_t)0) * H);
+            v0[b] = load_stream(r + l0);
+            v1[b] = load_stream(r + l1);
         }
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            if (ok[b]) {
+        for (int b = 0; b < KB; ++b) {
+            if (row[b] >= 0) {
                 fma_unit(acc0, wk[b], v0[b]);
                 fma_unit(acc1, wk[b], v1[b]);
             }
@@ -133,8 +120,17 @@ hipError_t launch_combine(const ep_shape &s, const uint16_t *expert_out, const i
     const int nchunks = (H + kChunk - 1) / kChunk;
     const int64_t items = (int64_t)N * nchunks;
     const dim3 grid((unsigned)((items + kWaves - 1) / kWaves));
-    hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, stream, N, H, K, E, S, nchunks,
-                       expert_out, topk_idx, topk_weights, expert_slot, combined_x, status);
+#define EP_COMBINE_ARGS N, H, K, E, S, nchunks, expert_out, topk_idx, topk_weights, expert_slot, \
+                        combined_x, status
+    if (K == 1)
+        hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(kThreads), 0, stream, EP_COMBINE_ARGS);
+    else if (K == 2)
+        hipLaunchKernelGGL(combine_kernel<2>, grid, dim3(kThreads), 0, stream, EP_COMBINE_ARGS);
+    else if (K <= 4)
+        hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(kThreads), 0, stream, EP_COMBINE_ARGS);
+    else
+        hipLaunchKernelGGL(combine_kernel<8>, grid, dim3(kThreads), 0, stream, EP_COMBINE_ARGS);
+#undef EP_COMBINE_ARGS
     return hipGetLastError();
 }
 

@@ -8,7 +8,8 @@
 // scale with the token).
 //
 // Work item = one wave on one (token, 1024-channel chunk).  The wave reads its
-// chunk of x once (16-byte loads), quantises it once in registers, then stores
+// chunk of x once (16-byte non-temporal loads: x is read exactly once),
+// quantises it once in registers, then stores
 // it to every valid destination row of the token (topk_idx / expert_slot are
 // wave-uniform scalar loads).  HBM traffic is therefore one read of x and one
 // write per (token, expert) entry, the minimum for this receive layout.
@@ -17,6 +18,10 @@
 // in, 16 bytes of FP8 out) per lane; the block amax is a 3-step xor-shuffle
 // reduction over the 8 lanes.  BF16 lane map: two 16-byte units per lane
 // (unit = 8 channels), so each store instruction covers 1 KiB contiguous.
+//
+// Destinations are taken KB entries at a time: the (expert id, slot) pairs
+// arrive together (one vector load per lane, broadcast with readlane), and
+// the stores of the batch follow back to back.
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -27,7 +32,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kChunk = 1024; // channels per work item
 
-template <bool kHwConvert>
+template <int KB>
 __global__ __launch_bounds__(kThreads) void pack_fp8_kernel(
     int32_t N, int32_t H, int32_t K, int32_t E, int32_t S, int32_t nchunks,
     const uint16_t *__restrict__ x, const int64_t *__restrict__ topk_idx,
@@ -35,12 +40,12 @@ __global__ __launch_bounds__(kThreads) void pack_fp8_kernel(
     float *__restrict__ recv_scales, int32_t *__restrict__ recv_src_idx, uint32_t *status)
 {
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t item = (int64_t)blockIdx.x * kWaves + wave;
-    if (item >= (int64_t)N * nchunks)
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t item = blockIdx.x * kWaves + wave; // host keeps N * nchunks < 2^31
+    if (item >= (uint32_t)N * (uint32_t)nchunks)
         return;
-    const int32_t t = (int32_t)(item / nchunks);
-    const int32_t chunk = (int32_t)(item - (int64_t)t * nchunks);
+    const uint32_t t = item / (uint32_t)nchunks;
+    const int32_t chunk = (int32_t)(item - t * (uint32_t)nchunks);
     const int32_t G = H / 128;
     const int32_t g = chunk * (kChunk / 128) + (lane >> 3);
     const bool active = g < G;
@@ -49,8 +54,8 @@ __global__ __launch_bounds__(kThreads) void pack_fp8_kernel(
     uint4 in0 = make_uint4(0, 0, 0, 0), in1 = make_uint4(0, 0, 0, 0);
     if (active) {
         const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)t * H + ch);
-        in0 = src[0];
-        in1 = src[1];
+        in0 = load_stream(src);
+        in1 = load_stream(src + 1);
     }
     const uint32_t w[8] = {in0.x, in0.y, in0.z, in0.w, in1.x, in1.y, in1.z, in1.w};
     float f[16];
@@ -74,46 +79,36 @@ __global__ __launch_bounds__(kThreads) void pack_fp8_kernel(
     for (int i = 0; i < 16; ++i)
         v[i] = clamp448(f[i] * inv);
     uint4 q;
-    if (kHwConvert) {
-        q.x = e4m3fn_x4_hw(v[0], v[1], v[2], v[3]);
-        q.y = e4m3fn_x4_hw(v[4], v[5], v[6], v[7]);
-        q.z = e4m3fn_x4_hw(v[8], v[9], v[10], v[11]);
-        q.w = e4m3fn_x4_hw(v[12], v[13], v[14], v[15]);
-    } else {
-        q.x = e4m3fn_x4_sw(v[0], v[1], v[2], v[3]);
-        q.y = e4m3fn_x4_sw(v[4], v[5], v[6], v[7]);
-        q.z = e4m3fn_x4_sw(v[8], v[9], v[10], v[11]);
-        q.w = e4m3fn_x4_sw(v[12], v[13], v[14], v[15]);
-    }
+    q.x = e4m3fn_x4_hw(v[0], v[1], v[2], v[3]);
+    q.y = e4m3fn_x4_hw(v[4], v[5], v[6], v[7]);
+    q.z = e4m3fn_x4_hw(v[8], v[9], v[10], v[11]);
+    q.w = e4m3fn_x4_hw(v[12], v[13], v[14], v[15]);
 
     uint32_t flags = 0;
     const int64_t *idx_t = topk_idx + (size_t)t * K;
     const int32_t *slot_t = expert_slot + (size_t)t * K;
-    for (int k = 0; k < K; ++k) {
-        const int64_t id = idx_t[k];
-        if (id < 0 || id >= (int64_t)E) {
-            if (id != -1)
-                flags |= EP_STATUS_BAD_EXPERT_ID;
-            continue;
+    for (int k0 = 0; k0 < K; k0 += KB) {
+        int64_t row[KB];
+        float unused[KB];
+        fetch_entries<KB>(idx_t, slot_t, nullptr, k0, K, E, S, lane, row, unused, flags);
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+            if (row[b] >= 0) {
+                if (active) {
+                    *reinterpret_cast<uint4 *>(recv_x + (size_t)row[b] * H + ch) = q;
+                    if ((lane & 7) == 0)
+                        recv_scales[(size_t)row[b] * G + g] = scale;
+                }
+                if (chunk == 0 && lane == 0)
+                    recv_src_idx[row[b]] = (int32_t)t;
+            }
         }
-        const int32_t j = slot_t[k];
-        if (j < 0 || j >= S) {
-            flags |= EP_STATUS_BAD_SLOT;
-            continue;
-        }
-        const size_t row = (size_t)id * S + j;
-        if (active) {
-            *reinterpret_cast<uint4 *>(recv_x + row * H + ch) = q;
-            if ((lane & 7) == 0)
-                recv_scales[row * G + g] = scale;
-        }
-        if (chunk == 0 && lane == 0)
-            recv_src_idx[row] = t;
     }
     if (flags && status && lane == 0 && chunk == 0)
         atomicOr(status, flags);
 }
 
+template <int KB>
 __global__ __launch_bounds__(kThreads) void pack_bf16_kernel(
     int32_t N, int32_t H, int32_t K, int32_t E, int32_t S, int32_t nchunks,
     const uint16_t *__restrict__ x, const int64_t *__restrict__ topk_idx,
@@ -121,45 +116,41 @@ __global__ __launch_bounds__(kThreads) void pack_bf16_kernel(
     int32_t *__restrict__ recv_src_idx, uint32_t *status)
 {
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t item = (int64_t)blockIdx.x * kWaves + wave;
-    if (item >= (int64_t)N * nchunks)
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t item = blockIdx.x * kWaves + wave; // host keeps N * nchunks < 2^31
+    if (item >= (uint32_t)N * (uint32_t)nchunks)
         return;
-    const int32_t t = (int32_t)(item / nchunks);
-    const int32_t chunk = (int32_t)(item - (int64_t)t * nchunks);
+    const uint32_t t = item / (uint32_t)nchunks;
+    const int32_t chunk = (int32_t)(item - t * (uint32_t)nchunks);
     const int32_t units = H / 8;
     const int32_t u0 = chunk * (kChunk / 8) + lane;
     const int32_t u1 = u0 + 64;
     const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)t * H);
     uint4 a0 = make_uint4(0, 0, 0, 0), a1 = make_uint4(0, 0, 0, 0);
     if (u0 < units)
-        a0 = src[u0];
+        a0 = load_stream(src + u0);
     if (u1 < units)
-        a1 = src[u1];
+        a1 = load_stream(src + u1);
 
     uint32_t flags = 0;
     const int64_t *idx_t = topk_idx + (size_t)t * K;
     const int32_t *slot_t = expert_slot + (size_t)t * K;
-    for (int k = 0; k < K; ++k) {
-        const int64_t id = idx_t[k];
-        if (id < 0 || id >= (int64_t)E) {
-            if (id != -1)
-                flags |= EP_STATUS_BAD_EXPERT_ID;
-            continue;
+    for (int k0 = 0; k0 < K; k0 += KB) {
+        int64_t row[KB];
+        float unused[KB];
+        fetch_entries<KB>(idx_t, slot_t, nullptr, k0, K, E, S, lane, row, unused, flags);
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+            if (row[b] >= 0) {
+                uint4 *dst = reinterpret_cast<uint4 *>(recv_x + (size_t)row[b] * H);
+                if (u0 < units)
+                    dst[u0] = a0;
+                if (u1 < units)
+                    dst[u1] = a1;
+                if (chunk == 0 && lane == 0)
+                    recv_src_idx[row[b]] = (int32_t)t;
+            }
         }
-        const int32_t j = slot_t[k];
-        if (j < 0 || j >= S) {
-            flags |= EP_STATUS_BAD_SLOT;
-            continue;
-        }
-        const size_t row = (size_t)id * S + j;
-        uint4 *dst = reinterpret_cast<uint4 *>(recv_x + row * H);
-        if (u0 < units)
-            dst[u0] = a0;
-        if (u1 < units)
-            dst[u1] = a1;
-        if (chunk == 0 && lane == 0)
-            recv_src_idx[row] = t;
     }
     if (flags && status && lane == 0 && chunk == 0)
         atomicOr(status, flags);
@@ -178,14 +169,35 @@ hipError_t launch_dispatch(const ep_shape &s, const uint16_t *x, const int64_t *
     const int nchunks = (H + kChunk - 1) / kChunk;
     const int64_t items = (int64_t)N * nchunks;
     const dim3 grid((unsigned)((items + kWaves - 1) / kWaves));
+    const int kb = K == 1 ? 1 : K == 2 ? 2 : K <= 4 ? 4 : 8;
     if (s.use_fp8) {
-        hipLaunchKernelGGL(pack_fp8_kernel<true>, grid, dim3(kThreads), 0, stream, N, H, K, E, S,
-                           nchunks, x, topk_idx, expert_slot, static_cast<uint8_t *>(recv_x),
-                           recv_scales, recv_src_idx, status);
+        uint8_t *rx = static_cast<uint8_t *>(recv_x);
+#define EP_PACK_FP8(KB)                                                                            \
+    hipLaunchKernelGGL(pack_fp8_kernel<KB>, grid, dim3(kThreads), 0, stream, N, H, K, E, S,        \
+                       nchunks, x, topk_idx, expert_slot, rx, recv_scales, recv_src_idx, status)
+        if (kb == 1)
+            EP_PACK_FP8(1);
+        else if (kb == 2)
+            EP_PACK_FP8(2);
+        else if (kb == 4)
+            EP_PACK_FP8(4);
+        else
+            EP_PACK_FP8(8);
+#undef EP_PACK_FP8
     } else {
-        hipLaunchKernelGGL(pack_bf16_kernel, grid, dim3(kThreads), 0, stream, N, H, K, E, S,
-                           nchunks, x, topk_idx, expert_slot, static_cast<uint16_t *>(recv_x),
-                           recv_src_idx, status);
+        uint16_t *rx = static_cast<uint16_t *>(recv_x);
+#define EP_PACK_BF16(KB)                                                                           \
+    hipLaunchKernelGGL(pack_bf16_kernel<KB>, grid, dim3(kThreads), 0, stream, N, H, K, E, S,       \
+                       nchunks, x, topk_idx, expert_slot, rx, recv_src_idx, status)
+        if (kb == 1)
+            EP_PACK_BF16(1);
+        else if (kb == 2)
+            EP_PACK_BF16(2);
+        else if (kb == 4)
+            EP_PACK_BF16(4);
+        else
+            EP_PACK_BF16(8);
+#undef EP_PACK_BF16
     }
     return hipGetLastError();
 }

@@ -32,6 +32,10 @@ int check_shape(const ep_shape *s)
         return EP_ERR_UNSUPPORTED;
     if (E * S > INT64_MAX / (H * 2))
         return EP_ERR_UNSUPPORTED;
+    // pack and combine number their work items (token, 1024-channel chunk)
+    // in 32 bits
+    if (N * ((H + 1023) / 1024) > INT32_MAX)
+        return EP_ERR_UNSUPPORTED;
     ep::LayoutPlan plan;
     if (!ep::plan_layout(*s, &plan))
         return EP_ERR_UNSUPPORTED;

@@ -8,15 +8,16 @@
 // number of entries before it with the same expert, so the result is unique
 // and the kernels are deterministic by construction (no global atomics).
 //
-// Tokens are split into blocks of T (64/128/256).  Two kernels:
+// Tokens are split into blocks of 256, one token per lane, the token's K
+// expert ids held in registers.  Two kernels:
 //   count : per-block histogram -> workspace[b][0..E+R) (expert entries, and
 //           tokens per rank, each token counted once per rank);
 //   assign: each block sums the histograms of the blocks before it (one
-//           coalesced pass, all loads in flight), ranks its own entries with
-//           per-64-token LDS bitmaps (bit = token within its 64-token group;
-//           an entry's in-block prefix is popcount of the lower bits of its
-//           expert's word plus the popcounts of the earlier groups' words),
-//           and the last block writes the totals and the offset scan.
+//           coalesced pass with all loads in flight), ranks its own entries
+//           with LDS bitmaps -- one 64-bit word per (wave, expert), bit = lane
+//           -- so an entry's in-block prefix is the popcount of the lower bits
+//           of its expert's word plus the popcounts of the earlier waves'
+//           words, and the last block writes the totals and the offset scan.
 // The count kernel is skipped when one block covers every token.
 //
 // A token may name one expert more than once.  Each repeat gets its own
@@ -28,56 +29,55 @@
 namespace ep {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr size_t kLdsBudget = 64 * 1024;
-
-__device__ __forceinline__ int32_t routed_expert(int64_t id, int32_t E, uint32_t &bad)
-{
-    if (id == -1)
-        return -1;
-    if (id < 0 || id >= (int64_t)E) {
-        bad = 1u;
-        return -1;
-    }
-    return (int32_t)id;
-}
+constexpr int kThreads = 256; // = tokens per block, one per lane
+constexpr int kGroups = kThreads / 64;
 
 __device__ __forceinline__ uint64_t bits_below(int bit) { return (1ull << bit) - 1ull; }
 
-// Per-block histogram: hist[b][e] = valid entries of expert e among block b's
-// tokens; hist[b][E + r] = tokens of block b with at least one entry on rank
-// r.  Padding columns up to `stride` are written as 0.
+// The token's K expert ids into e[0..KMAX): ids outside [0, E) become -1 (and
+// set `bad` unless they are -1); k >= K or a token past N gives -1.
+template <int KMAX>
+__device__ __forceinline__ void load_token(const int64_t *__restrict__ topk_idx, int64_t t,
+                                           int32_t N, int32_t K, int32_t E, int32_t (&e)[KMAX],
+                                           uint32_t &bad)
+{
+    int64_t v[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+        v[k] = (t < N && k < K) ? topk_idx[t * K + k] : -1;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        const bool ok = v[k] >= 0 && v[k] < (int64_t)E;
+        if (!ok && v[k] != -1)
+            bad = 1u;
+        e[k] = ok ? (int32_t)v[k] : -1;
+    }
+}
+
+template <int KMAX>
 __global__ __launch_bounds__(kThreads) void layout_count_kernel(
-    int32_t N, int32_t K, int32_t E, int32_t R, int32_t L, int32_t T, int32_t stride,
+    int32_t N, int32_t K, int32_t E, int32_t R, int32_t L, int32_t stride,
     const int64_t *__restrict__ topk_idx, int32_t *__restrict__ hist)
 {
     extern __shared__ int32_t s_cnt[]; // [E + R]
     const int tid = threadIdx.x;
+    int32_t e[KMAX];
+    uint32_t bad = 0;
+    load_token<KMAX>(topk_idx, (int64_t)blockIdx.x * kThreads + tid, N, K, E, e, bad);
     for (int i = tid; i < E + R; i += kThreads)
         s_cnt[i] = 0;
     __syncthreads();
-
-    const int64_t t0 = (int64_t)blockIdx.x * T;
-    const int nt = (int)min((int64_t)T, (int64_t)N - t0);
-    const int64_t *ids = topk_idx + t0 * K;
-    uint32_t bad = 0;
-    for (int j = tid; j < nt * K; j += kThreads) {
-        const int32_t e = routed_expert(ids[j], E, bad);
-        if (e >= 0)
-            atomicAdd(&s_cnt[e], 1);
+    uint64_t ranks = 0;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        if (e[k] >= 0) {
+            atomicAdd(&s_cnt[e[k]], 1);
+            ranks |= 1ull << (e[k] / L);
+        }
     }
-    for (int tl = tid; tl < nt; tl += kThreads) {
-        uint64_t ranks = 0;
-        for (int k = 0; k < K; ++k) {
-            const int32_t e = routed_expert(ids[tl * K + k], E, bad);
-            if (e >= 0)
-                ranks |= 1ull << (e / L);
-        }
-        while (ranks) {
-            const int r = __builtin_ctzll(ranks);
-            atomicAdd(&s_cnt[E + r], 1);
-            ranks &= ranks - 1ull;
-        }
+    while (ranks) {
+        atomicAdd(&s_cnt[E + __builtin_ctzll(ranks)], 1);
+        ranks &= ranks - 1ull;
     }
     __syncthreads();
     int32_t *row = hist + (size_t)blockIdx.x * stride;
@@ -85,78 +85,76 @@ __global__ __launch_bounds__(kThreads) void layout_count_kernel(
         row[i] = i < E + R ? s_cnt[i] : 0;
 }
 
-struct AssignLds {
-    uint64_t *bm;   // [G][E]  expert bitmaps of one layer
-    uint64_t *rbm;  // [G][R]  rank bitmaps
-    int32_t *ids;   // [T*K]   validated expert ids (-1 = masked)
-    int32_t *acc;   // [T*K]   in-block prefix of each entry
-    int32_t *base;  // [E+R]   counts of all earlier blocks
-    int32_t *blk;   // [E+R]   this block's counts, then the totals
-    int32_t *misc;  // [8]     0: layers, 1: bad id, 4..7: wave sums
-    uint8_t *occ;   // [T*K]   occurrence index of the entry's expert in its token
-};
-
-__device__ AssignLds carve(char *p, int G, int T, int K, int E, int R)
+__host__ __device__ inline size_t assign_lds_bytes(int E, int R)
 {
-    AssignLds s;
-    s.bm = (uint64_t *)p;
-    p += sizeof(uint64_t) * (size_t)G * E;
-    s.rbm = (uint64_t *)p;
-    p += sizeof(uint64_t) * (size_t)G * R;
-    s.ids = (int32_t *)p;
-    p += sizeof(int32_t) * (size_t)T * K;
-    s.acc = (int32_t *)p;
-    p += sizeof(int32_t) * (size_t)T * K;
-    s.base = (int32_t *)p;
-    p += sizeof(int32_t) * (size_t)(E + R);
-    s.blk = (int32_t *)p;
-    p += sizeof(int32_t) * (size_t)(E + R);
-    s.misc = (int32_t *)p;
-    p += sizeof(int32_t) * 8;
-    s.occ = (uint8_t *)p;
-    return s;
+    return sizeof(uint64_t) * (size_t)kGroups * (E + R) + sizeof(int32_t) * (size_t)(E + R) * 2 +
+           sizeof(int32_t) * 8;
 }
 
-__host__ __device__ inline size_t assign_lds_bytes(int T, int K, int E, int R)
+// Number of entries of `e` among the block's tokens before this lane's token
+// (same layer): lower bits of this wave's word plus the earlier waves' words.
+__device__ __forceinline__ int prefix_in_block(const uint64_t *words, int stride, int g, int lane)
 {
-    const int G = T / 64;
-    return sizeof(uint64_t) * (size_t)G * (E + R) + sizeof(int32_t) * (size_t)T * K * 2 +
-           sizeof(int32_t) * (size_t)(E + R) * 2 + sizeof(int32_t) * 8 + (size_t)T * K;
+    int cnt = __popcll(words[g * stride] & bits_below(lane));
+    for (int g2 = 0; g2 < g; ++g2)
+        cnt += __popcll(words[g2 * stride]);
+    return cnt;
 }
 
+template <int KMAX>
 __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
-    int32_t N, int32_t K, int32_t E, int32_t R, int32_t L, int32_t T, int32_t stride,
+    int32_t N, int32_t K, int32_t E, int32_t R, int32_t L, int32_t stride,
     const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ hist,
     int32_t *__restrict__ num_tokens_per_rank, int32_t *__restrict__ num_tokens_per_expert,
     uint8_t *__restrict__ is_token_in_rank, int32_t *__restrict__ expert_slot,
     int32_t *__restrict__ rank_slot, int32_t *__restrict__ expert_offset, uint32_t *status)
 {
     extern __shared__ __align__(16) char lds_raw[];
-    const int G = T / 64;
-    AssignLds s = carve(lds_raw, G, T, K, E, R);
-    const int tid = threadIdx.x;
-    const int b = blockIdx.x;
-    const int64_t t0 = (int64_t)b * T;
-    const int nt = (int)max((int64_t)0, min((int64_t)T, (int64_t)N - t0));
-    const int nent = nt * K;
-    const int64_t *ids = topk_idx + t0 * K;
+    uint64_t *s_bm = reinterpret_cast<uint64_t *>(lds_raw);      // [kGroups][E]
+    uint64_t *s_rbm = s_bm + (size_t)kGroups * E;                // [kGroups][R]
+    int32_t *s_base = reinterpret_cast<int32_t *>(s_rbm + (size_t)kGroups * R); // [E+R]
+    int32_t *s_tot = s_base + (E + R);                           // [E+R]
+    int32_t *s_misc = s_tot + (E + R);                           // [8]
 
-    // 1. zero the block's counters, stage validated ids
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int g = tid >> 6;
+    const int b = blockIdx.x;
+    const bool last_block = b == (int)gridDim.x - 1;
+    const int64_t t = (int64_t)b * kThreads + tid;
+    const bool live = t < N;
+
+    // 1. this token's ids (loads in flight while LDS is cleared)
+    int32_t e[KMAX];
+    uint32_t bad = 0;
+    load_token<KMAX>(topk_idx, t, N, K, E, e, bad);
+    for (int i = tid; i < kGroups * (E + R); i += kThreads)
+        s_bm[i] = 0ull; // s_bm and s_rbm are contiguous
     for (int i = tid; i < E + R; i += kThreads) {
-        s.base[i] = 0;
-        s.blk[i] = 0;
+        s_base[i] = 0;
+        s_tot[i] = 0;
     }
     if (tid < 8)
-        s.misc[tid] = tid == 0 ? 1 : 0;
-    uint32_t bad = 0;
-    for (int j = tid; j < nent; j += kThreads)
-        s.ids[j] = routed_expert(ids[j], E, bad);
-    __syncthreads();
-    if (bad)
-        atomicOr(&s.misc[1], 1);
+        s_misc[tid] = 0;
 
-    // 2. counts of all earlier blocks: the first b rows of the histogram are
-    //    one contiguous span; load it as int4 with eight loads in flight.
+    // 2. within-token occurrence index of each entry's expert, and rank set
+    int occ[KMAX];
+    int maxocc = 0;
+    uint64_t ranks = 0;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        occ[k] = 0;
+#pragma unroll
+        for (int k2 = 0; k2 < k; ++k2)
+            occ[k] += (e[k] >= 0 && e[k2] == e[k]) ? 1 : 0;
+        maxocc = max(maxocc, occ[k]);
+        if (e[k] >= 0)
+            ranks |= 1ull << (e[k] / L);
+    }
+    __syncthreads(); // LDS cleared
+
+    // 3. counts of all earlier blocks: the first b rows of the histogram are
+    //    one contiguous span; load it as int4 with eight loads in flight
     if (b > 0) {
         const int n4 = b * (stride / 4);
         const int4 *h4 = reinterpret_cast<const int4 *>(hist);
@@ -173,116 +171,105 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
                 if (i < n4) {
                     const int c = (i * 4) % stride;
                     if (c < E + R)
-                        atomicAdd(&s.base[c], v[u].x);
+                        atomicAdd(&s_base[c], v[u].x);
                     if (c + 1 < E + R)
-                        atomicAdd(&s.base[c + 1], v[u].y);
+                        atomicAdd(&s_base[c + 1], v[u].y);
                     if (c + 2 < E + R)
-                        atomicAdd(&s.base[c + 2], v[u].z);
+                        atomicAdd(&s_base[c + 2], v[u].z);
                     if (c + 3 < E + R)
-                        atomicAdd(&s.base[c + 3], v[u].w);
+                        atomicAdd(&s_base[c + 3], v[u].w);
                 }
             }
         }
     }
 
-    // 3. occurrence of each entry's expert among the token's earlier entries
-    for (int j = tid; j < nent; j += kThreads) {
-        const int32_t e = s.ids[j];
-        int occ = 0;
-        if (e >= 0) {
-            const int tl = j / K;
-            for (int k2 = tl * K; k2 < j; ++k2)
-                occ += s.ids[k2] == e;
-        }
-        s.occ[j] = (uint8_t)occ;
-        s.acc[j] = occ;
-        if (occ > 0)
-            atomicMax(&s.misc[0], occ + 1);
-    }
+    // 4. layer-0 bitmaps (first occurrences) and rank bitmaps
+    const uint64_t bit = 1ull << lane;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+        if (e[k] >= 0 && occ[k] == 0)
+            atomicOr((unsigned long long *)&s_bm[g * E + e[k]], (unsigned long long)bit);
+    for (uint64_t rs = ranks; rs; rs &= rs - 1ull)
+        atomicOr((unsigned long long *)&s_rbm[g * R + __builtin_ctzll(rs)], (unsigned long long)bit);
+    if (maxocc > 0)
+        atomicMax(&s_misc[0], maxocc);
+    if (bad)
+        atomicOr(&s_misc[1], 1);
     __syncthreads();
-    const int layers = s.misc[0];
 
-    // 4. rank entries layer by layer (one layer without repeated experts)
-    for (int layer = 0; layer < layers; ++layer) {
-        for (int i = tid; i < G * E; i += kThreads)
-            s.bm[i] = 0ull;
-        if (layer == 0)
-            for (int i = tid; i < G * R; i += kThreads)
-                s.rbm[i] = 0ull;
-        __syncthreads();
-        for (int j = tid; j < nent; j += kThreads) {
-            const int32_t e = s.ids[j];
-            if (e >= 0 && s.occ[j] == layer) {
-                const int tl = j / K;
-                const uint64_t bit = 1ull << (tl & 63);
-                atomicOr((unsigned long long *)&s.bm[(tl >> 6) * E + e], (unsigned long long)bit);
-                if (layer == 0)
-                    atomicOr((unsigned long long *)&s.rbm[(tl >> 6) * R + e / L],
-                             (unsigned long long)bit);
-            }
-        }
-        __syncthreads();
-        for (int j = tid; j < nent; j += kThreads) {
-            const int32_t e = s.ids[j];
-            if (e >= 0) {
-                const int tl = j / K;
-                const int g = tl >> 6;
-                int cnt = __popcll(s.bm[g * E + e] & bits_below(tl & 63));
-                for (int g2 = 0; g2 < g; ++g2)
-                    cnt += __popcll(s.bm[g2 * E + e]);
-                s.acc[j] += cnt;
-            }
-        }
+    int pre[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+        pre[k] = e[k] >= 0 ? prefix_in_block(&s_bm[e[k]], E, g, lane) : 0;
+    if (last_block) {
         for (int i = tid; i < E; i += kThreads) {
-            int tot = 0;
-            for (int g2 = 0; g2 < G; ++g2)
-                tot += __popcll(s.bm[g2 * E + i]);
-            s.blk[i] += tot;
+            int c = 0;
+            for (int g2 = 0; g2 < kGroups; ++g2)
+                c += __popcll(s_bm[g2 * E + i]);
+            s_tot[i] = c;
         }
+        for (int i = tid; i < R; i += kThreads) {
+            int c = 0;
+            for (int g2 = 0; g2 < kGroups; ++g2)
+                c += __popcll(s_rbm[g2 * R + i]);
+            s_tot[E + i] = c;
+        }
+    }
+
+    // 5. repeated experts: one more bitmap layer per occurrence index
+    const int layers = s_misc[0] + 1;
+    for (int layer = 1; layer < layers; ++layer) {
+        __syncthreads(); // every read of the previous layer is done
+        for (int i = tid; i < kGroups * E; i += kThreads)
+            s_bm[i] = 0ull;
         __syncthreads();
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (e[k] >= 0 && occ[k] == layer)
+                atomicOr((unsigned long long *)&s_bm[g * E + e[k]], (unsigned long long)bit);
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (e[k] >= 0)
+                pre[k] += prefix_in_block(&s_bm[e[k]], E, g, lane);
+        if (last_block) {
+            for (int i = tid; i < E; i += kThreads) {
+                int c = 0;
+                for (int g2 = 0; g2 < kGroups; ++g2)
+                    c += __popcll(s_bm[g2 * E + i]);
+                s_tot[i] += c;
+            }
+        }
     }
 
-    // 5. expert slots
-    int32_t *slot_out = expert_slot + t0 * K;
-    for (int j = tid; j < nent; j += kThreads) {
-        const int32_t e = s.ids[j];
-        slot_out[j] = e >= 0 ? s.base[e] + s.acc[j] : -1;
+    // 6. this token's outputs
+    if (live) {
+        int32_t *slot_out = expert_slot + t * K;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (k < K)
+                slot_out[k] = e[k] >= 0 ? s_base[e[k]] + pre[k] + occ[k] : -1;
+        uint8_t *mask_out = is_token_in_rank + t * R;
+        int32_t *rslot_out = rank_slot + t * R;
+        for (int r = 0; r < R; ++r) {
+            const bool in = (ranks >> r) & 1ull;
+            mask_out[r] = in ? 1 : 0;
+            rslot_out[r] = in ? s_base[E + r] + prefix_in_block(&s_rbm[r], R, g, lane) : -1;
+        }
     }
-
-    // 6. rank mask and rank slots, one (token, rank) pair per thread
-    uint8_t *mask_out = is_token_in_rank + t0 * R;
-    int32_t *rslot_out = rank_slot + t0 * R;
-    for (int q = tid; q < nt * R; q += kThreads) {
-        const int tl = q / R;
-        const int r = q - tl * R;
-        const int g = tl >> 6;
-        const uint64_t word = s.rbm[g * R + r];
-        const bool in = (word >> (tl & 63)) & 1ull;
-        int cnt = __popcll(word & bits_below(tl & 63));
-        for (int g2 = 0; g2 < g; ++g2)
-            cnt += __popcll(s.rbm[g2 * R + r]);
-        mask_out[q] = in ? 1 : 0;
-        rslot_out[q] = in ? s.base[E + r] + cnt : -1;
-    }
-    for (int i = tid; i < R; i += kThreads) {
-        int tot = 0;
-        for (int g2 = 0; g2 < G; ++g2)
-            tot += __popcll(s.rbm[g2 * R + i]);
-        s.blk[E + i] = tot;
-    }
-    if (tid == 0 && status && s.misc[1])
+    if (tid == 0 && status && s_misc[1])
         atomicOr(status, EP_STATUS_BAD_EXPERT_ID);
 
     // 7. the last block holds every count: write totals and the offset scan
-    if (b == (int)gridDim.x - 1) {
+    if (last_block) {
         __syncthreads();
         for (int i = tid; i < E + R; i += kThreads) {
-            const int tot = s.base[i] + s.blk[i];
+            const int tot = s_base[i] + s_tot[i];
             if (i < E)
                 num_tokens_per_expert[i] = tot;
             else
                 num_tokens_per_rank[i - E] = tot;
-            s.blk[i] = tot;
+            s_tot[i] = tot;
         }
         __syncthreads();
         if (expert_offset) {
@@ -291,9 +278,7 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
             int local = 0;
             for (int i = 0; i < per; ++i)
                 if (start + i < E)
-                    local += s.blk[start + i];
-            const int lane = tid & 63;
-            const int wave = tid >> 6;
+                    local += s_tot[start + i];
             int incl = local;
             for (int off = 1; off < 64; off <<= 1) {
                 const int up = __shfl_up(incl, off, 64);
@@ -301,16 +286,16 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
                     incl += up;
             }
             if (lane == 63)
-                s.misc[4 + wave] = incl;
+                s_misc[4 + g] = incl;
             __syncthreads();
             int woff = 0;
-            for (int w2 = 0; w2 < wave; ++w2)
-                woff += s.misc[4 + w2];
+            for (int g2 = 0; g2 < g; ++g2)
+                woff += s_misc[4 + g2];
             int run = woff + incl - local;
             for (int i = 0; i < per; ++i) {
                 if (start + i < E) {
                     expert_offset[start + i] = run;
-                    run += s.blk[start + i];
+                    run += s_tot[start + i];
                 }
             }
             if (tid == kThreads - 1)
@@ -323,20 +308,14 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
 
 bool plan_layout(const ep_shape &s, LayoutPlan *plan)
 {
-    const int N = s.num_tokens, K = s.num_topk, E = s.num_experts, R = s.num_ranks;
-    for (int T = 256; T >= 64; T /= 2) {
-        const size_t lds = assign_lds_bytes(T, K, E, R);
-        if (lds <= kLdsBudget) {
-            plan->tokens_per_block = T;
-            plan->num_blocks = N > 0 ? (N + T - 1) / T : 1;
-            plan->hist_stride = (E + R + 3) / 4 * 4;
-            plan->lds_bytes = lds;
-            plan->workspace_bytes =
-                plan->num_blocks > 1 ? sizeof(int32_t) * (size_t)plan->num_blocks * plan->hist_stride : 0;
-            return true;
-        }
-    }
-    return false;
+    const int N = s.num_tokens, E = s.num_experts, R = s.num_ranks;
+    plan->tokens_per_block = kThreads;
+    plan->num_blocks = N > 0 ? (N + kThreads - 1) / kThreads : 1;
+    plan->hist_stride = (E + R + 3) / 4 * 4;
+    plan->lds_bytes = assign_lds_bytes(E, R);
+    plan->workspace_bytes =
+        plan->num_blocks > 1 ? sizeof(int32_t) * (size_t)plan->num_blocks * plan->hist_stride : 0;
+    return plan->lds_bytes <= 64 * 1024;
 }
 
 hipError_t launch_layout(const ep_shape &s, const LayoutPlan &plan, const int64_t *topk_idx,
@@ -347,16 +326,23 @@ hipError_t launch_layout(const ep_shape &s, const LayoutPlan &plan, const int64_
 {
     const int N = s.num_tokens, K = s.num_topk, E = s.num_experts, R = s.num_ranks;
     const int L = E / R;
-    const int T = plan.tokens_per_block, B = plan.num_blocks, stride = plan.hist_stride;
-    if (B > 1) {
-        hipLaunchKernelGGL(layout_count_kernel, dim3(B), dim3(kThreads),
-                           sizeof(int32_t) * (size_t)(E + R), stream, N, K, E, R, L, T, stride,
-                           topk_idx, workspace);
-    }
-    hipLaunchKernelGGL(layout_assign_kernel, dim3(B), dim3(kThreads), plan.lds_bytes, stream, N, K,
-                       E, R, L, T, stride, topk_idx, workspace, num_tokens_per_rank,
-                       num_tokens_per_expert, is_token_in_rank, expert_slot, rank_slot,
-                       expert_offset, status);
+    const int B = plan.num_blocks, stride = plan.hist_stride;
+    const size_t count_lds = sizeof(int32_t) * (size_t)(E + R);
+#define EP_LAYOUT_LAUNCH(KMAX)                                                                     \
+    do {                                                                                           \
+        if (B > 1)                                                                                 \
+            hipLaunchKernelGGL(layout_count_kernel<KMAX>, dim3(B), dim3(kThreads), count_lds,      \
+                               stream, N, K, E, R, L, stride, topk_idx, workspace);                \
+        hipLaunchKernelGGL(layout_assign_kernel<KMAX>, dim3(B), dim3(kThreads), plan.lds_bytes,    \
+                           stream, N, K, E, R, L, stride, topk_idx, workspace,                     \
+                           num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank,           \
+                           expert_slot, rank_slot, expert_offset, status);                         \
+    } while (0)
+    if (K <= 8)
+        EP_LAYOUT_LAUNCH(8);
+    else
+        EP_LAYOUT_LAUNCH(EP_MAX_TOPK);
+#undef EP_LAYOUT_LAUNCH
     return hipGetLastError();
 }
 

@@ -94,14 +94,18 @@ class DispatchRun:
 
 
 def written_rows(counts: np.ndarray, S: int) -> np.ndarray:
-    """Flat row numbers e * S + j, j < counts[e], in expert order."""
-    return np.concatenate([e * S + np.arange(int(c), dtype=np.int64) for e, c in enumerate(counts)]
-                          + [np.zeros(0, np.int64)])
+    """Flat row numbers e * S + j for j < min(counts[e], S), in expert order
+    (an expert's entries past the capacity S are never written)."""
+    return np.concatenate([e * S + np.arange(min(int(c), S), dtype=np.int64)
+                           for e, c in enumerate(counts)] + [np.zeros(0, np.int64)])
 
 
 def gather_rows(t: torch.Tensor, rows: np.ndarray) -> np.ndarray:
     """Rows ``rows`` of a [E, S, ...] device tensor as a host array [P, ...]."""
-    flat = t.reshape(t.shape[0] * t.shape[1], *t.shape[2:])
+    nrows = t.shape[0] * t.shape[1]
+    if rows.size:
+        assert rows.min() >= 0 and rows.max() < nrows, "row index outside the buffer"
+    flat = t.reshape(nrows, *t.shape[2:])
     idx = torch.from_numpy(rows).cuda()
     return host(flat.index_select(0, idx))
 
@@ -120,13 +124,17 @@ def unwritten_rows_intact(t: torch.Tensor, counts: np.ndarray, poison: int) -> b
 def place_expert_rows(rows_bits: np.ndarray, topk_idx: np.ndarray, expert_slot: np.ndarray,
                       E: int, S: int, H: int) -> torch.Tensor:
     """A [E, S, H] bf16-bits device tensor (poisoned) holding one row per
-    valid (t, k) entry, in (t, k) order, at (expert, slot)."""
+    valid (t, k) entry, in (t, k) order, at (expert, slot); entries whose slot
+    is at or past the capacity S are dropped, as the kernels skip them."""
     y = torch.full((E * S, H), int(POISON_X16), dtype=torch.int16, device="cuda")
     flat_idx = topk_idx.reshape(-1)
+    flat_slot = expert_slot.reshape(-1)
     valid = flat_idx >= 0
-    where = (flat_idx[valid].astype(np.int64) * S + expert_slot.reshape(-1)[valid].astype(np.int64))
+    keep = flat_slot[valid] < S  # entries past the capacity have no row
+    where = flat_idx[valid][keep].astype(np.int64) * S + flat_slot[valid][keep].astype(np.int64)
     if where.size:
-        y.index_copy_(0, torch.from_numpy(where).cuda(), dev(rows_bits))
+        assert where.min() >= 0 and where.max() < E * S, "row index outside the buffer"
+        y.index_copy_(0, torch.from_numpy(where).cuda(), dev(rows_bits[keep]))
     return y.view(E, S, H)
 
 

@@ -111,13 +111,15 @@ def assert_combine_close(got_bits: np.ndarray, ref: np.ndarray, what: str = "com
 
 def place_rows(rows: np.ndarray, topk_idx: np.ndarray, expert_slot: np.ndarray, E: int, S: int,
                fill=0) -> np.ndarray:
-    """Scatter one row per valid (t, k) entry (in (t, k) order) to y[e][slot]."""
+    """Scatter one row per valid (t, k) entry (in (t, k) order) to y[e][slot];
+    entries whose slot is at or past the capacity S are dropped."""
     H = rows.shape[1]
     y = np.full((E, S, H), fill, dtype=rows.dtype)
     flat_idx = topk_idx.reshape(-1)
     flat_slot = expert_slot.reshape(-1)
     valid = flat_idx >= 0
-    y[flat_idx[valid], flat_slot[valid]] = rows
+    keep = flat_slot[valid] < S  # entries past the capacity have no row
+    y[flat_idx[valid][keep], flat_slot[valid][keep]] = rows[keep]
     return y
 
 
