@@ -17,8 +17,10 @@
 //           with LDS bitmaps -- one 64-bit word per (wave, expert), bit = lane
 //           -- so an entry's in-block prefix is the popcount of the lower bits
 //           of its expert's word plus the popcounts of the earlier waves'
-//           words, and the last block writes the totals and the offset scan.
-// The count kernel is skipped when one block covers every token.
+//           words.  One extra block sums every histogram row at the same time
+//           and writes the totals and the offset scan.
+// The count kernel is skipped when one block covers every token; that block
+// then counts its own totals.
 //
 // A token may name one expert more than once.  Each repeat gets its own
 // slot in k order: occurrence o of an expert within a token is ranked in
@@ -31,6 +33,7 @@ namespace {
 
 constexpr int kThreads = 256; // = tokens per block, one per lane
 constexpr int kGroups = kThreads / 64;
+constexpr int kHistBatch = 8; // int4 histogram loads in flight per thread
 
 __device__ __forceinline__ uint64_t bits_below(int bit) { return (1ull << bit) - 1ull; }
 
@@ -101,6 +104,93 @@ __device__ __forceinline__ int prefix_in_block(const uint64_t *words, int stride
     return cnt;
 }
 
+// Totals in s_tot[0..E+R) (LDS, complete) -> num_tokens_per_expert,
+// num_tokens_per_rank and the exclusive offset scan (expert_offset nullable).
+// Called by all kThreads threads of one block; uses s_misc[4..8).
+__device__ void write_totals_and_offsets(int E, int R, const int32_t *s_tot, int32_t *s_misc,
+                                         int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+                                         int32_t *expert_offset)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int g = tid >> 6;
+    for (int i = tid; i < E + R; i += kThreads) {
+        if (i < E)
+            num_tokens_per_expert[i] = s_tot[i];
+        else
+            num_tokens_per_rank[i - E] = s_tot[i];
+    }
+    if (!expert_offset)
+        return;
+    const int per = (E + kThreads - 1) / kThreads;
+    const int start = tid * per;
+    int local = 0;
+    for (int i = 0; i < per; ++i)
+        if (start + i < E)
+            local += s_tot[start + i];
+    int incl = local;
+    for (int off = 1; off < 64; off <<= 1) {
+        const int up = __shfl_up(incl, off, 64);
+        if (lane >= off)
+            incl += up;
+    }
+    if (lane == 63)
+        s_misc[4 + g] = incl;
+    __syncthreads();
+    int woff = 0;
+    for (int g2 = 0; g2 < g; ++g2)
+        woff += s_misc[4 + g2];
+    int run = woff + incl - local;
+    for (int i = 0; i < per; ++i) {
+        if (start + i < E) {
+            expert_offset[start + i] = run;
+            run += s_tot[start + i];
+        }
+    }
+    if (tid == kThreads - 1)
+        expert_offset[E] = woff + incl;
+}
+
+// The extra block of a multi-block layout: column sums of all B histogram
+// rows (int4 loads, kHistBatch in flight per thread), then totals and scan.
+__device__ void layout_totals(int B, int E, int R, int stride, const int32_t *__restrict__ hist,
+                              int32_t *s_tot, int32_t *s_misc, int32_t *num_tokens_per_rank,
+                              int32_t *num_tokens_per_expert, int32_t *expert_offset)
+{
+    const int tid = threadIdx.x;
+    for (int i = tid; i < E + R; i += kThreads)
+        s_tot[i] = 0;
+    __syncthreads();
+    const int n4 = B * (stride / 4);
+    const int4 *h4 = reinterpret_cast<const int4 *>(hist);
+    for (int i0 = tid; i0 < n4; i0 += kThreads * kHistBatch) {
+        int4 hv[kHistBatch];
+#pragma unroll
+        for (int u = 0; u < kHistBatch; ++u) {
+            const int i = i0 + u * kThreads;
+            hv[u] = i < n4 ? h4[i] : make_int4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kHistBatch; ++u) {
+            const int i = i0 + u * kThreads;
+            if (i < n4) {
+                const int c = (i * 4) % stride;
+                if (c < E + R)
+                    atomicAdd(&s_tot[c], hv[u].x);
+                if (c + 1 < E + R)
+                    atomicAdd(&s_tot[c + 1], hv[u].y);
+                if (c + 2 < E + R)
+                    atomicAdd(&s_tot[c + 2], hv[u].z);
+                if (c + 3 < E + R)
+                    atomicAdd(&s_tot[c + 3], hv[u].w);
+            }
+        }
+    }
+    __syncthreads();
+    write_totals_and_offsets(E, R, s_tot, s_misc, num_tokens_per_rank, num_tokens_per_expert,
+                             expert_offset);
+}
+
 template <int KMAX>
 __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
     int32_t N, int32_t K, int32_t E, int32_t R, int32_t L, int32_t stride,
@@ -120,14 +210,33 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
     const int lane = tid & 63;
     const int g = tid >> 6;
     const int b = blockIdx.x;
-    const bool last_block = b == (int)gridDim.x - 1;
+    const int num_token_blocks = hist ? (int)gridDim.x - 1 : 1;
+    if (b == num_token_blocks) {
+        // the extra block: totals are the column sums of every block's
+        // histogram; it writes them and the offset scan while the other
+        // blocks rank their tokens
+        layout_totals(num_token_blocks, E, R, stride, hist, s_tot, s_misc, num_tokens_per_rank,
+                      num_tokens_per_expert, expert_offset);
+        return;
+    }
+    // with a single token block there is no histogram: that block counts
+    const bool last_block = hist == nullptr;
     const int64_t t = (int64_t)b * kThreads + tid;
     const bool live = t < N;
 
-    // 1. this token's ids (loads in flight while LDS is cleared)
+    // 1. this token's ids and the first slice of the earlier blocks'
+    //    histograms (both in flight while LDS is cleared)
     int32_t e[KMAX];
     uint32_t bad = 0;
     load_token<KMAX>(topk_idx, t, N, K, E, e, bad);
+    const int n4 = b * (stride / 4); // the first b histogram rows are one contiguous span
+    const int4 *h4 = reinterpret_cast<const int4 *>(hist);
+    int4 hv[kHistBatch];
+#pragma unroll
+    for (int u = 0; u < kHistBatch; ++u) {
+        const int i = tid + u * kThreads;
+        hv[u] = i < n4 ? h4[i] : make_int4(0, 0, 0, 0);
+    }
     for (int i = tid; i < kGroups * (E + R); i += kThreads)
         s_bm[i] = 0ull; // s_bm and s_rbm are contiguous
     for (int i = tid; i < E + R; i += kThreads) {
@@ -153,32 +262,29 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
     }
     __syncthreads(); // LDS cleared
 
-    // 3. counts of all earlier blocks: the first b rows of the histogram are
-    //    one contiguous span; load it as int4 with eight loads in flight
-    if (b > 0) {
-        const int n4 = b * (stride / 4);
-        const int4 *h4 = reinterpret_cast<const int4 *>(hist);
-        for (int i0 = tid; i0 < n4; i0 += kThreads * 8) {
-            int4 v[8];
+    // 3. counts of all earlier blocks into s_base: the slice loaded above,
+    //    then further slices of kHistBatch int4 per thread (many blocks only)
+    for (int i0 = tid; i0 < n4; i0 += kThreads * kHistBatch) {
+        if (i0 != tid) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < kHistBatch; ++u) {
                 const int i = i0 + u * kThreads;
-                v[u] = i < n4 ? h4[i] : make_int4(0, 0, 0, 0);
+                hv[u] = i < n4 ? h4[i] : make_int4(0, 0, 0, 0);
             }
+        }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int i = i0 + u * kThreads;
-                if (i < n4) {
-                    const int c = (i * 4) % stride;
-                    if (c < E + R)
-                        atomicAdd(&s_base[c], v[u].x);
-                    if (c + 1 < E + R)
-                        atomicAdd(&s_base[c + 1], v[u].y);
-                    if (c + 2 < E + R)
-                        atomicAdd(&s_base[c + 2], v[u].z);
-                    if (c + 3 < E + R)
-                        atomicAdd(&s_base[c + 3], v[u].w);
-                }
+        for (int u = 0; u < kHistBatch; ++u) {
+            const int i = i0 + u * kThreads;
+            if (i < n4) {
+                const int c = (i * 4) % stride;
+                if (c < E + R)
+                    atomicAdd(&s_base[c], hv[u].x);
+                if (c + 1 < E + R)
+                    atomicAdd(&s_base[c + 1], hv[u].y);
+                if (c + 2 < E + R)
+                    atomicAdd(&s_base[c + 2], hv[u].z);
+                if (c + 3 < E + R)
+                    atomicAdd(&s_base[c + 3], hv[u].w);
             }
         }
     }
@@ -242,65 +348,61 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
         }
     }
 
-    // 6. this token's outputs
+    // 6. this token's outputs (16-byte stores where the row allows them)
     if (live) {
-        int32_t *slot_out = expert_slot + t * K;
+        int32_t slot[KMAX];
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
-            if (k < K)
-                slot_out[k] = e[k] >= 0 ? s_base[e[k]] + pre[k] + occ[k] : -1;
+            slot[k] = e[k] >= 0 ? s_base[e[k]] + pre[k] + occ[k] : -1;
+        int32_t *slot_out = expert_slot + t * K;
+        if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(slot_out) & 15) == 0) {
+#pragma unroll
+            for (int q = 0; q < KMAX / 4; ++q)
+                if (4 * q < K)
+                    reinterpret_cast<int4 *>(slot_out)[q] =
+                        make_int4(slot[4 * q], slot[4 * q + 1], slot[4 * q + 2], slot[4 * q + 3]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k)
+                if (k < K)
+                    slot_out[k] = slot[k];
+        }
         uint8_t *mask_out = is_token_in_rank + t * R;
         int32_t *rslot_out = rank_slot + t * R;
-        for (int r = 0; r < R; ++r) {
-            const bool in = (ranks >> r) & 1ull;
-            mask_out[r] = in ? 1 : 0;
-            rslot_out[r] = in ? s_base[E + r] + prefix_in_block(&s_rbm[r], R, g, lane) : -1;
+        const bool vec = (R & 3) == 0 && (reinterpret_cast<uintptr_t>(rslot_out) & 15) == 0 &&
+                         (reinterpret_cast<uintptr_t>(mask_out) & 3) == 0;
+        for (int r0 = 0; r0 < R; r0 += 4) {
+            int32_t v[4];
+            uint32_t m = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = r0 + q;
+                const bool in = r < R && ((ranks >> r) & 1ull);
+                v[q] = in ? s_base[E + r] + prefix_in_block(&s_rbm[r], R, g, lane) : -1;
+                m |= (in ? 1u : 0u) << (8 * q);
+            }
+            if (vec) {
+                *reinterpret_cast<int4 *>(rslot_out + r0) = make_int4(v[0], v[1], v[2], v[3]);
+                *reinterpret_cast<uint32_t *>(mask_out + r0) = m;
+            } else {
+                for (int q = 0; q < 4 && r0 + q < R; ++q) {
+                    rslot_out[r0 + q] = v[q];
+                    mask_out[r0 + q] = (uint8_t)((m >> (8 * q)) & 1u);
+                }
+            }
         }
     }
     if (tid == 0 && status && s_misc[1])
         atomicOr(status, EP_STATUS_BAD_EXPERT_ID);
 
-    // 7. the last block holds every count: write totals and the offset scan
+    // 7. single token block: it holds every count; write totals and the scan
     if (last_block) {
         __syncthreads();
-        for (int i = tid; i < E + R; i += kThreads) {
-            const int tot = s_base[i] + s_tot[i];
-            if (i < E)
-                num_tokens_per_expert[i] = tot;
-            else
-                num_tokens_per_rank[i - E] = tot;
-            s_tot[i] = tot;
-        }
+        for (int i = tid; i < E + R; i += kThreads)
+            s_tot[i] += s_base[i];
         __syncthreads();
-        if (expert_offset) {
-            const int per = (E + kThreads - 1) / kThreads;
-            const int start = tid * per;
-            int local = 0;
-            for (int i = 0; i < per; ++i)
-                if (start + i < E)
-                    local += s_tot[start + i];
-            int incl = local;
-            for (int off = 1; off < 64; off <<= 1) {
-                const int up = __shfl_up(incl, off, 64);
-                if (lane >= off)
-                    incl += up;
-            }
-            if (lane == 63)
-                s_misc[4 + g] = incl;
-            __syncthreads();
-            int woff = 0;
-            for (int g2 = 0; g2 < g; ++g2)
-                woff += s_misc[4 + g2];
-            int run = woff + incl - local;
-            for (int i = 0; i < per; ++i) {
-                if (start + i < E) {
-                    expert_offset[start + i] = run;
-                    run += s_tot[start + i];
-                }
-            }
-            if (tid == kThreads - 1)
-                expert_offset[E] = woff + incl;
-        }
+        write_totals_and_offsets(E, R, s_tot, s_misc, num_tokens_per_rank, num_tokens_per_expert,
+                                 expert_offset);
     }
 }
 
@@ -333,8 +435,9 @@ hipError_t launch_layout(const ep_shape &s, const LayoutPlan &plan, const int64_
         if (B > 1)                                                                                 \
             hipLaunchKernelGGL(layout_count_kernel<KMAX>, dim3(B), dim3(kThreads), count_lds,      \
                                stream, N, K, E, R, L, stride, topk_idx, workspace);                \
-        hipLaunchKernelGGL(layout_assign_kernel<KMAX>, dim3(B), dim3(kThreads), plan.lds_bytes,    \
-                           stream, N, K, E, R, L, stride, topk_idx, workspace,                     \
+        hipLaunchKernelGGL(layout_assign_kernel<KMAX>, dim3(B > 1 ? B + 1 : 1), dim3(kThreads),   \
+                           plan.lds_bytes, stream, N, K, E, R, L, stride, topk_idx,                \
+                           B > 1 ? workspace : nullptr,                                            \
                            num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank,           \
                            expert_slot, rank_slot, expert_offset, status);                         \
     } while (0)
