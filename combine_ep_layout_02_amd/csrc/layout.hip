@@ -78,9 +78,11 @@ __global__ __launch_bounds__(kThreads) void layout_count_kernel(
             ranks |= 1ull << (e[k] / L);
         }
     }
-    while (ranks) {
-        atomicAdd(&s_cnt[E + __builtin_ctzll(ranks)], 1);
-        ranks &= ranks - 1ull;
+    // tokens per rank: one ballot per rank gives the wave's count directly
+    for (int r = 0; r < R; ++r) {
+        const uint64_t m = __ballot((ranks >> r) & 1ull);
+        if ((tid & 63) == 0 && m)
+            atomicAdd(&s_cnt[E + r], __popcll(m));
     }
     __syncthreads();
     int32_t *row = hist + (size_t)blockIdx.x * stride;
@@ -295,18 +297,24 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
     for (int k = 0; k < KMAX; ++k)
         if (e[k] >= 0 && occ[k] == 0)
             atomicOr((unsigned long long *)&s_bm[g * E + e[k]], (unsigned long long)bit);
-    for (uint64_t rs = ranks; rs; rs &= rs - 1ull)
-        atomicOr((unsigned long long *)&s_rbm[g * R + __builtin_ctzll(rs)], (unsigned long long)bit);
+    // rank words: one ballot per rank gives this wave's word directly
+    for (int r = 0; r < R; ++r) {
+        const uint64_t m = __ballot((ranks >> r) & 1ull);
+        if (lane == 0)
+            s_rbm[g * R + r] = m;
+    }
     if (maxocc > 0)
         atomicMax(&s_misc[0], maxocc);
     if (bad)
         atomicOr(&s_misc[1], 1);
     __syncthreads();
 
+    // pre[k]: earlier blocks' entries of the expert + this block's entries of
+    // earlier tokens (layer 0) + earlier entries of this token (occ)
     int pre[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
-        pre[k] = e[k] >= 0 ? prefix_in_block(&s_bm[e[k]], E, g, lane) : 0;
+        pre[k] = e[k] >= 0 ? s_base[e[k]] + prefix_in_block(&s_bm[e[k]], E, g, lane) + occ[k] : 0;
     if (last_block) {
         for (int i = tid; i < E; i += kThreads) {
             int c = 0;
@@ -353,7 +361,7 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
         int32_t slot[KMAX];
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
-            slot[k] = e[k] >= 0 ? s_base[e[k]] + pre[k] + occ[k] : -1;
+            slot[k] = e[k] >= 0 ? pre[k] : -1;
         int32_t *slot_out = expert_slot + t * K;
         if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(slot_out) & 15) == 0) {
 #pragma unroll
