@@ -62,6 +62,11 @@ class Oracle:
         lib.oracle_bf16_rne_array.argtypes = [i64, vp, vp]
         lib.oracle_quantize_rows.argtypes = [i32, i32, vp, vp, vp]
         lib.oracle_dequant_rows.argtypes = [i32, i32, vp, vp, vp]
+        lib.oracle_pack_fmt.argtypes = [i32] * 7 + [vp] * 6
+        lib.oracle_pack_fmt.restype = ctypes.c_int
+        lib.oracle_quantize_rows_pow2.argtypes = [i32, i32, vp, vp, vp]
+        lib.oracle_pow2_scale_exponent.argtypes = [ctypes.c_float]
+        lib.oracle_pow2_scale_exponent.restype = ctypes.c_int
         self.lib = lib
 
     # ------------------------------------------------------------- layout
@@ -89,28 +94,49 @@ class Oracle:
 
     # --------------------------------------------------------------- pack
     def pack(self, x_bits: np.ndarray, topk_idx: np.ndarray, expert_slot: np.ndarray,
-             num_experts: int, capacity: int, use_fp8: bool, fill: int = 0):
+             num_experts: int, capacity: int, use_fp8: bool, fill: int = 0, scale_format: int = 0):
         """Dispatch pack (Lesson 14 §3 receive shape; DeepEP V1 Legacy guide
-        §5.2(6) and §6.3 FP8 with one scale per 128 channels).  ``x_bits`` is
-        the bf16 bit pattern, uint16 [N, H].  Returns (recv_x, recv_scales,
+        §5.2(6) and §6.3 FP8 with one scale per 128 channels; §6.3
+        round_scale / use_ue8m0 for scale_format 1 / 2).  ``x_bits`` is the
+        bf16 bit pattern, uint16 [N, H].  Returns (recv_x, recv_scales,
         recv_src_idx, status) with recv_x uint8 [E, S, H] (FP8) or uint16
-        [E, S, H] (BF16); rows never written keep ``fill``."""
+        [E, S, H] (BF16); recv_scales float32 [E, S, H/128] (formats 0, 1) or
+        uint32 [E, S, ceil(H/512)] (format 2, four UE8M0 bytes per word);
+        rows never written keep ``fill``."""
         x = np.ascontiguousarray(x_bits, dtype=np.uint16)
         idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
         slot = np.ascontiguousarray(expert_slot, dtype=np.int32)
         n, h = x.shape
         k = idx.shape[1]
         e, s = int(num_experts), int(capacity)
+        g = h // 128
         if use_fp8:
             recv_x = np.full((e, s, h), fill & 0xFF, np.uint8)
-            recv_scales = np.full((e, s, h // 128), np.nan, np.float32)
+            if scale_format == 2:
+                recv_scales = np.full((e, s, (g + 3) // 4), 0xDEADBEEF, np.uint32)
+            else:
+                recv_scales = np.full((e, s, g), np.nan, np.float32)
         else:
             recv_x = np.full((e, s, h), fill & 0xFFFF, np.uint16)
             recv_scales = None
         recv_src = np.full((e, s), -2, np.int32)
-        st = self.lib.oracle_pack(n, h, k, e, s, int(bool(use_fp8)), _ptr(x), _ptr(idx),
-                                  _ptr(slot), _ptr(recv_x), _ptr(recv_scales), _ptr(recv_src))
+        st = self.lib.oracle_pack_fmt(n, h, k, e, s, int(bool(use_fp8)), int(scale_format),
+                                      _ptr(x), _ptr(idx), _ptr(slot), _ptr(recv_x),
+                                      _ptr(recv_scales), _ptr(recv_src))
         return recv_x, recv_scales, recv_src, int(st)
+
+    def quantize_rows_pow2(self, x_bits: np.ndarray):
+        """Power-of-two-scale FP8 payload of each row: (q uint8 [N, H],
+        exponents int32 [N, H/128]); the scale of a block is 2^exponent."""
+        x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        n, h = x.shape
+        q = np.empty((n, h), np.uint8)
+        ex = np.empty((n, h // 128), np.int32)
+        self.lib.oracle_quantize_rows_pow2(n, h, _ptr(x), _ptr(q), _ptr(ex))
+        return q, ex
+
+    def pow2_scale_exponent(self, amax_floored: float) -> int:
+        return int(self.lib.oracle_pow2_scale_exponent(ctypes.c_float(amax_floored)))
 
     # ------------------------------------------------------------ combine
     def combine(self, y_bits: np.ndarray, topk_idx: np.ndarray, topk_weights: np.ndarray,

@@ -215,20 +215,68 @@ int oracle_layout(int32_t N, int32_t K, int32_t E, int32_t R, const int64_t *top
  *   scale = a' / 448          (one rounded fp32 division; what ships)
  *   q     = E4M3FN_RNE(clamp(x * inv, -448, 448))
  * The receiver reconstructs x ~ q * scale. */
+/* a' = max(max_c |x[c]|, 1e-4) over one 128-channel block (exact). */
+static float block_amax_floored(const uint16_t *xb)
+{
+    float a = 0.0f;
+    for (int c = 0; c < 128; ++c) {
+        float m = fabsf(oracle_bf16_to_f32(xb[c]));
+        if (m > a)
+            a = m;
+    }
+    return (a > 1e-4f) ? a : 1e-4f;
+}
+
 void oracle_quantize_row(int32_t H, const uint16_t *x_row, uint8_t *q_row, float *scales)
 {
     for (int32_t b = 0; b < H / 128; ++b) {
         const uint16_t *xb = x_row + (size_t)b * 128;
-        float a = 0.0f;
-        for (int c = 0; c < 128; ++c) {
-            float m = fabsf(oracle_bf16_to_f32(xb[c]));
-            if (m > a)
-                a = m;
-        }
-        float ap = (a > 1e-4f) ? a : 1e-4f;
+        float ap = block_amax_floored(xb);
         float inv = 448.0f / ap;
         float scale = ap / 448.0f;
         scales[b] = scale;
+        for (int c = 0; c < 128; ++c) {
+            float v = oracle_bf16_to_f32(xb[c]) * inv;
+            if (v > 448.0f)
+                v = 448.0f;
+            if (v < -448.0f)
+                v = -448.0f;
+            q_row[(size_t)b * 128 + c] = oracle_e4m3fn_encode(v);
+        }
+    }
+}
+
+/* Power-of-two scales ([V1] §6.3 names round_scale: scales rounded to powers
+ * of two, and use_ue8m0: those scales stored as 8-bit exponents).  For block
+ * amax a' (floored as above) the scale is the smallest power of two p = 2^e
+ * with 448 * p >= a', so every |x / p| <= 448 and nothing clips; found by
+ * exact comparisons in double (448 * 2^e is exact).  Then
+ *   q = E4M3FN_RNE(clamp(RN(x * 2^-e), -448, 448)).
+ * UE8M0 stores the byte e + 127 (value 2^(byte - 127)). */
+int oracle_pow2_scale_exponent(float ap)
+{
+    int e;
+    frexp((double)ap, &e); /* ap in [2^(e-1), 2^e) */
+    e -= 9;                /* 448 * 2^(e-1) < 2^(e+8) / 2 <= ap: no smaller e can hold */
+    while (ldexp(448.0, e) < (double)ap)
+        e += 1;            /* step up to the first e with 448 * 2^e >= ap */
+    return e;
+}
+
+#define ORACLE_SCALE_FP32 0
+#define ORACLE_SCALE_POW2 1
+#define ORACLE_SCALE_UE8M0 2
+
+/* One token row to FP8 with power-of-two block scales: e per block into
+ * exps[b]; the fp32 scale is 2^e. */
+void oracle_quantize_row_pow2(int32_t H, const uint16_t *x_row, uint8_t *q_row, int32_t *exps)
+{
+    for (int32_t b = 0; b < H / 128; ++b) {
+        const uint16_t *xb = x_row + (size_t)b * 128;
+        float ap = block_amax_floored(xb);
+        int e = oracle_pow2_scale_exponent(ap);
+        exps[b] = e;
+        float inv = (float)ldexp(1.0, -e);
         for (int c = 0; c < 128; ++c) {
             float v = oracle_bf16_to_f32(xb[c]) * inv;
             if (v > 448.0f)
@@ -265,25 +313,50 @@ void oracle_dequant_row(int32_t H, const uint8_t *q_row, const float *scales, ui
  *   recv_x[e][j] = payload, recv_scales[e][j][:] = scales (FP8 only),
  *   recv_src_idx[e][j] = t.
  * Rows j >= count_e are not written. */
-int oracle_pack(int32_t N, int32_t H, int32_t K, int32_t E, int32_t S, int32_t use_fp8,
-                const uint16_t *x, const int64_t *topk_idx, const int32_t *expert_slot,
-                void *recv_x, float *recv_scales, int32_t *recv_src_idx)
+/* Scale storage of one receive row ([V1] §5.2(6) and §6.3):
+ *   fp32 formats: G floats (the scale, or 2^e);
+ *   UE8M0: ceil(G/4) 32-bit words, byte j of word w = e + 127 of block
+ *   4w + j (little-endian), bytes past the last block 0. */
+static int32_t scale_words(int32_t G, int32_t fmt)
 {
-    if (N < 0 || H < 1 || K < 1 || E < 1 || S < 0 || (use_fp8 && H % 128 != 0))
+    return fmt == ORACLE_SCALE_UE8M0 ? (G + 3) / 4 : G;
+}
+
+int oracle_pack_fmt(int32_t N, int32_t H, int32_t K, int32_t E, int32_t S, int32_t use_fp8,
+                    int32_t scale_fmt, const uint16_t *x, const int64_t *topk_idx,
+                    const int32_t *expert_slot, void *recv_x, void *recv_scales,
+                    int32_t *recv_src_idx)
+{
+    if (N < 0 || H < 1 || K < 1 || E < 1 || S < 0 || (use_fp8 && H % 128 != 0) || scale_fmt < 0 ||
+        scale_fmt > 2 || (!use_fp8 && scale_fmt != 0))
         return ORACLE_BAD_ARGS;
     int status = ORACLE_OK;
     int32_t G = H / 128;
+    int32_t W = scale_words(G, scale_fmt);
     uint8_t *q = (uint8_t *)malloc((size_t)H);
     float *sc = (float *)malloc(sizeof(float) * (size_t)(G > 0 ? G : 1));
-    if (!q || !sc) {
+    int32_t *ex = (int32_t *)malloc(sizeof(int32_t) * (size_t)(G > 0 ? G : 1));
+    uint32_t *packed = (uint32_t *)calloc((size_t)(W > 0 ? W : 1), sizeof(uint32_t));
+    if (!q || !sc || !ex || !packed) {
         free(q);
         free(sc);
+        free(ex);
+        free(packed);
         return ORACLE_BAD_ARGS;
     }
     for (int32_t t = 0; t < N; ++t) {
         const uint16_t *xt = x + (size_t)t * H;
-        if (use_fp8)
+        if (use_fp8 && scale_fmt == ORACLE_SCALE_FP32) {
             oracle_quantize_row(H, xt, q, sc);
+        } else if (use_fp8) {
+            oracle_quantize_row_pow2(H, xt, q, ex);
+            for (int32_t b = 0; b < G; ++b)
+                sc[b] = (float)ldexp(1.0, ex[b]);
+            for (int32_t w = 0; w < W; ++w)
+                packed[w] = 0;
+            for (int32_t b = 0; b < G; ++b)
+                packed[b / 4] |= (uint32_t)(ex[b] + 127) << (8 * (b % 4));
+        }
         for (int32_t k = 0; k < K; ++k) {
             size_t i = (size_t)t * K + k;
             int32_t e = routed_expert(topk_idx[i], E, &status);
@@ -297,7 +370,10 @@ int oracle_pack(int32_t N, int32_t H, int32_t K, int32_t E, int32_t S, int32_t u
             size_t row = (size_t)e * S + j;
             if (use_fp8) {
                 memcpy((uint8_t *)recv_x + row * H, q, (size_t)H);
-                memcpy(recv_scales + row * G, sc, sizeof(float) * (size_t)G);
+                if (scale_fmt == ORACLE_SCALE_UE8M0)
+                    memcpy((uint32_t *)recv_scales + row * W, packed, sizeof(uint32_t) * (size_t)W);
+                else
+                    memcpy((float *)recv_scales + row * G, sc, sizeof(float) * (size_t)G);
             } else {
                 memcpy((uint16_t *)recv_x + row * H, xt, sizeof(uint16_t) * (size_t)H);
             }
@@ -306,7 +382,17 @@ int oracle_pack(int32_t N, int32_t H, int32_t K, int32_t E, int32_t S, int32_t u
     }
     free(q);
     free(sc);
+    free(ex);
+    free(packed);
     return status;
+}
+
+int oracle_pack(int32_t N, int32_t H, int32_t K, int32_t E, int32_t S, int32_t use_fp8,
+                const uint16_t *x, const int64_t *topk_idx, const int32_t *expert_slot,
+                void *recv_x, float *recv_scales, int32_t *recv_src_idx)
+{
+    return oracle_pack_fmt(N, H, K, E, S, use_fp8, ORACLE_SCALE_FP32, x, topk_idx, expert_slot,
+                           recv_x, recv_scales, recv_src_idx);
 }
 
 /* ---------------------------------------------------------------- combine */
@@ -385,4 +471,10 @@ void oracle_dequant_rows(int32_t N, int32_t H, const uint8_t *q, const float *sc
 {
     for (int32_t t = 0; t < N; ++t)
         oracle_dequant_row(H, q + (size_t)t * H, scales + (size_t)t * (H / 128), y + (size_t)t * H);
+}
+
+void oracle_quantize_rows_pow2(int32_t N, int32_t H, const uint16_t *x, uint8_t *q, int32_t *exps)
+{
+    for (int32_t t = 0; t < N; ++t)
+        oracle_quantize_row_pow2(H, x + (size_t)t * H, q + (size_t)t * H, exps + (size_t)t * (H / 128));
 }

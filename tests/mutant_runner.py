@@ -38,6 +38,9 @@ def main(path: str) -> int:
         ("identity", lambda: pins.pin_identity_expert(o, ident_cases)),
         ("lesson_dense", lambda: pins.pin_lesson_dense(o, H=4)),
         ("pages_bytes", lambda: pins.pin_pages_pass_bytes(o)),
+        ("pow2_scales", lambda: pins.pin_pow2_scales(o)),
+        ("pow2_dequant_bound", lambda: pins.pin_pow2_dequant_bound(o)),
+        ("ue8m0_packing", lambda: pins.pin_ue8m0_packing(o)),
         ("layout_bruteforce", lambda: pins.pin_layout_bruteforce(o)),
     ]
     for name, fn in steps:

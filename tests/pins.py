@@ -510,6 +510,76 @@ def pin_pages_pass_bytes(o):
     assert abs(total - g["bytes_approx"]) / g["bytes_approx"] < 0.01, total
 
 
+def pin_pow2_scales(o):
+    """Power-of-two scales ([V1] §6.3 round_scale): for every finite bf16
+    magnitude as the block amax (and the 1e-4 floor), the exponent e is the
+    smallest with 448 * 2^e >= max(amax, 1e-4) -- checked as the two
+    inequalities of that definition in float64 (exact) -- and every element
+    encodes to the nearest E4M3FN code of x * 2^-e."""
+    mags = np.arange(0, 0x7F80, dtype=np.uint32).astype(np.uint16)
+    floor = float(np.float32(1e-4))
+    ap = np.maximum(bf16_to_f64(mags), floor)
+    e = np.array([o.pow2_scale_exponent(float(v)) for v in ap[::37]] +
+                 [o.pow2_scale_exponent(float(v)) for v in ap[-64:]], dtype=np.int64)
+    apc = np.concatenate([ap[::37], ap[-64:]])
+    assert np.all(448.0 * np.exp2(e) >= apc), "scale too small: an element would clip"
+    assert np.all(448.0 * np.exp2(e - 1) < apc), "scale not the smallest power of two"
+    rows = _rows_with_amax(mags)
+    q, ex = o.quantize_rows_pow2(rows)
+    assert np.all(448.0 * np.exp2(ex[:, 0].astype(np.float64)) >= ap)
+    assert np.all(448.0 * np.exp2(ex[:, 0].astype(np.float64) - 1) < ap)
+    v = (bf16_to_f64(rows) * np.exp2(-ex[:, :1].astype(np.float64))).astype(np.float32)
+    assert np.array_equal(q, nearest_e4m3fn(np.clip(v, -448, 448).astype(np.float32)))
+
+
+def pin_pow2_dequant_bound(o):
+    """Quantise with a power-of-two scale p, dequantise: |x - q p| <= 2^-4 |x|
+    + 2^-10 p (half an ulp of the 3-bit mantissa, or of the subnormal step)."""
+    rng = np.random.default_rng(13)
+    n, h = 64, 512
+    base = rng.standard_normal((n, h)).astype(np.float32)
+    mag = np.exp2(rng.uniform(-20, 20, size=(n, h // 128, 1))).astype(np.float32)
+    x = (base.reshape(n, h // 128, 128) * mag).reshape(n, h)
+    x[0, :128] = 0.0
+    xb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    q, ex = o.quantize_rows_pow2(xb)
+    p = np.repeat(np.exp2(ex.astype(np.float64)), 128, axis=1)
+    y = o.e4m3fn_decode(q) * p
+    xv = bf16_to_f64(xb)
+    assert np.all(np.abs(y - xv) <= 2.0 ** -4 * np.abs(xv) + 2.0 ** -10 * p)
+
+
+def pin_ue8m0_packing(o):
+    """UE8M0 scales ([V1] §6.3 use_ue8m0): byte j of word w of a receive row is
+    e + 127 of block 4w + j, so 2^(byte - 127) equals the power-of-two fp32
+    scale; bytes past the last block are 0; FP8 bytes are the same in both
+    formats."""
+    rng = np.random.default_rng(21)
+    for h in (128, 640, 1152, 2048):
+        x = torch.from_numpy(rng.standard_normal((9, h)).astype(np.float32) *
+                             np.exp2(rng.uniform(-8, 8, size=(9, 1))).astype(np.float32))
+        xb = x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        idx = np.array([[0, 1], [1, 2], [2, 0], [0, 2], [1, -1], [2, 1], [0, 1], [1, 0], [2, 2]],
+                       dtype=np.int64)
+        lay = o.layout(idx, 3, 3)
+        S = 9
+        rx1, sc1, src1, st1 = o.pack(xb, idx, lay["expert_slot"], 3, S, True, scale_format=1)
+        rx2, sc2, src2, st2 = o.pack(xb, idx, lay["expert_slot"], 3, S, True, scale_format=2)
+        assert st1 == 0 and st2 == 0
+        assert np.array_equal(rx1, rx2) and np.array_equal(src1, src2)
+        g = h // 128
+        cnt = lay["num_tokens_per_expert"]
+        for e in range(3):
+            for j in range(int(cnt[e])):
+                words = sc2[e, j]
+                by = np.array([(int(words[b // 4]) >> (8 * (b % 4))) & 0xFF for b in range(4 * len(words))])
+                assert np.array_equal(np.exp2(by[:g].astype(np.float64) - 127), sc1[e, j].astype(np.float64))
+                assert np.all(by[g:] == 0)
+        q, ex = o.quantize_rows_pow2(xb)
+        t = src1[0, 0]
+        assert np.array_equal(rx1[0, 0], q[t])
+
+
 CHEAP_PINS = ("pin_lesson_example", "pin_bf16", "pin_e4m3fn", "pin_scales_closed_form",
               "pin_dequant_bound", "pin_pack_fp8_is_row_quantiser", "pin_lesson_dense",
               "pin_layout_bad_ids")

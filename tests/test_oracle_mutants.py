@@ -38,7 +38,7 @@ MUTANTS = [
     ("fp8_decode_bias", [("ldexp((double)(8 + m), E - 10)", "ldexp((double)(8 + m), E - 11)")]),
     ("inv_transposed", [("float inv = 448.0f / ap;", "float inv = ap / 448.0f;")]),
     ("scale_inverted", [("float scale = ap / 448.0f;", "float scale = 448.0f / ap;")]),
-    ("no_amax_floor", [("float ap = (a > 1e-4f) ? a : 1e-4f;", "float ap = (a > 0.0f) ? a : 1.0f;")]),
+    ("no_amax_floor", [("return (a > 1e-4f) ? a : 1e-4f;", "return (a > 0.0f) ? a : 1.0f;")]),
     ("amax_signed", [("float m = fabsf(oracle_bf16_to_f32(xb[c]));",
                       "float m = oracle_bf16_to_f32(xb[c]);")]),
     ("fma_operands_swapped", [("acc[c] = fmaf(w, oracle_bf16_to_f32(yr[c]), acc[c]);",
@@ -46,8 +46,12 @@ MUTANTS = [
     ("weight_of_first_k", [("float w = topk_weights[i];", "float w = topk_weights[(size_t)t * K];")]),
     ("combine_acc_negzero", [("            acc[c] = 0.0f;", "            acc[c] = -0.0f;")]),
     ("src_idx_is_k", [("recv_src_idx[row] = t;", "recv_src_idx[row] = k;")]),
-    ("scales_row_stride", [("memcpy(recv_scales + row * G, sc", "memcpy(recv_scales + row, sc")]),
+    ("scales_row_stride", [("memcpy((float *)recv_scales + row * G, sc", "memcpy((float *)recv_scales + row, sc")]),
     ("dequant_wrong_block", [("float v = qv * scales[c / 128];", "float v = qv * scales[c % (H / 128)];")]),
+    ("pow2_steps_past_equality", [("while (ldexp(448.0, e) < (double)ap)", "while (ldexp(448.0, e) <= (double)ap)")]),
+    ("pow2_search_starts_high", [("    e -= 9;", "    e -= 7;")]),
+    ("ue8m0_bias_128", [("(uint32_t)(ex[b] + 127) << (8 * (b % 4))", "(uint32_t)(ex[b] + 128) << (8 * (b % 4))")]),
+    ("ue8m0_byte_order", [("<< (8 * (b % 4))", "<< (8 * (3 - b % 4))")]),
 ]
 
 

@@ -132,3 +132,12 @@ def test_combine_random_rows_against_float64(o):
         np.add.at(mag, tt, np.abs(terms))
         K = idx.shape[1]
         pins.assert_combine_close(out, ref, abs_slack=K * 2.0 ** -24 * mag * 1.01)
+
+
+def test_pow2_scales(o):
+    pins.pin_pow2_scales(o)
+    pins.pin_pow2_dequant_bound(o)
+
+
+def test_ue8m0_packing(o):
+    pins.pin_ue8m0_packing(o)
