@@ -22,6 +22,9 @@ int check_shape(const ep_shape *s)
         return EP_ERR_SHAPE;
     if (s->use_fp8 && H % 128 != 0)
         return EP_ERR_SHAPE;
+    if (s->scale_format < EP_SCALE_FP32 || s->scale_format > EP_SCALE_UE8M0 ||
+        (!s->use_fp8 && s->scale_format != EP_SCALE_FP32))
+        return EP_ERR_SHAPE;
     if (K > EP_MAX_TOPK || E > EP_MAX_EXPERTS || R > EP_MAX_RANKS)
         return EP_ERR_UNSUPPORTED;
     if (M < 1 || N > M || S < M)
@@ -82,7 +85,10 @@ int ep_query_sizes(const ep_shape *s, ep_sizes *out)
                  R = s->num_ranks, S = s->expert_capacity;
     const size_t rows = E * S;
     out->recv_x = rows * H * (s->use_fp8 ? 1 : 2);
-    out->recv_scales = s->use_fp8 ? rows * (H / 128) * sizeof(float) : 0;
+    const size_t G = H / 128;
+    out->recv_scales = !s->use_fp8 ? 0
+                       : s->scale_format == EP_SCALE_UE8M0 ? rows * ((G + 3) / 4) * sizeof(uint32_t)
+                                                           : rows * G * sizeof(float);
     out->recv_src_idx = rows * sizeof(int32_t);
     out->expert_out = rows * H * 2;
     out->combined_x = N * H * 2;
@@ -127,7 +133,7 @@ int ep_layout(const ep_shape *s, const int64_t *topk_idx, int32_t *num_tokens_pe
 }
 
 int ep_dispatch(const ep_shape *s, const uint16_t *x, const int64_t *topk_idx,
-                const int32_t *expert_slot, void *recv_x, float *recv_scales,
+                const int32_t *expert_slot, void *recv_x, void *recv_scales,
                 int32_t *recv_src_idx, uint32_t *status, void *stream)
 {
     const int rc = check_shape(s);

@@ -35,7 +35,7 @@ hipError_t launch_layout(const ep_shape &s, const LayoutPlan &plan, const int64_
 
 // ---- dispatch pack -------------------------------------------------------
 hipError_t launch_dispatch(const ep_shape &s, const uint16_t *x, const int64_t *topk_idx,
-                           const int32_t *expert_slot, void *recv_x, float *recv_scales,
+                           const int32_t *expert_slot, void *recv_x, void *recv_scales,
                            int32_t *recv_src_idx, uint32_t *status, hipStream_t stream);
 
 // ---- combine ---------------------------------------------------------------

@@ -32,7 +32,10 @@ EP_STATUS_BAD_EXPERT_ID = 1
 EP_STATUS_BAD_SLOT = 2
 
 SHAPE_FIELDS = ("num_tokens", "hidden", "num_topk", "num_experts", "num_ranks",
-                "num_max_dispatch_tokens_per_rank", "expert_capacity", "use_fp8")
+                "num_max_dispatch_tokens_per_rank", "expert_capacity", "use_fp8", "scale_format")
+EP_SCALE_FP32 = 0
+EP_SCALE_POW2 = 1
+EP_SCALE_UE8M0 = 2
 SIZE_FIELDS = ("recv_x", "recv_scales", "recv_src_idx", "expert_out", "combined_x",
                "num_tokens_per_rank", "num_tokens_per_expert", "is_token_in_rank",
                "expert_slot", "rank_slot", "expert_offset", "layout_workspace")
@@ -82,16 +85,18 @@ def lib() -> ctypes.CDLL:
 
 def make_shape(num_tokens: int, hidden: int, num_topk: int, num_experts: int, num_ranks: int,
                num_max_dispatch_tokens_per_rank: int, expert_capacity: int,
-               use_fp8: bool) -> ep_shape:
+               use_fp8: bool, scale_format: int = EP_SCALE_FP32) -> ep_shape:
     return ep_shape(int(num_tokens), int(hidden), int(num_topk), int(num_experts), int(num_ranks),
-                    int(num_max_dispatch_tokens_per_rank), int(expert_capacity), int(bool(use_fp8)))
+                    int(num_max_dispatch_tokens_per_rank), int(expert_capacity), int(bool(use_fp8)),
+                    int(scale_format))
 
 
-def shape_of(workload) -> ep_shape:
-    """ep_shape of a ``workloads.Workload``."""
+def shape_of(workload, scale_format: int = EP_SCALE_FP32) -> ep_shape:
+    """ep_shape of a ``workloads.Workload`` (FP8 workloads may pick a scale format)."""
     w = workload
     return make_shape(w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks,
-                      w.num_max_dispatch_tokens_per_rank, w.expert_capacity, w.use_fp8)
+                      w.num_max_dispatch_tokens_per_rank, w.expert_capacity, w.use_fp8,
+                      scale_format if w.use_fp8 else EP_SCALE_FP32)
 
 
 def ep_strerror(code: int) -> str:
@@ -168,7 +173,9 @@ def ep_dispatch(shape: ep_shape, x: torch.Tensor, topk_idx: torch.Tensor, expert
     rc = lib().ep_dispatch(
         ctypes.byref(shape), _ptr(x, "x", _BF16, N * H), _ptr(topk_idx, "topk_idx", _I64, N * K),
         _ptr(expert_slot, "expert_slot", _I32, N * K), _ptr(recv_x, "recv_x", rx_types, rows * H),
-        _ptr(recv_scales, "recv_scales", _F32, rows * (H // 128)) if shape.use_fp8 else None,
+        (_ptr(recv_scales, "recv_scales", _STATUS, rows * ((H // 128 + 3) // 4))
+         if shape.scale_format == EP_SCALE_UE8M0 else
+         _ptr(recv_scales, "recv_scales", _F32, rows * (H // 128))) if shape.use_fp8 else None,
         _ptr(recv_src_idx, "recv_src_idx", _I32, rows), _ptr(status, "status", _STATUS, 1),
         _stream(stream, recv_x))
     if rc != EP_OK:
@@ -226,8 +233,10 @@ def allocate(shape: ep_shape, device="cuda", parts=("layout", "dispatch", "combi
         out.update({
             "recv_x": torch.empty((E, S, H), dtype=torch.uint8 if shape.use_fp8 else torch.int16,
                                   device=dev),
-            "recv_scales": (torch.empty((E, S, H // 128), dtype=torch.float32, device=dev)
-                            if shape.use_fp8 else None),
+            "recv_scales": (None if not shape.use_fp8 else
+                            torch.empty((E, S, (H // 128 + 3) // 4), dtype=torch.int32, device=dev)
+                            if shape.scale_format == EP_SCALE_UE8M0 else
+                            torch.empty((E, S, H // 128), dtype=torch.float32, device=dev)),
             "recv_src_idx": torch.empty((E, S), dtype=torch.int32, device=dev),
         })
     if "combine" in parts:

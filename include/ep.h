@@ -61,7 +61,8 @@ extern "C" {
 #define EP_OK 0
 #define EP_ERR_NULL 1        /* a required pointer is NULL                            */
 #define EP_ERR_SHAPE 2       /* N < 0, H, K, E or R out of range, E % R != 0, FP8 with
-                                H % 128 != 0, BF16 with H % 8 != 0                    */
+                                H % 128 != 0, BF16 with H % 8 != 0, a bad
+                                scale_format                                         */
 #define EP_ERR_CAPACITY 3    /* N > M or S < M: the fixed upper bounds are never grown
                                 ([V1] §6.1 and §8.4; [L14] capacity discussion)       */
 #define EP_ERR_ALIGN 4       /* a pointer is not aligned as required                  */
@@ -88,13 +89,25 @@ typedef struct {
     int32_t num_max_dispatch_tokens_per_rank; /* M >= max(N, 1): fixed token bound   */
     int32_t expert_capacity; /* S >= M: rows per expert receive buffer (the pages'
                                 low-latency shape uses S = R * M)                    */
-    int32_t use_fp8;     /* 0: BF16 rows; 1: E4M3FN rows + fp32 scale per 128 ch     */
+    int32_t use_fp8;     /* 0: BF16 rows; 1: E4M3FN rows + a scale per 128 channels  */
+    int32_t scale_format; /* FP8 scale per 128-channel block ([V1] §5.2(6), §6.3):
+                             EP_SCALE_FP32  (0) fp32 a'/448;
+                             EP_SCALE_POW2  (1) fp32 power of two ("round_scale");
+                             EP_SCALE_UE8M0 (2) that power of two as an 8-bit
+                             exponent, four per 32-bit word ("use_ue8m0").
+                             Must be 0 when use_fp8 == 0. */
 } ep_shape;
+
+/* Scale formats of ep_shape.scale_format. */
+#define EP_SCALE_FP32 0
+#define EP_SCALE_POW2 1
+#define EP_SCALE_UE8M0 2
 
 /* Bytes of every buffer for a shape (0 for a buffer the shape does not use). */
 typedef struct {
     size_t recv_x;                /* E*S*H (FP8) or E*S*H*2 (BF16)                    */
-    size_t recv_scales;           /* E*S*(H/128)*4 (FP8), else 0                      */
+    size_t recv_scales;           /* E*S*(H/128)*4 (FP8 fp32 scales),
+                                     E*S*ceil(H/512)*4 (UE8M0), else 0              */
     size_t recv_src_idx;          /* E*S*4                                            */
     size_t expert_out;            /* E*S*H*2: bf16 expert outputs read by combine     */
     size_t combined_x;            /* N*H*2                                            */
@@ -152,15 +165,20 @@ int ep_layout(const ep_shape *shape, const int64_t *topk_idx, int32_t *num_token
  * In:  x [N, H] bf16 bits; topk_idx [N, K]; expert_slot [N, K] from ep_layout.
  * Out: recv_x [E, S, H]: row expert_slot[t,k] of expert topk_idx[t,k] receives
  *        token t (BF16: a bit copy; FP8: per 128-channel block b, with
- *        a = max|x|, a' = max(a, 1e-4), inv = RN(448 / a'):
+ *        a = max|x|, a' = max(a, 1e-4):
+ *          EP_SCALE_FP32: inv = RN(448 / a'), scale = RN(a' / 448);
+ *          EP_SCALE_POW2 / EP_SCALE_UE8M0: scale = 2^e for the smallest e with
+ *            448 * 2^e >= a' (no element clips), inv = 2^-e;
  *        q = E4M3FN_RNE(clamp(RN(x * inv), -448, 448)));
- *      recv_scales [E, S, H/128] fp32: scale = RN(a' / 448) per block (FP8 only;
- *        NULL when use_fp8 == 0);
+ *      recv_scales (FP8 only; NULL when use_fp8 == 0):
+ *        EP_SCALE_FP32 / EP_SCALE_POW2: fp32 [E, S, H/128], the scale per block;
+ *        EP_SCALE_UE8M0: uint32 [E, S, ceil(H/512)], byte j of word w = e + 127
+ *          of block 4w + j (little-endian), bytes past the last block 0;
  *      recv_src_idx [E, S] int32: the source token t of each written row.
  * Each token is read and quantised once and written once per valid entry.
  * Rows at or beyond num_tokens_per_expert[e] are never written. */
 int ep_dispatch(const ep_shape *shape, const uint16_t *x, const int64_t *topk_idx,
-                const int32_t *expert_slot, void *recv_x, float *recv_scales,
+                const int32_t *expert_slot, void *recv_x, void *recv_scales,
                 int32_t *recv_src_idx, uint32_t *status, void *stream);
 
 /* Combine: top-k weighted gather-reduce back into token order ([ASC] "Two

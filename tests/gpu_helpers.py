@@ -82,8 +82,12 @@ class DispatchRun:
         self.x = dev(x_bits) if x_dev is None else x_dev
         if shape.use_fp8:
             self.recv_x = torch.full((E, S, H), POISON_X8, dtype=torch.uint8, device="cuda")
-            self.recv_scales = torch.full((E, S, H // 128), POISON_SCALE_BITS, dtype=torch.int32,
-                                          device="cuda").view(torch.float32)
+            if shape.scale_format == ep.EP_SCALE_UE8M0:  # four exponent bytes per word
+                self.recv_scales = torch.full((E, S, (H // 128 + 3) // 4), POISON_SCALE_BITS,
+                                              dtype=torch.int32, device="cuda")
+            else:
+                self.recv_scales = torch.full((E, S, H // 128), POISON_SCALE_BITS,
+                                              dtype=torch.int32, device="cuda").view(torch.float32)
         else:
             self.recv_x = torch.full((E, S, H), int(POISON_X16), dtype=torch.int16, device="cuda")
             self.recv_scales = None

@@ -67,6 +67,19 @@ def test_query_sizes_match_the_receive_geometry(wid):
     assert sz["layout_workspace"] == (blocks * stride * 4 if blocks > 1 else 0)
 
 
+@pytest.mark.parametrize("hidden", [128, 512, 640, 7168])
+def test_scale_buffer_sizes_per_format(hidden):
+    """DeepEP V1 Legacy guide §6.3: fp32 scales are one float per 128-channel
+    block; UE8M0 scales pack four block exponents per 32-bit word."""
+    w = W.WORKLOADS[3].scaled(64, hidden)
+    E, S, G = w.num_experts, w.expert_capacity, hidden // 128
+    for fmt, want in ((ep.EP_SCALE_FP32, E * S * G * 4), (ep.EP_SCALE_POW2, E * S * G * 4),
+                      (ep.EP_SCALE_UE8M0, E * S * ((G + 3) // 4) * 4)):
+        sz = ep.ep_query_sizes(ep.shape_of(w, fmt))
+        assert sz["recv_scales"] == want
+        assert sz["recv_x"] == E * S * hidden
+
+
 def test_decode_receive_buffer_is_the_pages_shape():
     """Lesson 14 §3 / DeepEP V1 Legacy guide §6.3: each of the 8 ranks
     receives [32, 8 * 128, 7168] FP8 bytes; here the 8 ranks are slices of
@@ -83,7 +96,8 @@ OK16 = ctypes.c_void_p(0x1000)  # aligned stand-in pointer, never dereferenced
 
 def _shape(**kw):
     base = dict(num_tokens=300, hidden=256, num_topk=4, num_experts=16, num_ranks=4,
-                num_max_dispatch_tokens_per_rank=300, expert_capacity=300, use_fp8=0)
+                num_max_dispatch_tokens_per_rank=300, expert_capacity=300, use_fp8=0,
+                scale_format=0)
     base.update(kw)
     return ep.ep_shape(*[int(base[f]) for f in ep.SHAPE_FIELDS])
 
@@ -97,6 +111,9 @@ def _shape(**kw):
     (dict(num_ranks=0), ep.EP_ERR_SHAPE),
     (dict(use_fp8=1, hidden=200), ep.EP_ERR_SHAPE),  # FP8 needs H % 128 == 0
     (dict(use_fp8=2), ep.EP_ERR_SHAPE),
+    (dict(scale_format=1), ep.EP_ERR_SHAPE),                 # scale formats are FP8-only
+    (dict(use_fp8=1, scale_format=3), ep.EP_ERR_SHAPE),
+    (dict(use_fp8=1, scale_format=-1), ep.EP_ERR_SHAPE),
     (dict(num_topk=33), ep.EP_ERR_UNSUPPORTED),
     (dict(num_experts=2048, num_ranks=4), ep.EP_ERR_UNSUPPORTED),
     (dict(num_experts=128, num_ranks=128), ep.EP_ERR_UNSUPPORTED),

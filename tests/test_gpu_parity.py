@@ -24,6 +24,7 @@ pytestmark = pytest.mark.gpu
 
 LAYOUT_KEYS = ("num_tokens_per_rank", "num_tokens_per_expert", "is_token_in_rank", "expert_slot",
                "rank_slot", "expert_offset")
+FORMATS = [ep.EP_SCALE_POW2, ep.EP_SCALE_UE8M0]  # beside the default EP_SCALE_FP32
 
 
 @pytest.fixture(scope="module")
@@ -58,13 +59,13 @@ def check_layout(o, shape, topk_idx, name):
 
 def check_dispatch(o, shape, inp, run, lay, name):
     E, S, H = shape.num_experts, shape.expert_capacity, shape.hidden
-    say(f"ep_dispatch {name} fp8={shape.use_fp8} S={S} H={H}")
+    say(f"ep_dispatch {name} fp8={shape.use_fp8} scale_format={shape.scale_format} S={S} H={H}")
     d = DispatchRun(shape, inp["x_bits"], run.topk_idx, run.expert_slot)
     torch.cuda.synchronize()
     counts = lay["num_tokens_per_expert"]
     s_or = oracle_capacity(counts, S)
     rx, rs, src, st = o.pack(inp["x_bits"], inp["topk_idx"], lay["expert_slot"], E, s_or,
-                             bool(shape.use_fp8))
+                             bool(shape.use_fp8), scale_format=shape.scale_format)
     rows_gpu = written_rows(counts, S)
     rows_or = written_rows(counts, s_or)
     got_x = gather_rows(d.recv_x, rows_gpu)
@@ -74,7 +75,7 @@ def check_dispatch(o, shape, inp, run, lay, name):
     assert np.array_equal(got_src, src.reshape(-1)[rows_or]), (name, "recv_src_idx")
     if shape.use_fp8:
         got_sc = gather_rows(d.recv_scales.view(torch.int32), rows_gpu)
-        want_sc = rs.reshape(E * s_or, H // 128)[rows_or].view(np.int32)
+        want_sc = rs.reshape(E * s_or, rs.shape[-1])[rows_or].view(np.int32)
         assert np.array_equal(got_sc, want_sc), (name, "recv_scales", first_diff(got_sc, want_sc))
         assert unwritten_rows_intact(d.recv_x, counts, POISON_X8)
         assert unwritten_rows_intact(d.recv_scales.view(torch.int32), counts, POISON_SCALE_BITS)
@@ -106,8 +107,8 @@ def check_combine(o, shape, inp, run, lay, y_dev, y_or, s_or, name, weights=None
     return got
 
 
-def check_path(o, w, inp, name):
-    shape = ep.shape_of(w)
+def check_path(o, w, inp, name, scale_format=ep.EP_SCALE_FP32):
+    shape = ep.shape_of(w, scale_format)
     run, lay = check_layout(o, shape, inp["topk_idx"], name)
     check_dispatch(o, shape, inp, run, lay, name)
     E, S, H = w.num_experts, w.expert_capacity, w.hidden
@@ -175,6 +176,14 @@ def test_path_full_size(o, wid):
     check_path(o, w, inp, f"full {w.name}")
 
 
+@pytest.mark.parametrize("fmt", FORMATS, ids=["pow2", "ue8m0"])
+def test_scale_formats_full_size(o, fmt):
+    """4,096 x 7,168 FP8 prefill with power-of-two / UE8M0 scales."""
+    w = W.WORKLOADS[3]
+    inp = W.make_inputs(w, with_expert_rows=True)
+    check_path(o, w, inp, f"full {w.name} fmt={fmt}", scale_format=fmt)
+
+
 def test_path_full_size_large_bf16(o):
     """16,384 x 7,168 BF16, top-6 (the Ascend page's 1.4 GB pass): layout and
     pack bit-exact; the combine with the identity expert (the receive buffer
@@ -190,9 +199,56 @@ def test_path_full_size_large_bf16(o):
     assert np.array_equal(pins.bf16_to_f64(got), pins.bf16_to_f64(inp["x_bits"]))
 
 
+# ------------------------------------------------------- FP8 scale formats
+
+@pytest.mark.parametrize("fmt", FORMATS, ids=["pow2", "ue8m0"])
+@pytest.mark.parametrize("case", [0, 1, 2, 4])  # the FP8 small cases
+def test_scale_formats_small(o, case, fmt):
+    """DeepEP V1 Legacy guide §6.3 round_scale / use_ue8m0: power-of-two
+    scales, as fp32 or as packed 8-bit exponents, bit-exact."""
+    w, inp = small_cases()[case]
+    assert w.use_fp8
+    check_path(o, w, inp, f"small {w.name} fmt={fmt}", scale_format=fmt)
+
+
+@pytest.mark.parametrize("fmt", FORMATS, ids=["pow2", "ue8m0"])
+@pytest.mark.parametrize("H", [128, 384, 640, 1152, 1920])
+def test_scale_formats_ragged_words(o, H, fmt):
+    """Block counts G = H/128 that leave a partly filled UE8M0 word (G % 4 != 0)
+    and chunks whose second half holds no block (H % 1024 <= 512)."""
+    _edge(o, f"H={H} fmt={fmt}", N=130, H=H, K=6, E=32, R=8, use_fp8=True, mask=0.05,
+          scale_format=fmt)
+
+
+@pytest.mark.parametrize("fmt", [ep.EP_SCALE_FP32] + FORMATS, ids=["fp32", "pow2", "ue8m0"])
+def test_scale_formats_exponent_boundaries(o, fmt):
+    """Block maxima at 1.75 * 2^E (the power of two 2^(E-8) is exact: 448
+    times it equals the maximum), one bf16 step above and below it, at plain
+    powers of two, under the 1e-4 floor, and at the extremes of bf16 range:
+    every branch of the exponent rule."""
+    rng = np.random.default_rng(7)
+    N, H = 96, 1024
+    G = H // 128
+    x = rng.uniform(-1.0, 1.0, (N, G, 128)).astype(np.float32)
+    mant = np.array([1.75, 1.75 + 2 ** -7, 1.75 - 2 ** -7, 1.0, 1.5, 1.9921875], np.float32)
+    for t in range(N):
+        for g in range(G):
+            E2 = int(rng.integers(-30, 120))
+            m = mant[(t + g) % mant.size]
+            x[t, g] *= np.float32(m * 2.0 ** (E2 - 1))
+            x[t, g, int(rng.integers(0, 128))] = np.float32((-1) ** t * m * 2.0 ** E2)
+    x[0, 0] = 0.0                   # all-zero block: a' = 1e-4
+    x[1, 1] = 3e-5                  # under the floor
+    x[2, 2, 5] = 3.3895314e38       # largest finite bf16
+    x_bits = W.bf16_bits(x.reshape(N, H))
+    _edge(o, f"exponent boundaries fmt={fmt}", N=N, H=H, K=4, E=16, R=4, use_fp8=True,
+          scale_format=fmt, x_bits=x_bits)
+
+
 # ------------------------------------------------------------------ edge cases
 
-def _edge(o, name, N, H, K, E, R, use_fp8, topk_idx=None, M=None, S=None, seed=0, mask=0.0):
+def _edge(o, name, N, H, K, E, R, use_fp8, topk_idx=None, M=None, S=None, seed=0, mask=0.0,
+          scale_format=ep.EP_SCALE_FP32, x_bits=None):
     rng = np.random.default_rng(seed)
     if topk_idx is None:
         topk_idx = np.argsort(rng.random((N, E)), axis=1)[:, :K].astype(np.int64) if K <= E else \
@@ -202,12 +258,12 @@ def _edge(o, name, N, H, K, E, R, use_fp8, topk_idx=None, M=None, S=None, seed=0
     M = max(N, 1) if M is None else M
     S = M if S is None else S
     w = W.Workload(0, name, N, H, K, E, R, M, S, use_fp8, "uniform")
-    x = W.bf16_bits(rng.standard_normal((N, H), dtype=np.float32))
+    x = W.bf16_bits(rng.standard_normal((N, H), dtype=np.float32)) if x_bits is None else x_bits
     wts = rng.random((N, K)).astype(np.float32)
     P = int((topk_idx >= 0).sum())
     rows = W.bf16_bits(rng.standard_normal((P, H), dtype=np.float32))
     inp = {"x_bits": x, "topk_idx": topk_idx, "topk_weights": wts, "expert_rows": rows}
-    check_path(o, w, inp, name)
+    check_path(o, w, inp, name, scale_format)
 
 
 EDGE = [
