@@ -40,7 +40,7 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak, AMD's published figure
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def algorithmic_bytes(n, h, k, e, r, p, use_fp8):
+def algorithmic_bytes(n, h, k, e, r, p, use_fp8, scale_format=0):
     """Bytes the method must move per call, by phase.
 
     layout : read topk_idx (8 B per entry); write expert_slot (4 B per entry),
@@ -48,12 +48,15 @@ def algorithmic_bytes(n, h, k, e, r, p, use_fp8):
              arrays and the offsets.
     pack   : read x once per token, topk_idx + expert_slot per entry; write
              per valid entry one row (H bytes FP8 or 2H bytes BF16), its
-             source index (4 B) and, for FP8, H/128 fp32 scales.
+             source index (4 B) and, for FP8, H/128 fp32 scales (UE8M0:
+             ceil(H/512) 32-bit words).
     combine: read one bf16 expert row per valid entry and idx + slot + weight
              per entry; write one bf16 output row per token."""
     b = 1 if use_fp8 else 2
     layout = 12 * n * k + 5 * n * r + 4 * (2 * e + r + 1)
-    pack = 2 * n * h + 12 * n * k + p * (b * h + 4 + (4 * (h // 128) if use_fp8 else 0))
+    g = h // 128
+    scale_bytes = 0 if not use_fp8 else 4 * ((g + 3) // 4) if scale_format == 2 else 4 * g
+    pack = 2 * n * h + 12 * n * k + p * (b * h + 4 + scale_bytes)
     combine = 2 * p * h + 16 * n * k + 2 * n * h
     return {"layout": layout, "dispatch": pack, "combine": combine,
             "total": layout + pack + combine}
@@ -268,6 +271,54 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
     }
 
 
+def time_scale_formats(wid, steps, scrub_bytes, say, batch=10):
+    """ep_dispatch alone on workload ``wid`` with each FP8 scale format:
+    ``batch`` back-to-back launches between two events after an untimed
+    eviction, ``steps`` times -> average launch duration."""
+    import torch
+    from combine_ep_layout_02_amd import ep
+    from combine_ep_layout_02_amd import workloads as W
+
+    w = W.WORKLOADS[wid]
+    inp = W.make_inputs(w)
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    topk_idx = torch.from_numpy(inp["topk_idx"]).to(dev)
+    x = torch.from_numpy(inp["x_bits"].view(np.int16)).to(dev)
+    scrub = torch.ones(scrub_bytes // 4, dtype=torch.float32, device=dev) if scrub_bytes else None
+    scrub_out = torch.zeros((), dtype=torch.float32, device=dev)
+    out = {}
+    for fmt, label in ((ep.EP_SCALE_FP32, "fp32"), (ep.EP_SCALE_POW2, "pow2"),
+                       (ep.EP_SCALE_UE8M0, "ue8m0")):
+        shape = ep.shape_of(w, fmt)
+        buf = ep.allocate(shape, dev, parts=("layout", "dispatch"))
+        ep.ep_layout(shape, topk_idx, buf["num_tokens_per_rank"], buf["num_tokens_per_expert"],
+                     buf["is_token_in_rank"], buf["expert_slot"], buf["rank_slot"],
+                     buf["expert_offset"], buf["workspace"], buf["status"])
+        say(f"ep_dispatch {w.name} scale format {label}: {steps} x {batch} launches")
+        times = []
+        for _ in range(steps):
+            if scrub is not None:
+                torch.sum(scrub, dim=0, out=scrub_out)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(batch):
+                ep.ep_dispatch(shape, x, topk_idx, buf["expert_slot"], buf["recv_x"],
+                               buf["recv_scales"], buf["recv_src_idx"], buf["status"])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3 / batch)
+        if int(buf["status"].item()) != 0:
+            raise RuntimeError(f"device status {int(buf['status'].item())}")
+        nb = algorithmic_bytes(w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks,
+                               inp["num_valid"], True, fmt)["dispatch"]
+        us = statistics.fmean(times)
+        out[label] = {"us_mean": round(us, 2), "gbps": round(nb / (us * 1e-6) / 1e9, 1),
+                      "frac_of_peak": round(nb / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+        del buf
+    return out
+
+
 def cpu_baseline(inp, w, reps, say):
     """The CPU oracle as it stands (single-threaded C through its ctypes
     wrapper, allocation of its output arrays included) on the same inputs."""
@@ -307,13 +358,13 @@ def cpu_baseline(inp, w, reps, say):
 PROFILE_COMMANDS = {
     "trace": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -T -f csv "
              "-d $REPO/gpurun_out/prof_trace -o trace -- python3 $REPO/bench.py --steps 30 "
-             "--warmup 5 --no-cpu-baseline --quiet",
+             "--warmup 5 --no-cpu-baseline --no-scale-formats --quiet",
     "FETCH_SIZE": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -T -f csv "
                   "-d $REPO/gpurun_out/prof_FETCH_SIZE -o pmc -- python3 $REPO/bench.py --steps 3 "
-                  "--warmup 1 --no-cpu-baseline --no-decode --quiet",
+                  "--warmup 1 --no-cpu-baseline --no-decode --no-scale-formats --quiet",
     "WRITE_SIZE": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -T -f csv "
                   "-d $REPO/gpurun_out/prof_WRITE_SIZE -o pmc -- python3 $REPO/bench.py --steps 3 "
-                  "--warmup 1 --no-cpu-baseline --no-decode --quiet",
+                  "--warmup 1 --no-cpu-baseline --no-decode --no-scale-formats --quiet",
 }
 
 
@@ -443,6 +494,8 @@ def main():
     ap.add_argument("--cpu-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-scale-formats", action="store_true",
+                    help="skip the ep_dispatch timing per FP8 scale format")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/ summaries from a profiling run's output directory and exit")
@@ -503,6 +556,9 @@ def main():
         "frac_of_peak_whole_step": round(value / PEAK_HBM_GBPS, 4),
         "wall_s_incl_eviction": round(prefill["wall_cold_s"], 4),
     }
+    if not args.no_scale_formats:
+        extra["dispatch_by_scale_format_4096x7168"] = time_scale_formats(
+            3, min(args.steps, 20), scrub_bytes, say)
     if decode is not None:
         extra["decode_128x7168"] = {
             "step_us_cold": decode["cold"], "step_us_cold_hip_graph": decode["graph_cold"],

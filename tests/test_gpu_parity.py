@@ -202,7 +202,7 @@ def test_path_full_size_large_bf16(o):
 # ------------------------------------------------------- FP8 scale formats
 
 @pytest.mark.parametrize("fmt", FORMATS, ids=["pow2", "ue8m0"])
-@pytest.mark.parametrize("case", [0, 1, 2, 4])  # the FP8 small cases
+@pytest.mark.parametrize("case", [1, 2, 4])  # the FP8 small cases
 def test_scale_formats_small(o, case, fmt):
     """DeepEP V1 Legacy guide §6.3 round_scale / use_ue8m0: power-of-two
     scales, as fp32 or as packed 8-bit exponents, bit-exact."""
