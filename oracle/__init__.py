@@ -67,13 +67,25 @@ class Oracle:
         lib.oracle_quantize_rows_pow2.argtypes = [i32, i32, vp, vp, vp]
         lib.oracle_pow2_scale_exponent.argtypes = [ctypes.c_float]
         lib.oracle_pow2_scale_exponent.restype = ctypes.c_int
+        lib.oracle_aligned_offsets.argtypes = [i32, vp, i32, vp]
+        lib.oracle_pack_expand.argtypes = [i32] * 7 + [vp] * 8
+        lib.oracle_pack_expand.restype = ctypes.c_int
+        lib.oracle_combine_expand.argtypes = [i32] * 5 + [vp] * 6
+        lib.oracle_combine_expand.restype = ctypes.c_int
+        lib.oracle_dispatch_normal.argtypes = [i32] * 8 + [vp] * 9
+        lib.oracle_dispatch_normal.restype = ctypes.c_int
+        lib.oracle_combine_normal.argtypes = [i32] * 5 + [vp] * 5
+        lib.oracle_combine_normal.restype = ctypes.c_int
         self.lib = lib
 
     # ------------------------------------------------------------- layout
-    def layout(self, topk_idx: np.ndarray, num_experts: int, num_ranks: int) -> dict:
+    def layout(self, topk_idx: np.ndarray, num_experts: int, num_ranks: int,
+               alignment: int = 1) -> dict:
         """Dispatch layout (DeepEP V1 Legacy guide §5.2(1); Ascend deep dive,
         "Dispatch's Three Phases", phase 2).  ``topk_idx`` int64 [N, K] with -1
-        for masked entries.  Returns counts, mask, slots, offsets, status."""
+        for masked entries.  Returns counts, mask, slots, offsets, status;
+        with ``alignment`` A > 1 the offsets are those of the expand layout
+        (each queue rounded up to a multiple of A; phase 1)."""
         idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
         n, k = idx.shape
         e, r = int(num_experts), int(num_ranks)
@@ -90,6 +102,16 @@ class Oracle:
             _ptr(out["num_tokens_per_expert"]), _ptr(out["is_token_in_rank"]),
             _ptr(out["expert_slot"]), _ptr(out["rank_slot"]), _ptr(out["expert_offset"]))
         out["status"] = int(st)
+        if alignment > 1:
+            out["expert_offset"] = self.aligned_offsets(out["num_tokens_per_expert"], alignment)
+        return out
+
+    def aligned_offsets(self, counts: np.ndarray, alignment: int) -> np.ndarray:
+        """Expand-layout queue starts (Ascend deep dive, "Dispatch's Three
+        Phases", phase 1: queues padded to a multiple of the alignment)."""
+        c = np.ascontiguousarray(counts, dtype=np.int32)
+        out = np.empty(c.size + 1, np.int32)
+        self.lib.oracle_aligned_offsets(c.size, _ptr(c), int(alignment), _ptr(out))
         return out
 
     # --------------------------------------------------------------- pack
@@ -124,6 +146,111 @@ class Oracle:
                                       _ptr(x), _ptr(idx), _ptr(slot), _ptr(recv_x),
                                       _ptr(recv_scales), _ptr(recv_src))
         return recv_x, recv_scales, recv_src, int(st)
+
+    @staticmethod
+    def _recv_buffers(rows: int, h: int, use_fp8: bool, scale_format: int, fill: int):
+        g = h // 128
+        if use_fp8:
+            recv_x = np.full((rows, h), fill & 0xFF, np.uint8)
+            if scale_format == 2:
+                recv_scales = np.full((rows, (g + 3) // 4), 0xDEADBEEF, np.uint32)
+            else:
+                recv_scales = np.full((rows, g), np.nan, np.float32)
+        else:
+            recv_x = np.full((rows, h), fill & 0xFFFF, np.uint16)
+            recv_scales = None
+        return recv_x, recv_scales
+
+    def pack_expand(self, x_bits: np.ndarray, topk_idx: np.ndarray, expert_slot: np.ndarray,
+                    expert_offset: np.ndarray, counts: np.ndarray, rows: int, use_fp8: bool,
+                    fill: int = 0, scale_format: int = 0):
+        """Dispatch pack into the expand layout (Ascend deep dive, "Dispatch's
+        Three Phases", phase 1).  One buffer of ``rows`` rows; returns
+        (recv_x [rows, H], recv_scales, recv_src_idx [rows], status); rows at
+        or past expert_offset[E] keep ``fill`` (-2 for the source index)."""
+        x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
+        slot = np.ascontiguousarray(expert_slot, dtype=np.int32)
+        off = np.ascontiguousarray(expert_offset, dtype=np.int32)
+        cnt = np.ascontiguousarray(counts, dtype=np.int32)
+        n, h = x.shape
+        k = idx.shape[1]
+        e = cnt.size
+        recv_x, recv_scales = self._recv_buffers(rows, h, use_fp8, scale_format, fill)
+        recv_src = np.full(rows, -2, np.int32)
+        st = self.lib.oracle_pack_expand(n, h, k, e, int(rows), int(bool(use_fp8)),
+                                         int(scale_format), _ptr(x), _ptr(idx), _ptr(slot),
+                                         _ptr(off), _ptr(cnt), _ptr(recv_x), _ptr(recv_scales),
+                                         _ptr(recv_src))
+        return recv_x, recv_scales, recv_src, int(st)
+
+    def combine_expand(self, y_bits: np.ndarray, topk_idx: np.ndarray, topk_weights: np.ndarray,
+                       expert_slot: np.ndarray, expert_offset: np.ndarray):
+        """Combine from expert outputs in the expand layout, y_bits [rows, H]."""
+        y = np.ascontiguousarray(y_bits, dtype=np.uint16)
+        idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
+        w = np.ascontiguousarray(topk_weights, dtype=np.float32)
+        slot = np.ascontiguousarray(expert_slot, dtype=np.int32)
+        off = np.ascontiguousarray(expert_offset, dtype=np.int32)
+        n, k = idx.shape
+        rows, h = y.shape
+        out = np.empty((n, h), np.uint16)
+        st = self.lib.oracle_combine_expand(n, h, k, off.size - 1, rows, _ptr(y), _ptr(idx),
+                                            _ptr(w), _ptr(slot), _ptr(off), _ptr(out))
+        return out, int(st)
+
+    def dispatch_normal(self, x_bits: np.ndarray, topk_idx: np.ndarray,
+                        topk_weights: np.ndarray | None, rank_slot: np.ndarray, num_experts: int,
+                        num_ranks: int, rows_per_rank: int, use_fp8: bool, fill: int = 0,
+                        scale_format: int = 0):
+        """Normal-mode dispatch (DeepEP V1 Legacy guide §5.1): one row per
+        (token, rank) in rank-major buffers [R, M, ...].  Returns a dict with
+        recv_x, recv_scales, recv_topk_idx [R, M, K], recv_topk_weights
+        [R, M, K] (None without weights), recv_src_idx [R, M] and status;
+        unwritten rows keep ``fill`` (-2 / -7 / NaN for the metadata)."""
+        x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
+        rs = np.ascontiguousarray(rank_slot, dtype=np.int32)
+        n, h = x.shape
+        k = idx.shape[1]
+        r, m = int(num_ranks), int(rows_per_rank)
+        recv_x, recv_scales = self._recv_buffers(r * m, h, use_fp8, scale_format, fill)
+        out = {
+            "recv_x": recv_x.reshape(r, m, h),
+            "recv_scales": None if recv_scales is None else recv_scales.reshape(r, m, -1),
+            "recv_topk_idx": np.full((r, m, k), -7, np.int64),
+            "recv_topk_weights": None,
+            "recv_src_idx": np.full((r, m), -2, np.int32),
+        }
+        w = None
+        if topk_weights is not None:
+            w = np.ascontiguousarray(topk_weights, dtype=np.float32)
+            out["recv_topk_weights"] = np.full((r, m, k), np.nan, np.float32)
+        st = self.lib.oracle_dispatch_normal(
+            n, h, k, int(num_experts), r, m, int(bool(use_fp8)), int(scale_format), _ptr(x),
+            _ptr(idx), _ptr(w), _ptr(rs), _ptr(recv_x), _ptr(recv_scales),
+            _ptr(out["recv_topk_idx"]), _ptr(out["recv_topk_weights"]), _ptr(out["recv_src_idx"]))
+        out["status"] = int(st)
+        return out
+
+    def combine_normal(self, y_bits: np.ndarray, rank_slot: np.ndarray,
+                       recv_topk_weights: np.ndarray | None = None):
+        """Normal-mode combine (DeepEP V1 Legacy guide §5.1): y_bits [R, M, H]
+        one row per received token; returns (combined bf16 bits [N, H],
+        combined topk weights [N, K] or None, status)."""
+        y = np.ascontiguousarray(y_bits, dtype=np.uint16)
+        rs = np.ascontiguousarray(rank_slot, dtype=np.int32)
+        r, m, h = y.shape
+        n = rs.shape[0]
+        out = np.empty((n, h), np.uint16)
+        rw, cw, k = None, None, 1
+        if recv_topk_weights is not None:
+            rw = np.ascontiguousarray(recv_topk_weights, dtype=np.float32)
+            k = rw.shape[-1]
+            cw = np.empty((n, k), np.float32)
+        st = self.lib.oracle_combine_normal(n, h, k, r, m, _ptr(y), _ptr(rs), _ptr(rw), _ptr(out),
+                                            _ptr(cw))
+        return out, cw, int(st)
 
     def quantize_rows_pow2(self, x_bits: np.ndarray):
         """Power-of-two-scale FP8 payload of each row: (q uint8 [N, H],

@@ -15,9 +15,11 @@
  *         ranks), §6.3 (use_fp8 receive shape; -1 in topk_idx is legal).
  *   [ASC] "DeepEP Ascend Deep Dive" (kongchang.com): "Two Transfers: Dispatch
  *         and Combine" (one copy per destination card; weighted sum at the
- *         origin), "Dispatch's Three Phases and FP8 Compression" (count per
- *         expert and per card; receive-source map; amax -> ratio -> multiply
- *         -> convert).
+ *         origin), "Dispatch's Three Phases and FP8 Compression" (phase 1:
+ *         the expand layout, one clone per routed expert grouped by expert,
+ *         each expert queue zero-padded to a multiple of 128; phase 2: count
+ *         per expert and per card; phase 3: receive-source map; amax -> ratio
+ *         -> multiply -> convert).
  *   [L14] "Lesson 14: DeepSeek DeepEP" (hpc.payai.win): §3 (low-latency call
  *         sketch: fixed-shape receive buffer [local experts, M * ranks,
  *         hidden] and a per-expert count), and the dispatch/combine simulator
@@ -322,41 +324,108 @@ static int32_t scale_words(int32_t G, int32_t fmt)
     return fmt == ORACLE_SCALE_UE8M0 ? (G + 3) / 4 : G;
 }
 
+/* The payload of one token, formed once and copied to each destination: the
+ * FP8 bytes, and the scales as fp32 (G values) or packed UE8M0 (W words). */
+typedef struct {
+    int32_t H, G, W, use_fp8, fmt;
+    uint8_t *q;
+    float *sc;
+    int32_t *ex;
+    uint32_t *packed;
+} payload;
+
+static int payload_init(payload *p, int32_t H, int32_t use_fp8, int32_t fmt)
+{
+    p->H = H;
+    p->G = H / 128;
+    p->W = scale_words(p->G, fmt);
+    p->use_fp8 = use_fp8;
+    p->fmt = fmt;
+    p->q = (uint8_t *)malloc((size_t)H);
+    p->sc = (float *)malloc(sizeof(float) * (size_t)(p->G > 0 ? p->G : 1));
+    p->ex = (int32_t *)malloc(sizeof(int32_t) * (size_t)(p->G > 0 ? p->G : 1));
+    p->packed = (uint32_t *)calloc((size_t)(p->W > 0 ? p->W : 1), sizeof(uint32_t));
+    return p->q && p->sc && p->ex && p->packed;
+}
+
+static void payload_free(payload *p)
+{
+    free(p->q);
+    free(p->sc);
+    free(p->ex);
+    free(p->packed);
+}
+
+/* Quantise token row xt (FP8 only; a BF16 payload is the row itself). */
+static void payload_form(payload *p, const uint16_t *xt)
+{
+    if (!p->use_fp8)
+        return;
+    if (p->fmt == ORACLE_SCALE_FP32) {
+        oracle_quantize_row(p->H, xt, p->q, p->sc);
+        return;
+    }
+    oracle_quantize_row_pow2(p->H, xt, p->q, p->ex);
+    for (int32_t b = 0; b < p->G; ++b)
+        p->sc[b] = (float)ldexp(1.0, p->ex[b]);
+    for (int32_t w = 0; w < p->W; ++w)
+        p->packed[w] = 0;
+    for (int32_t b = 0; b < p->G; ++b)
+        p->packed[b / 4] |= (uint32_t)(p->ex[b] + 127) << (8 * (b % 4));
+}
+
+/* Copy the payload of token row xt into receive row `row`. */
+static void payload_store(const payload *p, const uint16_t *xt, size_t row, void *recv_x,
+                          void *recv_scales)
+{
+    const int32_t H = p->H, G = p->G, W = p->W;
+    if (p->use_fp8) {
+        memcpy((uint8_t *)recv_x + row * H, p->q, (size_t)H);
+        if (p->fmt == ORACLE_SCALE_UE8M0)
+            memcpy((uint32_t *)recv_scales + row * W, p->packed, sizeof(uint32_t) * (size_t)W);
+        else
+            memcpy((float *)recv_scales + row * G, p->sc, sizeof(float) * (size_t)G);
+    } else {
+        memcpy((uint16_t *)recv_x + row * H, xt, sizeof(uint16_t) * (size_t)H);
+    }
+}
+
+/* Zero a receive row and its scales (expand-layout padding). */
+static void payload_zero(const payload *p, size_t row, void *recv_x, void *recv_scales)
+{
+    const int32_t H = p->H;
+    if (p->use_fp8) {
+        memset((uint8_t *)recv_x + row * H, 0, (size_t)H);
+        if (p->fmt == ORACLE_SCALE_UE8M0)
+            memset((uint32_t *)recv_scales + row * p->W, 0, sizeof(uint32_t) * (size_t)p->W);
+        else
+            memset((float *)recv_scales + row * p->G, 0, sizeof(float) * (size_t)p->G);
+    } else {
+        memset((uint16_t *)recv_x + row * H, 0, sizeof(uint16_t) * (size_t)H);
+    }
+}
+
+static int fmt_ok(int32_t H, int32_t use_fp8, int32_t fmt)
+{
+    return !(H < 1 || (use_fp8 && H % 128 != 0) || fmt < 0 || fmt > 2 || (!use_fp8 && fmt != 0));
+}
+
 int oracle_pack_fmt(int32_t N, int32_t H, int32_t K, int32_t E, int32_t S, int32_t use_fp8,
                     int32_t scale_fmt, const uint16_t *x, const int64_t *topk_idx,
                     const int32_t *expert_slot, void *recv_x, void *recv_scales,
                     int32_t *recv_src_idx)
 {
-    if (N < 0 || H < 1 || K < 1 || E < 1 || S < 0 || (use_fp8 && H % 128 != 0) || scale_fmt < 0 ||
-        scale_fmt > 2 || (!use_fp8 && scale_fmt != 0))
+    if (N < 0 || K < 1 || E < 1 || S < 0 || !fmt_ok(H, use_fp8, scale_fmt))
         return ORACLE_BAD_ARGS;
     int status = ORACLE_OK;
-    int32_t G = H / 128;
-    int32_t W = scale_words(G, scale_fmt);
-    uint8_t *q = (uint8_t *)malloc((size_t)H);
-    float *sc = (float *)malloc(sizeof(float) * (size_t)(G > 0 ? G : 1));
-    int32_t *ex = (int32_t *)malloc(sizeof(int32_t) * (size_t)(G > 0 ? G : 1));
-    uint32_t *packed = (uint32_t *)calloc((size_t)(W > 0 ? W : 1), sizeof(uint32_t));
-    if (!q || !sc || !ex || !packed) {
-        free(q);
-        free(sc);
-        free(ex);
-        free(packed);
+    payload p;
+    if (!payload_init(&p, H, use_fp8, scale_fmt)) {
+        payload_free(&p);
         return ORACLE_BAD_ARGS;
     }
     for (int32_t t = 0; t < N; ++t) {
         const uint16_t *xt = x + (size_t)t * H;
-        if (use_fp8 && scale_fmt == ORACLE_SCALE_FP32) {
-            oracle_quantize_row(H, xt, q, sc);
-        } else if (use_fp8) {
-            oracle_quantize_row_pow2(H, xt, q, ex);
-            for (int32_t b = 0; b < G; ++b)
-                sc[b] = (float)ldexp(1.0, ex[b]);
-            for (int32_t w = 0; w < W; ++w)
-                packed[w] = 0;
-            for (int32_t b = 0; b < G; ++b)
-                packed[b / 4] |= (uint32_t)(ex[b] + 127) << (8 * (b % 4));
-        }
+        payload_form(&p, xt);
         for (int32_t k = 0; k < K; ++k) {
             size_t i = (size_t)t * K + k;
             int32_t e = routed_expert(topk_idx[i], E, &status);
@@ -368,22 +437,11 @@ int oracle_pack_fmt(int32_t N, int32_t H, int32_t K, int32_t E, int32_t S, int32
                 continue;
             }
             size_t row = (size_t)e * S + j;
-            if (use_fp8) {
-                memcpy((uint8_t *)recv_x + row * H, q, (size_t)H);
-                if (scale_fmt == ORACLE_SCALE_UE8M0)
-                    memcpy((uint32_t *)recv_scales + row * W, packed, sizeof(uint32_t) * (size_t)W);
-                else
-                    memcpy((float *)recv_scales + row * G, sc, sizeof(float) * (size_t)G);
-            } else {
-                memcpy((uint16_t *)recv_x + row * H, xt, sizeof(uint16_t) * (size_t)H);
-            }
+            payload_store(&p, xt, row, recv_x, recv_scales);
             recv_src_idx[row] = t;
         }
     }
-    free(q);
-    free(sc);
-    free(ex);
-    free(packed);
+    payload_free(&p);
     return status;
 }
 
@@ -438,6 +496,233 @@ int oracle_combine(int32_t N, int32_t H, int32_t K, int32_t E, int32_t S, const 
             combined_x[(size_t)t * H + c] = oracle_bf16_rne(acc[c]);
     }
     free(acc);
+    return status;
+}
+
+/* ---------------------------------------------------- expand layout */
+
+/* Expert alignment ([ASC] "Dispatch's Three Phases", phase 1: each expert's
+ * queue is padded to a multiple of 128 because the grouped GEMM after it
+ * takes only 128-aligned inputs).  With alignment A (A <= 1: none), expert
+ * e's queue holds round_up(count_e, A) rows and starts at
+ *   offset[e] = sum over e' < e of round_up(count_e', A);
+ * offset[E] is the total.  An expert with no tokens gets no rows. */
+void oracle_aligned_offsets(int32_t E, const int32_t *counts, int32_t A, int32_t *offsets)
+{
+    int32_t a = A > 1 ? A : 1;
+    int32_t run = 0;
+    for (int32_t e = 0; e < E; ++e) {
+        offsets[e] = run;
+        run += (counts[e] + a - 1) / a * a;
+    }
+    offsets[E] = run;
+}
+
+/* Dispatch pack into the expand layout ([ASC] phase 1: one clone of the
+ * token per routed expert, grouped by expert, each queue zero-padded; [ASC]
+ * phase 3: the receive-source map).  One buffer of T rows; the clone of
+ * valid entry (t,k) with expert e and slot j sits at row offset[e] + j
+ * (offsets from oracle_aligned_offsets, slots from oracle_layout).  A slot
+ * must fall inside its expert's queue (offset[e] + j < offset[e+1] <= T),
+ * else the entry is skipped and reported.  Padding rows
+ * [offset[e] + counts[e], offset[e+1]) are zero bytes with zero scales and
+ * source -1; rows at or past offset[E] are not written. */
+int oracle_pack_expand(int32_t N, int32_t H, int32_t K, int32_t E, int32_t T, int32_t use_fp8,
+                       int32_t scale_fmt, const uint16_t *x, const int64_t *topk_idx,
+                       const int32_t *expert_slot, const int32_t *expert_offset,
+                       const int32_t *counts, void *recv_x, void *recv_scales,
+                       int32_t *recv_src_idx)
+{
+    if (N < 0 || K < 1 || E < 1 || T < 0 || !fmt_ok(H, use_fp8, scale_fmt))
+        return ORACLE_BAD_ARGS;
+    int status = ORACLE_OK;
+    payload p;
+    if (!payload_init(&p, H, use_fp8, scale_fmt)) {
+        payload_free(&p);
+        return ORACLE_BAD_ARGS;
+    }
+    for (int32_t t = 0; t < N; ++t) {
+        const uint16_t *xt = x + (size_t)t * H;
+        payload_form(&p, xt);
+        for (int32_t k = 0; k < K; ++k) {
+            size_t i = (size_t)t * K + k;
+            int32_t e = routed_expert(topk_idx[i], E, &status);
+            if (e < 0)
+                continue;
+            int64_t row = (int64_t)expert_offset[e] + expert_slot[i];
+            if (expert_slot[i] < 0 || row >= expert_offset[e + 1] || expert_offset[e + 1] > T) {
+                status |= ORACLE_BAD_SLOT;
+                continue;
+            }
+            payload_store(&p, xt, (size_t)row, recv_x, recv_scales);
+            recv_src_idx[row] = t;
+        }
+    }
+    for (int32_t e = 0; e < E; ++e) {
+        for (int64_t row = (int64_t)expert_offset[e] + counts[e]; row < expert_offset[e + 1];
+             ++row) {
+            if (row < 0 || row >= T)
+                continue;
+            payload_zero(&p, (size_t)row, recv_x, recv_scales);
+            recv_src_idx[row] = -1;
+        }
+    }
+    payload_free(&p);
+    return status;
+}
+
+/* Combine from expert outputs in the expand layout: as oracle_combine, with
+ * the output row of entry (t,k) at offset[e] + j of a T-row buffer. */
+int oracle_combine_expand(int32_t N, int32_t H, int32_t K, int32_t E, int32_t T, const uint16_t *y,
+                          const int64_t *topk_idx, const float *topk_weights,
+                          const int32_t *expert_slot, const int32_t *expert_offset,
+                          uint16_t *combined_x)
+{
+    if (N < 0 || H < 1 || K < 1 || E < 1 || T < 0)
+        return ORACLE_BAD_ARGS;
+    int status = ORACLE_OK;
+    float *acc = (float *)malloc(sizeof(float) * (size_t)H);
+    if (!acc)
+        return ORACLE_BAD_ARGS;
+    for (int32_t t = 0; t < N; ++t) {
+        for (int32_t c = 0; c < H; ++c)
+            acc[c] = 0.0f;
+        for (int32_t k = 0; k < K; ++k) {
+            size_t i = (size_t)t * K + k;
+            int32_t e = routed_expert(topk_idx[i], E, &status);
+            if (e < 0)
+                continue;
+            int64_t row = (int64_t)expert_offset[e] + expert_slot[i];
+            if (expert_slot[i] < 0 || row >= expert_offset[e + 1] || expert_offset[e + 1] > T) {
+                status |= ORACLE_BAD_SLOT;
+                continue;
+            }
+            const uint16_t *yr = y + (size_t)row * H;
+            float w = topk_weights[i];
+            for (int32_t c = 0; c < H; ++c)
+                acc[c] = fmaf(w, oracle_bf16_to_f32(yr[c]), acc[c]);
+        }
+        for (int32_t c = 0; c < H; ++c)
+            combined_x[(size_t)t * H + c] = oracle_bf16_rne(acc[c]);
+    }
+    free(acc);
+    return status;
+}
+
+/* ------------------------------------------------------ normal mode */
+
+/* Normal-mode dispatch ([V1] §5.1: dispatch returns recv_x, recv_topk_idx,
+ * recv_topk_weights and the per-expert receive counts; [L14] §2(3) and [ASC]
+ * "Two Transfers": a token crosses to a card once however many of its
+ * experts live there).  Rank r's receive buffer has M rows; token t, if its
+ * rank set holds r, sits at row j = rank_slot[t,r] (from oracle_layout) of
+ * rank r:
+ *   recv_x[r][j]            = the token's payload (formed once per token);
+ *   recv_src_idx[r][j]      = t;
+ *   recv_topk_idx[r][j][k]  = e - r*L if entry (t,k) routes to expert e on
+ *                             rank r (the local expert id), else -1;
+ *   recv_topk_weights[r][j][k] = topk_weights[t,k] for those entries, else 0
+ *                             (skipped when either weight pointer is NULL).
+ * A slot j >= M is skipped and reported; rows j >= num_tokens_per_rank[r]
+ * are not written. */
+int oracle_dispatch_normal(int32_t N, int32_t H, int32_t K, int32_t E, int32_t R, int32_t M,
+                           int32_t use_fp8, int32_t scale_fmt, const uint16_t *x,
+                           const int64_t *topk_idx, const float *topk_weights,
+                           const int32_t *rank_slot, void *recv_x, void *recv_scales,
+                           int64_t *recv_topk_idx, float *recv_topk_weights,
+                           int32_t *recv_src_idx)
+{
+    if (N < 0 || K < 1 || E < 1 || R < 1 || E % R != 0 || M < 0 || !fmt_ok(H, use_fp8, scale_fmt))
+        return ORACLE_BAD_ARGS;
+    int status = ORACLE_OK;
+    const int32_t L = E / R;
+    payload p;
+    if (!payload_init(&p, H, use_fp8, scale_fmt)) {
+        payload_free(&p);
+        return ORACLE_BAD_ARGS;
+    }
+    for (int32_t t = 0; t < N; ++t) {
+        const uint16_t *xt = x + (size_t)t * H;
+        payload_form(&p, xt);
+        for (int32_t r = 0; r < R; ++r) {
+            int32_t j = rank_slot[(size_t)t * R + r];
+            if (j < 0)
+                continue; /* token not sent to rank r */
+            if (j >= M) {
+                status |= ORACLE_BAD_SLOT;
+                continue;
+            }
+            size_t row = (size_t)r * M + j;
+            payload_store(&p, xt, row, recv_x, recv_scales);
+            recv_src_idx[row] = t;
+            for (int32_t k = 0; k < K; ++k) {
+                size_t i = (size_t)t * K + k;
+                int32_t e = routed_expert(topk_idx[i], E, &status);
+                int local = e >= 0 && rank_of(e, E, R) == r;
+                recv_topk_idx[row * K + k] = local ? (int64_t)(e - r * L) : -1;
+                if (topk_weights && recv_topk_weights)
+                    recv_topk_weights[row * K + k] = local ? topk_weights[i] : 0.0f;
+            }
+        }
+    }
+    payload_free(&p);
+    return status;
+}
+
+/* Normal-mode combine ([V1] §5.1: combine takes one row per received token
+ * and the handle, and also reduces a topk_weights tensor of the received
+ * layout; dispatch's backward is such a combine, so the reduction is the
+ * adjoint of dispatch's copy: a plain sum over the ranks the token was sent
+ * to).  Per token t, ranks r ascending with j = rank_slot[t,r] >= 0:
+ *   acc[c]  = acc[c] + float(y[r][j][c])            (from +0; fp32)
+ *   wacc[k] = wacc[k] + recv_topk_weights[r][j][k]  (from +0; fp32)
+ *   combined_x[t][c] = bf16_RNE(acc[c]); combined_topk_weights[t][k] = wacc[k]
+ * (the weight reduction only when both weight pointers are non-NULL).  A
+ * token sent nowhere gets +0. */
+int oracle_combine_normal(int32_t N, int32_t H, int32_t K, int32_t R, int32_t M, const uint16_t *y,
+                          const int32_t *rank_slot, const float *recv_topk_weights,
+                          uint16_t *combined_x, float *combined_topk_weights)
+{
+    if (N < 0 || H < 1 || K < 1 || R < 1 || M < 0)
+        return ORACLE_BAD_ARGS;
+    int status = ORACLE_OK;
+    const int with_w = recv_topk_weights && combined_topk_weights;
+    float *acc = (float *)malloc(sizeof(float) * (size_t)H);
+    float *wacc = (float *)malloc(sizeof(float) * (size_t)K);
+    if (!acc || !wacc) {
+        free(acc);
+        free(wacc);
+        return ORACLE_BAD_ARGS;
+    }
+    for (int32_t t = 0; t < N; ++t) {
+        for (int32_t c = 0; c < H; ++c)
+            acc[c] = 0.0f;
+        for (int32_t k = 0; k < K; ++k)
+            wacc[k] = 0.0f;
+        for (int32_t r = 0; r < R; ++r) {
+            int32_t j = rank_slot[(size_t)t * R + r];
+            if (j < 0)
+                continue;
+            if (j >= M) {
+                status |= ORACLE_BAD_SLOT;
+                continue;
+            }
+            size_t row = (size_t)r * M + j;
+            const uint16_t *yr = y + row * H;
+            for (int32_t c = 0; c < H; ++c)
+                acc[c] = acc[c] + oracle_bf16_to_f32(yr[c]);
+            if (with_w)
+                for (int32_t k = 0; k < K; ++k)
+                    wacc[k] = wacc[k] + recv_topk_weights[row * K + k];
+        }
+        for (int32_t c = 0; c < H; ++c)
+            combined_x[(size_t)t * H + c] = oracle_bf16_rne(acc[c]);
+        if (with_w)
+            for (int32_t k = 0; k < K; ++k)
+                combined_topk_weights[(size_t)t * K + k] = wacc[k];
+    }
+    free(acc);
+    free(wacc);
     return status;
 }
 

@@ -41,6 +41,10 @@ def main(path: str) -> int:
         ("pow2_scales", lambda: pins.pin_pow2_scales(o)),
         ("pow2_dequant_bound", lambda: pins.pin_pow2_dequant_bound(o)),
         ("ue8m0_packing", lambda: pins.pin_ue8m0_packing(o)),
+        ("receive_layouts_golden", lambda: pins.pin_receive_layouts_golden(o)),
+        ("expand_matches_dense", lambda: pins.pin_expand_matches_dense(o, pack_cases)),
+        ("normal_matches_dense", lambda: pins.pin_normal_matches_dense(o, ident_cases)),
+        ("combine_normal_scalar", lambda: pins.pin_combine_normal_scalar_ranks(o, ident_cases)),
         ("layout_bruteforce", lambda: pins.pin_layout_bruteforce(o)),
     ]
     for name, fn in steps:

@@ -583,3 +583,184 @@ def pin_ue8m0_packing(o):
 CHEAP_PINS = ("pin_lesson_example", "pin_bf16", "pin_e4m3fn", "pin_scales_closed_form",
               "pin_dequant_bound", "pin_pack_fp8_is_row_quantiser", "pin_lesson_dense",
               "pin_layout_bad_ids")
+
+
+# ---------------------------------------------------- second receive layouts
+
+def _golden_layouts():
+    with open(os.path.join(GOLDEN, "receive_layouts.json")) as f:
+        return json.load(f)["routings"]
+
+
+def pin_receive_layouts_golden(o):
+    """Hand-derived expand layouts (Ascend deep dive, "Dispatch's Three
+    Phases", phase 1) and normal-mode layouts (V1 guide §5.1) of two small
+    routings (``tests/golden/receive_layouts.json``): queue offsets, the
+    receive-source map, local expert ids, the weights that travel with each
+    row and the weights the normal combine gives back."""
+    for name, rt in _golden_layouts().items():
+        idx = np.array(rt["topk_idx"], np.int64)
+        w = np.array(rt["topk_weights"], np.float32)
+        E = rt["num_experts"]
+        N, K = idx.shape
+        H = 8
+        x = (np.arange(N * H, dtype=np.uint16).reshape(N, H) + 0x3F80)  # distinct bf16 rows
+        for case in rt["expand"]:
+            A = case["alignment"]
+            lay = o.layout(idx, E, 1, alignment=A)
+            assert lay["expert_offset"].tolist() == case["expert_offset"], (name, A, "offsets")
+            rows = len(case["recv_src_idx"])
+            rx, _, src, st = o.pack_expand(x, idx, lay["expert_slot"], lay["expert_offset"],
+                                           lay["num_tokens_per_expert"], rows + 3, False, fill=0x7777)
+            assert st == 0
+            assert src[:rows].tolist() == case["recv_src_idx"], (name, A, "expand src")
+            assert np.all(src[rows:] == -2), (name, A, "rows past the last queue written")
+            for r_, t in enumerate(case["recv_src_idx"]):
+                want = x[t] if t >= 0 else np.zeros(H, np.uint16)
+                assert np.array_equal(rx[r_], want), (name, A, "expand row", r_)
+        for case in rt["normal"]:
+            R = case["num_ranks"]
+            lay = o.layout(idx, E, R)
+            M = N
+            d = o.dispatch_normal(x, idx, w, lay["rank_slot"], E, R, M, False, fill=0x7777)
+            assert d["status"] == 0
+            for r in range(R):
+                cnt = len(case["recv_src_idx"][r])
+                assert int(lay["num_tokens_per_rank"][r]) == cnt
+                assert d["recv_src_idx"][r, :cnt].tolist() == case["recv_src_idx"][r], (name, R, r)
+                assert d["recv_topk_idx"][r, :cnt].tolist() == case["recv_topk_idx"][r], (name, R, r)
+                assert d["recv_topk_weights"][r, :cnt].tolist() == case["recv_topk_weights"][r], (name, R, r)
+                for j, t in enumerate(case["recv_src_idx"][r]):
+                    assert np.array_equal(d["recv_x"][r, j], x[t]), (name, R, r, j)
+                assert np.all(d["recv_src_idx"][r, cnt:] == -2), (name, R, r, "rows past count written")
+            y = d["recv_x"].copy()
+            _, cw, st = o.combine_normal(y, lay["rank_slot"], d["recv_topk_weights"])
+            assert st == 0
+            assert cw.tolist() == case["combined_topk_weights"], (name, R, "combined weights")
+
+
+def pin_expand_matches_dense(o, cases, alignments=(1, 4, 128)):
+    """The expand layout with its padding removed is the per-expert layout
+    (whose pack is pinned above) with the expert queues laid end to end:
+    row offset[e] + j of the expand buffer equals row j of expert e's dense
+    buffer for j < count_e.  Queues are multiples of A and shorter than
+    count_e + A; padding rows are zero with zero scales and source -1.  The
+    combine over expand-placed rows equals the combine over dense-placed
+    rows.  FP8 cases run all three scale formats."""
+    for inp, E, R, S, use_fp8 in cases:
+        idx = inp["topk_idx"]
+        fmts = (0, 1, 2) if use_fp8 else (0,)
+        for A in alignments:
+            lay = o.layout(idx, E, R, alignment=A)
+            cnt = lay["num_tokens_per_expert"].astype(np.int64)
+            off = lay["expert_offset"].astype(np.int64)
+            q = np.diff(off)
+            assert np.all(q % A == 0) and np.all(q >= cnt) and np.all(q < cnt + A)
+            assert np.all((q == 0) == (cnt == 0))
+            rows = int(off[-1]) + 5
+            s_d = max(1, int(cnt.max()) if cnt.size else 1)
+            for fmt in fmts:
+                rx, rs, src, st = o.pack_expand(inp["x_bits"], idx, lay["expert_slot"], off, cnt,
+                                                rows, use_fp8, fill=0x5A5A, scale_format=fmt)
+                dx, ds, dsrc, dst = o.pack(inp["x_bits"], idx, lay["expert_slot"], E, s_d, use_fp8,
+                                           fill=0x5A5A, scale_format=fmt)
+                assert st == dst == 0
+                for e in range(E):
+                    c, b = int(cnt[e]), int(off[e])
+                    assert np.array_equal(rx[b:b + c], dx[e, :c]), (A, fmt, e, "rows")
+                    assert np.array_equal(src[b:b + c], dsrc[e, :c]), (A, fmt, e, "src")
+                    if use_fp8:
+                        assert np.array_equal(rs[b:b + c].view(np.uint32), ds[e, :c].view(np.uint32))
+                    pad = slice(b + c, int(off[e + 1]))
+                    assert np.all(rx[pad] == 0) and np.all(src[pad] == -1), (A, fmt, e, "padding")
+                    if use_fp8:
+                        assert np.all(rs[pad].view(np.uint32) == 0), (A, fmt, e, "padding scales")
+                assert np.all(src[int(off[-1]):] == -2), "rows past the last queue written"
+            # combine: same rows placed in both layouts
+            P = int((idx >= 0).sum())
+            yrows = inp.get("expert_rows")
+            if yrows is None or yrows.shape[0] != P:
+                continue
+            y_dense = place_rows(yrows, idx, lay["expert_slot"], E, s_d)
+            y_exp = np.zeros((rows, yrows.shape[1]), np.uint16)
+            for e in range(E):
+                c, b = int(cnt[e]), int(off[e])
+                y_exp[b:b + c] = y_dense[e, :c]
+            got, st1 = o.combine_expand(y_exp, idx, inp["topk_weights"], lay["expert_slot"], off)
+            want, st2 = o.combine(y_dense, idx, inp["topk_weights"], lay["expert_slot"], E, s_d)
+            assert st1 == st2 and np.array_equal(got, want), (A, "combine expand vs dense")
+
+
+def pin_normal_matches_dense(o, cases):
+    """Normal-mode dispatch against the per-expert pack (pinned above) and
+    the routing itself: the row of token t at rank r holds the same payload
+    as t's rows in the per-expert layout; every valid entry (t,k) appears as
+    local id e - r(e)*L in exactly the row of rank r(e) and as -1 in the
+    token's other rows; its weight travels only there.  FP8 cases run all
+    three scale formats."""
+    for inp, E, R, S, use_fp8 in cases:
+        idx, w = inp["topk_idx"], inp["topk_weights"]
+        N, K = idx.shape
+        L = E // R
+        lay = o.layout(idx, E, R)
+        M = max(N, 1)
+        s_d = max(1, int(lay["num_tokens_per_expert"].max()))
+        for fmt in ((0, 1, 2) if use_fp8 else (0,)):
+            d = o.dispatch_normal(inp["x_bits"], idx, w, lay["rank_slot"], E, R, M, use_fp8,
+                                  fill=0x5A5A, scale_format=fmt)
+            dx, ds, dsrc, _ = o.pack(inp["x_bits"], idx, lay["expert_slot"], E, s_d, use_fp8,
+                                     fill=0x5A5A, scale_format=fmt)
+            assert d["status"] == 0
+            seen = np.zeros((N, K), np.int64)
+            for r in range(R):
+                cnt = int(lay["num_tokens_per_rank"][r])
+                src = d["recv_src_idx"][r, :cnt]
+                assert np.all(np.diff(src) > 0), "rows of a rank are in token order"
+                assert np.all(d["recv_src_idx"][r, cnt:] == -2)
+                for j, t in enumerate(src):
+                    ks = [k for k in range(K) if idx[t, k] >= 0]
+                    assert ks, "a row for a token with no expert"
+                    e0, j0 = int(idx[t, ks[0]]), int(lay["expert_slot"][t, ks[0]])
+                    assert np.array_equal(d["recv_x"][r, j], dx[e0, j0]), (fmt, r, j)
+                    if use_fp8:
+                        assert np.array_equal(d["recv_scales"][r, j].view(np.uint32),
+                                              ds[e0, j0].view(np.uint32))
+                    for k in range(K):
+                        e = int(idx[t, k])
+                        got = int(d["recv_topk_idx"][r, j, k])
+                        if e >= 0 and e // L == r:
+                            assert got + r * L == e
+                            assert d["recv_topk_weights"][r, j, k] == w[t, k]
+                            seen[t, k] += 1
+                        else:
+                            assert got == -1 and d["recv_topk_weights"][r, j, k] == 0.0
+            assert np.array_equal(seen, (idx >= 0).astype(np.int64)), "each entry in exactly one row"
+
+
+def pin_combine_normal_scalar_ranks(o, cases):
+    """Normal combine with a scalar "rank" map: the row a token gets back from
+    rank r is c_r times its own bf16 row, c_r = 2^((r mod 5) - 2).  The fp32
+    sum over the token's ranks is exact, so the output is bf16_RNE((sum c_r)
+    x) computed in float64 and rounded by torch.  The combined weights equal
+    topk_weights on valid entries and 0 on masked ones."""
+    for inp, E, R, S, use_fp8 in cases:
+        idx, w = inp["topk_idx"], inp["topk_weights"]
+        N, K = idx.shape
+        lay = o.layout(idx, E, R)
+        M = max(N, 1)
+        d = o.dispatch_normal(inp["x_bits"], idx, w, lay["rank_slot"], E, R, M, False)
+        c = np.exp2((np.arange(R) % 5) - 2.0)
+        xv = bf16_to_f64(inp["x_bits"])
+        y = np.zeros((R, M, xv.shape[1]), np.uint16)
+        for r in range(R):
+            cnt = int(lay["num_tokens_per_rank"][r])
+            t = d["recv_src_idx"][r, :cnt]
+            y[r, :cnt] = torch.from_numpy((xv[t] * c[r]).astype(np.float32)).to(torch.bfloat16) \
+                .view(torch.int16).numpy().view(np.uint16)
+        got, cw, st = o.combine_normal(y, lay["rank_slot"], d["recv_topk_weights"])
+        assert st == 0
+        mult = (lay["is_token_in_rank"].astype(np.float64) * c[None, :]).sum(axis=1)
+        want = torch.from_numpy((xv * mult[:, None]).astype(np.float32)).to(torch.bfloat16) \
+            .view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(bf16_to_f64(got), bf16_to_f64(want)), "normal combine != (sum c_r) x"
+        assert np.array_equal(cw, np.where(idx >= 0, w, 0.0).astype(np.float32))

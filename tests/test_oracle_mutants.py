@@ -18,6 +18,16 @@ import oracle
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 # (name, [(exact text in ep_oracle.c, replacement), ...])
+COMBINE_YR = "const uint16_t *yr = y + ((size_t)e * S + j) * H;\n            float w = topk_weights[i];"
+COMBINE_FMA = "\n            for (int32_t c = 0; c < H; ++c)\n                acc[c] = fmaf(w, oracle_bf16_to_f32(yr[c]), acc[c]);"
+COMBINE_INIT = ("            acc[c] = 0.0f;\n        for (int32_t k = 0; k < K; ++k) {\n"
+                "            size_t i = (size_t)t * K + k;\n"
+                "            int32_t e = routed_expert(topk_idx[i], E, &status);\n"
+                "            if (e < 0)\n                continue;\n            int32_t j = expert_slot[i];")
+PACK_STORE = "size_t row = (size_t)e * S + j;\n            payload_store(&p, xt, row, recv_x, recv_scales);\n"
+NORMAL_ROW = "size_t row = (size_t)r * M + j;\n            payload_store(&p, xt, row, recv_x, recv_scales);"
+NORMAL_COMBINE_ROW = "size_t row = (size_t)r * M + j;\n            const uint16_t *yr = y + row * H;"
+
 MUTANTS = [
     ("slot_off_by_one", [("expert_slot[i] = num_tokens_per_expert[e];",
                           "expert_slot[i] = num_tokens_per_expert[e] + 1;")]),
@@ -41,17 +51,43 @@ MUTANTS = [
     ("no_amax_floor", [("return (a > 1e-4f) ? a : 1e-4f;", "return (a > 0.0f) ? a : 1.0f;")]),
     ("amax_signed", [("float m = fabsf(oracle_bf16_to_f32(xb[c]));",
                       "float m = oracle_bf16_to_f32(xb[c]);")]),
-    ("fma_operands_swapped", [("acc[c] = fmaf(w, oracle_bf16_to_f32(yr[c]), acc[c]);",
-                               "acc[c] = fmaf(w, acc[c], oracle_bf16_to_f32(yr[c]));")]),
-    ("weight_of_first_k", [("float w = topk_weights[i];", "float w = topk_weights[(size_t)t * K];")]),
-    ("combine_acc_negzero", [("            acc[c] = 0.0f;", "            acc[c] = -0.0f;")]),
-    ("src_idx_is_k", [("recv_src_idx[row] = t;", "recv_src_idx[row] = k;")]),
-    ("scales_row_stride", [("memcpy((float *)recv_scales + row * G, sc", "memcpy((float *)recv_scales + row, sc")]),
+    ("fma_operands_swapped", [(COMBINE_YR + COMBINE_FMA, COMBINE_YR + COMBINE_FMA.replace(
+        "fmaf(w, oracle_bf16_to_f32(yr[c]), acc[c])", "fmaf(w, acc[c], oracle_bf16_to_f32(yr[c]))"))]),
+    ("weight_of_first_k", [(COMBINE_YR, COMBINE_YR.replace("topk_weights[i]", "topk_weights[(size_t)t * K]"))]),
+    ("combine_acc_negzero", [(COMBINE_INIT, COMBINE_INIT.replace("acc[c] = 0.0f;", "acc[c] = -0.0f;"))]),
+    ("src_idx_is_k", [(PACK_STORE + "            recv_src_idx[row] = t;",
+                       PACK_STORE + "            recv_src_idx[row] = k;")]),
+    ("scales_row_stride", [("memcpy((float *)recv_scales + row * G, p->sc",
+                            "memcpy((float *)recv_scales + row, p->sc")]),
     ("dequant_wrong_block", [("float v = qv * scales[c / 128];", "float v = qv * scales[c % (H / 128)];")]),
     ("pow2_steps_past_equality", [("while (ldexp(448.0, e) < (double)ap)", "while (ldexp(448.0, e) <= (double)ap)")]),
     ("pow2_search_starts_high", [("    e -= 9;", "    e -= 7;")]),
-    ("ue8m0_bias_128", [("(uint32_t)(ex[b] + 127) << (8 * (b % 4))", "(uint32_t)(ex[b] + 128) << (8 * (b % 4))")]),
+    ("ue8m0_bias_128", [("(uint32_t)(p->ex[b] + 127) << (8 * (b % 4))", "(uint32_t)(p->ex[b] + 128) << (8 * (b % 4))")]),
     ("ue8m0_byte_order", [("<< (8 * (b % 4))", "<< (8 * (3 - b % 4))")]),
+    # expand layout (Ascend deep dive, phase 1)
+    ("aligned_floor", [("run += (counts[e] + a - 1) / a * a;", "run += counts[e] / a * a;")]),
+    ("aligned_pads_full_queues", [("run += (counts[e] + a - 1) / a * a;", "run += (counts[e] / a + 1) * a;")]),
+    ("expand_padding_not_zeroed", [("payload_zero(&p, (size_t)row, recv_x, recv_scales);", "")]),
+    ("expand_padding_src_zero", [("recv_src_idx[row] = -1;", "recv_src_idx[row] = 0;")]),
+    ("expand_next_queue", [("int64_t row = (int64_t)expert_offset[e] + expert_slot[i];\n"
+                            "            if (expert_slot[i] < 0 || row >= expert_offset[e + 1] || expert_offset[e + 1] > T) {\n"
+                            "                status |= ORACLE_BAD_SLOT;\n                continue;\n            }\n"
+                            "            payload_store",
+                            "int64_t row = (int64_t)expert_offset[e] + expert_slot[i] + 1;\n"
+                            "            if (expert_slot[i] < 0 || row > expert_offset[e + 1] || expert_offset[e + 1] > T) {\n"
+                            "                status |= ORACLE_BAD_SLOT;\n                continue;\n            }\n"
+                            "            payload_store")]),
+    # normal mode ([V1] §5.1)
+    ("normal_global_ids", [("local ? (int64_t)(e - r * L) : -1;", "local ? (int64_t)e : -1;")]),
+    ("normal_weights_not_masked", [("recv_topk_weights[row * K + k] = local ? topk_weights[i] : 0.0f;",
+                                    "recv_topk_weights[row * K + k] = topk_weights[i];")]),
+    ("normal_row_transposed", [(NORMAL_ROW, NORMAL_ROW.replace("(size_t)r * M + j", "(size_t)j * R + r"))]),
+    ("normal_combine_row_transposed", [(NORMAL_COMBINE_ROW,
+                                        NORMAL_COMBINE_ROW.replace("(size_t)r * M + j", "(size_t)j * R + r"))]),
+    ("normal_combine_overwrites", [("acc[c] = acc[c] + oracle_bf16_to_f32(yr[c]);",
+                                    "acc[c] = oracle_bf16_to_f32(yr[c]);")]),
+    ("normal_weights_overwrite", [("wacc[k] = wacc[k] + recv_topk_weights[row * K + k];",
+                                   "wacc[k] = recv_topk_weights[row * K + k];")]),
 ]
 
 

@@ -141,3 +141,29 @@ def test_pow2_scales(o):
 
 def test_ue8m0_packing(o):
     pins.pin_ue8m0_packing(o)
+
+
+def _pack_cases(dead=False):
+    cases = []
+    for w, inp in small_cases():
+        cases.append((inp, w.num_experts, w.num_ranks, w.expert_capacity, w.use_fp8))
+        if dead:
+            cases.append((with_dead_tokens(inp), w.num_experts, w.num_ranks, w.expert_capacity,
+                          w.use_fp8))
+    return cases
+
+
+def test_receive_layouts_golden(o):
+    pins.pin_receive_layouts_golden(o)
+
+
+def test_expand_layout_matches_dense(o):
+    pins.pin_expand_matches_dense(o, _pack_cases())
+
+
+def test_normal_layout_matches_dense(o):
+    pins.pin_normal_matches_dense(o, _pack_cases(dead=True))
+
+
+def test_normal_combine_scalar_ranks(o):
+    pins.pin_combine_normal_scalar_ranks(o, _pack_cases(dead=True))
