@@ -1,31 +1,37 @@
-// dispatch.hip -- dispatch pack on gfx950.
+// dispatch.hip -- dispatch pack on gfx950, into three receive layouts.
 //
-// Writes each token into the fixed-shape per-expert receive buffers (Lesson 14
-// §3 and DeepEP V1 Legacy guide §6.3: data [local experts, M * ranks, hidden]
-// with a count per local expert), optionally as FP8 E4M3FN with one fp32
-// scale per 128 channels (V1 guide §5.2(6); Ascend deep dive, "Dispatch's
-// Three Phases and FP8 Compression": amax, ratio, multiply, convert, ship the
-// scale with the token).
+// Writes each token into receive buffers, optionally as FP8 E4M3FN with one
+// scale per 128 channels (DeepEP V1 Legacy guide §5.2(6); DeepEP Ascend deep
+// dive, "Dispatch's Three Phases and FP8 Compression": amax, ratio, multiply,
+// convert, ship the scale with the token):
+//  - per-expert rows [E, S, H] (Lesson 14 §3 and V1 guide §6.3: data
+//    [local experts, M * ranks, hidden] with a count per local expert);
+//  - the expand layout (Ascend deep dive, phase 1): one clone per routed
+//    expert in one buffer, expert queues zero-padded to the alignment;
+//  - normal mode (V1 guide §5.1): one row per (token, rank) in rank-major
+//    buffers, with the token's routing entries as local expert ids and the
+//    weights that travel with the row.
 //
 // Work item = one wave on one (token, 1024-channel chunk).  The wave reads its
 // chunk of x once (16-byte non-temporal loads: x is read exactly once),
-// quantises it once in registers, then stores
-// it to every valid destination row of the token (topk_idx / expert_slot are
-// wave-uniform scalar loads).  HBM traffic is therefore one read of x and one
-// write per (token, expert) entry, the minimum for this receive layout.
+// quantises it once in registers, then stores it to every destination row of
+// the token.  HBM traffic is therefore one read of x and one write per
+// destination row, the minimum for each layout.
 //
 // FP8 lane map: 8 lanes per 128-channel block, 16 channels (32 bytes of bf16
 // in, 16 bytes of FP8 out) per lane; the block amax is a 3-step xor-shuffle
 // reduction over the 8 lanes.  The block scale is a'/448 or, for the
-// power-of-two formats (DeepEP V1 Legacy guide §6.3, round_scale and
-// use_ue8m0), 2^e with e read off the exponent and mantissa bits of a'; the
-// packed UE8M0 word of blocks 4w..4w+3 is gathered by shuffles into the first
-// lane of block 4w.  BF16 lane map: two 16-byte units per lane (unit = 8
-// channels), so each store instruction covers 1 KiB contiguous.
+// power-of-two formats (V1 guide §6.3, round_scale and use_ue8m0), 2^e with e
+// read off the exponent and mantissa bits of a'; the packed UE8M0 word of
+// blocks 4w..4w+3 is gathered by shuffles into the first lane of block 4w.
+// BF16 lane map: two 16-byte units per lane (unit = 8 channels), so each store
+// instruction covers 1 KiB contiguous.
 //
-// Destinations are taken KB entries at a time: the (expert id, slot) pairs
-// arrive together (one vector load per lane, broadcast with readlane), and
-// the stores of the batch follow back to back.
+// Per-expert and expand destinations are taken KB entries at a time: the
+// (expert id, slot) pairs arrive together (one vector load per lane,
+// broadcast with readlane), and the stores of the batch follow back to back.
+// Normal-mode destinations are the set bits of a ballot over the token's
+// rank_slot row.
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -48,28 +54,41 @@ __device__ __forceinline__ int pow2_scale_exponent(float ap)
 
 __device__ __forceinline__ float exp2_int(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
 
-template <int KB, int SF>
-__global__ __launch_bounds__(kThreads) void pack_fp8_kernel(
-    int32_t N, int32_t H, int32_t K, int32_t E, int32_t S, int32_t nchunks,
-    const uint16_t *__restrict__ x, const int64_t *__restrict__ topk_idx,
-    const int32_t *__restrict__ expert_slot, uint8_t *__restrict__ recv_x,
-    void *__restrict__ recv_scales_raw, int32_t *__restrict__ recv_src_idx, uint32_t *status)
-{
-    const int lane = threadIdx.x & 63;
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t item = blockIdx.x * kWaves + wave; // host keeps N * nchunks < 2^31
-    if (item >= (uint32_t)N * (uint32_t)nchunks)
-        return;
-    const uint32_t t = item / (uint32_t)nchunks;
-    const int32_t chunk = (int32_t)(item - t * (uint32_t)nchunks);
-    const int32_t G = H / 128;
-    const int32_t g = chunk * (kChunk / 128) + (lane >> 3);
-    const bool active = g < G;
-    const int32_t ch = g * 128 + (lane & 7) * 16;
+// Where one lane's FP8 output of a (token, chunk) goes in a receive row.
+struct Fp8Lane {
+    int32_t G, W;   // scale blocks per row; UE8M0 words per row
+    int32_t g, ch;  // this lane's block and first channel
+    bool active;    // g < G
+    bool word_lane; // first lane of blocks 4w..4w+3 with w < W
+};
 
+__device__ __forceinline__ Fp8Lane fp8_lane(int32_t H, int32_t chunk, int lane)
+{
+    Fp8Lane l;
+    l.G = H / 128;
+    l.W = (l.G + 3) / 4;
+    l.g = chunk * (kChunk / 128) + (lane >> 3);
+    l.active = l.g < l.G;
+    l.ch = l.g * 128 + (lane & 7) * 16;
+    l.word_lane = (lane & 31) == 0 && (l.g >> 2) < l.W;
+    return l;
+}
+
+// The FP8 payload of one lane: 16 E4M3FN bytes, its block's fp32 scale and,
+// for UE8M0, the packed exponent word (meaningful on word lanes).
+struct Fp8Payload {
+    uint4 q;
+    float scale;
+    uint32_t ue8m0_word;
+};
+
+template <int SF>
+__device__ __forceinline__ Fp8Payload quantize_lane(const uint16_t *__restrict__ x_row,
+                                                    const Fp8Lane &l, int lane)
+{
     uint4 in0 = make_uint4(0, 0, 0, 0), in1 = make_uint4(0, 0, 0, 0);
-    if (active) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)t * H + ch);
+    if (l.active) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(x_row + l.ch);
         in0 = load_stream(src);
         in1 = load_stream(src + 1);
     }
@@ -88,36 +107,155 @@ __global__ __launch_bounds__(kThreads) void pack_fp8_kernel(
     amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
     amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
     const float ap = fmaxf(amax, 1e-4f);
-    float inv, scale;
+    Fp8Payload p;
+    float inv;
     int e2 = 0;
     if (SF == EP_SCALE_FP32) {
-        inv = 448.0f / ap;   // correctly rounded fp32 division
-        scale = ap / 448.0f; // correctly rounded fp32 division
+        inv = 448.0f / ap;     // correctly rounded fp32 division
+        p.scale = ap / 448.0f; // correctly rounded fp32 division
     } else {
         e2 = pow2_scale_exponent(ap); // in [-22, 120] for finite input
         inv = exp2_int(-e2);
-        scale = exp2_int(e2);
+        p.scale = exp2_int(e2);
     }
-    // UE8M0: the first lane of every 4 blocks packs their 4 exponent bytes
-    // (bytes of blocks past the row end are 0)
-    uint32_t ue8m0_word = 0;
-    const int32_t W = (G + 3) / 4;
-    const bool word_lane = (lane & 31) == 0 && (g >> 2) < W;
+    p.ue8m0_word = 0;
     if (SF == EP_SCALE_UE8M0) {
-        const uint32_t byte = active ? (uint32_t)(e2 + 127) : 0u;
-        ue8m0_word = byte | ((uint32_t)__shfl(byte, lane + 8, 64) << 8) |
-                     ((uint32_t)__shfl(byte, lane + 16, 64) << 16) |
-                     ((uint32_t)__shfl(byte, lane + 24, 64) << 24);
+        // bytes of blocks past the row end are 0
+        const uint32_t byte = l.active ? (uint32_t)(e2 + 127) : 0u;
+        p.ue8m0_word = byte | ((uint32_t)__shfl(byte, lane + 8, 64) << 8) |
+                       ((uint32_t)__shfl(byte, lane + 16, 64) << 16) |
+                       ((uint32_t)__shfl(byte, lane + 24, 64) << 24);
     }
     float v[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i)
         v[i] = clamp448(f[i] * inv);
-    uint4 q;
-    q.x = e4m3fn_x4_hw(v[0], v[1], v[2], v[3]);
-    q.y = e4m3fn_x4_hw(v[4], v[5], v[6], v[7]);
-    q.z = e4m3fn_x4_hw(v[8], v[9], v[10], v[11]);
-    q.w = e4m3fn_x4_hw(v[12], v[13], v[14], v[15]);
+    p.q.x = e4m3fn_x4_hw(v[0], v[1], v[2], v[3]);
+    p.q.y = e4m3fn_x4_hw(v[4], v[5], v[6], v[7]);
+    p.q.z = e4m3fn_x4_hw(v[8], v[9], v[10], v[11]);
+    p.q.w = e4m3fn_x4_hw(v[12], v[13], v[14], v[15]);
+    return p;
+}
+
+// One lane's share of an FP8 receive row (bytes and scales).
+template <int SF>
+__device__ __forceinline__ void store_fp8(const Fp8Payload &p, const Fp8Lane &l, int lane,
+                                          int64_t row, int32_t H, uint8_t *__restrict__ recv_x,
+                                          void *__restrict__ recv_scales)
+{
+    if (l.active)
+        *reinterpret_cast<uint4 *>(recv_x + (size_t)row * H + l.ch) = p.q;
+    if (SF == EP_SCALE_UE8M0) {
+        if (l.word_lane)
+            static_cast<uint32_t *>(recv_scales)[(size_t)row * l.W + (l.g >> 2)] = p.ue8m0_word;
+    } else if (l.active && (lane & 7) == 0) {
+        static_cast<float *>(recv_scales)[(size_t)row * l.G + l.g] = p.scale;
+    }
+}
+
+// Where one lane's BF16 units of a (token, chunk) lie.
+struct Bf16Lane {
+    int32_t u0, u1, units;
+};
+
+__device__ __forceinline__ Bf16Lane bf16_lane(int32_t H, int32_t chunk, int lane)
+{
+    Bf16Lane l;
+    l.units = H / 8;
+    l.u0 = chunk * (kChunk / 8) + lane;
+    l.u1 = l.u0 + 64;
+    return l;
+}
+
+__device__ __forceinline__ void store_bf16(const uint4 &a0, const uint4 &a1, const Bf16Lane &l,
+                                           int64_t row, int32_t H, uint16_t *__restrict__ recv_x)
+{
+    uint4 *dst = reinterpret_cast<uint4 *>(recv_x + (size_t)row * H);
+    if (l.u0 < l.units)
+        dst[l.u0] = a0;
+    if (l.u1 < l.units)
+        dst[l.u1] = a1;
+}
+
+// Expand-layout padding (Ascend deep dive, phase 1: the empty slots of a
+// queue are zeros): rows [offset[e] + count[e], offset[e+1]) below T get zero
+// bytes, zero scales and source -1, one (expert, chunk) per wave.
+template <bool FP8, int SF>
+__device__ void zero_padding(int32_t e, int32_t chunk, int lane, int32_t H,
+                             const int32_t *__restrict__ offset, const int32_t *__restrict__ counts,
+                             int64_t T, void *__restrict__ recv_x, void *__restrict__ recv_scales,
+                             int32_t *__restrict__ recv_src_idx)
+{
+    const int64_t first = max((int64_t)offset[e] + counts[e], (int64_t)0);
+    const int64_t end = min((int64_t)offset[e + 1], T);
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    if (FP8) {
+        const Fp8Lane l = fp8_lane(H, chunk, lane);
+        Fp8Payload p;
+        p.q = z;
+        p.scale = 0.0f;
+        p.ue8m0_word = 0;
+        for (int64_t row = first; row < end; ++row) {
+            store_fp8<SF>(p, l, lane, row, H, static_cast<uint8_t *>(recv_x), recv_scales);
+            if (chunk == 0 && lane == 0)
+                recv_src_idx[row] = -1;
+        }
+    } else {
+        const Bf16Lane l = bf16_lane(H, chunk, lane);
+        for (int64_t row = first; row < end; ++row) {
+            store_bf16(z, z, l, row, H, static_cast<uint16_t *>(recv_x));
+            if (chunk == 0 && lane == 0)
+                recv_src_idx[row] = -1;
+        }
+    }
+}
+
+// Per-expert / expand pack.  Items [0, pad_items) zero the expand padding,
+// one per (expert, chunk) (pad_items = 0 for the per-expert layout); the rest
+// are (token, chunk) items.  Padding items come first so that their longer
+// loops start early.
+template <int KB, int SF, bool FP8, class Rows>
+__global__ __launch_bounds__(kThreads) void pack_kernel(
+    int32_t N, int32_t H, int32_t K, int32_t E, int32_t nchunks, int32_t pad_items, Rows rows,
+    const int32_t *__restrict__ counts, const uint16_t *__restrict__ x,
+    const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ expert_slot,
+    void *__restrict__ recv_x, void *__restrict__ recv_scales, int32_t *__restrict__ recv_src_idx,
+    uint32_t *status)
+{
+    const int lane = threadIdx.x & 63;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    uint32_t item = blockIdx.x * kWaves + wave; // host keeps the item count < 2^31
+    if (item < (uint32_t)pad_items) {
+        if constexpr (__is_same(Rows, ExpandRows)) {
+            const int32_t e = (int32_t)(item / (uint32_t)nchunks);
+            const int32_t chunk = (int32_t)(item - (uint32_t)e * (uint32_t)nchunks);
+            zero_padding<FP8, SF>(e, chunk, lane, H, rows.offset, counts, rows.T, recv_x,
+                                  recv_scales, recv_src_idx);
+        }
+        return;
+    }
+    item -= (uint32_t)pad_items;
+    if (item >= (uint32_t)N * (uint32_t)nchunks)
+        return;
+    const uint32_t t = item / (uint32_t)nchunks;
+    const int32_t chunk = (int32_t)(item - t * (uint32_t)nchunks);
+    const uint16_t *x_row = x + (size_t)t * H;
+
+    Fp8Lane fl;
+    Fp8Payload p;
+    Bf16Lane bl;
+    uint4 a0 = make_uint4(0, 0, 0, 0), a1 = make_uint4(0, 0, 0, 0);
+    if (FP8) {
+        fl = fp8_lane(H, chunk, lane);
+        p = quantize_lane<SF>(x_row, fl, lane);
+    } else {
+        bl = bf16_lane(H, chunk, lane);
+        const uint4 *src = reinterpret_cast<const uint4 *>(x_row);
+        if (bl.u0 < bl.units)
+            a0 = load_stream(src + bl.u0);
+        if (bl.u1 < bl.units)
+            a1 = load_stream(src + bl.u1);
+    }
 
     uint32_t flags = 0;
     const int64_t *idx_t = topk_idx + (size_t)t * K;
@@ -125,19 +263,15 @@ __global__ __launch_bounds__(kThreads) void pack_fp8_kernel(
     for (int k0 = 0; k0 < K; k0 += KB) {
         int64_t row[KB];
         float unused[KB];
-        fetch_entries<KB>(idx_t, slot_t, nullptr, k0, K, E, S, lane, row, unused, flags);
+        fetch_entries<KB>(idx_t, slot_t, nullptr, k0, K, E, rows, lane, row, unused, flags);
 #pragma unroll
         for (int b = 0; b < KB; ++b) {
             if (row[b] >= 0) {
-                if (active)
-                    *reinterpret_cast<uint4 *>(recv_x + (size_t)row[b] * H + ch) = q;
-                if (SF == EP_SCALE_UE8M0) {
-                    if (word_lane)
-                        static_cast<uint32_t *>(recv_scales_raw)[(size_t)row[b] * W + (g >> 2)] =
-                            ue8m0_word;
-                } else if (active && (lane & 7) == 0) {
-                    static_cast<float *>(recv_scales_raw)[(size_t)row[b] * G + g] = scale;
-                }
+                if (FP8)
+                    store_fp8<SF>(p, fl, lane, row[b], H, static_cast<uint8_t *>(recv_x),
+                                  recv_scales);
+                else
+                    store_bf16(a0, a1, bl, row[b], H, static_cast<uint16_t *>(recv_x));
                 if (chunk == 0 && lane == 0)
                     recv_src_idx[row[b]] = (int32_t)t;
             }
@@ -147,11 +281,19 @@ __global__ __launch_bounds__(kThreads) void pack_fp8_kernel(
         atomicOr(status, flags);
 }
 
-template <int KB>
-__global__ __launch_bounds__(kThreads) void pack_bf16_kernel(
-    int32_t N, int32_t H, int32_t K, int32_t E, int32_t S, int32_t nchunks,
+// Normal-mode pack: the token's destinations are the ranks r with
+// 0 <= rank_slot[t, r] < M, row r * M + rank_slot[t, r].  The chunk-0 wave
+// also writes the row's routing entries: lane k < K writes
+//   recv_topk_idx[row][k]     = e - r * L if entry k routes to expert e on r,
+//                               else -1;
+//   recv_topk_weights[row][k] = topk_weights[t][k] for those entries, else 0.
+template <int SF, bool FP8>
+__global__ __launch_bounds__(kThreads) void pack_normal_kernel(
+    int32_t N, int32_t H, int32_t K, int32_t E, int32_t R, int32_t M, int32_t nchunks,
     const uint16_t *__restrict__ x, const int64_t *__restrict__ topk_idx,
-    const int32_t *__restrict__ expert_slot, uint16_t *__restrict__ recv_x,
+    const float *__restrict__ topk_weights, const int32_t *__restrict__ rank_slot,
+    void *__restrict__ recv_x, void *__restrict__ recv_scales,
+    int64_t *__restrict__ recv_topk_idx, float *__restrict__ recv_topk_weights,
     int32_t *__restrict__ recv_src_idx, uint32_t *status)
 {
     const int lane = threadIdx.x & 63;
@@ -161,38 +303,108 @@ __global__ __launch_bounds__(kThreads) void pack_bf16_kernel(
         return;
     const uint32_t t = item / (uint32_t)nchunks;
     const int32_t chunk = (int32_t)(item - t * (uint32_t)nchunks);
-    const int32_t units = H / 8;
-    const int32_t u0 = chunk * (kChunk / 8) + lane;
-    const int32_t u1 = u0 + 64;
-    const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)t * H);
-    uint4 a0 = make_uint4(0, 0, 0, 0), a1 = make_uint4(0, 0, 0, 0);
-    if (u0 < units)
-        a0 = load_stream(src + u0);
-    if (u1 < units)
-        a1 = load_stream(src + u1);
+    const uint16_t *x_row = x + (size_t)t * H;
+    const int32_t L = E / R;
 
     uint32_t flags = 0;
-    const int64_t *idx_t = topk_idx + (size_t)t * K;
-    const int32_t *slot_t = expert_slot + (size_t)t * K;
-    for (int k0 = 0; k0 < K; k0 += KB) {
-        int64_t row[KB];
-        float unused[KB];
-        fetch_entries<KB>(idx_t, slot_t, nullptr, k0, K, E, S, lane, row, unused, flags);
-#pragma unroll
-        for (int b = 0; b < KB; ++b) {
-            if (row[b] >= 0) {
-                uint4 *dst = reinterpret_cast<uint4 *>(recv_x + (size_t)row[b] * H);
-                if (u0 < units)
-                    dst[u0] = a0;
-                if (u1 < units)
-                    dst[u1] = a1;
-                if (chunk == 0 && lane == 0)
-                    recv_src_idx[row[b]] = (int32_t)t;
+    int32_t j;
+    uint64_t dest = rank_destinations(rank_slot + (size_t)t * R, R, M, lane, j, flags);
+    // the token's routing entries (chunk-0 waves write them per destination)
+    int64_t id = -1;
+    float wt = 0.0f;
+    if (chunk == 0) {
+        const int kk = min(lane, K - 1);
+        id = topk_idx[(size_t)t * K + kk];
+        if (topk_weights)
+            wt = topk_weights[(size_t)t * K + kk];
+        if (dest && __ballot(lane < K && id != -1 && (id < 0 || id >= (int64_t)E)))
+            flags |= EP_STATUS_BAD_EXPERT_ID;
+    }
+    const bool routed = id >= 0 && id < (int64_t)E;
+    const int32_t id_rank = routed ? (int32_t)id / L : -1;
+
+    Fp8Lane fl;
+    Fp8Payload p;
+    Bf16Lane bl;
+    uint4 a0 = make_uint4(0, 0, 0, 0), a1 = make_uint4(0, 0, 0, 0);
+    if (FP8) {
+        fl = fp8_lane(H, chunk, lane);
+        p = quantize_lane<SF>(x_row, fl, lane);
+    } else {
+        bl = bf16_lane(H, chunk, lane);
+        const uint4 *src = reinterpret_cast<const uint4 *>(x_row);
+        if (bl.u0 < bl.units)
+            a0 = load_stream(src + bl.u0);
+        if (bl.u1 < bl.units)
+            a1 = load_stream(src + bl.u1);
+    }
+
+    while (dest) {
+        const int r = __builtin_ctzll(dest);
+        dest &= dest - 1;
+        const int64_t row = (int64_t)r * M + __builtin_amdgcn_readlane(j, r);
+        if (FP8)
+            store_fp8<SF>(p, fl, lane, row, H, static_cast<uint8_t *>(recv_x), recv_scales);
+        else
+            store_bf16(a0, a1, bl, row, H, static_cast<uint16_t *>(recv_x));
+        if (chunk == 0) {
+            if (lane == 0)
+                recv_src_idx[row] = (int32_t)t;
+            if (lane < K) {
+                const bool local = id_rank == r;
+                recv_topk_idx[(size_t)row * K + lane] = local ? id - (int64_t)r * L : -1;
+                if (topk_weights && recv_topk_weights)
+                    recv_topk_weights[(size_t)row * K + lane] = local ? wt : 0.0f;
             }
         }
     }
     if (flags && status && lane == 0 && chunk == 0)
         atomicOr(status, flags);
+}
+
+int batch_of(int K) { return K == 1 ? 1 : K == 2 ? 2 : K <= 4 ? 4 : 8; }
+
+// Launch of the per-expert / expand pack for every (batch, scale format,
+// FP8 / BF16) combination.
+template <class Rows>
+hipError_t launch_pack(const ep_shape &s, int32_t pad_items, const Rows &rows,
+                       const int32_t *counts, const uint16_t *x, const int64_t *topk_idx,
+                       const int32_t *expert_slot, void *recv_x, void *recv_scales,
+                       int32_t *recv_src_idx, uint32_t *status, hipStream_t stream)
+{
+    const int N = s.num_tokens, H = s.hidden, K = s.num_topk, E = s.num_experts;
+    const int nchunks = (H + kChunk - 1) / kChunk;
+    const int64_t items = (int64_t)pad_items + (int64_t)N * nchunks;
+    if (items == 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)((items + kWaves - 1) / kWaves));
+    const int kb = batch_of(K);
+#define EP_PACK(KB, SF, FP8)                                                                       \
+    hipLaunchKernelGGL((pack_kernel<KB, SF, FP8, Rows>), grid, dim3(kThreads), 0, stream, N, H, K, \
+                       E, nchunks, pad_items, rows, counts, x, topk_idx, expert_slot, recv_x,      \
+                       recv_scales, recv_src_idx, status)
+#define EP_PACK_KB(SF, FP8)                                                                        \
+    do {                                                                                           \
+        if (kb == 1)                                                                               \
+            EP_PACK(1, SF, FP8);                                                                   \
+        else if (kb == 2)                                                                          \
+            EP_PACK(2, SF, FP8);                                                                   \
+        else if (kb == 4)                                                                          \
+            EP_PACK(4, SF, FP8);                                                                   \
+        else                                                                                       \
+            EP_PACK(8, SF, FP8);                                                                   \
+    } while (0)
+    if (!s.use_fp8)
+        EP_PACK_KB(EP_SCALE_FP32, false);
+    else if (s.scale_format == EP_SCALE_POW2)
+        EP_PACK_KB(EP_SCALE_POW2, true);
+    else if (s.scale_format == EP_SCALE_UE8M0)
+        EP_PACK_KB(EP_SCALE_UE8M0, true);
+    else
+        EP_PACK_KB(EP_SCALE_FP32, true);
+#undef EP_PACK_KB
+#undef EP_PACK
+    return hipGetLastError();
 }
 
 } // namespace
@@ -201,53 +413,48 @@ hipError_t launch_dispatch(const ep_shape &s, const uint16_t *x, const int64_t *
                            const int32_t *expert_slot, void *recv_x, void *recv_scales,
                            int32_t *recv_src_idx, uint32_t *status, hipStream_t stream)
 {
+    return launch_pack(s, 0, DenseRows{s.expert_capacity}, nullptr, x, topk_idx, expert_slot,
+                       recv_x, recv_scales, recv_src_idx, status, stream);
+}
+
+hipError_t launch_dispatch_expand(const ep_shape &s, const uint16_t *x, const int64_t *topk_idx,
+                                  const int32_t *expert_slot, const int32_t *expert_offset,
+                                  const int32_t *num_tokens_per_expert, void *recv_x,
+                                  void *recv_scales, int32_t *recv_src_idx, uint32_t *status,
+                                  hipStream_t stream)
+{
+    const int nchunks = (s.hidden + kChunk - 1) / kChunk;
+    return launch_pack(s, s.num_experts * nchunks, ExpandRows{expert_offset, expand_rows(s)},
+                       num_tokens_per_expert, x, topk_idx, expert_slot, recv_x, recv_scales,
+                       recv_src_idx, status, stream);
+}
+
+hipError_t launch_dispatch_normal(const ep_shape &s, const uint16_t *x, const int64_t *topk_idx,
+                                  const float *topk_weights, const int32_t *rank_slot,
+                                  void *recv_x, void *recv_scales, int64_t *recv_topk_idx,
+                                  float *recv_topk_weights, int32_t *recv_src_idx,
+                                  uint32_t *status, hipStream_t stream)
+{
     const int N = s.num_tokens, H = s.hidden, K = s.num_topk, E = s.num_experts;
-    const int S = s.expert_capacity;
+    const int R = s.num_ranks, M = s.num_max_dispatch_tokens_per_rank;
     if (N == 0)
         return hipSuccess;
     const int nchunks = (H + kChunk - 1) / kChunk;
     const int64_t items = (int64_t)N * nchunks;
     const dim3 grid((unsigned)((items + kWaves - 1) / kWaves));
-    const int kb = K == 1 ? 1 : K == 2 ? 2 : K <= 4 ? 4 : 8;
-    if (s.use_fp8) {
-        uint8_t *rx = static_cast<uint8_t *>(recv_x);
-#define EP_PACK_FP8(KB, SF)                                                                        \
-    hipLaunchKernelGGL((pack_fp8_kernel<KB, SF>), grid, dim3(kThreads), 0, stream, N, H, K, E, S,  \
-                       nchunks, x, topk_idx, expert_slot, rx, recv_scales, recv_src_idx, status)
-#define EP_PACK_FP8_SF(SF)                                                                         \
-    do {                                                                                           \
-        if (kb == 1)                                                                               \
-            EP_PACK_FP8(1, SF);                                                                    \
-        else if (kb == 2)                                                                          \
-            EP_PACK_FP8(2, SF);                                                                    \
-        else if (kb == 4)                                                                          \
-            EP_PACK_FP8(4, SF);                                                                    \
-        else                                                                                       \
-            EP_PACK_FP8(8, SF);                                                                    \
-    } while (0)
-        if (s.scale_format == EP_SCALE_POW2)
-            EP_PACK_FP8_SF(EP_SCALE_POW2);
-        else if (s.scale_format == EP_SCALE_UE8M0)
-            EP_PACK_FP8_SF(EP_SCALE_UE8M0);
-        else
-            EP_PACK_FP8_SF(EP_SCALE_FP32);
-#undef EP_PACK_FP8_SF
-#undef EP_PACK_FP8
-    } else {
-        uint16_t *rx = static_cast<uint16_t *>(recv_x);
-#define EP_PACK_BF16(KB)                                                                           \
-    hipLaunchKernelGGL(pack_bf16_kernel<KB>, grid, dim3(kThreads), 0, stream, N, H, K, E, S,       \
-                       nchunks, x, topk_idx, expert_slot, rx, recv_src_idx, status)
-        if (kb == 1)
-            EP_PACK_BF16(1);
-        else if (kb == 2)
-            EP_PACK_BF16(2);
-        else if (kb == 4)
-            EP_PACK_BF16(4);
-        else
-            EP_PACK_BF16(8);
-#undef EP_PACK_BF16
-    }
+#define EP_PACK_NORMAL(SF, FP8)                                                                    \
+    hipLaunchKernelGGL((pack_normal_kernel<SF, FP8>), grid, dim3(kThreads), 0, stream, N, H, K, E, \
+                       R, M, nchunks, x, topk_idx, topk_weights, rank_slot, recv_x, recv_scales,   \
+                       recv_topk_idx, recv_topk_weights, recv_src_idx, status)
+    if (!s.use_fp8)
+        EP_PACK_NORMAL(EP_SCALE_FP32, false);
+    else if (s.scale_format == EP_SCALE_POW2)
+        EP_PACK_NORMAL(EP_SCALE_POW2, true);
+    else if (s.scale_format == EP_SCALE_UE8M0)
+        EP_PACK_NORMAL(EP_SCALE_UE8M0, true);
+    else
+        EP_PACK_NORMAL(EP_SCALE_FP32, true);
+#undef EP_PACK_NORMAL
     return hipGetLastError();
 }
 

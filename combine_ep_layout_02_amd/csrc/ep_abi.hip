@@ -25,7 +25,10 @@ int check_shape(const ep_shape *s)
     if (s->scale_format < EP_SCALE_FP32 || s->scale_format > EP_SCALE_UE8M0 ||
         (!s->use_fp8 && s->scale_format != EP_SCALE_FP32))
         return EP_ERR_SHAPE;
-    if (K > EP_MAX_TOPK || E > EP_MAX_EXPERTS || R > EP_MAX_RANKS)
+    if (s->expert_alignment < 0)
+        return EP_ERR_SHAPE;
+    if (K > EP_MAX_TOPK || E > EP_MAX_EXPERTS || R > EP_MAX_RANKS ||
+        s->expert_alignment > EP_MAX_ALIGNMENT)
         return EP_ERR_UNSUPPORTED;
     if (M < 1 || N > M || S < M)
         return EP_ERR_CAPACITY;
@@ -35,9 +38,12 @@ int check_shape(const ep_shape *s)
         return EP_ERR_UNSUPPORTED;
     if (E * S > INT64_MAX / (H * 2))
         return EP_ERR_UNSUPPORTED;
-    // pack and combine number their work items (token, 1024-channel chunk)
-    // in 32 bits
-    if (N * ((H + 1023) / 1024) > INT32_MAX)
+    // normal-mode rows (R * M) and expand rows (T) are numbered in 32 bits
+    if (R * M > INT32_MAX || ep::expand_rows(*s) > INT32_MAX)
+        return EP_ERR_UNSUPPORTED;
+    // pack and combine number their work items (token or expand-padding
+    // expert, 1024-channel chunk) in 32 bits
+    if ((N + E) * ((H + 1023) / 1024) > INT32_MAX)
         return EP_ERR_UNSUPPORTED;
     ep::LayoutPlan plan;
     if (!ep::plan_layout(*s, &plan))
@@ -101,6 +107,23 @@ int ep_query_sizes(const ep_shape *s, ep_sizes *out)
     ep::LayoutPlan plan;
     ep::plan_layout(*s, &plan);
     out->layout_workspace = plan.workspace_bytes;
+    const size_t M = s->num_max_dispatch_tokens_per_rank;
+    const size_t scale_row = !s->use_fp8 ? 0
+                             : s->scale_format == EP_SCALE_UE8M0 ? ((G + 3) / 4) * sizeof(uint32_t)
+                                                                 : G * sizeof(float);
+    const size_t nrows = R * M;
+    out->recv_x_normal = nrows * H * (s->use_fp8 ? 1 : 2);
+    out->recv_scales_normal = nrows * scale_row;
+    out->recv_topk_idx = nrows * K * sizeof(int64_t);
+    out->recv_topk_weights = nrows * K * sizeof(float);
+    out->recv_src_idx_normal = nrows * sizeof(int32_t);
+    out->expert_out_normal = nrows * H * 2;
+    out->combined_topk_weights = N * K * sizeof(float);
+    const size_t T = (size_t)ep::expand_rows(*s);
+    out->recv_x_expand = T * H * (s->use_fp8 ? 1 : 2);
+    out->recv_scales_expand = T * scale_row;
+    out->recv_src_idx_expand = T * sizeof(int32_t);
+    out->expert_out_expand = T * H * 2;
     return EP_OK;
 }
 
@@ -172,6 +195,103 @@ int ep_combine(const ep_shape *s, const uint16_t *expert_out, const int64_t *top
     const hipError_t err =
         ep::launch_combine(*s, expert_out, topk_idx, topk_weights, expert_slot, combined_x, status,
                            static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+int ep_dispatch_expand(const ep_shape *s, const uint16_t *x, const int64_t *topk_idx,
+                       const int32_t *expert_slot, const int32_t *expert_offset,
+                       const int32_t *num_tokens_per_expert, void *recv_x, void *recv_scales,
+                       int32_t *recv_src_idx, uint32_t *status, void *stream)
+{
+    const int rc = check_shape(s);
+    if (rc != EP_OK)
+        return rc;
+    // the padding rows are written even without tokens (every queue is then
+    // empty, so nothing is), but the offsets and counts are always read
+    if (!expert_offset || !num_tokens_per_expert || !recv_x || !recv_src_idx)
+        return EP_ERR_NULL;
+    if (s->num_tokens > 0 && (!x || !topk_idx || !expert_slot))
+        return EP_ERR_NULL;
+    if (s->use_fp8 && !recv_scales)
+        return EP_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(topk_idx, 8) ||
+        !aligned(expert_slot, 4) || !aligned(expert_offset, 4) ||
+        !aligned(num_tokens_per_expert, 4) || !aligned(recv_scales, 4) ||
+        !aligned(recv_src_idx, 4) || !aligned(status, 4))
+        return EP_ERR_ALIGN;
+    const hipError_t err = ep::launch_dispatch_expand(
+        *s, x, topk_idx, expert_slot, expert_offset, num_tokens_per_expert, recv_x, recv_scales,
+        recv_src_idx, status, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+int ep_combine_expand(const ep_shape *s, const uint16_t *expert_out, const int64_t *topk_idx,
+                      const float *topk_weights, const int32_t *expert_slot,
+                      const int32_t *expert_offset, uint16_t *combined_x, uint32_t *status,
+                      void *stream)
+{
+    const int rc = check_shape(s);
+    if (rc != EP_OK)
+        return rc;
+    if (s->num_tokens == 0)
+        return EP_OK;
+    if (!expert_out || !topk_idx || !topk_weights || !expert_slot || !expert_offset || !combined_x)
+        return EP_ERR_NULL;
+    if (!aligned(expert_out, 16) || !aligned(combined_x, 16) || !aligned(topk_idx, 8) ||
+        !aligned(topk_weights, 4) || !aligned(expert_slot, 4) || !aligned(expert_offset, 4) ||
+        !aligned(status, 4))
+        return EP_ERR_ALIGN;
+    const hipError_t err =
+        ep::launch_combine_expand(*s, expert_out, topk_idx, topk_weights, expert_slot,
+                                  expert_offset, combined_x, status,
+                                  static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+int ep_dispatch_normal(const ep_shape *s, const uint16_t *x, const int64_t *topk_idx,
+                       const float *topk_weights, const int32_t *rank_slot, void *recv_x,
+                       void *recv_scales, int64_t *recv_topk_idx, float *recv_topk_weights,
+                       int32_t *recv_src_idx, uint32_t *status, void *stream)
+{
+    const int rc = check_shape(s);
+    if (rc != EP_OK)
+        return rc;
+    if (s->num_tokens == 0)
+        return EP_OK;
+    if (!x || !topk_idx || !rank_slot || !recv_x || !recv_topk_idx || !recv_src_idx)
+        return EP_ERR_NULL;
+    if (s->use_fp8 && !recv_scales)
+        return EP_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(topk_idx, 8) ||
+        !aligned(topk_weights, 4) || !aligned(rank_slot, 4) || !aligned(recv_scales, 4) ||
+        !aligned(recv_topk_idx, 8) || !aligned(recv_topk_weights, 4) ||
+        !aligned(recv_src_idx, 4) || !aligned(status, 4))
+        return EP_ERR_ALIGN;
+    const hipError_t err = ep::launch_dispatch_normal(
+        *s, x, topk_idx, topk_weights, rank_slot, recv_x, recv_scales, recv_topk_idx,
+        recv_topk_weights, recv_src_idx, status, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+int ep_combine_normal(const ep_shape *s, const uint16_t *x, const int32_t *rank_slot,
+                      const float *recv_topk_weights, uint16_t *combined_x,
+                      float *combined_topk_weights, uint32_t *status, void *stream)
+{
+    const int rc = check_shape(s);
+    if (rc != EP_OK)
+        return rc;
+    if (s->num_tokens == 0)
+        return EP_OK;
+    if (!x || !rank_slot || !combined_x)
+        return EP_ERR_NULL;
+    if (recv_topk_weights && !combined_topk_weights)
+        return EP_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(combined_x, 16) || !aligned(rank_slot, 4) ||
+        !aligned(recv_topk_weights, 4) || !aligned(combined_topk_weights, 4) || !aligned(status, 4))
+        return EP_ERR_ALIGN;
+    const hipError_t err = ep::launch_combine_normal(*s, x, rank_slot, recv_topk_weights,
+                                                     combined_x, combined_topk_weights, status,
+                                                     static_cast<hipStream_t>(stream));
     return err == hipSuccess ? EP_OK : EP_ERR_HIP;
 }
 

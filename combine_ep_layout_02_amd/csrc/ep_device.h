@@ -77,19 +77,50 @@ __device__ __forceinline__ uint32_t e4m3fn_x4_sw(float a, float b, float c, floa
 
 __device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
 
+// Where the receive row of (expert e, slot j) lies, and whether it exists.
+//  DenseRows:  the per-expert layout [E, S, ...]: row e * S + j, 0 <= j < S
+//              (Lesson 14 §3 and DeepEP V1 Legacy guide §6.3);
+//  ExpandRows: the expand layout (DeepEP Ascend deep dive, "Dispatch's Three
+//              Phases", phase 1): one buffer of T rows, expert e's queue is
+//              [offset[e], offset[e+1]); row offset[e] + j must fall inside it
+//              and below T.
+// `e` is already a routed id in [0, E).
+struct DenseRows {
+    int32_t S;
+    __device__ __forceinline__ int64_t row(int64_t e, int32_t j, bool &ok) const
+    {
+        ok = j >= 0 && j < S;
+        return e * S + j;
+    }
+};
+
+struct ExpandRows {
+    const int32_t *offset; // [E + 1]
+    int64_t T;
+    __device__ __forceinline__ int64_t row(int64_t e, int32_t j, bool &ok) const
+    {
+        const int64_t begin = offset[e], end = offset[e + 1];
+        const int64_t r = begin + j;
+        ok = j >= 0 && begin >= 0 && r < end && end <= T;
+        return r;
+    }
+};
+
 // Receive rows of entries k0 .. k0+KB-1 of one token, for a whole wave.
 // Lanes 0..KB-1 each load one entry (expert id, slot and, when `w_t` is not
 // NULL, weight) with an ordinary vector load -- indices are clamped to the
 // token's last entry, so every lane's load is in bounds -- and the results are
-// broadcast with readlane, so all KB entries arrive after a single wait.
-// row[b] = id * S + slot for a routed entry with 0 <= slot < S, else -1; an id
-// outside [-1, E) or a slot outside [0, S) also sets its status bit.
-template <int KB>
+// broadcast with readlane, so all KB entries arrive after a single wait (the
+// expand layout adds one dependent load of the expert's queue bounds).
+// row[b] = the entry's receive row (see DenseRows / ExpandRows) for a routed
+// entry whose row exists, else -1; an id outside [-1, E) or a missing row
+// also sets its status bit.
+template <int KB, class Rows>
 __device__ __forceinline__ void fetch_entries(const int64_t *__restrict__ idx_t,
                                               const int32_t *__restrict__ slot_t,
                                               const float *__restrict__ w_t, int k0, int K, int E,
-                                              int S, int lane, int64_t (&row)[KB], float (&w)[KB],
-                                              uint32_t &flags)
+                                              const Rows &rows, int lane, int64_t (&row)[KB],
+                                              float (&w)[KB], uint32_t &flags)
 {
     static_assert(KB >= 1 && KB <= 64, "one entry per lane");
     const int kk = min(k0 + lane, K - 1);
@@ -98,8 +129,9 @@ __device__ __forceinline__ void fetch_entries(const int64_t *__restrict__ idx_t,
     const float wv = w_t ? w_t[kk] : 0.0f;
     const bool in_k = lane < KB && k0 + lane < K;
     const bool routed = id >= 0 && id < (int64_t)E;
-    const bool slot_ok = j >= 0 && j < S;
-    const int64_t r = (in_k && routed && slot_ok) ? id * S + j : -1;
+    bool slot_ok;
+    const int64_t rr = rows.row(routed ? id : 0, j, slot_ok);
+    const int64_t r = (in_k && routed && slot_ok) ? rr : -1;
     if (__ballot(in_k && id != -1 && !routed))
         flags |= EP_STATUS_BAD_EXPERT_ID;
     if (__ballot(in_k && routed && !slot_ok))
@@ -114,6 +146,21 @@ __device__ __forceinline__ void fetch_entries(const int64_t *__restrict__ idx_t,
         row[b] = (int64_t)(((uint64_t)hi << 32) | lo);
         w[b] = __int_as_float(__builtin_amdgcn_readlane(w_bits, b));
     }
+}
+
+// The ranks a token was sent to (normal mode, DeepEP V1 Legacy guide §5.1):
+// lane r < R loads rank_slot[t, r]; the returned mask has bit r set when the
+// token has a row 0 <= j < M at rank r, and `j` holds that lane's slot (read
+// it for rank r with readlane).  A slot >= M sets EP_STATUS_BAD_SLOT.
+__device__ __forceinline__ uint64_t rank_destinations(const int32_t *__restrict__ rank_slot_t,
+                                                      int R, int M, int lane, int32_t &j,
+                                                      uint32_t &flags)
+{
+    j = rank_slot_t[min(lane, R - 1)];
+    const bool mine = lane < R;
+    if (__ballot(mine && j >= M))
+        flags |= EP_STATUS_BAD_SLOT;
+    return __ballot(mine && j >= 0 && j < M);
 }
 
 } // namespace ep

@@ -33,14 +33,50 @@ hipError_t launch_layout(const ep_shape &s, const LayoutPlan &plan, const int64_
                          int32_t *expert_offset, int32_t *workspace, uint32_t *status,
                          hipStream_t stream);
 
+// Expert alignment of the expand layout (1 when the shape sets none).
+inline int32_t expert_alignment(const ep_shape &s)
+{
+    return s.expert_alignment > 1 ? s.expert_alignment : 1;
+}
+
+// Rows of the expand-layout buffer: the valid entries (at most M * K) plus at
+// most A - 1 padding rows per expert.
+inline int64_t expand_rows(const ep_shape &s)
+{
+    return (int64_t)s.num_max_dispatch_tokens_per_rank * s.num_topk +
+           (int64_t)s.num_experts * (expert_alignment(s) - 1);
+}
+
 // ---- dispatch pack -------------------------------------------------------
 hipError_t launch_dispatch(const ep_shape &s, const uint16_t *x, const int64_t *topk_idx,
                            const int32_t *expert_slot, void *recv_x, void *recv_scales,
                            int32_t *recv_src_idx, uint32_t *status, hipStream_t stream);
 
+hipError_t launch_dispatch_expand(const ep_shape &s, const uint16_t *x, const int64_t *topk_idx,
+                                  const int32_t *expert_slot, const int32_t *expert_offset,
+                                  const int32_t *num_tokens_per_expert, void *recv_x,
+                                  void *recv_scales, int32_t *recv_src_idx, uint32_t *status,
+                                  hipStream_t stream);
+
+hipError_t launch_dispatch_normal(const ep_shape &s, const uint16_t *x, const int64_t *topk_idx,
+                                  const float *topk_weights, const int32_t *rank_slot,
+                                  void *recv_x, void *recv_scales, int64_t *recv_topk_idx,
+                                  float *recv_topk_weights, int32_t *recv_src_idx,
+                                  uint32_t *status, hipStream_t stream);
+
 // ---- combine ---------------------------------------------------------------
 hipError_t launch_combine(const ep_shape &s, const uint16_t *expert_out, const int64_t *topk_idx,
                           const float *topk_weights, const int32_t *expert_slot,
                           uint16_t *combined_x, uint32_t *status, hipStream_t stream);
+
+hipError_t launch_combine_expand(const ep_shape &s, const uint16_t *expert_out,
+                                 const int64_t *topk_idx, const float *topk_weights,
+                                 const int32_t *expert_slot, const int32_t *expert_offset,
+                                 uint16_t *combined_x, uint32_t *status, hipStream_t stream);
+
+hipError_t launch_combine_normal(const ep_shape &s, const uint16_t *x, const int32_t *rank_slot,
+                                 const float *recv_topk_weights, uint16_t *combined_x,
+                                 float *combined_topk_weights, uint32_t *status,
+                                 hipStream_t stream);
 
 } // namespace ep

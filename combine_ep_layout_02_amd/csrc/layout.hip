@@ -106,10 +106,16 @@ __device__ __forceinline__ int prefix_in_block(const uint64_t *words, int stride
     return cnt;
 }
 
+// Rows of expert queue with c entries under expert alignment A >= 1 (the
+// expand layout of the Ascend deep dive, phase 1: queues padded to a
+// multiple of A; A = 1 gives the plain count).
+__device__ __forceinline__ int aligned_count(int c, int A) { return (c + A - 1) / A * A; }
+
 // Totals in s_tot[0..E+R) (LDS, complete) -> num_tokens_per_expert,
-// num_tokens_per_rank and the exclusive offset scan (expert_offset nullable).
-// Called by all kThreads threads of one block; uses s_misc[4..8).
-__device__ void write_totals_and_offsets(int E, int R, const int32_t *s_tot, int32_t *s_misc,
+// num_tokens_per_rank and the exclusive offset scan of the aligned counts
+// (expert_offset nullable).  Called by all kThreads threads of one block;
+// uses s_misc[4..8).
+__device__ void write_totals_and_offsets(int E, int R, int A, const int32_t *s_tot, int32_t *s_misc,
                                          int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
                                          int32_t *expert_offset)
 {
@@ -129,7 +135,7 @@ __device__ void write_totals_and_offsets(int E, int R, const int32_t *s_tot, int
     int local = 0;
     for (int i = 0; i < per; ++i)
         if (start + i < E)
-            local += s_tot[start + i];
+            local += aligned_count(s_tot[start + i], A);
     int incl = local;
     for (int off = 1; off < 64; off <<= 1) {
         const int up = __shfl_up(incl, off, 64);
@@ -146,7 +152,7 @@ __device__ void write_totals_and_offsets(int E, int R, const int32_t *s_tot, int
     for (int i = 0; i < per; ++i) {
         if (start + i < E) {
             expert_offset[start + i] = run;
-            run += s_tot[start + i];
+            run += aligned_count(s_tot[start + i], A);
         }
     }
     if (tid == kThreads - 1)
@@ -155,7 +161,7 @@ __device__ void write_totals_and_offsets(int E, int R, const int32_t *s_tot, int
 
 // The extra block of a multi-block layout: column sums of all B histogram
 // rows (int4 loads, kHistBatch in flight per thread), then totals and scan.
-__device__ void layout_totals(int B, int E, int R, int stride, const int32_t *__restrict__ hist,
+__device__ void layout_totals(int B, int E, int R, int A, int stride, const int32_t *__restrict__ hist,
                               int32_t *s_tot, int32_t *s_misc, int32_t *num_tokens_per_rank,
                               int32_t *num_tokens_per_expert, int32_t *expert_offset)
 {
@@ -189,13 +195,13 @@ __device__ void layout_totals(int B, int E, int R, int stride, const int32_t *__
         }
     }
     __syncthreads();
-    write_totals_and_offsets(E, R, s_tot, s_misc, num_tokens_per_rank, num_tokens_per_expert,
+    write_totals_and_offsets(E, R, A, s_tot, s_misc, num_tokens_per_rank, num_tokens_per_expert,
                              expert_offset);
 }
 
 template <int KMAX>
 __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
-    int32_t N, int32_t K, int32_t E, int32_t R, int32_t L, int32_t stride,
+    int32_t N, int32_t K, int32_t E, int32_t R, int32_t L, int32_t A, int32_t stride,
     const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ hist,
     int32_t *__restrict__ num_tokens_per_rank, int32_t *__restrict__ num_tokens_per_expert,
     uint8_t *__restrict__ is_token_in_rank, int32_t *__restrict__ expert_slot,
@@ -217,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
         // the extra block: totals are the column sums of every block's
         // histogram; it writes them and the offset scan while the other
         // blocks rank their tokens
-        layout_totals(num_token_blocks, E, R, stride, hist, s_tot, s_misc, num_tokens_per_rank,
+        layout_totals(num_token_blocks, E, R, A, stride, hist, s_tot, s_misc, num_tokens_per_rank,
                       num_tokens_per_expert, expert_offset);
         return;
     }
@@ -409,8 +415,8 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
         for (int i = tid; i < E + R; i += kThreads)
             s_tot[i] += s_base[i];
         __syncthreads();
-        write_totals_and_offsets(E, R, s_tot, s_misc, num_tokens_per_rank, num_tokens_per_expert,
-                                 expert_offset);
+        write_totals_and_offsets(E, R, A, s_tot, s_misc, num_tokens_per_rank,
+                                 num_tokens_per_expert, expert_offset);
     }
 }
 
@@ -436,6 +442,7 @@ hipError_t launch_layout(const ep_shape &s, const LayoutPlan &plan, const int64_
 {
     const int N = s.num_tokens, K = s.num_topk, E = s.num_experts, R = s.num_ranks;
     const int L = E / R;
+    const int A = expert_alignment(s);
     const int B = plan.num_blocks, stride = plan.hist_stride;
     const size_t count_lds = sizeof(int32_t) * (size_t)(E + R);
 #define EP_LAYOUT_LAUNCH(KMAX)                                                                     \
@@ -444,7 +451,7 @@ hipError_t launch_layout(const ep_shape &s, const LayoutPlan &plan, const int64_
             hipLaunchKernelGGL(layout_count_kernel<KMAX>, dim3(B), dim3(kThreads), count_lds,      \
                                stream, N, K, E, R, L, stride, topk_idx, workspace);                \
         hipLaunchKernelGGL(layout_assign_kernel<KMAX>, dim3(B > 1 ? B + 1 : 1), dim3(kThreads),   \
-                           plan.lds_bytes, stream, N, K, E, R, L, stride, topk_idx,                \
+                           plan.lds_bytes, stream, N, K, E, R, L, A, stride, topk_idx,             \
                            B > 1 ? workspace : nullptr,                                            \
                            num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank,           \
                            expert_slot, rank_slot, expert_offset, status);                         \

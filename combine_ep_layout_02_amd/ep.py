@@ -1,8 +1,9 @@
 """Thin ctypes binding of libep_mi355x.so (declared in include/ep.h).
 
 Same entry points as the C ABI: ``ep_query_sizes``, ``ep_layout``,
-``ep_dispatch``, ``ep_combine``, ``ep_strerror`` (plus ``ep_probe_e4m3fn``
-from include/ep_probe.h).  Functions take torch tensors that already live on
+``ep_dispatch``, ``ep_combine``, ``ep_dispatch_expand``, ``ep_combine_expand``,
+``ep_dispatch_normal``, ``ep_combine_normal``, ``ep_strerror`` (plus
+``ep_probe_e4m3fn`` from include/ep_probe.h).  Functions take torch tensors that already live on
 the GPU, check dtype / device / contiguity, and pass ``data_ptr()`` and the
 current HIP stream to the library.  Every step of the path runs in the HIP
 kernels; this module only marshals arguments and allocates buffers with torch
@@ -32,15 +33,21 @@ EP_STATUS_BAD_EXPERT_ID = 1
 EP_STATUS_BAD_SLOT = 2
 
 SHAPE_FIELDS = ("num_tokens", "hidden", "num_topk", "num_experts", "num_ranks",
-                "num_max_dispatch_tokens_per_rank", "expert_capacity", "use_fp8", "scale_format")
+                "num_max_dispatch_tokens_per_rank", "expert_capacity", "use_fp8", "scale_format",
+                "expert_alignment")
 EP_SCALE_FP32 = 0
 EP_SCALE_POW2 = 1
 EP_SCALE_UE8M0 = 2
 SIZE_FIELDS = ("recv_x", "recv_scales", "recv_src_idx", "expert_out", "combined_x",
                "num_tokens_per_rank", "num_tokens_per_expert", "is_token_in_rank",
-               "expert_slot", "rank_slot", "expert_offset", "layout_workspace")
-EXPORTED = ("ep_query_sizes", "ep_layout", "ep_dispatch", "ep_combine", "ep_strerror",
+               "expert_slot", "rank_slot", "expert_offset", "layout_workspace",
+               "recv_x_normal", "recv_scales_normal", "recv_topk_idx", "recv_topk_weights",
+               "recv_src_idx_normal", "expert_out_normal", "combined_topk_weights",
+               "recv_x_expand", "recv_scales_expand", "recv_src_idx_expand", "expert_out_expand")
+EXPORTED = ("ep_query_sizes", "ep_layout", "ep_dispatch", "ep_combine", "ep_dispatch_expand",
+            "ep_combine_expand", "ep_dispatch_normal", "ep_combine_normal", "ep_strerror",
             "ep_probe_e4m3fn")
+EP_MAX_ALIGNMENT = 1024
 
 
 class ep_shape(ctypes.Structure):
@@ -74,29 +81,48 @@ def lib() -> ctypes.CDLL:
         L.ep_layout.argtypes = [sp] + [vp] * 8 + [sz, vp, vp]
         L.ep_dispatch.argtypes = [sp] + [vp] * 8
         L.ep_combine.argtypes = [sp] + [vp] * 7
+        L.ep_dispatch_expand.argtypes = [sp] + [vp] * 10
+        L.ep_combine_expand.argtypes = [sp] + [vp] * 8
+        L.ep_dispatch_normal.argtypes = [sp] + [vp] * 11
+        L.ep_combine_normal.argtypes = [sp] + [vp] * 7
         L.ep_probe_e4m3fn.argtypes = [vp, vp, vp, i64, vp]
         L.ep_strerror.argtypes = [ctypes.c_int]
         L.ep_strerror.restype = ctypes.c_char_p
-        for name in ("ep_query_sizes", "ep_layout", "ep_dispatch", "ep_combine", "ep_probe_e4m3fn"):
-            getattr(L, name).restype = ctypes.c_int
+        for name in EXPORTED:
+            if name != "ep_strerror":
+                getattr(L, name).restype = ctypes.c_int
         _LIB = L
     return _LIB
 
 
 def make_shape(num_tokens: int, hidden: int, num_topk: int, num_experts: int, num_ranks: int,
                num_max_dispatch_tokens_per_rank: int, expert_capacity: int,
-               use_fp8: bool, scale_format: int = EP_SCALE_FP32) -> ep_shape:
+               use_fp8: bool, scale_format: int = EP_SCALE_FP32,
+               expert_alignment: int = 0) -> ep_shape:
     return ep_shape(int(num_tokens), int(hidden), int(num_topk), int(num_experts), int(num_ranks),
                     int(num_max_dispatch_tokens_per_rank), int(expert_capacity), int(bool(use_fp8)),
-                    int(scale_format))
+                    int(scale_format), int(expert_alignment))
 
 
-def shape_of(workload, scale_format: int = EP_SCALE_FP32) -> ep_shape:
-    """ep_shape of a ``workloads.Workload`` (FP8 workloads may pick a scale format)."""
+def shape_of(workload, scale_format: int = EP_SCALE_FP32, expert_alignment: int = 0) -> ep_shape:
+    """ep_shape of a ``workloads.Workload`` (FP8 workloads may pick a scale
+    format; ``expert_alignment`` sets the expand layout's queue alignment)."""
     w = workload
     return make_shape(w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks,
                       w.num_max_dispatch_tokens_per_rank, w.expert_capacity, w.use_fp8,
-                      scale_format if w.use_fp8 else EP_SCALE_FP32)
+                      scale_format if w.use_fp8 else EP_SCALE_FP32, expert_alignment)
+
+
+def expand_rows(shape: ep_shape) -> int:
+    """Rows T of the expand-layout buffers: M * K + E * (A - 1)."""
+    a = max(int(shape.expert_alignment), 1)
+    return shape.num_max_dispatch_tokens_per_rank * shape.num_topk + shape.num_experts * (a - 1)
+
+
+def scale_row_elems(shape: ep_shape) -> int:
+    """Scale elements per receive row: H/128 floats, or ceil(H/512) UE8M0 words."""
+    g = shape.hidden // 128
+    return (g + 3) // 4 if shape.scale_format == EP_SCALE_UE8M0 else g
 
 
 def ep_strerror(code: int) -> str:
@@ -182,6 +208,89 @@ def ep_dispatch(shape: ep_shape, x: torch.Tensor, topk_idx: torch.Tensor, expert
         raise EpError(rc, "ep_dispatch")
 
 
+def _scales_ptr(shape: ep_shape, recv_scales, rows: int):
+    if not shape.use_fp8:
+        return None
+    types = _STATUS if shape.scale_format == EP_SCALE_UE8M0 else _F32
+    return _ptr(recv_scales, "recv_scales", types, rows * scale_row_elems(shape))
+
+
+def ep_dispatch_expand(shape: ep_shape, x: torch.Tensor, topk_idx: torch.Tensor,
+                       expert_slot: torch.Tensor, expert_offset: torch.Tensor,
+                       num_tokens_per_expert: torch.Tensor, recv_x: torch.Tensor,
+                       recv_scales: Optional[torch.Tensor], recv_src_idx: torch.Tensor,
+                       status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Dispatch pack into the expand layout; see ``ep_dispatch_expand`` in include/ep.h."""
+    N, H, K, E = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts
+    T = expand_rows(shape)
+    rc = lib().ep_dispatch_expand(
+        ctypes.byref(shape), _ptr(x, "x", _BF16, N * H), _ptr(topk_idx, "topk_idx", _I64, N * K),
+        _ptr(expert_slot, "expert_slot", _I32, N * K),
+        _ptr(expert_offset, "expert_offset", _I32, E + 1),
+        _ptr(num_tokens_per_expert, "num_tokens_per_expert", _I32, E),
+        _ptr(recv_x, "recv_x", _FP8 if shape.use_fp8 else _BF16, T * H),
+        _scales_ptr(shape, recv_scales, T), _ptr(recv_src_idx, "recv_src_idx", _I32, T),
+        _ptr(status, "status", _STATUS, 1), _stream(stream, recv_x))
+    if rc != EP_OK:
+        raise EpError(rc, "ep_dispatch_expand")
+
+
+def ep_combine_expand(shape: ep_shape, expert_out: torch.Tensor, topk_idx: torch.Tensor,
+                      topk_weights: torch.Tensor, expert_slot: torch.Tensor,
+                      expert_offset: torch.Tensor, combined_x: torch.Tensor,
+                      status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Combine from the expand layout; see ``ep_combine_expand`` in include/ep.h."""
+    N, H, K, E = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts
+    rc = lib().ep_combine_expand(
+        ctypes.byref(shape), _ptr(expert_out, "expert_out", _BF16, expand_rows(shape) * H),
+        _ptr(topk_idx, "topk_idx", _I64, N * K), _ptr(topk_weights, "topk_weights", _F32, N * K),
+        _ptr(expert_slot, "expert_slot", _I32, N * K),
+        _ptr(expert_offset, "expert_offset", _I32, E + 1),
+        _ptr(combined_x, "combined_x", _BF16, N * H), _ptr(status, "status", _STATUS, 1),
+        _stream(stream, combined_x))
+    if rc != EP_OK:
+        raise EpError(rc, "ep_combine_expand")
+
+
+def ep_dispatch_normal(shape: ep_shape, x: torch.Tensor, topk_idx: torch.Tensor,
+                       topk_weights: Optional[torch.Tensor], rank_slot: torch.Tensor,
+                       recv_x: torch.Tensor, recv_scales: Optional[torch.Tensor],
+                       recv_topk_idx: torch.Tensor, recv_topk_weights: Optional[torch.Tensor],
+                       recv_src_idx: torch.Tensor, status: Optional[torch.Tensor] = None,
+                       stream=None) -> None:
+    """Normal-mode dispatch; see ``ep_dispatch_normal`` in include/ep.h."""
+    N, H, K, R = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_ranks
+    rows = R * shape.num_max_dispatch_tokens_per_rank
+    rc = lib().ep_dispatch_normal(
+        ctypes.byref(shape), _ptr(x, "x", _BF16, N * H), _ptr(topk_idx, "topk_idx", _I64, N * K),
+        _ptr(topk_weights, "topk_weights", _F32, N * K), _ptr(rank_slot, "rank_slot", _I32, N * R),
+        _ptr(recv_x, "recv_x", _FP8 if shape.use_fp8 else _BF16, rows * H),
+        _scales_ptr(shape, recv_scales, rows),
+        _ptr(recv_topk_idx, "recv_topk_idx", _I64, rows * K),
+        _ptr(recv_topk_weights, "recv_topk_weights", _F32, rows * K),
+        _ptr(recv_src_idx, "recv_src_idx", _I32, rows), _ptr(status, "status", _STATUS, 1),
+        _stream(stream, recv_x))
+    if rc != EP_OK:
+        raise EpError(rc, "ep_dispatch_normal")
+
+
+def ep_combine_normal(shape: ep_shape, x: torch.Tensor, rank_slot: torch.Tensor,
+                      recv_topk_weights: Optional[torch.Tensor], combined_x: torch.Tensor,
+                      combined_topk_weights: Optional[torch.Tensor] = None,
+                      status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Normal-mode combine; see ``ep_combine_normal`` in include/ep.h."""
+    N, H, K, R = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_ranks
+    rows = R * shape.num_max_dispatch_tokens_per_rank
+    rc = lib().ep_combine_normal(
+        ctypes.byref(shape), _ptr(x, "x", _BF16, rows * H), _ptr(rank_slot, "rank_slot", _I32, N * R),
+        _ptr(recv_topk_weights, "recv_topk_weights", _F32, rows * K),
+        _ptr(combined_x, "combined_x", _BF16, N * H),
+        _ptr(combined_topk_weights, "combined_topk_weights", _F32, N * K),
+        _ptr(status, "status", _STATUS, 1), _stream(stream, combined_x))
+    if rc != EP_OK:
+        raise EpError(rc, "ep_combine_normal")
+
+
 def ep_combine(shape: ep_shape, expert_out: torch.Tensor, topk_idx: torch.Tensor,
                topk_weights: torch.Tensor, expert_slot: torch.Tensor, combined_x: torch.Tensor,
                status: Optional[torch.Tensor] = None, stream=None) -> None:
@@ -211,8 +320,9 @@ def ep_probe_e4m3fn(values: torch.Tensor, out_hw: Optional[torch.Tensor],
 
 def allocate(shape: ep_shape, device="cuda", parts=("layout", "dispatch", "combine")) -> dict:
     """torch.empty buffers for the outputs of the requested parts of the path
-    ("layout", "dispatch", "combine", "expert_out"), sized as ep_query_sizes
-    says.  Contents are uninitialised except ``status`` (zero)."""
+    ("layout", "dispatch", "combine", "expert_out", and for the other receive
+    layouts "normal" and "expand"), sized as ep_query_sizes says.  Contents
+    are uninitialised except ``status`` (zero)."""
     sz = ep_query_sizes(shape)
     N, H, K, E, R, S = (shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts,
                         shape.num_ranks, shape.expert_capacity)
@@ -243,4 +353,26 @@ def allocate(shape: ep_shape, device="cuda", parts=("layout", "dispatch", "combi
         out["combined_x"] = torch.empty((N, H), dtype=torch.int16, device=dev)
     if "expert_out" in parts:
         out["expert_out"] = torch.empty((E, S, H), dtype=torch.int16, device=dev)
+    rx_dtype = torch.uint8 if shape.use_fp8 else torch.int16
+    sc_dtype = torch.int32 if shape.scale_format == EP_SCALE_UE8M0 else torch.float32
+    G = scale_row_elems(shape)
+    if "normal" in parts:
+        M = shape.num_max_dispatch_tokens_per_rank
+        out.update({
+            "recv_x_normal": torch.empty((R, M, H), dtype=rx_dtype, device=dev),
+            "recv_scales_normal": (torch.empty((R, M, G), dtype=sc_dtype, device=dev)
+                                   if shape.use_fp8 else None),
+            "recv_topk_idx": torch.empty((R, M, K), dtype=torch.int64, device=dev),
+            "recv_topk_weights": torch.empty((R, M, K), dtype=torch.float32, device=dev),
+            "recv_src_idx_normal": torch.empty((R, M), dtype=torch.int32, device=dev),
+            "combined_topk_weights": torch.empty((N, K), dtype=torch.float32, device=dev),
+        })
+    if "expand" in parts:
+        T = expand_rows(shape)
+        out.update({
+            "recv_x_expand": torch.empty((T, H), dtype=rx_dtype, device=dev),
+            "recv_scales_expand": (torch.empty((T, G), dtype=sc_dtype, device=dev)
+                                   if shape.use_fp8 else None),
+            "recv_src_idx_expand": torch.empty(T, dtype=torch.int32, device=dev),
+        })
     return out

@@ -13,8 +13,9 @@
  *         legal), §8.2 (fixed-size buffers at maximum capacity);
  *   [ASC] "DeepEP Ascend Deep Dive" (kongchang.com): "Two Transfers: Dispatch
  *         and Combine" (one copy per destination card; weighted sum at the
- *         origin), "Dispatch's Three Phases and FP8 Compression" (counts per
- *         expert and per card; the receive-source map);
+ *         origin), "Dispatch's Three Phases and FP8 Compression" (phase 1: the
+ *         expand layout with 128-aligned, zero-padded expert queues; phase 2:
+ *         counts per expert and per card; phase 3: the receive-source map);
  *   [L14] "Lesson 14: DeepSeek DeepEP" (hpc.payai.win): §3 (low-latency call
  *         sequence: x [tokens, hidden] bf16, topk_idx [tokens, topk] global
  *         expert ids, receive data plus a count per local expert, combine
@@ -23,7 +24,9 @@
  * One GPU plays every logical EP rank: rank r owns experts [r*L, (r+1)*L),
  * L = E / R, and its receive buffer is the slice recv_x[r*L : (r+1)*L] of one
  * [E, S, H] buffer in this GPU's HBM; its per-expert counts are the slice
- * num_tokens_per_expert[r*L : (r+1)*L].
+ * num_tokens_per_expert[r*L : (r+1)*L].  Two more receive layouts exist: the
+ * expand layout (ep_dispatch_expand, ep_combine_expand) and the normal-mode
+ * rank-major layout (ep_dispatch_normal, ep_combine_normal).
  *
  * Conventions of every entry point:
  *  - Pointers are DEVICE pointers unless the comment says "host".  The caller
@@ -62,7 +65,7 @@ extern "C" {
 #define EP_ERR_NULL 1        /* a required pointer is NULL                            */
 #define EP_ERR_SHAPE 2       /* N < 0, H, K, E or R out of range, E % R != 0, FP8 with
                                 H % 128 != 0, BF16 with H % 8 != 0, a bad
-                                scale_format                                         */
+                                scale_format, expert_alignment < 0                   */
 #define EP_ERR_CAPACITY 3    /* N > M or S < M: the fixed upper bounds are never grown
                                 ([V1] §6.1 and §8.4; [L14] capacity discussion)       */
 #define EP_ERR_ALIGN 4       /* a pointer is not aligned as required                  */
@@ -78,6 +81,7 @@ extern "C" {
 #define EP_MAX_EXPERTS 1024 /* E */
 #define EP_MAX_RANKS 64     /* R: a token's rank set is one 64-bit mask          */
 #define EP_MAX_TOPK 32      /* K */
+#define EP_MAX_ALIGNMENT 1024 /* expert_alignment */
 
 /* The problem's shape ([V1] §5.1 and §6.1; [L14] §3).  Passed by host pointer. */
 typedef struct {
@@ -96,6 +100,14 @@ typedef struct {
                              EP_SCALE_UE8M0 (2) that power of two as an 8-bit
                              exponent, four per 32-bit word ("use_ue8m0").
                              Must be 0 when use_fp8 == 0. */
+    int32_t expert_alignment; /* A in [0, EP_MAX_ALIGNMENT]; 0 and 1 mean none.
+                             ep_layout's expert_offset is the exclusive prefix
+                             of round_up(count_e, A): the queue starts of the
+                             expand layout ([ASC] phase 1: queues padded to a
+                             multiple of 128 for the grouped GEMM).  Also the
+                             per-expert receive counts of normal mode rounded
+                             up the same way are expert_offset[e+1] -
+                             expert_offset[e]. */
 } ep_shape;
 
 /* Scale formats of ep_shape.scale_format. */
@@ -118,6 +130,19 @@ typedef struct {
     size_t rank_slot;             /* N*R*4                                            */
     size_t expert_offset;         /* (E+1)*4                                          */
     size_t layout_workspace;      /* scratch for ep_layout (0: none needed)           */
+    /* normal mode (ep_dispatch_normal / ep_combine_normal), M rows per rank: */
+    size_t recv_x_normal;         /* R*M*H (FP8) or R*M*H*2 (BF16)                    */
+    size_t recv_scales_normal;    /* R*M*(H/128)*4, R*M*ceil(H/512)*4 (UE8M0), or 0   */
+    size_t recv_topk_idx;         /* R*M*K*8                                          */
+    size_t recv_topk_weights;     /* R*M*K*4                                          */
+    size_t recv_src_idx_normal;   /* R*M*4                                            */
+    size_t expert_out_normal;     /* R*M*H*2: bf16 rows read by ep_combine_normal     */
+    size_t combined_topk_weights; /* N*K*4                                            */
+    /* expand layout, T = M*K + E*(A-1) rows (A = max(expert_alignment, 1)):    */
+    size_t recv_x_expand;         /* T*H (FP8) or T*H*2 (BF16)                        */
+    size_t recv_scales_expand;    /* T*(H/128)*4, T*ceil(H/512)*4 (UE8M0), or 0       */
+    size_t recv_src_idx_expand;   /* T*4                                              */
+    size_t expert_out_expand;     /* T*H*2: bf16 rows read by ep_combine_expand       */
 } ep_sizes;
 
 /* Host only.  Fills `out` (host) with the byte size of every buffer for
@@ -141,8 +166,10 @@ int ep_query_sizes(const ep_shape *shape, ep_sizes *out);
  *   rank_slot          [N, R] int32  the number of tokens t' < t in rank r's set,
  *       -1 where token t is not in the set (each token appears at most once per
  *       rank; this is the one row per (token, rank) a link would carry);
- *   expert_offset      [E+1]  int32  exclusive prefix of num_tokens_per_expert,
- *       expert_offset[E] = number of valid entries.  Nullable.
+ *   expert_offset      [E+1]  int32  exclusive prefix of num_tokens_per_expert
+ *       rounded up to multiples of A = max(expert_alignment, 1); with A = 1,
+ *       expert_offset[E] = number of valid entries.  Nullable (required by
+ *       ep_dispatch_expand and ep_combine_expand).
  * expert_slot is the handle that ep_dispatch and ep_combine take ([V1] §5.2(4):
  * the handle holds the routing metadata and can be reused while the routing is
  * unchanged).
@@ -197,6 +224,82 @@ int ep_dispatch(const ep_shape *shape, const uint16_t *x, const int64_t *topk_id
 int ep_combine(const ep_shape *shape, const uint16_t *expert_out, const int64_t *topk_idx,
                const float *topk_weights, const int32_t *expert_slot, uint16_t *combined_x,
                uint32_t *status, void *stream);
+
+/* Dispatch pack into the expand layout ([ASC] "Dispatch's Three Phases and
+ * FP8 Compression", phase 1: each token is cloned once per routed expert, the
+ * clones are grouped by expert, and each expert's queue is padded with zero
+ * rows to a multiple of the expert alignment, because the grouped GEMM after
+ * it takes only aligned row counts; phase 3: the receive-source map).
+ *
+ * In:  x, topk_idx, expert_slot as for ep_dispatch; expert_offset [E+1] and
+ *      num_tokens_per_expert [E] from ep_layout run with the same shape
+ *      (expert_offset then holds the aligned queue starts).
+ * Out: one buffer of T = M*K + E*(A-1) rows (A = max(expert_alignment, 1)):
+ *      recv_x [T, H] (FP8 bytes or bf16), recv_scales [T, H/128] fp32 or
+ *      [T, ceil(H/512)] UE8M0 words (FP8 only, NULL otherwise), recv_src_idx
+ *      [T] int32.  Entry (t, k) with expert e goes to row expert_offset[e] +
+ *      expert_slot[t,k] with the payload ep_dispatch writes; padding rows
+ *      [expert_offset[e] + count_e, expert_offset[e+1]) get zero bytes, zero
+ *      scales and source -1; rows at or past expert_offset[E] are not
+ *      written.  An entry whose row falls outside its expert's queue or past T
+ *      is skipped and sets EP_STATUS_BAD_SLOT. */
+int ep_dispatch_expand(const ep_shape *shape, const uint16_t *x, const int64_t *topk_idx,
+                       const int32_t *expert_slot, const int32_t *expert_offset,
+                       const int32_t *num_tokens_per_expert, void *recv_x, void *recv_scales,
+                       int32_t *recv_src_idx, uint32_t *status, void *stream);
+
+/* Combine from expert outputs in the expand layout: as ep_combine, with the
+ * output row of entry (t, k) at expert_offset[e] + expert_slot[t,k] of
+ * expert_out [T, H] bf16 (same bounds rule as ep_dispatch_expand). */
+int ep_combine_expand(const ep_shape *shape, const uint16_t *expert_out, const int64_t *topk_idx,
+                      const float *topk_weights, const int32_t *expert_slot,
+                      const int32_t *expert_offset, uint16_t *combined_x, uint32_t *status,
+                      void *stream);
+
+/* Normal-mode dispatch ([V1] §5.1: dispatch returns recv_x, recv_topk_idx,
+ * recv_topk_weights and the per-expert receive counts, and its handle holds
+ * the source index; [L14] §2(3) and [ASC] "Two Transfers": a token reaches a
+ * rank once however many of its experts live there).
+ *
+ * In:  x [N, H] bf16 bits; topk_idx [N, K]; topk_weights [N, K] fp32
+ *      (nullable); rank_slot [N, R] from ep_layout.
+ * Out: rank r's rows are r*M .. r*M + num_tokens_per_rank[r] - 1 of
+ *        recv_x [R, M, H] (the ep_dispatch payload: FP8 bytes or bf16),
+ *        recv_scales [R, M, H/128] fp32 or [R, M, ceil(H/512)] UE8M0 words
+ *          (FP8 only, NULL otherwise),
+ *        recv_topk_idx [R, M, K] int64: e - r*L for an entry routed to expert
+ *          e on rank r (the local expert id), -1 otherwise,
+ *        recv_topk_weights [R, M, K] fp32: topk_weights[t,k] for those
+ *          entries, 0 otherwise (written only when both weight pointers are
+ *          non-NULL),
+ *        recv_src_idx [R, M] int32: the source token t;
+ *      token t with rank_slot[t,r] = j >= 0 fills row j of rank r.  Rows at or
+ *      past num_tokens_per_rank[r] are not written.  A slot j >= M is skipped
+ *      and sets EP_STATUS_BAD_SLOT; an expert id outside [-1, E) of a token
+ *      that is written sets EP_STATUS_BAD_EXPERT_ID. */
+int ep_dispatch_normal(const ep_shape *shape, const uint16_t *x, const int64_t *topk_idx,
+                       const float *topk_weights, const int32_t *rank_slot, void *recv_x,
+                       void *recv_scales, int64_t *recv_topk_idx, float *recv_topk_weights,
+                       int32_t *recv_src_idx, uint32_t *status, void *stream);
+
+/* Normal-mode combine ([V1] §5.1: combine takes one row per received token
+ * and the handle, and can reduce a tensor of per-row top-k weights; the
+ * backward of dispatch is such a combine, so the reduction is a plain sum over
+ * the ranks the token was sent to -- the expert layer applied the weights).
+ *
+ * In:  x [R, M, H] bf16 bits, one row per received token (rows < count are
+ *      read); rank_slot [N, R] from ep_layout; recv_topk_weights [R, M, K]
+ *      fp32 (nullable).
+ * Out: combined_x [N, H] bf16 bits:
+ *        acc = +0; for r = 0..R-1 with j = rank_slot[t,r] in [0, M):
+ *            acc = acc + float(x[r][j][c]);
+ *        combined_x[t,c] = bf16 round-to-nearest-even(acc);
+ *      combined_topk_weights [N, K] fp32 (nullable; written when
+ *        recv_topk_weights is given): the same fp32 sum over the same rows.
+ *      A token sent nowhere gets +0. */
+int ep_combine_normal(const ep_shape *shape, const uint16_t *x, const int32_t *rank_slot,
+                      const float *recv_topk_weights, uint16_t *combined_x,
+                      float *combined_topk_weights, uint32_t *status, void *stream);
 
 /* Host only.  A static string naming a return code. */
 const char *ep_strerror(int code);

@@ -97,7 +97,7 @@ OK16 = ctypes.c_void_p(0x1000)  # aligned stand-in pointer, never dereferenced
 def _shape(**kw):
     base = dict(num_tokens=300, hidden=256, num_topk=4, num_experts=16, num_ranks=4,
                 num_max_dispatch_tokens_per_rank=300, expert_capacity=300, use_fp8=0,
-                scale_format=0)
+                scale_format=0, expert_alignment=0)
     base.update(kw)
     return ep.ep_shape(*[int(base[f]) for f in ep.SHAPE_FIELDS])
 
@@ -114,6 +114,8 @@ def _shape(**kw):
     (dict(scale_format=1), ep.EP_ERR_SHAPE),                 # scale formats are FP8-only
     (dict(use_fp8=1, scale_format=3), ep.EP_ERR_SHAPE),
     (dict(use_fp8=1, scale_format=-1), ep.EP_ERR_SHAPE),
+    (dict(expert_alignment=-1), ep.EP_ERR_SHAPE),
+    (dict(expert_alignment=ep.EP_MAX_ALIGNMENT + 1), ep.EP_ERR_UNSUPPORTED),
     (dict(num_topk=33), ep.EP_ERR_UNSUPPORTED),
     (dict(num_experts=2048, num_ranks=4), ep.EP_ERR_UNSUPPORTED),
     (dict(num_experts=128, num_ranks=128), ep.EP_ERR_UNSUPPORTED),
@@ -130,6 +132,10 @@ def test_static_shape_errors_are_reported_before_any_launch(kw, code):
     assert lib.ep_layout(ctypes.byref(s), *args9[:7], OK16, ctypes.c_size_t(1 << 30), None, None) == code
     assert lib.ep_dispatch(ctypes.byref(s), *[OK16] * 6, None, None) == code
     assert lib.ep_combine(ctypes.byref(s), *[OK16] * 5, None, None) == code
+    assert lib.ep_dispatch_expand(ctypes.byref(s), *[OK16] * 8, None, None) == code
+    assert lib.ep_combine_expand(ctypes.byref(s), *[OK16] * 6, None, None) == code
+    assert lib.ep_dispatch_normal(ctypes.byref(s), *[OK16] * 9, None, None) == code
+    assert lib.ep_combine_normal(ctypes.byref(s), *[OK16] * 5, None, None) == code
 
 
 def test_null_pointers_are_rejected():
@@ -152,6 +158,77 @@ def test_null_pointers_are_rejected():
         q = [OK16] * 5
         q[i] = None
         assert lib.ep_combine(ctypes.byref(s), *q, None, None) == ep.EP_ERR_NULL
+
+
+def test_null_pointers_are_rejected_by_the_other_layouts():
+    s = _shape()
+    sf = _shape(use_fp8=1, hidden=256)
+    lib = ep.lib()
+    # expand: x, topk_idx, expert_slot, expert_offset, counts, recv_x, (scales), recv_src_idx
+    for i in (0, 1, 2, 3, 4, 5, 7):
+        q = [OK16] * 8
+        q[i] = None
+        assert lib.ep_dispatch_expand(ctypes.byref(s), *q, None, None) == ep.EP_ERR_NULL
+    q = [OK16] * 8
+    q[6] = None
+    assert lib.ep_dispatch_expand(ctypes.byref(sf), *q, None, None) == ep.EP_ERR_NULL
+    for i in range(6):  # expert_out, topk_idx, topk_weights, expert_slot, expert_offset, out
+        q = [OK16] * 6
+        q[i] = None
+        assert lib.ep_combine_expand(ctypes.byref(s), *q, None, None) == ep.EP_ERR_NULL
+    # normal: x, topk_idx, (weights), rank_slot, recv_x, (scales), recv_topk_idx, (w), src
+    for i in (0, 1, 3, 4, 6, 8):
+        q = [OK16] * 9
+        q[i] = None
+        assert lib.ep_dispatch_normal(ctypes.byref(s), *q, None, None) == ep.EP_ERR_NULL
+    q = [OK16] * 9
+    q[5] = None
+    assert lib.ep_dispatch_normal(ctypes.byref(sf), *q, None, None) == ep.EP_ERR_NULL
+    for i in (0, 1, 3, 4):  # x, rank_slot, combined_x, and combined weights when weights are given
+        q = [OK16] * 5
+        q[i] = None
+        assert lib.ep_combine_normal(ctypes.byref(s), *q, None, None) == ep.EP_ERR_NULL
+
+
+def test_misaligned_pointers_are_rejected_by_the_other_layouts():
+    s = _shape(use_fp8=1, hidden=256)
+    lib = ep.lib()
+    for n, fn in ((8, lib.ep_dispatch_expand), (6, lib.ep_combine_expand),
+                  (9, lib.ep_dispatch_normal), (5, lib.ep_combine_normal)):
+        for i in range(n):
+            q = [OK16] * n
+            q[i] = BAD
+            assert fn(ctypes.byref(s), *q, None, None) == ep.EP_ERR_ALIGN, (fn.__name__, i)
+    # token rows need 16 bytes
+    assert lib.ep_dispatch_expand(ctypes.byref(s), ctypes.c_void_p(0x1008), *[OK16] * 7, None,
+                                  None) == ep.EP_ERR_ALIGN
+    assert lib.ep_combine_normal(ctypes.byref(s), ctypes.c_void_p(0x1008), *[OK16] * 4, None,
+                                 None) == ep.EP_ERR_ALIGN
+    # recv_topk_idx is int64
+    q = [OK16] * 9
+    q[6] = ctypes.c_void_p(0x1004)
+    assert lib.ep_dispatch_normal(ctypes.byref(s), *q, None, None) == ep.EP_ERR_ALIGN
+
+
+@pytest.mark.parametrize("wid", sorted(W.WORKLOADS))
+@pytest.mark.parametrize("align", [0, 1, 128])
+def test_query_sizes_of_the_other_layouts(wid, align):
+    """Normal mode: M rows per rank (V1 guide §5.1); expand layout: M*K rows
+    plus at most A-1 padding rows per expert (Ascend deep dive, phase 1)."""
+    w = W.WORKLOADS[wid]
+    sz = ep.ep_query_sizes(ep.shape_of(w, expert_alignment=align))
+    N, H, K, E, R, M = (w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks,
+                        w.num_max_dispatch_tokens_per_rank)
+    b = 1 if w.use_fp8 else 2
+    g = H // 128 if w.use_fp8 else 0
+    assert sz["recv_x_normal"] == R * M * H * b and sz["recv_scales_normal"] == R * M * g * 4
+    assert sz["recv_topk_idx"] == R * M * K * 8 and sz["recv_topk_weights"] == R * M * K * 4
+    assert sz["recv_src_idx_normal"] == R * M * 4 and sz["expert_out_normal"] == R * M * H * 2
+    assert sz["combined_topk_weights"] == N * K * 4
+    T = M * K + E * (max(align, 1) - 1)
+    assert T == ep.expand_rows(ep.shape_of(w, expert_alignment=align))
+    assert sz["recv_x_expand"] == T * H * b and sz["recv_scales_expand"] == T * g * 4
+    assert sz["recv_src_idx_expand"] == T * 4 and sz["expert_out_expand"] == T * H * 2
 
 
 def test_misaligned_pointers_are_rejected():
