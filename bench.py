@@ -271,6 +271,160 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
     }
 
 
+def receive_layout_bytes(n, h, k, r, p, rows_sent, pad_rows, use_fp8, scale_format=0):
+    """Algorithmic bytes of the other receive layouts, by entry point.
+
+    dispatch_normal : read x once, rank_slot, topk_idx, topk_weights; write per
+                      (token, rank) row the payload, scales, its source index
+                      and K routing entries (8 B id + 4 B weight);
+    combine_normal  : read rank_slot, one bf16 row and K weights per
+                      (token, rank) row; write the bf16 output and K weights
+                      per token;
+    dispatch_expand : the per-expert pack's bytes plus the padding rows
+                      (payload, scales and source index each);
+    combine_expand  : the per-expert combine's bytes."""
+    b = 1 if use_fp8 else 2
+    g = h // 128
+    scale_bytes = 0 if not use_fp8 else 4 * ((g + 3) // 4) if scale_format == 2 else 4 * g
+    row = b * h + scale_bytes + 4
+    return {
+        "dispatch_normal": 2 * n * h + 4 * n * r + 12 * n * k + rows_sent * (row + 12 * k),
+        "combine_normal": 4 * n * r + rows_sent * (2 * h + 4 * k) + n * (2 * h + 4 * k),
+        "dispatch_expand": 2 * n * h + 12 * n * k + (p + pad_rows) * row,
+        "combine_expand": 2 * p * h + 16 * n * k + 2 * n * h,
+    }
+
+
+def _timed_batches(fn, steps, batch, evict, stream):
+    """Average duration of one call: ``batch`` back-to-back calls between two
+    events after an untimed eviction, ``steps`` times."""
+    import torch
+
+    times = []
+    for _ in range(steps):
+        evict()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(batch):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / batch)
+    return statistics.fmean(times)
+
+
+def _timed_cold(fn, steps, evict, stream):
+    """Median duration of one call with a cold Infinity Cache: an untimed
+    eviction, then two events around the call, ``steps`` times.  The events
+    add a few us of launch latency, so this is an upper bound on the kernel
+    time (the rocprofv3 trace of the same run gives the kernel-only time)."""
+    import torch
+
+    times = []
+    for _ in range(steps):
+        evict()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    return statistics.median(times)
+
+
+def time_receive_layouts(wid, steps, scrub_bytes, say, alignment=128, batch=10):
+    """The normal-mode and expand paths on workload ``wid``: each entry point
+    timed alone, cold (one launch after an eviction, the same protocol as the
+    bench's step) and back to back (``batch`` launches after an eviction:
+    once a kernel writes more than the 256 MB Infinity Cache holds, each
+    launch also pays the write-back of the previous one's lines), and the
+    whole layout + dispatch + combine step of each mode, cold."""
+    import torch
+    from combine_ep_layout_02_amd import ep
+    from combine_ep_layout_02_amd import workloads as W
+
+    w = W.WORKLOADS[wid]
+    inp = W.make_inputs(w)
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    shape = ep.shape_of(w, expert_alignment=alignment)
+    topk_idx = torch.from_numpy(inp["topk_idx"]).to(dev)
+    topk_weights = torch.from_numpy(inp["topk_weights"]).to(dev)
+    x = torch.from_numpy(inp["x_bits"].view(np.int16)).to(dev)
+    buf = ep.allocate(shape, dev, parts=("layout", "combine", "normal", "expand"))
+    scrub = torch.ones(scrub_bytes // 4, dtype=torch.float32, device=dev) if scrub_bytes else None
+    scrub_out = torch.zeros((), dtype=torch.float32, device=dev)
+
+    def evict():
+        if scrub is not None:
+            torch.sum(scrub, dim=0, out=scrub_out)
+
+    def layout():
+        ep.ep_layout(shape, topk_idx, buf["num_tokens_per_rank"], buf["num_tokens_per_expert"],
+                     buf["is_token_in_rank"], buf["expert_slot"], buf["rank_slot"],
+                     buf["expert_offset"], buf["workspace"], buf["status"])
+
+    def dispatch_normal():
+        ep.ep_dispatch_normal(shape, x, topk_idx, topk_weights, buf["rank_slot"],
+                              buf["recv_x_normal"], buf["recv_scales_normal"], buf["recv_topk_idx"],
+                              buf["recv_topk_weights"], buf["recv_src_idx_normal"], buf["status"])
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(2100 + wid)
+    R, M, H = w.num_ranks, w.num_max_dispatch_tokens_per_rank, w.hidden
+    y_normal = torch.randn((R, M, H), dtype=torch.bfloat16, device=dev, generator=g).view(torch.int16)
+    T = ep.expand_rows(shape)
+    y_expand = torch.randn((T, H), dtype=torch.bfloat16, device=dev, generator=g).view(torch.int16)
+
+    def combine_normal():
+        ep.ep_combine_normal(shape, y_normal, buf["rank_slot"], buf["recv_topk_weights"],
+                             buf["combined_x"], buf["combined_topk_weights"], buf["status"])
+
+    def dispatch_expand():
+        ep.ep_dispatch_expand(shape, x, topk_idx, buf["expert_slot"], buf["expert_offset"],
+                              buf["num_tokens_per_expert"], buf["recv_x_expand"],
+                              buf["recv_scales_expand"], buf["recv_src_idx_expand"], buf["status"])
+
+    def combine_expand():
+        ep.ep_combine_expand(shape, y_expand, topk_idx, topk_weights, buf["expert_slot"],
+                             buf["expert_offset"], buf["combined_x"], buf["status"])
+
+    layout()
+    dispatch_normal()
+    dispatch_expand()
+    torch.cuda.synchronize()
+    if int(buf["status"].item()) != 0:
+        raise RuntimeError(f"device status {int(buf['status'].item())}")
+    rows_sent = int(buf["num_tokens_per_rank"].sum().item())
+    used = int(buf["expert_offset"][-1].item())
+    P = inp["num_valid"]
+    nb = receive_layout_bytes(w.num_tokens, H, w.num_topk, R, P, rows_sent, used - P, w.use_fp8)
+    out = {"workload": w.name, "expert_alignment": alignment, "rows_sent_normal": rows_sent,
+           "expand_rows_used": used, "expand_padding_rows": used - P, "bytes": nb}
+    for name, fn in (("dispatch_normal", dispatch_normal), ("combine_normal", combine_normal),
+                     ("dispatch_expand", dispatch_expand), ("combine_expand", combine_expand)):
+        say(f"{name} {w.name}: {steps} cold launches, {steps} x {batch} back to back")
+        cold = _timed_cold(fn, steps, evict, stream)
+        b2b = _timed_batches(fn, steps, batch, evict, stream)
+        out[name] = {"us_cold_median": round(cold, 2),
+                     "gbps_cold": round(nb[name] / (cold * 1e-6) / 1e9, 1),
+                     "frac_of_peak_cold": round(nb[name] / (cold * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                     "us_back_to_back_mean": round(b2b, 2),
+                     "gbps_back_to_back": round(nb[name] / (b2b * 1e-6) / 1e9, 1)}
+    for mode, d, c in (("normal", dispatch_normal, combine_normal),
+                       ("expand", dispatch_expand, combine_expand)):
+        def step():
+            layout()
+            d()
+            c()
+        say(f"{mode} step {w.name}: {steps} steps")
+        out[f"step_us_cold_{mode}"] = round(_timed_cold(step, steps, evict, stream), 2)
+    torch.cuda.synchronize()
+    if int(buf["status"].item()) != 0:
+        raise RuntimeError(f"device status {int(buf['status'].item())}")
+    return out
+
+
 def time_scale_formats(wid, steps, scrub_bytes, say, batch=10):
     """ep_dispatch alone on workload ``wid`` with each FP8 scale format:
     ``batch`` back-to-back launches between two events after an untimed
@@ -356,15 +510,20 @@ def cpu_baseline(inp, w, reps, say):
 
 
 PROFILE_COMMANDS = {
+    "layouts_trace": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -T -f csv "
+                     "-d $REPO/gpurun_out/prof_layouts -o trace -- python3 $REPO/bench.py "
+                     "--receive-layouts-only --steps 20 --quiet",
     "trace": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -T -f csv "
              "-d $REPO/gpurun_out/prof_trace -o trace -- python3 $REPO/bench.py --steps 30 "
-             "--warmup 5 --no-cpu-baseline --no-scale-formats --quiet",
+             "--warmup 5 --no-cpu-baseline --no-scale-formats --no-receive-layouts --quiet",
     "FETCH_SIZE": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -T -f csv "
                   "-d $REPO/gpurun_out/prof_FETCH_SIZE -o pmc -- python3 $REPO/bench.py --steps 3 "
-                  "--warmup 1 --no-cpu-baseline --no-decode --no-scale-formats --quiet",
+                  "--warmup 1 --no-cpu-baseline --no-decode --no-scale-formats --no-receive-layouts "
+                  "--quiet",
     "WRITE_SIZE": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -T -f csv "
                   "-d $REPO/gpurun_out/prof_WRITE_SIZE -o pmc -- python3 $REPO/bench.py --steps 3 "
-                  "--warmup 1 --no-cpu-baseline --no-decode --no-scale-formats --quiet",
+                  "--warmup 1 --no-cpu-baseline --no-decode --no-scale-formats --no-receive-layouts "
+                  "--quiet",
 }
 
 
@@ -482,6 +641,77 @@ def summarize_profiles(out_dir):
             with open(path, "w") as f:
                 f.write("\n".join(lines) + "\n")
             written.append(path)
+    written += summarize_layout_profiles(out_dir)
+    return written
+
+
+def summarize_layout_profiles(out_dir):
+    """Summaries of the normal-mode and expand kernels from the
+    ``--receive-layouts-only`` trace run (``prof_layouts``), if present: every
+    dispatch of each kernel in that run (cold single launches and
+    back-to-back batches) and the figures the bench printed in the same run."""
+    import csv
+
+    tdir = os.path.join(out_dir, "prof_layouts")
+    log = os.path.join(out_dir, "prof_layouts.log")
+    if not os.path.isdir(tdir) or not os.path.exists(log):
+        return []
+    with open(os.path.join(tdir, "trace_kernel_trace.csv")) as f:
+        trace = list(csv.DictReader(f))
+    figures = None
+    for line in reversed(open(log).read().splitlines()):
+        if line.startswith("{"):
+            figures = json.loads(line)
+            break
+    if figures is None:
+        raise RuntimeError(f"no JSON line in {log}")
+    rl = figures["receive_layouts_4096x7168"]
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    written = []
+    # in this run the per-expert kernels only serve the expand layout
+    for kname, entry, short in (("pack_normal_kernel", "dispatch_normal", "pack_normal"),
+                                ("combine_normal_kernel", "combine_normal", "combine_normal"),
+                                ("pack_kernel", "dispatch_expand", "pack_expand"),
+                                ("combine_kernel", "combine_expand", "combine_expand")):
+        # a dispatch right after another kernel (the eviction, or the layout
+        # in a step) ran cold; one right after itself ran back to back
+        cold, b2b = [], []
+        for i, r in enumerate(trace):
+            if r["Kernel_Name"] != kname:
+                continue
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            after_self = i > 0 and trace[i - 1]["Kernel_Name"] == kname
+            (b2b if after_self else cold).append(d)
+        durs = sorted(cold + b2b)
+        if not durs:
+            continue
+        nb = rl["bytes"][entry]
+        med = statistics.median(cold) if cold else statistics.median(durs)
+        lines = [
+            f"# {kname} ({entry}), workload {rl['workload']}, expert_alignment "
+            f"{rl['expert_alignment']}",
+            f"kernel_source_digest: {figures['kernel_source_digest']}",
+            "",
+            "## rocprofv3 kernel trace (kernel-only durations of every dispatch in the run: "
+            "cold single launches and back-to-back batches)",
+            f"command: {PROFILE_COMMANDS['layouts_trace']}",
+            f"dispatches: {len(durs)} ({len(cold)} after another kernel = cold, {len(b2b)} right "
+            f"after itself = back to back)",
+            f"avg_us_all: {statistics.fmean(durs):.2f}",
+            f"median_us_cold: {med:.2f}",
+            f"median_us_back_to_back: {statistics.median(b2b) if b2b else float('nan'):.2f}",
+            f"min_us: {durs[0]:.2f}  max_us: {durs[-1]:.2f}",
+            f"algorithmic_bytes_per_launch: {nb}",
+            f"achieved_GBps_at_cold_median: {nb / med / 1e3:.1f}",
+            f"bench_same_run: cold {rl[entry]['us_cold_median']} us (events around one launch), "
+            f"back to back {rl[entry]['us_back_to_back_mean']} us",
+            f"rows_sent_normal: {rl['rows_sent_normal']}  expand_rows_used: {rl['expand_rows_used']}  "
+            f"expand_padding_rows: {rl['expand_padding_rows']}",
+        ]
+        path = os.path.join(PROFILES, f"{short}_{rl['workload']}_trace.txt")
+        with open(path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        written.append(path)
     return written
 
 
@@ -496,6 +726,11 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-scale-formats", action="store_true",
                     help="skip the ep_dispatch timing per FP8 scale format")
+    ap.add_argument("--no-receive-layouts", action="store_true",
+                    help="skip the normal-mode and expand-layout timings")
+    ap.add_argument("--receive-layouts-only", action="store_true",
+                    help="time only the normal-mode and expand paths (a profiling run) and print "
+                         "their figures as the JSON line")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/ summaries from a profiling run's output directory and exit")
@@ -523,6 +758,11 @@ def main():
 
     ep.lib()  # fail loudly if the HIP library is missing
     scrub_bytes = args.scrub_mib << 20
+    if args.receive_layouts_only:
+        print(json.dumps({"receive_layouts_4096x7168": time_receive_layouts(
+            3, args.steps, scrub_bytes, say), "kernel_source_digest": kernel_source_digest()}),
+            flush=True)
+        return
     prefill = run_workload(3, args.steps, args.warmup, scrub_bytes, say)
     decode = None if args.no_decode else run_workload(2, args.steps, args.warmup, scrub_bytes, say)
 
@@ -558,6 +798,9 @@ def main():
     }
     if not args.no_scale_formats:
         extra["dispatch_by_scale_format_4096x7168"] = time_scale_formats(
+            3, min(args.steps, 20), scrub_bytes, say)
+    if not args.no_receive_layouts:
+        extra["receive_layouts_4096x7168"] = time_receive_layouts(
             3, min(args.steps, 20), scrub_bytes, say)
     if decode is not None:
         extra["decode_128x7168"] = {
