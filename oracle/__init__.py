@@ -55,7 +55,7 @@ class Oracle:
         lib.oracle_layout.restype = ctypes.c_int
         lib.oracle_pack.argtypes = [i32] * 6 + [vp] * 6
         lib.oracle_pack.restype = ctypes.c_int
-        lib.oracle_combine.argtypes = [i32] * 5 + [vp] * 5
+        lib.oracle_combine.argtypes = [i32] * 5 + [vp] * 6
         lib.oracle_combine.restype = ctypes.c_int
         lib.oracle_e4m3fn_encode_array.argtypes = [i64, vp, vp]
         lib.oracle_e4m3fn_decode_array.argtypes = [i64, vp, vp]
@@ -70,11 +70,11 @@ class Oracle:
         lib.oracle_aligned_offsets.argtypes = [i32, vp, i32, vp]
         lib.oracle_pack_expand.argtypes = [i32] * 7 + [vp] * 8
         lib.oracle_pack_expand.restype = ctypes.c_int
-        lib.oracle_combine_expand.argtypes = [i32] * 5 + [vp] * 6
+        lib.oracle_combine_expand.argtypes = [i32] * 5 + [vp] * 7
         lib.oracle_combine_expand.restype = ctypes.c_int
         lib.oracle_dispatch_normal.argtypes = [i32] * 8 + [vp] * 9
         lib.oracle_dispatch_normal.restype = ctypes.c_int
-        lib.oracle_combine_normal.argtypes = [i32] * 5 + [vp] * 5
+        lib.oracle_combine_normal.argtypes = [i32] * 5 + [vp] * 6
         lib.oracle_combine_normal.restype = ctypes.c_int
         self.lib = lib
 
@@ -185,7 +185,8 @@ class Oracle:
         return recv_x, recv_scales, recv_src, int(st)
 
     def combine_expand(self, y_bits: np.ndarray, topk_idx: np.ndarray, topk_weights: np.ndarray,
-                       expert_slot: np.ndarray, expert_offset: np.ndarray):
+                       expert_slot: np.ndarray, expert_offset: np.ndarray,
+                       bias: np.ndarray | None = None):
         """Combine from expert outputs in the expand layout, y_bits [rows, H]."""
         y = np.ascontiguousarray(y_bits, dtype=np.uint16)
         idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
@@ -195,8 +196,9 @@ class Oracle:
         n, k = idx.shape
         rows, h = y.shape
         out = np.empty((n, h), np.uint16)
+        b = self._bias(bias, n, h)
         st = self.lib.oracle_combine_expand(n, h, k, off.size - 1, rows, _ptr(y), _ptr(idx),
-                                            _ptr(w), _ptr(slot), _ptr(off), _ptr(out))
+                                            _ptr(w), _ptr(slot), _ptr(off), _ptr(b), _ptr(out))
         return out, int(st)
 
     def dispatch_normal(self, x_bits: np.ndarray, topk_idx: np.ndarray,
@@ -234,7 +236,8 @@ class Oracle:
         return out
 
     def combine_normal(self, y_bits: np.ndarray, rank_slot: np.ndarray,
-                       recv_topk_weights: np.ndarray | None = None):
+                       recv_topk_weights: np.ndarray | None = None,
+                       bias: np.ndarray | None = None):
         """Normal-mode combine (DeepEP V1 Legacy guide §5.1): y_bits [R, M, H]
         one row per received token; returns (combined bf16 bits [N, H],
         combined topk weights [N, K] or None, status)."""
@@ -248,8 +251,9 @@ class Oracle:
             rw = np.ascontiguousarray(recv_topk_weights, dtype=np.float32)
             k = rw.shape[-1]
             cw = np.empty((n, k), np.float32)
-        st = self.lib.oracle_combine_normal(n, h, k, r, m, _ptr(y), _ptr(rs), _ptr(rw), _ptr(out),
-                                            _ptr(cw))
+        b = self._bias(bias, n, h)
+        st = self.lib.oracle_combine_normal(n, h, k, r, m, _ptr(y), _ptr(rs), _ptr(rw), _ptr(b),
+                                            _ptr(out), _ptr(cw))
         return out, cw, int(st)
 
     def quantize_rows_pow2(self, x_bits: np.ndarray):
@@ -266,12 +270,22 @@ class Oracle:
         return int(self.lib.oracle_pow2_scale_exponent(ctypes.c_float(amax_floored)))
 
     # ------------------------------------------------------------ combine
+    @staticmethod
+    def _bias(bias, n, h):
+        if bias is None:
+            return None
+        b = np.ascontiguousarray(bias, dtype=np.uint16)
+        assert b.shape == (n, h), "bias must be [N, H] bf16 bits"
+        return b
+
     def combine(self, y_bits: np.ndarray, topk_idx: np.ndarray, topk_weights: np.ndarray,
-                expert_slot: np.ndarray, num_experts: int, capacity: int):
+                expert_slot: np.ndarray, num_experts: int, capacity: int,
+                bias: np.ndarray | None = None):
         """Combine (Ascend deep dive, "Two Transfers" and "Combine: More
         Output, Same Cost"; Lesson 14 exercise; DeepEP V1 Legacy guide
-        §5.2(6)).  ``y_bits`` uint16 [E, S, H] bf16 expert outputs.  Returns
-        (combined bf16 bits uint16 [N, H], status)."""
+        §5.2(6)).  ``y_bits`` uint16 [E, S, H] bf16 expert outputs; ``bias``
+        optional [N, H] bf16 bits (the shared expert's output, added in the
+        epilogue).  Returns (combined bf16 bits uint16 [N, H], status)."""
         y = np.ascontiguousarray(y_bits, dtype=np.uint16)
         idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
         w = np.ascontiguousarray(topk_weights, dtype=np.float32)
@@ -279,8 +293,9 @@ class Oracle:
         n, k = idx.shape
         h = y.shape[-1]
         out = np.empty((n, h), np.uint16)
+        b = self._bias(bias, n, h)
         st = self.lib.oracle_combine(n, h, k, int(num_experts), int(capacity), _ptr(y),
-                                     _ptr(idx), _ptr(w), _ptr(slot), _ptr(out))
+                                     _ptr(idx), _ptr(w), _ptr(slot), _ptr(b), _ptr(out))
         return out, int(st)
 
     # ------------------------------------------------------------ formats

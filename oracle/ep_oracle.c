@@ -462,11 +462,23 @@ int oracle_pack(int32_t N, int32_t H, int32_t K, int32_t E, int32_t S, int32_t u
  *   acc = +0
  *   for k = 0..K-1 with a valid expert e and slot j:
  *       acc = fmaf(w[t,k], float(y[e][j][c]), acc)
+ *   acc = acc + float(bias[t][c])        (only when bias is not NULL)
  *   out[t,c] = bf16_RNE(acc)
- * A token with every entry masked gets +0. */
+ * A token with every entry masked gets +0 (or its bias row).  The bias is
+ * the shared expert's output folded into the combine's epilogue ([ASC]
+ * "Combine: More Output, Same Cost": added as a bias at the end, in the same
+ * pass), so it is added after the weighted sum, before the one rounding. */
+static void add_bias_row(float *acc, const uint16_t *bias_row, int32_t H)
+{
+    if (!bias_row)
+        return;
+    for (int32_t c = 0; c < H; ++c)
+        acc[c] = acc[c] + oracle_bf16_to_f32(bias_row[c]);
+}
+
 int oracle_combine(int32_t N, int32_t H, int32_t K, int32_t E, int32_t S, const uint16_t *y,
                    const int64_t *topk_idx, const float *topk_weights,
-                   const int32_t *expert_slot, uint16_t *combined_x)
+                   const int32_t *expert_slot, const uint16_t *bias, uint16_t *combined_x)
 {
     if (N < 0 || H < 1 || K < 1 || E < 1 || S < 0)
         return ORACLE_BAD_ARGS;
@@ -492,6 +504,7 @@ int oracle_combine(int32_t N, int32_t H, int32_t K, int32_t E, int32_t S, const 
             for (int32_t c = 0; c < H; ++c)
                 acc[c] = fmaf(w, oracle_bf16_to_f32(yr[c]), acc[c]);
         }
+        add_bias_row(acc, bias ? bias + (size_t)t * H : NULL, H);
         for (int32_t c = 0; c < H; ++c)
             combined_x[(size_t)t * H + c] = oracle_bf16_rne(acc[c]);
     }
@@ -572,11 +585,12 @@ int oracle_pack_expand(int32_t N, int32_t H, int32_t K, int32_t E, int32_t T, in
 }
 
 /* Combine from expert outputs in the expand layout: as oracle_combine, with
- * the output row of entry (t,k) at offset[e] + j of a T-row buffer. */
+ * the output row of entry (t,k) at offset[e] + j of a T-row buffer (and the
+ * same optional bias). */
 int oracle_combine_expand(int32_t N, int32_t H, int32_t K, int32_t E, int32_t T, const uint16_t *y,
                           const int64_t *topk_idx, const float *topk_weights,
                           const int32_t *expert_slot, const int32_t *expert_offset,
-                          uint16_t *combined_x)
+                          const uint16_t *bias, uint16_t *combined_x)
 {
     if (N < 0 || H < 1 || K < 1 || E < 1 || T < 0)
         return ORACLE_BAD_ARGS;
@@ -602,6 +616,7 @@ int oracle_combine_expand(int32_t N, int32_t H, int32_t K, int32_t E, int32_t T,
             for (int32_t c = 0; c < H; ++c)
                 acc[c] = fmaf(w, oracle_bf16_to_f32(yr[c]), acc[c]);
         }
+        add_bias_row(acc, bias ? bias + (size_t)t * H : NULL, H);
         for (int32_t c = 0; c < H; ++c)
             combined_x[(size_t)t * H + c] = oracle_bf16_rne(acc[c]);
     }
@@ -676,12 +691,14 @@ int oracle_dispatch_normal(int32_t N, int32_t H, int32_t K, int32_t E, int32_t R
  * to).  Per token t, ranks r ascending with j = rank_slot[t,r] >= 0:
  *   acc[c]  = acc[c] + float(y[r][j][c])            (from +0; fp32)
  *   wacc[k] = wacc[k] + recv_topk_weights[r][j][k]  (from +0; fp32)
+ *   acc[c]  = acc[c] + float(bias[t][c])           (only when bias is not NULL)
  *   combined_x[t][c] = bf16_RNE(acc[c]); combined_topk_weights[t][k] = wacc[k]
  * (the weight reduction only when both weight pointers are non-NULL).  A
- * token sent nowhere gets +0. */
+ * token sent nowhere gets +0 (or its bias row). */
 int oracle_combine_normal(int32_t N, int32_t H, int32_t K, int32_t R, int32_t M, const uint16_t *y,
                           const int32_t *rank_slot, const float *recv_topk_weights,
-                          uint16_t *combined_x, float *combined_topk_weights)
+                          const uint16_t *bias, uint16_t *combined_x,
+                          float *combined_topk_weights)
 {
     if (N < 0 || H < 1 || K < 1 || R < 1 || M < 0)
         return ORACLE_BAD_ARGS;
@@ -715,6 +732,7 @@ int oracle_combine_normal(int32_t N, int32_t H, int32_t K, int32_t R, int32_t M,
                 for (int32_t k = 0; k < K; ++k)
                     wacc[k] = wacc[k] + recv_topk_weights[row * K + k];
         }
+        add_bias_row(acc, bias ? bias + (size_t)t * H : NULL, H);
         for (int32_t c = 0; c < H; ++c)
             combined_x[(size_t)t * H + c] = oracle_bf16_rne(acc[c]);
         if (with_w)

@@ -45,6 +45,9 @@ def main(path: str) -> int:
         ("expand_matches_dense", lambda: pins.pin_expand_matches_dense(o, pack_cases)),
         ("normal_matches_dense", lambda: pins.pin_normal_matches_dense(o, ident_cases)),
         ("combine_normal_scalar", lambda: pins.pin_combine_normal_scalar_ranks(o, ident_cases)),
+        ("combine_bias_order", lambda: pins.pin_combine_bias_order(o)),
+        ("combine_bias_relations", lambda: pins.pin_combine_bias_relations(o, pack_cases)),
+        ("backward_pair_adjoint", lambda: pins.pin_backward_pair_adjoint(o, ident_cases)),
         ("layout_bruteforce", lambda: pins.pin_layout_bruteforce(o)),
     ]
     for name, fn in steps:

@@ -764,3 +764,129 @@ def pin_combine_normal_scalar_ranks(o, cases):
             .view(torch.int16).numpy().view(np.uint16)
         assert np.array_equal(bf16_to_f64(got), bf16_to_f64(want)), "normal combine != (sum c_r) x"
         assert np.array_equal(cw, np.where(idx >= 0, w, 0.0).astype(np.float32))
+
+
+# ------------------------------------------------ combine epilogue and backward
+
+def _bf16_of(v: float) -> int:
+    """bf16 bits of a float that is exact in bf16 (checked)."""
+    b = int(np.float32(v).view(np.uint32))
+    assert b & 0xFFFF == 0, f"{v} is not exact in bf16"
+    return b >> 16
+
+
+def pin_combine_bias_order(o):
+    """The shared expert's row is added after the weighted sum (Ascend deep
+    dive, "Combine: More Output, Same Cost": folded in at the end of the
+    combine's pass), before the one rounding.  Worked by hand: three entries
+    with weight 1 and rows 2^-8, 2^-24, 2^-24 and a bias of 1.  Summing the
+    rows first gives 2^-8 + 2^-23 exactly, then 1 + 2^-8 + 2^-23 exactly in
+    fp32, which rounds up to the bf16 value 1 + 2^-7.  Adding the bias first
+    would give 1 + 2^-8 (each 2^-24 is a tie to even against 1 + 2^-8), which
+    rounds to 1.  The same holds for the expand and normal-mode combines."""
+    H, E = 8, 3
+    rows = [2.0 ** -8, 2.0 ** -24, 2.0 ** -24]
+    idx = np.array([[0, 1, 2]], np.int64)
+    w = np.ones((1, 3), np.float32)
+    lay = o.layout(idx, E, 1)
+    y = np.zeros((E, 1, H), np.uint16)
+    for e, v in enumerate(rows):
+        y[e, 0, :] = _bf16_of(v)
+    bias = np.full((1, H), _bf16_of(1.0), np.uint16)
+    want = _bf16_of(1.0 + 2.0 ** -7)
+    out, st = o.combine(y, idx, w, lay["expert_slot"], E, 1, bias=bias)
+    assert st == 0 and np.all(out == want), ("combine", out[0, 0], want)
+    off = o.aligned_offsets(lay["num_tokens_per_expert"], 1)
+    out, st = o.combine_expand(y.reshape(E, H), idx, w, lay["expert_slot"], off, bias=bias)
+    assert st == 0 and np.all(out == want), ("combine_expand", out[0, 0], want)
+    # normal mode: one token sent to three ranks, rows 2^-8, 2^-24, 2^-24
+    lay3 = o.layout(idx, E, 3)
+    yn = y.reshape(3, 1, H)
+    out, _, st = o.combine_normal(yn, lay3["rank_slot"], bias=bias)
+    assert st == 0 and np.all(out == want), ("combine_normal", out[0, 0], want)
+    # and without the bias the three rows round to 2^-8 (2^-8 + 2^-23 is below
+    # half a bf16 ulp above 2^-8)
+    out, _ = o.combine(y, idx, w, lay["expert_slot"], E, 1)
+    assert np.all(out == _bf16_of(2.0 ** -8))
+
+
+def pin_combine_bias_relations(o, cases):
+    """Special cases and a float64 reference for the bias:
+    all weights 0 -> the output is the bias row exactly; an all-zero bias ->
+    the output equals the combine without bias bit for bit; random rows and
+    bias -> within the combine tolerance of sum_k w_k y_k + b in float64 (plus
+    the fp32 summation bound).  Normal mode: a token sent nowhere returns its
+    bias row."""
+    for inp, E, R, S, use_fp8 in cases:
+        idx, w = inp["topk_idx"], inp["topk_weights"]
+        rows = inp.get("expert_rows")
+        if rows is None:
+            continue
+        N, H = inp["x_bits"].shape
+        lay = o.layout(idx, E, R)
+        s_d = max(1, int(lay["num_tokens_per_expert"].max()))
+        y = place_rows(rows, idx, lay["expert_slot"], E, s_d)
+        rng = np.random.default_rng(17)
+        bias = torch.from_numpy(rng.standard_normal((N, H)).astype(np.float32)).to(
+            torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        out, st = o.combine(y, idx, np.zeros_like(w), lay["expert_slot"], E, s_d, bias=bias)
+        assert st == 0 and np.array_equal(bf16_to_f64(out), bf16_to_f64(bias)), "zero weights"
+        plain, _ = o.combine(y, idx, w, lay["expert_slot"], E, s_d)
+        zb, _ = o.combine(y, idx, w, lay["expert_slot"], E, s_d, bias=np.zeros_like(bias))
+        assert np.array_equal(bf16_to_f64(zb), bf16_to_f64(plain)), "zero bias"
+        got, _ = o.combine(y, idx, w, lay["expert_slot"], E, s_d, bias=bias)
+        yv = bf16_to_f64(y)
+        valid = idx >= 0
+        ref = bf16_to_f64(bias).copy()
+        mag = np.abs(ref).copy()
+        for k in range(idx.shape[1]):
+            t = np.nonzero(valid[:, k])[0]
+            term = w[t, k].astype(np.float64)[:, None] * yv[idx[t, k], lay["expert_slot"][t, k]]
+            ref[t] += term
+            mag[t] += np.abs(term)
+        assert_combine_close(got, ref, "combine with bias", abs_slack=(idx.shape[1] + 1) * 2.0 ** -24 * mag)
+        # normal mode: tokens sent nowhere come back as their bias row
+        d = o.dispatch_normal(inp["x_bits"], idx, None, lay["rank_slot"], E, R, max(N, 1), False)
+        yn = d["recv_x"]
+        outn, _, st = o.combine_normal(yn, lay["rank_slot"], bias=bias)
+        dead = lay["is_token_in_rank"].sum(axis=1) == 0
+        assert st == 0 and np.array_equal(outn[dead], bias[dead]), "tokens sent nowhere"
+
+
+def pin_backward_pair_adjoint(o, cases):
+    """V1 guide §5.1: dispatch's backward is a combine of the gradients (and
+    of the weight gradients), combine's backward is a dispatch.  For the
+    normal mode that makes ep_combine_normal the adjoint of
+    ep_dispatch_normal: for any x and any receive-side g,
+        sum_{r,j} <recv_x[r][j], g[r][j]> == sum_t <x[t], combined_g[t]>,
+    and for the weights, with weight gradients that are zero where the
+    receive side holds no weight (non-local entries),
+        sum <recv_topk_weights, gw> == sum <topk_weights, combined_gw>.
+    With small-integer data every sum is exact, so both identities hold
+    exactly in float64."""
+    for inp, E, R, S, use_fp8 in cases:
+        idx = inp["topk_idx"]
+        N, H = inp["x_bits"].shape
+        K = idx.shape[1]
+        lay = o.layout(idx, E, R)
+        M = max(N, 1)
+        rng = np.random.default_rng(23)
+        xi = rng.integers(-8, 9, size=(N, H)).astype(np.float32)
+        x = torch.from_numpy(xi).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        wi = rng.integers(-8, 9, size=(N, K)).astype(np.float32)
+        d = o.dispatch_normal(x, idx, wi, lay["rank_slot"], E, R, M, False)
+        written = np.zeros((R, M), bool)
+        for r in range(R):
+            written[r, :int(lay["num_tokens_per_rank"][r])] = True
+        gi = rng.integers(-8, 9, size=(R, M, H)).astype(np.float32) * written[:, :, None]
+        g = torch.from_numpy(gi).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        gwi = rng.integers(-8, 9, size=(R, M, K)).astype(np.float32)
+        gwi *= (d["recv_topk_idx"] >= 0) & written[:, :, None]
+        out, cgw, st = o.combine_normal(g, lay["rank_slot"], gwi)
+        assert st == 0
+        lhs = float((bf16_to_f64(d["recv_x"]) * written[:, :, None] * gi).sum())
+        rhs = float((xi.astype(np.float64) * bf16_to_f64(out)).sum())
+        assert lhs == rhs, ("dispatch/combine adjoint", lhs, rhs)
+        lw = float((np.where(written[:, :, None], d["recv_topk_weights"], 0.0) * gwi).sum())
+        rw = float((wi.astype(np.float64) * cgw).sum())
+        assert lw == rw, ("weights adjoint", lw, rw)

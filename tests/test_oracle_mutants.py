@@ -88,6 +88,16 @@ MUTANTS = [
                                     "acc[c] = oracle_bf16_to_f32(yr[c]);")]),
     ("normal_weights_overwrite", [("wacc[k] = wacc[k] + recv_topk_weights[row * K + k];",
                                    "wacc[k] = recv_topk_weights[row * K + k];")]),
+    # shared-expert bias (Ascend deep dive, "Combine: More Output, Same Cost")
+    ("bias_added_first", [
+        (COMBINE_INIT, COMBINE_INIT.replace(
+            "acc[c] = 0.0f;", "acc[c] = bias ? oracle_bf16_to_f32(bias[(size_t)t * H + c]) : 0.0f;")),
+        (COMBINE_YR + COMBINE_FMA + "\n        }\n        add_bias_row(acc, bias ? bias + (size_t)t * H : NULL, H);",
+         COMBINE_YR + COMBINE_FMA + "\n        }")]),
+    ("bias_overwrites", [("acc[c] = acc[c] + oracle_bf16_to_f32(bias_row[c]);",
+                          "acc[c] = oracle_bf16_to_f32(bias_row[c]);")]),
+    ("bias_row_of_token0", [(COMBINE_YR + COMBINE_FMA + "\n        }\n        add_bias_row(acc, bias ? bias + (size_t)t * H : NULL, H);",
+                             COMBINE_YR + COMBINE_FMA + "\n        }\n        add_bias_row(acc, bias, H);")]),
 ]
 
 

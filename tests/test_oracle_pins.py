@@ -167,3 +167,15 @@ def test_normal_layout_matches_dense(o):
 
 def test_normal_combine_scalar_ranks(o):
     pins.pin_combine_normal_scalar_ranks(o, _pack_cases(dead=True))
+
+
+def test_combine_bias_order(o):
+    pins.pin_combine_bias_order(o)
+
+
+def test_combine_bias_relations(o):
+    pins.pin_combine_bias_relations(o, _pack_cases())
+
+
+def test_backward_pair_adjoint(o):
+    pins.pin_backward_pair_adjoint(o, _pack_cases(dead=True))
