@@ -7,6 +7,9 @@
 // reduce on chip instead of gathering every output back to HBM first).
 //
 //   acc = +0; for k ascending with a valid expert: acc = fmaf(w[t,k], y, acc);
+//   acc = acc + bias[t]   (optional: the shared expert's output, folded into
+//                          the epilogue -- Ascend deep dive, "Combine: More
+//                          Output, Same Cost")
 //   out = bf16 round-to-nearest-even(acc)
 //
 // Normal-mode combine (V1 guide §5.1): one row per (token, rank) comes back
@@ -15,7 +18,7 @@
 // top-k weights may be reduced the same way.
 //
 //   acc = +0; for r ascending with a row at rank r: acc = acc + y[r][row];
-//   out = bf16 round-to-nearest-even(acc)
+//   acc = acc + bias[t] (optional); out = bf16 round-to-nearest-even(acc)
 //
 // Work item = one wave on one (token, 1024-channel chunk); each lane owns two
 // 8-channel units (16-byte loads, so every load instruction reads 1 KiB
@@ -86,6 +89,16 @@ __device__ __forceinline__ Units units_of(int32_t H, uint32_t chunk, int lane)
     return u;
 }
 
+// The bias row's two units of this lane (read once: non-temporal), issued
+// before the row loads so its latency overlaps theirs.
+__device__ __forceinline__ void load_bias(const uint16_t *__restrict__ bias_row, const Units &u,
+                                          uint4 &b0, uint4 &b1)
+{
+    const uint4 *r = reinterpret_cast<const uint4 *>(bias_row);
+    b0 = load_stream(r + u.l0);
+    b1 = load_stream(r + u.l1);
+}
+
 __device__ __forceinline__ void store_out(uint16_t *__restrict__ out_row, const Units &u,
                                           const float (&acc0)[8], const float (&acc1)[8])
 {
@@ -96,12 +109,12 @@ __device__ __forceinline__ void store_out(uint16_t *__restrict__ out_row, const 
         dst[u.u1] = to_bf16_unit(acc1);
 }
 
-template <int KB, class Rows>
+template <int KB, bool BIAS, class Rows>
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     int32_t N, int32_t H, int32_t K, int32_t E, int32_t nchunks, Rows rows,
     const uint16_t *__restrict__ y, const int64_t *__restrict__ topk_idx,
     const float *__restrict__ topk_weights, const int32_t *__restrict__ expert_slot,
-    uint16_t *__restrict__ out, uint32_t *status)
+    const uint16_t *__restrict__ bias, uint16_t *__restrict__ out, uint32_t *status)
 {
     const int lane = threadIdx.x & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -111,6 +124,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
     const uint32_t t = item / (uint32_t)nchunks;
     const uint32_t chunk = item - t * (uint32_t)nchunks;
     const Units u = units_of(H, chunk, lane);
+    uint4 b0, b1;
+    if (BIAS)
+        load_bias(bias + (size_t)t * H, u, b0, b1);
 
     float acc0[8], acc1[8];
 #pragma unroll
@@ -143,6 +159,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
             }
         }
     }
+    if (BIAS) {
+        add_unit(acc0, b0);
+        add_unit(acc1, b1);
+    }
     store_out(out + (size_t)t * H, u, acc0, acc1);
     if (flags && status && lane == 0 && chunk == 0)
         atomicOr(status, flags);
@@ -151,12 +171,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
 // Normal-mode combine: rows y[r * M + rank_slot[t, r]] for the ranks r the
 // token was sent to, KB ranks per batch in ascending order.  The chunk-0 wave
 // also reduces recv_topk_weights (lane k < K) over the same rows.
-template <int KB>
+template <int KB, bool BIAS>
 __global__ __launch_bounds__(kThreads) void combine_normal_kernel(
     int32_t N, int32_t H, int32_t K, int32_t R, int32_t M, int32_t nchunks,
     const uint16_t *__restrict__ y, const int32_t *__restrict__ rank_slot,
-    const float *__restrict__ recv_topk_weights, uint16_t *__restrict__ out,
-    float *__restrict__ combined_topk_weights, uint32_t *status)
+    const float *__restrict__ recv_topk_weights, const uint16_t *__restrict__ bias,
+    uint16_t *__restrict__ out, float *__restrict__ combined_topk_weights, uint32_t *status)
 {
     const int lane = threadIdx.x & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -167,6 +187,9 @@ __global__ __launch_bounds__(kThreads) void combine_normal_kernel(
     const uint32_t chunk = item - t * (uint32_t)nchunks;
     const Units u = units_of(H, chunk, lane);
     const bool with_w = chunk == 0 && recv_topk_weights && combined_topk_weights;
+    uint4 b0, b1;
+    if (BIAS)
+        load_bias(bias + (size_t)t * H, u, b0, b1);
 
     uint32_t flags = 0;
     int32_t j;
@@ -209,6 +232,10 @@ __global__ __launch_bounds__(kThreads) void combine_normal_kernel(
             }
         }
     }
+    if (BIAS) {
+        add_unit(acc0, b0);
+        add_unit(acc1, b1);
+    }
     store_out(out + (size_t)t * H, u, acc0, acc1);
     if (with_w && lane < K)
         combined_topk_weights[(size_t)t * K + lane] = wacc;
@@ -219,8 +246,8 @@ __global__ __launch_bounds__(kThreads) void combine_normal_kernel(
 template <class Rows>
 hipError_t launch_topk_combine(const ep_shape &s, const Rows &rows, const uint16_t *expert_out,
                                const int64_t *topk_idx, const float *topk_weights,
-                               const int32_t *expert_slot, uint16_t *combined_x, uint32_t *status,
-                               hipStream_t stream)
+                               const int32_t *expert_slot, const uint16_t *bias,
+                               uint16_t *combined_x, uint32_t *status, hipStream_t stream)
 {
     const int N = s.num_tokens, H = s.hidden, K = s.num_topk, E = s.num_experts;
     if (N == 0)
@@ -228,18 +255,26 @@ hipError_t launch_topk_combine(const ep_shape &s, const Rows &rows, const uint16
     const int nchunks = (H + kChunk - 1) / kChunk;
     const int64_t items = (int64_t)N * nchunks;
     const dim3 grid((unsigned)((items + kWaves - 1) / kWaves));
-#define EP_COMBINE(KB)                                                                             \
-    hipLaunchKernelGGL((combine_kernel<KB, Rows>), grid, dim3(kThreads), 0, stream, N, H, K, E,    \
-                       nchunks, rows, expert_out, topk_idx, topk_weights, expert_slot, combined_x, \
-                       status)
-    if (K == 1)
-        EP_COMBINE(1);
-    else if (K == 2)
-        EP_COMBINE(2);
-    else if (K <= 4)
-        EP_COMBINE(4);
+#define EP_COMBINE(KB, BIAS)                                                                       \
+    hipLaunchKernelGGL((combine_kernel<KB, BIAS, Rows>), grid, dim3(kThreads), 0, stream, N, H, K, \
+                       E, nchunks, rows, expert_out, topk_idx, topk_weights, expert_slot, bias,    \
+                       combined_x, status)
+#define EP_COMBINE_KB(BIAS)                                                                        \
+    do {                                                                                           \
+        if (K == 1)                                                                                \
+            EP_COMBINE(1, BIAS);                                                                   \
+        else if (K == 2)                                                                           \
+            EP_COMBINE(2, BIAS);                                                                   \
+        else if (K <= 4)                                                                           \
+            EP_COMBINE(4, BIAS);                                                                   \
+        else                                                                                       \
+            EP_COMBINE(8, BIAS);                                                                   \
+    } while (0)
+    if (bias)
+        EP_COMBINE_KB(true);
     else
-        EP_COMBINE(8);
+        EP_COMBINE_KB(false);
+#undef EP_COMBINE_KB
 #undef EP_COMBINE
     return hipGetLastError();
 }
@@ -248,25 +283,27 @@ hipError_t launch_topk_combine(const ep_shape &s, const Rows &rows, const uint16
 
 hipError_t launch_combine(const ep_shape &s, const uint16_t *expert_out, const int64_t *topk_idx,
                           const float *topk_weights, const int32_t *expert_slot,
-                          uint16_t *combined_x, uint32_t *status, hipStream_t stream)
+                          const uint16_t *bias, uint16_t *combined_x, uint32_t *status,
+                          hipStream_t stream)
 {
     return launch_topk_combine(s, DenseRows{s.expert_capacity}, expert_out, topk_idx, topk_weights,
-                               expert_slot, combined_x, status, stream);
+                               expert_slot, bias, combined_x, status, stream);
 }
 
 hipError_t launch_combine_expand(const ep_shape &s, const uint16_t *expert_out,
                                  const int64_t *topk_idx, const float *topk_weights,
                                  const int32_t *expert_slot, const int32_t *expert_offset,
-                                 uint16_t *combined_x, uint32_t *status, hipStream_t stream)
+                                 const uint16_t *bias, uint16_t *combined_x, uint32_t *status,
+                                 hipStream_t stream)
 {
     return launch_topk_combine(s, ExpandRows{expert_offset, expand_rows(s)}, expert_out, topk_idx,
-                               topk_weights, expert_slot, combined_x, status, stream);
+                               topk_weights, expert_slot, bias, combined_x, status, stream);
 }
 
 hipError_t launch_combine_normal(const ep_shape &s, const uint16_t *x, const int32_t *rank_slot,
-                                 const float *recv_topk_weights, uint16_t *combined_x,
-                                 float *combined_topk_weights, uint32_t *status,
-                                 hipStream_t stream)
+                                 const float *recv_topk_weights, const uint16_t *bias,
+                                 uint16_t *combined_x, float *combined_topk_weights,
+                                 uint32_t *status, hipStream_t stream)
 {
     const int N = s.num_tokens, H = s.hidden, K = s.num_topk, R = s.num_ranks;
     const int M = s.num_max_dispatch_tokens_per_rank;
@@ -275,9 +312,14 @@ hipError_t launch_combine_normal(const ep_shape &s, const uint16_t *x, const int
     const int nchunks = (H + kChunk - 1) / kChunk;
     const int64_t items = (int64_t)N * nchunks;
     const dim3 grid((unsigned)((items + kWaves - 1) / kWaves));
-    hipLaunchKernelGGL(combine_normal_kernel<8>, grid, dim3(kThreads), 0, stream, N, H, K, R, M,
-                       nchunks, x, rank_slot, recv_topk_weights, combined_x, combined_topk_weights,
-                       status);
+    if (bias)
+        hipLaunchKernelGGL((combine_normal_kernel<8, true>), grid, dim3(kThreads), 0, stream, N, H,
+                           K, R, M, nchunks, x, rank_slot, recv_topk_weights, bias, combined_x,
+                           combined_topk_weights, status);
+    else
+        hipLaunchKernelGGL((combine_normal_kernel<8, false>), grid, dim3(kThreads), 0, stream, N,
+                           H, K, R, M, nchunks, x, rank_slot, recv_topk_weights, bias, combined_x,
+                           combined_topk_weights, status);
     return hipGetLastError();
 }
 

@@ -179,8 +179,8 @@ int ep_dispatch(const ep_shape *s, const uint16_t *x, const int64_t *topk_idx,
 }
 
 int ep_combine(const ep_shape *s, const uint16_t *expert_out, const int64_t *topk_idx,
-               const float *topk_weights, const int32_t *expert_slot, uint16_t *combined_x,
-               uint32_t *status, void *stream)
+               const float *topk_weights, const int32_t *expert_slot, const uint16_t *bias,
+               uint16_t *combined_x, uint32_t *status, void *stream)
 {
     const int rc = check_shape(s);
     if (rc != EP_OK)
@@ -189,12 +189,13 @@ int ep_combine(const ep_shape *s, const uint16_t *expert_out, const int64_t *top
         return EP_OK;
     if (!expert_out || !topk_idx || !topk_weights || !expert_slot || !combined_x)
         return EP_ERR_NULL;
-    if (!aligned(expert_out, 16) || !aligned(combined_x, 16) || !aligned(topk_idx, 8) ||
-        !aligned(topk_weights, 4) || !aligned(expert_slot, 4) || !aligned(status, 4))
+    if (!aligned(expert_out, 16) || !aligned(combined_x, 16) || !aligned(bias, 16) ||
+        !aligned(topk_idx, 8) || !aligned(topk_weights, 4) || !aligned(expert_slot, 4) ||
+        !aligned(status, 4))
         return EP_ERR_ALIGN;
     const hipError_t err =
-        ep::launch_combine(*s, expert_out, topk_idx, topk_weights, expert_slot, combined_x, status,
-                           static_cast<hipStream_t>(stream));
+        ep::launch_combine(*s, expert_out, topk_idx, topk_weights, expert_slot, bias, combined_x,
+                           status, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? EP_OK : EP_ERR_HIP;
 }
 
@@ -227,8 +228,8 @@ int ep_dispatch_expand(const ep_shape *s, const uint16_t *x, const int64_t *topk
 
 int ep_combine_expand(const ep_shape *s, const uint16_t *expert_out, const int64_t *topk_idx,
                       const float *topk_weights, const int32_t *expert_slot,
-                      const int32_t *expert_offset, uint16_t *combined_x, uint32_t *status,
-                      void *stream)
+                      const int32_t *expert_offset, const uint16_t *bias, uint16_t *combined_x,
+                      uint32_t *status, void *stream)
 {
     const int rc = check_shape(s);
     if (rc != EP_OK)
@@ -237,13 +238,13 @@ int ep_combine_expand(const ep_shape *s, const uint16_t *expert_out, const int64
         return EP_OK;
     if (!expert_out || !topk_idx || !topk_weights || !expert_slot || !expert_offset || !combined_x)
         return EP_ERR_NULL;
-    if (!aligned(expert_out, 16) || !aligned(combined_x, 16) || !aligned(topk_idx, 8) ||
-        !aligned(topk_weights, 4) || !aligned(expert_slot, 4) || !aligned(expert_offset, 4) ||
-        !aligned(status, 4))
+    if (!aligned(expert_out, 16) || !aligned(combined_x, 16) || !aligned(bias, 16) ||
+        !aligned(topk_idx, 8) || !aligned(topk_weights, 4) || !aligned(expert_slot, 4) ||
+        !aligned(expert_offset, 4) || !aligned(status, 4))
         return EP_ERR_ALIGN;
     const hipError_t err =
         ep::launch_combine_expand(*s, expert_out, topk_idx, topk_weights, expert_slot,
-                                  expert_offset, combined_x, status,
+                                  expert_offset, bias, combined_x, status,
                                   static_cast<hipStream_t>(stream));
     return err == hipSuccess ? EP_OK : EP_ERR_HIP;
 }
@@ -274,8 +275,9 @@ int ep_dispatch_normal(const ep_shape *s, const uint16_t *x, const int64_t *topk
 }
 
 int ep_combine_normal(const ep_shape *s, const uint16_t *x, const int32_t *rank_slot,
-                      const float *recv_topk_weights, uint16_t *combined_x,
-                      float *combined_topk_weights, uint32_t *status, void *stream)
+                      const float *recv_topk_weights, const uint16_t *bias,
+                      uint16_t *combined_x, float *combined_topk_weights, uint32_t *status,
+                      void *stream)
 {
     const int rc = check_shape(s);
     if (rc != EP_OK)
@@ -286,10 +288,11 @@ int ep_combine_normal(const ep_shape *s, const uint16_t *x, const int32_t *rank_
         return EP_ERR_NULL;
     if (recv_topk_weights && !combined_topk_weights)
         return EP_ERR_NULL;
-    if (!aligned(x, 16) || !aligned(combined_x, 16) || !aligned(rank_slot, 4) ||
-        !aligned(recv_topk_weights, 4) || !aligned(combined_topk_weights, 4) || !aligned(status, 4))
+    if (!aligned(x, 16) || !aligned(combined_x, 16) || !aligned(bias, 16) ||
+        !aligned(rank_slot, 4) || !aligned(recv_topk_weights, 4) ||
+        !aligned(combined_topk_weights, 4) || !aligned(status, 4))
         return EP_ERR_ALIGN;
-    const hipError_t err = ep::launch_combine_normal(*s, x, rank_slot, recv_topk_weights,
+    const hipError_t err = ep::launch_combine_normal(*s, x, rank_slot, recv_topk_weights, bias,
                                                      combined_x, combined_topk_weights, status,
                                                      static_cast<hipStream_t>(stream));
     return err == hipSuccess ? EP_OK : EP_ERR_HIP;

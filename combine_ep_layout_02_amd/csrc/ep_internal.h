@@ -67,16 +67,18 @@ hipError_t launch_dispatch_normal(const ep_shape &s, const uint16_t *x, const in
 // ---- combine ---------------------------------------------------------------
 hipError_t launch_combine(const ep_shape &s, const uint16_t *expert_out, const int64_t *topk_idx,
                           const float *topk_weights, const int32_t *expert_slot,
-                          uint16_t *combined_x, uint32_t *status, hipStream_t stream);
+                          const uint16_t *bias, uint16_t *combined_x, uint32_t *status,
+                          hipStream_t stream);
 
 hipError_t launch_combine_expand(const ep_shape &s, const uint16_t *expert_out,
                                  const int64_t *topk_idx, const float *topk_weights,
                                  const int32_t *expert_slot, const int32_t *expert_offset,
-                                 uint16_t *combined_x, uint32_t *status, hipStream_t stream);
+                                 const uint16_t *bias, uint16_t *combined_x, uint32_t *status,
+                                 hipStream_t stream);
 
 hipError_t launch_combine_normal(const ep_shape &s, const uint16_t *x, const int32_t *rank_slot,
-                                 const float *recv_topk_weights, uint16_t *combined_x,
-                                 float *combined_topk_weights, uint32_t *status,
-                                 hipStream_t stream);
+                                 const float *recv_topk_weights, const uint16_t *bias,
+                                 uint16_t *combined_x, float *combined_topk_weights,
+                                 uint32_t *status, hipStream_t stream);
 
 } // namespace ep

@@ -80,11 +80,11 @@ def lib() -> ctypes.CDLL:
         L.ep_query_sizes.argtypes = [sp, ctypes.POINTER(ep_sizes)]
         L.ep_layout.argtypes = [sp] + [vp] * 8 + [sz, vp, vp]
         L.ep_dispatch.argtypes = [sp] + [vp] * 8
-        L.ep_combine.argtypes = [sp] + [vp] * 7
+        L.ep_combine.argtypes = [sp] + [vp] * 8
         L.ep_dispatch_expand.argtypes = [sp] + [vp] * 10
-        L.ep_combine_expand.argtypes = [sp] + [vp] * 8
+        L.ep_combine_expand.argtypes = [sp] + [vp] * 9
         L.ep_dispatch_normal.argtypes = [sp] + [vp] * 11
-        L.ep_combine_normal.argtypes = [sp] + [vp] * 7
+        L.ep_combine_normal.argtypes = [sp] + [vp] * 8
         L.ep_probe_e4m3fn.argtypes = [vp, vp, vp, i64, vp]
         L.ep_strerror.argtypes = [ctypes.c_int]
         L.ep_strerror.restype = ctypes.c_char_p
@@ -238,14 +238,15 @@ def ep_dispatch_expand(shape: ep_shape, x: torch.Tensor, topk_idx: torch.Tensor,
 def ep_combine_expand(shape: ep_shape, expert_out: torch.Tensor, topk_idx: torch.Tensor,
                       topk_weights: torch.Tensor, expert_slot: torch.Tensor,
                       expert_offset: torch.Tensor, combined_x: torch.Tensor,
-                      status: Optional[torch.Tensor] = None, stream=None) -> None:
+                      status: Optional[torch.Tensor] = None, stream=None,
+                      bias: Optional[torch.Tensor] = None) -> None:
     """Combine from the expand layout; see ``ep_combine_expand`` in include/ep.h."""
     N, H, K, E = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts
     rc = lib().ep_combine_expand(
         ctypes.byref(shape), _ptr(expert_out, "expert_out", _BF16, expand_rows(shape) * H),
         _ptr(topk_idx, "topk_idx", _I64, N * K), _ptr(topk_weights, "topk_weights", _F32, N * K),
         _ptr(expert_slot, "expert_slot", _I32, N * K),
-        _ptr(expert_offset, "expert_offset", _I32, E + 1),
+        _ptr(expert_offset, "expert_offset", _I32, E + 1), _ptr(bias, "bias", _BF16, N * H),
         _ptr(combined_x, "combined_x", _BF16, N * H), _ptr(status, "status", _STATUS, 1),
         _stream(stream, combined_x))
     if rc != EP_OK:
@@ -277,14 +278,15 @@ def ep_dispatch_normal(shape: ep_shape, x: torch.Tensor, topk_idx: torch.Tensor,
 def ep_combine_normal(shape: ep_shape, x: torch.Tensor, rank_slot: torch.Tensor,
                       recv_topk_weights: Optional[torch.Tensor], combined_x: torch.Tensor,
                       combined_topk_weights: Optional[torch.Tensor] = None,
-                      status: Optional[torch.Tensor] = None, stream=None) -> None:
+                      status: Optional[torch.Tensor] = None, stream=None,
+                      bias: Optional[torch.Tensor] = None) -> None:
     """Normal-mode combine; see ``ep_combine_normal`` in include/ep.h."""
     N, H, K, R = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_ranks
     rows = R * shape.num_max_dispatch_tokens_per_rank
     rc = lib().ep_combine_normal(
         ctypes.byref(shape), _ptr(x, "x", _BF16, rows * H), _ptr(rank_slot, "rank_slot", _I32, N * R),
         _ptr(recv_topk_weights, "recv_topk_weights", _F32, rows * K),
-        _ptr(combined_x, "combined_x", _BF16, N * H),
+        _ptr(bias, "bias", _BF16, N * H), _ptr(combined_x, "combined_x", _BF16, N * H),
         _ptr(combined_topk_weights, "combined_topk_weights", _F32, N * K),
         _ptr(status, "status", _STATUS, 1), _stream(stream, combined_x))
     if rc != EP_OK:
@@ -293,14 +295,15 @@ def ep_combine_normal(shape: ep_shape, x: torch.Tensor, rank_slot: torch.Tensor,
 
 def ep_combine(shape: ep_shape, expert_out: torch.Tensor, topk_idx: torch.Tensor,
                topk_weights: torch.Tensor, expert_slot: torch.Tensor, combined_x: torch.Tensor,
-               status: Optional[torch.Tensor] = None, stream=None) -> None:
+               status: Optional[torch.Tensor] = None, stream=None,
+               bias: Optional[torch.Tensor] = None) -> None:
     """Combine; see ``ep_combine`` in include/ep.h."""
     N, H, K, E, S = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts, \
         shape.expert_capacity
     rc = lib().ep_combine(
         ctypes.byref(shape), _ptr(expert_out, "expert_out", _BF16, E * S * H),
         _ptr(topk_idx, "topk_idx", _I64, N * K), _ptr(topk_weights, "topk_weights", _F32, N * K),
-        _ptr(expert_slot, "expert_slot", _I32, N * K),
+        _ptr(expert_slot, "expert_slot", _I32, N * K), _ptr(bias, "bias", _BF16, N * H),
         _ptr(combined_x, "combined_x", _BF16, N * H), _ptr(status, "status", _STATUS, 1),
         _stream(stream, combined_x))
     if rc != EP_OK:

@@ -215,15 +215,19 @@ int ep_dispatch(const ep_shape *shape, const uint16_t *x, const int64_t *topk_id
  * handle).
  *
  * In:  expert_out [E, S, H] bf16 bits (rows < count are read); topk_idx
- *      [N, K]; topk_weights [N, K] fp32; expert_slot [N, K] from ep_layout.
+ *      [N, K]; topk_weights [N, K] fp32; expert_slot [N, K] from ep_layout;
+ *      bias [N, H] bf16 bits, nullable, 16-byte aligned: the shared expert's
+ *      output, added in the epilogue ([ASC] "Combine: More Output, Same
+ *      Cost": folded in at the end of the same pass).
  * Out: combined_x [N, H] bf16 bits:
  *        acc = +0; for k = 0..K-1 with a valid expert e:
  *            acc = fmaf(topk_weights[t,k], float(expert_out[e][slot][c]), acc);
+ *        acc = acc + float(bias[t][c])   (when bias is not NULL);
  *        combined_x[t,c] = bf16 round-to-nearest-even(acc).
- *      A token whose entries are all masked gets +0. */
+ *      A token whose entries are all masked gets +0 (or its bias row). */
 int ep_combine(const ep_shape *shape, const uint16_t *expert_out, const int64_t *topk_idx,
-               const float *topk_weights, const int32_t *expert_slot, uint16_t *combined_x,
-               uint32_t *status, void *stream);
+               const float *topk_weights, const int32_t *expert_slot, const uint16_t *bias,
+               uint16_t *combined_x, uint32_t *status, void *stream);
 
 /* Dispatch pack into the expand layout ([ASC] "Dispatch's Three Phases and
  * FP8 Compression", phase 1: each token is cloned once per routed expert, the
@@ -248,13 +252,14 @@ int ep_dispatch_expand(const ep_shape *shape, const uint16_t *x, const int64_t *
                        const int32_t *num_tokens_per_expert, void *recv_x, void *recv_scales,
                        int32_t *recv_src_idx, uint32_t *status, void *stream);
 
-/* Combine from expert outputs in the expand layout: as ep_combine, with the
- * output row of entry (t, k) at expert_offset[e] + expert_slot[t,k] of
- * expert_out [T, H] bf16 (same bounds rule as ep_dispatch_expand). */
+/* Combine from expert outputs in the expand layout: as ep_combine (bias
+ * included), with the output row of entry (t, k) at expert_offset[e] +
+ * expert_slot[t,k] of expert_out [T, H] bf16 (same bounds rule as
+ * ep_dispatch_expand). */
 int ep_combine_expand(const ep_shape *shape, const uint16_t *expert_out, const int64_t *topk_idx,
                       const float *topk_weights, const int32_t *expert_slot,
-                      const int32_t *expert_offset, uint16_t *combined_x, uint32_t *status,
-                      void *stream);
+                      const int32_t *expert_offset, const uint16_t *bias, uint16_t *combined_x,
+                      uint32_t *status, void *stream);
 
 /* Normal-mode dispatch ([V1] §5.1: dispatch returns recv_x, recv_topk_idx,
  * recv_topk_weights and the per-expert receive counts, and its handle holds
@@ -289,16 +294,21 @@ int ep_dispatch_normal(const ep_shape *shape, const uint16_t *x, const int64_t *
  *
  * In:  x [R, M, H] bf16 bits, one row per received token (rows < count are
  *      read); rank_slot [N, R] from ep_layout; recv_topk_weights [R, M, K]
- *      fp32 (nullable).
+ *      fp32 (nullable); bias [N, H] bf16 bits (nullable, as in ep_combine).
  * Out: combined_x [N, H] bf16 bits:
  *        acc = +0; for r = 0..R-1 with j = rank_slot[t,r] in [0, M):
  *            acc = acc + float(x[r][j][c]);
+ *        acc = acc + float(bias[t][c])   (when bias is not NULL);
  *        combined_x[t,c] = bf16 round-to-nearest-even(acc);
  *      combined_topk_weights [N, K] fp32 (nullable; written when
  *        recv_topk_weights is given): the same fp32 sum over the same rows.
- *      A token sent nowhere gets +0. */
+ *      A token sent nowhere gets +0 (or its bias row).
+ * The backward pair of [V1] §5.1 is this pair of entry points: dispatch's
+ * backward is ep_combine_normal of (grad_recv_x, grad_recv_topk_weights);
+ * combine's backward is ep_dispatch_normal (BF16) of grad_combined_x.  The
+ * sum over ranks is exactly the adjoint of the copy to each rank. */
 int ep_combine_normal(const ep_shape *shape, const uint16_t *x, const int32_t *rank_slot,
-                      const float *recv_topk_weights, uint16_t *combined_x,
+                      const float *recv_topk_weights, const uint16_t *bias, uint16_t *combined_x,
                       float *combined_topk_weights, uint32_t *status, void *stream);
 
 /* Host only.  A static string naming a return code. */

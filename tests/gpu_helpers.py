@@ -143,11 +143,14 @@ def place_expert_rows(rows_bits: np.ndarray, topk_idx: np.ndarray, expert_slot: 
 
 
 def run_combine(shape: ep.ep_shape, y_dev: torch.Tensor, topk_idx_dev: torch.Tensor,
-                weights: np.ndarray, expert_slot_dev: torch.Tensor, stream=None):
+                weights: np.ndarray, expert_slot_dev: torch.Tensor, stream=None,
+                bias: np.ndarray | None = None):
     N, H = shape.num_tokens, shape.hidden
     w = dev(np.asarray(weights, dtype=np.float32))
     out = torch.full((N, H), int(POISON_X16), dtype=torch.int16, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    ep.ep_combine(shape, y_dev, topk_idx_dev, w, expert_slot_dev, out, status, stream=stream)
+    b = None if bias is None else dev(bias)
+    ep.ep_combine(shape, y_dev, topk_idx_dev, w, expert_slot_dev, out, status, stream=stream,
+                  bias=b)
     torch.cuda.synchronize()
     return host(out), status_bits(status)

@@ -131,11 +131,11 @@ def test_static_shape_errors_are_reported_before_any_launch(kw, code):
     args9 = [OK16] * 8
     assert lib.ep_layout(ctypes.byref(s), *args9[:7], OK16, ctypes.c_size_t(1 << 30), None, None) == code
     assert lib.ep_dispatch(ctypes.byref(s), *[OK16] * 6, None, None) == code
-    assert lib.ep_combine(ctypes.byref(s), *[OK16] * 5, None, None) == code
+    assert lib.ep_combine(ctypes.byref(s), *[OK16] * 6, None, None) == code
     assert lib.ep_dispatch_expand(ctypes.byref(s), *[OK16] * 8, None, None) == code
-    assert lib.ep_combine_expand(ctypes.byref(s), *[OK16] * 6, None, None) == code
+    assert lib.ep_combine_expand(ctypes.byref(s), *[OK16] * 7, None, None) == code
     assert lib.ep_dispatch_normal(ctypes.byref(s), *[OK16] * 9, None, None) == code
-    assert lib.ep_combine_normal(ctypes.byref(s), *[OK16] * 5, None, None) == code
+    assert lib.ep_combine_normal(ctypes.byref(s), *[OK16] * 6, None, None) == code
 
 
 def test_null_pointers_are_rejected():
@@ -154,8 +154,8 @@ def test_null_pointers_are_rejected():
         assert lib.ep_dispatch(ctypes.byref(s), *q, None, None) == ep.EP_ERR_NULL
     sf = _shape(use_fp8=1)
     assert lib.ep_dispatch(ctypes.byref(sf), OK16, OK16, OK16, OK16, None, OK16, None, None) == ep.EP_ERR_NULL
-    for i in range(5):
-        q = [OK16] * 5
+    for i in (0, 1, 2, 3, 5):  # expert_out, topk_idx, topk_weights, expert_slot, (bias), out
+        q = [OK16] * 6
         q[i] = None
         assert lib.ep_combine(ctypes.byref(s), *q, None, None) == ep.EP_ERR_NULL
 
@@ -172,8 +172,8 @@ def test_null_pointers_are_rejected_by_the_other_layouts():
     q = [OK16] * 8
     q[6] = None
     assert lib.ep_dispatch_expand(ctypes.byref(sf), *q, None, None) == ep.EP_ERR_NULL
-    for i in range(6):  # expert_out, topk_idx, topk_weights, expert_slot, expert_offset, out
-        q = [OK16] * 6
+    for i in (0, 1, 2, 3, 4, 6):  # expert_out .. expert_offset, (bias), out
+        q = [OK16] * 7
         q[i] = None
         assert lib.ep_combine_expand(ctypes.byref(s), *q, None, None) == ep.EP_ERR_NULL
     # normal: x, topk_idx, (weights), rank_slot, recv_x, (scales), recv_topk_idx, (w), src
@@ -184,8 +184,8 @@ def test_null_pointers_are_rejected_by_the_other_layouts():
     q = [OK16] * 9
     q[5] = None
     assert lib.ep_dispatch_normal(ctypes.byref(sf), *q, None, None) == ep.EP_ERR_NULL
-    for i in (0, 1, 3, 4):  # x, rank_slot, combined_x, and combined weights when weights are given
-        q = [OK16] * 5
+    for i in (0, 1, 4, 5):  # x, rank_slot, (w), (bias), combined_x, combined weights given w
+        q = [OK16] * 6
         q[i] = None
         assert lib.ep_combine_normal(ctypes.byref(s), *q, None, None) == ep.EP_ERR_NULL
 
@@ -193,8 +193,8 @@ def test_null_pointers_are_rejected_by_the_other_layouts():
 def test_misaligned_pointers_are_rejected_by_the_other_layouts():
     s = _shape(use_fp8=1, hidden=256)
     lib = ep.lib()
-    for n, fn in ((8, lib.ep_dispatch_expand), (6, lib.ep_combine_expand),
-                  (9, lib.ep_dispatch_normal), (5, lib.ep_combine_normal)):
+    for n, fn in ((8, lib.ep_dispatch_expand), (7, lib.ep_combine_expand),
+                  (9, lib.ep_dispatch_normal), (6, lib.ep_combine_normal)):
         for i in range(n):
             q = [OK16] * n
             q[i] = BAD
@@ -202,8 +202,12 @@ def test_misaligned_pointers_are_rejected_by_the_other_layouts():
     # token rows need 16 bytes
     assert lib.ep_dispatch_expand(ctypes.byref(s), ctypes.c_void_p(0x1008), *[OK16] * 7, None,
                                   None) == ep.EP_ERR_ALIGN
-    assert lib.ep_combine_normal(ctypes.byref(s), ctypes.c_void_p(0x1008), *[OK16] * 4, None,
+    assert lib.ep_combine_normal(ctypes.byref(s), ctypes.c_void_p(0x1008), *[OK16] * 5, None,
                                  None) == ep.EP_ERR_ALIGN
+    # the bias row is a token row: 16 bytes
+    q = [OK16] * 6
+    q[3] = ctypes.c_void_p(0x1008)
+    assert lib.ep_combine_normal(ctypes.byref(s), *q, None, None) == ep.EP_ERR_ALIGN
     # recv_topk_idx is int64
     q = [OK16] * 9
     q[6] = ctypes.c_void_p(0x1004)
@@ -245,11 +249,14 @@ def test_misaligned_pointers_are_rejected():
         q[i] = BAD
         assert lib.ep_dispatch(ctypes.byref(s), *q, None, None) == ep.EP_ERR_ALIGN
     assert lib.ep_dispatch(ctypes.byref(s), ctypes.c_void_p(0x1008), *[OK16] * 5, None, None) == ep.EP_ERR_ALIGN
-    for i in range(5):
-        q = [OK16] * 5
+    for i in range(6):
+        q = [OK16] * 6
         q[i] = BAD
         assert lib.ep_combine(ctypes.byref(s), *q, None, None) == ep.EP_ERR_ALIGN
-    assert lib.ep_combine(ctypes.byref(s), *[OK16] * 4, ctypes.c_void_p(0x1008), None, None) == ep.EP_ERR_ALIGN
+    for i in (4, 5):  # bias and combined_x are token rows: 16 bytes
+        q = [OK16] * 6
+        q[i] = ctypes.c_void_p(0x1008)
+        assert lib.ep_combine(ctypes.byref(s), *q, None, None) == ep.EP_ERR_ALIGN
 
 
 def test_layout_workspace_is_checked():

@@ -70,7 +70,7 @@ def check_layout_aligned(o, shape, topk_idx, name):
     return run, want
 
 
-def check_expand(o, shape, inp, name, y_rows=None):
+def check_expand(o, shape, inp, name, y_rows=None, bias=None):
     """Layout (aligned) + ep_dispatch_expand + ep_combine_expand against the
     oracle.  ``y_rows`` (one bf16 row per valid entry, (t, k) order) are the
     expert outputs for the combine; without them the combine is skipped."""
@@ -122,10 +122,10 @@ def check_expand(o, shape, inp, name, y_rows=None):
     status.zero_()
     say(f"ep_combine_expand {name}")
     ep.ep_combine_expand(shape, y, run.topk_idx, dev(inp["topk_weights"]), run.expert_slot,
-                         run.expert_offset, out, status)
+                         run.expert_offset, out, status, bias=None if bias is None else dev(bias))
     torch.cuda.synchronize()
     got = host(out)
-    want, st2 = o.combine_expand(y_host, idx, inp["topk_weights"], slot, off)
+    want, st2 = o.combine_expand(y_host, idx, inp["topk_weights"], slot, off, bias=bias)
     assert status_bits(status) == st2
     pins.assert_combine_close(got, pins.bf16_to_f64(want), f"{name} combine_expand")
     assert int((got != want).sum()) == 0, f"{name}: combine_expand not bit-identical"
@@ -223,7 +223,7 @@ def test_expand_slot_outside_queue_is_skipped_and_reported(o):
 
 # -------------------------------------------------------------- normal mode
 
-def check_normal(o, shape, inp, name, with_weights=True, rank_slot_override=None):
+def check_normal(o, shape, inp, name, with_weights=True, rank_slot_override=None, bias=None):
     """Layout + ep_dispatch_normal + ep_combine_normal against the oracle."""
     run = LayoutRun(shape, inp["topk_idx"])
     lay = run.numpy()
@@ -287,11 +287,13 @@ def check_normal(o, shape, inp, name, with_weights=True, rank_slot_override=None
     status.zero_()
     say(f"ep_combine_normal {name}")
     ep.ep_combine_normal(shape, dev(y_host), run.rank_slot, rtw if with_weights else None, out,
-                         cw if with_weights else None, status)
+                         cw if with_weights else None, status,
+                         bias=None if bias is None else dev(bias))
     torch.cuda.synchronize()
     got = host(out)
     want_out, want_cw, st = o.combine_normal(y_host, rank_slot,
-                                             want["recv_topk_weights"] if with_weights else None)
+                                             want["recv_topk_weights"] if with_weights else None,
+                                             bias=bias)
     assert status_bits(status) == st
     pins.assert_combine_close(got, pins.bf16_to_f64(want_out), f"{name} combine_normal")
     assert int((got != want_out).sum()) == 0, f"{name}: combine_normal not bit-identical"
