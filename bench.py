@@ -181,6 +181,7 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
     torch.cuda.synchronize()
     wall_cold = time.perf_counter() - t0
     cold = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
+    say(f"workload {w.name}: cold step times (us): " + " ".join(f"{v:.1f}" for v in cold))
 
     say(f"workload {w.name}: {steps} steps with an event between phases")
     evs = [new_events(4) for _ in range(steps)]
@@ -419,6 +420,55 @@ def time_receive_layouts(wid, steps, scrub_bytes, say, alignment=128, batch=10):
             c()
         say(f"{mode} step {w.name}: {steps} steps")
         out[f"step_us_cold_{mode}"] = round(_timed_cold(step, steps, evict, stream), 2)
+    torch.cuda.synchronize()
+    if int(buf["status"].item()) != 0:
+        raise RuntimeError(f"device status {int(buf['status'].item())}")
+    return out
+
+
+def time_combine_bias(wid, steps, scrub_bytes, say):
+    """ep_combine with and without the shared expert's bias row (one more bf16
+    row read per token), cold single launches after an eviction."""
+    import torch
+    from combine_ep_layout_02_amd import ep
+    from combine_ep_layout_02_amd import workloads as W
+
+    w = W.WORKLOADS[wid]
+    inp = W.make_inputs(w)
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    shape = ep.shape_of(w)
+    topk_idx = torch.from_numpy(inp["topk_idx"]).to(dev)
+    topk_weights = torch.from_numpy(inp["topk_weights"]).to(dev)
+    buf = ep.allocate(shape, dev, parts=("layout", "combine"))
+    ep.ep_layout(shape, topk_idx, buf["num_tokens_per_rank"], buf["num_tokens_per_expert"],
+                 buf["is_token_in_rank"], buf["expert_slot"], buf["rank_slot"],
+                 buf["expert_offset"], buf["workspace"], buf["status"])
+    g = torch.Generator(device=dev)
+    g.manual_seed(2200 + wid)
+    y = torch.randn((w.num_experts, w.expert_capacity, w.hidden), dtype=torch.bfloat16, device=dev,
+                    generator=g).view(torch.int16)
+    bias = torch.randn((w.num_tokens, w.hidden), dtype=torch.bfloat16, device=dev,
+                       generator=g).view(torch.int16)
+    scrub = torch.ones(scrub_bytes // 4, dtype=torch.float32, device=dev) if scrub_bytes else None
+    scrub_out = torch.zeros((), dtype=torch.float32, device=dev)
+
+    def evict():
+        if scrub is not None:
+            torch.sum(scrub, dim=0, out=scrub_out)
+
+    P = inp["num_valid"]
+    nb = algorithmic_bytes(w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks, P,
+                           w.use_fp8)["combine"]
+    out = {}
+    for label, b in (("plain", None), ("bias", bias)):
+        say(f"ep_combine {label} {w.name}: {steps} cold launches")
+        fn = lambda: ep.ep_combine(shape, y, topk_idx, topk_weights, buf["expert_slot"],
+                                   buf["combined_x"], buf["status"], bias=b)
+        us = _timed_cold(fn, steps, evict, stream)
+        nbytes = nb + (2 * w.num_tokens * w.hidden if b is not None else 0)
+        out[label] = {"us_cold_median": round(us, 2), "bytes": nbytes,
+                      "gbps_cold": round(nbytes / (us * 1e-6) / 1e9, 1)}
     torch.cuda.synchronize()
     if int(buf["status"].item()) != 0:
         raise RuntimeError(f"device status {int(buf['status'].item())}")
@@ -725,7 +775,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-scale-formats", action="store_true",
-                    help="skip the ep_dispatch timing per FP8 scale format")
+                    help="skip the per-variant timings (ep_dispatch per FP8 scale format, "
+                         "ep_combine with the shared expert's bias)")
     ap.add_argument("--no-receive-layouts", action="store_true",
                     help="skip the normal-mode and expand-layout timings")
     ap.add_argument("--receive-layouts-only", action="store_true",
@@ -798,6 +849,8 @@ def main():
     }
     if not args.no_scale_formats:
         extra["dispatch_by_scale_format_4096x7168"] = time_scale_formats(
+            3, min(args.steps, 20), scrub_bytes, say)
+        extra["combine_shared_expert_bias_4096x7168"] = time_combine_bias(
             3, min(args.steps, 20), scrub_bytes, say)
     if not args.no_receive_layouts:
         extra["receive_layouts_4096x7168"] = time_receive_layouts(
