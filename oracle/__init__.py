@@ -76,6 +76,8 @@ class Oracle:
         lib.oracle_dispatch_normal.restype = ctypes.c_int
         lib.oracle_combine_normal.argtypes = [i32] * 5 + [vp] * 6
         lib.oracle_combine_normal.restype = ctypes.c_int
+        lib.oracle_group_limited_topk.argtypes = [i32] * 5 + [vp] * 3
+        lib.oracle_group_limited_topk.restype = ctypes.c_int
         self.lib = lib
 
     # ------------------------------------------------------------- layout
@@ -255,6 +257,20 @@ class Oracle:
         st = self.lib.oracle_combine_normal(n, h, k, r, m, _ptr(y), _ptr(rs), _ptr(rw), _ptr(b),
                                             _ptr(out), _ptr(cw))
         return out, cw, int(st)
+
+    def group_limited_topk(self, scores: np.ndarray, num_groups: int, topk_groups: int,
+                           num_topk: int):
+        """Group-limited top-k gating (DeepEP V1 Legacy guide §1 and §2.1;
+        Lesson 14 §3 Q3 and exercise).  ``scores`` float32 [N, E].  Returns
+        (topk_idx int64 [N, K], topk_weights float32 [N, K], status)."""
+        sc = np.ascontiguousarray(scores, dtype=np.float32)
+        n, e = sc.shape
+        k = int(num_topk)
+        idx = np.empty((n, k), np.int64)
+        w = np.empty((n, k), np.float32)
+        st = self.lib.oracle_group_limited_topk(n, e, int(num_groups), int(topk_groups), k,
+                                                _ptr(sc), _ptr(idx), _ptr(w))
+        return idx, w, int(st)
 
     def quantize_rows_pow2(self, x_bits: np.ndarray):
         """Power-of-two-scale FP8 payload of each row: (q uint8 [N, H],

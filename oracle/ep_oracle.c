@@ -744,6 +744,82 @@ int oracle_combine_normal(int32_t N, int32_t H, int32_t K, int32_t R, int32_t M,
     return status;
 }
 
+/* ---------------------------------------------------------------- gating */
+
+/* Group-limited top-k gating, the step before the layout ([V1] §1 and §2.1:
+ * the normal kernels serve group-limited gating, benchmarked as top-4 groups
+ * then top-8 experts; [L14] §3 Q3: each token reaches at most 4 nodes;
+ * [L14] exercise: the gating weights are normalised softmax weights).
+ *
+ * Experts are split into G groups of L = E / G consecutive experts.  Per
+ * token t, with router scores s[t, 0..E-1]:
+ *   group score gs[g] = max of s over the group's experts (exact);
+ *   keep the TG groups with the largest gs (ties: the lower group index);
+ *   topk_idx[t, 0..K-1] = the K experts of the kept groups with the largest
+ *     s, in that order (ties: the lower expert index);
+ *   topk_weights[t, k] = exp(s_k - s_0) / sum_j exp(s_j - s_0) over the K
+ *     picks (softmax of the picked scores; evaluated in double, then rounded
+ *     to float).
+ * Needs 1 <= TG <= G, E % G == 0 and K <= TG * L.  Scores are finite. */
+int oracle_group_limited_topk(int32_t N, int32_t E, int32_t G, int32_t TG, int32_t K,
+                              const float *scores, int64_t *topk_idx, float *topk_weights)
+{
+    if (N < 0 || E < 1 || G < 1 || E % G != 0 || TG < 1 || TG > G || K < 1 || K > TG * (E / G))
+        return ORACLE_BAD_ARGS;
+    const int32_t L = E / G;
+    float *gs = (float *)malloc(sizeof(float) * (size_t)G);
+    uint8_t *kept = (uint8_t *)malloc((size_t)G);
+    uint8_t *taken = (uint8_t *)malloc((size_t)E);
+    double *z = (double *)malloc(sizeof(double) * (size_t)K);
+    if (!gs || !kept || !taken || !z) {
+        free(gs);
+        free(kept);
+        free(taken);
+        free(z);
+        return ORACLE_BAD_ARGS;
+    }
+    for (int32_t t = 0; t < N; ++t) {
+        const float *st = scores + (size_t)t * E;
+        for (int32_t g = 0; g < G; ++g) {
+            gs[g] = st[g * L];
+            for (int32_t i = 1; i < L; ++i)
+                if (st[g * L + i] > gs[g])
+                    gs[g] = st[g * L + i];
+            kept[g] = 0;
+        }
+        for (int32_t n = 0; n < TG; ++n) {
+            int32_t best = -1;
+            for (int32_t g = 0; g < G; ++g)
+                if (!kept[g] && (best < 0 || gs[g] > gs[best]))
+                    best = g;
+            kept[best] = 1;
+        }
+        for (int32_t e = 0; e < E; ++e)
+            taken[e] = 0;
+        for (int32_t k = 0; k < K; ++k) {
+            int32_t best = -1;
+            for (int32_t e = 0; e < E; ++e)
+                if (kept[e / L] && !taken[e] && (best < 0 || st[e] > st[best]))
+                    best = e;
+            taken[best] = 1;
+            topk_idx[(size_t)t * K + k] = best;
+        }
+        double sum = 0.0;
+        const double top = st[topk_idx[(size_t)t * K]];
+        for (int32_t k = 0; k < K; ++k) {
+            z[k] = exp((double)st[topk_idx[(size_t)t * K + k]] - top);
+            sum += z[k];
+        }
+        for (int32_t k = 0; k < K; ++k)
+            topk_weights[(size_t)t * K + k] = (float)(z[k] / sum);
+    }
+    free(gs);
+    free(kept);
+    free(taken);
+    free(z);
+    return ORACLE_OK;
+}
+
 /* ------------------------------------------------- array forms for pinning */
 
 void oracle_e4m3fn_encode_array(int64_t n, const float *v, uint8_t *out)

@@ -48,6 +48,9 @@ def main(path: str) -> int:
         ("combine_bias_order", lambda: pins.pin_combine_bias_order(o)),
         ("combine_bias_relations", lambda: pins.pin_combine_bias_relations(o, pack_cases)),
         ("backward_pair_adjoint", lambda: pins.pin_backward_pair_adjoint(o, ident_cases)),
+        ("gating_golden", lambda: pins.pin_gating_golden(o)),
+        ("gating_special_cases", lambda: pins.pin_gating_special_cases(o)),
+        ("gating_invariants", lambda: pins.pin_gating_invariants(o)),
         ("layout_bruteforce", lambda: pins.pin_layout_bruteforce(o)),
     ]
     for name, fn in steps:

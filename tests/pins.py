@@ -890,3 +890,81 @@ def pin_backward_pair_adjoint(o, cases):
         lw = float((np.where(written[:, :, None], d["recv_topk_weights"], 0.0) * gwi).sum())
         rw = float((wi.astype(np.float64) * cgw).sum())
         assert lw == rw, ("weights adjoint", lw, rw)
+
+
+# ------------------------------------------------------------------- gating
+
+def _plain_topk(scores: np.ndarray, k: int) -> np.ndarray:
+    """Top-k by library sort: descending score, ties to the lower index
+    (numpy's stable lexsort on (index, -score))."""
+    n, e = scores.shape
+    out = np.empty((n, k), np.int64)
+    for t in range(n):
+        order = np.lexsort((np.arange(e), -scores[t].astype(np.float64)))
+        out[t] = order[:k]
+    return out
+
+
+def _check_softmax(scores, idx, w):
+    """Weights sum to 1 and w_k / w_0 = exp(s_k - s_0) (float64 reference)."""
+    s = np.take_along_axis(scores.astype(np.float64), idx, axis=1)
+    ref = np.exp(s - s[:, :1])
+    ref /= ref.sum(axis=1, keepdims=True)
+    assert np.allclose(w, ref, rtol=0, atol=2e-7), "weights are not the softmax of the picks"
+    assert np.allclose(w.astype(np.float64).sum(axis=1), 1.0, atol=1e-6)
+
+
+def pin_gating_golden(o):
+    """Hand-worked picks (``tests/golden/group_limited_topk.json``)."""
+    with open(os.path.join(GOLDEN, "group_limited_topk.json")) as f:
+        g = json.load(f)
+    sc = np.array(g["scores"], np.float32)
+    idx, w, st = o.group_limited_topk(sc, g["num_groups"], g["topk_groups"], g["num_topk"])
+    assert st == 0
+    assert idx.tolist() == g["topk_idx"], idx.tolist()
+    _check_softmax(sc, idx, w)
+
+
+def pin_gating_special_cases(o):
+    """Keeping every group (TG = G), or one expert per group with TG = K,
+    is plain top-k: compared with a library sort, on continuous scores and on
+    scores from a 5-value set (many ties)."""
+    rng = np.random.default_rng(29)
+    for E, G, K in ((256, 8, 8), (64, 64, 6), (16, 4, 5), (1024, 32, 32)):
+        for sc in (rng.standard_normal((40, E)).astype(np.float32),
+                   rng.integers(0, 5, size=(40, E)).astype(np.float32)):
+            idx, w, st = o.group_limited_topk(sc, G, G, K)
+            assert st == 0 and np.array_equal(idx, _plain_topk(sc, K)), ("TG = G", E, G, K)
+            _check_softmax(sc, idx, w)
+        sc = rng.standard_normal((40, E)).astype(np.float32)
+        idx, _, st = o.group_limited_topk(sc, E, K, K)
+        assert st == 0 and np.array_equal(idx, _plain_topk(sc, K)), ("G = E", E, K)
+
+
+def pin_gating_invariants(o):
+    """Random and tied scores: the picks lie in exactly the TG groups with the
+    largest group maxima (library sort of the maxima, ties to the lower
+    group); among those groups' experts they are the K largest, best first
+    (library sort); weights are the softmax of the picks."""
+    rng = np.random.default_rng(31)
+    for E, G, TG, K in ((256, 8, 4, 8), (256, 8, 3, 8), (64, 16, 2, 5), (128, 4, 1, 12)):
+        L = E // G
+        for sc in (rng.standard_normal((60, E)).astype(np.float32),
+                   rng.integers(0, 4, size=(60, E)).astype(np.float32)):
+            idx, w, st = o.group_limited_topk(sc, G, TG, K)
+            assert st == 0
+            gmax = sc.reshape(-1, G, L).max(axis=2)
+            keep = _plain_topk(gmax, TG)
+            for t in range(sc.shape[0]):
+                cand = np.concatenate([np.arange(g * L, (g + 1) * L) for g in sorted(keep[t])])
+                masked = np.full(E, -np.inf, np.float64)
+                masked[cand] = sc[t, cand]
+                want = _plain_topk(masked[None, :], K)[0]
+                assert np.array_equal(idx[t], want), (E, G, TG, K, t)
+            _check_softmax(sc, idx, w)
+
+
+def pin_gating_bad_args(o):
+    sc = np.zeros((2, 16), np.float32)
+    for G, TG, K in ((5, 2, 2), (4, 0, 2), (4, 5, 2), (4, 1, 5), (4, 2, 0)):
+        assert o.group_limited_topk(sc, G, TG, K)[2] == 4, (G, TG, K)

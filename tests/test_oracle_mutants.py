@@ -96,6 +96,19 @@ MUTANTS = [
          COMBINE_YR + COMBINE_FMA + "\n        }")]),
     ("bias_overwrites", [("acc[c] = acc[c] + oracle_bf16_to_f32(bias_row[c]);",
                           "acc[c] = oracle_bf16_to_f32(bias_row[c]);")]),
+    # group-limited gating
+    ("gating_group_sum", [("                if (st[g * L + i] > gs[g])\n                    gs[g] = st[g * L + i];",
+                           "                gs[g] = gs[g] + st[g * L + i];")]),
+    ("gating_group_ties_high", [("if (!kept[g] && (best < 0 || gs[g] > gs[best]))",
+                                 "if (!kept[g] && (best < 0 || gs[g] >= gs[best]))")]),
+    ("gating_expert_ties_high", [("if (kept[e / L] && !taken[e] && (best < 0 || st[e] > st[best]))",
+                                  "if (kept[e / L] && !taken[e] && (best < 0 || st[e] >= st[best]))")]),
+    ("gating_ignores_groups", [("if (kept[e / L] && !taken[e] && (best < 0 || st[e] > st[best]))",
+                                "if (!taken[e] && (best < 0 || st[e] > st[best]))")]),
+    ("gating_group_of_expert", [("if (kept[e / L] && !taken[e]", "if (kept[e % G] && !taken[e]")]),
+    ("gating_one_group_short", [("for (int32_t n = 0; n < TG; ++n) {", "for (int32_t n = 1; n < TG; ++n) {")]),
+    ("gating_unnormalised", [("topk_weights[(size_t)t * K + k] = (float)(z[k] / sum);",
+                              "topk_weights[(size_t)t * K + k] = (float)z[k];")]),
     ("bias_row_of_token0", [(COMBINE_YR + COMBINE_FMA + "\n        }\n        add_bias_row(acc, bias ? bias + (size_t)t * H : NULL, H);",
                              COMBINE_YR + COMBINE_FMA + "\n        }\n        add_bias_row(acc, bias, H);")]),
 ]

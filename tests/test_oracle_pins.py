@@ -179,3 +179,16 @@ def test_combine_bias_relations(o):
 
 def test_backward_pair_adjoint(o):
     pins.pin_backward_pair_adjoint(o, _pack_cases(dead=True))
+
+
+def test_gating_golden(o):
+    pins.pin_gating_golden(o)
+
+
+def test_gating_special_cases(o):
+    pins.pin_gating_special_cases(o)
+
+
+def test_gating_invariants(o):
+    pins.pin_gating_invariants(o)
+    pins.pin_gating_bad_args(o)
