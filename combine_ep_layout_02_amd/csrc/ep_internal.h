@@ -64,6 +64,11 @@ hipError_t launch_dispatch_normal(const ep_shape &s, const uint16_t *x, const in
                                   float *recv_topk_weights, int32_t *recv_src_idx,
                                   uint32_t *status, hipStream_t stream);
 
+// ---- gating ----------------------------------------------------------------
+hipError_t launch_gate(const ep_shape &s, int32_t num_groups, int32_t topk_groups,
+                       const float *scores, int64_t *topk_idx, float *topk_weights,
+                       hipStream_t stream);
+
 // ---- combine ---------------------------------------------------------------
 hipError_t launch_combine(const ep_shape &s, const uint16_t *expert_out, const int64_t *topk_idx,
                           const float *topk_weights, const int32_t *expert_slot,

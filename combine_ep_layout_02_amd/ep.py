@@ -2,7 +2,8 @@
 
 Same entry points as the C ABI: ``ep_query_sizes``, ``ep_layout``,
 ``ep_dispatch``, ``ep_combine``, ``ep_dispatch_expand``, ``ep_combine_expand``,
-``ep_dispatch_normal``, ``ep_combine_normal``, ``ep_strerror`` (plus
+``ep_dispatch_normal``, ``ep_combine_normal``, ``ep_group_limited_topk``,
+``ep_strerror`` (plus
 ``ep_probe_e4m3fn`` from include/ep_probe.h).  Functions take torch tensors that already live on
 the GPU, check dtype / device / contiguity, and pass ``data_ptr()`` and the
 current HIP stream to the library.  Every step of the path runs in the HIP
@@ -45,8 +46,9 @@ SIZE_FIELDS = ("recv_x", "recv_scales", "recv_src_idx", "expert_out", "combined_
                "recv_src_idx_normal", "expert_out_normal", "combined_topk_weights",
                "recv_x_expand", "recv_scales_expand", "recv_src_idx_expand", "expert_out_expand")
 EXPORTED = ("ep_query_sizes", "ep_layout", "ep_dispatch", "ep_combine", "ep_dispatch_expand",
-            "ep_combine_expand", "ep_dispatch_normal", "ep_combine_normal", "ep_strerror",
-            "ep_probe_e4m3fn")
+            "ep_combine_expand", "ep_dispatch_normal", "ep_combine_normal",
+            "ep_group_limited_topk", "ep_strerror", "ep_probe_e4m3fn")
+EP_MAX_GROUPS = 64
 EP_MAX_ALIGNMENT = 1024
 
 
@@ -85,6 +87,7 @@ def lib() -> ctypes.CDLL:
         L.ep_combine_expand.argtypes = [sp] + [vp] * 9
         L.ep_dispatch_normal.argtypes = [sp] + [vp] * 11
         L.ep_combine_normal.argtypes = [sp] + [vp] * 8
+        L.ep_group_limited_topk.argtypes = [sp, ctypes.c_int32, ctypes.c_int32] + [vp] * 4
         L.ep_probe_e4m3fn.argtypes = [vp, vp, vp, i64, vp]
         L.ep_strerror.argtypes = [ctypes.c_int]
         L.ep_strerror.restype = ctypes.c_char_p
@@ -308,6 +311,19 @@ def ep_combine(shape: ep_shape, expert_out: torch.Tensor, topk_idx: torch.Tensor
         _stream(stream, combined_x))
     if rc != EP_OK:
         raise EpError(rc, "ep_combine")
+
+
+def ep_group_limited_topk(shape: ep_shape, num_groups: int, topk_groups: int,
+                          scores: torch.Tensor, topk_idx: torch.Tensor,
+                          topk_weights: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Group-limited top-k gating; see ``ep_group_limited_topk`` in include/ep.h."""
+    N, E, K = shape.num_tokens, shape.num_experts, shape.num_topk
+    rc = lib().ep_group_limited_topk(
+        ctypes.byref(shape), ctypes.c_int32(int(num_groups)), ctypes.c_int32(int(topk_groups)),
+        _ptr(scores, "scores", _F32, N * E), _ptr(topk_idx, "topk_idx", _I64, N * K),
+        _ptr(topk_weights, "topk_weights", _F32, N * K), _stream(stream, topk_idx))
+    if rc != EP_OK:
+        raise EpError(rc, "ep_group_limited_topk")
 
 
 def ep_probe_e4m3fn(values: torch.Tensor, out_hw: Optional[torch.Tensor],

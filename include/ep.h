@@ -82,6 +82,7 @@ extern "C" {
 #define EP_MAX_RANKS 64     /* R: a token's rank set is one 64-bit mask          */
 #define EP_MAX_TOPK 32      /* K */
 #define EP_MAX_ALIGNMENT 1024 /* expert_alignment */
+#define EP_MAX_GROUPS 64      /* num_groups of ep_group_limited_topk */
 
 /* The problem's shape ([V1] §5.1 and §6.1; [L14] §3).  Passed by host pointer. */
 typedef struct {
@@ -310,6 +311,29 @@ int ep_dispatch_normal(const ep_shape *shape, const uint16_t *x, const int64_t *
 int ep_combine_normal(const ep_shape *shape, const uint16_t *x, const int32_t *rank_slot,
                       const float *recv_topk_weights, const uint16_t *bias, uint16_t *combined_x,
                       float *combined_topk_weights, uint32_t *status, void *stream);
+
+/* Group-limited top-k gating, the step that produces topk_idx for
+ * ep_layout ([V1] §1 and §2.1: the normal kernels serve group-limited
+ * gating, benchmarked with top-4 groups then top-8 experts; [L14] §3 Q3: a
+ * token reaches at most 4 nodes; [L14] exercise: normalised softmax gating
+ * weights).
+ *
+ * In:  shape (num_tokens N, num_experts E, num_topk K are used; the rest is
+ *      validated as for the other entry points); scores [N, E] fp32 router
+ *      scores, finite; num_groups G in [1, EP_MAX_GROUPS] with E % G == 0:
+ *      group g holds experts [g*E/G, (g+1)*E/G); topk_groups TG in [1, G];
+ *      K <= TG * E/G.
+ * Out: topk_idx [N, K] int64: per token, a group's score is its best
+ *        expert's score; the TG best groups are kept (ties: lower group
+ *        index); the K best experts of the kept groups, best first (ties:
+ *        lower expert index);
+ *      topk_weights [N, K] fp32 (nullable): exp(s_k - s_0) / sum_j exp(s_j -
+ *        s_0) over the K picks (fp32 expf and division; the picks are exact).
+ * Errors: EP_ERR_SHAPE for G, TG or K outside the rules above,
+ * EP_ERR_UNSUPPORTED for G > EP_MAX_GROUPS. */
+int ep_group_limited_topk(const ep_shape *shape, int32_t num_groups, int32_t topk_groups,
+                          const float *scores, int64_t *topk_idx, float *topk_weights,
+                          void *stream);
 
 /* Host only.  A static string naming a return code. */
 const char *ep_strerror(int code);

@@ -285,3 +285,20 @@ def test_binding_refuses_cpu_tensors():
         ep.ep_combine(s, torch.zeros(4, dtype=torch.int16), torch.zeros(4, dtype=torch.int64),
                       torch.zeros(4), torch.zeros(4, dtype=torch.int32),
                       torch.zeros(4, dtype=torch.int16), stream=0)
+
+
+def test_gating_argument_checks():
+    """ep_group_limited_topk: group rules are checked before any launch."""
+    s = _shape(num_experts=16, num_ranks=4, num_topk=4)
+    lib = ep.lib()
+    call = lambda sh, G, TG, *p: lib.ep_group_limited_topk(ctypes.byref(sh), G, TG, *p, None)
+    for G, TG, code in ((5, 2, ep.EP_ERR_SHAPE), (0, 1, ep.EP_ERR_SHAPE), (4, 0, ep.EP_ERR_SHAPE),
+                        (4, 5, ep.EP_ERR_SHAPE), (8, 1, ep.EP_ERR_SHAPE),  # K=4 > 1 * 16/8
+                        (128, 1, ep.EP_ERR_UNSUPPORTED)):
+        assert call(s, G, TG, OK16, OK16, OK16) == code, (G, TG)
+    assert call(s, 4, 2, None, OK16, OK16) == ep.EP_ERR_NULL
+    assert call(s, 4, 2, OK16, None, OK16) == ep.EP_ERR_NULL
+    assert call(s, 4, 2, BAD, OK16, OK16) == ep.EP_ERR_ALIGN
+    assert call(s, 4, 2, OK16, ctypes.c_void_p(0x1004), OK16) == ep.EP_ERR_ALIGN
+    assert call(s, 4, 2, OK16, OK16, BAD) == ep.EP_ERR_ALIGN
+    assert call(_shape(num_tokens=-1), 4, 2, OK16, OK16, OK16) == ep.EP_ERR_SHAPE
