@@ -426,6 +426,62 @@ def time_receive_layouts(wid, steps, scrub_bytes, say, alignment=128, batch=10):
     return out
 
 
+def time_gating(wid, steps, scrub_bytes, say, num_groups=8, topk_groups=4):
+    """Group-limited gating on workload ``wid``'s shape (router scores N(0, 1)
+    [N, E] fp32): ep_group_limited_topk alone, cold, and the whole step with
+    the gating in front (gating + layout + dispatch + combine), cold.  The
+    gating's algorithmic bytes: read the scores (4 B per (token, expert)),
+    write topk_idx (8 B) and topk_weights (4 B) per entry."""
+    import torch
+    from combine_ep_layout_02_amd import ep
+    from combine_ep_layout_02_amd import workloads as W
+
+    w = W.WORKLOADS[wid]
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    shape = ep.shape_of(w)
+    N, E, K, H = w.num_tokens, w.num_experts, w.num_topk, w.hidden
+    g = torch.Generator(device=dev)
+    g.manual_seed(2300 + wid)
+    scores = torch.randn((N, E), dtype=torch.float32, device=dev, generator=g)
+    topk_idx = torch.empty((N, K), dtype=torch.int64, device=dev)
+    topk_weights = torch.empty((N, K), dtype=torch.float32, device=dev)
+    x = torch.randn((N, H), dtype=torch.bfloat16, device=dev, generator=g).view(torch.int16)
+    y = torch.randn((E, w.expert_capacity, H), dtype=torch.bfloat16, device=dev,
+                    generator=g).view(torch.int16)
+    buf = ep.allocate(shape, dev, parts=("layout", "dispatch", "combine"))
+    scrub = torch.ones(scrub_bytes // 4, dtype=torch.float32, device=dev) if scrub_bytes else None
+    scrub_out = torch.zeros((), dtype=torch.float32, device=dev)
+
+    def evict():
+        if scrub is not None:
+            torch.sum(scrub, dim=0, out=scrub_out)
+
+    def gate():
+        ep.ep_group_limited_topk(shape, num_groups, topk_groups, scores, topk_idx, topk_weights)
+
+    def step():
+        gate()
+        ep.ep_layout(shape, topk_idx, buf["num_tokens_per_rank"], buf["num_tokens_per_expert"],
+                     buf["is_token_in_rank"], buf["expert_slot"], buf["rank_slot"],
+                     buf["expert_offset"], buf["workspace"], buf["status"])
+        ep.ep_dispatch(shape, x, topk_idx, buf["expert_slot"], buf["recv_x"], buf["recv_scales"],
+                       buf["recv_src_idx"], buf["status"])
+        ep.ep_combine(shape, y, topk_idx, topk_weights, buf["expert_slot"], buf["combined_x"],
+                      buf["status"])
+
+    step()
+    torch.cuda.synchronize()
+    if int(buf["status"].item()) != 0:
+        raise RuntimeError(f"device status {int(buf['status'].item())}")
+    nb = 4 * N * E + 12 * N * K
+    say(f"ep_group_limited_topk {w.name}: {steps} cold launches, {steps} gated steps")
+    us = _timed_cold(gate, steps, evict, stream)
+    return {"num_groups": num_groups, "topk_groups": topk_groups, "bytes": nb,
+            "us_cold_median": round(us, 2), "gbps_cold": round(nb / (us * 1e-6) / 1e9, 1),
+            "step_us_cold_with_gating": round(_timed_cold(step, steps, evict, stream), 2)}
+
+
 def time_combine_bias(wid, steps, scrub_bytes, say):
     """ep_combine with and without the shared expert's bias row (one more bf16
     row read per token), cold single launches after an eviction."""
@@ -762,6 +818,30 @@ def summarize_layout_profiles(out_dir):
         with open(path, "w") as f:
             f.write("\n".join(lines) + "\n")
         written.append(path)
+    gt = figures.get("gating_4096x256")
+    durs = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
+                  if r["Kernel_Name"] == "gate_kernel")
+    if gt and durs:
+        med = statistics.median(durs)
+        lines = [
+            f"# gate_kernel (ep_group_limited_topk), {gt['num_groups']} groups, top "
+            f"{gt['topk_groups']} groups, prefill shape (4096 tokens, 256 experts, top-8)",
+            f"kernel_source_digest: {figures['kernel_source_digest']}",
+            "",
+            "## rocprofv3 kernel trace (every dispatch in the run: cold launches and gated steps)",
+            f"command: {PROFILE_COMMANDS['layouts_trace']}",
+            f"dispatches: {len(durs)}",
+            f"median_us: {med:.2f}",
+            f"min_us: {durs[0]:.2f}  max_us: {durs[-1]:.2f}",
+            f"algorithmic_bytes_per_launch: {gt['bytes']}",
+            f"achieved_GBps_at_trace_median: {gt['bytes'] / med / 1e3:.1f}",
+            f"bench_same_run: cold {gt['us_cold_median']} us (events around one launch); gated step "
+            f"{gt['step_us_cold_with_gating']} us",
+        ]
+        path = os.path.join(PROFILES, "gate_prefill_4096x7168_trace.txt")
+        with open(path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        written.append(path)
     return written
 
 
@@ -811,8 +891,9 @@ def main():
     scrub_bytes = args.scrub_mib << 20
     if args.receive_layouts_only:
         print(json.dumps({"receive_layouts_4096x7168": time_receive_layouts(
-            3, args.steps, scrub_bytes, say), "kernel_source_digest": kernel_source_digest()}),
-            flush=True)
+            3, args.steps, scrub_bytes, say),
+            "gating_4096x256": time_gating(3, args.steps, scrub_bytes, say),
+            "kernel_source_digest": kernel_source_digest()}), flush=True)
         return
     prefill = run_workload(3, args.steps, args.warmup, scrub_bytes, say)
     decode = None if args.no_decode else run_workload(2, args.steps, args.warmup, scrub_bytes, say)
@@ -855,6 +936,7 @@ def main():
     if not args.no_receive_layouts:
         extra["receive_layouts_4096x7168"] = time_receive_layouts(
             3, min(args.steps, 20), scrub_bytes, say)
+        extra["gating_4096x256"] = time_gating(3, min(args.steps, 20), scrub_bytes, say)
     if decode is not None:
         extra["decode_128x7168"] = {
             "step_us_cold": decode["cold"], "step_us_cold_hip_graph": decode["graph_cold"],

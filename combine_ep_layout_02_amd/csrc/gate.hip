@@ -9,14 +9,22 @@
 // softmax of the picked scores.
 //
 // Work item = one wave per token.  Lane l holds experts i * 64 + l (so each
-// load instruction reads 64 consecutive scores).  Scores become
-// order-preserving 32-bit keys (after adding +0, so -0 and +0 compare equal,
-// as floats do); the group maxima are LDS atomicMax on those keys.  Every pick
-// -- a group, then an expert -- is a wave-wide maximum of the 64-bit key
-// (score key << 32 | ~index), so the larger score wins and equal scores go to
-// the lower index, without a branch per compare.  All decisions are exact
-// comparisons of the inputs, so they match the CPU definition bit for bit;
-// only the weights involve rounding (expf and one division per pick).
+// load instruction reads 64 consecutive scores, and the index order of the
+// experts is the order of (i, lane)).  Scores become order-preserving 32-bit
+// keys (after adding +0, so -0 and +0 compare equal, as floats do).  The group
+// maxima are LDS atomicMax on the keys.  Selection moves no data between
+// lanes, only ballots counted on the scalar unit:
+//   groups:  group g's rank is the number of groups whose (key, lower index)
+//            beats it (G readlanes); the TG lowest ranks are kept;
+//   experts: a 32-step radix select finds T, the K-th largest candidate key
+//            counted with multiplicity (keep a bit when at least K candidates
+//            are >= the trial value).  The candidates above T are picked, and
+//            the remaining picks are the lowest-index candidates equal to T.
+//            A pick's position is the number of candidates above its key
+//            plus the number of equal keys at lower indices.
+// All decisions are exact comparisons of the inputs, so they match the CPU
+// definition bit for bit; only the weights involve rounding (expf and one
+// division per pick).
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -39,16 +47,15 @@ __device__ __forceinline__ float key_value(uint32_t k)
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+// Number of candidate keys of the wave that are >= t.
+template <int V>
+__device__ __forceinline__ int count_at_least(const uint32_t (&c)[V], uint32_t t)
 {
+    int n = 0;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
-        const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
+    for (int i = 0; i < V; ++i)
+        n += __popcll(__ballot(c[i] >= t));
+    return n;
 }
 
 template <int V>
@@ -62,59 +69,84 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(int32_t N, int32_t E, in
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t t = (int64_t)blockIdx.x * kWaves + wave;
-    const bool live = t < N; // waves past the last token still take part in the barriers
+    const bool live = t < N; // waves past the last token take part in the barriers only
     const int32_t L = E / G;
 
     uint32_t key[V];
+    int32_t grp[V];
     bool valid[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         const int32_t e = i * 64 + lane;
         valid[i] = live && e < E;
         key[i] = valid[i] ? order_key(scores[t * E + e]) : 0u;
+        grp[i] = e / L;
     }
     s_gkey[wave][lane] = 0u;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < V; ++i)
         if (valid[i])
-            atomicMax(&s_gkey[wave][(i * 64 + lane) / L], key[i]);
+            atomicMax(&s_gkey[wave][grp[i]], key[i]);
     __syncthreads();
+    if (!live)
+        return;
+
+    // groups: rank of group `lane` among the G group keys (ties: lower index)
     const uint32_t gk = lane < G ? s_gkey[wave][lane] : 0u;
-
-    // the TG best groups
-    uint64_t kept = 0;
-    for (int n = 0; n < TG; ++n) {
-        const bool cand = lane < G && !((kept >> lane) & 1u);
-        const uint64_t c = cand ? ((uint64_t)gk << 32) | (uint32_t)~(uint32_t)lane : 0u;
-        const uint64_t best = wave_max_u64(c);
-        kept |= 1ull << (~(uint32_t)best & 63u);
+    int grank = 0;
+    for (int g = 0; g < G; ++g) {
+        const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)gk, g);
+        grank += (o > gk || (o == gk && g < lane)) ? 1 : 0;
     }
+    const uint64_t kept = __ballot(lane < G && grank < TG);
 
-    // the K best experts of the kept groups; lane k keeps pick k
-    bool taken[V];
+    // experts: candidate keys, 0 where not a candidate
+    uint32_t c[V];
 #pragma unroll
     for (int i = 0; i < V; ++i)
-        taken[i] = !valid[i] || !((kept >> ((i * 64 + lane) / L)) & 1u);
+        c[i] = (valid[i] && ((kept >> grp[i]) & 1u)) ? key[i] : 0u;
+    // T = the K-th largest candidate key (the host ensures K candidates exist)
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t trial = T | (1u << bit);
+        if (count_at_least<V>(c, trial) >= K)
+            T = trial;
+    }
+    // picks: every candidate above T, then the lowest-index ones equal to T
+    int need = K - count_at_least<V>(c, T + 1); // >= 1
+    uint64_t pick[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        pick[i] = __ballot(c[i] > T);
+        uint64_t eq = __ballot(c[i] == T);
+        while (eq && need > 0) {
+            pick[i] |= eq & (~eq + 1); // lowest remaining lane
+            eq &= eq - 1;
+            --need;
+        }
+    }
+    // each pick at its position; lane k keeps pick k
     int64_t my_idx = -1;
     float my_score = 0.0f;
-    for (int k = 0; k < K; ++k) {
-        uint64_t c = 0;
 #pragma unroll
-        for (int i = 0; i < V; ++i) {
-            const uint64_t ci = ((uint64_t)key[i] << 32) | (uint32_t)~(uint32_t)(i * 64 + lane);
-            if (!taken[i] && ci > c)
-                c = ci;
-        }
-        const uint64_t best = wave_max_u64(c);
-        const uint32_t e = ~(uint32_t)best; // the host ensures K candidates exist
+    for (int i = 0; i < V; ++i) {
+        uint64_t p = pick[i];
+        while (p) {
+            const int l = __builtin_ctzll(p);
+            p &= p - 1;
+            const uint32_t ck = (uint32_t)__builtin_amdgcn_readlane((int)c[i], l);
+            int pos = 0;
 #pragma unroll
-        for (int i = 0; i < V; ++i)
-            if ((uint32_t)(i * 64 + lane) == e)
-                taken[i] = true;
-        if (lane == k) {
-            my_idx = (int64_t)e;
-            my_score = key_value((uint32_t)(best >> 32));
+            for (int i2 = 0; i2 < V; ++i2) {
+                pos += __popcll(__ballot(c[i2] > ck));
+                const uint64_t eq = __ballot(c[i2] == ck);
+                pos += i2 < i ? __popcll(eq) : i2 == i ? __popcll(eq & ((1ull << l) - 1)) : 0;
+            }
+            if (lane == pos) {
+                my_idx = (int64_t)(i * 64 + l);
+                my_score = key_value(ck);
+            }
         }
     }
 
@@ -124,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(int32_t N, int32_t E, in
     float sum = 0.0f;
     for (int k = 0; k < K; ++k)
         sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), k));
-    if (live && lane < K) {
+    if (lane < K) {
         topk_idx[t * K + lane] = my_idx;
         if (topk_weights)
             topk_weights[t * K + lane] = z / sum;
