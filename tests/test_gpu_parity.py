@@ -456,3 +456,40 @@ def test_hip_graph_capture_and_replay(o):
         assert np.array_equal(replay["slot"], lay["expert_slot"])
         assert np.array_equal(replay["cnt"], lay["num_tokens_per_expert"])
     assert int(buf["status"].item()) == 0
+
+
+def _layout_into(shape, topk_idx_dev, ws, status):
+    N, K, E, R = shape.num_tokens, shape.num_topk, shape.num_experts, shape.num_ranks
+    out = {
+        "num_tokens_per_rank": torch.full((R,), -5, dtype=torch.int32, device="cuda"),
+        "num_tokens_per_expert": torch.full((E,), -5, dtype=torch.int32, device="cuda"),
+        "is_token_in_rank": torch.full((N, R), 0xEE, dtype=torch.uint8, device="cuda"),
+        "expert_slot": torch.full((N, K), -5, dtype=torch.int32, device="cuda"),
+        "rank_slot": torch.full((N, R), -5, dtype=torch.int32, device="cuda"),
+        "expert_offset": torch.full((E + 1,), -5, dtype=torch.int32, device="cuda"),
+    }
+    ep.ep_layout(shape, topk_idx_dev, out["num_tokens_per_rank"], out["num_tokens_per_expert"],
+                 out["is_token_in_rank"], out["expert_slot"], out["rank_slot"],
+                 out["expert_offset"], ws, status)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def test_layout_workspace_reused_across_sizes(o):
+    """One workspace, never cleared, serves layout calls of different sizes
+    one after another (its contents on entry are irrelevant)."""
+    big = W.WORKLOADS[4]  # 16,384 tokens: 64 blocks
+    ws_bytes = ep.ep_query_sizes(ep.shape_of(big))["layout_workspace"]
+    ws = torch.full((ws_bytes // 4,), 0x7B7B7B7B, dtype=torch.int32, device="cuda")
+    for wid, n in ((4, 16384), (3, 4096), (5, 1000), (3, 257), (4, 16384)):
+        w = W.WORKLOADS[wid].scaled(n, 128)
+        shape = ep.shape_of(w)
+        inp = W.make_inputs(w)
+        assert ep.ep_query_sizes(shape)["layout_workspace"] <= ws_bytes
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        say(f"ep_layout N={n} into a shared workspace")
+        got = _layout_into(shape, dev(inp["topk_idx"]), ws, status)
+        want = o.layout(inp["topk_idx"], w.num_experts, w.num_ranks)
+        for key in LAYOUT_KEYS:
+            assert np.array_equal(got[key], want[key]), (n, key)
+        assert int(status.item()) == 0
