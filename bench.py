@@ -426,6 +426,69 @@ def time_receive_layouts(wid, steps, scrub_bytes, say, alignment=128, batch=10):
     return out
 
 
+def time_config(wid, steps, warmup, scrub_bytes, say):
+    """The whole step (layout + dispatch + combine) on another workload, cold
+    (eviction before each step, two events around it): median and mean us,
+    and algorithmic GB/s at the mean, against the 60 % of peak bar."""
+    import torch
+    from combine_ep_layout_02_amd import ep
+    from combine_ep_layout_02_amd import workloads as W
+
+    w = W.WORKLOADS[wid]
+    shape = ep.shape_of(w)
+    say(f"workload {w.name}: generating inputs")
+    inp = W.make_inputs(w)
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    topk_idx = torch.from_numpy(inp["topk_idx"]).to(dev)
+    topk_weights = torch.from_numpy(inp["topk_weights"]).to(dev)
+    x = torch.from_numpy(inp["x_bits"].view(np.int16)).to(dev)
+    buf = ep.allocate(shape, dev, parts=("layout", "dispatch", "combine"))
+    g = torch.Generator(device=dev)
+    g.manual_seed(2400 + wid)
+    y = torch.randn((w.num_experts, w.expert_capacity, w.hidden), dtype=torch.bfloat16,
+                    device=dev, generator=g).view(torch.int16)
+    scrub = torch.ones(scrub_bytes // 4, dtype=torch.float32, device=dev) if scrub_bytes else None
+    scrub_out = torch.zeros((), dtype=torch.float32, device=dev)
+
+    def evict():
+        if scrub is not None:
+            torch.sum(scrub, dim=0, out=scrub_out)
+
+    def step():
+        ep.ep_layout(shape, topk_idx, buf["num_tokens_per_rank"], buf["num_tokens_per_expert"],
+                     buf["is_token_in_rank"], buf["expert_slot"], buf["rank_slot"],
+                     buf["expert_offset"], buf["workspace"], buf["status"])
+        ep.ep_dispatch(shape, x, topk_idx, buf["expert_slot"], buf["recv_x"], buf["recv_scales"],
+                       buf["recv_src_idx"], buf["status"])
+        ep.ep_combine(shape, y, topk_idx, topk_weights, buf["expert_slot"], buf["combined_x"],
+                      buf["status"])
+
+    for _ in range(warmup):
+        step()
+        evict()
+    torch.cuda.synchronize()
+    say(f"workload {w.name}: {steps} cold steps")
+    times = []
+    for _ in range(steps):
+        evict()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    if int(buf["status"].item()) != 0:
+        raise RuntimeError(f"device status {int(buf['status'].item())}")
+    nb = algorithmic_bytes(w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks,
+                           inp["num_valid"], w.use_fp8)["total"]
+    mean = statistics.fmean(times)
+    return {"us_median": round(statistics.median(times), 2), "us_mean": round(mean, 2),
+            "bytes": nb, "gbps_at_mean": round(nb / (mean * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(nb / (mean * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+            "bar_60pct_us": round(nb / (0.6 * PEAK_HBM_GBPS * 1e9) * 1e6, 1)}
+
+
 def time_gating(wid, steps, scrub_bytes, say, num_groups=8, topk_groups=4):
     """Group-limited gating on workload ``wid``'s shape (router scores N(0, 1)
     [N, E] fp32): ep_group_limited_topk alone, cold, and the whole step with
@@ -621,15 +684,16 @@ PROFILE_COMMANDS = {
                      "--receive-layouts-only --steps 20 --quiet",
     "trace": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -T -f csv "
              "-d $REPO/gpurun_out/prof_trace -o trace -- python3 $REPO/bench.py --steps 30 "
-             "--warmup 5 --no-cpu-baseline --no-scale-formats --no-receive-layouts --quiet",
+             "--warmup 5 --no-cpu-baseline --no-scale-formats --no-receive-layouts "
+             "--no-other-configs --quiet",
     "FETCH_SIZE": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -T -f csv "
                   "-d $REPO/gpurun_out/prof_FETCH_SIZE -o pmc -- python3 $REPO/bench.py --steps 3 "
                   "--warmup 1 --no-cpu-baseline --no-decode --no-scale-formats --no-receive-layouts "
-                  "--quiet",
+                  "--no-other-configs --quiet",
     "WRITE_SIZE": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -T -f csv "
                   "-d $REPO/gpurun_out/prof_WRITE_SIZE -o pmc -- python3 $REPO/bench.py --steps 3 "
                   "--warmup 1 --no-cpu-baseline --no-decode --no-scale-formats --no-receive-layouts "
-                  "--quiet",
+                  "--no-other-configs --quiet",
 }
 
 
@@ -857,6 +921,8 @@ def main():
     ap.add_argument("--no-scale-formats", action="store_true",
                     help="skip the per-variant timings (ep_dispatch per FP8 scale format, "
                          "ep_combine with the shared expert's bias)")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the cold steps of the large and skewed workloads")
     ap.add_argument("--no-receive-layouts", action="store_true",
                     help="skip the normal-mode and expand-layout timings")
     ap.add_argument("--receive-layouts-only", action="store_true",
@@ -933,6 +999,11 @@ def main():
             3, min(args.steps, 20), scrub_bytes, say)
         extra["combine_shared_expert_bias_4096x7168"] = time_combine_bias(
             3, min(args.steps, 20), scrub_bytes, say)
+    if not args.no_other_configs:
+        torch.cuda.empty_cache()
+        for wid, key in ((4, "large_16384x7168_bf16"), (5, "skewed_4096x4096")):
+            extra[key] = time_config(wid, min(args.steps, 20), min(args.warmup, 3), scrub_bytes, say)
+            torch.cuda.empty_cache()
     if not args.no_receive_layouts:
         extra["receive_layouts_4096x7168"] = time_receive_layouts(
             3, min(args.steps, 20), scrub_bytes, say)

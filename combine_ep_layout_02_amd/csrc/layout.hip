@@ -34,6 +34,9 @@ namespace {
 constexpr int kThreads = 256; // = tokens per block, one per lane
 constexpr int kGroups = kThreads / 64;
 constexpr int kHistBatch = 8; // int4 histogram loads in flight per thread
+// Up to this many ranks, per-rank work is one ballot per rank; above it, each
+// token visits only its own ranks (at most K of them) with LDS atomics.
+constexpr int kBallotRanks = 16;
 
 __device__ __forceinline__ uint64_t bits_below(int bit) { return (1ull << bit) - 1ull; }
 
@@ -78,11 +81,17 @@ __global__ __launch_bounds__(kThreads) void layout_count_kernel(
             ranks |= 1ull << (e[k] / L);
         }
     }
-    // tokens per rank: one ballot per rank gives the wave's count directly
-    for (int r = 0; r < R; ++r) {
-        const uint64_t m = __ballot((ranks >> r) & 1ull);
-        if ((tid & 63) == 0 && m)
-            atomicAdd(&s_cnt[E + r], __popcll(m));
+    // tokens per rank: one ballot per rank gives the wave's count directly;
+    // with many ranks each token adds itself to its own ranks instead
+    if (R <= kBallotRanks) {
+        for (int r = 0; r < R; ++r) {
+            const uint64_t m = __ballot((ranks >> r) & 1ull);
+            if ((tid & 63) == 0 && m)
+                atomicAdd(&s_cnt[E + r], __popcll(m));
+        }
+    } else {
+        for (uint64_t m = ranks; m; m &= m - 1)
+            atomicAdd(&s_cnt[E + __builtin_ctzll(m)], 1);
     }
     __syncthreads();
     int32_t *row = hist + (size_t)blockIdx.x * stride;
@@ -93,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void layout_count_kernel(
 __host__ __device__ inline size_t assign_lds_bytes(int E, int R)
 {
     return sizeof(uint64_t) * (size_t)kGroups * (E + R) + sizeof(int32_t) * (size_t)(E + R) * 2 +
-           sizeof(int32_t) * 8;
+           sizeof(int32_t) * 8 + sizeof(int32_t) * (size_t)kGroups * R;
 }
 
 // Number of entries of `e` among the block's tokens before this lane's token
@@ -213,6 +222,7 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
     int32_t *s_base = reinterpret_cast<int32_t *>(s_rbm + (size_t)kGroups * R); // [E+R]
     int32_t *s_tot = s_base + (E + R);                           // [E+R]
     int32_t *s_misc = s_tot + (E + R);                           // [8]
+    int32_t *s_rbase = s_misc + 8; // [kGroups][R], many-rank path: rank slot base per wave
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -303,11 +313,18 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
     for (int k = 0; k < KMAX; ++k)
         if (e[k] >= 0 && occ[k] == 0)
             atomicOr((unsigned long long *)&s_bm[g * E + e[k]], (unsigned long long)bit);
-    // rank words: one ballot per rank gives this wave's word directly
-    for (int r = 0; r < R; ++r) {
-        const uint64_t m = __ballot((ranks >> r) & 1ull);
-        if (lane == 0)
-            s_rbm[g * R + r] = m;
+    // rank words: one ballot per rank gives this wave's word directly; with
+    // many ranks each token sets its bit in its own ranks' words
+    if (R <= kBallotRanks) {
+        for (int r = 0; r < R; ++r) {
+            const uint64_t m = __ballot((ranks >> r) & 1ull);
+            if (lane == 0)
+                s_rbm[g * R + r] = m;
+        }
+    } else {
+        for (uint64_t m = ranks; m; m &= m - 1)
+            atomicOr((unsigned long long *)&s_rbm[g * R + __builtin_ctzll(m)],
+                     (unsigned long long)bit);
     }
     if (maxocc > 0)
         atomicMax(&s_misc[0], maxocc);
@@ -333,6 +350,19 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
             for (int g2 = 0; g2 < kGroups; ++g2)
                 c += __popcll(s_rbm[g2 * R + i]);
             s_tot[E + i] = c;
+        }
+    }
+
+    // many ranks: each wave's rank-slot base (earlier blocks' tokens of the
+    // rank plus this block's earlier waves'), so a token's rank slot is one
+    // popcount away
+    if (R > kBallotRanks) {
+        for (int i = tid; i < kGroups * R; i += kThreads) {
+            const int g2 = i / R, r = i - g2 * R;
+            int c = s_base[E + r];
+            for (int g3 = 0; g3 < g2; ++g3)
+                c += __popcll(s_rbm[g3 * R + r]);
+            s_rbase[i] = c;
         }
     }
 
@@ -363,6 +393,8 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
     }
 
     // 6. this token's outputs (16-byte stores where the row allows them)
+    if (R > kBallotRanks)
+        __syncthreads(); // s_rbase complete
     if (live) {
         int32_t slot[KMAX];
 #pragma unroll
@@ -385,7 +417,27 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
         int32_t *rslot_out = rank_slot + t * R;
         const bool vec = (R & 3) == 0 && (reinterpret_cast<uintptr_t>(rslot_out) & 15) == 0 &&
                          (reinterpret_cast<uintptr_t>(mask_out) & 3) == 0;
-        for (int r0 = 0; r0 < R; r0 += 4) {
+        if (R > kBallotRanks) {
+            // the row as "not sent" first, then the token's own ranks (the
+            // same thread's stores to one address land in program order)
+            if (vec) {
+                for (int r0 = 0; r0 < R; r0 += 4) {
+                    *reinterpret_cast<int4 *>(rslot_out + r0) = make_int4(-1, -1, -1, -1);
+                    *reinterpret_cast<uint32_t *>(mask_out + r0) = 0u;
+                }
+            } else {
+                for (int r = 0; r < R; ++r) {
+                    rslot_out[r] = -1;
+                    mask_out[r] = 0;
+                }
+            }
+            for (uint64_t m = ranks; m; m &= m - 1) {
+                const int r = __builtin_ctzll(m);
+                rslot_out[r] = s_rbase[g * R + r] + __popcll(s_rbm[g * R + r] & bits_below(lane));
+                mask_out[r] = 1;
+            }
+        }
+        for (int r0 = 0; R <= kBallotRanks && r0 < R; r0 += 4) {
             int32_t v[4];
             uint32_t m = 0;
 #pragma unroll
