@@ -157,3 +157,93 @@ def test_backward_pair_adjoint(o, which):
     lw = float((rtw.double() * written[:, :, None] * gw.double()).sum())
     rw = float((wi.double() * cgw.double()).sum())
     assert lw == rw, (lw, rw)
+
+
+def test_hip_graph_other_paths(o):
+    """Gating, layout, expand pack and combine, normal pack and combine (with
+    the bias) captured once in a HIP graph and replayed with new inputs
+    copied into the captured buffers, eager work between replays; every
+    replay equals an eager run on the same inputs and the oracle."""
+    w = W.WORKLOADS[3].scaled(300, 512)
+    N, H, K, E, R = w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks
+    shape = ep.shape_of(w, expert_alignment=128)
+    dev = torch.device("cuda")
+    buf = ep.allocate(shape, dev, parts=("layout", "normal", "expand"))
+    T = ep.expand_rows(shape)
+    scores = torch.empty((N, E), dtype=torch.float32, device=dev)
+    x = torch.empty((N, H), dtype=torch.int16, device=dev)
+    y_exp = torch.empty((T, H), dtype=torch.int16, device=dev)
+    y_nrm = torch.empty((R, w.num_max_dispatch_tokens_per_rank, H), dtype=torch.int16, device=dev)
+    bias = torch.empty((N, H), dtype=torch.int16, device=dev)
+    idx = torch.empty((N, K), dtype=torch.int64, device=dev)
+    wts = torch.empty((N, K), dtype=torch.float32, device=dev)
+    out_e = torch.empty((N, H), dtype=torch.int16, device=dev)
+    out_n = torch.empty((N, H), dtype=torch.int16, device=dev)
+
+    def step():
+        ep.ep_group_limited_topk(shape, 8, 4, scores, idx, wts)
+        ep.ep_layout(shape, idx, buf["num_tokens_per_rank"], buf["num_tokens_per_expert"],
+                     buf["is_token_in_rank"], buf["expert_slot"], buf["rank_slot"],
+                     buf["expert_offset"], buf["workspace"], buf["status"])
+        ep.ep_dispatch_expand(shape, x, idx, buf["expert_slot"], buf["expert_offset"],
+                              buf["num_tokens_per_expert"], buf["recv_x_expand"],
+                              buf["recv_scales_expand"], buf["recv_src_idx_expand"], buf["status"])
+        ep.ep_combine_expand(shape, y_exp, idx, wts, buf["expert_slot"], buf["expert_offset"], out_e,
+                             buf["status"], bias=bias)
+        ep.ep_dispatch_normal(shape, x, idx, wts, buf["rank_slot"], buf["recv_x_normal"],
+                              buf["recv_scales_normal"], buf["recv_topk_idx"],
+                              buf["recv_topk_weights"], buf["recv_src_idx_normal"], buf["status"])
+        ep.ep_combine_normal(shape, y_nrm, buf["rank_slot"], buf["recv_topk_weights"], out_n,
+                             buf["combined_topk_weights"], buf["status"], bias=bias)
+
+    def load(seed):
+        rng = np.random.default_rng(seed)
+        scores.copy_(torch.from_numpy(rng.standard_normal((N, E)).astype(np.float32)))
+        x.copy_(torch.from_numpy(W.bf16_bits(rng.standard_normal((N, H), dtype=np.float32)).view(np.int16)))
+        y_exp.copy_(torch.from_numpy(W.bf16_bits(rng.standard_normal((T, H), dtype=np.float32)).view(np.int16)))
+        y_nrm.copy_(torch.from_numpy(W.bf16_bits(
+            rng.standard_normal(tuple(y_nrm.shape), dtype=np.float32)).view(np.int16)))
+        bias.copy_(torch.from_numpy(W.bf16_bits(rng.standard_normal((N, H), dtype=np.float32)).view(np.int16)))
+
+    def snapshot():
+        torch.cuda.synchronize()
+        used = int(buf["expert_offset"][-1].item())
+        return {"idx": idx.cpu().numpy(), "wts": wts.cpu().numpy(),
+                "off": buf["expert_offset"].cpu().numpy(),
+                "recv_e": buf["recv_x_expand"][:used].cpu().numpy(),
+                "recv_n": buf["recv_x_normal"].cpu().numpy(),
+                "cnt_r": buf["num_tokens_per_rank"].cpu().numpy(),
+                "out_e": out_e.cpu().numpy(), "out_n": out_n.cpu().numpy(),
+                "cw": buf["combined_topk_weights"].cpu().numpy()}
+
+    load(3)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep, seed in enumerate((5, 5, 6, 7)):
+        say(f"graph replay {rep} of the other paths (seed {seed})")
+        load(seed)
+        torch.cuda.synchronize()
+        step()
+        eager = snapshot()
+        out_e.fill_(-1)
+        out_n.fill_(-1)  # ordinary eager work between replays
+        graph.replay()
+        replay = snapshot()
+        for key in eager:
+            assert np.array_equal(eager[key].view(np.uint8), replay[key].view(np.uint8)), (rep, key)
+        assert int(buf["status"].item()) == 0
+        # and the oracle on this replay's inputs
+        want_idx, _, _ = o.group_limited_topk(scores.cpu().numpy(), 8, 4, K)
+        assert np.array_equal(replay["idx"], want_idx)
+        lay = o.layout(want_idx, E, R, alignment=128)
+        assert np.array_equal(replay["off"], lay["expert_offset"])
+        want_e, _ = o.combine_expand(y_exp.cpu().numpy().view(np.uint16), want_idx, replay["wts"],
+                                     lay["expert_slot"], lay["expert_offset"],
+                                     bias=bias.cpu().numpy().view(np.uint16))
+        assert np.array_equal(replay["out_e"].view(np.uint16), want_e)
