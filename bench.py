@@ -700,9 +700,12 @@ PROFILE_COMMANDS = {
 def _grid_threads(n, h, kind):
     """Grid size (threads) of a kernel on a workload: pack and combine run one
     wave per (token, 1024-channel chunk), four waves per block; the layout
-    kernels one lane per token, 256 tokens per block."""
-    if kind == "layout":
-        return max(1, -(-n // 256)) * 256
+    kernels one lane per token, 256 tokens per block, and the assign kernel
+    one more block (the totals) when there are several token blocks."""
+    if kind in ("layout_count", "layout_assign"):
+        blocks = max(1, -(-n // 256))
+        extra = 1 if kind == "layout_assign" and blocks > 1 else 0
+        return (blocks + extra) * 256
     return -(-(n * -(-h // 1024)) // 4) * 256
 
 
@@ -749,16 +752,19 @@ def summarize_profiles(out_dir):
         p = inp["num_valid"]
         nb = algorithmic_bytes(w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks, p,
                                w.use_fp8)
-        for kname, kind, phase in (("combine_kernel", "combine", "combine"),
-                                   ("pack_fp8_kernel", "pack", "dispatch"),
-                                   ("layout_assign_kernel", "layout", "layout"),
-                                   ("layout_count_kernel", "layout", "layout")):
+        # (kernel, grid kind, entry point, summary name); the pack is the FP8
+        # instantiation of pack_kernel on dense rows
+        for kname, kind, phase, short in (("combine_kernel", "combine", "combine", "combine"),
+                                          ("pack_kernel", "pack", "dispatch", "pack_fp8"),
+                                          ("layout_assign_kernel", "layout_assign", "layout",
+                                           "layout_assign"),
+                                          ("layout_count_kernel", "layout_count", "layout",
+                                           "layout_count")):
             grid = str(_grid_threads(w.num_tokens, w.hidden, kind))
             durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
                     if r["Kernel_Name"] == kname and r["Grid_Size_X"] == grid]
             if not durs:
                 continue
-            short = kname.replace("_kernel", "")
             lines = [
                 f"# {kname}, workload {w.name}",
                 f"# N={w.num_tokens} H={w.hidden} K={w.num_topk} E={w.num_experts} R={w.num_ranks} "
@@ -778,13 +784,13 @@ def summarize_profiles(out_dir):
             if wid == 3:
                 lines += [f"algorithmic_bytes_per_launch ({phase} entry point): {nb[phase]}",
                           f"achieved_GBps_at_trace_avg: {nb[phase] / statistics.fmean(durs) / 1e3:.1f}"
-                          if kind != "layout" else "achieved_GBps_at_trace_avg: n/a (two kernels)"]
+                          if phase != "layout" else "achieved_GBps_at_trace_avg: n/a (two kernels)"]
             lines += ["", "## rocprofv3 --stats (all kernels of the run, both workloads)", stats_txt]
             path = os.path.join(PROFILES, f"{short}_{w.name}_trace.txt")
             with open(path, "w") as f:
                 f.write("\n".join(lines) + "\n")
             written.append(path)
-            if wid != 3 or kind == "layout":
+            if wid != 3 or phase == "layout":
                 continue
             per = {}
             for c in ("FETCH_SIZE", "WRITE_SIZE"):
