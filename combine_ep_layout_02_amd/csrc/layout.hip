@@ -14,11 +14,13 @@
 //           tokens per rank, each token counted once per rank);
 //   assign: each block sums the histograms of the blocks before it (one
 //           coalesced pass with all loads in flight), ranks its own entries
-//           with LDS bitmaps -- one 64-bit word per (wave, expert), bit = lane
-//           -- so an entry's in-block prefix is the popcount of the lower bits
-//           of its expert's word plus the popcounts of the earlier waves'
-//           words.  One extra block sums every histogram row at the same time
-//           and writes the totals and the offset scan.
+//           with LDS bitmaps -- one 64-bit word per (wave, expert) and per
+//           (wave, rank), bit = lane.  One pass over the columns turns the
+//           words into a base per (wave, column): earlier blocks' count plus
+//           the popcounts of the earlier waves' words.  An entry's slot is
+//           then its wave's base plus the popcount of the lower bits of its
+//           own wave's word.  One extra block sums every histogram row at the
+//           same time and writes the totals and the offset scan.
 // The count kernel is skipped when one block covers every token; that block
 // then counts its own totals.
 //
@@ -40,6 +42,12 @@ constexpr int kBallotRanks = 16;
 
 __device__ __forceinline__ uint64_t bits_below(int bit) { return (1ull << bit) - 1ull; }
 
+// e / L for 0 <= e < 1024 and 1 <= L <= 1024 as a multiply and a shift:
+// with m = ceil(2^21 / L) the error of e * m / 2^21 against e / L is below
+// e * L / (L * 2^21) < 1 / L, too small to cross the next multiple of 1 / L.
+__device__ __forceinline__ uint32_t rank_magic(int32_t L) { return ((1u << 21) + L - 1) / L; }
+__device__ __forceinline__ int rank_of(int32_t e, uint32_t magic) { return (int)(((uint32_t)e * magic) >> 21); }
+
 // The token's K expert ids into e[0..KMAX): ids outside [0, E) become -1 (and
 // set `bad` unless they are -1); k >= K or a token past N gives -1.
 template <int KMAX>
@@ -48,9 +56,21 @@ __device__ __forceinline__ void load_token(const int64_t *__restrict__ topk_idx,
                                            uint32_t &bad)
 {
     int64_t v[KMAX];
+    if ((K & 1) == 0 && (reinterpret_cast<uintptr_t>(topk_idx) & 15) == 0) {
+        // an even K on a 16-byte aligned base keeps every row aligned: two
+        // ids per load
+        const longlong2 *row = reinterpret_cast<const longlong2 *>(topk_idx + t * K);
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-        v[k] = (t < N && k < K) ? topk_idx[t * K + k] : -1;
+        for (int q = 0; q < KMAX / 2; ++q) {
+            const longlong2 p = (t < N && 2 * q < K) ? row[q] : make_longlong2(-1, -1);
+            v[2 * q] = p.x;
+            v[2 * q + 1] = p.y;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            v[k] = (t < N && k < K) ? topk_idx[t * K + k] : -1;
+    }
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
         const bool ok = v[k] >= 0 && v[k] < (int64_t)E;
@@ -73,12 +93,13 @@ __global__ __launch_bounds__(kThreads) void layout_count_kernel(
     for (int i = tid; i < E + R; i += kThreads)
         s_cnt[i] = 0;
     __syncthreads();
+    const uint32_t magic = rank_magic(L);
     uint64_t ranks = 0;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
         if (e[k] >= 0) {
             atomicAdd(&s_cnt[e[k]], 1);
-            ranks |= 1ull << (e[k] / L);
+            ranks |= 1ull << rank_of(e[k], magic);
         }
     }
     // tokens per rank: one ballot per rank gives the wave's count directly;
@@ -101,8 +122,10 @@ __global__ __launch_bounds__(kThreads) void layout_count_kernel(
 
 __host__ __device__ inline size_t assign_lds_bytes(int E, int R)
 {
-    return sizeof(uint64_t) * (size_t)kGroups * (E + R) + sizeof(int32_t) * (size_t)(E + R) * 2 +
-           sizeof(int32_t) * 8 + sizeof(int32_t) * (size_t)kGroups * R;
+    // bitmaps [kGroups][E + R] (u64), wave bases [kGroups][E + R], totals
+    // [E + R], misc [8]
+    return sizeof(uint64_t) * (size_t)kGroups * (E + R) + sizeof(int32_t) * (size_t)kGroups * (E + R) +
+           sizeof(int32_t) * (size_t)(E + R) + sizeof(int32_t) * 8;
 }
 
 // Number of entries of `e` among the block's tokens before this lane's token
@@ -217,16 +240,15 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
     int32_t *__restrict__ rank_slot, int32_t *__restrict__ expert_offset, uint32_t *status)
 {
     extern __shared__ __align__(16) char lds_raw[];
-    uint64_t *s_bm = reinterpret_cast<uint64_t *>(lds_raw);      // [kGroups][E]
-    uint64_t *s_rbm = s_bm + (size_t)kGroups * E;                // [kGroups][R]
-    int32_t *s_base = reinterpret_cast<int32_t *>(s_rbm + (size_t)kGroups * R); // [E+R]
-    int32_t *s_tot = s_base + (E + R);                           // [E+R]
-    int32_t *s_misc = s_tot + (E + R);                           // [8]
-    int32_t *s_rbase = s_misc + 8; // [kGroups][R], many-rank path: rank slot base per wave
+    const int W = E + R; // one column per expert, then one per rank
+    uint64_t *s_bm = reinterpret_cast<uint64_t *>(lds_raw); // [kGroups][W]: expert, then rank words
+    int32_t *s_wb = reinterpret_cast<int32_t *>(s_bm + (size_t)kGroups * W); // [kGroups][W]
+    int32_t *s_tot = s_wb + (size_t)kGroups * W;                             // [W]
+    int32_t *s_misc = s_tot + W;                                             // [8]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int g = tid >> 6;
+    const int g = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b = blockIdx.x;
     const int num_token_blocks = hist ? (int)gridDim.x - 1 : 1;
     if (b == num_token_blocks) {
@@ -255,16 +277,15 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
         const int i = tid + u * kThreads;
         hv[u] = i < n4 ? h4[i] : make_int4(0, 0, 0, 0);
     }
-    for (int i = tid; i < kGroups * (E + R); i += kThreads)
-        s_bm[i] = 0ull; // s_bm and s_rbm are contiguous
-    for (int i = tid; i < E + R; i += kThreads) {
-        s_base[i] = 0;
-        s_tot[i] = 0;
-    }
+    for (int i = tid; i < kGroups * W; i += kThreads)
+        s_bm[i] = 0ull;
+    for (int i = tid; i < W; i += kThreads)
+        s_wb[i] = 0; // row 0: the earlier blocks' counts
     if (tid < 8)
         s_misc[tid] = 0;
 
     // 2. within-token occurrence index of each entry's expert, and rank set
+    const uint32_t magic = rank_magic(L);
     int occ[KMAX];
     int maxocc = 0;
     uint64_t ranks = 0;
@@ -276,12 +297,12 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
             occ[k] += (e[k] >= 0 && e[k2] == e[k]) ? 1 : 0;
         maxocc = max(maxocc, occ[k]);
         if (e[k] >= 0)
-            ranks |= 1ull << (e[k] / L);
+            ranks |= 1ull << rank_of(e[k], magic);
     }
     __syncthreads(); // LDS cleared
 
-    // 3. counts of all earlier blocks into s_base: the slice loaded above,
-    //    then further slices of kHistBatch int4 per thread (many blocks only)
+    // 3. counts of all earlier blocks into row 0 of s_wb: the slice loaded
+    //    above, then further slices of kHistBatch int4 per thread
     for (int i0 = tid; i0 < n4; i0 += kThreads * kHistBatch) {
         if (i0 != tid) {
 #pragma unroll
@@ -295,36 +316,36 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
             const int i = i0 + u * kThreads;
             if (i < n4) {
                 const int c = (i * 4) % stride;
-                if (c < E + R)
-                    atomicAdd(&s_base[c], hv[u].x);
-                if (c + 1 < E + R)
-                    atomicAdd(&s_base[c + 1], hv[u].y);
-                if (c + 2 < E + R)
-                    atomicAdd(&s_base[c + 2], hv[u].z);
-                if (c + 3 < E + R)
-                    atomicAdd(&s_base[c + 3], hv[u].w);
+                if (c < W)
+                    atomicAdd(&s_wb[c], hv[u].x);
+                if (c + 1 < W)
+                    atomicAdd(&s_wb[c + 1], hv[u].y);
+                if (c + 2 < W)
+                    atomicAdd(&s_wb[c + 2], hv[u].z);
+                if (c + 3 < W)
+                    atomicAdd(&s_wb[c + 3], hv[u].w);
             }
         }
     }
 
-    // 4. layer-0 bitmaps (first occurrences) and rank bitmaps
+    // 4. layer-0 bitmaps (first occurrences) and rank words
+    uint64_t *my_words = s_bm + (size_t)g * W;
     const uint64_t bit = 1ull << lane;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
         if (e[k] >= 0 && occ[k] == 0)
-            atomicOr((unsigned long long *)&s_bm[g * E + e[k]], (unsigned long long)bit);
+            atomicOr((unsigned long long *)&my_words[e[k]], (unsigned long long)bit);
     // rank words: one ballot per rank gives this wave's word directly; with
     // many ranks each token sets its bit in its own ranks' words
     if (R <= kBallotRanks) {
         for (int r = 0; r < R; ++r) {
             const uint64_t m = __ballot((ranks >> r) & 1ull);
             if (lane == 0)
-                s_rbm[g * R + r] = m;
+                my_words[E + r] = m;
         }
     } else {
         for (uint64_t m = ranks; m; m &= m - 1)
-            atomicOr((unsigned long long *)&s_rbm[g * R + __builtin_ctzll(m)],
-                     (unsigned long long)bit);
+            atomicOr((unsigned long long *)&my_words[E + __builtin_ctzll(m)], (unsigned long long)bit);
     }
     if (maxocc > 0)
         atomicMax(&s_misc[0], maxocc);
@@ -332,69 +353,88 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
         atomicOr(&s_misc[1], 1);
     __syncthreads();
 
-    // pre[k]: earlier blocks' entries of the expert + this block's entries of
-    // earlier tokens (layer 0) + earlier entries of this token (occ)
+    // 5. wave bases: s_wb[g][c] = earlier blocks' entries of column c plus
+    //    this block's in waves before g; the running sum past the last wave
+    //    is the block's total, which a single block keeps as the totals
+    for (int c = tid; c < W; c += kThreads) {
+        int run = s_wb[c];
+#pragma unroll
+        for (int g2 = 0; g2 < kGroups; ++g2) {
+            if (g2 > 0)
+                s_wb[g2 * W + c] = run;
+            run += __popcll(s_bm[g2 * W + c]);
+        }
+        s_tot[c] = run;
+    }
+    __syncthreads();
+
+    // pre[k]: wave base of the expert + earlier lanes of this wave (layer 0)
+    // + earlier entries of this token (occ)
+    const int32_t *my_base = s_wb + (size_t)g * W;
+    const uint64_t below = bits_below(lane);
     int pre[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
-        pre[k] = e[k] >= 0 ? s_base[e[k]] + prefix_in_block(&s_bm[e[k]], E, g, lane) + occ[k] : 0;
-    if (last_block) {
-        for (int i = tid; i < E; i += kThreads) {
-            int c = 0;
-            for (int g2 = 0; g2 < kGroups; ++g2)
-                c += __popcll(s_bm[g2 * E + i]);
-            s_tot[i] = c;
+        pre[k] = e[k] >= 0 ? my_base[e[k]] + __popcll(my_words[e[k]] & below) + occ[k] : 0;
+    // rank slots of the token's ranks (read before a repeat layer reuses the words)
+    int32_t rs[kBallotRanks];
+    if (R <= kBallotRanks) {
+#pragma unroll
+        for (int r = 0; r < kBallotRanks; ++r)
+            rs[r] = (r < R && ((ranks >> r) & 1ull)) ? my_base[E + r] + __popcll(my_words[E + r] & below) : -1;
+    }
+    const bool vec_rows = (R & 3) == 0 && (reinterpret_cast<uintptr_t>(rank_slot) & 15) == 0 &&
+                          (reinterpret_cast<uintptr_t>(is_token_in_rank) & 3) == 0;
+    if (live && R > kBallotRanks) {
+        // many ranks: the row as "not sent" first, then the token's own ranks
+        // (the same thread's stores to one address land in program order)
+        uint8_t *mask_out = is_token_in_rank + t * R;
+        int32_t *rslot_out = rank_slot + t * R;
+        if (vec_rows) {
+            for (int r0 = 0; r0 < R; r0 += 4) {
+                *reinterpret_cast<int4 *>(rslot_out + r0) = make_int4(-1, -1, -1, -1);
+                *reinterpret_cast<uint32_t *>(mask_out + r0) = 0u;
+            }
+        } else {
+            for (int r = 0; r < R; ++r) {
+                rslot_out[r] = -1;
+                mask_out[r] = 0;
+            }
         }
-        for (int i = tid; i < R; i += kThreads) {
-            int c = 0;
-            for (int g2 = 0; g2 < kGroups; ++g2)
-                c += __popcll(s_rbm[g2 * R + i]);
-            s_tot[E + i] = c;
+        for (uint64_t m = ranks; m; m &= m - 1) {
+            const int r = __builtin_ctzll(m);
+            rslot_out[r] = my_base[E + r] + __popcll(my_words[E + r] & below);
+            mask_out[r] = 1;
         }
     }
 
-    // many ranks: each wave's rank-slot base (earlier blocks' tokens of the
-    // rank plus this block's earlier waves'), so a token's rank slot is one
-    // popcount away
-    if (R > kBallotRanks) {
-        for (int i = tid; i < kGroups * R; i += kThreads) {
-            const int g2 = i / R, r = i - g2 * R;
-            int c = s_base[E + r];
-            for (int g3 = 0; g3 < g2; ++g3)
-                c += __popcll(s_rbm[g3 * R + r]);
-            s_rbase[i] = c;
-        }
-    }
-
-    // 5. repeated experts: one more bitmap layer per occurrence index
+    // 6. repeated experts: one more bitmap layer per occurrence index
     const int layers = s_misc[0] + 1;
     for (int layer = 1; layer < layers; ++layer) {
         __syncthreads(); // every read of the previous layer is done
-        for (int i = tid; i < kGroups * E; i += kThreads)
+        for (int i = tid; i < kGroups * W; i += kThreads)
             s_bm[i] = 0ull;
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
             if (e[k] >= 0 && occ[k] == layer)
-                atomicOr((unsigned long long *)&s_bm[g * E + e[k]], (unsigned long long)bit);
+                atomicOr((unsigned long long *)&my_words[e[k]], (unsigned long long)bit);
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
             if (e[k] >= 0)
-                pre[k] += prefix_in_block(&s_bm[e[k]], E, g, lane);
+                pre[k] += prefix_in_block(&s_bm[e[k]], W, g, lane);
         if (last_block) {
             for (int i = tid; i < E; i += kThreads) {
                 int c = 0;
                 for (int g2 = 0; g2 < kGroups; ++g2)
-                    c += __popcll(s_bm[g2 * E + i]);
+                    c += __popcll(s_bm[g2 * W + i]);
                 s_tot[i] += c;
             }
         }
     }
 
-    // 6. this token's outputs (16-byte stores where the row allows them)
-    if (R > kBallotRanks)
-        __syncthreads(); // s_rbase complete
+    // 7. this token's outputs (16-byte stores where the row allows them)
     if (live) {
         int32_t slot[KMAX];
 #pragma unroll
@@ -413,47 +453,26 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
                 if (k < K)
                     slot_out[k] = slot[k];
         }
-        uint8_t *mask_out = is_token_in_rank + t * R;
-        int32_t *rslot_out = rank_slot + t * R;
-        const bool vec = (R & 3) == 0 && (reinterpret_cast<uintptr_t>(rslot_out) & 15) == 0 &&
-                         (reinterpret_cast<uintptr_t>(mask_out) & 3) == 0;
-        if (R > kBallotRanks) {
-            // the row as "not sent" first, then the token's own ranks (the
-            // same thread's stores to one address land in program order)
-            if (vec) {
-                for (int r0 = 0; r0 < R; r0 += 4) {
-                    *reinterpret_cast<int4 *>(rslot_out + r0) = make_int4(-1, -1, -1, -1);
-                    *reinterpret_cast<uint32_t *>(mask_out + r0) = 0u;
-                }
-            } else {
-                for (int r = 0; r < R; ++r) {
-                    rslot_out[r] = -1;
-                    mask_out[r] = 0;
-                }
-            }
-            for (uint64_t m = ranks; m; m &= m - 1) {
-                const int r = __builtin_ctzll(m);
-                rslot_out[r] = s_rbase[g * R + r] + __popcll(s_rbm[g * R + r] & bits_below(lane));
-                mask_out[r] = 1;
-            }
-        }
-        for (int r0 = 0; R <= kBallotRanks && r0 < R; r0 += 4) {
-            int32_t v[4];
-            uint32_t m = 0;
+        if (R <= kBallotRanks) {
+            uint8_t *mask_out = is_token_in_rank + t * R;
+            int32_t *rslot_out = rank_slot + t * R;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int r = r0 + q;
-                const bool in = r < R && ((ranks >> r) & 1ull);
-                v[q] = in ? s_base[E + r] + prefix_in_block(&s_rbm[r], R, g, lane) : -1;
-                m |= (in ? 1u : 0u) << (8 * q);
-            }
-            if (vec) {
-                *reinterpret_cast<int4 *>(rslot_out + r0) = make_int4(v[0], v[1], v[2], v[3]);
-                *reinterpret_cast<uint32_t *>(mask_out + r0) = m;
-            } else {
-                for (int q = 0; q < 4 && r0 + q < R; ++q) {
-                    rslot_out[r0 + q] = v[q];
-                    mask_out[r0 + q] = (uint8_t)((m >> (8 * q)) & 1u);
+            for (int r0 = 0; r0 < kBallotRanks; r0 += 4) {
+                if (r0 < R) {
+                    uint32_t m = 0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        m |= (rs[r0 + q] >= 0 ? 1u : 0u) << (8 * q);
+                    if (vec_rows) {
+                        *reinterpret_cast<int4 *>(rslot_out + r0) =
+                            make_int4(rs[r0], rs[r0 + 1], rs[r0 + 2], rs[r0 + 3]);
+                        *reinterpret_cast<uint32_t *>(mask_out + r0) = m;
+                    } else {
+                        for (int q = 0; q < 4 && r0 + q < R; ++q) {
+                            rslot_out[r0 + q] = rs[r0 + q];
+                            mask_out[r0 + q] = (uint8_t)((m >> (8 * q)) & 1u);
+                        }
+                    }
                 }
             }
         }
@@ -461,11 +480,8 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
     if (tid == 0 && status && s_misc[1])
         atomicOr(status, EP_STATUS_BAD_EXPERT_ID);
 
-    // 7. single token block: it holds every count; write totals and the scan
+    // 8. single token block: it holds every count; write totals and the scan
     if (last_block) {
-        __syncthreads();
-        for (int i = tid; i < E + R; i += kThreads)
-            s_tot[i] += s_base[i];
         __syncthreads();
         write_totals_and_offsets(E, R, A, s_tot, s_misc, num_tokens_per_rank,
                                  num_tokens_per_expert, expert_offset);
