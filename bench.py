@@ -23,6 +23,7 @@ Prints ONE JSON line.  With --gpus > 1 it exits: the path runs on one GPU.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -37,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak, AMD's published figure
+FUSED_MAX_TOKENS = 256  # ep_layout_dispatch is one launch up to this many tokens
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -150,12 +152,24 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
         ep.ep_combine(shape, y, topk_idx, topk_weights, buf["expert_slot"], buf["combined_x"],
                       buf["status"])
 
+    def layout_dispatch():
+        ep.ep_layout_dispatch(shape, topk_idx, x, buf["num_tokens_per_rank"],
+                              buf["num_tokens_per_expert"], buf["is_token_in_rank"],
+                              buf["expert_slot"], buf["rank_slot"], buf["expert_offset"],
+                              buf["workspace"], buf["recv_x"], buf["recv_scales"],
+                              buf["recv_src_idx"], buf["status"])
+
     def evict():
         if scrub is not None:
             torch.sum(scrub, dim=0, out=scrub_out)
 
     def new_events(n):
-        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        # torch creates an event's handle at its first record: record each
+        # once here so that no handle is created inside a timed region
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record(stream)
+        return evs
 
     say(f"workload {w.name}: {warmup} warmup steps")
     for _ in range(warmup):
@@ -170,6 +184,8 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
     say(f"workload {w.name}: {steps} timed steps, cache evicted before each")
     evs = [new_events(2) for _ in range(steps)]
     torch.cuda.synchronize()
+    gc.collect()
+    gc.disable()  # no collector pause while the host enqueues a timed step
     t0 = time.perf_counter()
     for e in evs:
         evict()
@@ -180,6 +196,7 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
         e[1].record(stream)
     torch.cuda.synchronize()
     wall_cold = time.perf_counter() - t0
+    gc.enable()
     cold = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
     say(f"workload {w.name}: cold step times (us): " + " ".join(f"{v:.1f}" for v in cold))
 
@@ -211,6 +228,37 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
             e[1].record(stream)
         torch.cuda.synchronize()
         kernels[name] = [e[0].elapsed_time(e[1]) * 1e3 / batch for e in evs]
+
+    fused = None
+    if w.num_tokens <= FUSED_MAX_TOKENS:
+        # the one-launch layout + dispatch entry point, then the combine
+        say(f"workload {w.name}: {steps} cold steps through ep_layout_dispatch")
+        evs = [new_events(2) for _ in range(steps)]
+        for e in evs:
+            evict()
+            e[0].record(stream)
+            layout_dispatch()
+            combine()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        fused = {"step": [e[0].elapsed_time(e[1]) * 1e3 for e in evs]}
+        evs = [new_events(2) for _ in range(steps)]
+        for e in evs:
+            evict()
+            e[0].record(stream)
+            layout_dispatch()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        fused["layout_dispatch"] = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
+        evs = [new_events(2) for _ in range(steps)]
+        for e in evs:
+            evict()
+            e[0].record(stream)
+            for _ in range(batch):
+                layout_dispatch()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        fused["back_to_back"] = [e[0].elapsed_time(e[1]) * 1e3 / batch for e in evs]
 
     say(f"workload {w.name}: the step captured in a HIP graph, {steps} replays")
     graph = torch.cuda.CUDAGraph()
@@ -267,6 +315,12 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
         "phases": {k: stats(v, nbytes[k]) for k, v in phases.items()},
         "kernels": {k: stats(v, nbytes[k]) for k, v in kernels.items()},
         "warm_us_per_step": round(warm_us, 2),
+        "fused": None if fused is None else {
+            "step_us_cold": stats(fused["step"], nbytes["total"]),
+            "layout_dispatch_us_cold": stats(fused["layout_dispatch"],
+                                             nbytes["layout"] + nbytes["dispatch"]),
+            "layout_dispatch_us_back_to_back": stats(fused["back_to_back"],
+                                                     nbytes["layout"] + nbytes["dispatch"])},
         "wall_cold_s": wall_cold,
         "inputs": inp,
     }
@@ -296,15 +350,27 @@ def receive_layout_bytes(n, h, k, r, p, rows_sent, pad_rows, use_fp8, scale_form
     }
 
 
+def _recorded_event_pair(stream):
+    """Two timing events, each recorded once (torch creates an event's handle
+    at its first record), so no handle is created inside a timed region."""
+    import torch
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0, e1
+
+
 def _timed_batches(fn, steps, batch, evict, stream):
     """Average duration of one call: ``batch`` back-to-back calls between two
     events after an untimed eviction, ``steps`` times."""
     import torch
 
     times = []
+    e0, e1 = _recorded_event_pair(stream)
     for _ in range(steps):
         evict()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(batch):
             fn()
@@ -322,9 +388,9 @@ def _timed_cold(fn, steps, evict, stream):
     import torch
 
     times = []
+    e0, e1 = _recorded_event_pair(stream)
     for _ in range(steps):
         evict()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         fn()
         e1.record(stream)
@@ -470,9 +536,9 @@ def time_config(wid, steps, warmup, scrub_bytes, say):
     torch.cuda.synchronize()
     say(f"workload {w.name}: {steps} cold steps")
     times = []
+    e0, e1 = _recorded_event_pair(stream)
     for _ in range(steps):
         evict()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         step()
         e1.record(stream)
@@ -620,10 +686,10 @@ def time_scale_formats(wid, steps, scrub_bytes, say, batch=10):
                      buf["expert_offset"], buf["workspace"], buf["status"])
         say(f"ep_dispatch {w.name} scale format {label}: {steps} x {batch} launches")
         times = []
+        e0, e1 = _recorded_event_pair(stream)
         for _ in range(steps):
             if scrub is not None:
                 torch.sum(scrub, dim=0, out=scrub_out)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for _ in range(batch):
                 ep.ep_dispatch(shape, x, topk_idx, buf["expert_slot"], buf["recv_x"],
@@ -706,6 +772,8 @@ def _grid_threads(n, h, kind):
         blocks = max(1, -(-n // 256))
         extra = 1 if kind == "layout_assign" and blocks > 1 else 0
         return (blocks + extra) * 256
+    if kind == "fused":  # one 512-thread block per token plus the totals block
+        return (n + 1) * 512
     return -(-(n * -(-h // 1024)) // 4) * 256
 
 
@@ -759,12 +827,19 @@ def summarize_profiles(out_dir):
                                           ("layout_assign_kernel", "layout_assign", "layout",
                                            "layout_assign"),
                                           ("layout_count_kernel", "layout_count", "layout",
-                                           "layout_count")):
+                                           "layout_count"),
+                                          ("layout_pack_small_kernel", "fused", "layout_dispatch",
+                                           "layout_pack_small")):
             grid = str(_grid_threads(w.num_tokens, w.hidden, kind))
             durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
                     if r["Kernel_Name"] == kname and r["Grid_Size_X"] == grid]
             if not durs:
                 continue
+            ex = traced["extra"] if wid == 3 else traced["extra"]["decode_128x7168"]
+            if phase == "layout_dispatch":
+                same_run = ex["step_through_ep_layout_dispatch"]["layout_dispatch_us_back_to_back"]
+            else:
+                same_run = ex["kernel_avg_us_back_to_back"][phase]
             lines = [
                 f"# {kname}, workload {w.name}",
                 f"# N={w.num_tokens} H={w.hidden} K={w.num_topk} E={w.num_experts} R={w.num_ranks} "
@@ -777,8 +852,7 @@ def summarize_profiles(out_dir):
                 f"avg_us: {statistics.fmean(durs):.2f}",
                 f"median_us: {statistics.median(durs):.2f}",
                 f"min_us: {min(durs):.2f}  max_us: {max(durs):.2f}",
-                f"bench_avg_launch_us_same_run: "
-                f"{(traced['extra'] if wid == 3 else traced['extra']['decode_128x7168'])['kernel_avg_us_back_to_back'][phase]['us_mean']}"
+                f"bench_avg_launch_us_same_run: {same_run['us_mean']}"
                 f" ({phase} entry point, back-to-back launches timed with HIP events)",
             ]
             if wid == 3:
@@ -1020,6 +1094,7 @@ def main():
             "phases_us_with_events_between": decode["phases"],
             "kernel_avg_us_back_to_back": decode["kernels"],
             "step_us_warm": decode["warm_us_per_step"], "bytes_per_step": decode["bytes"],
+            "step_through_ep_layout_dispatch": decode["fused"],
         }
     line = {
         "metric": "dispatch+combine achieved HBM GB/s (4096 tok x hidden 7168, FP8 dispatch, BF16 combine)",

@@ -362,6 +362,185 @@ __global__ __launch_bounds__(kThreads) void pack_normal_kernel(
         atomicOr(status, flags);
 }
 
+// Layout and per-expert pack of a small batch in one launch.  Block t < N
+// owns token t.  Its threads first count, in LDS, the expert ids of tokens
+// 0..t-1 (thread i takes token i) and the ranks those tokens go to.  The
+// slot of entry (t, k) -- the number of earlier entries with the same expert
+// in (token, k) order -- is then that count plus the entries of t before k
+// with the same expert, and the token's rank slot at rank r is the number of
+// earlier tokens sent to r.  Wave w packs chunks w, w + 8, ... exactly as
+// pack_kernel does, and wave 0 writes the token's layout rows.  Block N counts
+// every token and writes the totals and the offset scan.  The first chunk's
+// loads are issued together with the id loads, so their latencies overlap.
+// Work per block grows with t, which the host bounds (kFusedMaxTokens).
+constexpr int kFusedThreads = 512;
+constexpr int kFusedWaves = kFusedThreads / 64;
+
+template <int KMAX, int SF, bool FP8>
+__global__ __launch_bounds__(kFusedThreads) void layout_pack_small_kernel(
+    int32_t N, int32_t H, int32_t K, int32_t E, int32_t R, int32_t S, int32_t A, int32_t nchunks,
+    const uint16_t *__restrict__ x, const int64_t *__restrict__ topk_idx,
+    int32_t *__restrict__ num_tokens_per_rank, int32_t *__restrict__ num_tokens_per_expert,
+    uint8_t *__restrict__ is_token_in_rank, int32_t *__restrict__ expert_slot,
+    int32_t *__restrict__ rank_slot, int32_t *__restrict__ expert_offset,
+    void *__restrict__ recv_x, void *__restrict__ recv_scales, int32_t *__restrict__ recv_src_idx,
+    uint32_t *status)
+{
+    __shared__ int32_t s_hist[EP_MAX_EXPERTS + EP_MAX_RANKS]; // experts, then ranks
+    __shared__ int32_t s_bad;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int t = blockIdx.x; // the token, or N for the totals block
+    const int W = E + R;
+    const uint32_t magic = rank_magic(E / R);
+
+    // 1. loads: ids of token `tid` if it precedes t; this token's entry
+    //    `lane` (every wave); the first chunk of x
+    int32_t e[KMAX];
+    uint32_t bad = 0;
+    load_token<KMAX>(topk_idx, tid, t, K, E, e, bad);
+    const bool own = t < N;
+    const int64_t id = own ? topk_idx[(size_t)t * K + min(lane, K - 1)] : -1;
+    Fp8Lane fl;
+    Fp8Payload p;
+    Bf16Lane bl;
+    uint4 a0 = make_uint4(0, 0, 0, 0), a1 = make_uint4(0, 0, 0, 0);
+    const uint16_t *x_row = x + (size_t)(own ? t : 0) * H;
+    if (own && wave < nchunks) {
+        if (FP8) {
+            fl = fp8_lane(H, wave, lane);
+            p = quantize_lane<SF>(x_row, fl, lane);
+        } else {
+            bl = bf16_lane(H, wave, lane);
+            const uint4 *src = reinterpret_cast<const uint4 *>(x_row);
+            if (bl.u0 < bl.units)
+                a0 = load_stream(src + bl.u0);
+            if (bl.u1 < bl.units)
+                a1 = load_stream(src + bl.u1);
+        }
+    }
+    for (int i = tid; i < W; i += kFusedThreads)
+        s_hist[i] = 0;
+    if (tid == 0)
+        s_bad = 0;
+    __syncthreads();
+
+    // 2. counts of the earlier tokens' entries and of their ranks
+    uint64_t ranks = 0;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        if (e[k] >= 0) {
+            atomicAdd(&s_hist[e[k]], 1);
+            ranks |= 1ull << rank_of(e[k], magic);
+        }
+    }
+    for (uint64_t m = ranks; m; m &= m - 1)
+        atomicAdd(&s_hist[E + __builtin_ctzll(m)], 1);
+    if (bad)
+        s_bad = 1;
+    __syncthreads();
+
+    if (!own) {
+        // 3a. totals block: counts, then the offset scan on wave 0 (each
+        //     lane a run of consecutive experts)
+        for (int i = tid; i < W; i += kFusedThreads) {
+            if (i < E)
+                num_tokens_per_expert[i] = s_hist[i];
+            else
+                num_tokens_per_rank[i - E] = s_hist[i];
+        }
+        if (wave == 0 && expert_offset) {
+            const int per = (E + 63) / 64;
+            const int first = lane * per;
+            int local = 0;
+            for (int i = 0; i < per; ++i)
+                if (first + i < E)
+                    local += (s_hist[first + i] + A - 1) / A * A;
+            int incl = local;
+            for (int off = 1; off < 64; off <<= 1) {
+                const int up = __shfl_up(incl, off, 64);
+                if (lane >= off)
+                    incl += up;
+            }
+            int run = incl - local;
+            for (int i = 0; i < per; ++i) {
+                if (first + i < E) {
+                    expert_offset[first + i] = run;
+                    run += (s_hist[first + i] + A - 1) / A * A;
+                }
+            }
+            if (lane == 63)
+                expert_offset[E] = incl;
+        }
+        if (tid == 0 && status && s_bad)
+            atomicOr(status, EP_STATUS_BAD_EXPERT_ID);
+        return;
+    }
+
+    // 3b. this token's entries: lane k < K holds entry k
+    const bool in_k = lane < K;
+    const bool routed = in_k && id >= 0 && id < (int64_t)E;
+    const int32_t e32 = routed ? (int32_t)id : -1;
+    int occ = 0;
+    uint64_t tok_ranks = 0;
+    for (int k2 = 0; k2 < K; ++k2) {
+        const int32_t o = __builtin_amdgcn_readlane(e32, k2);
+        occ += (k2 < lane && o >= 0 && o == e32) ? 1 : 0;
+        if (o >= 0)
+            tok_ranks |= 1ull << rank_of(o, magic);
+    }
+    const int32_t slot = routed ? s_hist[e32] + occ : -1;
+    const bool slot_ok = routed && slot < S;
+    const int64_t row = slot_ok ? (int64_t)e32 * S + slot : -1;
+    uint32_t flags = 0;
+    if (__ballot(in_k && id != -1 && !routed))
+        flags |= EP_STATUS_BAD_EXPERT_ID;
+    if (__ballot(routed && !slot_ok))
+        flags |= EP_STATUS_BAD_SLOT;
+    if (wave == 0) {
+        if (in_k)
+            expert_slot[(size_t)t * K + lane] = slot;
+        if (lane < R) {
+            const bool in = (tok_ranks >> lane) & 1ull;
+            rank_slot[(size_t)t * R + lane] = in ? s_hist[E + lane] : -1;
+            is_token_in_rank[(size_t)t * R + lane] = in ? 1 : 0;
+        }
+        if (flags && status && lane == 0)
+            atomicOr(status, flags);
+    }
+
+    // 4. pack: the first chunk's payload is ready; later chunks load theirs
+    const int32_t r_lo = (int32_t)(uint32_t)(uint64_t)row;
+    const int32_t r_hi = (int32_t)(uint32_t)((uint64_t)row >> 32);
+    for (int chunk = wave; chunk < nchunks; chunk += kFusedWaves) {
+        if (chunk != wave) {
+            if (FP8) {
+                fl = fp8_lane(H, chunk, lane);
+                p = quantize_lane<SF>(x_row, fl, lane);
+            } else {
+                bl = bf16_lane(H, chunk, lane);
+                const uint4 *src = reinterpret_cast<const uint4 *>(x_row);
+                a0 = bl.u0 < bl.units ? load_stream(src + bl.u0) : make_uint4(0, 0, 0, 0);
+                a1 = bl.u1 < bl.units ? load_stream(src + bl.u1) : make_uint4(0, 0, 0, 0);
+            }
+        }
+        for (int k2 = 0; k2 < K; ++k2) {
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane(r_lo, k2);
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane(r_hi, k2);
+            const int64_t r = (int64_t)(((uint64_t)hi << 32) | lo);
+            if (r < 0)
+                continue;
+            if (FP8)
+                store_fp8<SF>(p, fl, lane, r, H, static_cast<uint8_t *>(recv_x), recv_scales);
+            else
+                store_bf16(a0, a1, bl, r, H, static_cast<uint16_t *>(recv_x));
+            if (chunk == 0 && lane == 0)
+                recv_src_idx[r] = (int32_t)t;
+        }
+    }
+}
+
 int batch_of(int K) { return K == 1 ? 1 : K == 2 ? 2 : K <= 4 ? 4 : 8; }
 
 // Launch of the per-expert / expand pack for every (batch, scale format,
@@ -415,6 +594,45 @@ hipError_t launch_dispatch(const ep_shape &s, const uint16_t *x, const int64_t *
 {
     return launch_pack(s, 0, DenseRows{s.expert_capacity}, nullptr, x, topk_idx, expert_slot,
                        recv_x, recv_scales, recv_src_idx, status, stream);
+}
+
+bool layout_dispatch_fused(const ep_shape &s) { return s.num_tokens <= kFusedMaxTokens; }
+
+hipError_t launch_layout_dispatch_small(const ep_shape &s, const uint16_t *x,
+                                        const int64_t *topk_idx, int32_t *num_tokens_per_rank,
+                                        int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank,
+                                        int32_t *expert_slot, int32_t *rank_slot,
+                                        int32_t *expert_offset, void *recv_x, void *recv_scales,
+                                        int32_t *recv_src_idx, uint32_t *status,
+                                        hipStream_t stream)
+{
+    const int N = s.num_tokens, H = s.hidden, K = s.num_topk, E = s.num_experts;
+    const int R = s.num_ranks, S = s.expert_capacity, A = expert_alignment(s);
+    const int nchunks = (H + kChunk - 1) / kChunk;
+    const dim3 grid((unsigned)(N + 1));
+#define EP_FUSED(KMAX, SF, FP8)                                                                    \
+    hipLaunchKernelGGL((layout_pack_small_kernel<KMAX, SF, FP8>), grid, dim3(kFusedThreads), 0,    \
+                       stream, N, H, K, E, R, S, A, nchunks, x, topk_idx, num_tokens_per_rank,     \
+                       num_tokens_per_expert, is_token_in_rank, expert_slot, rank_slot,            \
+                       expert_offset, recv_x, recv_scales, recv_src_idx, status)
+#define EP_FUSED_SF(KMAX)                                                                          \
+    do {                                                                                           \
+        if (!s.use_fp8)                                                                            \
+            EP_FUSED(KMAX, EP_SCALE_FP32, false);                                                  \
+        else if (s.scale_format == EP_SCALE_POW2)                                                  \
+            EP_FUSED(KMAX, EP_SCALE_POW2, true);                                                   \
+        else if (s.scale_format == EP_SCALE_UE8M0)                                                 \
+            EP_FUSED(KMAX, EP_SCALE_UE8M0, true);                                                  \
+        else                                                                                       \
+            EP_FUSED(KMAX, EP_SCALE_FP32, true);                                                   \
+    } while (0)
+    if (K <= 8)
+        EP_FUSED_SF(8);
+    else
+        EP_FUSED_SF(EP_MAX_TOPK);
+#undef EP_FUSED_SF
+#undef EP_FUSED
+    return hipGetLastError();
 }
 
 hipError_t launch_dispatch_expand(const ep_shape &s, const uint16_t *x, const int64_t *topk_idx,

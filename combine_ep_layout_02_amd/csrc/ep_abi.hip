@@ -178,6 +178,58 @@ int ep_dispatch(const ep_shape *s, const uint16_t *x, const int64_t *topk_idx,
     return err == hipSuccess ? EP_OK : EP_ERR_HIP;
 }
 
+int ep_layout_dispatch(const ep_shape *s, const int64_t *topk_idx, const uint16_t *x,
+                       int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+                       uint8_t *is_token_in_rank, int32_t *expert_slot, int32_t *rank_slot,
+                       int32_t *expert_offset, void *workspace, size_t workspace_bytes,
+                       void *recv_x, void *recv_scales, int32_t *recv_src_idx, uint32_t *status,
+                       void *stream)
+{
+    const int rc = check_shape(s);
+    if (rc != EP_OK)
+        return rc;
+    const bool has_tokens = s->num_tokens > 0;
+    // the checks of ep_layout, then those of ep_dispatch
+    if (!num_tokens_per_rank || !num_tokens_per_expert)
+        return EP_ERR_NULL;
+    if (has_tokens && (!topk_idx || !is_token_in_rank || !expert_slot || !rank_slot))
+        return EP_ERR_NULL;
+    if (!aligned(topk_idx, 8) || !aligned(num_tokens_per_rank, 4) ||
+        !aligned(num_tokens_per_expert, 4) || !aligned(expert_slot, 4) || !aligned(rank_slot, 4) ||
+        !aligned(expert_offset, 4) || !aligned(status, 4) || !aligned(workspace, 16))
+        return EP_ERR_ALIGN;
+    ep::LayoutPlan plan;
+    ep::plan_layout(*s, &plan);
+    const bool fused = ep::layout_dispatch_fused(*s);
+    if (!fused && plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+        return EP_ERR_WORKSPACE;
+    if (has_tokens) {
+        if (!x || !recv_x || !recv_src_idx)
+            return EP_ERR_NULL;
+        if (s->use_fp8 && !recv_scales)
+            return EP_ERR_NULL;
+        if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(recv_scales, 4) ||
+            !aligned(recv_src_idx, 4))
+            return EP_ERR_ALIGN;
+    }
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (fused) {
+        err = ep::launch_layout_dispatch_small(*s, x, topk_idx, num_tokens_per_rank,
+                                               num_tokens_per_expert, is_token_in_rank, expert_slot,
+                                               rank_slot, expert_offset, recv_x, recv_scales,
+                                               recv_src_idx, status, st);
+    } else {
+        err = ep::launch_layout(*s, plan, topk_idx, num_tokens_per_rank, num_tokens_per_expert,
+                                is_token_in_rank, expert_slot, rank_slot, expert_offset,
+                                static_cast<int32_t *>(workspace), status, st);
+        if (err == hipSuccess)
+            err = ep::launch_dispatch(*s, x, topk_idx, expert_slot, recv_x, recv_scales,
+                                      recv_src_idx, status, st);
+    }
+    return err == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
 int ep_combine(const ep_shape *s, const uint16_t *expert_out, const int64_t *topk_idx,
                const float *topk_weights, const int32_t *expert_slot, const uint16_t *bias,
                uint16_t *combined_x, uint32_t *status, void *stream)

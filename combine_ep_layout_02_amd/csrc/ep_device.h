@@ -1,4 +1,5 @@
-// ep_device.h -- small device helpers shared by the pack and combine kernels.
+// ep_device.h -- small device helpers shared by the layout, pack and combine
+// kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -76,6 +77,44 @@ __device__ __forceinline__ uint32_t e4m3fn_x4_sw(float a, float b, float c, floa
 }
 
 __device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
+
+// e / L for 0 <= e < 1024 and 1 <= L <= 1024 as a multiply and a shift:
+// with m = ceil(2^21 / L) the error of e * m / 2^21 against e / L is below
+// e * L / (L * 2^21) < 1 / L, too small to cross the next multiple of 1 / L.
+__device__ __forceinline__ uint32_t rank_magic(int32_t L) { return ((1u << 21) + L - 1) / L; }
+__device__ __forceinline__ int rank_of(int32_t e, uint32_t magic) { return (int)(((uint32_t)e * magic) >> 21); }
+
+// Token t's K expert ids into e[0..KMAX): ids outside [0, E) become -1 (and
+// set `bad` unless they are -1); k >= K or a token past N gives -1.
+template <int KMAX>
+__device__ __forceinline__ void load_token(const int64_t *__restrict__ topk_idx, int64_t t,
+                                           int32_t N, int32_t K, int32_t E, int32_t (&e)[KMAX],
+                                           uint32_t &bad)
+{
+    int64_t v[KMAX];
+    if ((K & 1) == 0 && (reinterpret_cast<uintptr_t>(topk_idx) & 15) == 0) {
+        // an even K on a 16-byte aligned base keeps every row aligned: two
+        // ids per load
+        const longlong2 *row = reinterpret_cast<const longlong2 *>(topk_idx + t * K);
+#pragma unroll
+        for (int q = 0; q < KMAX / 2; ++q) {
+            const longlong2 p = (t < N && 2 * q < K) ? row[q] : make_longlong2(-1, -1);
+            v[2 * q] = p.x;
+            v[2 * q + 1] = p.y;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            v[k] = (t < N && k < K) ? topk_idx[t * K + k] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        const bool ok = v[k] >= 0 && v[k] < (int64_t)E;
+        if (!ok && v[k] != -1)
+            bad = 1u;
+        e[k] = ok ? (int32_t)v[k] : -1;
+    }
+}
 
 // Where the receive row of (expert e, slot j) lies, and whether it exists.
 //  DenseRows:  the per-expert layout [E, S, ...]: row e * S + j, 0 <= j < S

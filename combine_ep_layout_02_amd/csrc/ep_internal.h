@@ -12,10 +12,10 @@
 namespace ep {
 
 // ---- dispatch layout ---------------------------------------------------
-// The layout splits tokens into blocks of `tokens_per_block` (64, 128 or 256,
-// the largest whose LDS footprint fits) and runs two kernels: a per-block
-// histogram (skipped when one block covers every token) and a pass that adds
-// the histograms of earlier blocks to each block's local ranking.
+// The layout splits tokens into blocks of `tokens_per_block` (256) and runs
+// two kernels: a per-block histogram (skipped when one block covers every
+// token) and a pass that adds the histograms of earlier blocks to each
+// block's local ranking.
 struct LayoutPlan {
     int tokens_per_block;   // T
     int num_blocks;         // B = ceil(N / T), at least 1
@@ -24,7 +24,7 @@ struct LayoutPlan {
     size_t workspace_bytes; // B * hist_stride * 4 when B > 1, else 0
 };
 
-// Returns false when no tokens_per_block fits the LDS budget.
+// Returns false when the assign kernel's LDS does not fit in 64 KiB.
 bool plan_layout(const ep_shape &s, LayoutPlan *plan);
 
 hipError_t launch_layout(const ep_shape &s, const LayoutPlan &plan, const int64_t *topk_idx,
@@ -51,6 +51,18 @@ inline int64_t expand_rows(const ep_shape &s)
 hipError_t launch_dispatch(const ep_shape &s, const uint16_t *x, const int64_t *topk_idx,
                            const int32_t *expert_slot, void *recv_x, void *recv_scales,
                            int32_t *recv_src_idx, uint32_t *status, hipStream_t stream);
+
+// Layout and per-expert pack in one launch, for at most kFusedMaxTokens
+// tokens: the same outputs as launch_layout followed by launch_dispatch.
+constexpr int kFusedMaxTokens = 256;
+bool layout_dispatch_fused(const ep_shape &s);
+hipError_t launch_layout_dispatch_small(const ep_shape &s, const uint16_t *x,
+                                        const int64_t *topk_idx, int32_t *num_tokens_per_rank,
+                                        int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank,
+                                        int32_t *expert_slot, int32_t *rank_slot,
+                                        int32_t *expert_offset, void *recv_x, void *recv_scales,
+                                        int32_t *recv_src_idx, uint32_t *status,
+                                        hipStream_t stream);
 
 hipError_t launch_dispatch_expand(const ep_shape &s, const uint16_t *x, const int64_t *topk_idx,
                                   const int32_t *expert_slot, const int32_t *expert_offset,

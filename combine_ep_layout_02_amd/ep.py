@@ -45,7 +45,8 @@ SIZE_FIELDS = ("recv_x", "recv_scales", "recv_src_idx", "expert_out", "combined_
                "recv_x_normal", "recv_scales_normal", "recv_topk_idx", "recv_topk_weights",
                "recv_src_idx_normal", "expert_out_normal", "combined_topk_weights",
                "recv_x_expand", "recv_scales_expand", "recv_src_idx_expand", "expert_out_expand")
-EXPORTED = ("ep_query_sizes", "ep_layout", "ep_dispatch", "ep_combine", "ep_dispatch_expand",
+EXPORTED = ("ep_query_sizes", "ep_layout", "ep_dispatch", "ep_layout_dispatch", "ep_combine",
+            "ep_dispatch_expand",
             "ep_combine_expand", "ep_dispatch_normal", "ep_combine_normal",
             "ep_group_limited_topk", "ep_strerror", "ep_probe_e4m3fn")
 EP_MAX_GROUPS = 64
@@ -82,6 +83,7 @@ def lib() -> ctypes.CDLL:
         L.ep_query_sizes.argtypes = [sp, ctypes.POINTER(ep_sizes)]
         L.ep_layout.argtypes = [sp] + [vp] * 8 + [sz, vp, vp]
         L.ep_dispatch.argtypes = [sp] + [vp] * 8
+        L.ep_layout_dispatch.argtypes = [sp] + [vp] * 9 + [sz] + [vp] * 5
         L.ep_combine.argtypes = [sp] + [vp] * 8
         L.ep_dispatch_expand.argtypes = [sp] + [vp] * 10
         L.ep_combine_expand.argtypes = [sp] + [vp] * 9
@@ -209,6 +211,34 @@ def ep_dispatch(shape: ep_shape, x: torch.Tensor, topk_idx: torch.Tensor, expert
         _stream(stream, recv_x))
     if rc != EP_OK:
         raise EpError(rc, "ep_dispatch")
+
+
+def ep_layout_dispatch(shape: ep_shape, topk_idx: torch.Tensor, x: torch.Tensor,
+                       num_tokens_per_rank: torch.Tensor, num_tokens_per_expert: torch.Tensor,
+                       is_token_in_rank: torch.Tensor, expert_slot: torch.Tensor,
+                       rank_slot: torch.Tensor, expert_offset: Optional[torch.Tensor],
+                       workspace: Optional[torch.Tensor], recv_x: torch.Tensor,
+                       recv_scales: Optional[torch.Tensor], recv_src_idx: torch.Tensor,
+                       status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Layout and dispatch pack in one call; see ``ep_layout_dispatch`` in
+    include/ep.h."""
+    N, H, K, E, R, S = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts, \
+        shape.num_ranks, shape.expert_capacity
+    rows = E * S
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().ep_layout_dispatch(
+        ctypes.byref(shape), _ptr(topk_idx, "topk_idx", _I64, N * K), _ptr(x, "x", _BF16, N * H),
+        _ptr(num_tokens_per_rank, "num_tokens_per_rank", _I32, R),
+        _ptr(num_tokens_per_expert, "num_tokens_per_expert", _I32, E),
+        _ptr(is_token_in_rank, "is_token_in_rank", _U8, N * R),
+        _ptr(expert_slot, "expert_slot", _I32, N * K), _ptr(rank_slot, "rank_slot", _I32, N * R),
+        _ptr(expert_offset, "expert_offset", _I32, E + 1),
+        _ptr(workspace, "workspace", (torch.uint8, torch.int32)), ctypes.c_size_t(ws_bytes),
+        _ptr(recv_x, "recv_x", _FP8 if shape.use_fp8 else _BF16, rows * H),
+        _scales_ptr(shape, recv_scales, rows), _ptr(recv_src_idx, "recv_src_idx", _I32, rows),
+        _ptr(status, "status", _STATUS, 1), _stream(stream, num_tokens_per_expert))
+    if rc != EP_OK:
+        raise EpError(rc, "ep_layout_dispatch")
 
 
 def _scales_ptr(shape: ep_shape, recv_scales, rows: int):

@@ -209,6 +209,24 @@ int ep_dispatch(const ep_shape *shape, const uint16_t *x, const int64_t *topk_id
                 const int32_t *expert_slot, void *recv_x, void *recv_scales,
                 int32_t *recv_src_idx, uint32_t *status, void *stream);
 
+/* Layout and dispatch pack in one call ([V1] §5.2(1): the layout is computed
+ * from topk_idx before the dispatch moves data; [V1] §6.1 and §2.2: the
+ * low-latency decode path, 128 tokens per batch).  Outputs, status bits and
+ * error codes are exactly those of ep_layout followed by ep_dispatch on the
+ * same stream; the arguments are the union of theirs.
+ *
+ * Up to 256 tokens it is one launch: each token's block counts the expert
+ * ids of the tokens before it and derives the token's slots from those
+ * counts, so the pack needs no separate layout pass.  Above 256 tokens it
+ * runs the two ordinary launches, which need the workspace (the layout's;
+ * NULL with workspace_bytes 0 is allowed up to 256 tokens). */
+int ep_layout_dispatch(const ep_shape *shape, const int64_t *topk_idx, const uint16_t *x,
+                       int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+                       uint8_t *is_token_in_rank, int32_t *expert_slot, int32_t *rank_slot,
+                       int32_t *expert_offset, void *workspace, size_t workspace_bytes,
+                       void *recv_x, void *recv_scales, int32_t *recv_src_idx, uint32_t *status,
+                       void *stream);
+
 /* Combine: top-k weighted gather-reduce back into token order ([ASC] "Two
  * Transfers" and "Combine: More Output, Same Cost": outputs return to the
  * origin and are summed with the router weights; [V1] §5.2(6): BF16 in and

@@ -136,6 +136,43 @@ def test_static_shape_errors_are_reported_before_any_launch(kw, code):
     assert lib.ep_combine_expand(ctypes.byref(s), *[OK16] * 7, None, None) == code
     assert lib.ep_dispatch_normal(ctypes.byref(s), *[OK16] * 9, None, None) == code
     assert lib.ep_combine_normal(ctypes.byref(s), *[OK16] * 6, None, None) == code
+    assert _layout_dispatch(lib, s, [OK16] * 13) == code
+
+
+def _layout_dispatch(lib, s, p, ws_bytes=1 << 30):
+    """ep_layout_dispatch with pointer list p = topk_idx, x, ntpr, ntpe,
+    is_token_in_rank, expert_slot, rank_slot, expert_offset, workspace,
+    recv_x, recv_scales, recv_src_idx, status."""
+    return lib.ep_layout_dispatch(ctypes.byref(s), *p[:9], ctypes.c_size_t(ws_bytes), *p[9:], None)
+
+
+def test_layout_dispatch_argument_checks():
+    lib = ep.lib()
+    s = _shape()                               # 300 tokens: the two-launch path
+    small = _shape(num_tokens=200)             # one launch
+    for shape in (s, small):
+        for i in (0, 1, 2, 3, 4, 5, 6, 9, 11):  # every pointer but expert_offset, workspace, scales, status
+            q = [OK16] * 13
+            q[i] = None
+            assert _layout_dispatch(lib, shape, q) == ep.EP_ERR_NULL, i
+        for i in (0, 1, 2, 3, 5, 6, 7, 9, 10, 11, 12):  # is_token_in_rank is bytes
+            q = [OK16] * 13
+            q[i] = BAD
+            assert _layout_dispatch(lib, shape, q) == ep.EP_ERR_ALIGN, i
+        q = [OK16] * 13
+        q[1] = ctypes.c_void_p(0x1008)         # x rows need 16 bytes
+        assert _layout_dispatch(lib, shape, q) == ep.EP_ERR_ALIGN
+    sf = _shape(use_fp8=1)
+    q = [OK16] * 13
+    q[10] = None                               # FP8 needs the scales
+    assert _layout_dispatch(lib, sf, q) == ep.EP_ERR_NULL
+    # the workspace is the layout's, needed only above 256 tokens
+    need = ep.ep_query_sizes(s)["layout_workspace"]
+    assert need > 0
+    q = [OK16] * 13
+    q[8] = None
+    assert _layout_dispatch(lib, s, q, need) == ep.EP_ERR_WORKSPACE
+    assert _layout_dispatch(lib, s, [OK16] * 13, need - 1) == ep.EP_ERR_WORKSPACE
 
 
 def test_null_pointers_are_rejected():

@@ -390,11 +390,13 @@ def test_side_stream_and_handle_reuse(o):
     assert torch.equal(d1.recv_x, d2.recv_x) and torch.equal(d1.recv_src_idx, d2.recv_src_idx)
 
 
-def test_hip_graph_capture_and_replay(o):
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "ep_layout_dispatch"])
+def test_hip_graph_capture_and_replay(o, fused):
     """The path is capturable (no allocation, no host sync, no memset): one
-    capture of layout + dispatch + combine, replayed several times with eager
-    work in between and a new routing copied into the captured input, each
-    replay checked against an eager run and the oracle."""
+    capture of layout + dispatch + combine (the first two as separate calls or
+    as one ep_layout_dispatch), replayed several times with eager work in
+    between and a new routing copied into the captured input, each replay
+    checked against an eager run and the oracle."""
     w = W.WORKLOADS[2]
     shape = ep.shape_of(w)
     dev = torch.device("cuda")
@@ -405,11 +407,18 @@ def test_hip_graph_capture_and_replay(o):
     x = torch.empty((w.num_tokens, w.hidden), dtype=torch.int16, device=dev)
 
     def step():
-        ep.ep_layout(shape, idx, buf["num_tokens_per_rank"], buf["num_tokens_per_expert"],
-                     buf["is_token_in_rank"], buf["expert_slot"], buf["rank_slot"],
-                     buf["expert_offset"], buf["workspace"], buf["status"])
-        ep.ep_dispatch(shape, x, idx, buf["expert_slot"], buf["recv_x"], buf["recv_scales"],
-                       buf["recv_src_idx"], buf["status"])
+        if fused:
+            ep.ep_layout_dispatch(shape, idx, x, buf["num_tokens_per_rank"],
+                                  buf["num_tokens_per_expert"], buf["is_token_in_rank"],
+                                  buf["expert_slot"], buf["rank_slot"], buf["expert_offset"],
+                                  buf["workspace"], buf["recv_x"], buf["recv_scales"],
+                                  buf["recv_src_idx"], buf["status"])
+        else:
+            ep.ep_layout(shape, idx, buf["num_tokens_per_rank"], buf["num_tokens_per_expert"],
+                         buf["is_token_in_rank"], buf["expert_slot"], buf["rank_slot"],
+                         buf["expert_offset"], buf["workspace"], buf["status"])
+            ep.ep_dispatch(shape, x, idx, buf["expert_slot"], buf["recv_x"], buf["recv_scales"],
+                           buf["recv_src_idx"], buf["status"])
         ep.ep_combine(shape, y, idx, wts, buf["expert_slot"], buf["combined_x"], buf["status"])
 
     def load(seed):
