@@ -822,7 +822,10 @@ def summarize_profiles(out_dir):
                                w.use_fp8)
         # (kernel, grid kind, entry point, summary name); the pack is the FP8
         # instantiation of pack_kernel on dense rows
-        for kname, kind, phase, short in (("combine_kernel", "combine", "combine", "combine"),
+        # the prefill combine runs the multi-item kernel (more items than one
+        # round of resident waves covers), the decode combine the one-item one
+        for kname, kind, phase, short in (("combine_multi_kernel", "any", "combine", "combine"),
+                                          ("combine_kernel", "combine", "combine", "combine"),
                                           ("pack_kernel", "pack", "dispatch", "pack_fp8"),
                                           ("layout_assign_kernel", "layout_assign", "layout",
                                            "layout_assign"),
@@ -830,7 +833,13 @@ def summarize_profiles(out_dir):
                                            "layout_count"),
                                           ("layout_pack_small_kernel", "fused", "layout_dispatch",
                                            "layout_pack_small")):
-            grid = str(_grid_threads(w.num_tokens, w.hidden, kind))
+            grid = None if kind == "any" else str(_grid_threads(w.num_tokens, w.hidden, kind))
+            if grid is None:  # the workload's launches of this kernel, whatever their grid
+                mine = [r for r in trace if r["Kernel_Name"] == kname]
+                grids = {r["Grid_Size_X"] for r in mine}
+                if wid != 3 or len(grids) != 1:
+                    continue
+                grid = grids.pop()
             durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
                     if r["Kernel_Name"] == kname and r["Grid_Size_X"] == grid]
             if not durs:
@@ -922,7 +931,7 @@ def summarize_layout_profiles(out_dir):
     for kname, entry, short in (("pack_normal_kernel", "dispatch_normal", "pack_normal"),
                                 ("combine_normal_kernel", "combine_normal", "combine_normal"),
                                 ("pack_kernel", "dispatch_expand", "pack_expand"),
-                                ("combine_kernel", "combine_expand", "combine_expand")):
+                                ("combine_multi_kernel", "combine_expand", "combine_expand")):
         # a dispatch right after another kernel (the eviction, or the layout
         # in a step) ran cold; one right after itself ran back to back
         cold, b2b = [], []
@@ -1051,7 +1060,7 @@ def main():
     digest = kernel_source_digest()
     roofline = {
         "bound": "hbm",
-        "kernel": "combine_kernel (ep_combine)",
+        "kernel": "combine_multi_kernel (ep_combine; 14 items per wave at this size)",
         "achieved": round(prefill["bytes"]["combine"] / (comb_us * 1e-6) / 1e9, 1),
         "peak": PEAK_HBM_GBPS,
         "unit": "GB/s",
