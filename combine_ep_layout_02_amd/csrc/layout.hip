@@ -246,6 +246,31 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
         s_wb[i] = 0; // row 0: the earlier blocks' counts
     if (tid < 8)
         s_misc[tid] = 0;
+    const bool vec_rows = (R & 3) == 0 && (reinterpret_cast<uintptr_t>(rank_slot) & 15) == 0 &&
+                          (reinterpret_cast<uintptr_t>(is_token_in_rank) & 3) == 0;
+    if (R > kBallotRanks) {
+        // many ranks: the block's rank rows as "not sent", written by the
+        // whole block in address order; each token's own ranks are written
+        // over them after the barriers below, which order the two writes
+        const int64_t t0 = (int64_t)b * kThreads;
+        const int64_t rows = min((int64_t)N - t0, (int64_t)kThreads);
+        if (rows > 0) {
+            const int64_t n = rows * R; // entries in the block's span
+            int32_t *rs_span = rank_slot + t0 * R;
+            uint8_t *mask_span = is_token_in_rank + t0 * R;
+            if (vec_rows) {
+                for (int64_t i = tid; i < n / 4; i += kThreads) {
+                    reinterpret_cast<int4 *>(rs_span)[i] = make_int4(-1, -1, -1, -1);
+                    reinterpret_cast<uint32_t *>(mask_span)[i] = 0u;
+                }
+            } else {
+                for (int64_t i = tid; i < n; i += kThreads) {
+                    rs_span[i] = -1;
+                    mask_span[i] = 0;
+                }
+            }
+        }
+    }
 
     // 2. within-token occurrence index of each entry's expert, and rank set
     const uint32_t magic = rank_magic(L);
@@ -346,24 +371,10 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
         for (int r = 0; r < kBallotRanks; ++r)
             rs[r] = (r < R && ((ranks >> r) & 1ull)) ? my_base[E + r] + __popcll(my_words[E + r] & below) : -1;
     }
-    const bool vec_rows = (R & 3) == 0 && (reinterpret_cast<uintptr_t>(rank_slot) & 15) == 0 &&
-                          (reinterpret_cast<uintptr_t>(is_token_in_rank) & 3) == 0;
     if (live && R > kBallotRanks) {
-        // many ranks: the row as "not sent" first, then the token's own ranks
-        // (the same thread's stores to one address land in program order)
+        // many ranks: the token's own ranks, over the block's fill
         uint8_t *mask_out = is_token_in_rank + t * R;
         int32_t *rslot_out = rank_slot + t * R;
-        if (vec_rows) {
-            for (int r0 = 0; r0 < R; r0 += 4) {
-                *reinterpret_cast<int4 *>(rslot_out + r0) = make_int4(-1, -1, -1, -1);
-                *reinterpret_cast<uint32_t *>(mask_out + r0) = 0u;
-            }
-        } else {
-            for (int r = 0; r < R; ++r) {
-                rslot_out[r] = -1;
-                mask_out[r] = 0;
-            }
-        }
         for (uint64_t m = ranks; m; m &= m - 1) {
             const int r = __builtin_ctzll(m);
             rslot_out[r] = my_base[E + r] + __popcll(my_words[E + r] & below);
