@@ -12,16 +12,14 @@
 // load instruction reads 64 consecutive scores, and the index order of the
 // experts is the order of (i, lane)).  Scores become order-preserving 32-bit
 // keys (after adding +0, so -0 and +0 compare equal, as floats do).  The group
-// maxima are LDS atomicMax on the keys.  Selection moves no data between
-// lanes, only ballots counted on the scalar unit:
+// maxima are LDS atomicMax on the keys.  Selection moves no data through
+// memory:
 //   groups:  group g's rank is the number of groups whose (key, lower index)
 //            beats it (G readlanes); the TG lowest ranks are kept;
-//   experts: a 32-step radix select finds T, the K-th largest candidate key
-//            counted with multiplicity (keep a bit when at least K candidates
-//            are >= the trial value).  The candidates above T are picked, and
-//            the remaining picks are the lowest-index candidates equal to T.
-//            A pick's position is the number of candidates above its key
-//            plus the number of equal keys at lower indices.
+//   experts: K rounds, each taking the largest remaining candidate key (a
+//            register-only wave maximum: DPP inside rows of 16 lanes, then the
+//            four row maxima by readlane) at the lowest expert index holding
+//            it (one ballot per key slot), which lane k keeps for pick k.
 // All decisions are exact comparisons of the inputs, so they match the CPU
 // definition bit for bit; only the weights involve rounding (expf and one
 // division per pick).
@@ -47,15 +45,25 @@ __device__ __forceinline__ float key_value(uint32_t k)
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// Number of candidate keys of the wave that are >= t.
-template <int V>
-__device__ __forceinline__ int count_at_least(const uint32_t (&c)[V], uint32_t t)
+// Maximum of v over the wave: DPP moves inside each row of 16 lanes (swap
+// neighbours, swap pairs, rotate by 4, rotate by 8 -- after which every lane
+// of a row holds the row's maximum), then the four row maxima by readlane.
+// Register-only: no LDS traffic.
+__device__ __forceinline__ uint32_t wave_max(uint32_t v)
 {
-    int n = 0;
-#pragma unroll
-    for (int i = 0; i < V; ++i)
-        n += __popcll(__ballot(c[i] >= t));
-    return n;
+    constexpr int kQuadSwap1 = 0xB1; // quad_perm [1, 0, 3, 2]
+    constexpr int kQuadSwap2 = 0x4E; // quad_perm [2, 3, 0, 1]
+    constexpr int kRowRor4 = 0x124;  // row_ror:4
+    constexpr int kRowRor8 = 0x128;  // row_ror:8
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kQuadSwap1, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kQuadSwap2, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kRowRor4, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kRowRor8, 0xF, 0xF, false));
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(r0, r1), max(r2, r3));
 }
 
 template <int V>
@@ -106,47 +114,33 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(int32_t N, int32_t E, in
 #pragma unroll
     for (int i = 0; i < V; ++i)
         c[i] = (valid[i] && ((kept >> grp[i]) & 1u)) ? key[i] : 0u;
-    // T = the K-th largest candidate key (the host ensures K candidates exist)
-    uint32_t T = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t trial = T | (1u << bit);
-        if (count_at_least<V>(c, trial) >= K)
-            T = trial;
-    }
-    // picks: every candidate above T, then the lowest-index ones equal to T
-    int need = K - count_at_least<V>(c, T + 1); // >= 1
-    uint64_t pick[V];
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-        pick[i] = __ballot(c[i] > T);
-        uint64_t eq = __ballot(c[i] == T);
-        while (eq && need > 0) {
-            pick[i] |= eq & (~eq + 1); // lowest remaining lane
-            eq &= eq - 1;
-            --need;
-        }
-    }
-    // each pick at its position; lane k keeps pick k
+    // K rounds: the largest remaining candidate key, the lowest expert index
+    // holding it (index order is (i, lane)), taken out; lane k keeps pick k.
+    // Equal keys therefore go out in index order, as the definition wants.
     int64_t my_idx = -1;
     float my_score = 0.0f;
+    for (int k = 0; k < K; ++k) {
+        uint32_t m = c[0];
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-        uint64_t p = pick[i];
-        while (p) {
-            const int l = __builtin_ctzll(p);
-            p &= p - 1;
-            const uint32_t ck = (uint32_t)__builtin_amdgcn_readlane((int)c[i], l);
-            int pos = 0;
+        for (int i = 1; i < V; ++i)
+            m = max(m, c[i]);
+        const uint32_t top = wave_max(m);
+        int pick_i = 0, pick_l = 0;
 #pragma unroll
-            for (int i2 = 0; i2 < V; ++i2) {
-                pos += __popcll(__ballot(c[i2] > ck));
-                const uint64_t eq = __ballot(c[i2] == ck);
-                pos += i2 < i ? __popcll(eq) : i2 == i ? __popcll(eq & ((1ull << l) - 1)) : 0;
+        for (int i = V - 1; i >= 0; --i) {
+            const uint64_t b = __ballot(c[i] == top);
+            if (b) {
+                pick_i = i;
+                pick_l = __builtin_ctzll(b);
             }
-            if (lane == pos) {
-                my_idx = (int64_t)(i * 64 + l);
-                my_score = key_value(ck);
-            }
+        }
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+            if (i == pick_i && lane == pick_l)
+                c[i] = 0u;
+        if (lane == k) {
+            my_idx = (int64_t)(pick_i * 64 + pick_l);
+            my_score = key_value(top);
         }
     }
 
