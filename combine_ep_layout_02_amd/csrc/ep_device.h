@@ -82,7 +82,10 @@ __device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.
 // with m = ceil(2^21 / L) the error of e * m / 2^21 against e / L is below
 // e * L / (L * 2^21) < 1 / L, too small to cross the next multiple of 1 / L.
 __device__ __forceinline__ uint32_t rank_magic(int32_t L) { return ((1u << 21) + L - 1) / L; }
-__device__ __forceinline__ int rank_of(int32_t e, uint32_t magic) { return (int)(((uint32_t)e * magic) >> 21); }
+__device__ __forceinline__ int rank_of(int32_t e, uint32_t magic)
+{
+    return (int)(((uint32_t)e * magic) >> 21);
+}
 
 // Token t's K expert ids into e[0..KMAX): ids outside [0, E) become -1 (and
 // set `bad` unless they are -1); k >= K or a token past N gives -1.

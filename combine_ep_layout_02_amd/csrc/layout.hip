@@ -369,7 +369,9 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
     if (R <= kBallotRanks) {
 #pragma unroll
         for (int r = 0; r < kBallotRanks; ++r)
-            rs[r] = (r < R && ((ranks >> r) & 1ull)) ? my_base[E + r] + __popcll(my_words[E + r] & below) : -1;
+            rs[r] = (r < R && ((ranks >> r) & 1ull))
+                        ? my_base[E + r] + __popcll(my_words[E + r] & below)
+                        : -1;
     }
     if (live && R > kBallotRanks) {
         // many ranks: the token's own ranks, over the block's fill
