@@ -744,20 +744,23 @@ def cpu_baseline(inp, w, reps, say):
                       f"host has {os.cpu_count()} logical CPUs"}
 
 
+# The profiling commands whose outputs the summaries in profiles/ come from.
+# $REPO is the repository root and $OUT the directory a profiling run writes
+# to; `bench.py --summarize-profiles $OUT` reads that directory back.
 PROFILE_COMMANDS = {
     "layouts_trace": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -T -f csv "
-                     "-d $REPO/gpurun_out/prof_layouts -o trace -- python3 $REPO/bench.py "
+                     "-d $OUT/prof_layouts -o trace -- python3 $REPO/bench.py "
                      "--receive-layouts-only --steps 20 --quiet",
     "trace": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -T -f csv "
-             "-d $REPO/gpurun_out/prof_trace -o trace -- python3 $REPO/bench.py --steps 30 "
+             "-d $OUT/prof_trace -o trace -- python3 $REPO/bench.py --steps 30 "
              "--warmup 5 --no-cpu-baseline --no-scale-formats --no-receive-layouts "
              "--no-other-configs --quiet",
     "FETCH_SIZE": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -T -f csv "
-                  "-d $REPO/gpurun_out/prof_FETCH_SIZE -o pmc -- python3 $REPO/bench.py --steps 3 "
+                  "-d $OUT/prof_FETCH_SIZE -o pmc -- python3 $REPO/bench.py --steps 3 "
                   "--warmup 1 --no-cpu-baseline --no-decode --no-scale-formats --no-receive-layouts "
                   "--no-other-configs --quiet",
     "WRITE_SIZE": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -T -f csv "
-                  "-d $REPO/gpurun_out/prof_WRITE_SIZE -o pmc -- python3 $REPO/bench.py --steps 3 "
+                  "-d $OUT/prof_WRITE_SIZE -o pmc -- python3 $REPO/bench.py --steps 3 "
                   "--warmup 1 --no-cpu-baseline --no-decode --no-scale-formats --no-receive-layouts "
                   "--no-other-configs --quiet",
 }
