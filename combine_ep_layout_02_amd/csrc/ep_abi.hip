@@ -70,7 +70,7 @@ const char *ep_strerror(int code)
     case EP_ERR_ALIGN:
         return "EP_ERR_ALIGN: misaligned pointer";
     case EP_ERR_UNSUPPORTED:
-        return "EP_ERR_UNSUPPORTED: size outside this build's limits";
+        return "EP_ERR_UNSUPPORTED: size outside the library's limits";
     case EP_ERR_HIP:
         return "EP_ERR_HIP: kernel launch failed";
     case EP_ERR_WORKSPACE:

@@ -69,7 +69,7 @@ extern "C" {
 #define EP_ERR_CAPACITY 3    /* N > M or S < M: the fixed upper bounds are never grown
                                 ([V1] §6.1 and §8.4; [L14] capacity discussion)       */
 #define EP_ERR_ALIGN 4       /* a pointer is not aligned as required                  */
-#define EP_ERR_UNSUPPORTED 5 /* a size this build does not support (see limits)       */
+#define EP_ERR_UNSUPPORTED 5 /* a size the library does not support (see limits)     */
 #define EP_ERR_HIP 6         /* a HIP launch failed                                   */
 #define EP_ERR_WORKSPACE 7   /* workspace NULL or smaller than ep_query_sizes says    */
 
@@ -77,7 +77,7 @@ extern "C" {
 #define EP_STATUS_BAD_EXPERT_ID 1u
 #define EP_STATUS_BAD_SLOT 2u
 
-/* Limits of this build. */
+/* Limits of the library. */
 #define EP_MAX_EXPERTS 1024 /* E */
 #define EP_MAX_RANKS 64     /* R: a token's rank set is one 64-bit mask          */
 #define EP_MAX_TOPK 32      /* K */
