@@ -775,8 +775,9 @@ def _grid_threads(n, h, kind):
         blocks = max(1, -(-n // 256))
         extra = 1 if kind == "layout_assign" and blocks > 1 else 0
         return (blocks + extra) * 256
-    if kind == "fused":  # one 512-thread block per token plus the totals block
-        return (n + 1) * 512
+    if kind == "fused":  # one block per token plus the totals block: 512 threads up to
+        # 256 tokens, 256 threads above
+        return (n + 1) * (512 if n <= 256 else 256)
     return -(-(n * -(-h // 1024)) // 4) * 256
 
 
@@ -834,8 +835,8 @@ def summarize_profiles(out_dir):
                                            "layout_assign"),
                                           ("layout_count_kernel", "layout_count", "layout",
                                            "layout_count"),
-                                          ("layout_pack_small_kernel", "fused", "layout_dispatch",
-                                           "layout_pack_small")):
+                                          ("layout_pack_kernel", "fused", "layout_dispatch",
+                                           "layout_pack")):
             grid = None if kind == "any" else str(_grid_threads(w.num_tokens, w.hidden, kind))
             if grid is None:  # the workload's launches of this kernel, whatever their grid
                 mine = [r for r in trace if r["Kernel_Name"] == kname]

@@ -82,16 +82,11 @@ struct Fp8Payload {
     uint32_t ue8m0_word;
 };
 
+// Quantise one lane's 16 channels of bf16 (in0, in1) on the FP8 lane map.
 template <int SF>
-__device__ __forceinline__ Fp8Payload quantize_lane(const uint16_t *__restrict__ x_row,
+__device__ __forceinline__ Fp8Payload quantize_regs(const uint4 &in0, const uint4 &in1,
                                                     const Fp8Lane &l, int lane)
 {
-    uint4 in0 = make_uint4(0, 0, 0, 0), in1 = make_uint4(0, 0, 0, 0);
-    if (l.active) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(x_row + l.ch);
-        in0 = load_stream(src);
-        in1 = load_stream(src + 1);
-    }
     const uint32_t w[8] = {in0.x, in0.y, in0.z, in0.w, in1.x, in1.y, in1.z, in1.w};
     float f[16];
 #pragma unroll
@@ -137,6 +132,20 @@ __device__ __forceinline__ Fp8Payload quantize_lane(const uint16_t *__restrict__
     return p;
 }
 
+// Load one lane's bf16 of a (token, chunk) and quantise it.
+template <int SF>
+__device__ __forceinline__ Fp8Payload quantize_lane(const uint16_t *__restrict__ x_row,
+                                                    const Fp8Lane &l, int lane)
+{
+    uint4 in0 = make_uint4(0, 0, 0, 0), in1 = make_uint4(0, 0, 0, 0);
+    if (l.active) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(x_row + l.ch);
+        in0 = load_stream(src);
+        in1 = load_stream(src + 1);
+    }
+    return quantize_regs<SF>(in0, in1, l, lane);
+}
+
 // One lane's share of an FP8 receive row (bytes and scales).
 template <int SF>
 __device__ __forceinline__ void store_fp8(const Fp8Payload &p, const Fp8Lane &l, int lane,
@@ -175,6 +184,30 @@ __device__ __forceinline__ void store_bf16(const uint4 &a0, const uint4 &a1, con
         dst[l.u0] = a0;
     if (l.u1 < l.units)
         dst[l.u1] = a1;
+}
+
+// The raw bf16 of one lane's share of a (token, chunk): the 32 bytes the FP8
+// lane map quantises, or the two 16-byte units of the BF16 lane map.  Lanes
+// past the row end keep their inputs.
+template <bool FP8>
+__device__ __forceinline__ void load_chunk(const uint16_t *__restrict__ x_row, int32_t H,
+                                           int32_t chunk, int lane, uint4 &in0, uint4 &in1)
+{
+    if (FP8) {
+        const Fp8Lane l = fp8_lane(H, chunk, lane);
+        if (l.active) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(x_row + l.ch);
+            in0 = load_stream(src);
+            in1 = load_stream(src + 1);
+        }
+    } else {
+        const Bf16Lane l = bf16_lane(H, chunk, lane);
+        const uint4 *src = reinterpret_cast<const uint4 *>(x_row);
+        if (l.u0 < l.units)
+            in0 = load_stream(src + l.u0);
+        if (l.u1 < l.units)
+            in1 = load_stream(src + l.u1);
+    }
 }
 
 // Expand-layout padding (Ascend deep dive, phase 1: the empty slots of a
@@ -362,23 +395,33 @@ __global__ __launch_bounds__(kThreads) void pack_normal_kernel(
         atomicOr(status, flags);
 }
 
-// Layout and per-expert pack of a small batch in one launch.  Block t < N
-// owns token t.  Its threads first count, in LDS, the expert ids of tokens
-// 0..t-1 (thread i takes token i) and the ranks those tokens go to.  The
-// slot of entry (t, k) -- the number of earlier entries with the same expert
-// in (token, k) order -- is then that count plus the entries of t before k
-// with the same expert, and the token's rank slot at rank r is the number of
-// earlier tokens sent to r.  Wave w packs chunks w, w + 8, ... exactly as
-// pack_kernel does, and wave 0 writes the token's layout rows.  Block N counts
-// every token and writes the totals and the offset scan.  The first chunk's
-// loads are issued together with the id loads, so their latencies overlap.
-// Work per block grows with t, which the host bounds (kFusedMaxTokens).
-constexpr int kFusedThreads = 512;
-constexpr int kFusedWaves = kFusedThreads / 64;
+// Layout and per-expert pack in one launch.  Block t + 1 owns token t.
+// Tokens fall into the layout's count blocks of tpb tokens; when the batch
+// spans more than one, `hist` holds each count block's histogram (experts,
+// then tokens per rank) and is otherwise null.  Block t + 1 counts, in LDS,
+// the expert ids of the tokens of its own count block that precede t (thread
+// i takes the i-th) and the ranks those tokens go to, and adds the earlier
+// count blocks' histograms at the columns it needs: the experts of its own
+// entries and every rank.  The slot of entry (t, k) -- the number of earlier
+// entries with the same expert in (token, k) order -- is then that expert's
+// sum plus the entries of t before k with the same expert, and the token's
+// rank slot at rank r is the number of earlier tokens sent to r.  Wave w
+// packs chunks w, w + W, ... (W waves per block) exactly as pack_kernel does,
+// and wave 0 writes the token's layout rows.  Block 0 writes the totals and
+// the offset scan: the column sums of every histogram, or, with a single
+// count block, its own count of every token; it comes first so that it is
+// not the launch's last block to start.  Each wave's first two chunks of x
+// are loaded together with the ids, so their latencies overlap, and
+// quantised once the slots are known.  Counting work per block is at most
+// tpb - 1 tokens (or N for block 0 without histograms), which the host keeps
+// within one thread per token.
+constexpr int kSmallThreads = 512;   // no histograms: counting up to kFusedMaxTokens tokens
+constexpr int kCountedThreads = 256; // with histograms: count blocks of up to 256 tokens
 
-template <int KMAX, int SF, bool FP8>
-__global__ __launch_bounds__(kFusedThreads) void layout_pack_small_kernel(
+template <int KMAX, int SF, bool FP8, int THREADS>
+__global__ __launch_bounds__(THREADS) void layout_pack_kernel(
     int32_t N, int32_t H, int32_t K, int32_t E, int32_t R, int32_t S, int32_t A, int32_t nchunks,
+    const int32_t *__restrict__ hist, int32_t tpb, int32_t stride,
     const uint16_t *__restrict__ x, const int64_t *__restrict__ topk_idx,
     int32_t *__restrict__ num_tokens_per_rank, int32_t *__restrict__ num_tokens_per_expert,
     uint8_t *__restrict__ is_token_in_rank, int32_t *__restrict__ expert_slot,
@@ -386,47 +429,56 @@ __global__ __launch_bounds__(kFusedThreads) void layout_pack_small_kernel(
     void *__restrict__ recv_x, void *__restrict__ recv_scales, int32_t *__restrict__ recv_src_idx,
     uint32_t *status)
 {
+    constexpr int kWavesPerBlock = THREADS / 64;
+    constexpr int kHistLoads = 4; // histogram values in flight per thread
     __shared__ int32_t s_hist[EP_MAX_EXPERTS + EP_MAX_RANKS]; // experts, then ranks
+    __shared__ int32_t s_base[EP_MAX_TOPK + EP_MAX_RANKS];    // own entries' experts, then ranks
+    __shared__ int32_t s_own[EP_MAX_TOPK];                    // this token's experts (-1: none)
     __shared__ int32_t s_bad;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int t = blockIdx.x; // the token, or N for the totals block
+    const int t = (int)blockIdx.x - 1; // the token, or -1 for the totals block
     const int W = E + R;
     const uint32_t magic = rank_magic(E / R);
+    const bool own = t >= 0;
+    // the tokens this block counts, [c0, c1), and the number of earlier
+    // count blocks whose histograms it adds
+    const int c0 = own && hist ? t / tpb * tpb : 0;
+    const int c1 = own ? t : (hist ? 0 : N);
+    const int nb = hist ? (own ? t / tpb : (N + tpb - 1) / tpb) : 0;
 
-    // 1. loads: ids of token `tid` if it precedes t; this token's entry
-    //    `lane` (every wave); the first chunk of x
+    // 1. loads: ids of the counted token `c0 + tid`; this token's entry
+    //    `lane` (every wave); the raw x of this wave's first two chunks
     int32_t e[KMAX];
     uint32_t bad = 0;
-    load_token<KMAX>(topk_idx, tid, t, K, E, e, bad);
-    const bool own = t < N;
+    load_token<KMAX>(topk_idx, (int64_t)c0 + tid, c1, K, E, e, bad);
     const int64_t id = own ? topk_idx[(size_t)t * K + min(lane, K - 1)] : -1;
-    Fp8Lane fl;
-    Fp8Payload p;
-    Bf16Lane bl;
-    uint4 a0 = make_uint4(0, 0, 0, 0), a1 = make_uint4(0, 0, 0, 0);
     const uint16_t *x_row = x + (size_t)(own ? t : 0) * H;
-    if (own && wave < nchunks) {
-        if (FP8) {
-            fl = fp8_lane(H, wave, lane);
-            p = quantize_lane<SF>(x_row, fl, lane);
-        } else {
-            bl = bf16_lane(H, wave, lane);
-            const uint4 *src = reinterpret_cast<const uint4 *>(x_row);
-            if (bl.u0 < bl.units)
-                a0 = load_stream(src + bl.u0);
-            if (bl.u1 < bl.units)
-                a1 = load_stream(src + bl.u1);
-        }
+    uint4 xr[2][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        xr[c][0] = make_uint4(0, 0, 0, 0);
+        xr[c][1] = make_uint4(0, 0, 0, 0);
+        const int chunk = wave + c * kWavesPerBlock;
+        if (own && chunk < nchunks)
+            load_chunk<FP8>(x_row, H, chunk, lane, xr[c][0], xr[c][1]);
     }
-    for (int i = tid; i < W; i += kFusedThreads)
+    for (int i = tid; i < W; i += THREADS)
         s_hist[i] = 0;
+    for (int i = tid; i < K + R; i += THREADS)
+        s_base[i] = 0;
     if (tid == 0)
         s_bad = 0;
+    // this token's entries: lane k < K of every wave holds entry k
+    const bool in_k = lane < K;
+    const bool routed = in_k && id >= 0 && id < (int64_t)E;
+    const int32_t e32 = routed ? (int32_t)id : -1;
+    if (wave == 0 && in_k)
+        s_own[lane] = e32;
     __syncthreads();
 
-    // 2. counts of the earlier tokens' entries and of their ranks
+    // 2. counts of the counted tokens' entries and of their ranks
     uint64_t ranks = 0;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
@@ -439,12 +491,35 @@ __global__ __launch_bounds__(kFusedThreads) void layout_pack_small_kernel(
         atomicAdd(&s_hist[E + __builtin_ctzll(m)], 1);
     if (bad)
         s_bad = 1;
+    // histogram values: a token's block takes pair i = (count block
+    // i / (K + R), column i % (K + R)), where column k < K is entry k's
+    // expert and the rest are the ranks; the totals block takes every column
+    // of every row
+    const int cols = own ? K + R : W;
+    const int n = nb * cols;
+    for (int i0 = tid; i0 < n; i0 += THREADS * kHistLoads) {
+        int32_t v[kHistLoads];
+        int32_t dst[kHistLoads];
+#pragma unroll
+        for (int u = 0; u < kHistLoads; ++u) {
+            const int i = i0 + u * THREADS;
+            const int blk = i / cols;
+            const int c = i - blk * cols;
+            const int col = !own ? c : c < K ? s_own[min(c, K - 1)] : E + (c - K);
+            dst[u] = i < n && col >= 0 ? c : -1;
+            v[u] = dst[u] >= 0 ? hist[(size_t)blk * stride + col] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kHistLoads; ++u)
+            if (dst[u] >= 0)
+                atomicAdd(own ? &s_base[dst[u]] : &s_hist[dst[u]], v[u]);
+    }
     __syncthreads();
 
     if (!own) {
         // 3a. totals block: counts, then the offset scan on wave 0 (each
         //     lane a run of consecutive experts)
-        for (int i = tid; i < W; i += kFusedThreads) {
+        for (int i = tid; i < W; i += THREADS) {
             if (i < E)
                 num_tokens_per_expert[i] = s_hist[i];
             else
@@ -478,10 +553,7 @@ __global__ __launch_bounds__(kFusedThreads) void layout_pack_small_kernel(
         return;
     }
 
-    // 3b. this token's entries: lane k < K holds entry k
-    const bool in_k = lane < K;
-    const bool routed = in_k && id >= 0 && id < (int64_t)E;
-    const int32_t e32 = routed ? (int32_t)id : -1;
+    // 3b. slots of this token's entries and ranks
     int occ = 0;
     uint64_t tok_ranks = 0;
     for (int k2 = 0; k2 < K; ++k2) {
@@ -490,7 +562,7 @@ __global__ __launch_bounds__(kFusedThreads) void layout_pack_small_kernel(
         if (o >= 0)
             tok_ranks |= 1ull << rank_of(o, magic);
     }
-    const int32_t slot = routed ? s_hist[e32] + occ : -1;
+    const int32_t slot = routed ? s_base[lane] + s_hist[e32] + occ : -1;
     const bool slot_ok = routed && slot < S;
     const int64_t row = slot_ok ? (int64_t)e32 * S + slot : -1;
     uint32_t flags = 0;
@@ -503,27 +575,35 @@ __global__ __launch_bounds__(kFusedThreads) void layout_pack_small_kernel(
             expert_slot[(size_t)t * K + lane] = slot;
         if (lane < R) {
             const bool in = (tok_ranks >> lane) & 1ull;
-            rank_slot[(size_t)t * R + lane] = in ? s_hist[E + lane] : -1;
+            rank_slot[(size_t)t * R + lane] = in ? s_base[K + lane] + s_hist[E + lane] : -1;
             is_token_in_rank[(size_t)t * R + lane] = in ? 1 : 0;
         }
         if (flags && status && lane == 0)
             atomicOr(status, flags);
     }
 
-    // 4. pack: the first chunk's payload is ready; later chunks load theirs
+    // 4. pack: the first two chunks are loaded; later ones load here
     const int32_t r_lo = (int32_t)(uint32_t)(uint64_t)row;
     const int32_t r_hi = (int32_t)(uint32_t)((uint64_t)row >> 32);
-    for (int chunk = wave; chunk < nchunks; chunk += kFusedWaves) {
-        if (chunk != wave) {
-            if (FP8) {
-                fl = fp8_lane(H, chunk, lane);
-                p = quantize_lane<SF>(x_row, fl, lane);
-            } else {
-                bl = bf16_lane(H, chunk, lane);
-                const uint4 *src = reinterpret_cast<const uint4 *>(x_row);
-                a0 = bl.u0 < bl.units ? load_stream(src + bl.u0) : make_uint4(0, 0, 0, 0);
-                a1 = bl.u1 < bl.units ? load_stream(src + bl.u1) : make_uint4(0, 0, 0, 0);
-            }
+    for (int chunk = wave, c = 0; chunk < nchunks; chunk += kWavesPerBlock, ++c) {
+        uint4 in0 = make_uint4(0, 0, 0, 0), in1 = make_uint4(0, 0, 0, 0);
+        if (c == 0) {
+            in0 = xr[0][0];
+            in1 = xr[0][1];
+        } else if (c == 1) {
+            in0 = xr[1][0];
+            in1 = xr[1][1];
+        } else {
+            load_chunk<FP8>(x_row, H, chunk, lane, in0, in1);
+        }
+        Fp8Lane fl;
+        Fp8Payload p;
+        Bf16Lane bl;
+        if (FP8) {
+            fl = fp8_lane(H, chunk, lane);
+            p = quantize_regs<SF>(in0, in1, fl, lane);
+        } else {
+            bl = bf16_lane(H, chunk, lane);
         }
         for (int k2 = 0; k2 < K; ++k2) {
             const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane(r_lo, k2);
@@ -534,7 +614,7 @@ __global__ __launch_bounds__(kFusedThreads) void layout_pack_small_kernel(
             if (FP8)
                 store_fp8<SF>(p, fl, lane, r, H, static_cast<uint8_t *>(recv_x), recv_scales);
             else
-                store_bf16(a0, a1, bl, r, H, static_cast<uint16_t *>(recv_x));
+                store_bf16(in0, in1, bl, r, H, static_cast<uint16_t *>(recv_x));
             if (chunk == 0 && lane == 0)
                 recv_src_idx[r] = (int32_t)t;
         }
@@ -596,41 +676,54 @@ hipError_t launch_dispatch(const ep_shape &s, const uint16_t *x, const int64_t *
                        recv_x, recv_scales, recv_src_idx, status, stream);
 }
 
-bool layout_dispatch_fused(const ep_shape &s) { return s.num_tokens <= kFusedMaxTokens; }
-
-hipError_t launch_layout_dispatch_small(const ep_shape &s, const uint16_t *x,
-                                        const int64_t *topk_idx, int32_t *num_tokens_per_rank,
-                                        int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank,
-                                        int32_t *expert_slot, int32_t *rank_slot,
-                                        int32_t *expert_offset, void *recv_x, void *recv_scales,
-                                        int32_t *recv_src_idx, uint32_t *status,
-                                        hipStream_t stream)
+hipError_t launch_layout_dispatch(const ep_shape &s, const LayoutPlan &plan, const int32_t *hist,
+                                  const uint16_t *x, const int64_t *topk_idx,
+                                  int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+                                  uint8_t *is_token_in_rank, int32_t *expert_slot,
+                                  int32_t *rank_slot, int32_t *expert_offset, void *recv_x,
+                                  void *recv_scales, int32_t *recv_src_idx, uint32_t *status,
+                                  hipStream_t stream)
 {
     const int N = s.num_tokens, H = s.hidden, K = s.num_topk, E = s.num_experts;
     const int R = s.num_ranks, S = s.expert_capacity, A = expert_alignment(s);
     const int nchunks = (H + kChunk - 1) / kChunk;
+    const int tpb = plan.tokens_per_block, stride = plan.hist_stride;
+    // One counting thread per token: without histograms a 512-thread block
+    // (8 waves, all chunks of a 7,168-wide row at once) counts up to every
+    // token; with them a 256-thread block (twice the blocks per CU) counts
+    // the earlier tokens of one count block.
+    if (hist ? tpb > kCountedThreads || N > kFusedCountedMaxTokens : N > kFusedMaxTokens)
+        return hipErrorInvalidValue;
     const dim3 grid((unsigned)(N + 1));
-#define EP_FUSED(KMAX, SF, FP8)                                                                    \
-    hipLaunchKernelGGL((layout_pack_small_kernel<KMAX, SF, FP8>), grid, dim3(kFusedThreads), 0,    \
-                       stream, N, H, K, E, R, S, A, nchunks, x, topk_idx, num_tokens_per_rank,     \
+#define EP_FUSED(KMAX, SF, FP8, T)                                                                 \
+    hipLaunchKernelGGL((layout_pack_kernel<KMAX, SF, FP8, T>), grid, dim3(T), 0, stream, N, H, K, \
+                       E, R, S, A, nchunks, hist, tpb, stride, x, topk_idx, num_tokens_per_rank,   \
                        num_tokens_per_expert, is_token_in_rank, expert_slot, rank_slot,            \
                        expert_offset, recv_x, recv_scales, recv_src_idx, status)
+#define EP_FUSED_T(KMAX, SF, FP8)                                                                  \
+    do {                                                                                           \
+        if (hist)                                                                                  \
+            EP_FUSED(KMAX, SF, FP8, kCountedThreads);                                              \
+        else                                                                                       \
+            EP_FUSED(KMAX, SF, FP8, kSmallThreads);                                                \
+    } while (0)
 #define EP_FUSED_SF(KMAX)                                                                          \
     do {                                                                                           \
         if (!s.use_fp8)                                                                            \
-            EP_FUSED(KMAX, EP_SCALE_FP32, false);                                                  \
+            EP_FUSED_T(KMAX, EP_SCALE_FP32, false);                                                \
         else if (s.scale_format == EP_SCALE_POW2)                                                  \
-            EP_FUSED(KMAX, EP_SCALE_POW2, true);                                                   \
+            EP_FUSED_T(KMAX, EP_SCALE_POW2, true);                                                 \
         else if (s.scale_format == EP_SCALE_UE8M0)                                                 \
-            EP_FUSED(KMAX, EP_SCALE_UE8M0, true);                                                  \
+            EP_FUSED_T(KMAX, EP_SCALE_UE8M0, true);                                                \
         else                                                                                       \
-            EP_FUSED(KMAX, EP_SCALE_FP32, true);                                                   \
+            EP_FUSED_T(KMAX, EP_SCALE_FP32, true);                                                 \
     } while (0)
     if (K <= 8)
         EP_FUSED_SF(8);
     else
         EP_FUSED_SF(EP_MAX_TOPK);
 #undef EP_FUSED_SF
+#undef EP_FUSED_T
 #undef EP_FUSED
     return hipGetLastError();
 }

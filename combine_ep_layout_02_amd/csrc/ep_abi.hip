@@ -200,8 +200,7 @@ int ep_layout_dispatch(const ep_shape *s, const int64_t *topk_idx, const uint16_
         return EP_ERR_ALIGN;
     ep::LayoutPlan plan;
     ep::plan_layout(*s, &plan);
-    const bool fused = ep::layout_dispatch_fused(*s);
-    if (!fused && plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+    if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
         return EP_ERR_WORKSPACE;
     if (has_tokens) {
         if (!x || !recv_x || !recv_src_idx)
@@ -213,16 +212,27 @@ int ep_layout_dispatch(const ep_shape *s, const int64_t *topk_idx, const uint16_
             return EP_ERR_ALIGN;
     }
     const hipStream_t st = static_cast<hipStream_t>(stream);
+    // up to 256 tokens one kernel; up to 1,024 the layout's count kernel and
+    // then one kernel for the rest; above that the layout and the pack
+    const int N = s->num_tokens;
+    int32_t *ws = static_cast<int32_t *>(workspace);
     hipError_t err;
-    if (fused) {
-        err = ep::launch_layout_dispatch_small(*s, x, topk_idx, num_tokens_per_rank,
-                                               num_tokens_per_expert, is_token_in_rank, expert_slot,
-                                               rank_slot, expert_offset, recv_x, recv_scales,
-                                               recv_src_idx, status, st);
+    if (N <= ep::kFusedMaxTokens) {
+        err = ep::launch_layout_dispatch(*s, plan, nullptr, x, topk_idx, num_tokens_per_rank,
+                                         num_tokens_per_expert, is_token_in_rank, expert_slot,
+                                         rank_slot, expert_offset, recv_x, recv_scales,
+                                         recv_src_idx, status, st);
+    } else if (N <= ep::kFusedCountedMaxTokens) {
+        err = ep::launch_layout_count(*s, plan, topk_idx, ws, st);
+        if (err == hipSuccess)
+            err = ep::launch_layout_dispatch(*s, plan, ws, x, topk_idx, num_tokens_per_rank,
+                                             num_tokens_per_expert, is_token_in_rank, expert_slot,
+                                             rank_slot, expert_offset, recv_x, recv_scales,
+                                             recv_src_idx, status, st);
     } else {
         err = ep::launch_layout(*s, plan, topk_idx, num_tokens_per_rank, num_tokens_per_expert,
-                                is_token_in_rank, expert_slot, rank_slot, expert_offset,
-                                static_cast<int32_t *>(workspace), status, st);
+                                is_token_in_rank, expert_slot, rank_slot, expert_offset, ws, status,
+                                st);
         if (err == hipSuccess)
             err = ep::launch_dispatch(*s, x, topk_idx, expert_slot, recv_x, recv_scales,
                                       recv_src_idx, status, st);

@@ -52,17 +52,27 @@ hipError_t launch_dispatch(const ep_shape &s, const uint16_t *x, const int64_t *
                            const int32_t *expert_slot, void *recv_x, void *recv_scales,
                            int32_t *recv_src_idx, uint32_t *status, hipStream_t stream);
 
-// Layout and per-expert pack in one launch, for at most kFusedMaxTokens
-// tokens: the same outputs as launch_layout followed by launch_dispatch.
+// The layout's first kernel alone: one histogram row per count block into
+// `workspace` (nothing when plan.num_blocks == 1).
+hipError_t launch_layout_count(const ep_shape &s, const LayoutPlan &plan, const int64_t *topk_idx,
+                               int32_t *workspace, hipStream_t stream);
+
+// Layout and per-expert pack in one launch: the same outputs as
+// launch_layout followed by launch_dispatch.  Up to kFusedMaxTokens tokens
+// (one count block) it is the only launch and `hist` is null; up to
+// kFusedCountedMaxTokens it follows launch_layout_count, with `hist` = that
+// workspace.  Larger batches take launch_layout and launch_dispatch, which
+// measured faster there: the fused blocks' counting then costs more than the
+// layout's second kernel.
 constexpr int kFusedMaxTokens = 256;
-bool layout_dispatch_fused(const ep_shape &s);
-hipError_t launch_layout_dispatch_small(const ep_shape &s, const uint16_t *x,
-                                        const int64_t *topk_idx, int32_t *num_tokens_per_rank,
-                                        int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank,
-                                        int32_t *expert_slot, int32_t *rank_slot,
-                                        int32_t *expert_offset, void *recv_x, void *recv_scales,
-                                        int32_t *recv_src_idx, uint32_t *status,
-                                        hipStream_t stream);
+constexpr int kFusedCountedMaxTokens = 1024;
+hipError_t launch_layout_dispatch(const ep_shape &s, const LayoutPlan &plan, const int32_t *hist,
+                                  const uint16_t *x, const int64_t *topk_idx,
+                                  int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+                                  uint8_t *is_token_in_rank, int32_t *expert_slot,
+                                  int32_t *rank_slot, int32_t *expert_offset, void *recv_x,
+                                  void *recv_scales, int32_t *recv_src_idx, uint32_t *status,
+                                  hipStream_t stream);
 
 hipError_t launch_dispatch_expand(const ep_shape &s, const uint16_t *x, const int64_t *topk_idx,
                                   const int32_t *expert_slot, const int32_t *expert_offset,

@@ -508,4 +508,21 @@ hipError_t launch_layout(const ep_shape &s, const LayoutPlan &plan, const int64_
     return hipGetLastError();
 }
 
+hipError_t launch_layout_count(const ep_shape &s, const LayoutPlan &plan, const int64_t *topk_idx,
+                               int32_t *workspace, hipStream_t stream)
+{
+    const int N = s.num_tokens, K = s.num_topk, E = s.num_experts, R = s.num_ranks;
+    const int B = plan.num_blocks;
+    if (B <= 1)
+        return hipSuccess;
+    const size_t count_lds = sizeof(int32_t) * (size_t)(E + R);
+    if (K <= 8)
+        hipLaunchKernelGGL(layout_count_kernel<8>, dim3(B), dim3(kThreads), count_lds, stream, N, K,
+                           E, R, E / R, plan.hist_stride, topk_idx, workspace);
+    else
+        hipLaunchKernelGGL(layout_count_kernel<EP_MAX_TOPK>, dim3(B), dim3(kThreads), count_lds,
+                           stream, N, K, E, R, E / R, plan.hist_stride, topk_idx, workspace);
+    return hipGetLastError();
+}
+
 } // namespace ep

@@ -217,9 +217,12 @@ int ep_dispatch(const ep_shape *shape, const uint16_t *x, const int64_t *topk_id
  *
  * Up to 256 tokens it is one launch: each token's block counts the expert
  * ids of the tokens before it and derives the token's slots from those
- * counts, so the pack needs no separate layout pass.  Above 256 tokens it
- * runs the two ordinary launches, which need the workspace (the layout's;
- * NULL with workspace_bytes 0 is allowed up to 256 tokens). */
+ * counts, so the pack needs no separate layout pass.  From 257 to 1,024
+ * tokens the layout's per-block histogram kernel runs first, and each
+ * token's block adds the histograms of the blocks before its own to its
+ * count of the earlier tokens of its block.  Above 1,024 tokens it runs the
+ * two ordinary launches.  Above 256 tokens the layout's workspace is needed
+ * (NULL with workspace_bytes 0 is allowed up to 256 tokens). */
 int ep_layout_dispatch(const ep_shape *shape, const int64_t *topk_idx, const uint16_t *x,
                        int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
                        uint8_t *is_token_in_rank, int32_t *expert_slot, int32_t *rank_slot,

@@ -4,8 +4,10 @@ against the CPU oracle's layout and pack.
 Bar: the same as ep_layout and ep_dispatch separately -- every layout output,
 FP8 byte, scale, BF16 row and recv_src_idx bit-exact, rows past each expert's
 count still poisoned, and the status word equal to the oracle's layout and
-pack bits together.  Up to 256 tokens the call is one fused launch; above it,
-the ordinary two launches (one case checks that side of the boundary too)."""
+pack bits together.  Up to 256 tokens the call is one fused launch; up to
+1,024 the layout's count kernel and one fused launch that adds the earlier
+count blocks' histograms; above that the ordinary layout and pack.  The cases
+step across both boundaries."""
 import numpy as np
 import pytest
 import torch
@@ -22,7 +24,6 @@ pytestmark = pytest.mark.gpu
 
 LAYOUT_KEYS = ("num_tokens_per_rank", "num_tokens_per_expert", "is_token_in_rank", "expert_slot",
                "rank_slot", "expert_offset")
-FUSED_MAX_TOKENS = 256  # one launch up to here (include/ep.h)
 
 
 @pytest.fixture(scope="module")
@@ -129,6 +130,16 @@ def test_fused_decode_full_size(o, fmt):
     check_fused(o, ep.shape_of(w, fmt), inp["x_bits"], inp["topk_idx"], f"full {w.name}")
 
 
+@pytest.mark.parametrize("fmt", [ep.EP_SCALE_FP32, ep.EP_SCALE_POW2, ep.EP_SCALE_UE8M0],
+                         ids=["fp32", "pow2", "ue8m0"])
+def test_fused_prefill_1024_tokens(o, fmt):
+    """The prefill routing (group-limited top-8 of 256 experts, 8 ranks) at
+    1,024 tokens x 7,168, the largest batch of the count-kernel form."""
+    w = W.WORKLOADS[3].scaled(1024, 7168)
+    inp = W.make_inputs(w)
+    check_fused(o, ep.shape_of(w, fmt), inp["x_bits"], inp["topk_idx"], f"prefill {w.name}")
+
+
 EDGE = [
     # name, N, H, K, E, R, fp8, extra
     ("N=0", 0, 256, 4, 16, 4, True, {}),
@@ -137,8 +148,15 @@ EDGE = [
     ("R=1", 200, 128, 4, 16, 1, True, {}),
     ("R=E=64 masked", 250, 256, 6, 64, 64, True, dict(mask=0.2)),
     ("odd K=5 bf16 H=520", 256, 520, 5, 32, 8, False, dict(mask=0.05)),
-    ("N=256 (largest fused)", 256, 1152, 8, 256, 8, True, {}),
-    ("N=257 (two launches)", 257, 1152, 8, 256, 8, True, {}),
+    ("N=256 (largest single launch)", 256, 1152, 8, 256, 8, True, {}),
+    ("N=257 (count kernel + fused)", 257, 1152, 8, 256, 8, True, {}),
+    ("N=513 R=1", 513, 128, 4, 16, 1, True, {}),
+    ("N=600 R=E=64 masked", 600, 256, 6, 64, 64, True, dict(mask=0.2)),
+    ("N=700 K=32 E=1024 R=64", 700, 128, 32, 1024, 64, False, dict(mask=0.1)),
+    ("N=800 H=9216: three chunks per wave", 800, 9216, 8, 64, 8, True, {}),
+    ("N=900 repeats K=12 E=8", 900, 128, 12, 8, 4, True, dict(repeats=True)),
+    ("N=1024 odd K=5 bf16 H=520", 1024, 520, 5, 32, 8, False, dict(mask=0.05)),
+    ("N=1025 (layout and pack)", 1025, 1152, 8, 256, 8, True, {}),
     ("K=32 E=1024 R=64", 150, 128, 32, 1024, 64, False, dict(mask=0.1)),
     ("repeats K=12 E=8", 200, 128, 12, 8, 4, True, dict(repeats=True)),
     ("H=9216: more chunks than waves", 60, 9216, 8, 64, 8, True, {}),
@@ -154,24 +172,28 @@ def test_fused_edge_shapes(o, name, N, H, K, E, R, fp8, extra):
     check_fused(o, shape, x, idx, name)
 
 
-def test_fused_capacity_overflow_and_bad_ids(o):
+@pytest.mark.parametrize("N", [200, 600])
+def test_fused_capacity_overflow_and_bad_ids(o, N):
     """Entries past the capacity are skipped and reported; ids outside
-    [-1, E) are masked and reported; both as the separate calls do."""
-    N, H, K, E, R = 200, 256, 12, 8, 4
+    [-1, E) are masked and reported; both as the separate calls do (one
+    launch at 200 tokens, the count-kernel form at 600)."""
+    H, K, E, R = 256, 12, 8, 4
     x, idx = _random(N, H, K, E, R, seed=9, repeats=True)
     check_fused(o, ep.make_shape(N, H, K, E, R, N, N, True), x, idx, "capacity overflow")
     rng = np.random.default_rng(5)
-    x, idx = _random(180, 256, 4, 32, 4, seed=5)
+    n = N - 20
+    x, idx = _random(n, 256, 4, 32, 4, seed=5)
     pos = rng.permutation(idx.size)[:41]
     idx.reshape(-1)[pos] = rng.choice([-7, -2, 32, 132, 1 << 40], size=41)
-    check_fused(o, ep.make_shape(180, 256, 4, 32, 4, 180, 180, True), x, idx, "bad ids")
+    check_fused(o, ep.make_shape(n, 256, 4, 32, 4, n, n, True), x, idx, "bad ids")
 
 
-def test_fused_ids_on_an_8_byte_boundary(o):
+@pytest.mark.parametrize("N", [100, 400])
+def test_fused_ids_on_an_8_byte_boundary(o, N):
     """topk_idx at a base that is 8- but not 16-byte aligned: the kernel
     reads ids one at a time instead of two per load."""
-    x, idx = _random(100, 256, 8, 64, 8, seed=3)
-    check_fused(o, ep.make_shape(100, 256, 8, 64, 8, 100, 100, True), x, idx, "ids at +8 bytes",
+    x, idx = _random(N, 256, 8, 64, 8, seed=3)
+    check_fused(o, ep.make_shape(N, 256, 8, 64, 8, N, N, True), x, idx, "ids at +8 bytes",
                 topk_offset=1)
 
 
