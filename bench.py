@@ -555,6 +555,49 @@ def time_config(wid, steps, warmup, scrub_bytes, say):
             "bar_60pct_us": round(nb / (0.6 * PEAK_HBM_GBPS * 1e9) * 1e6, 1)}
 
 
+def time_copy_ceiling(steps, say):
+    """A plain device-to-device copy of 2 GiB (torch copy_, which the runtime
+    runs as its own copy kernel): the rate a streaming half-read, half-write
+    pattern reaches on this GPU, as context for the step's GB/s.  The buffers
+    are far larger than the 256 MB Infinity Cache, so no eviction is needed."""
+    import torch
+
+    n = 1 << 31
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    say(f"plain copy of {n >> 20} MiB, {steps} times")
+    for _ in range(2):
+        dst.copy_(src)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in evs:  # handles are created at the first record, outside the timed region
+        e[0].record(stream)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    for e in evs:
+        e[0].record(stream)
+        dst.copy_(src)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    us = statistics.median([e[0].elapsed_time(e[1]) * 1e3 for e in evs])
+    del src, dst
+    torch.cuda.empty_cache()
+    gbps = 2 * n / (us * 1e-6) / 1e9
+    return {"bytes_read": n, "bytes_written": n, "us_median": round(us, 1),
+            "gbps_read_plus_write": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+
+
+def device_info():
+    """The device and software the figures were measured on."""
+    import torch
+
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""),
+            "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2 ** 30, 1), "hip": torch.version.hip,
+            "torch": torch.__version__}
+
+
 def time_gating(wid, steps, scrub_bytes, say, num_groups=8, topk_groups=4):
     """Group-limited gating on workload ``wid``'s shape (router scores N(0, 1)
     [N, E] fp32): ep_group_limited_topk alone, cold, and the whole step with
@@ -758,11 +801,11 @@ PROFILE_COMMANDS = {
     "FETCH_SIZE": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -T -f csv "
                   "-d $OUT/prof_FETCH_SIZE -o pmc -- python3 $REPO/bench.py --steps 3 "
                   "--warmup 1 --no-cpu-baseline --no-decode --no-scale-formats --no-receive-layouts "
-                  "--no-other-configs --quiet",
+                  "--no-other-configs --no-copy-ceiling --quiet",
     "WRITE_SIZE": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -T -f csv "
                   "-d $OUT/prof_WRITE_SIZE -o pmc -- python3 $REPO/bench.py --steps 3 "
                   "--warmup 1 --no-cpu-baseline --no-decode --no-scale-formats --no-receive-layouts "
-                  "--no-other-configs --quiet",
+                  "--no-other-configs --no-copy-ceiling --quiet",
 }
 
 
@@ -1021,6 +1064,9 @@ def main():
     ap.add_argument("--receive-layouts-only", action="store_true",
                     help="time only the normal-mode and expand paths (a profiling run) and print "
                          "their figures as the JSON line")
+    ap.add_argument("--no-copy-ceiling", action="store_true",
+                    help="skip the 2 GiB plain-copy context figure (counter runs calibrate on "
+                         "the bench's 512 MiB copy and must see no other copy)")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/ summaries from a profiling run's output directory and exit")
@@ -1101,6 +1147,9 @@ def main():
         extra["receive_layouts_4096x7168"] = time_receive_layouts(
             3, min(args.steps, 20), scrub_bytes, say)
         extra["gating_4096x256"] = time_gating(3, min(args.steps, 20), scrub_bytes, say)
+    extra["device"] = device_info()
+    if not args.no_copy_ceiling:
+        extra["copy_2GiB_context"] = time_copy_ceiling(min(args.steps, 20), say)
     if decode is not None:
         extra["decode_128x7168"] = {
             "step_us_cold": decode["cold"], "step_us_cold_hip_graph": decode["graph_cold"],

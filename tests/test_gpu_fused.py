@@ -197,8 +197,11 @@ def test_fused_ids_on_an_8_byte_boundary(o, N):
                 topk_offset=1)
 
 
-def test_fused_matches_separate_calls_and_expand_offsets(o):
-    """With an expert alignment, expert_offset follows it exactly as ep_layout's."""
-    x, idx = _random(120, 256, 8, 64, 8, seed=21, mask=0.1)
-    shape = ep.make_shape(120, 256, 8, 64, 8, 120, 120, True, expert_alignment=128)
+@pytest.mark.parametrize("N", [120, 500])
+def test_fused_matches_separate_calls_and_expand_offsets(o, N):
+    """With an expert alignment, expert_offset follows it exactly as ep_layout's
+    (the totals block counts every token at 120 tokens, sums the count
+    kernel's histograms at 500)."""
+    x, idx = _random(N, 256, 8, 64, 8, seed=21, mask=0.1)
+    shape = ep.make_shape(N, 256, 8, 64, 8, N, N, True, expert_alignment=128)
     check_fused(o, shape, x, idx, "expert alignment 128")
