@@ -200,6 +200,30 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
     cold = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
     say(f"workload {w.name}: cold step times (us): " + " ".join(f"{v:.1f}" for v in cold))
 
+    # The step without the latency an event marker adds before the next
+    # launch: (eviction + step) minus (eviction alone), each between two
+    # events, so both carry one marker.  An untimed eviction first takes the
+    # previous step's dirty lines, so both timed evictions start alike.
+    say(f"workload {w.name}: {steps} pairs of eviction alone and eviction + step")
+    evs = [new_events(4) for _ in range(steps)]
+    for e in evs:
+        evict()
+        e[0].record(stream)
+        evict()
+        e[1].record(stream)
+        e[2].record(stream)
+        evict()
+        layout()
+        dispatch()
+        combine()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    evict_only = statistics.median([e[0].elapsed_time(e[1]) * 1e3 for e in evs])
+    evict_step = statistics.median([e[2].elapsed_time(e[3]) * 1e3 for e in evs])
+    net = {"eviction_us_median": round(evict_only, 2),
+           "eviction_plus_step_us_median": round(evict_step, 2),
+           "step_us": round(evict_step - evict_only, 2)}
+
     say(f"workload {w.name}: {steps} steps with an event between phases")
     evs = [new_events(4) for _ in range(steps)]
     for e in evs:
@@ -312,6 +336,7 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
         "workload": w, "bytes": nbytes, "num_valid": P,
         "cold": stats(cold, nbytes["total"]),
         "graph_cold": stats(graph_cold, nbytes["total"]),
+        "cold_net_of_marker": dict(net, gbps=round(nbytes["total"] / (net["step_us"] * 1e-6) / 1e9, 1)),
         "phases": {k: stats(v, nbytes[k]) for k, v in phases.items()},
         "kernels": {k: stats(v, nbytes[k]) for k, v in kernels.items()},
         "warm_us_per_step": round(warm_us, 2),
@@ -1124,6 +1149,7 @@ def main():
     extra = {
         "step_us_cold": prefill["cold"],
         "step_us_cold_hip_graph": prefill["graph_cold"],
+        "step_cold_net_of_event_marker": prefill["cold_net_of_marker"],
         "phases_us_with_events_between": prefill["phases"],
         "kernel_avg_us_back_to_back": prefill["kernels"],
         "step_us_warm": prefill["warm_us_per_step"],
@@ -1153,6 +1179,7 @@ def main():
     if decode is not None:
         extra["decode_128x7168"] = {
             "step_us_cold": decode["cold"], "step_us_cold_hip_graph": decode["graph_cold"],
+            "step_cold_net_of_event_marker": decode["cold_net_of_marker"],
             "phases_us_with_events_between": decode["phases"],
             "kernel_avg_us_back_to_back": decode["kernels"],
             "step_us_warm": decode["warm_us_per_step"], "bytes_per_step": decode["bytes"],
