@@ -390,14 +390,17 @@ def test_side_stream_and_handle_reuse(o):
     assert torch.equal(d1.recv_x, d2.recv_x) and torch.equal(d1.recv_src_idx, d2.recv_src_idx)
 
 
-@pytest.mark.parametrize("fused", [False, True], ids=["separate", "ep_layout_dispatch"])
-def test_hip_graph_capture_and_replay(o, fused):
+@pytest.mark.parametrize("fused,num_tokens,hidden",
+                         [(False, 128, 7168), (True, 128, 7168), (True, 600, 1024)],
+                         ids=["separate", "ep_layout_dispatch", "ep_layout_dispatch-600-tokens"])
+def test_hip_graph_capture_and_replay(o, fused, num_tokens, hidden):
     """The path is capturable (no allocation, no host sync, no memset): one
     capture of layout + dispatch + combine (the first two as separate calls or
-    as one ep_layout_dispatch), replayed several times with eager work in
-    between and a new routing copied into the captured input, each replay
-    checked against an eager run and the oracle."""
-    w = W.WORKLOADS[2]
+    as one ep_layout_dispatch; at 600 tokens that is the layout's count kernel
+    and one fused kernel), replayed several times with eager work in between
+    and a new routing copied into the captured input, each replay checked
+    against an eager run and the oracle."""
+    w = W.WORKLOADS[2].scaled(num_tokens, hidden)
     shape = ep.shape_of(w)
     dev = torch.device("cuda")
     buf = ep.allocate(shape, dev)
