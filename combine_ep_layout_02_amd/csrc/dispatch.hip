@@ -720,6 +720,8 @@ hipError_t launch_layout_dispatch(const ep_shape &s, const LayoutPlan &plan, con
     } while (0)
     if (K <= 8)
         EP_FUSED_SF(8);
+    else if (K <= 16)
+        EP_FUSED_SF(16);
     else
         EP_FUSED_SF(EP_MAX_TOPK);
 #undef EP_FUSED_SF

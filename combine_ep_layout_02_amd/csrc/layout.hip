@@ -502,6 +502,8 @@ hipError_t launch_layout(const ep_shape &s, const LayoutPlan &plan, const int64_
     } while (0)
     if (K <= 8)
         EP_LAYOUT_LAUNCH(8);
+    else if (K <= 16)
+        EP_LAYOUT_LAUNCH(16);
     else
         EP_LAYOUT_LAUNCH(EP_MAX_TOPK);
 #undef EP_LAYOUT_LAUNCH
@@ -519,6 +521,9 @@ hipError_t launch_layout_count(const ep_shape &s, const LayoutPlan &plan, const 
     if (K <= 8)
         hipLaunchKernelGGL(layout_count_kernel<8>, dim3(B), dim3(kThreads), count_lds, stream, N, K,
                            E, R, E / R, plan.hist_stride, topk_idx, workspace);
+    else if (K <= 16)
+        hipLaunchKernelGGL(layout_count_kernel<16>, dim3(B), dim3(kThreads), count_lds, stream, N,
+                           K, E, R, E / R, plan.hist_stride, topk_idx, workspace);
     else
         hipLaunchKernelGGL(layout_count_kernel<EP_MAX_TOPK>, dim3(B), dim3(kThreads), count_lds,
                            stream, N, K, E, R, E / R, plan.hist_stride, topk_idx, workspace);

@@ -155,6 +155,8 @@ EDGE = [
     ("N=700 K=32 E=1024 R=64", 700, 128, 32, 1024, 64, False, dict(mask=0.1)),
     ("N=800 H=9216: three chunks per wave", 800, 9216, 8, 64, 8, True, {}),
     ("N=900 repeats K=12 E=8", 900, 128, 12, 8, 4, True, dict(repeats=True)),
+    ("N=1000 K=16 E=256 R=32", 1000, 256, 16, 256, 32, True, dict(mask=0.1)),
+    ("N=150 K=10 bf16", 150, 520, 10, 64, 8, False, {}),
     ("N=1024 odd K=5 bf16 H=520", 1024, 520, 5, 32, 8, False, dict(mask=0.05)),
     ("N=1025 (layout and pack)", 1025, 1152, 8, 256, 8, True, {}),
     ("K=32 E=1024 R=64", 150, 128, 32, 1024, 64, False, dict(mask=0.1)),

@@ -281,6 +281,10 @@ EDGE = [
     ("E=1024", dict(N=600, H=128, K=8, E=1024, R=64, use_fp8=True)),
     ("K=32 E=1024 R=64", dict(N=300, H=128, K=32, E=1024, R=64, use_fp8=False, mask=0.1)),
     ("K>E repeats", dict(N=200, H=128, K=12, E=8, R=4, use_fp8=True, S=200 * 12)),
+    # 8 < K <= 16 over several layout blocks (the kernels' 16-entry form)
+    ("K=10 N=1500 bf16", dict(N=1500, H=256, K=10, E=64, R=8, use_fp8=False, mask=0.05)),
+    ("K=16 N=2100 R=32", dict(N=2100, H=128, K=16, E=256, R=32, use_fp8=True)),
+    ("K=12 repeats N=1300", dict(N=1300, H=128, K=12, E=8, R=4, use_fp8=True, S=1300 * 12)),
     # repeated experts push counts past the capacity: those entries are
     # skipped by pack and combine and reported as EP_STATUS_BAD_SLOT
     ("capacity overflow", dict(N=200, H=256, K=12, E=8, R=4, use_fp8=True)),
