@@ -339,6 +339,9 @@ __global__ __launch_bounds__(kThreads) void pack_normal_kernel(
     const uint16_t *x_row = x + (size_t)t * H;
     const int32_t L = E / R;
 
+    // this chunk of x, in flight while the rank-slot row loads
+    uint4 in0 = make_uint4(0, 0, 0, 0), in1 = make_uint4(0, 0, 0, 0);
+    load_chunk<FP8>(x_row, H, chunk, lane, in0, in1);
     uint32_t flags = 0;
     int32_t j;
     uint64_t dest = rank_destinations(rank_slot + (size_t)t * R, R, M, lane, j, flags);
@@ -359,17 +362,12 @@ __global__ __launch_bounds__(kThreads) void pack_normal_kernel(
     Fp8Lane fl;
     Fp8Payload p;
     Bf16Lane bl;
-    uint4 a0 = make_uint4(0, 0, 0, 0), a1 = make_uint4(0, 0, 0, 0);
+    const uint4 a0 = in0, a1 = in1;
     if (FP8) {
         fl = fp8_lane(H, chunk, lane);
-        p = quantize_lane<SF>(x_row, fl, lane);
+        p = quantize_regs<SF>(in0, in1, fl, lane);
     } else {
         bl = bf16_lane(H, chunk, lane);
-        const uint4 *src = reinterpret_cast<const uint4 *>(x_row);
-        if (bl.u0 < bl.units)
-            a0 = load_stream(src + bl.u0);
-        if (bl.u1 < bl.units)
-            a1 = load_stream(src + bl.u1);
     }
 
     while (dest) {
