@@ -29,11 +29,12 @@
 // fixed order, so the fp32 sum is the same chain on every run (deterministic,
 // no atomics).
 //
-// When one round of resident waves would not cover every item (the large
-// batches), the top-k combine instead runs a grid that is resident all at
-// once, 8 or 14 items per wave, and each wave stores its outputs after its
-// last read: HBM loses bandwidth when reads and writes interleave, and this
-// moves the writes into one burst at the end.  Same arithmetic per item.
+// When one round of resident waves would not cover every item but 14 rounds
+// would (K <= 8; e.g. 4,096 tokens of 7,168 channels), the top-k combine
+// instead runs a grid that is resident all at once, 8 or 14 items per wave,
+// and each wave stores its outputs after its last read: HBM loses bandwidth
+// when reads and writes interleave, and this moves the writes towards the
+// end.  Same arithmetic per item.  Larger batches run the one-item kernel.
 #include <atomic>
 
 #include "ep_device.h"
