@@ -1073,7 +1073,7 @@ def summarize_layout_profiles(out_dir):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--scrub-mib", type=int, default=1024)
     ap.add_argument("--cpu-reps", type=int, default=5)
