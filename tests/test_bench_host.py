@@ -80,3 +80,19 @@ def test_more_than_one_gpu_is_refused():
     assert res.returncode != 0
     assert "one GPU" in res.stderr
     assert res.stdout.strip() == ""
+
+
+def test_profile_grid_sizes():
+    """The grid sizes the profile summaries match kernels by: pack and
+    combine one 64-lane wave per (token, 1024-channel chunk) in 256-thread
+    blocks; the layout 256 tokens per block plus the totals block; the fused
+    layout + pack one block per token plus the totals block, 512 threads up
+    to 256 tokens and 256 above."""
+    assert bench._grid_threads(4096, 7168, "pack") == 4096 * 7 * 64
+    assert bench._grid_threads(128, 7168, "combine") == 128 * 7 * 64
+    assert bench._grid_threads(130, 1000, "pack") == -(-130 // 4) * 256
+    assert bench._grid_threads(4096, 7168, "layout_count") == 16 * 256
+    assert bench._grid_threads(4096, 7168, "layout_assign") == 17 * 256
+    assert bench._grid_threads(128, 7168, "layout_assign") == 256
+    assert bench._grid_threads(128, 7168, "fused") == 129 * 512
+    assert bench._grid_threads(600, 7168, "fused") == 601 * 256
