@@ -101,6 +101,7 @@ def check_fused(o, shape, x_bits, topk_idx, name, topk_offset=0):
         assert unwritten_rows_intact(recv_x, counts, int(POISON_X16))
     assert unwritten_rows_intact(recv_src_idx, counts, POISON_SRC)
     assert status_bits(status) == (lay["status"] | st), (name, status_bits(status), lay["status"], st)
+    return status_bits(status)
 
 
 def _random(N, H, K, E, R, seed, mask=0.0, repeats=False):
@@ -188,6 +189,20 @@ def test_fused_capacity_overflow_and_bad_ids(o, N):
     pos = rng.permutation(idx.size)[:41]
     idx.reshape(-1)[pos] = rng.choice([-7, -2, 32, 132, 1 << 40], size=41)
     check_fused(o, ep.make_shape(n, 256, 4, 32, 4, n, n, True), x, idx, "bad ids")
+
+
+@pytest.mark.parametrize("N", [150, 700, 1100])
+def test_fused_both_status_bits_in_one_call(o, N):
+    """Bad ids and entries past the capacity in the same call: both status
+    bits are set, by blocks that may run on different XCDs (one launch at
+    150 tokens, the count-kernel form at 700, layout and pack at 1,100)."""
+    H, K, E, R = 256, 12, 8, 4
+    x, idx = _random(N, H, K, E, R, seed=N, repeats=True)
+    rng = np.random.default_rng(N + 1)
+    pos = rng.permutation(idx.size)[:23]
+    idx.reshape(-1)[pos] = rng.choice([-9, E, E + 7, 1 << 33], size=23)
+    bits = check_fused(o, ep.make_shape(N, H, K, E, R, N, N, True), x, idx, "bad ids and overflow")
+    assert bits & ep.EP_STATUS_BAD_EXPERT_ID and bits & ep.EP_STATUS_BAD_SLOT, bits
 
 
 @pytest.mark.parametrize("N", [100, 400])
