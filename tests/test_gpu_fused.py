@@ -160,6 +160,8 @@ EDGE = [
     ("N=150 K=10 bf16", 150, 520, 10, 64, 8, False, {}),
     ("N=1024 odd K=5 bf16 H=520", 1024, 520, 5, 32, 8, False, dict(mask=0.05)),
     ("N=1025 (layout and pack)", 1025, 1152, 8, 256, 8, True, {}),
+    ("N=600 K=1", 600, 256, 1, 32, 8, True, {}),
+    ("N=300 all masked", 300, 256, 4, 16, 4, True, dict(mask=1.0)),
     ("K=32 E=1024 R=64", 150, 128, 32, 1024, 64, False, dict(mask=0.1)),
     ("repeats K=12 E=8", 200, 128, 12, 8, 4, True, dict(repeats=True)),
     ("H=9216: more chunks than waves", 60, 9216, 8, 64, 8, True, {}),
