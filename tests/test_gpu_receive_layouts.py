@@ -357,3 +357,86 @@ def test_normal_bad_ids_and_slots_are_reported(o):
     r0 = int(np.nonzero(rs[20] >= 0)[0][0])
     rs[20, r0] = N + 5  # >= M
     check_normal(o, shape, inp, "bad ids", rank_slot_override=rs)
+
+
+@pytest.mark.parametrize("mode", ["normal", "expand"])
+def test_receive_layout_step_hip_graph_replay(mode):
+    """The normal-mode and expand steps (layout, dispatch, combine) captured
+    once in a HIP graph and replayed with new routings, inputs and expert
+    outputs copied into the captured buffers, eager work in between; every
+    replay must reproduce an eager run of the same inputs exactly."""
+    base = W.WORKLOADS[2].scaled(300, 1024)
+    shape = ep.shape_of(base, expert_alignment=128 if mode == "expand" else 0)
+    N, H, K, E, R, M = (shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts,
+                        shape.num_ranks, shape.num_max_dispatch_tokens_per_rank)
+    d = torch.device("cuda")
+    buf = ep.allocate(shape, d, parts=("layout", "combine", mode))
+    idx = torch.empty((N, K), dtype=torch.int64, device=d)
+    wts = torch.empty((N, K), dtype=torch.float32, device=d)
+    x = torch.empty((N, H), dtype=torch.int16, device=d)
+    if mode == "normal":
+        y = torch.empty((R, M, H), dtype=torch.int16, device=d)
+        rw = torch.empty((R, M, K), dtype=torch.float32, device=d)
+        keys = ("recv_x_normal", "recv_scales_normal", "recv_topk_idx", "recv_topk_weights",
+                "recv_src_idx_normal", "combined_x", "combined_topk_weights", "rank_slot",
+                "num_tokens_per_rank")
+    else:
+        y = torch.empty((ep.expand_rows(shape), H), dtype=torch.int16, device=d)
+        rw = None
+        keys = ("recv_x_expand", "recv_scales_expand", "recv_src_idx_expand", "combined_x",
+                "expert_slot", "expert_offset", "num_tokens_per_expert")
+
+    def step():
+        ep.ep_layout(shape, idx, buf["num_tokens_per_rank"], buf["num_tokens_per_expert"],
+                     buf["is_token_in_rank"], buf["expert_slot"], buf["rank_slot"],
+                     buf["expert_offset"], buf["workspace"], buf["status"])
+        if mode == "normal":
+            ep.ep_dispatch_normal(shape, x, idx, wts, buf["rank_slot"], buf["recv_x_normal"],
+                                  buf["recv_scales_normal"], buf["recv_topk_idx"],
+                                  buf["recv_topk_weights"], buf["recv_src_idx_normal"], buf["status"])
+            ep.ep_combine_normal(shape, y, buf["rank_slot"], rw, buf["combined_x"],
+                                 buf["combined_topk_weights"], buf["status"])
+        else:
+            ep.ep_dispatch_expand(shape, x, idx, buf["expert_slot"], buf["expert_offset"],
+                                  buf["num_tokens_per_expert"], buf["recv_x_expand"],
+                                  buf["recv_scales_expand"], buf["recv_src_idx_expand"], buf["status"])
+            ep.ep_combine_expand(shape, y, idx, wts, buf["expert_slot"], buf["expert_offset"],
+                                 buf["combined_x"], buf["status"])
+
+    def load(seed):
+        inp = W.make_inputs(base, seed=seed)
+        idx.copy_(torch.from_numpy(inp["topk_idx"]))
+        wts.copy_(torch.from_numpy(inp["topk_weights"]))
+        x.copy_(torch.from_numpy(inp["x_bits"].view(np.int16)))
+        g = torch.Generator(device=d)
+        g.manual_seed(seed)
+        y.copy_(torch.randn(y.shape, dtype=torch.bfloat16, device=d, generator=g).view(torch.int16))
+        if rw is not None:
+            rw.copy_(torch.rand(rw.shape, dtype=torch.float32, device=d, generator=g))
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return {k: buf[k].view(torch.uint8).cpu().numpy().copy() for k in keys if buf[k] is not None}
+
+    load(3)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep, seed in enumerate((5, 5, 6, 7)):
+        say(f"{mode} graph replay {rep} (seed {seed})")
+        load(seed)
+        torch.cuda.synchronize()
+        step()  # eager reference on the same inputs
+        eager = snapshot()
+        buf["combined_x"].fill_(-1)  # ordinary eager work between replays
+        buf["num_tokens_per_rank" if mode == "normal" else "num_tokens_per_expert"].fill_(-1)
+        graph.replay()
+        replay = snapshot()
+        for k in eager:
+            assert np.array_equal(eager[k], replay[k]), (mode, rep, k)
+    assert int(buf["status"].item()) == 0
