@@ -104,3 +104,71 @@ def test_gating_feeds_the_layout(o):
         assert np.array_equal(lay[key], ref[key]), key
     # at most TG ranks per token (groups are the ranks here)
     assert lay["is_token_in_rank"].sum(axis=1).max() <= TG
+
+
+def test_gated_step_hip_graph_replay(o):
+    """Gating, then layout + pack in one call (the count-kernel form at 600
+    tokens), then the combine, captured once in a HIP graph and replayed with
+    new scores and expert outputs copied in; each replay must reproduce an
+    eager run exactly, and its picks must match the oracle."""
+    N, H, K, E, R, G, TG = 600, 512, 8, 256, 8, 8, 4
+    shape = ep.make_shape(N, H, K, E, R, N, N, True)
+    d = torch.device("cuda")
+    buf = ep.allocate(shape, d)
+    scores = torch.empty((N, E), dtype=torch.float32, device=d)
+    x = torch.empty((N, H), dtype=torch.int16, device=d)
+    idx = torch.empty((N, K), dtype=torch.int64, device=d)
+    wts = torch.empty((N, K), dtype=torch.float32, device=d)
+    y = torch.empty((E, N, H), dtype=torch.int16, device=d)
+    keys = ("recv_x", "recv_scales", "recv_src_idx", "combined_x", "expert_slot", "rank_slot",
+            "num_tokens_per_expert")
+
+    def step():
+        ep.ep_group_limited_topk(shape, G, TG, scores, idx, wts)
+        ep.ep_layout_dispatch(shape, idx, x, buf["num_tokens_per_rank"], buf["num_tokens_per_expert"],
+                              buf["is_token_in_rank"], buf["expert_slot"], buf["rank_slot"],
+                              buf["expert_offset"], buf["workspace"], buf["recv_x"],
+                              buf["recv_scales"], buf["recv_src_idx"], buf["status"])
+        ep.ep_combine(shape, y, idx, wts, buf["expert_slot"], buf["combined_x"], buf["status"])
+
+    def load(seed):
+        rng = np.random.default_rng(seed)
+        sc = rng.standard_normal((N, E), dtype=np.float32)
+        scores.copy_(torch.from_numpy(sc))
+        g = torch.Generator(device=d)
+        g.manual_seed(seed)
+        x.copy_(torch.randn((N, H), dtype=torch.bfloat16, device=d, generator=g).view(torch.int16))
+        y.copy_(torch.randn(y.shape, dtype=torch.bfloat16, device=d, generator=g).view(torch.int16))
+        return sc
+
+    def snapshot():
+        torch.cuda.synchronize()
+        out = {k: buf[k].view(torch.uint8).cpu().numpy().copy() for k in keys}
+        out["idx"] = host(idx)
+        out["wts"] = host(wts).view(np.int32)
+        return out
+
+    load(1)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep, seed in enumerate((2, 2, 3)):
+        say(f"gated step graph replay {rep} (seed {seed})")
+        sc = load(seed)
+        torch.cuda.synchronize()
+        step()
+        eager = snapshot()
+        idx.fill_(-5)
+        buf["combined_x"].fill_(-1)
+        graph.replay()
+        replay = snapshot()
+        for k in eager:
+            assert np.array_equal(eager[k], replay[k]), (rep, k)
+        want_i, _, _ = o.group_limited_topk(sc, G, TG, K)
+        assert np.array_equal(replay["idx"], want_i), rep
+    assert int(buf["status"].item()) == 0
