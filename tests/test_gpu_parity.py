@@ -509,3 +509,68 @@ def test_layout_workspace_reused_across_sizes(o):
         for key in LAYOUT_KEYS:
             assert np.array_equal(got[key], want[key]), (n, key)
         assert int(status.item()) == 0
+
+
+def test_two_streams_and_two_host_threads(o):
+    """Reentrancy: two independent prefill-shaped steps (different routings,
+    inputs and buffers) issued on two streams from two host threads at once
+    give exactly what each gives when run alone."""
+    import threading
+
+    w = W.WORKLOADS[3].scaled(1500, 1024)
+    shape = ep.shape_of(w)
+    d = torch.device("cuda")
+    runs = []
+    for seed in (21, 22):
+        inp = W.make_inputs(w, seed=seed)
+        buf = ep.allocate(shape, d)
+        g = torch.Generator(device=d)
+        g.manual_seed(seed)
+        runs.append({
+            "buf": buf,
+            "idx": torch.from_numpy(inp["topk_idx"]).to(d),
+            "x": torch.from_numpy(inp["x_bits"].view(np.int16)).to(d),
+            "wts": torch.from_numpy(inp["topk_weights"]).to(d),
+            "y": torch.randn((w.num_experts, w.expert_capacity, w.hidden), dtype=torch.bfloat16,
+                             device=d, generator=g).view(torch.int16),
+            "stream": torch.cuda.Stream(),
+        })
+
+    def step(r):
+        b = r["buf"]
+        with torch.cuda.stream(r["stream"]):
+            for _ in range(3):
+                ep.ep_layout(shape, r["idx"], b["num_tokens_per_rank"], b["num_tokens_per_expert"],
+                             b["is_token_in_rank"], b["expert_slot"], b["rank_slot"], b["expert_offset"],
+                             b["workspace"], b["status"])
+                ep.ep_dispatch(shape, r["x"], r["idx"], b["expert_slot"], b["recv_x"], b["recv_scales"],
+                               b["recv_src_idx"], b["status"])
+                ep.ep_combine(shape, r["y"], r["idx"], r["wts"], b["expert_slot"], b["combined_x"],
+                              b["status"])
+
+    keys = ("expert_slot", "rank_slot", "num_tokens_per_expert", "combined_x", "recv_src_idx")
+
+    def snap(r):
+        r["stream"].synchronize()
+        return {k: r["buf"][k].cpu().numpy().copy() for k in keys}
+
+    alone = []
+    for r in runs:
+        for k in keys:  # rows past each expert's count are never written
+            r["buf"][k].fill_(-1)
+        step(r)
+        alone.append(snap(r))
+        for k in keys:
+            r["buf"][k].fill_(-1)
+    torch.cuda.synchronize()
+    say("two host threads, two streams")
+    threads = [threading.Thread(target=step, args=(r,)) for r in runs]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    for i, r in enumerate(runs):
+        got = snap(r)
+        for k in keys:
+            assert np.array_equal(got[k], alone[i][k]), (i, k)
+        assert int(r["buf"]["status"].item()) == 0
