@@ -1,0 +1,79 @@
+"""Seeded random shapes through every entry point, against the CPU oracle.
+
+Each case draws N, H, K, E, R, the routing (distinct experts, or repeats when
+K > E or by chance), a masked fraction, the FP8 scale format, the capacity S
+(sometimes too small, so that entries are skipped and reported), the expand
+alignment and a combine bias (ids outside [-1, E) have tests of their own).
+The same inputs then go through the per-expert path (ep_layout, ep_dispatch,
+ep_combine), ep_layout_dispatch, the expand layout and normal mode, each
+checked with the bar of its own tests: integer outputs, FP8 bytes and scales
+bit-exact, combines bit-identical to the oracle.  The shapes are small enough
+for the oracle to finish in seconds and step across the library's block and
+launch boundaries (256 and 1,024 tokens, 1,024-channel chunks, K of 8, 16
+and 32)."""
+import numpy as np
+import pytest
+
+import oracle
+from combine_ep_layout_02_amd import ep
+from combine_ep_layout_02_amd import workloads as W
+from gpu_helpers import say
+from test_gpu_fused import check_fused
+from test_gpu_parity import check_path
+from test_gpu_receive_layouts import check_expand, check_normal
+
+pytestmark = pytest.mark.gpu
+
+CASES = 24
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.get()
+
+
+def draw(seed):
+    rng = np.random.default_rng(5000 + seed)
+    N = int(rng.choice([0, 1, 37, 129, 256, 257, 511, 700, 1024, 1025, 1300]))
+    fp8 = bool(rng.random() < 0.6)
+    H = int(128 * rng.integers(1, 13)) if fp8 else int(8 * rng.integers(1, 200))
+    E = int(rng.choice([4, 8, 16, 32, 64, 256, 1024]))
+    R = int(rng.choice([r for r in (1, 2, 4, 8, 16, 32, 64) if E % r == 0]))
+    K = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 9, 12, 16, 24, 32]))
+    repeats = K > E or rng.random() < 0.15
+    if repeats:
+        idx = rng.integers(0, E, size=(N, K)).astype(np.int64)
+    else:
+        idx = np.argsort(rng.random((N, E)), axis=1)[:, :K].astype(np.int64)
+    mask = float(rng.choice([0.0, 0.0, 0.05, 0.3]))
+    if mask and N:
+        idx[rng.random((N, K)) < mask] = -1
+    M = max(N, 1)
+    tight = rng.random() < 0.2
+    S = M if tight or E * M * K * H > 4e8 else M * K
+    fmt = int(rng.choice([ep.EP_SCALE_FP32, ep.EP_SCALE_POW2, ep.EP_SCALE_UE8M0])) if fp8 else \
+        ep.EP_SCALE_FP32
+    A = int(rng.choice([1, 2, 16, 128]))
+    x = W.bf16_bits(rng.standard_normal((N, H), dtype=np.float32))
+    wts = rng.random((N, K)).astype(np.float32)
+    P = int((idx >= 0).sum())
+    rows = W.bf16_bits(rng.standard_normal((P, H), dtype=np.float32))
+    bias = W.bf16_bits(rng.standard_normal((N, H), dtype=np.float32)) if rng.random() < 0.3 else None
+    name = (f"seed {seed}: N={N} H={H} K={K} E={E} R={R} fp8={fp8} fmt={fmt} S={S} A={A} "
+            f"mask={mask} repeats={repeats} bias={bias is not None}")
+    inp = {"x_bits": x, "topk_idx": idx, "topk_weights": wts, "expert_rows": rows}
+    return name, (N, H, K, E, R, M, S, fp8, fmt, A), inp, bias
+
+
+@pytest.mark.parametrize("seed", range(CASES))
+def test_random_shape_every_entry_point(o, seed):
+    name, (N, H, K, E, R, M, S, fp8, fmt, A), inp, bias = draw(seed)
+    say(name)
+    w = W.Workload(0, f"random {seed}", N, H, K, E, R, M, S, fp8, "uniform")
+    check_path(o, w, inp, name, scale_format=fmt)
+    shape = ep.make_shape(N, H, K, E, R, M, S, fp8, fmt)
+    check_fused(o, shape, inp["x_bits"], inp["topk_idx"], name)
+    if N * K * H <= 4e7:  # the expand buffer holds M * K rows plus the padding
+        check_expand(o, ep.make_shape(N, H, K, E, R, M, S, fp8, fmt, A), inp, name,
+                     y_rows=inp["expert_rows"], bias=bias)
+    check_normal(o, shape, inp, name, bias=bias)
