@@ -1,12 +1,13 @@
 """Thin ctypes binding of libep_mi355x.so (declared in include/ep.h).
 
 Same entry points as the C ABI: ``ep_query_sizes``, ``ep_layout``,
-``ep_dispatch``, ``ep_combine``, ``ep_dispatch_expand``, ``ep_combine_expand``,
-``ep_dispatch_normal``, ``ep_combine_normal``, ``ep_group_limited_topk``,
-``ep_strerror`` (plus
-``ep_probe_e4m3fn`` from include/ep_probe.h).  Functions take torch tensors that already live on
-the GPU, check dtype / device / contiguity, and pass ``data_ptr()`` and the
-current HIP stream to the library.  Every step of the path runs in the HIP
+``ep_dispatch``, ``ep_layout_dispatch``, ``ep_combine``, ``ep_dispatch_expand``,
+``ep_combine_expand``, ``ep_dispatch_normal``, ``ep_combine_normal``,
+``ep_group_limited_topk``, ``ep_strerror`` (plus ``ep_probe_e4m3fn`` from
+include/ep_probe.h); and ``layout`` / ``dispatch`` / ``combine``, the path in
+three calls that allocate their outputs.  Functions take torch tensors that
+already live on the GPU, check dtype / device / contiguity, and pass
+``data_ptr()`` and the current HIP stream to the library.  Every step of the path runs in the HIP
 kernels; this module only marshals arguments and allocates buffers with torch
 on request.  There is no fallback: without the built library every call
 raises.
@@ -14,6 +15,7 @@ raises.
 from __future__ import annotations
 
 import ctypes
+import dataclasses
 import os
 from typing import Optional
 
@@ -424,4 +426,74 @@ def allocate(shape: ep_shape, device="cuda", parts=("layout", "dispatch", "combi
                                    if shape.use_fp8 else None),
             "recv_src_idx_expand": torch.empty(T, dtype=torch.int32, device=dev),
         })
+    return out
+
+
+# ---- the path in three calls, allocating with torch --------------------------
+@dataclasses.dataclass
+class Handle:
+    """The layout of one routing, reused by its dispatch and combine (the
+    handle the pages' dispatch returns for the combine): the shape without a
+    hidden size, the routing itself and every layout output."""
+    shape: ep_shape
+    topk_idx: torch.Tensor
+    num_tokens_per_rank: torch.Tensor
+    num_tokens_per_expert: torch.Tensor
+    is_token_in_rank: torch.Tensor
+    expert_slot: torch.Tensor
+    rank_slot: torch.Tensor
+    expert_offset: torch.Tensor
+    status: torch.Tensor
+
+    def with_hidden(self, hidden: int, use_fp8: bool = False,
+                    scale_format: int = EP_SCALE_FP32) -> ep_shape:
+        s = self.shape
+        return make_shape(s.num_tokens, hidden, s.num_topk, s.num_experts, s.num_ranks,
+                          s.num_max_dispatch_tokens_per_rank, s.expert_capacity, use_fp8,
+                          scale_format if use_fp8 else EP_SCALE_FP32, s.expert_alignment)
+
+
+def layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: int,
+           num_max_dispatch_tokens_per_rank: Optional[int] = None,
+           expert_capacity: Optional[int] = None, expert_alignment: int = 0,
+           stream=None) -> Handle:
+    """``ep_layout`` on a [N, K] int64 routing (-1 = masked), outputs allocated
+    here.  M defaults to N and the expert capacity S to M."""
+    N, K = topk_idx.shape
+    M = max(N, 1) if num_max_dispatch_tokens_per_rank is None else num_max_dispatch_tokens_per_rank
+    S = M if expert_capacity is None else expert_capacity
+    # the layout reads no activations: any valid hidden size will do here
+    shape = make_shape(N, 8, K, num_experts, num_ranks, M, S, False, EP_SCALE_FP32, expert_alignment)
+    b = allocate(shape, topk_idx.device, parts=("layout",))
+    ep_layout(shape, topk_idx, b["num_tokens_per_rank"], b["num_tokens_per_expert"],
+              b["is_token_in_rank"], b["expert_slot"], b["rank_slot"], b["expert_offset"],
+              b["workspace"], b["status"], stream=stream)
+    return Handle(shape, topk_idx, b["num_tokens_per_rank"], b["num_tokens_per_expert"],
+                  b["is_token_in_rank"], b["expert_slot"], b["rank_slot"], b["expert_offset"],
+                  b["status"])
+
+
+def dispatch(x: torch.Tensor, handle: Handle, use_fp8: bool = True,
+             scale_format: int = EP_SCALE_FP32, stream=None):
+    """``ep_dispatch`` of bf16 ``x`` [N, H] by a layout's handle.  Returns
+    (recv_x [E, S, H] as float8_e4m3fn or bfloat16, recv_scales [E, S, H/128]
+    fp32 (int32 words for UE8M0) or None, recv_src_idx [E, S]); rows at or past
+    num_tokens_per_expert[e] are unwritten."""
+    shape = handle.with_hidden(x.shape[1], use_fp8, scale_format)
+    b = allocate(shape, x.device, parts=("dispatch",))
+    ep_dispatch(shape, x, handle.topk_idx, handle.expert_slot, b["recv_x"], b["recv_scales"],
+                b["recv_src_idx"], handle.status, stream=stream)
+    recv_x = b["recv_x"].view(torch.float8_e4m3fn if use_fp8 else torch.bfloat16)
+    return recv_x, b["recv_scales"], b["recv_src_idx"]
+
+
+def combine(expert_out: torch.Tensor, handle: Handle, topk_weights: torch.Tensor,
+            bias: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """``ep_combine`` of bf16 expert outputs [E, S, H] by a layout's handle:
+    returns the [N, H] bfloat16 weighted sums in token order (plus ``bias``)."""
+    shape = handle.with_hidden(expert_out.shape[-1])
+    out = torch.empty((shape.num_tokens, shape.hidden), dtype=torch.bfloat16,
+                      device=expert_out.device)
+    ep_combine(shape, expert_out, handle.topk_idx, topk_weights, handle.expert_slot, out,
+               handle.status, stream=stream, bias=bias)
     return out

@@ -17,7 +17,7 @@ from cases import small_cases
 from combine_ep_layout_02_amd import ep
 from combine_ep_layout_02_amd import workloads as W
 from gpu_helpers import (POISON_SCALE_BITS, POISON_SRC, POISON_X8, POISON_X16, DispatchRun,
-                         LayoutRun, dev, gather_rows, place_expert_rows, run_combine, say,
+                         LayoutRun, dev, gather_rows, host, place_expert_rows, run_combine, say,
                          unwritten_rows_intact, written_rows)
 
 pytestmark = pytest.mark.gpu
@@ -574,3 +574,41 @@ def test_two_streams_and_two_host_threads(o):
         for k in keys:
             assert np.array_equal(got[k], alone[i][k]), (i, k)
         assert int(r["buf"]["status"].item()) == 0
+
+
+@pytest.mark.parametrize("wid", [2, 1])
+def test_three_call_api(o, wid):
+    """ep.layout / ep.dispatch / ep.combine (outputs allocated by the binding)
+    give what the oracle gives, on the decode workload (FP8) and the tiny one
+    (BF16)."""
+    w = W.WORKLOADS[wid]
+    inp = W.make_inputs(w, with_expert_rows=True)
+    E, S, H = w.num_experts, w.expert_capacity, w.hidden
+    idx = dev(inp["topk_idx"])
+    handle = ep.layout(idx, E, w.num_ranks, w.num_max_dispatch_tokens_per_rank, S)
+    x = dev(inp["x_bits"]).view(torch.bfloat16)
+    recv_x, recv_scales, recv_src = ep.dispatch(x, handle, use_fp8=w.use_fp8)
+    torch.cuda.synchronize()
+    lay = o.layout(inp["topk_idx"], E, w.num_ranks)
+    for key in ("num_tokens_per_rank", "num_tokens_per_expert", "expert_slot", "rank_slot",
+                "is_token_in_rank"):
+        assert np.array_equal(host(getattr(handle, key)), lay[key]), key
+    cnt = lay["num_tokens_per_expert"]
+    s_or = oracle_capacity(cnt, S)
+    rx, rs, src, st = o.pack(inp["x_bits"], inp["topk_idx"], lay["expert_slot"], E, s_or, w.use_fp8)
+    got_x = recv_x.view(torch.uint8 if w.use_fp8 else torch.int16).cpu().numpy()
+    got_src = host(recv_src)
+    for e in range(E):
+        c = int(cnt[e])
+        assert np.array_equal(got_x[e, :c].view(rx.dtype), rx[e, :c]), e
+        assert np.array_equal(got_src[e, :c], src[e, :c]), e
+        if w.use_fp8:
+            assert np.array_equal(host(recv_scales[e, :c]).view(np.int32), rs[e, :c].view(np.int32)), e
+    y_or = pins.place_rows(inp["expert_rows"], inp["topk_idx"], lay["expert_slot"], E, s_or)
+    y = place_expert_rows(inp["expert_rows"], inp["topk_idx"], lay["expert_slot"], E, S, H)
+    out = ep.combine(y.view(torch.bfloat16), handle, dev(inp["topk_weights"]))
+    torch.cuda.synchronize()
+    want, st_c = o.combine(y_or, inp["topk_idx"], inp["topk_weights"], lay["expert_slot"], E, s_or)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert out.dtype == torch.bfloat16 and np.array_equal(got, want)
+    assert int(handle.status.item()) == (lay["status"] | st | st_c)
