@@ -3,6 +3,9 @@
 // before anything is enqueued; no entry point allocates or synchronises.
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "ep_internal.h"
 
 namespace {
@@ -51,6 +54,72 @@ int check_shape(const ep_shape *s)
     return EP_OK;
 }
 
+// Scratch of ep_layout_noalloc: the layout's per-block histograms live in
+// this file-scope device array instead of a caller workspace.  Every GPU the
+// library runs on holds its own copy until the process ends.  On the host the
+// name `scratch` is only a stand-in, not a device address, so it is never
+// passed to a kernel: its address on each device is looked up once, with that
+// device current, and kept in scratch_addr[].  Calls that overlap on one GPU
+// share the array and race; the histograms need no clearing (the count
+// kernel writes every row before the assign kernel reads it).
+static __device__ __align__(256) unsigned char scratch[EP_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> scratch_addr[kMaxDevices];
+std::mutex scratch_mutex;
+
+// Device address of `scratch` on device `dev` (looked up at the first call
+// on that device).
+hipError_t scratch_on(int dev, void **out)
+{
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    void *p = scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(scratch_mutex);
+        p = scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            int cur = 0;
+            hipError_t err = hipGetDevice(&cur);
+            if (err == hipSuccess && cur != dev)
+                err = hipSetDevice(dev);
+            if (err != hipSuccess)
+                return err;
+            err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+            if (err != hipSuccess)
+                return err;
+            if (back != hipSuccess)
+                return back;
+            scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+// The host checks of ep_layout that do not concern the workspace: shape,
+// null and misaligned pointers.
+int layout_args(const ep_shape *s, const int64_t *topk_idx, const int32_t *num_tokens_per_rank,
+                const int32_t *num_tokens_per_expert, const uint8_t *is_token_in_rank,
+                const int32_t *expert_slot, const int32_t *rank_slot, const int32_t *expert_offset,
+                const uint32_t *status)
+{
+    const int rc = check_shape(s);
+    if (rc != EP_OK)
+        return rc;
+    const bool has_tokens = s->num_tokens > 0;
+    if (!num_tokens_per_rank || !num_tokens_per_expert)
+        return EP_ERR_NULL;
+    if (has_tokens && (!topk_idx || !is_token_in_rank || !expert_slot || !rank_slot))
+        return EP_ERR_NULL;
+    if (!aligned(topk_idx, 8) || !aligned(num_tokens_per_rank, 4) ||
+        !aligned(num_tokens_per_expert, 4) || !aligned(expert_slot, 4) || !aligned(rank_slot, 4) ||
+        !aligned(expert_offset, 4) || !aligned(status, 4))
+        return EP_ERR_ALIGN;
+    return EP_OK;
+}
+
 } // namespace
 
 extern "C" {
@@ -75,6 +144,9 @@ const char *ep_strerror(int code)
         return "EP_ERR_HIP: kernel launch failed";
     case EP_ERR_WORKSPACE:
         return "EP_ERR_WORKSPACE: layout workspace missing or too small";
+    case EP_ERR_SCRATCH:
+        return "EP_ERR_SCRATCH: the layout needs more scratch than ep_layout_noalloc's static "
+               "buffer holds (EP_NOALLOC_SCRATCH_BYTES); use ep_layout with a workspace";
     default:
         return "unknown ep status code";
     }
@@ -132,17 +204,11 @@ int ep_layout(const ep_shape *s, const int64_t *topk_idx, int32_t *num_tokens_pe
               int32_t *rank_slot, int32_t *expert_offset, void *workspace, size_t workspace_bytes,
               uint32_t *status, void *stream)
 {
-    const int rc = check_shape(s);
+    const int rc = layout_args(s, topk_idx, num_tokens_per_rank, num_tokens_per_expert,
+                               is_token_in_rank, expert_slot, rank_slot, expert_offset, status);
     if (rc != EP_OK)
         return rc;
-    const bool has_tokens = s->num_tokens > 0;
-    if (!num_tokens_per_rank || !num_tokens_per_expert)
-        return EP_ERR_NULL;
-    if (has_tokens && (!topk_idx || !is_token_in_rank || !expert_slot || !rank_slot))
-        return EP_ERR_NULL;
-    if (!aligned(topk_idx, 8) || !aligned(num_tokens_per_rank, 4) ||
-        !aligned(num_tokens_per_expert, 4) || !aligned(expert_slot, 4) || !aligned(rank_slot, 4) ||
-        !aligned(expert_offset, 4) || !aligned(status, 4) || !aligned(workspace, 16))
+    if (!aligned(workspace, 16))
         return EP_ERR_ALIGN;
     ep::LayoutPlan plan;
     ep::plan_layout(*s, &plan);
@@ -152,6 +218,34 @@ int ep_layout(const ep_shape *s, const int64_t *topk_idx, int32_t *num_tokens_pe
         *s, plan, topk_idx, num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank,
         expert_slot, rank_slot, expert_offset, static_cast<int32_t *>(workspace), status,
         static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+int ep_layout_noalloc(const ep_shape *s, const int64_t *topk_idx, int32_t *num_tokens_per_rank,
+                      int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank,
+                      int32_t *expert_slot, int32_t *rank_slot, int32_t *expert_offset,
+                      uint32_t *status, void *stream)
+{
+    const int rc = layout_args(s, topk_idx, num_tokens_per_rank, num_tokens_per_expert,
+                               is_token_in_rank, expert_slot, rank_slot, expert_offset, status);
+    if (rc != EP_OK)
+        return rc;
+    ep::LayoutPlan plan;
+    ep::plan_layout(*s, &plan);
+    if (plan.workspace_bytes > EP_NOALLOC_SCRATCH_BYTES)
+        return EP_ERR_SCRATCH;
+    // the scratch of the stream's device (its address is looked up at the
+    // first call on that device)
+    int dev = 0;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev)) != hipSuccess)
+        return EP_ERR_HIP;
+    void *ws = nullptr;
+    if (scratch_on(dev, &ws) != hipSuccess)
+        return EP_ERR_HIP;
+    const hipError_t err = ep::launch_layout(
+        *s, plan, topk_idx, num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank,
+        expert_slot, rank_slot, expert_offset, static_cast<int32_t *>(ws), status, st);
     return err == hipSuccess ? EP_OK : EP_ERR_HIP;
 }
 

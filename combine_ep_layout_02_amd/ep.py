@@ -1,6 +1,6 @@
 """Thin ctypes binding of libep_mi355x.so (declared in include/ep.h).
 
-Same entry points as the C ABI: ``ep_query_sizes``, ``ep_layout``,
+Same entry points as the C ABI: ``ep_query_sizes``, ``ep_layout``, ``ep_layout_noalloc``,
 ``ep_dispatch``, ``ep_layout_dispatch``, ``ep_combine``, ``ep_dispatch_expand``,
 ``ep_combine_expand``, ``ep_dispatch_normal``, ``ep_combine_normal``,
 ``ep_group_limited_topk``, ``ep_strerror`` (plus ``ep_probe_e4m3fn`` from
@@ -32,6 +32,8 @@ EP_ERR_ALIGN = 4
 EP_ERR_UNSUPPORTED = 5
 EP_ERR_HIP = 6
 EP_ERR_WORKSPACE = 7
+EP_ERR_SCRATCH = 8
+EP_NOALLOC_SCRATCH_BYTES = 1 << 20
 EP_STATUS_BAD_EXPERT_ID = 1
 EP_STATUS_BAD_SLOT = 2
 
@@ -47,7 +49,7 @@ SIZE_FIELDS = ("recv_x", "recv_scales", "recv_src_idx", "expert_out", "combined_
                "recv_x_normal", "recv_scales_normal", "recv_topk_idx", "recv_topk_weights",
                "recv_src_idx_normal", "expert_out_normal", "combined_topk_weights",
                "recv_x_expand", "recv_scales_expand", "recv_src_idx_expand", "expert_out_expand")
-EXPORTED = ("ep_query_sizes", "ep_layout", "ep_dispatch", "ep_layout_dispatch", "ep_combine",
+EXPORTED = ("ep_query_sizes", "ep_layout", "ep_layout_noalloc", "ep_dispatch", "ep_layout_dispatch", "ep_combine",
             "ep_dispatch_expand",
             "ep_combine_expand", "ep_dispatch_normal", "ep_combine_normal",
             "ep_group_limited_topk", "ep_strerror", "ep_probe_e4m3fn")
@@ -84,6 +86,7 @@ def lib() -> ctypes.CDLL:
         sp = ctypes.POINTER(ep_shape)
         L.ep_query_sizes.argtypes = [sp, ctypes.POINTER(ep_sizes)]
         L.ep_layout.argtypes = [sp] + [vp] * 8 + [sz, vp, vp]
+        L.ep_layout_noalloc.argtypes = [sp] + [vp] * 9
         L.ep_dispatch.argtypes = [sp] + [vp] * 8
         L.ep_layout_dispatch.argtypes = [sp] + [vp] * 9 + [sz] + [vp] * 5
         L.ep_combine.argtypes = [sp] + [vp] * 8
@@ -192,6 +195,26 @@ def ep_layout(shape: ep_shape, topk_idx: torch.Tensor, num_tokens_per_rank: torc
         _ptr(status, "status", _STATUS, 1), _stream(stream, num_tokens_per_expert))
     if rc != EP_OK:
         raise EpError(rc, "ep_layout")
+
+
+def ep_layout_noalloc(shape: ep_shape, topk_idx: torch.Tensor, num_tokens_per_rank: torch.Tensor,
+                      num_tokens_per_expert: torch.Tensor, is_token_in_rank: torch.Tensor,
+                      expert_slot: torch.Tensor, rank_slot: torch.Tensor,
+                      expert_offset: Optional[torch.Tensor] = None,
+                      status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Dispatch layout with the library's static per-device scratch instead of
+    a workspace; see ``ep_layout_noalloc`` in include/ep.h."""
+    N, K, E, R = shape.num_tokens, shape.num_topk, shape.num_experts, shape.num_ranks
+    rc = lib().ep_layout_noalloc(
+        ctypes.byref(shape), _ptr(topk_idx, "topk_idx", _I64, N * K),
+        _ptr(num_tokens_per_rank, "num_tokens_per_rank", _I32, R),
+        _ptr(num_tokens_per_expert, "num_tokens_per_expert", _I32, E),
+        _ptr(is_token_in_rank, "is_token_in_rank", _U8, N * R),
+        _ptr(expert_slot, "expert_slot", _I32, N * K), _ptr(rank_slot, "rank_slot", _I32, N * R),
+        _ptr(expert_offset, "expert_offset", _I32, E + 1),
+        _ptr(status, "status", _STATUS, 1), _stream(stream, num_tokens_per_expert))
+    if rc != EP_OK:
+        raise EpError(rc, "ep_layout_noalloc")
 
 
 def ep_dispatch(shape: ep_shape, x: torch.Tensor, topk_idx: torch.Tensor, expert_slot: torch.Tensor,

@@ -72,6 +72,8 @@ extern "C" {
 #define EP_ERR_UNSUPPORTED 5 /* a size the library does not support (see limits)     */
 #define EP_ERR_HIP 6         /* a HIP launch failed                                   */
 #define EP_ERR_WORKSPACE 7   /* workspace NULL or smaller than ep_query_sizes says    */
+#define EP_ERR_SCRATCH 8     /* ep_layout_noalloc: the shape's layout scratch is larger
+                                than EP_NOALLOC_SCRATCH_BYTES                        */
 
 /* Bits OR-ed into the optional device status word. */
 #define EP_STATUS_BAD_EXPERT_ID 1u
@@ -83,6 +85,10 @@ extern "C" {
 #define EP_MAX_TOPK 32      /* K */
 #define EP_MAX_ALIGNMENT 1024 /* expert_alignment */
 #define EP_MAX_GROUPS 64      /* num_groups of ep_group_limited_topk */
+/* Bytes of the static per-device scratch of ep_layout_noalloc (1 MiB):
+ * enough for ep_sizes.layout_workspace of up to 253,952 tokens at E = 256,
+ * R = 8, or 61,440 tokens at E = 1024, R = 64. */
+#define EP_NOALLOC_SCRATCH_BYTES (1u << 20)
 
 /* The problem's shape ([V1] §5.1 and §6.1; [L14] §3).  Passed by host pointer. */
 typedef struct {
@@ -183,6 +189,26 @@ int ep_layout(const ep_shape *shape, const int64_t *topk_idx, int32_t *num_token
               int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank, int32_t *expert_slot,
               int32_t *rank_slot, int32_t *expert_offset, void *workspace, size_t workspace_bytes,
               uint32_t *status, void *stream);
+
+/* ep_layout without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Arguments, outputs, status bits and error codes
+ * are those of ep_layout; the per-block histograms go to a static device
+ * array of EP_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on until the process ends (its address is looked up at the first call
+ * on each device).  The call allocates nothing.
+ * The scratch belongs to the device of `stream` (the current device when
+ * `stream` is NULL); every call on one GPU shares it, so calls that may
+ * overlap on one GPU (different streams, or host threads without ordering)
+ * race and must be serialised by the caller.  Nothing in it needs clearing:
+ * each call writes every histogram row before it reads one.
+ * Returns EP_ERR_SCRATCH, before anything is enqueued, when the shape needs
+ * more than EP_NOALLOC_SCRATCH_BYTES (ep_sizes.layout_workspace says how much),
+ * and EP_ERR_HIP when the device address cannot be looked up. */
+int ep_layout_noalloc(const ep_shape *shape, const int64_t *topk_idx,
+                      int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+                      uint8_t *is_token_in_rank, int32_t *expert_slot, int32_t *rank_slot,
+                      int32_t *expert_offset, uint32_t *status, void *stream);
 
 /* Dispatch pack into the fixed-shape per-expert receive buffers ([L14] §3 and
  * [V1] §6.3: data [local experts, M * ranks, hidden] with a count per local

@@ -46,7 +46,7 @@ def test_struct_layout_matches_header():
 
 
 def test_strerror_names_every_code():
-    for code in range(0, 8):
+    for code in range(0, 9):
         assert ep.ep_strerror(code).startswith("EP_")
     assert "unknown" in ep.ep_strerror(99)
 
@@ -303,6 +303,22 @@ def test_layout_workspace_is_checked():
     lib = ep.lib()
     assert lib.ep_layout(ctypes.byref(s), *[OK16] * 7, None, ctypes.c_size_t(need), None, None) == ep.EP_ERR_WORKSPACE
     assert lib.ep_layout(ctypes.byref(s), *[OK16] * 7, OK16, ctypes.c_size_t(need - 1), None, None) == ep.EP_ERR_WORKSPACE
+
+
+def test_layout_noalloc_static_errors():
+    """ep_layout_noalloc: a shape whose histograms exceed the static scratch,
+    a bad shape, null and misaligned pointers are refused on the host, before
+    the device's scratch address is looked up."""
+    lib = ep.lib()
+    big = _shape(num_tokens=300_000, num_topk=8, num_experts=256, num_ranks=8,
+                 num_max_dispatch_tokens_per_rank=300_000,
+                 expert_capacity=300_000)
+    assert ep.ep_query_sizes(big)["layout_workspace"] > ep.EP_NOALLOC_SCRATCH_BYTES
+    call = lambda sh, *p: lib.ep_layout_noalloc(ctypes.byref(sh), *p, None, None)
+    assert call(big, *[OK16] * 7) == ep.EP_ERR_SCRATCH
+    assert call(_shape(num_ranks=3), *[OK16] * 7) == ep.EP_ERR_SHAPE
+    assert call(_shape(), OK16, None, *[OK16] * 5) == ep.EP_ERR_NULL
+    assert call(_shape(), BAD, *[OK16] * 6) == ep.EP_ERR_ALIGN
 
 
 def test_probe_argument_checks():
