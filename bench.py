@@ -623,12 +623,15 @@ def device_info():
             "torch": torch.__version__}
 
 
-def time_gating(wid, steps, scrub_bytes, say, num_groups=8, topk_groups=4):
-    """Group-limited gating on workload ``wid``'s shape (router scores N(0, 1)
-    [N, E] fp32): ep_group_limited_topk alone, cold, and the whole step with
-    the gating in front (gating + layout + dispatch + combine), cold.  The
-    gating's algorithmic bytes: read the scores (4 B per (token, expert)),
-    write topk_idx (8 B) and topk_weights (4 B) per entry."""
+def time_gating(wid, steps, scrub_bytes, say):
+    """Group-limited gating on workload ``wid``'s own router scores with the
+    summed-score rule (top groups by the ordered binary32 sum of their
+    scores, normalised sigmoid weights), which reproduces the workload's
+    routing exactly (checked here): ep_group_limited_topk alone, cold; the
+    whole step with the gating in front (gating + layout + dispatch +
+    combine), cold; and the same step without the gating in the same run.
+    The gating's algorithmic bytes: read the scores (4 B per (token,
+    expert)), write topk_idx (8 B) and topk_weights (4 B) per entry."""
     import torch
     from combine_ep_layout_02_amd import ep
     from combine_ep_layout_02_amd import workloads as W
@@ -638,12 +641,15 @@ def time_gating(wid, steps, scrub_bytes, say, num_groups=8, topk_groups=4):
     stream = torch.cuda.current_stream()
     shape = ep.shape_of(w)
     N, E, K, H = w.num_tokens, w.num_experts, w.num_topk, w.hidden
-    g = torch.Generator(device=dev)
-    g.manual_seed(2300 + wid)
-    scores = torch.randn((N, E), dtype=torch.float32, device=dev, generator=g)
+    G, TG = w.num_groups, w.topk_groups
+    say(f"gating {w.name}: generating inputs")
+    inp = W.make_inputs(w)
+    scores = torch.from_numpy(inp["router_scores"]).to(dev)
     topk_idx = torch.empty((N, K), dtype=torch.int64, device=dev)
     topk_weights = torch.empty((N, K), dtype=torch.float32, device=dev)
-    x = torch.randn((N, H), dtype=torch.bfloat16, device=dev, generator=g).view(torch.int16)
+    x = torch.from_numpy(inp["x_bits"].view(np.int16)).to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(2300 + wid)
     y = torch.randn((E, w.expert_capacity, H), dtype=torch.bfloat16, device=dev,
                     generator=g).view(torch.int16)
     buf = ep.allocate(shape, dev, parts=("layout", "dispatch", "combine"))
@@ -655,10 +661,10 @@ def time_gating(wid, steps, scrub_bytes, say, num_groups=8, topk_groups=4):
             torch.sum(scrub, dim=0, out=scrub_out)
 
     def gate():
-        ep.ep_group_limited_topk(shape, num_groups, topk_groups, scores, topk_idx, topk_weights)
+        ep.ep_group_limited_topk(shape, G, TG, ep.EP_GATE_SUM_SIGMOID, scores, topk_idx,
+                                 topk_weights)
 
-    def step():
-        gate()
+    def path():
         ep.ep_layout(shape, topk_idx, buf["num_tokens_per_rank"], buf["num_tokens_per_expert"],
                      buf["is_token_in_rank"], buf["expert_slot"], buf["rank_slot"],
                      buf["expert_offset"], buf["workspace"], buf["status"])
@@ -667,16 +673,25 @@ def time_gating(wid, steps, scrub_bytes, say, num_groups=8, topk_groups=4):
         ep.ep_combine(shape, y, topk_idx, topk_weights, buf["expert_slot"], buf["combined_x"],
                       buf["status"])
 
+    def step():
+        gate()
+        path()
+
     step()
     torch.cuda.synchronize()
     if int(buf["status"].item()) != 0:
         raise RuntimeError(f"device status {int(buf['status'].item())}")
+    if not np.array_equal(topk_idx.cpu().numpy(), inp["topk_idx"]):
+        raise RuntimeError("the gating did not reproduce the workload's routing")
     nb = 4 * N * E + 12 * N * K
     say(f"ep_group_limited_topk {w.name}: {steps} cold launches, {steps} gated steps")
     us = _timed_cold(gate, steps, evict, stream)
-    return {"num_groups": num_groups, "topk_groups": topk_groups, "bytes": nb,
+    return {"rule": "group score = ordered binary32 sum; weights = normalised sigmoids",
+            "num_groups": G, "topk_groups": TG, "bytes": nb,
+            "picks_equal_the_workload_routing": True,
             "us_cold_median": round(us, 2), "gbps_cold": round(nb / (us * 1e-6) / 1e9, 1),
-            "step_us_cold_with_gating": round(_timed_cold(step, steps, evict, stream), 2)}
+            "step_us_cold_with_gating": round(_timed_cold(step, steps, evict, stream), 2),
+            "step_us_cold_without_gating": round(_timed_cold(path, steps, evict, stream), 2)}
 
 
 def time_combine_bias(wid, steps, scrub_bytes, say):

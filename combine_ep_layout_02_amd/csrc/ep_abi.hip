@@ -455,8 +455,8 @@ int ep_combine_normal(const ep_shape *s, const uint16_t *x, const int32_t *rank_
 }
 
 int ep_group_limited_topk(const ep_shape *s, int32_t num_groups, int32_t topk_groups,
-                          const float *scores, int64_t *topk_idx, float *topk_weights,
-                          void *stream)
+                          int32_t rule, const float *scores, int64_t *topk_idx,
+                          float *topk_weights, void *stream)
 {
     const int rc = check_shape(s);
     if (rc != EP_OK)
@@ -467,13 +467,15 @@ int ep_group_limited_topk(const ep_shape *s, int32_t num_groups, int32_t topk_gr
     if (num_groups < 1 || E % num_groups != 0 || topk_groups < 1 || topk_groups > num_groups ||
         (int64_t)K > (int64_t)topk_groups * (E / num_groups))
         return EP_ERR_SHAPE;
+    if (rule != EP_GATE_MAX_SOFTMAX && rule != EP_GATE_SUM_SIGMOID)
+        return EP_ERR_SHAPE;
     if (s->num_tokens == 0)
         return EP_OK;
     if (!scores || !topk_idx)
         return EP_ERR_NULL;
     if (!aligned(scores, 4) || !aligned(topk_idx, 8) || !aligned(topk_weights, 4))
         return EP_ERR_ALIGN;
-    const hipError_t err = ep::launch_gate(*s, num_groups, topk_groups, scores, topk_idx,
+    const hipError_t err = ep::launch_gate(*s, num_groups, topk_groups, rule, scores, topk_idx,
                                            topk_weights, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? EP_OK : EP_ERR_HIP;
 }

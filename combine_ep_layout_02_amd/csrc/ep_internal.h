@@ -87,7 +87,7 @@ hipError_t launch_dispatch_normal(const ep_shape &s, const uint16_t *x, const in
                                   uint32_t *status, hipStream_t stream);
 
 // ---- gating ----------------------------------------------------------------
-hipError_t launch_gate(const ep_shape &s, int32_t num_groups, int32_t topk_groups,
+hipError_t launch_gate(const ep_shape &s, int32_t num_groups, int32_t topk_groups, int32_t rule,
                        const float *scores, int64_t *topk_idx, float *topk_weights,
                        hipStream_t stream);
 

@@ -3,26 +3,32 @@
 // groups then top-8 experts; Lesson 14 §3 Q3: at most 4 nodes per token; its
 // exercise: normalised softmax gating weights).
 //
-// Per token: a group's score is its best expert's score; the TG best groups
-// are kept (ties: lower group index); the K best experts of the kept groups
-// are picked, best first (ties: lower expert index); the weights are the
-// softmax of the picked scores.
+// Per token, under one of two rules for the group score and the weights:
+//   EP_GATE_MAX_SOFTMAX: a group's score is its best expert's score; the
+//     weights are the softmax of the picked scores;
+//   EP_GATE_SUM_SIGMOID: a group's score is the binary32 sum of its experts'
+//     scores in ascending expert index from +0 (one lane per group adds them
+//     one after another, so the rounding is the definition's); the weights
+//     are the sigmoids of the picked scores normalised to sum 1.
+// Then the TG best groups are kept (ties: lower group index) and the K best
+// experts of the kept groups are picked, best first (ties: lower expert
+// index).
 //
 // Work item = one wave per token.  Lane l holds experts i * 64 + l (so each
 // load instruction reads 64 consecutive scores, and the index order of the
 // experts is the order of (i, lane)).  Scores become order-preserving 32-bit
 // keys (after adding +0, so -0 and +0 compare equal, as floats do).  The group
-// maxima are LDS atomicMax on the keys.  Selection moves no data through
-// memory:
+// maxima are LDS atomicMax on the keys; group sums are taken by lane g from
+// the wave's scores staged in LDS.  Selection moves no data through memory:
 //   groups:  group g's rank is the number of groups whose (key, lower index)
 //            beats it (G readlanes); the TG lowest ranks are kept;
 //   experts: K rounds, each taking the largest remaining candidate key (a
 //            register-only wave maximum: DPP inside rows of 16 lanes, then the
 //            four row maxima by readlane) at the lowest expert index holding
 //            it (one ballot per key slot), which lane k keeps for pick k.
-// All decisions are exact comparisons of the inputs, so they match the CPU
-// definition bit for bit; only the weights involve rounding (expf and one
-// division per pick).
+// All decisions are exact comparisons of the inputs (or of sums rounded in
+// the defined order), so they match the CPU definition bit for bit; only the
+// weights involve further rounding (expf and one division per pick).
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -66,7 +72,7 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v)
     return max(max(r0, r1), max(r2, r3));
 }
 
-template <int V>
+template <int V, int RULE>
 __global__ __launch_bounds__(kThreads) void gate_kernel(int32_t N, int32_t E, int32_t G,
                                                         int32_t TG, int32_t K,
                                                         const float *__restrict__ scores,
@@ -83,25 +89,46 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(int32_t N, int32_t E, in
     uint32_t key[V];
     int32_t grp[V];
     bool valid[V];
+    float sc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         const int32_t e = i * 64 + lane;
         valid[i] = live && e < E;
-        key[i] = valid[i] ? order_key(scores[t * E + e]) : 0u;
+        sc[i] = valid[i] ? scores[t * E + e] : 0.0f;
+        key[i] = valid[i] ? order_key(sc[i]) : 0u;
         grp[i] = e / L;
     }
-    s_gkey[wave][lane] = 0u;
-    __syncthreads();
+    uint32_t gk;
+    if constexpr (RULE == EP_GATE_MAX_SOFTMAX) {
+        s_gkey[wave][lane] = 0u;
+        __syncthreads();
 #pragma unroll
-    for (int i = 0; i < V; ++i)
-        if (valid[i])
-            atomicMax(&s_gkey[wave][grp[i]], key[i]);
-    __syncthreads();
-    if (!live)
-        return;
+        for (int i = 0; i < V; ++i)
+            if (valid[i])
+                atomicMax(&s_gkey[wave][grp[i]], key[i]);
+        __syncthreads();
+        if (!live)
+            return;
+        gk = lane < G ? s_gkey[wave][lane] : 0u;
+    } else {
+        // the wave's scores in LDS, then lane g adds group g's scores in
+        // ascending expert index from +0 (each sum a finite float, so its
+        // key is above 0)
+        __shared__ float s_sc[kWaves][V * 64];
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+            s_sc[wave][i * 64 + lane] = sc[i];
+        __syncthreads();
+        if (!live)
+            return;
+        float acc = 0.0f;
+        if (lane < G)
+            for (int32_t i = 0; i < L; ++i)
+                acc = acc + s_sc[wave][lane * L + i];
+        gk = lane < G ? order_key(acc) : 0u;
+    }
 
     // groups: rank of group `lane` among the G group keys (ties: lower index)
-    const uint32_t gk = lane < G ? s_gkey[wave][lane] : 0u;
     int grank = 0;
     for (int g = 0; g < G; ++g) {
         const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)gk, g);
@@ -144,9 +171,15 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(int32_t N, int32_t E, in
         }
     }
 
-    // softmax of the picks, summed in pick order
-    const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_score), 0));
-    const float z = lane < K ? expf(my_score - top) : 0.0f;
+    // the weights: softmax of the picks, or their sigmoids, normalised by the
+    // sum taken in pick order
+    float z = 0.0f;
+    if constexpr (RULE == EP_GATE_MAX_SOFTMAX) {
+        const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_score), 0));
+        z = lane < K ? expf(my_score - top) : 0.0f;
+    } else {
+        z = lane < K ? 1.0f / (1.0f + expf(-my_score)) : 0.0f;
+    }
     float sum = 0.0f;
     for (int k = 0; k < K; ++k)
         sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), k));
@@ -159,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(int32_t N, int32_t E, in
 
 } // namespace
 
-hipError_t launch_gate(const ep_shape &s, int32_t num_groups, int32_t topk_groups,
+hipError_t launch_gate(const ep_shape &s, int32_t num_groups, int32_t topk_groups, int32_t rule,
                        const float *scores, int64_t *topk_idx, float *topk_weights,
                        hipStream_t stream)
 {
@@ -168,8 +201,16 @@ hipError_t launch_gate(const ep_shape &s, int32_t num_groups, int32_t topk_group
         return hipSuccess;
     const dim3 grid((unsigned)((N + kWaves - 1) / kWaves));
 #define EP_GATE(V)                                                                                 \
-    hipLaunchKernelGGL(gate_kernel<V>, grid, dim3(kThreads), 0, stream, N, E, num_groups,          \
-                       topk_groups, K, scores, topk_idx, topk_weights)
+    do {                                                                                           \
+        if (rule == EP_GATE_SUM_SIGMOID)                                                           \
+            hipLaunchKernelGGL((gate_kernel<V, EP_GATE_SUM_SIGMOID>), grid, dim3(kThreads), 0,     \
+                               stream, N, E, num_groups, topk_groups, K, scores, topk_idx,         \
+                               topk_weights);                                                      \
+        else                                                                                       \
+            hipLaunchKernelGGL((gate_kernel<V, EP_GATE_MAX_SOFTMAX>), grid, dim3(kThreads), 0,     \
+                               stream, N, E, num_groups, topk_groups, K, scores, topk_idx,         \
+                               topk_weights);                                                      \
+    } while (0)
     if (E <= 64)
         EP_GATE(1);
     else if (E <= 128)

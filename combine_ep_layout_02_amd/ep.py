@@ -14,6 +14,7 @@ raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import dataclasses
 import os
@@ -54,6 +55,8 @@ EXPORTED = ("ep_query_sizes", "ep_layout", "ep_layout_noalloc", "ep_dispatch", "
             "ep_combine_expand", "ep_dispatch_normal", "ep_combine_normal",
             "ep_group_limited_topk", "ep_strerror", "ep_probe_e4m3fn")
 EP_MAX_GROUPS = 64
+EP_GATE_MAX_SOFTMAX = 0
+EP_GATE_SUM_SIGMOID = 1
 EP_MAX_ALIGNMENT = 1024
 
 
@@ -94,7 +97,7 @@ def lib() -> ctypes.CDLL:
         L.ep_combine_expand.argtypes = [sp] + [vp] * 9
         L.ep_dispatch_normal.argtypes = [sp] + [vp] * 11
         L.ep_combine_normal.argtypes = [sp] + [vp] * 8
-        L.ep_group_limited_topk.argtypes = [sp, ctypes.c_int32, ctypes.c_int32] + [vp] * 4
+        L.ep_group_limited_topk.argtypes = [sp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32] + [vp] * 4
         L.ep_probe_e4m3fn.argtypes = [vp, vp, vp, i64, vp]
         L.ep_strerror.argtypes = [ctypes.c_int]
         L.ep_strerror.restype = ctypes.c_char_p
@@ -368,14 +371,15 @@ def ep_combine(shape: ep_shape, expert_out: torch.Tensor, topk_idx: torch.Tensor
         raise EpError(rc, "ep_combine")
 
 
-def ep_group_limited_topk(shape: ep_shape, num_groups: int, topk_groups: int,
+def ep_group_limited_topk(shape: ep_shape, num_groups: int, topk_groups: int, rule: int,
                           scores: torch.Tensor, topk_idx: torch.Tensor,
                           topk_weights: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Group-limited top-k gating; see ``ep_group_limited_topk`` in include/ep.h."""
+    """Group-limited top-k gating under ``rule`` (EP_GATE_MAX_SOFTMAX or
+    EP_GATE_SUM_SIGMOID); see ``ep_group_limited_topk`` in include/ep.h."""
     N, E, K = shape.num_tokens, shape.num_experts, shape.num_topk
     rc = lib().ep_group_limited_topk(
         ctypes.byref(shape), ctypes.c_int32(int(num_groups)), ctypes.c_int32(int(topk_groups)),
-        _ptr(scores, "scores", _F32, N * E), _ptr(topk_idx, "topk_idx", _I64, N * K),
+        ctypes.c_int32(int(rule)), _ptr(scores, "scores", _F32, N * E), _ptr(topk_idx, "topk_idx", _I64, N * K),
         _ptr(topk_weights, "topk_weights", _F32, N * K), _stream(stream, topk_idx))
     if rc != EP_OK:
         raise EpError(rc, "ep_group_limited_topk")
@@ -453,6 +457,18 @@ def allocate(shape: ep_shape, device="cuda", parts=("layout", "dispatch", "combi
 
 
 # ---- the path in three calls, allocating with torch --------------------------
+def _on_stream(stream):
+    """Context in which torch allocates (and fills) on the stream the library
+    launches on, so the caching allocator orders every reuse of these blocks
+    after the launches that use them: ``stream`` may be None (torch's current
+    stream), a torch stream, or a raw hipStream_t handle."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream))
+    return torch.cuda.stream(stream)
+
+
 @dataclasses.dataclass
 class Handle:
     """The layout of one routing, reused by its dispatch and combine (the
@@ -481,16 +497,18 @@ def layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: int,
            expert_capacity: Optional[int] = None, expert_alignment: int = 0,
            stream=None) -> Handle:
     """``ep_layout`` on a [N, K] int64 routing (-1 = masked), outputs allocated
-    here.  M defaults to N and the expert capacity S to M."""
+    here on ``stream`` (torch's current stream when None).  M defaults to N
+    and the expert capacity S to M."""
     N, K = topk_idx.shape
     M = max(N, 1) if num_max_dispatch_tokens_per_rank is None else num_max_dispatch_tokens_per_rank
     S = M if expert_capacity is None else expert_capacity
     # the layout reads no activations: any valid hidden size will do here
     shape = make_shape(N, 8, K, num_experts, num_ranks, M, S, False, EP_SCALE_FP32, expert_alignment)
-    b = allocate(shape, topk_idx.device, parts=("layout",))
-    ep_layout(shape, topk_idx, b["num_tokens_per_rank"], b["num_tokens_per_expert"],
-              b["is_token_in_rank"], b["expert_slot"], b["rank_slot"], b["expert_offset"],
-              b["workspace"], b["status"], stream=stream)
+    with _on_stream(stream):
+        b = allocate(shape, topk_idx.device, parts=("layout",))
+        ep_layout(shape, topk_idx, b["num_tokens_per_rank"], b["num_tokens_per_expert"],
+                  b["is_token_in_rank"], b["expert_slot"], b["rank_slot"], b["expert_offset"],
+                  b["workspace"], b["status"], stream=stream)
     return Handle(shape, topk_idx, b["num_tokens_per_rank"], b["num_tokens_per_expert"],
                   b["is_token_in_rank"], b["expert_slot"], b["rank_slot"], b["expert_offset"],
                   b["status"])
@@ -500,12 +518,13 @@ def dispatch(x: torch.Tensor, handle: Handle, use_fp8: bool = True,
              scale_format: int = EP_SCALE_FP32, stream=None):
     """``ep_dispatch`` of bf16 ``x`` [N, H] by a layout's handle.  Returns
     (recv_x [E, S, H] as float8_e4m3fn or bfloat16, recv_scales [E, S, H/128]
-    fp32 (int32 words for UE8M0) or None, recv_src_idx [E, S]); rows at or past
-    num_tokens_per_expert[e] are unwritten."""
+    fp32 (int32 words for UE8M0) or None, recv_src_idx [E, S]), allocated on
+    ``stream``; rows at or past num_tokens_per_expert[e] are unwritten."""
     shape = handle.with_hidden(x.shape[1], use_fp8, scale_format)
-    b = allocate(shape, x.device, parts=("dispatch",))
-    ep_dispatch(shape, x, handle.topk_idx, handle.expert_slot, b["recv_x"], b["recv_scales"],
-                b["recv_src_idx"], handle.status, stream=stream)
+    with _on_stream(stream):
+        b = allocate(shape, x.device, parts=("dispatch",))
+        ep_dispatch(shape, x, handle.topk_idx, handle.expert_slot, b["recv_x"], b["recv_scales"],
+                    b["recv_src_idx"], handle.status, stream=stream)
     recv_x = b["recv_x"].view(torch.float8_e4m3fn if use_fp8 else torch.bfloat16)
     return recv_x, b["recv_scales"], b["recv_src_idx"]
 
@@ -513,10 +532,16 @@ def dispatch(x: torch.Tensor, handle: Handle, use_fp8: bool = True,
 def combine(expert_out: torch.Tensor, handle: Handle, topk_weights: torch.Tensor,
             bias: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """``ep_combine`` of bf16 expert outputs [E, S, H] by a layout's handle:
-    returns the [N, H] bfloat16 weighted sums in token order (plus ``bias``)."""
+    returns the [N, H] bfloat16 weighted sums in token order (plus ``bias``),
+    allocated on ``stream``."""
+    s = handle.shape
+    if expert_out.dim() != 3 or tuple(expert_out.shape[:2]) != (s.num_experts, s.expert_capacity):
+        raise ValueError(f"expert_out has shape {tuple(expert_out.shape)}, expected "
+                         f"[{s.num_experts}, {s.expert_capacity}, H]")
     shape = handle.with_hidden(expert_out.shape[-1])
-    out = torch.empty((shape.num_tokens, shape.hidden), dtype=torch.bfloat16,
-                      device=expert_out.device)
-    ep_combine(shape, expert_out, handle.topk_idx, topk_weights, handle.expert_slot, out,
-               handle.status, stream=stream, bias=bias)
+    with _on_stream(stream):
+        out = torch.empty((shape.num_tokens, shape.hidden), dtype=torch.bfloat16,
+                          device=expert_out.device)
+        ep_combine(shape, expert_out, handle.topk_idx, topk_weights, handle.expert_slot, out,
+                   handle.status, stream=stream, bias=bias)
     return out

@@ -27,7 +27,8 @@ workload, drawn in this order: x, routing, weight logits, mask, expert rows):
 * uniform routing: K distinct experts per token, the first K of a random
   permutation (argsort of uniform keys);
 * group-limited routing: scores s ~ N(0, 1) [N, E]; group g holds experts
-  [g E/G, (g+1) E/G); a group's score is the sum of its experts' scores; the
+  [g E/G, (g+1) E/G); a group's score is the binary32 sum of its experts'
+  scores in ascending expert index from +0; the
   top-4 groups are kept, then the top-K experts by s among them (stable
   order, lowest index first on ties); weights = sigmoid(s_sel) normalised to
   sum 1;
@@ -109,7 +110,12 @@ def _uniform_routing(rng, n, e, k):
 
 def _group_limited_routing(rng, n, e, k, groups, topk_groups):
     s = rng.standard_normal((n, e), dtype=np.float32)
-    gscore = s.reshape(n, groups, e // groups).sum(axis=2)
+    # a group's score: binary32 sum of its experts' scores in ascending expert
+    # index, from +0 (a fixed order, so every consumer ranks groups alike)
+    per = s.reshape(n, groups, e // groups)
+    gscore = np.zeros((n, groups), dtype=np.float32)
+    for i in range(e // groups):
+        gscore = gscore + per[:, :, i]
     top_groups = np.argsort(-gscore, axis=1, kind="stable")[:, :topk_groups]
     allowed = np.zeros((n, groups), dtype=bool)
     np.put_along_axis(allowed, top_groups, True, axis=1)
@@ -119,7 +125,7 @@ def _group_limited_routing(rng, n, e, k, groups, topk_groups):
     sel = np.take_along_axis(s, idx, axis=1).astype(np.float64)
     sig = 1.0 / (1.0 + np.exp(-sel))
     w = (sig / sig.sum(axis=1, keepdims=True)).astype(np.float32)
-    return idx, w
+    return idx, w, s
 
 
 def _zipf_routing(rng, n, e, k, s_exp):
@@ -134,7 +140,9 @@ def make_inputs(w: Workload, seed: Optional[int] = None, with_expert_rows: bool 
 
     Returns a dict with ``x_bits`` (uint16 [N, H], bf16 patterns),
     ``topk_idx`` (int64 [N, K], -1 = masked), ``topk_weights`` (float32
-    [N, K]), ``num_valid`` (number of entries that are not -1) and, when
+    [N, K]), ``num_valid`` (number of entries that are not -1), for
+    group-limited routing ``router_scores`` (float32 [N, E], the scores the
+    routing was drawn from) and, when
     ``with_expert_rows``, ``expert_rows`` (uint16 [P, H], one bf16 row per
     valid entry in (t, k) order)."""
     rng = np.random.default_rng(1000 + w.wid if seed is None else seed)
@@ -144,7 +152,8 @@ def make_inputs(w: Workload, seed: Optional[int] = None, with_expert_rows: bool 
         topk_idx = _uniform_routing(rng, n, e, k)
         weights = _softmax_f32(rng.standard_normal((n, k), dtype=np.float32))
     elif w.routing == "group_limited":
-        topk_idx, weights = _group_limited_routing(rng, n, e, k, w.num_groups, w.topk_groups)
+        topk_idx, weights, scores = _group_limited_routing(rng, n, e, k, w.num_groups,
+                                                           w.topk_groups)
     elif w.routing == "zipf":
         topk_idx = _zipf_routing(rng, n, e, k, w.zipf_s)
         weights = _softmax_f32(rng.standard_normal((n, k), dtype=np.float32))
@@ -160,6 +169,8 @@ def make_inputs(w: Workload, seed: Optional[int] = None, with_expert_rows: bool 
         "topk_weights": np.ascontiguousarray(weights),
         "num_valid": int((topk_idx >= 0).sum()),
     }
+    if w.routing == "group_limited":
+        out["router_scores"] = scores
     if with_expert_rows:
         out["expert_rows"] = bf16_bits(rng.standard_normal((out["num_valid"], h), dtype=np.float32))
     return out

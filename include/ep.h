@@ -359,6 +359,15 @@ int ep_combine_normal(const ep_shape *shape, const uint16_t *x, const int32_t *r
                       const float *recv_topk_weights, const uint16_t *bias, uint16_t *combined_x,
                       float *combined_topk_weights, uint32_t *status, void *stream);
 
+/* Rules of ep_group_limited_topk: how a group is scored and how the picks
+ * are weighted. */
+#define EP_GATE_MAX_SOFTMAX 0 /* group score = its best expert's score;
+                                 weights = softmax of the picked scores   */
+#define EP_GATE_SUM_SIGMOID 1 /* group score = binary32 sum of its experts'
+                                 scores, ascending expert index, from +0;
+                                 weights = sigmoids of the picked scores
+                                 normalised to sum 1                       */
+
 /* Group-limited top-k gating, the step that produces topk_idx for
  * ep_layout ([V1] §1 and §2.1: the normal kernels serve group-limited
  * gating, benchmarked with top-4 groups then top-8 experts; [L14] §3 Q3: a
@@ -367,20 +376,25 @@ int ep_combine_normal(const ep_shape *shape, const uint16_t *x, const int32_t *r
  *
  * In:  shape (num_tokens N, num_experts E, num_topk K are used; the rest is
  *      validated as for the other entry points); scores [N, E] fp32 router
- *      scores, finite; num_groups G in [1, EP_MAX_GROUPS] with E % G == 0:
- *      group g holds experts [g*E/G, (g+1)*E/G); topk_groups TG in [1, G];
- *      K <= TG * E/G.
- * Out: topk_idx [N, K] int64: per token, a group's score is its best
- *        expert's score; the TG best groups are kept (ties: lower group
- *        index); the K best experts of the kept groups, best first (ties:
- *        lower expert index);
- *      topk_weights [N, K] fp32 (nullable): exp(s_k - s_0) / sum_j exp(s_j -
- *        s_0) over the K picks (fp32 expf and division; the picks are exact).
- * Errors: EP_ERR_SHAPE for G, TG or K outside the rules above,
+ *      scores, finite (and, for EP_GATE_SUM_SIGMOID, with finite group
+ *      sums); num_groups G in [1, EP_MAX_GROUPS] with E % G == 0: group g
+ *      holds experts [g*E/G, (g+1)*E/G); topk_groups TG in [1, G];
+ *      K <= TG * E/G; rule EP_GATE_MAX_SOFTMAX or EP_GATE_SUM_SIGMOID.
+ * Out: topk_idx [N, K] int64: per token, each group gets the rule's score
+ *        (EP_GATE_MAX_SOFTMAX: the best expert's score, exact;
+ *        EP_GATE_SUM_SIGMOID: acc = +0; for the group's experts in ascending
+ *        index acc = RN(acc + s), the binary32 sum in that order); the TG
+ *        best groups are kept (ties: lower group index); the K best experts
+ *        of the kept groups, best first (ties: lower expert index);
+ *      topk_weights [N, K] fp32 (nullable), over the K picks s_0..s_{K-1}:
+ *        EP_GATE_MAX_SOFTMAX exp(s_k - s_0) / sum_j exp(s_j - s_0);
+ *        EP_GATE_SUM_SIGMOID sig(s_k) / sum_j sig(s_j), sig(v) = 1/(1+exp(-v))
+ *        (fp32 expf and division; the picks are exact).
+ * Errors: EP_ERR_SHAPE for G, TG, K or rule outside the rules above,
  * EP_ERR_UNSUPPORTED for G > EP_MAX_GROUPS. */
 int ep_group_limited_topk(const ep_shape *shape, int32_t num_groups, int32_t topk_groups,
-                          const float *scores, int64_t *topk_idx, float *topk_weights,
-                          void *stream);
+                          int32_t rule, const float *scores, int64_t *topk_idx,
+                          float *topk_weights, void *stream);
 
 /* Host only.  A static string naming a return code. */
 const char *ep_strerror(int code);

@@ -32,6 +32,9 @@ STATUS_BAD_EXPERT_ID = 1
 STATUS_BAD_SLOT = 2
 STATUS_BAD_ARGS = 4
 
+GATE_MAX_SOFTMAX = 0
+GATE_SUM_SIGMOID = 1
+
 
 def build(source: str = SOURCE, output: str = LIBRARY) -> str:
     """Compile the oracle with gcc into a shared library and return its path."""
@@ -76,7 +79,7 @@ class Oracle:
         lib.oracle_dispatch_normal.restype = ctypes.c_int
         lib.oracle_combine_normal.argtypes = [i32] * 5 + [vp] * 6
         lib.oracle_combine_normal.restype = ctypes.c_int
-        lib.oracle_group_limited_topk.argtypes = [i32] * 5 + [vp] * 3
+        lib.oracle_group_limited_topk.argtypes = [i32] * 6 + [vp] * 3
         lib.oracle_group_limited_topk.restype = ctypes.c_int
         self.lib = lib
 
@@ -259,17 +262,20 @@ class Oracle:
         return out, cw, int(st)
 
     def group_limited_topk(self, scores: np.ndarray, num_groups: int, topk_groups: int,
-                           num_topk: int):
+                           num_topk: int, rule: int = 0):
         """Group-limited top-k gating (DeepEP V1 Legacy guide §1 and §2.1;
-        Lesson 14 §3 Q3 and exercise).  ``scores`` float32 [N, E].  Returns
-        (topk_idx int64 [N, K], topk_weights float32 [N, K], status)."""
+        Lesson 14 §3 Q3 and exercise).  ``scores`` float32 [N, E]; ``rule``
+        GATE_MAX_SOFTMAX (group score = best expert, softmax weights) or
+        GATE_SUM_SIGMOID (group score = ordered binary32 sum, normalised
+        sigmoid weights).  Returns (topk_idx int64 [N, K], topk_weights
+        float32 [N, K], status)."""
         sc = np.ascontiguousarray(scores, dtype=np.float32)
         n, e = sc.shape
         k = int(num_topk)
         idx = np.empty((n, k), np.int64)
         w = np.empty((n, k), np.float32)
         st = self.lib.oracle_group_limited_topk(n, e, int(num_groups), int(topk_groups), k,
-                                                _ptr(sc), _ptr(idx), _ptr(w))
+                                                int(rule), _ptr(sc), _ptr(idx), _ptr(w))
         return idx, w, int(st)
 
     def quantize_rows_pow2(self, x_bits: np.ndarray):

@@ -746,25 +746,41 @@ int oracle_combine_normal(int32_t N, int32_t H, int32_t K, int32_t R, int32_t M,
 
 /* ---------------------------------------------------------------- gating */
 
+#define ORACLE_GATE_MAX_SOFTMAX 0
+#define ORACLE_GATE_SUM_SIGMOID 1
+
 /* Group-limited top-k gating, the step before the layout ([V1] §1 and §2.1:
  * the normal kernels serve group-limited gating, benchmarked as top-4 groups
- * then top-8 experts; [L14] §3 Q3: each token reaches at most 4 nodes;
- * [L14] exercise: the gating weights are normalised softmax weights).
+ * then top-8 experts; [L14] §3 Q3: each token reaches at most 4 nodes).
  *
  * Experts are split into G groups of L = E / G consecutive experts.  Per
- * token t, with router scores s[t, 0..E-1]:
- *   group score gs[g] = max of s over the group's experts (exact);
- *   keep the TG groups with the largest gs (ties: the lower group index);
+ * token t, with router scores s[t, 0..E-1], under one of two rules:
+ *   ORACLE_GATE_MAX_SOFTMAX: a group's score is the largest score of its
+ *     experts (exact); the weights are the softmax of the picked scores
+ *     ([L14] exercise: normalised softmax gating weights);
+ *   ORACLE_GATE_SUM_SIGMOID: a group's score is the binary32 sum of its
+ *     experts' scores taken in ascending expert index from +0, each addition
+ *     rounded to nearest even (the order is part of the definition, so both
+ *     sides rank the groups identically); the weights are the sigmoids of
+ *     the picked scores normalised to sum 1 (the prefill benchmark routing:
+ *     top-4 groups by summed scores, then top-8 experts).
+ * Then, for both rules:
+ *   keep the TG groups with the largest group score (ties: the lower group
+ *     index);
  *   topk_idx[t, 0..K-1] = the K experts of the kept groups with the largest
  *     s, in that order (ties: the lower expert index);
- *   topk_weights[t, k] = exp(s_k - s_0) / sum_j exp(s_j - s_0) over the K
- *     picks (softmax of the picked scores; evaluated in double, then rounded
- *     to float).
- * Needs 1 <= TG <= G, E % G == 0 and K <= TG * L.  Scores are finite. */
+ *   topk_weights[t, k]: MAX_SOFTMAX exp(s_k - s_0) / sum_j exp(s_j - s_0);
+ *     SUM_SIGMOID sig(s_k) / sum_j sig(s_j), sig(v) = 1 / (1 + exp(-v));
+ *     both evaluated in double over the K picks, then rounded to float.
+ * Needs 1 <= TG <= G, E % G == 0, K <= TG * L and a known rule.  Scores and
+ * group sums are finite. */
 int oracle_group_limited_topk(int32_t N, int32_t E, int32_t G, int32_t TG, int32_t K,
-                              const float *scores, int64_t *topk_idx, float *topk_weights)
+                              int32_t rule, const float *scores, int64_t *topk_idx,
+                              float *topk_weights)
 {
     if (N < 0 || E < 1 || G < 1 || E % G != 0 || TG < 1 || TG > G || K < 1 || K > TG * (E / G))
+        return ORACLE_BAD_ARGS;
+    if (rule != ORACLE_GATE_MAX_SOFTMAX && rule != ORACLE_GATE_SUM_SIGMOID)
         return ORACLE_BAD_ARGS;
     const int32_t L = E / G;
     float *gs = (float *)malloc(sizeof(float) * (size_t)G);
@@ -781,10 +797,17 @@ int oracle_group_limited_topk(int32_t N, int32_t E, int32_t G, int32_t TG, int32
     for (int32_t t = 0; t < N; ++t) {
         const float *st = scores + (size_t)t * E;
         for (int32_t g = 0; g < G; ++g) {
-            gs[g] = st[g * L];
-            for (int32_t i = 1; i < L; ++i)
-                if (st[g * L + i] > gs[g])
-                    gs[g] = st[g * L + i];
+            if (rule == ORACLE_GATE_MAX_SOFTMAX) {
+                gs[g] = st[g * L];
+                for (int32_t i = 1; i < L; ++i)
+                    if (st[g * L + i] > gs[g])
+                        gs[g] = st[g * L + i];
+            } else {
+                float acc = 0.0f;
+                for (int32_t i = 0; i < L; ++i)
+                    acc = acc + st[g * L + i];
+                gs[g] = acc;
+            }
             kept[g] = 0;
         }
         for (int32_t n = 0; n < TG; ++n) {
@@ -807,7 +830,8 @@ int oracle_group_limited_topk(int32_t N, int32_t E, int32_t G, int32_t TG, int32
         double sum = 0.0;
         const double top = st[topk_idx[(size_t)t * K]];
         for (int32_t k = 0; k < K; ++k) {
-            z[k] = exp((double)st[topk_idx[(size_t)t * K + k]] - top);
+            const double v = st[topk_idx[(size_t)t * K + k]];
+            z[k] = rule == ORACLE_GATE_MAX_SOFTMAX ? exp(v - top) : 1.0 / (1.0 + exp(-v));
             sum += z[k];
         }
         for (int32_t k = 0; k < K; ++k)

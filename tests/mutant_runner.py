@@ -51,6 +51,9 @@ def main(path: str) -> int:
         ("gating_golden", lambda: pins.pin_gating_golden(o)),
         ("gating_special_cases", lambda: pins.pin_gating_special_cases(o)),
         ("gating_invariants", lambda: pins.pin_gating_invariants(o)),
+        ("gating_sum_golden", lambda: pins.pin_gating_sum_golden(o)),
+        ("gating_sum_special_cases", lambda: pins.pin_gating_sum_special_cases(o)),
+        ("gating_bad_args", lambda: pins.pin_gating_bad_args(o)),
         ("layout_bruteforce", lambda: pins.pin_layout_bruteforce(o)),
     ]
     for name, fn in steps:

@@ -20,6 +20,9 @@ import os
 import numpy as np
 import torch
 
+GATE_MAX_SOFTMAX = 0  # group score = best expert, softmax weights
+GATE_SUM_SIGMOID = 1  # group score = ordered binary32 sum, normalised sigmoid weights
+
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
@@ -964,7 +967,78 @@ def pin_gating_invariants(o):
             _check_softmax(sc, idx, w)
 
 
+def _check_sigmoid(scores, idx, w):
+    """Weights are the picks' sigmoids normalised to 1: scipy's logistic
+    function (a library routine) in float64."""
+    from scipy.special import expit
+
+    z = expit(np.take_along_axis(scores.astype(np.float64), idx, axis=1))
+    ref = z / z.sum(axis=1, keepdims=True)
+    assert np.allclose(w, ref, rtol=0, atol=2e-7), "weights are not the normalised sigmoids"
+
+
+def pin_gating_sum_golden(o):
+    """Hand-worked picks and weights under the summed-score rule
+    (``tests/golden/group_limited_topk_sum.json``): the sums and the maxima
+    keep different groups; 2^24 + 1 rounds back to 2^24, so the ascending
+    binary32 order (not the exact sum, nor a descending order) decides which
+    group is kept."""
+    with open(os.path.join(GOLDEN, "group_limited_topk_sum.json")) as f:
+        g = json.load(f)
+    sc = np.array(g["scores"], np.float32)
+    idx, w, st = o.group_limited_topk(sc, g["num_groups"], g["topk_groups"], g["num_topk"],
+                                      GATE_SUM_SIGMOID)
+    assert st == 0
+    assert idx.tolist() == g["topk_idx"], idx.tolist()
+    assert np.allclose(w, np.array(g["topk_weights"]), rtol=0, atol=1e-7), w.tolist()
+
+
+def pin_gating_sum_special_cases(o):
+    """One expert per group (G = E): a group's sum is its one score, so the
+    sum rule picks exactly what the maximum rule picks, and with TG = K both
+    are plain top-k by library sort.  Small integer scores make every group
+    sum exact, so the kept groups are those with the largest float64 sums
+    (library sort, ties to the lower group) and the picks the K largest of
+    their experts (library sort); weights are the normalised sigmoids."""
+    rng = np.random.default_rng(37)
+    for E, K in ((256, 8), (64, 6), (16, 5)):
+        sc = rng.standard_normal((40, E)).astype(np.float32)
+        i_sum, w_sum, st = o.group_limited_topk(sc, E, K, K, GATE_SUM_SIGMOID)
+        i_max, _, _ = o.group_limited_topk(sc, E, K, K, GATE_MAX_SOFTMAX)
+        assert st == 0 and np.array_equal(i_sum, i_max) and np.array_equal(i_sum, _plain_topk(sc, K))
+        _check_sigmoid(sc, i_sum, w_sum)
+    for E, G, TG, K in ((256, 8, 4, 8), (64, 16, 2, 5), (128, 4, 1, 12), (96, 3, 2, 7)):
+        L = E // G
+        sc = rng.integers(-6, 7, size=(60, E)).astype(np.float32)
+        idx, w, st = o.group_limited_topk(sc, G, TG, K, GATE_SUM_SIGMOID)
+        assert st == 0
+        gsum = sc.astype(np.float64).reshape(-1, G, L).sum(axis=2)
+        keep = _plain_topk(gsum, TG)
+        for t in range(sc.shape[0]):
+            cand = np.concatenate([np.arange(g * L, (g + 1) * L) for g in sorted(keep[t])])
+            masked = np.full(E, -np.inf, np.float64)
+            masked[cand] = sc[t, cand]
+            assert np.array_equal(idx[t], _plain_topk(masked[None, :], K)[0]), (E, G, TG, K, t)
+        _check_sigmoid(sc, idx, w)
+
+
+def pin_prefill_routing_is_sum_gating(o):
+    """The prefill workload's routing (drawn by the input generator's own
+    group-limited selection on summed scores) is exactly what the oracle's
+    sum rule picks from the same router scores, with the same weights."""
+    from combine_ep_layout_02_amd import workloads as W
+
+    w = W.WORKLOADS[3]
+    inp = W.make_inputs(w.scaled(w.num_tokens, 128))
+    idx, wts, st = o.group_limited_topk(inp["router_scores"], w.num_groups, w.topk_groups,
+                                        w.num_topk, GATE_SUM_SIGMOID)
+    assert st == 0 and np.array_equal(idx, inp["topk_idx"])
+    assert np.allclose(wts, inp["topk_weights"], rtol=0, atol=1e-7)
+
+
 def pin_gating_bad_args(o):
     sc = np.zeros((2, 16), np.float32)
     for G, TG, K in ((5, 2, 2), (4, 0, 2), (4, 5, 2), (4, 1, 5), (4, 2, 0)):
         assert o.group_limited_topk(sc, G, TG, K)[2] == 4, (G, TG, K)
+    for rule in (-1, 2):
+        assert o.group_limited_topk(sc, 4, 2, 2, rule)[2] == 4, rule

@@ -344,7 +344,8 @@ def test_gating_argument_checks():
     """ep_group_limited_topk: group rules are checked before any launch."""
     s = _shape(num_experts=16, num_ranks=4, num_topk=4)
     lib = ep.lib()
-    call = lambda sh, G, TG, *p: lib.ep_group_limited_topk(ctypes.byref(sh), G, TG, *p, None)
+    call = lambda sh, G, TG, *p, rule=0: lib.ep_group_limited_topk(ctypes.byref(sh), G, TG, rule,
+                                                                       *p, None)
     for G, TG, code in ((5, 2, ep.EP_ERR_SHAPE), (0, 1, ep.EP_ERR_SHAPE), (4, 0, ep.EP_ERR_SHAPE),
                         (4, 5, ep.EP_ERR_SHAPE), (8, 1, ep.EP_ERR_SHAPE),  # K=4 > 1 * 16/8
                         (128, 1, ep.EP_ERR_UNSUPPORTED)):
@@ -355,3 +356,19 @@ def test_gating_argument_checks():
     assert call(s, 4, 2, OK16, ctypes.c_void_p(0x1004), OK16) == ep.EP_ERR_ALIGN
     assert call(s, 4, 2, OK16, OK16, BAD) == ep.EP_ERR_ALIGN
     assert call(_shape(num_tokens=-1), 4, 2, OK16, OK16, OK16) == ep.EP_ERR_SHAPE
+    for rule in (-1, 2):
+        assert call(s, 4, 2, OK16, OK16, OK16, rule=rule) == ep.EP_ERR_SHAPE
+    assert call(s, 4, 2, None, OK16, OK16, rule=ep.EP_GATE_SUM_SIGMOID) == ep.EP_ERR_NULL
+
+
+def test_combine_helper_checks_expert_out_shape():
+    """ep.combine refuses expert outputs whose leading dims are not [E, S]
+    before any call into the library."""
+    import torch
+
+    s = ep.make_shape(4, 8, 2, 8, 2, 4, 4, False)
+    z = lambda *shape, dt=torch.int32: torch.zeros(shape, dtype=dt)
+    h = ep.Handle(s, z(4, 2, dt=torch.int64), z(2), z(8), z(4, 2, dt=torch.uint8), z(4, 2), z(4, 2),
+                  z(9), z(1))
+    with pytest.raises(ValueError):
+        ep.combine(torch.zeros((8, 5, 8), dtype=torch.bfloat16), h, torch.zeros((4, 2)))

@@ -181,7 +181,7 @@ def test_hip_graph_other_paths(o):
     out_n = torch.empty((N, H), dtype=torch.int16, device=dev)
 
     def step():
-        ep.ep_group_limited_topk(shape, 8, 4, scores, idx, wts)
+        ep.ep_group_limited_topk(shape, 8, 4, ep.EP_GATE_SUM_SIGMOID, scores, idx, wts)
         ep.ep_layout(shape, idx, buf["num_tokens_per_rank"], buf["num_tokens_per_expert"],
                      buf["is_token_in_rank"], buf["expert_slot"], buf["rank_slot"],
                      buf["expert_offset"], buf["workspace"], buf["status"])
@@ -239,7 +239,8 @@ def test_hip_graph_other_paths(o):
             assert np.array_equal(eager[key].view(np.uint8), replay[key].view(np.uint8)), (rep, key)
         assert int(buf["status"].item()) == 0
         # and the oracle on this replay's inputs
-        want_idx, _, _ = o.group_limited_topk(scores.cpu().numpy(), 8, 4, K)
+        want_idx, _, _ = o.group_limited_topk(scores.cpu().numpy(), 8, 4, K,
+                                             oracle.GATE_SUM_SIGMOID)
         assert np.array_equal(replay["idx"], want_idx)
         lay = o.layout(want_idx, E, R, alignment=128)
         assert np.array_equal(replay["off"], lay["expert_offset"])

@@ -612,3 +612,52 @@ def test_three_call_api(o, wid):
     got = out.view(torch.int16).cpu().numpy().view(np.uint16)
     assert out.dtype == torch.bfloat16 and np.array_equal(got, want)
     assert int(handle.status.item()) == (lay["status"] | st | st_c)
+
+
+def test_three_call_api_side_stream_with_workspace(o):
+    """ep.layout / ep.dispatch / ep.combine on a stream that is not torch's
+    current one, at a batch whose layout needs the histogram workspace (700
+    tokens: three count blocks).  The binding allocates on that stream, so the
+    caching allocator cannot hand a block the launches still use to other
+    work; the current stream is kept busy meanwhile to give a misordered
+    allocation the chance to show."""
+    w = W.WORKLOADS[3].scaled(700, 1024)
+    inp = W.make_inputs(w, seed=4242, with_expert_rows=True)
+    E, S, H, R = w.num_experts, w.expert_capacity, w.hidden, w.num_ranks
+    assert ep.ep_query_sizes(ep.shape_of(w))["layout_workspace"] > 0
+    side = torch.cuda.Stream()
+    idx = dev(inp["topk_idx"])
+    x = dev(inp["x_bits"]).view(torch.bfloat16)
+    wts = dev(inp["topk_weights"])
+    lay = o.layout(inp["topk_idx"], E, R)
+    y = place_expert_rows(inp["expert_rows"], inp["topk_idx"], lay["expert_slot"], E, S, H)
+    side.wait_stream(torch.cuda.current_stream())
+    busy = torch.empty(1 << 26, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        handle = ep.layout(idx, E, R, w.num_max_dispatch_tokens_per_rank, S, stream=side)
+        # work on the current stream that allocates and writes while the side
+        # stream runs
+        for _ in range(4):
+            busy.add_(1.0)
+            torch.full((1 << 20,), -7, dtype=torch.int32, device="cuda")
+        recv_x, recv_scales, recv_src = ep.dispatch(x, handle, use_fp8=True, stream=side)
+        out = ep.combine(y.view(torch.bfloat16), handle, wts, stream=side)
+        side.synchronize()
+        for key in ("num_tokens_per_rank", "num_tokens_per_expert", "expert_slot", "rank_slot",
+                    "is_token_in_rank"):
+            assert np.array_equal(host(getattr(handle, key)), lay[key]), key
+        cnt = lay["num_tokens_per_expert"]
+        s_or = oracle_capacity(cnt, S)
+        rx, rs, src, st = o.pack(inp["x_bits"], inp["topk_idx"], lay["expert_slot"], E, s_or, True)
+        got_x = recv_x.view(torch.uint8).cpu().numpy()
+        got_src = host(recv_src)
+        got_sc = host(recv_scales).view(np.int32)
+        for e in range(E):
+            c = int(cnt[e])
+            assert np.array_equal(got_x[e, :c], rx[e, :c]), e
+            assert np.array_equal(got_src[e, :c], src[e, :c]), e
+            assert np.array_equal(got_sc[e, :c], rs[e, :c].view(np.int32)), e
+        y_or = pins.place_rows(inp["expert_rows"], inp["topk_idx"], lay["expert_slot"], E, s_or)
+        want, st_c = o.combine(y_or, inp["topk_idx"], inp["topk_weights"], lay["expert_slot"], E, s_or)
+        assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), want)
+        assert int(handle.status.item()) == 0

@@ -97,8 +97,17 @@ MUTANTS = [
     ("bias_overwrites", [("acc[c] = acc[c] + oracle_bf16_to_f32(bias_row[c]);",
                           "acc[c] = oracle_bf16_to_f32(bias_row[c]);")]),
     # group-limited gating
-    ("gating_group_sum", [("                if (st[g * L + i] > gs[g])\n                    gs[g] = st[g * L + i];",
-                           "                gs[g] = gs[g] + st[g * L + i];")]),
+    ("gating_group_sum", [("                    if (st[g * L + i] > gs[g])\n                        gs[g] = st[g * L + i];",
+                           "                    gs[g] = gs[g] + st[g * L + i];")]),
+    ("gating_sum_descending", [("for (int32_t i = 0; i < L; ++i)\n                    acc = acc + st[g * L + i];",
+                                "for (int32_t i = L - 1; i >= 0; --i)\n                    acc = acc + st[g * L + i];")]),
+    ("gating_sum_in_double", [("float acc = 0.0f;\n                for (int32_t i = 0; i < L; ++i)\n                    acc = acc + st[g * L + i];\n                gs[g] = acc;",
+                               "double acc = 0.0;\n                for (int32_t i = 0; i < L; ++i)\n                    acc = acc + st[g * L + i];\n                gs[g] = (float)acc;")]),
+    ("gating_sum_is_max", [("                    acc = acc + st[g * L + i];",
+                            "                    acc = (i == 0 || st[g * L + i] > acc) ? st[g * L + i] : acc;")]),
+    ("gating_sum_rule_softmax", [("z[k] = rule == ORACLE_GATE_MAX_SOFTMAX ? exp(v - top) : 1.0 / (1.0 + exp(-v));",
+                                  "z[k] = exp(v - top);")]),
+    ("gating_sigmoid_sign", [("1.0 / (1.0 + exp(-v))", "1.0 / (1.0 + exp(v))")]),
     ("gating_group_ties_high", [("if (!kept[g] && (best < 0 || gs[g] > gs[best]))",
                                  "if (!kept[g] && (best < 0 || gs[g] >= gs[best]))")]),
     ("gating_expert_ties_high", [("if (kept[e / L] && !taken[e] && (best < 0 || st[e] > st[best]))",

@@ -192,3 +192,9 @@ def test_gating_special_cases(o):
 def test_gating_invariants(o):
     pins.pin_gating_invariants(o)
     pins.pin_gating_bad_args(o)
+
+
+def test_gating_sum_rule(o):
+    pins.pin_gating_sum_golden(o)
+    pins.pin_gating_sum_special_cases(o)
+    pins.pin_prefill_routing_is_sum_gating(o)
