@@ -791,40 +791,73 @@ def time_scale_formats(wid, steps, scrub_bytes, say, batch=10):
     return out
 
 
-def cpu_baseline(inp, w, reps, say):
-    """The CPU oracle as it stands (single-threaded C through its ctypes
-    wrapper, allocation of its output arrays included) on the same inputs."""
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+CPU_BASELINE_WORKLOADS = (1, 2, 3, 5, 4)
+
+
+def cpu_baseline(reps, say, workloads=CPU_BASELINE_WORKLOADS):
+    """The CPU oracle as it stands (plain single-threaded C) on each
+    workload's own inputs: layout, pack and combine, each timed inside the C
+    library on buffers allocated beforehand, so allocation is not in the
+    figures.  The combine reads identity-expert outputs (each routed row holds
+    its token's bf16 row, placed before timing).  Median of ``reps`` runs per
+    phase; one run for the 16,384-token workload, which takes seconds.  The
+    ``value`` is the prefill workload's GB/s at the sum of its phase
+    medians."""
     import oracle
+    from combine_ep_layout_02_amd import workloads as W
 
     o = oracle.get()
-    P = inp["num_valid"]
-    nbytes = algorithmic_bytes(w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks, P,
-                               w.use_fp8)["total"]
-    rng = np.random.default_rng(3000)
-    times = []
-    rows = None
-    for r in range(reps):
-        say(f"cpu oracle step {r + 1}/{reps}")
-        t0 = time.perf_counter()
-        lay = o.layout(inp["topk_idx"], w.num_experts, w.num_ranks)
-        s_or = max(1, int(lay["num_tokens_per_expert"].max()))
-        o.pack(inp["x_bits"], inp["topk_idx"], lay["expert_slot"], w.num_experts, s_or, w.use_fp8)
-        t1 = time.perf_counter()
-        if rows is None:  # expert outputs (input generation, not timed)
-            from combine_ep_layout_02_amd import workloads as W
-            rows = W.bf16_bits(rng.standard_normal((P, w.hidden), dtype=np.float32))
-            yv = np.zeros((w.num_experts, s_or, w.hidden), np.uint16)
-            valid = inp["topk_idx"] >= 0
-            yv[inp["topk_idx"][valid], lay["expert_slot"][valid]] = rows
-        t2 = time.perf_counter()
-        o.combine(yv, inp["topk_idx"], inp["topk_weights"], lay["expert_slot"], w.num_experts, s_or)
-        t3 = time.perf_counter()
-        times.append((t1 - t0) + (t3 - t2))
-    med = statistics.median(times)
-    return {"value": round(nbytes / med / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} full steps of {w.name} (layout + pack + combine, {w.num_tokens} tokens), "
-                      f"median {med * 1e3:.0f} ms per step, single-threaded C, "
-                      f"host has {os.cpu_count()} logical CPUs"}
+    per = {}
+    for wid in workloads:
+        w = W.WORKLOADS[wid]
+        say(f"cpu oracle {w.name}: inputs")
+        inp = W.make_inputs(w)
+        idx, x = inp["topk_idx"], inp["x_bits"]
+        lay = o.layout(idx, w.num_experts, w.num_ranks)
+        S = max(1, int(lay["num_tokens_per_expert"].max()))
+        y = np.zeros((w.num_experts, S, w.hidden), np.uint16)
+        for k in range(w.num_topk):
+            m = idx[:, k] >= 0
+            y[idx[m, k], lay["expert_slot"][m, k]] = x[m]
+        n = 1 if wid == 4 else reps
+        runs = []
+        for r in range(n):
+            say(f"cpu oracle {w.name}: run {r + 1}/{n}")
+            secs, st = o.timed_path(x, idx, inp["topk_weights"], y, w.num_experts, w.num_ranks, S,
+                                    w.use_fp8)
+            if st != 0:
+                raise RuntimeError(f"oracle status {st} on {w.name}")
+            runs.append(secs)
+        del y
+        med = [statistics.median(r[i] for r in runs) for i in range(3)]
+        nb = algorithmic_bytes(w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks,
+                               inp["num_valid"], w.use_fp8)
+        per[w.name] = {"layout_ms": round(med[0] * 1e3, 3), "pack_ms": round(med[1] * 1e3, 3),
+                       "combine_ms": round(med[2] * 1e3, 3),
+                       "step_ms": round(sum(med) * 1e3, 3), "runs": n,
+                       "gbps": round(nb["total"] / sum(med) / 1e9, 3)}
+    head_name = "prefill_4096x7168" if "prefill_4096x7168" in per else next(iter(per))
+    head = per[head_name]
+    return {"value": head["gbps"], "unit": "GB/s", "cores": 1, "threads": 1, "kind": "oracle",
+            "sample": f"every workload once through layout + pack + combine, median of {reps} runs "
+                      f"per phase (1 for large_16384x7168); the value is {head_name} "
+                      f"({head['step_ms']:.0f} ms per step); single-threaded C, phases timed "
+                      "inside the library on preallocated buffers",
+            "cpu_model": cpu_model(), "logical_cpus": os.cpu_count(), "per_workload": per}
 
 
 # The profiling commands whose outputs the summaries in profiles/ come from.
@@ -1091,7 +1124,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--scrub-mib", type=int, default=1024)
-    ap.add_argument("--cpu-reps", type=int, default=5)
+    ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-scale-formats", action="store_true",
@@ -1224,7 +1257,7 @@ def main():
         "extra": extra,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(prefill["inputs"], w, args.cpu_reps, say)
+        line["cpu_baseline"] = cpu_baseline(args.cpu_reps, say)
     print(json.dumps(line), flush=True)
 
 

@@ -80,6 +80,8 @@ class Oracle:
         lib.oracle_combine_normal.argtypes = [i32] * 5 + [vp] * 6
         lib.oracle_combine_normal.restype = ctypes.c_int
         lib.oracle_group_limited_topk.argtypes = [i32] * 6 + [vp] * 3
+        lib.oracle_timed_path.argtypes = [i32] * 7 + [vp] * 15
+        lib.oracle_timed_path.restype = ctypes.c_int
         lib.oracle_group_limited_topk.restype = ctypes.c_int
         self.lib = lib
 
@@ -319,6 +321,32 @@ class Oracle:
         st = self.lib.oracle_combine(n, h, k, int(num_experts), int(capacity), _ptr(y),
                                      _ptr(idx), _ptr(w), _ptr(slot), _ptr(b), _ptr(out))
         return out, int(st)
+
+    def timed_path(self, x_bits: np.ndarray, topk_idx: np.ndarray, topk_weights: np.ndarray,
+                   expert_out: np.ndarray, num_experts: int, num_ranks: int, capacity: int,
+                   use_fp8: bool):
+        """The path (layout, pack with fp32 scales, combine of ``expert_out``
+        [E, S, H] bf16 bits) on output buffers allocated here, beforehand;
+        each phase timed inside the C library.  Returns ((layout_s, pack_s,
+        combine_s), status)."""
+        x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
+        w = np.ascontiguousarray(topk_weights, dtype=np.float32)
+        y = np.ascontiguousarray(expert_out, dtype=np.uint16)
+        n, h = x.shape
+        k = idx.shape[1]
+        e, r, s = int(num_experts), int(num_ranks), int(capacity)
+        lay = [np.empty(r, np.int32), np.empty(e, np.int32), np.empty((n, r), np.uint8),
+               np.empty((n, k), np.int32), np.empty((n, r), np.int32), np.empty(e + 1, np.int32)]
+        recv_x = np.empty((e, s, h), np.uint8 if use_fp8 else np.uint16)
+        recv_scales = np.empty((e, s, h // 128), np.float32) if use_fp8 else None
+        recv_src = np.empty((e, s), np.int32)
+        out = np.empty((n, h), np.uint16)
+        secs = np.zeros(3, np.float64)
+        st = self.lib.oracle_timed_path(n, h, k, e, r, s, int(bool(use_fp8)), _ptr(x), _ptr(idx),
+                                        _ptr(w), _ptr(y), *[_ptr(a) for a in lay], _ptr(recv_x),
+                                        _ptr(recv_scales), _ptr(recv_src), _ptr(out), _ptr(secs))
+        return tuple(float(v) for v in secs), int(st)
 
     # ------------------------------------------------------------ formats
     def e4m3fn_encode(self, v: np.ndarray) -> np.ndarray:

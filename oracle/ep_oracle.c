@@ -36,10 +36,12 @@
  * every float operation below is one IEEE binary32 operation in the order
  * written.
  */
+#define _POSIX_C_SOURCE 200809L /* clock_gettime, for the timed path below */
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#include <time.h>
 
 #define ORACLE_OK 0
 #define ORACLE_BAD_EXPERT_ID 1 /* an id >= E or < -1 was seen (treated as -1) */
@@ -880,4 +882,43 @@ void oracle_quantize_rows_pow2(int32_t N, int32_t H, const uint16_t *x, uint8_t 
 {
     for (int32_t t = 0; t < N; ++t)
         oracle_quantize_row_pow2(H, x + (size_t)t * H, q + (size_t)t * H, exps + (size_t)t * (H / 128));
+}
+
+/* ------------------------------------------------ timed path (CPU baseline) */
+
+static double now_seconds(void)
+{
+    struct timespec ts;
+    clock_gettime(CLOCK_MONOTONIC, &ts);
+    return (double)ts.tv_sec + 1e-9 * (double)ts.tv_nsec;
+}
+
+/* The whole path -- layout, pack (FP32 scales), combine -- on buffers the
+ * caller allocated beforehand, each phase timed on its own with the
+ * monotonic clock (seconds[0..2] = layout, pack, combine), so the figures
+ * hold the oracle's arithmetic and memory traffic only, not allocation.
+ * expert_out [E, S, H] is the combine's input.  Returns the OR of the three
+ * statuses. */
+int oracle_timed_path(int32_t N, int32_t H, int32_t K, int32_t E, int32_t R, int32_t S,
+                      int32_t use_fp8, const uint16_t *x, const int64_t *topk_idx,
+                      const float *topk_weights, const uint16_t *expert_out,
+                      int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+                      uint8_t *is_token_in_rank, int32_t *expert_slot, int32_t *rank_slot,
+                      int32_t *expert_offset, void *recv_x, float *recv_scales,
+                      int32_t *recv_src_idx, uint16_t *combined_x, double *seconds)
+{
+    double t0 = now_seconds();
+    int st = oracle_layout(N, K, E, R, topk_idx, num_tokens_per_rank, num_tokens_per_expert,
+                           is_token_in_rank, expert_slot, rank_slot, expert_offset);
+    double t1 = now_seconds();
+    st |= oracle_pack(N, H, K, E, S, use_fp8, x, topk_idx, expert_slot, recv_x, recv_scales,
+                      recv_src_idx);
+    double t2 = now_seconds();
+    st |= oracle_combine(N, H, K, E, S, expert_out, topk_idx, topk_weights, expert_slot, NULL,
+                         combined_x);
+    double t3 = now_seconds();
+    seconds[0] = t1 - t0;
+    seconds[1] = t2 - t1;
+    seconds[2] = t3 - t2;
+    return st;
 }

@@ -96,3 +96,15 @@ def test_profile_grid_sizes():
     assert bench._grid_threads(128, 7168, "layout_assign") == 256
     assert bench._grid_threads(128, 7168, "fused") == 129 * 512
     assert bench._grid_threads(600, 7168, "fused") == 601 * 256
+
+
+def test_cpu_baseline_times_each_phase():
+    """The CPU baseline runs the oracle's timed path per workload: three
+    phase figures, their sum, the GB/s they give, the CPU model and one
+    thread."""
+    cb = bench.cpu_baseline(2, lambda m: None, workloads=(1,))
+    ph = cb["per_workload"]["tiny_64x256"]
+    assert ph["runs"] == 2 and min(ph["layout_ms"], ph["pack_ms"], ph["combine_ms"]) >= 0
+    assert abs(ph["step_ms"] - (ph["layout_ms"] + ph["pack_ms"] + ph["combine_ms"])) < 0.01
+    assert cb["value"] == ph["gbps"] > 0 and cb["cores"] == 1 and cb["threads"] == 1
+    assert cb["cpu_model"] and cb["kind"] == "oracle"
