@@ -580,6 +580,23 @@ def time_config(wid, steps, warmup, scrub_bytes, say):
             "bar_60pct_us": round(nb / (0.6 * PEAK_HBM_GBPS * 1e9) * 1e6, 1)}
 
 
+# the other workloads timed as whole cold steps (workload id -> JSON key)
+OTHER_CONFIGS = {4: "large_16384x7168_bf16", 5: "skewed_4096x4096"}
+
+
+def calibration_copy():
+    """A plain copy of 512 MiB (torch copy_, which the runtime runs as its own
+    copy kernel): the known-size reference that scales the HBM counters of a
+    profiling run."""
+    import torch
+
+    src = torch.ones(1 << 29, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def time_copy_ceiling(steps, say):
     """A plain device-to-device copy of 2 GiB (torch copy_, which the runtime
     runs as its own copy kernel): the rate a streaming half-read, half-write
@@ -861,8 +878,9 @@ def cpu_baseline(reps, say, workloads=CPU_BASELINE_WORKLOADS):
 
 
 # The profiling commands whose outputs the summaries in profiles/ come from.
-# $REPO is the repository root and $OUT the directory a profiling run writes
-# to; `bench.py --summarize-profiles $OUT` reads that directory back.
+# $REPO is the repository root, $OUT the directory a profiling run writes to
+# and ${WID} the workload of a --configs-only run (4 or 5);
+# `bench.py --summarize-profiles $OUT` reads that directory back.
 PROFILE_COMMANDS = {
     "layouts_trace": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -T -f csv "
                      "-d $OUT/prof_layouts -o trace -- python3 $REPO/bench.py "
@@ -871,6 +889,15 @@ PROFILE_COMMANDS = {
              "-d $OUT/prof_trace -o trace -- python3 $REPO/bench.py --steps 30 "
              "--warmup 5 --no-cpu-baseline --no-scale-formats --no-receive-layouts "
              "--no-other-configs --quiet",
+    "configs_trace": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -T -f csv "
+                     "-d $OUT/prof_cfg${WID}_trace -o trace -- python3 $REPO/bench.py "
+                     "--configs-only ${WID} --steps 20 --warmup 3 --quiet",
+    "configs_FETCH_SIZE": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -T -f csv "
+                          "-d $OUT/prof_cfg${WID}_FETCH_SIZE -o pmc -- python3 $REPO/bench.py "
+                          "--configs-only ${WID} --steps 3 --warmup 1 --quiet",
+    "configs_WRITE_SIZE": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -T -f csv "
+                          "-d $OUT/prof_cfg${WID}_WRITE_SIZE -o pmc -- python3 $REPO/bench.py "
+                          "--configs-only ${WID} --steps 3 --warmup 1 --quiet",
     "FETCH_SIZE": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -T -f csv "
                   "-d $OUT/prof_FETCH_SIZE -o pmc -- python3 $REPO/bench.py --steps 3 "
                   "--warmup 1 --no-cpu-baseline --no-decode --no-scale-formats --no-receive-layouts "
@@ -898,8 +925,21 @@ def _grid_threads(n, h, kind):
 
 
 def summarize_profiles(out_dir):
-    """Write short text summaries of a profiling run (the three commands in
-    PROFILE_COMMANDS, outputs under ``out_dir``) into profiles/."""
+    """Write short text summaries of a profiling run (the commands in
+    PROFILE_COMMANDS, outputs under ``out_dir``) into profiles/: those of the
+    headline runs, the receive-layout run and the other workloads' runs,
+    whichever are present."""
+    written = []
+    if os.path.isdir(os.path.join(out_dir, "prof_trace")):
+        written += summarize_headline_profiles(out_dir)
+    written += summarize_layout_profiles(out_dir)
+    written += summarize_config_profiles(out_dir)
+    return written
+
+
+def summarize_headline_profiles(out_dir):
+    """Summaries of the prefill and decode kernels from the headline trace
+    and counter runs (``prof_trace``, ``prof_FETCH_SIZE``, ``prof_WRITE_SIZE``)."""
     import csv
 
     from combine_ep_layout_02_amd import workloads as W
@@ -1020,7 +1060,110 @@ def summarize_profiles(out_dir):
             with open(path, "w") as f:
                 f.write("\n".join(lines) + "\n")
             written.append(path)
-    written += summarize_layout_profiles(out_dir)
+    return written
+
+
+def summarize_config_profiles(out_dir):
+    """Summaries of the large and skewed workloads' kernels from the
+    ``--configs-only`` runs (``prof_cfg<WID>_trace``, ``_FETCH_SIZE``,
+    ``_WRITE_SIZE`` and their logs), if present: kernel-trace durations of
+    each kernel of the step, and HBM bytes per launch from the two counters,
+    each scaled by its reading on the run's 512 MiB calibration copy."""
+    import csv
+
+    from combine_ep_layout_02_amd import workloads as W
+
+    def rows(path):
+        with open(path) as f:
+            return list(csv.DictReader(f))
+
+    def bench_json(log):
+        for line in reversed(open(log).read().splitlines()):
+            if line.startswith("{"):
+                return json.loads(line)
+        raise RuntimeError(f"no bench JSON line in {log}")
+
+    written = []
+    for wid in OTHER_CONFIGS:
+        tdir = os.path.join(out_dir, f"prof_cfg{wid}_trace")
+        if not os.path.isdir(tdir):
+            continue
+        w = W.WORKLOADS[wid]
+        fig = bench_json(os.path.join(out_dir, f"prof_cfg{wid}_trace.log"))
+        digest = fig["kernel_source_digest"]
+        trace = rows(os.path.join(tdir, "trace_kernel_trace.csv"))
+        inp = W.make_inputs(w.scaled(w.num_tokens, 128))
+        nb = algorithmic_bytes(w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.num_ranks,
+                               inp["num_valid"], w.use_fp8)
+        pmc = {}
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            pdir = os.path.join(out_dir, f"prof_cfg{wid}_{c}")
+            if os.path.isdir(pdir):
+                pmc[c] = rows(os.path.join(pdir, "pmc_counter_collection.csv"))
+                d = bench_json(os.path.join(out_dir, f"prof_cfg{wid}_{c}.log"))["kernel_source_digest"]
+                if d != digest:
+                    raise RuntimeError("profile runs were taken on different kernel sources")
+        cal = {}
+        for c, rs in pmc.items():
+            top = max(float(r["Counter_Value"]) for r in rs if "copyBuffer" in r["Kernel_Name"])
+            cal[c] = (top, (512 << 20) / 1024.0 / top)
+        kernels = [("layout_count_kernel", "layout_count", "layout"),
+                   ("layout_assign_kernel", "layout_assign", "layout"),
+                   ("pack_kernel", "pack", "dispatch"),
+                   ("combine_kernel", "combine", "combine"),
+                   ("combine_multi_kernel", "combine", "combine")]
+        for kname, short, phase in kernels:
+            durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
+                    if r["Kernel_Name"] == kname]
+            if not durs:
+                continue
+            grids = sorted({r["Grid_Size_X"] for r in trace if r["Kernel_Name"] == kname})
+            med = statistics.median(durs)
+            lines = [
+                f"# {kname}, workload {w.name} (cold steps: an eviction read of 1 GiB before each)",
+                f"# N={w.num_tokens} H={w.hidden} K={w.num_topk} E={w.num_experts} R={w.num_ranks} "
+                f"S={w.expert_capacity} {'FP8' if w.use_fp8 else 'BF16'} dispatch; grid {', '.join(grids)} "
+                "threads",
+                f"kernel_source_digest: {digest}",
+                "",
+                "## rocprofv3 kernel trace (kernel-only durations of every dispatch in the run)",
+                f"command: {PROFILE_COMMANDS['configs_trace'].replace('${WID}', str(wid))}",
+                f"dispatches: {len(durs)}",
+                f"avg_us: {statistics.fmean(durs):.2f}",
+                f"median_us: {med:.2f}",
+                f"min_us: {min(durs):.2f}  max_us: {max(durs):.2f}",
+                f"bench_same_run: whole cold step {fig['figures']['us_median']} us median "
+                f"({fig['figures']['frac_of_peak']} of 8 TB/s at the mean)",
+            ]
+            if phase != "layout":
+                lines += [f"algorithmic_bytes_per_launch ({phase} entry point): {nb[phase]}",
+                          f"achieved_GBps_at_trace_median: {nb[phase] / med / 1e3:.1f}"]
+            else:
+                lines += [f"algorithmic_bytes_per_launch (layout entry point, both kernels): {nb['layout']}"]
+            if len(pmc) == 2 and phase != "layout":
+                per = {}
+                for c, rs in pmc.items():
+                    per[c] = statistics.median(float(r["Counter_Value"]) for r in rs
+                                               if r["Kernel_Name"] == kname)
+                hbm = (per["FETCH_SIZE"] * cal["FETCH_SIZE"][1] + per["WRITE_SIZE"] * cal["WRITE_SIZE"][1]) * 1024
+                lines += [
+                    "",
+                    "## HBM traffic from rocprofv3 counters (one run per counter)",
+                    f"command_fetch: {PROFILE_COMMANDS['configs_FETCH_SIZE'].replace('${WID}', str(wid))}",
+                    f"command_write: {PROFILE_COMMANDS['configs_WRITE_SIZE'].replace('${WID}', str(wid))}",
+                    "calibration: the run's plain copy of 512 MiB (torch copy_, __amd_rocclr_copyBuffer) "
+                    "reads and writes 524288 KiB",
+                    f"  FETCH_SIZE on the copy: {cal['FETCH_SIZE'][0]:.0f} KiB -> factor {cal['FETCH_SIZE'][1]:.4f}",
+                    f"  WRITE_SIZE on the copy: {cal['WRITE_SIZE'][0]:.0f} KiB -> factor {cal['WRITE_SIZE'][1]:.4f}",
+                    f"FETCH_SIZE_KiB_per_dispatch (median): {per['FETCH_SIZE']:.0f}",
+                    f"WRITE_SIZE_KiB_per_dispatch (median): {per['WRITE_SIZE']:.0f}",
+                    f"hbm_bytes_per_launch: {hbm:.0f}",
+                    f"traffic_over_algorithmic: {hbm / nb[phase]:.4f}",
+                ]
+            path = os.path.join(PROFILES, f"{short}_{w.name}.txt")
+            with open(path, "w") as f:
+                f.write("\n".join(lines) + "\n")
+            written.append(path)
     return written
 
 
@@ -1137,6 +1280,10 @@ def main():
     ap.add_argument("--receive-layouts-only", action="store_true",
                     help="time only the normal-mode and expand paths (a profiling run) and print "
                          "their figures as the JSON line")
+    ap.add_argument("--configs-only", metavar="WID", type=int, choices=(4, 5),
+                    help="time only the cold steps of one other workload (4: large, 5: skewed) "
+                         "and a 512 MiB calibration copy (a profiling run), and print their "
+                         "figures as the JSON line")
     ap.add_argument("--no-copy-ceiling", action="store_true",
                     help="skip the 2 GiB plain-copy context figure (counter runs calibrate on "
                          "the bench's 512 MiB copy and must see no other copy)")
@@ -1167,6 +1314,13 @@ def main():
 
     ep.lib()  # fail loudly if the HIP library is missing
     scrub_bytes = args.scrub_mib << 20
+    if args.configs_only:
+        cfg = time_config(args.configs_only, args.steps, args.warmup, scrub_bytes, say)
+        torch.cuda.empty_cache()
+        calibration_copy()
+        print(json.dumps({"workload": OTHER_CONFIGS[args.configs_only], "figures": cfg,
+                          "kernel_source_digest": kernel_source_digest()}), flush=True)
+        return
     if args.receive_layouts_only:
         print(json.dumps({"receive_layouts_4096x7168": time_receive_layouts(
             3, args.steps, scrub_bytes, say),
@@ -1214,7 +1368,7 @@ def main():
             3, min(args.steps, 20), scrub_bytes, say)
     if not args.no_other_configs:
         torch.cuda.empty_cache()
-        for wid, key in ((4, "large_16384x7168_bf16"), (5, "skewed_4096x4096")):
+        for wid, key in OTHER_CONFIGS.items():
             extra[key] = time_config(wid, min(args.steps, 20), min(args.warmup, 3), scrub_bytes, say)
             torch.cuda.empty_cache()
     if not args.no_receive_layouts:
