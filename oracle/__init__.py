@@ -81,6 +81,11 @@ class Oracle:
         lib.oracle_combine_normal.restype = ctypes.c_int
         lib.oracle_group_limited_topk.argtypes = [i32] * 6 + [vp] * 3
         lib.oracle_timed_path.argtypes = [i32] * 7 + [vp] * 15
+        lib.oracle_log2_rn_array.argtypes = [i64, vp, vp]
+        lib.oracle_logfmt_encode_rows.argtypes = [i64, i32, vp, vp, vp]
+        lib.oracle_logfmt_decode_rows.argtypes = [i64, i32, vp, vp, vp]
+        lib.oracle_combine_logfmt.argtypes = [i32] * 5 + [vp] * 7
+        lib.oracle_combine_logfmt.restype = ctypes.c_int
         lib.oracle_timed_path.restype = ctypes.c_int
         lib.oracle_group_limited_topk.restype = ctypes.c_int
         self.lib = lib
@@ -347,6 +352,55 @@ class Oracle:
                                         _ptr(w), _ptr(y), *[_ptr(a) for a in lay], _ptr(recv_x),
                                         _ptr(recv_scales), _ptr(recv_src), _ptr(out), _ptr(secs))
         return tuple(float(v) for v in secs), int(st)
+
+    # ------------------------------------------------------------ LogFMT
+    def log2_rn(self, a: np.ndarray) -> np.ndarray:
+        """log2 of positive floats, rounded to the nearest binary32."""
+        v = np.ascontiguousarray(a, dtype=np.float32).ravel()
+        out = np.empty_like(v)
+        self.lib.oracle_log2_rn_array(v.size, _ptr(v), _ptr(out))
+        return out.reshape(np.shape(a))
+
+    def logfmt_encode(self, rows_bits: np.ndarray):
+        """LogFMT of bf16 rows uint16 [R, H] (H % 128 == 0; DeepEP V1 Legacy
+        guide §6.2: a min/max header per 128 channels, then the data; §7.1
+        LogFMT combine): (codes uint8 [R, H], headers float32 [R, H/128, 2]
+        holding (lo, hi) per block)."""
+        x = np.ascontiguousarray(rows_bits, dtype=np.uint16)
+        r, h = x.shape
+        codes = np.empty((r, h), np.uint8)
+        headers = np.empty((r, h // 128, 2), np.float32)
+        self.lib.oracle_logfmt_encode_rows(r, h, _ptr(x), _ptr(codes), _ptr(headers))
+        return codes, headers
+
+    def logfmt_decode(self, codes: np.ndarray, headers: np.ndarray) -> np.ndarray:
+        """Decoded float32 values [R, H] of LogFMT codes and headers."""
+        c = np.ascontiguousarray(codes, dtype=np.uint8)
+        hd = np.ascontiguousarray(headers, dtype=np.float32)
+        r, h = c.shape
+        out = np.empty((r, h), np.float32)
+        self.lib.oracle_logfmt_decode_rows(r, h, _ptr(c), _ptr(hd), _ptr(out))
+        return out
+
+    def combine_logfmt(self, codes: np.ndarray, headers: np.ndarray, topk_idx: np.ndarray,
+                       topk_weights: np.ndarray, expert_slot: np.ndarray, num_experts: int,
+                       capacity: int, bias: np.ndarray | None = None):
+        """Combine of expert outputs carried as LogFMT: ``codes`` uint8
+        [E, S, H], ``headers`` float32 [E, S, H/128, 2].  Returns (combined
+        bf16 bits uint16 [N, H], status)."""
+        c = np.ascontiguousarray(codes, dtype=np.uint8)
+        hd = np.ascontiguousarray(headers, dtype=np.float32)
+        idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
+        w = np.ascontiguousarray(topk_weights, dtype=np.float32)
+        slot = np.ascontiguousarray(expert_slot, dtype=np.int32)
+        n, k = idx.shape
+        h = c.shape[-1]
+        out = np.empty((n, h), np.uint16)
+        b = self._bias(bias, n, h)
+        st = self.lib.oracle_combine_logfmt(n, h, k, int(num_experts), int(capacity), _ptr(c),
+                                            _ptr(hd), _ptr(idx), _ptr(w), _ptr(slot), _ptr(b),
+                                            _ptr(out))
+        return out, int(st)
 
     # ------------------------------------------------------------ formats
     def e4m3fn_encode(self, v: np.ndarray) -> np.ndarray:

@@ -846,6 +846,145 @@ int oracle_group_limited_topk(int32_t N, int32_t E, int32_t G, int32_t TG, int32
     return ORACLE_OK;
 }
 
+/* ------------------------------------------------ LogFMT combine payload */
+
+/* [V1] §6.2: the low-latency combine message carries, per 128 channels, a
+ * min/max header followed by the hidden data; [V1] §7.1: the low-latency
+ * test has a LogFMT combine switch.  The pages define nothing further.  The
+ * reading used here (an 8-bit logarithmic format) is:
+ *   L(a)   = log2(a) rounded to the nearest binary32, for a > 0;
+ *   header = per 128-channel block b, lo_b = min and hi_b = max of L(|x|)
+ *            over the block's nonzero channels (both 0 when there are none);
+ *   code   = one byte per channel: bit 7 the sign, bits 0..6 a magnitude code
+ *            m; m = 0 is zero (code 0x00, either sign), otherwise
+ *            m = 1 + rint(RN(RN(L(|x|) - lo) * RN(126 / (hi - lo)))) clamped
+ *            to [1, 127] (rint ties to even; m = 1 when hi == lo): codes
+ *            1..127 spread evenly over [lo, hi] in the log domain;
+ *   decode = sign * RN(2^RN(lo + RN((m - 1) * RN((hi - lo) / 126)))), and 0
+ *            for m = 0.
+ * Every step before the exponential is an IEEE binary32 operation, so the
+ * codes are exact; the decoded value is within half a log-domain step
+ * (plus rounding) of |x|. */
+
+/* L(a): log2 of a positive float, rounded to nearest binary32 (evaluated in
+ * double, then rounded once; an exhaustive pin over every bf16 input checks
+ * that this is the correctly rounded value). */
+float oracle_log2_rn(float a) { return (float)log2((double)a); }
+
+void oracle_logfmt_encode_row(int32_t H, const uint16_t *x, uint8_t *codes, float *header)
+{
+    for (int32_t b = 0; b < H / 128; ++b) {
+        const uint16_t *xb = x + (size_t)b * 128;
+        int any = 0;
+        float lo = 0.0f, hi = 0.0f;
+        for (int32_t c = 0; c < 128; ++c) {
+            const float v = oracle_bf16_to_f32(xb[c]);
+            if (v != 0.0f) {
+                const float l = oracle_log2_rn(fabsf(v));
+                if (!any || l < lo)
+                    lo = l;
+                if (!any || l > hi)
+                    hi = l;
+                any = 1;
+            }
+        }
+        header[2 * b] = lo;
+        header[2 * b + 1] = hi;
+        const float span = hi - lo;
+        const float inv = span > 0.0f ? 126.0f / span : 0.0f;
+        for (int32_t c = 0; c < 128; ++c) {
+            const float v = oracle_bf16_to_f32(xb[c]);
+            uint8_t code = 0;
+            if (v != 0.0f) {
+                const float q = (oracle_log2_rn(fabsf(v)) - lo) * inv;
+                int m = 1 + (int)nearbyintf(q);
+                m = m < 1 ? 1 : m > 127 ? 127 : m;
+                code = (uint8_t)((v < 0.0f ? 0x80 : 0x00) | m);
+            }
+            codes[(size_t)b * 128 + c] = code;
+        }
+    }
+}
+
+float oracle_logfmt_decode(uint8_t code, float lo, float hi)
+{
+    const int m = code & 0x7F;
+    if (m == 0)
+        return 0.0f;
+    const float step = (hi - lo) / 126.0f;
+    const float d = lo + (float)(m - 1) * step;
+    const float mag = (float)exp2((double)d);
+    return (code & 0x80) ? -mag : mag;
+}
+
+/* rows x [R, H] bf16 -> codes [R, H], headers [R, H/128, 2] (lo, hi). */
+void oracle_logfmt_encode_rows(int64_t rows, int32_t H, const uint16_t *x, uint8_t *codes,
+                               float *headers)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        oracle_logfmt_encode_row(H, x + (size_t)r * H, codes + (size_t)r * H,
+                                 headers + (size_t)r * (H / 128) * 2);
+}
+
+/* codes [R, H], headers [R, H/128, 2] -> float values [R, H]. */
+void oracle_logfmt_decode_rows(int64_t rows, int32_t H, const uint8_t *codes, const float *headers,
+                               float *out)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int32_t c = 0; c < H; ++c) {
+            const float *hd = headers + ((size_t)r * (H / 128) + c / 128) * 2;
+            out[(size_t)r * H + c] = oracle_logfmt_decode(codes[(size_t)r * H + c], hd[0], hd[1]);
+        }
+}
+
+/* Combine of expert outputs carried as LogFMT ([V1] §6.2 and §7.1): as
+ * oracle_combine, with each expert value the decoded float of its code:
+ *   acc = +0; for k = 0..K-1 with a valid expert e and slot j:
+ *       acc = fmaf(w[t,k], decode(codes[e][j][c], header[e][j][c / 128]), acc)
+ *   acc = acc + float(bias[t][c]) (when bias is not NULL); out = bf16_RNE(acc). */
+int oracle_combine_logfmt(int32_t N, int32_t H, int32_t K, int32_t E, int32_t S,
+                          const uint8_t *codes, const float *headers, const int64_t *topk_idx,
+                          const float *topk_weights, const int32_t *expert_slot,
+                          const uint16_t *bias, uint16_t *combined_x)
+{
+    if (N < 0 || H < 128 || H % 128 != 0 || K < 1 || E < 1 || S < 0)
+        return ORACLE_BAD_ARGS;
+    int status = ORACLE_OK;
+    float *acc = (float *)malloc(sizeof(float) * (size_t)H);
+    float *y = (float *)malloc(sizeof(float) * (size_t)H);
+    if (!acc || !y) {
+        free(acc);
+        free(y);
+        return ORACLE_BAD_ARGS;
+    }
+    for (int32_t t = 0; t < N; ++t) {
+        memset(acc, 0, sizeof(float) * (size_t)H); /* +0.0f */
+        for (int32_t k = 0; k < K; ++k) {
+            const size_t i = (size_t)t * K + k;
+            const int32_t e = routed_expert(topk_idx[i], E, &status);
+            if (e < 0)
+                continue;
+            const int32_t j = expert_slot[i];
+            if (j < 0 || j >= S) {
+                status |= ORACLE_BAD_SLOT;
+                continue;
+            }
+            /* the expert's output row, decoded */
+            const size_t row = (size_t)e * S + j;
+            oracle_logfmt_decode_rows(1, H, codes + row * H, headers + row * (H / 128) * 2, y);
+            const float w = topk_weights[i];
+            for (int32_t c = 0; c < H; ++c)
+                acc[c] = fmaf(w, y[c], acc[c]);
+        }
+        add_bias_row(acc, bias ? bias + (size_t)t * H : NULL, H);
+        for (int32_t c = 0; c < H; ++c)
+            combined_x[(size_t)t * H + c] = oracle_bf16_rne(acc[c]);
+    }
+    free(acc);
+    free(y);
+    return status;
+}
+
 /* ------------------------------------------------- array forms for pinning */
 
 void oracle_e4m3fn_encode_array(int64_t n, const float *v, uint8_t *out)
@@ -921,4 +1060,10 @@ int oracle_timed_path(int32_t N, int32_t H, int32_t K, int32_t E, int32_t R, int
     seconds[1] = t2 - t1;
     seconds[2] = t3 - t2;
     return st;
+}
+
+void oracle_log2_rn_array(int64_t n, const float *a, float *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_log2_rn(a[i]);
 }

@@ -54,6 +54,10 @@ def main(path: str) -> int:
         ("gating_sum_golden", lambda: pins.pin_gating_sum_golden(o)),
         ("gating_sum_special_cases", lambda: pins.pin_gating_sum_special_cases(o)),
         ("gating_bad_args", lambda: pins.pin_gating_bad_args(o)),
+        ("log2_rn_exhaustive", lambda: pins.pin_log2_rn_exhaustive(o)),
+        ("logfmt_golden", lambda: pins.pin_logfmt_golden(o)),
+        ("logfmt_roundtrip_bound", lambda: pins.pin_logfmt_roundtrip_bound(o)),
+        ("combine_logfmt", lambda: pins.pin_combine_logfmt_exact_cases(o)),
         ("layout_bruteforce", lambda: pins.pin_layout_bruteforce(o)),
     ]
     for name, fn in steps:

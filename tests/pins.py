@@ -1042,3 +1042,167 @@ def pin_gating_bad_args(o):
         assert o.group_limited_topk(sc, G, TG, K)[2] == 4, (G, TG, K)
     for rule in (-1, 2):
         assert o.group_limited_topk(sc, 4, 2, 2, rule)[2] == 4, rule
+
+
+# ------------------------------------------------------------ LogFMT payload
+
+def all_bf16_magnitudes() -> np.ndarray:
+    """Every positive finite bf16 value's bit pattern (subnormals included)."""
+    return np.arange(1, 0x7F80, dtype=np.uint16)
+
+
+def exact_log2_rn(bits: np.ndarray) -> np.ndarray:
+    """log2 of positive bf16 values, rounded to the nearest binary32, from a
+    100-bit evaluation (mpmath): the float32 neighbours of the double nearest
+    the exact value are compared with it and the closest kept (log2 of a
+    rational that is not a power of two is irrational, so there is no tie)."""
+    import mpmath
+
+    mpmath.mp.prec = 100
+    out = np.empty(bits.size, np.float32)
+    vals = bf16_to_f64(bits)
+    for i, v in enumerate(vals):
+        ex = mpmath.log(mpmath.mpf(float(v)), 2)
+        c = np.float32(float(ex))
+        cands = (np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf)))
+        out[i] = min(cands, key=lambda f: abs(mpmath.mpf(float(f)) - ex))
+    return out
+
+
+def pin_log2_rn_exhaustive(o):
+    """L(a) for every positive finite bf16 input equals the correctly rounded
+    binary32 log2 (100-bit reference), and powers of two give their exponent."""
+    bits = all_bf16_magnitudes()
+    a = bf16_to_f64(bits).astype(np.float32)
+    got = o.log2_rn(a)
+    want = exact_log2_rn(bits)
+    bad = np.nonzero(got.view(np.uint32) != want.view(np.uint32))[0]
+    assert bad.size == 0, f"log2 not correctly rounded at {bits[bad[:5]]}: {got[bad[:5]]} vs {want[bad[:5]]}"
+    p2 = np.arange(-133, 128)
+    assert np.array_equal(o.log2_rn(np.exp2(p2).astype(np.float32)), p2.astype(np.float32))
+
+
+def _logfmt_golden_rows(g):
+    H = g["hidden"]
+    row = np.zeros(H, np.float32)
+    for b, vals in enumerate(g["values"]):
+        row[b * 128:b * 128 + len(vals)] = vals
+    bits = (row.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(bf16_to_f64(bits), row.astype(np.float64)), "golden values must be exact in bf16"
+    return bits[None, :]
+
+
+def pin_logfmt_golden(o):
+    """Hand-worked codes and headers (``tests/golden/logfmt_blocks.json``),
+    including a rounding tie (to even) and single-value and all-zero blocks."""
+    with open(os.path.join(GOLDEN, "logfmt_blocks.json")) as f:
+        g = json.load(f)
+    bits = _logfmt_golden_rows(g)
+    codes, hd = o.logfmt_encode(bits)
+    l5 = o.log2_rn(np.array([5.0], np.float32))[0]
+    for b, (want_c, want_h) in enumerate(zip(g["codes"], g["headers"])):
+        blk = codes[0, b * 128:(b + 1) * 128]
+        assert blk[:len(want_c)].tolist() == want_c, (b, blk[:len(want_c)].tolist())
+        assert not blk[len(want_c):].any(), b
+        want_h = [l5 if v == "L(5)" else v for v in want_h]
+        assert hd[0, b].tolist() == [np.float32(v) for v in want_h], (b, hd[0, b])
+    dec = o.logfmt_decode(codes, hd)[0]
+    assert dec[128:256].tolist() == [0.0] * 128 and dec[4] == 0.0 and not np.signbit(dec[5])
+    assert abs(dec[256] - 5.0) <= 5.0 * 2 ** -22  # lo == hi: the value itself
+
+
+def _logfmt_rows(rng):
+    """Rows of every kind the bound must cover: N(0,1), wide dynamic range,
+    zeros and negatives, tiny (subnormal) and huge magnitudes."""
+    H = 384
+    rows = [rng.standard_normal((20, H)).astype(np.float32)]
+    wide = rng.standard_normal((20, H)) * np.exp2(rng.uniform(-40, 40, size=(20, H)))
+    rows.append(wide.astype(np.float32))
+    z = rng.standard_normal((20, H)).astype(np.float32)
+    z[rng.random((20, H)) < 0.3] = 0.0
+    rows.append(z)
+    rows.append((rng.standard_normal((4, H)) * 2.0 ** -128).astype(np.float32))
+    rows.append((rng.standard_normal((4, H)) * 2.0 ** 120).astype(np.float32))
+    x = np.concatenate(rows)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def pin_logfmt_roundtrip_bound(o):
+    """Decoding an encoded row returns each value's sign and zero exactly,
+    every nonzero magnitude within half a log-domain step of the original
+    (plus the binary32 roundings of the log-domain arithmetic and the
+    exponential), the block's smallest and largest magnitudes as codes 1 and
+    127, and headers equal to the extreme logs of the nonzero channels
+    (numpy's float64 log2, within binary32 rounding)."""
+    rng = np.random.default_rng(41)
+    bits = _logfmt_rows(rng)
+    codes, hd = o.logfmt_encode(bits)
+    dec = o.logfmt_decode(codes, hd).astype(np.float64)
+    x = bf16_to_f64(bits)
+    R, H = x.shape
+    G = H // 128
+    assert np.array_equal(np.sign(dec), np.sign(x)), "sign or zero lost"
+    assert not codes[x == 0].any(), "zero must be code 0"
+    for r in range(R):
+        for b in range(G):
+            xs = x[r, b * 128:(b + 1) * 128]
+            nz = xs != 0
+            lo, hi = float(hd[r, b, 0]), float(hd[r, b, 1])
+            if not nz.any():
+                assert lo == 0.0 and hi == 0.0
+                continue
+            mags = np.abs(xs[nz])
+            lx = np.log2(mags)
+            assert abs(lo - lx.min()) <= 2.0 ** -22 * max(1.0, abs(lo)) and \
+                abs(hi - lx.max()) <= 2.0 ** -22 * max(1.0, abs(hi)), (r, b)
+            m = codes[r, b * 128:(b + 1) * 128][nz] & 0x7F
+            assert m.min() == 1 and (m.max() == 127 or hi == lo), (r, b)
+            step = (hi - lo) / 126.0
+            slack = 2.0 ** -21 * (1.0 + max(abs(lo), abs(hi)))
+            err = np.abs(np.log2(np.abs(dec[r, b * 128:(b + 1) * 128][nz])) - lx)
+            assert (err <= step / 2 + slack).all(), (r, b, err.max(), step)
+
+
+def pin_combine_logfmt_exact_cases(o):
+    """Expert rows whose nonzero values in each 128-channel block are +-2^j
+    with one j per block decode exactly (lo == hi == j), so the LogFMT
+    combine equals the pinned plain combine of the same rows bit for bit; and
+    on general rows it equals the float64 weighted sum of the decoded values
+    within the combine bar (with masked entries and a bias)."""
+    rng = np.random.default_rng(43)
+    N, H, K, E, R = 50, 256, 4, 16, 4
+    idx = np.argsort(rng.random((N, E)), axis=1)[:, :K].astype(np.int64)
+    idx[rng.random((N, K)) < 0.15] = -1
+    w = rng.random((N, K)).astype(np.float32)
+    lay = o.layout(idx, E, R)
+    S = max(1, int(lay["num_tokens_per_expert"].max()))
+    P = int((idx >= 0).sum())
+    j = rng.integers(-20, 20, size=(P, H // 128))
+    signs = rng.choice([-1.0, 1.0, 0.0], size=(P, H), p=[0.45, 0.45, 0.1])
+    rows = (signs * np.exp2(np.repeat(j, 128, axis=1))).astype(np.float32)
+    bits = (rows.view(np.uint32) >> 16).astype(np.uint16)
+    y = place_rows(bits, idx, lay["expert_slot"], E, S)
+    codes, hd = o.logfmt_encode(y.reshape(-1, H))
+    got, st = o.combine_logfmt(codes.reshape(E, S, H), hd.reshape(E, S, H // 128, 2), idx, w,
+                               lay["expert_slot"], E, S)
+    want, st2 = o.combine(y, idx, w, lay["expert_slot"], E, S)
+    assert st == st2 == 0 and np.array_equal(got, want)
+    # general rows: float64 weighted sum of the decoded values, plus a bias
+    gen = (rng.standard_normal((P, H)) * np.exp2(rng.uniform(-8, 8, size=(P, H)))).astype(np.float32)
+    gbits = (gen.view(np.uint32) >> 16).astype(np.uint16)
+    y = place_rows(gbits, idx, lay["expert_slot"], E, S)
+    codes, hd = o.logfmt_encode(y.reshape(-1, H))
+    dec = o.logfmt_decode(codes, hd).astype(np.float64).reshape(E, S, H)
+    bias = (rng.standard_normal((N, H)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    got, st = o.combine_logfmt(codes.reshape(E, S, H), hd.reshape(E, S, H // 128, 2), idx, w,
+                               lay["expert_slot"], E, S, bias=bias)
+    ref = bf16_to_f64(bias).copy()
+    absum = np.zeros((N, H))
+    for t in range(N):
+        for k in range(K):
+            if idx[t, k] >= 0:
+                term = float(w[t, k]) * dec[idx[t, k], lay["expert_slot"][t, k]]
+                ref[t] += term
+                absum[t] += np.abs(term)
+    assert st == 0
+    assert_combine_close(got, ref, "combine_logfmt", abs_slack=(K + 1) * 2.0 ** -24 * absum)

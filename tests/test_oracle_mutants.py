@@ -118,6 +118,21 @@ MUTANTS = [
     ("gating_one_group_short", [("for (int32_t n = 0; n < TG; ++n) {", "for (int32_t n = 1; n < TG; ++n) {")]),
     ("gating_unnormalised", [("topk_weights[(size_t)t * K + k] = (float)(z[k] / sum);",
                               "topk_weights[(size_t)t * K + k] = (float)z[k];")]),
+    # LogFMT combine payload
+    ("logfmt_lo_is_max", [("if (!any || l < lo)\n                    lo = l;", "if (!any || l > lo)\n                    lo = l;")]),
+    ("logfmt_127_steps", [("const float inv = span > 0.0f ? 126.0f / span : 0.0f;",
+                           "const float inv = span > 0.0f ? 127.0f / span : 0.0f;")]),
+    ("logfmt_ties_away", [("int m = 1 + (int)nearbyintf(q);", "int m = 1 + (int)roundf(q);")]),
+    ("logfmt_sign_dropped", [("code = (uint8_t)((v < 0.0f ? 0x80 : 0x00) | m);", "code = (uint8_t)m;")]),
+    ("logfmt_zero_code_1", [("            uint8_t code = 0;\n", "            uint8_t code = 1;\n")]),
+    ("logfmt_decode_from_m", [("const float d = lo + (float)(m - 1) * step;", "const float d = lo + (float)m * step;")]),
+    ("logfmt_decode_127_steps", [("const float step = (hi - lo) / 126.0f;", "const float step = (hi - lo) / 127.0f;")]),
+    ("logfmt_natural_log", [("float oracle_log2_rn(float a) { return (float)log2((double)a); }",
+                             "float oracle_log2_rn(float a) { return (float)log((double)a); }")]),
+    ("logfmt_log_truncated", [("float oracle_log2_rn(float a) { return (float)log2((double)a); }",
+                               "float oracle_log2_rn(float a) { float l = (float)log2((double)a); double d = log2((double)a); return (double)l > d ? nextafterf(l, -1e30f) : l; }")]),
+    ("combine_logfmt_header_of_block0", [("const float *hd = headers + ((size_t)r * (H / 128) + c / 128) * 2;",
+                                          "const float *hd = headers + ((size_t)r * (H / 128)) * 2;")]),
     ("bias_row_of_token0", [(COMBINE_YR + COMBINE_FMA + "\n        }\n        add_bias_row(acc, bias ? bias + (size_t)t * H : NULL, H);",
                              COMBINE_YR + COMBINE_FMA + "\n        }\n        add_bias_row(acc, bias, H);")]),
 ]

@@ -198,3 +198,10 @@ def test_gating_sum_rule(o):
     pins.pin_gating_sum_golden(o)
     pins.pin_gating_sum_special_cases(o)
     pins.pin_prefill_routing_is_sum_gating(o)
+
+
+def test_logfmt(o):
+    pins.pin_log2_rn_exhaustive(o)
+    pins.pin_logfmt_golden(o)
+    pins.pin_logfmt_roundtrip_bound(o)
+    pins.pin_combine_logfmt_exact_cases(o)
