@@ -15,7 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libep_mi355x.so")
-SOURCES = ["ep_abi.hip", "layout.hip", "dispatch.hip", "combine.hip", "gate.hip", "probe.hip"]
+SOURCES = ["ep_abi.hip", "layout.hip", "dispatch.hip", "combine.hip", "gate.hip", "logfmt.hip",
+           "probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

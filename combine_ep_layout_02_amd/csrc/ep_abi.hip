@@ -196,6 +196,8 @@ int ep_query_sizes(const ep_shape *s, ep_sizes *out)
     out->recv_scales_expand = T * scale_row;
     out->recv_src_idx_expand = T * sizeof(int32_t);
     out->expert_out_expand = T * H * 2;
+    out->logfmt_codes = H % 128 == 0 ? rows * H : 0;
+    out->logfmt_headers = H % 128 == 0 ? rows * (H / 128) * 2 * sizeof(float) : 0;
     return EP_OK;
 }
 
@@ -451,6 +453,51 @@ int ep_combine_normal(const ep_shape *s, const uint16_t *x, const int32_t *rank_
     const hipError_t err = ep::launch_combine_normal(*s, x, rank_slot, recv_topk_weights, bias,
                                                      combined_x, combined_topk_weights, status,
                                                      static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+int ep_logfmt_encode(const ep_shape *s, const uint16_t *expert_out, const int64_t *topk_idx,
+                     const int32_t *expert_slot, uint8_t *codes, float *headers,
+                     uint32_t *status, void *stream)
+{
+    const int rc = check_shape(s);
+    if (rc != EP_OK)
+        return rc;
+    if (s->hidden % 128 != 0)
+        return EP_ERR_SHAPE;
+    if (s->num_tokens == 0)
+        return EP_OK;
+    if (!expert_out || !topk_idx || !expert_slot || !codes || !headers)
+        return EP_ERR_NULL;
+    if (!aligned(expert_out, 16) || !aligned(codes, 16) || !aligned(headers, 8) ||
+        !aligned(topk_idx, 8) || !aligned(expert_slot, 4) || !aligned(status, 4))
+        return EP_ERR_ALIGN;
+    const hipError_t err = ep::launch_logfmt_encode(*s, expert_out, topk_idx, expert_slot, codes,
+                                                    headers, status, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+int ep_combine_logfmt(const ep_shape *s, const uint8_t *codes, const float *headers,
+                      const int64_t *topk_idx, const float *topk_weights,
+                      const int32_t *expert_slot, const uint16_t *bias, uint16_t *combined_x,
+                      uint32_t *status, void *stream)
+{
+    const int rc = check_shape(s);
+    if (rc != EP_OK)
+        return rc;
+    if (s->hidden % 128 != 0)
+        return EP_ERR_SHAPE;
+    if (s->num_tokens == 0)
+        return EP_OK;
+    if (!codes || !headers || !topk_idx || !topk_weights || !expert_slot || !combined_x)
+        return EP_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(headers, 8) || !aligned(combined_x, 16) ||
+        !aligned(bias, 16) || !aligned(topk_idx, 8) || !aligned(topk_weights, 4) ||
+        !aligned(expert_slot, 4) || !aligned(status, 4))
+        return EP_ERR_ALIGN;
+    const hipError_t err =
+        ep::launch_combine_logfmt(*s, codes, headers, topk_idx, topk_weights, expert_slot, bias,
+                                  combined_x, status, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? EP_OK : EP_ERR_HIP;
 }
 

@@ -103,6 +103,16 @@ hipError_t launch_combine_expand(const ep_shape &s, const uint16_t *expert_out,
                                  const uint16_t *bias, uint16_t *combined_x, uint32_t *status,
                                  hipStream_t stream);
 
+hipError_t launch_logfmt_encode(const ep_shape &s, const uint16_t *expert_out,
+                                const int64_t *topk_idx, const int32_t *expert_slot,
+                                uint8_t *codes, float *headers, uint32_t *status,
+                                hipStream_t stream);
+
+hipError_t launch_combine_logfmt(const ep_shape &s, const uint8_t *codes, const float *headers,
+                                 const int64_t *topk_idx, const float *topk_weights,
+                                 const int32_t *expert_slot, const uint16_t *bias,
+                                 uint16_t *combined_x, uint32_t *status, hipStream_t stream);
+
 hipError_t launch_combine_normal(const ep_shape &s, const uint16_t *x, const int32_t *rank_slot,
                                  const float *recv_topk_weights, const uint16_t *bias,
                                  uint16_t *combined_x, float *combined_topk_weights,

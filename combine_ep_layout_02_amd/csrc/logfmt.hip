@@ -1,0 +1,352 @@
+// logfmt.hip -- the LogFMT combine payload on gfx950: expert outputs carried
+// as one byte per channel plus a (lo, hi) header per 128 channels, and the
+// top-k combine that reads them.
+//
+// DeepEP V1 Legacy guide §6.2: the low-latency combine message is a min/max
+// header per 128 channels followed by the hidden data; §7.1: the low-latency
+// test has a LogFMT combine switch.  The format (an 8-bit logarithmic one):
+//   L(a)   = log2(a) rounded to the nearest binary32, a > 0;
+//   header = per 128-channel block, lo / hi = min / max of L(|x|) over the
+//            block's nonzero channels (0, 0 when there are none);
+//   code   = bit 7 the sign, bits 0..6 m: 0 for zero, else
+//            m = 1 + rint(RN(RN(L(|x|) - lo) * RN(126 / (hi - lo)))) clamped
+//            to [1, 127] (ties to even; 1 when hi == lo);
+//   decode = sign * 2^RN(lo + RN((m - 1) * RN((hi - lo) / 126))).
+// Every step of the encoding is a binary32 operation, so codes and headers
+// are exact; only the decode's exponential rounds differently from the
+// definition (within a unit in the last place).
+//
+// L of a bf16 value: with |x| = 2^e * (1 + f/128) (subnormals normalised
+// first), L = RN32(e + T[f]), T[f] = log2(1 + f/128) in binary64 from a
+// 128-entry table each block builds in LDS.  binary64 leaves 29 bits of
+// margin before the rounding to binary32; every bf16 input is checked
+// against the correctly rounded value by ep_probe_log2_bf16.
+//
+// Work item = one wave on one (token, 1024-channel chunk), as in the pack
+// and the combine; a lane owns 16 channels (32 bytes of bf16, 16 code bytes)
+// and 8 lanes make one 128-channel block, whose min and max take three
+// xor-shuffles.  The encoder takes the token's routed rows (e, slot) -- each
+// expert output row is referenced by exactly one (token, k) -- loads every
+// row of a batch of 8 entries before encoding the first, and writes the
+// codes and headers in place of the bf16 row.  The combine loads every
+// row's codes and header of a batch before decoding the first, then runs
+// the combine's k-ordered fp32 FMA chain.
+#include "ep_device.h"
+#include "ep_internal.h"
+#include "ep_probe.h"
+
+namespace ep {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kChunk = 1024; // channels per work item
+constexpr int kKB = 8;       // routing entries per batch
+
+// T[f] = log2(1 + f / 128), f = 0..127, built by the block's first 128
+// threads (1 + f/128 is exact in binary64).  Needs a barrier after.
+__device__ __forceinline__ void build_log2_table(double *T)
+{
+    if (threadIdx.x < 128)
+        T[threadIdx.x] = log2(1.0 + (double)threadIdx.x * (1.0 / 128.0));
+}
+
+// L of a nonzero bf16 magnitude (bits 0..14 of the pattern, not 0).
+__device__ __forceinline__ float log2_rn_bf16(uint32_t mag, const double *T)
+{
+    const uint32_t ex = mag >> 7, mant = mag & 127u;
+    int e;
+    uint32_t f;
+    if (ex != 0) {
+        e = (int)ex - 127;
+        f = mant;
+    } else {
+        // subnormal: mant * 2^-133, mant in 1..127; p = position of the top bit
+        const int p = 31 - __builtin_clz(mant);
+        e = -133 + p;
+        f = (mant << (7 - p)) & 127u;
+    }
+    return (float)((double)e + T[f]);
+}
+
+// One lane's place on the (token, chunk) lane map: block g, first channel ch.
+struct LfLane {
+    int32_t G, g, ch;
+    bool active;
+};
+
+__device__ __forceinline__ LfLane lf_lane(int32_t H, int32_t chunk, int lane)
+{
+    LfLane l;
+    l.G = H / 128;
+    l.g = chunk * (kChunk / 128) + (lane >> 3);
+    l.active = l.g < l.G;
+    l.ch = l.g * 128 + (lane & 7) * 16;
+    return l;
+}
+
+// Encode one lane's 16 channels (in0, in1: bf16 pairs) into 16 code bytes,
+// with the block's (lo, hi) from its 8 lanes.  Called by every lane.
+__device__ __forceinline__ void encode_lane(const uint4 &in0, const uint4 &in1, const double *T,
+                                            uint4 &codes, float &lo, float &hi)
+{
+    const uint32_t w[8] = {in0.x, in0.y, in0.z, in0.w, in1.x, in1.y, in1.z, in1.w};
+    uint32_t h[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        h[2 * i] = w[i] & 0xFFFFu;
+        h[2 * i + 1] = w[i] >> 16;
+    }
+    float l[16];
+    float lmin = __builtin_inff(), lmax = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t mag = h[i] & 0x7FFFu;
+        l[i] = mag ? log2_rn_bf16(mag, T) : 0.0f;
+        if (mag) {
+            lmin = fminf(lmin, l[i]);
+            lmax = fmaxf(lmax, l[i]);
+        }
+    }
+    lmin = fminf(lmin, __shfl_xor(lmin, 1, 64));
+    lmax = fmaxf(lmax, __shfl_xor(lmax, 1, 64));
+    lmin = fminf(lmin, __shfl_xor(lmin, 2, 64));
+    lmax = fmaxf(lmax, __shfl_xor(lmax, 2, 64));
+    lmin = fminf(lmin, __shfl_xor(lmin, 4, 64));
+    lmax = fmaxf(lmax, __shfl_xor(lmax, 4, 64));
+    const bool any = lmin <= lmax; // a block with no nonzero channel keeps +inf > -inf
+    lo = any ? lmin : 0.0f;
+    hi = any ? lmax : 0.0f;
+    const float span = hi - lo;
+    const float inv = span > 0.0f ? 126.0f / span : 0.0f; // correctly rounded division
+    uint32_t out[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t mag = h[i] & 0x7FFFu;
+        uint32_t code = 0u;
+        if (mag) {
+            const float q = (l[i] - lo) * inv;
+            const int m = min(max(1 + (int)__builtin_rintf(q), 1), 127);
+            code = ((h[i] >> 8) & 0x80u) | (uint32_t)m;
+        }
+        out[i >> 2] |= code << (8 * (i & 3));
+    }
+    codes = make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+template <int KB, class Rows>
+__global__ __launch_bounds__(kThreads) void logfmt_encode_kernel(
+    int32_t N, int32_t H, int32_t K, int32_t E, int32_t nchunks, Rows rows,
+    const uint16_t *__restrict__ y, const int64_t *__restrict__ topk_idx,
+    const int32_t *__restrict__ expert_slot, uint8_t *__restrict__ codes,
+    float *__restrict__ headers, uint32_t *status)
+{
+    __shared__ double s_T[128];
+    build_log2_table(s_T);
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t item = blockIdx.x * kWaves + wave; // host keeps N * nchunks < 2^31
+    if (item >= (uint32_t)N * (uint32_t)nchunks)
+        return;
+    const uint32_t t = item / (uint32_t)nchunks;
+    const int32_t chunk = (int32_t)(item - t * (uint32_t)nchunks);
+    const LfLane l = lf_lane(H, chunk, lane);
+    const int32_t ch = l.active ? l.ch : 0; // lanes past the row end read channel 0 (unused)
+    uint32_t flags = 0;
+    const int64_t *idx_t = topk_idx + (size_t)t * K;
+    const int32_t *slot_t = expert_slot + (size_t)t * K;
+    for (int k0 = 0; k0 < K; k0 += KB) {
+        int64_t row[KB];
+        float unused[KB];
+        fetch_entries<KB>(idx_t, slot_t, nullptr, k0, K, E, rows, lane, row, unused, flags);
+        uint4 a0[KB], a1[KB];
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(y + (size_t)max(row[b], (int64_t)0) * H + ch);
+            a0[b] = load_stream(src);
+            a1[b] = load_stream(src + 1);
+        }
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+            if (row[b] < 0)
+                continue;
+            uint4 c;
+            float lo, hi;
+            encode_lane(a0[b], a1[b], s_T, c, lo, hi);
+            if (l.active) {
+                *reinterpret_cast<uint4 *>(codes + (size_t)row[b] * H + l.ch) = c;
+                if ((lane & 7) == 0)
+                    *reinterpret_cast<float2 *>(headers + ((size_t)row[b] * l.G + l.g) * 2) =
+                        make_float2(lo, hi);
+            }
+        }
+    }
+    if (flags && status && lane == 0 && chunk == 0)
+        atomicOr(status, flags);
+}
+
+// Decode one lane's 16 codes and add w * value to acc (ascending channel).
+__device__ __forceinline__ void fma_decoded(float (&acc)[16], float w, const uint4 &c, float lo,
+                                            float hi)
+{
+    const float step = (hi - lo) / 126.0f; // correctly rounded division
+    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t code = (cw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+        const uint32_t m = code & 0x7Fu;
+        const float d = lo + (float)((int)m - 1) * step;
+        const float mag = m ? exp2f(d) : 0.0f;
+        acc[i] = fmaf(w, (code & 0x80u) ? -mag : mag, acc[i]);
+    }
+}
+
+template <int KB, bool BIAS, class Rows>
+__global__ __launch_bounds__(kThreads) void logfmt_combine_kernel(
+    int32_t N, int32_t H, int32_t K, int32_t E, int32_t nchunks, Rows rows,
+    const uint8_t *__restrict__ codes, const float *__restrict__ headers,
+    const int64_t *__restrict__ topk_idx, const float *__restrict__ topk_weights,
+    const int32_t *__restrict__ expert_slot, const uint16_t *__restrict__ bias,
+    uint16_t *__restrict__ out, uint32_t *status)
+{
+    const int lane = threadIdx.x & 63;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t item = blockIdx.x * kWaves + wave; // host keeps N * nchunks < 2^31
+    if (item >= (uint32_t)N * (uint32_t)nchunks)
+        return;
+    const uint32_t t = item / (uint32_t)nchunks;
+    const int32_t chunk = (int32_t)(item - t * (uint32_t)nchunks);
+    const LfLane l = lf_lane(H, chunk, lane);
+    const int32_t ch = l.active ? l.ch : 0;
+    const int32_t g = l.active ? l.g : 0;
+    uint4 b0 = make_uint4(0, 0, 0, 0), b1 = make_uint4(0, 0, 0, 0);
+    if (BIAS) {
+        const uint4 *br = reinterpret_cast<const uint4 *>(bias + (size_t)t * H + ch);
+        b0 = load_stream(br);
+        b1 = load_stream(br + 1);
+    }
+    float acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        acc[i] = 0.0f;
+    uint32_t flags = 0;
+    const int64_t *idx_t = topk_idx + (size_t)t * K;
+    const int32_t *slot_t = expert_slot + (size_t)t * K;
+    const float *w_t = topk_weights + (size_t)t * K;
+    const int32_t G = H / 128;
+    for (int k0 = 0; k0 < K; k0 += KB) {
+        int64_t row[KB];
+        float wk[KB];
+        fetch_entries<KB>(idx_t, slot_t, w_t, k0, K, E, rows, lane, row, wk, flags);
+        // every row's codes and header of the batch in flight before the
+        // first decode; an entry without a row reads row 0 and is not added
+        uint4 c[KB];
+        float2 hd[KB];
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+            const size_t r = (size_t)max(row[b], (int64_t)0);
+            c[b] = load_stream(reinterpret_cast<const uint4 *>(codes + r * H + ch));
+            hd[b] = *reinterpret_cast<const float2 *>(headers + (r * G + g) * 2);
+        }
+#pragma unroll
+        for (int b = 0; b < KB; ++b)
+            if (row[b] >= 0)
+                fma_decoded(acc, wk[b], c[b], hd[b].x, hd[b].y);
+    }
+    if (BIAS) {
+        const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            acc[2 * i] = acc[2 * i] + bf16_lo(bw[i]);
+            acc[2 * i + 1] = acc[2 * i + 1] + bf16_hi(bw[i]);
+        }
+    }
+    if (l.active) {
+        uint4 *dst = reinterpret_cast<uint4 *>(out + (size_t)t * H + l.ch);
+        dst[0] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                            pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+        dst[1] = make_uint4(pack_bf16x2(acc[8], acc[9]), pack_bf16x2(acc[10], acc[11]),
+                            pack_bf16x2(acc[12], acc[13]), pack_bf16x2(acc[14], acc[15]));
+    }
+    if (flags && status && lane == 0 && chunk == 0)
+        atomicOr(status, flags);
+}
+
+__global__ __launch_bounds__(kThreads) void log2_probe_kernel(const uint16_t *__restrict__ bits,
+                                                              float *__restrict__ out, int64_t n)
+{
+    __shared__ double s_T[128];
+    build_log2_table(s_T);
+    __syncthreads();
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n)
+        return;
+    const uint32_t mag = bits[i] & 0x7FFFu;
+    out[i] = mag ? log2_rn_bf16(mag, s_T) : -__builtin_inff();
+}
+
+} // namespace
+
+hipError_t launch_logfmt_encode(const ep_shape &s, const uint16_t *expert_out,
+                                const int64_t *topk_idx, const int32_t *expert_slot,
+                                uint8_t *codes, float *headers, uint32_t *status,
+                                hipStream_t stream)
+{
+    const int N = s.num_tokens, H = s.hidden, K = s.num_topk, E = s.num_experts;
+    if (N == 0)
+        return hipSuccess;
+    const int nchunks = (H + kChunk - 1) / kChunk;
+    const dim3 grid((unsigned)(((int64_t)N * nchunks + kWaves - 1) / kWaves));
+    hipLaunchKernelGGL((logfmt_encode_kernel<kKB, DenseRows>), grid, dim3(kThreads), 0, stream, N, H,
+                       K, E, nchunks, DenseRows{s.expert_capacity}, expert_out, topk_idx,
+                       expert_slot, codes, headers, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_logfmt(const ep_shape &s, const uint8_t *codes, const float *headers,
+                                 const int64_t *topk_idx, const float *topk_weights,
+                                 const int32_t *expert_slot, const uint16_t *bias,
+                                 uint16_t *combined_x, uint32_t *status, hipStream_t stream)
+{
+    const int N = s.num_tokens, H = s.hidden, K = s.num_topk, E = s.num_experts;
+    if (N == 0)
+        return hipSuccess;
+    const int nchunks = (H + kChunk - 1) / kChunk;
+    const dim3 grid((unsigned)(((int64_t)N * nchunks + kWaves - 1) / kWaves));
+#define EP_LF_COMBINE(KB, BIAS)                                                                    \
+    hipLaunchKernelGGL((logfmt_combine_kernel<KB, BIAS, DenseRows>), grid, dim3(kThreads), 0,      \
+                       stream, N, H, K, E, nchunks, DenseRows{s.expert_capacity}, codes, headers,  \
+                       topk_idx, topk_weights, expert_slot, bias, combined_x, status)
+    if (bias) {
+        if (K <= 4)
+            EP_LF_COMBINE(4, true);
+        else
+            EP_LF_COMBINE(8, true);
+    } else {
+        if (K <= 4)
+            EP_LF_COMBINE(4, false);
+        else
+            EP_LF_COMBINE(8, false);
+    }
+#undef EP_LF_COMBINE
+    return hipGetLastError();
+}
+
+} // namespace ep
+
+extern "C" int ep_probe_log2_bf16(const uint16_t *bits, float *out, int64_t n, void *stream)
+{
+    if (n < 0)
+        return EP_ERR_SHAPE;
+    if (n == 0)
+        return EP_OK;
+    if (!bits || !out)
+        return EP_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(bits) & 1) || (reinterpret_cast<uintptr_t>(out) & 3))
+        return EP_ERR_ALIGN;
+    const dim3 grid((unsigned)((n + ep::kThreads - 1) / ep::kThreads));
+    hipLaunchKernelGGL(ep::log2_probe_kernel, grid, dim3(ep::kThreads), 0,
+                       static_cast<hipStream_t>(stream), bits, out, n);
+    return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
+}

@@ -3,7 +3,8 @@
 Same entry points as the C ABI: ``ep_query_sizes``, ``ep_layout``, ``ep_layout_noalloc``,
 ``ep_dispatch``, ``ep_layout_dispatch``, ``ep_combine``, ``ep_dispatch_expand``,
 ``ep_combine_expand``, ``ep_dispatch_normal``, ``ep_combine_normal``,
-``ep_group_limited_topk``, ``ep_strerror`` (plus ``ep_probe_e4m3fn`` from
+``ep_group_limited_topk``, ``ep_logfmt_encode``, ``ep_combine_logfmt``,
+``ep_strerror`` (plus ``ep_probe_e4m3fn`` and ``ep_probe_log2_bf16`` from
 include/ep_probe.h); and ``layout`` / ``dispatch`` / ``combine``, the path in
 three calls that allocate their outputs.  Functions take torch tensors that
 already live on the GPU, check dtype / device / contiguity, and pass
@@ -49,11 +50,13 @@ SIZE_FIELDS = ("recv_x", "recv_scales", "recv_src_idx", "expert_out", "combined_
                "expert_slot", "rank_slot", "expert_offset", "layout_workspace",
                "recv_x_normal", "recv_scales_normal", "recv_topk_idx", "recv_topk_weights",
                "recv_src_idx_normal", "expert_out_normal", "combined_topk_weights",
-               "recv_x_expand", "recv_scales_expand", "recv_src_idx_expand", "expert_out_expand")
+               "recv_x_expand", "recv_scales_expand", "recv_src_idx_expand", "expert_out_expand",
+               "logfmt_codes", "logfmt_headers")
 EXPORTED = ("ep_query_sizes", "ep_layout", "ep_layout_noalloc", "ep_dispatch", "ep_layout_dispatch", "ep_combine",
             "ep_dispatch_expand",
             "ep_combine_expand", "ep_dispatch_normal", "ep_combine_normal",
-            "ep_group_limited_topk", "ep_strerror", "ep_probe_e4m3fn")
+            "ep_group_limited_topk", "ep_logfmt_encode", "ep_combine_logfmt", "ep_strerror",
+            "ep_probe_e4m3fn", "ep_probe_log2_bf16")
 EP_MAX_GROUPS = 64
 EP_GATE_MAX_SOFTMAX = 0
 EP_GATE_SUM_SIGMOID = 1
@@ -99,6 +102,9 @@ def lib() -> ctypes.CDLL:
         L.ep_combine_normal.argtypes = [sp] + [vp] * 8
         L.ep_group_limited_topk.argtypes = [sp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32] + [vp] * 4
         L.ep_probe_e4m3fn.argtypes = [vp, vp, vp, i64, vp]
+        L.ep_probe_log2_bf16.argtypes = [vp, vp, i64, vp]
+        L.ep_logfmt_encode.argtypes = [sp] + [vp] * 7
+        L.ep_combine_logfmt.argtypes = [sp] + [vp] * 9
         L.ep_strerror.argtypes = [ctypes.c_int]
         L.ep_strerror.restype = ctypes.c_char_p
         for name in EXPORTED:
@@ -385,6 +391,52 @@ def ep_group_limited_topk(shape: ep_shape, num_groups: int, topk_groups: int, ru
         raise EpError(rc, "ep_group_limited_topk")
 
 
+def ep_logfmt_encode(shape: ep_shape, expert_out: torch.Tensor, topk_idx: torch.Tensor,
+                     expert_slot: torch.Tensor, codes: torch.Tensor, headers: torch.Tensor,
+                     status: Optional[torch.Tensor] = None, stream=None) -> None:
+    """LogFMT encoding of the routed expert-output rows; see
+    ``ep_logfmt_encode`` in include/ep.h."""
+    N, H, K, E, S = (shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts,
+                     shape.expert_capacity)
+    rc = lib().ep_logfmt_encode(
+        ctypes.byref(shape), _ptr(expert_out, "expert_out", _BF16, E * S * H),
+        _ptr(topk_idx, "topk_idx", _I64, N * K), _ptr(expert_slot, "expert_slot", _I32, N * K),
+        _ptr(codes, "codes", (torch.uint8,), E * S * H),
+        _ptr(headers, "headers", _F32, E * S * (H // 128) * 2), _ptr(status, "status", _STATUS, 1),
+        _stream(stream, codes))
+    if rc != EP_OK:
+        raise EpError(rc, "ep_logfmt_encode")
+
+
+def ep_combine_logfmt(shape: ep_shape, codes: torch.Tensor, headers: torch.Tensor,
+                      topk_idx: torch.Tensor, topk_weights: torch.Tensor, expert_slot: torch.Tensor,
+                      combined_x: torch.Tensor, status: Optional[torch.Tensor] = None, stream=None,
+                      bias: Optional[torch.Tensor] = None) -> None:
+    """Combine of LogFMT expert outputs; see ``ep_combine_logfmt`` in
+    include/ep.h."""
+    N, H, K, E, S = (shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts,
+                     shape.expert_capacity)
+    rc = lib().ep_combine_logfmt(
+        ctypes.byref(shape), _ptr(codes, "codes", (torch.uint8,), E * S * H),
+        _ptr(headers, "headers", _F32, E * S * (H // 128) * 2),
+        _ptr(topk_idx, "topk_idx", _I64, N * K), _ptr(topk_weights, "topk_weights", _F32, N * K),
+        _ptr(expert_slot, "expert_slot", _I32, N * K), _ptr(bias, "bias", _BF16, N * H),
+        _ptr(combined_x, "combined_x", _BF16, N * H), _ptr(status, "status", _STATUS, 1),
+        _stream(stream, combined_x))
+    if rc != EP_OK:
+        raise EpError(rc, "ep_combine_logfmt")
+
+
+def ep_probe_log2_bf16(bits: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """The LogFMT encoder's rounded log2 over an array of bf16 patterns; see
+    include/ep_probe.h."""
+    n = bits.numel()
+    rc = lib().ep_probe_log2_bf16(_ptr(bits, "bits", _BF16), _ptr(out, "out", _F32, n),
+                                  ctypes.c_int64(n), _stream(stream, bits))
+    if rc != EP_OK:
+        raise EpError(rc, "ep_probe_log2_bf16")
+
+
 def ep_probe_e4m3fn(values: torch.Tensor, out_hw: Optional[torch.Tensor],
                     out_sw: Optional[torch.Tensor], stream=None) -> None:
     """The pack's clamp + FP8 conversion over an array; see include/ep_probe.h."""
@@ -429,6 +481,11 @@ def allocate(shape: ep_shape, device="cuda", parts=("layout", "dispatch", "combi
         })
     if "combine" in parts:
         out["combined_x"] = torch.empty((N, H), dtype=torch.int16, device=dev)
+    if "logfmt" in parts:
+        out.update({
+            "logfmt_codes": torch.empty((E, S, H), dtype=torch.uint8, device=dev),
+            "logfmt_headers": torch.empty((E, S, H // 128, 2), dtype=torch.float32, device=dev),
+        })
     if "expert_out" in parts:
         out["expert_out"] = torch.empty((E, S, H), dtype=torch.int16, device=dev)
     rx_dtype = torch.uint8 if shape.use_fp8 else torch.int16

@@ -150,6 +150,9 @@ typedef struct {
     size_t recv_scales_expand;    /* T*(H/128)*4, T*ceil(H/512)*4 (UE8M0), or 0       */
     size_t recv_src_idx_expand;   /* T*4                                              */
     size_t expert_out_expand;     /* T*H*2: bf16 rows read by ep_combine_expand       */
+    /* LogFMT combine payload (H % 128 == 0, else 0):                          */
+    size_t logfmt_codes;          /* E*S*H: one code byte per channel                 */
+    size_t logfmt_headers;        /* E*S*(H/128)*8: (lo, hi) fp32 per 128 channels    */
 } ep_sizes;
 
 /* Host only.  Fills `out` (host) with the byte size of every buffer for
@@ -276,6 +279,44 @@ int ep_layout_dispatch(const ep_shape *shape, const int64_t *topk_idx, const uin
 int ep_combine(const ep_shape *shape, const uint16_t *expert_out, const int64_t *topk_idx,
                const float *topk_weights, const int32_t *expert_slot, const uint16_t *bias,
                uint16_t *combined_x, uint32_t *status, void *stream);
+
+/* LogFMT combine payload ([V1] §6.2: the low-latency combine message is a
+ * min/max header per 128 channels followed by the hidden data; [V1] §7.1:
+ * the low-latency test's LogFMT combine).  The pages define no more; the
+ * format used (8 bits per channel, logarithmic):
+ *   L(a)   = log2(a) rounded to the nearest binary32 (a > 0);
+ *   header = per 128-channel block b: lo = min, hi = max of L(|x|) over the
+ *            block's nonzero channels (0, 0 when there are none);
+ *   code   = bit 7 the sign, bits 0..6 m: m = 0 for a zero, otherwise
+ *            m = 1 + rint(RN(RN(L(|x|) - lo) * RN(126 / (hi - lo)))) clamped to
+ *            [1, 127] (rint: ties to even; m = 1 when hi == lo), each RN a
+ *            binary32 rounding;
+ *   value  = sign * 2^RN(lo + RN((m - 1) * RN((hi - lo) / 126))), 0 for m = 0
+ *            (within half a log-domain step, (hi - lo) / 252, of |x|).
+ * Requires H % 128 == 0 (EP_ERR_SHAPE otherwise) and finite inputs. */
+
+/* Encode the expert outputs the routing references: for every valid entry
+ * (t, k) with expert e and slot j = expert_slot[t,k] < S, row (e, j) of
+ * expert_out [E, S, H] bf16 becomes codes [E, S, H] uint8 (16-byte aligned)
+ * and headers [E, S, H/128, 2] fp32 (lo, hi; 8-byte aligned).  Other rows are
+ * not written.  Status bits as ep_combine. */
+int ep_logfmt_encode(const ep_shape *shape, const uint16_t *expert_out, const int64_t *topk_idx,
+                     const int32_t *expert_slot, uint8_t *codes, float *headers,
+                     uint32_t *status, void *stream);
+
+/* Combine of LogFMT expert outputs: as ep_combine, with each expert value
+ * the decoded float of its code (codes [E, S, H], headers [E, S, H/128, 2]
+ * from ep_logfmt_encode):
+ *   acc = +0; for k = 0..K-1 with a valid expert e and slot j:
+ *       acc = fmaf(topk_weights[t,k], value(codes[e][j][c], header[e][j][c/128]), acc);
+ *   acc = acc + float(bias[t][c]) (when bias is not NULL);
+ *   combined_x[t,c] = bf16 round-to-nearest-even(acc).
+ * The exponential is the device's fp32 exp2f (within an ulp of the binary32
+ * rounding of the definition). */
+int ep_combine_logfmt(const ep_shape *shape, const uint8_t *codes, const float *headers,
+                      const int64_t *topk_idx, const float *topk_weights,
+                      const int32_t *expert_slot, const uint16_t *bias, uint16_t *combined_x,
+                      uint32_t *status, void *stream);
 
 /* Dispatch pack into the expand layout ([ASC] "Dispatch's Three Phases and
  * FP8 Compression", phase 1: each token is cloned once per routed expert, the

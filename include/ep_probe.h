@@ -8,6 +8,10 @@
  * a test can compare it, value by value, against an independent encoder over
  * every binary32 input the pack can produce.  It is not part of the
  * dispatch/combine path.
+ *
+ * ep_probe_log2_bf16 applies the LogFMT encoder's logarithm (log2 rounded to
+ * the nearest binary32, of a bf16 magnitude) to an array, so a test can check
+ * it against the correctly rounded value for every bf16 input.
  */
 #ifndef EP_MI355X_PROBE_H
 #define EP_MI355X_PROBE_H
@@ -24,6 +28,13 @@ extern "C" {
  * n % 4 == 0, pointers 16-byte aligned.  Enqueued on `stream`; returns
  * EP_OK, EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_ALIGN or EP_ERR_HIP (ep.h). */
 int ep_probe_e4m3fn(const float *in, uint8_t *out_hw, uint8_t *out_sw, int64_t n, void *stream);
+
+/* bits [n] bf16 patterns (device, 2-byte aligned), out [n] float (device,
+ * 4-byte aligned): out[i] = log2(|x_i|) rounded to the nearest binary32 as
+ * the LogFMT encoder computes it, -inf for a zero.  Inputs must be finite.
+ * Returns EP_OK, EP_ERR_NULL, EP_ERR_SHAPE (n < 0), EP_ERR_ALIGN or
+ * EP_ERR_HIP. */
+int ep_probe_log2_bf16(const uint16_t *bits, float *out, int64_t n, void *stream);
 
 #ifdef __cplusplus
 }
