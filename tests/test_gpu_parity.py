@@ -292,6 +292,48 @@ EDGE = [
 ]
 
 
+# layout shapes across the kernels' forms: 2 to 33 blocks of 256 tokens, the
+# 16- and 32-entry register forms (K = 16, 17), scalar rank rows (R = 6), 64
+# ranks on skewed ids (many lanes of a wave on one expert), repeated experts,
+# E = 1024, with a bad id in each, against the oracle
+LAYOUT_FORMS = [  # (name, N, K, E, R, mask, repeats, alignment)
+    ("32 blocks", 8192, 8, 256, 8, 0.0, False, 0),
+    ("33 blocks", 8193, 8, 256, 8, 0.0, False, 0),
+    ("K=16", 3000, 16, 256, 32, 0.02, False, 0),
+    ("K=17", 3000, 17, 256, 32, 0.02, False, 0),
+    ("R=6 (scalar rank rows)", 3001, 3, 12, 6, 0.1, False, 128),
+    ("R=64 skewed ids", 4096, 6, 64, 64, 0.1, False, 0),
+    ("repeats", 2500, 12, 8, 4, 0.05, True, 0),
+    ("E=1024 R=64", 1500, 8, 1024, 64, 0.0, False, 32),
+    ("2 blocks", 257, 8, 256, 8, 0.0, False, 0),
+]
+
+
+@pytest.mark.parametrize("name,N,K,E,R,mask,repeats,A", LAYOUT_FORMS, ids=[f[0] for f in LAYOUT_FORMS])
+def test_layout_forms(o, name, N, K, E, R, mask, repeats, A):
+    rng = np.random.default_rng(N + K + E + R)
+    if repeats:
+        idx = rng.integers(0, E, size=(N, K)).astype(np.int64)
+    elif name.endswith("skewed ids"):
+        p = 1.0 / np.arange(1, E + 1) ** 1.2
+        keys = np.log(p / p.sum())[None, :] + rng.gumbel(size=(N, E))
+        idx = np.argsort(-keys, axis=1, kind="stable")[:, :K].astype(np.int64)
+    else:
+        idx = np.argsort(rng.random((N, E)), axis=1)[:, :K].astype(np.int64)
+    if mask:
+        idx[rng.random((N, K)) < mask] = -1
+    idx[5, 0] = E + 3  # a bad id: treated as masked and reported
+    S = N * K if repeats else N
+    shape = ep.make_shape(N, 128, K, E, R, N, S, False, ep.EP_SCALE_FP32, A)
+    say(f"ep_layout {name} N={N} K={K} E={E} R={R} A={A}")
+    run = LayoutRun(shape, idx)
+    got = run.numpy()
+    want = o.layout(idx, E, R, alignment=max(A, 1))
+    for key in LAYOUT_KEYS:
+        assert np.array_equal(got[key], want[key]), (name, key, first_diff(got[key], want[key]))
+    assert got["status"] == want["status"] == ep.EP_STATUS_BAD_EXPERT_ID
+
+
 @pytest.mark.parametrize("name,kw", EDGE, ids=[e[0] for e in EDGE])
 def test_edge_shapes(o, name, kw):
     _edge(o, name, **kw)

@@ -50,10 +50,10 @@ def routing(wid, num_tokens):
     return ep.shape_of(w), inp["topk_idx"]
 
 
-# the first call uses the most histogram rows, each later one fewer (and the
-# last none), so a call that read a row its own count kernel did not write
-# would see the previous call's contents
-SEQUENCE = [(4, 16384), (3, 4096), (5, 1000), (3, 300), (2, 128)]
+# each call uses fewer histogram rows than the one before (the last none), so
+# a call that read a row its own count kernel did not write would see the
+# previous call's contents
+SEQUENCE = [(4, 16384), (4, 12000), (3, 4096), (5, 1000), (3, 300), (2, 128)]
 
 
 @pytest.mark.parametrize("stream_kind", ["current", "side"])
