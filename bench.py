@@ -163,6 +163,24 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
         if scrub is not None:
             torch.sum(scrub, dim=0, out=scrub_out)
 
+    # the timing loops re-issue prepared calls (arguments checked and
+    # converted once, on torch's current stream); the graph capture below
+    # uses the plain binding, which takes the capture stream
+    plain = {"layout": layout, "dispatch": dispatch, "combine": combine,
+             "layout_dispatch": layout_dispatch}
+    layout = ep.prepare(ep.ep_layout, shape, topk_idx, buf["num_tokens_per_rank"],
+                        buf["num_tokens_per_expert"], buf["is_token_in_rank"], buf["expert_slot"],
+                        buf["rank_slot"], buf["expert_offset"], buf["workspace"], buf["status"])
+    dispatch = ep.prepare(ep.ep_dispatch, shape, x, topk_idx, buf["expert_slot"], buf["recv_x"],
+                          buf["recv_scales"], buf["recv_src_idx"], buf["status"])
+    combine = ep.prepare(ep.ep_combine, shape, y, topk_idx, topk_weights, buf["expert_slot"],
+                         buf["combined_x"], buf["status"])
+    layout_dispatch = ep.prepare(ep.ep_layout_dispatch, shape, topk_idx, x,
+                                 buf["num_tokens_per_rank"], buf["num_tokens_per_expert"],
+                                 buf["is_token_in_rank"], buf["expert_slot"], buf["rank_slot"],
+                                 buf["expert_offset"], buf["workspace"], buf["recv_x"],
+                                 buf["recv_scales"], buf["recv_src_idx"], buf["status"])
+
     def new_events(n):
         # torch creates an event's handle at its first record: record each
         # once here so that no handle is created inside a timed region
@@ -289,14 +307,14 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
     side = torch.cuda.Stream()
     side.wait_stream(stream)
     with torch.cuda.stream(side):
-        layout()
-        dispatch()
-        combine()
+        plain["layout"]()
+        plain["dispatch"]()
+        plain["combine"]()
     stream.wait_stream(side)
     with torch.cuda.graph(graph):
-        layout()
-        dispatch()
-        combine()
+        plain["layout"]()
+        plain["dispatch"]()
+        plain["combine"]()
     torch.cuda.synchronize()
     evs = [new_events(2) for _ in range(steps)]
     for e in evs:
@@ -308,16 +326,23 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
     graph_cold = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
     del graph
 
-    say(f"workload {w.name}: {steps} steps back to back (warm)")
-    e = new_events(2)
-    e[0].record(stream)
-    for _ in range(steps):
-        layout()
-        dispatch()
-        combine()
-    e[1].record(stream)
-    torch.cuda.synchronize()
-    warm_us = e[0].elapsed_time(e[1]) * 1e3 / steps
+    say(f"workload {w.name}: {steps} steps back to back (warm), prepared and plain calls")
+    warm = {}
+    for kind, fns in (("prepared", (layout, dispatch, combine)),
+                      ("plain", (plain["layout"], plain["dispatch"], plain["combine"]))):
+        e = new_events(2)
+        torch.cuda.synchronize()
+        e[0].record(stream)
+        h0 = time.perf_counter()
+        for _ in range(steps):
+            for fn in fns:
+                fn()
+        h1 = time.perf_counter()
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        warm[kind] = {"us_per_step": round(e[0].elapsed_time(e[1]) * 1e3 / steps, 2),
+                      "host_enqueue_us_per_step": round((h1 - h0) * 1e6 / steps, 2)}
+    warm_us = warm["prepared"]["us_per_step"]
     # a plain copy of known size, for scaling counter readings of a profile run
     if scrub is not None:
         half = scrub.numel() // 2
@@ -340,6 +365,7 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
         "phases": {k: stats(v, nbytes[k]) for k, v in phases.items()},
         "kernels": {k: stats(v, nbytes[k]) for k, v in kernels.items()},
         "warm_us_per_step": round(warm_us, 2),
+        "warm": warm,
         "fused": None if fused is None else {
             "step_us_cold": stats(fused["step"], nbytes["total"]),
             "layout_dispatch_us_cold": stats(fused["layout_dispatch"],
@@ -754,6 +780,84 @@ def time_combine_bias(wid, steps, scrub_bytes, say):
         nbytes = nb + (2 * w.num_tokens * w.hidden if b is not None else 0)
         out[label] = {"us_cold_median": round(us, 2), "bytes": nbytes,
                       "gbps_cold": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    torch.cuda.synchronize()
+    if int(buf["status"].item()) != 0:
+        raise RuntimeError(f"device status {int(buf['status'].item())}")
+    return out
+
+
+def logfmt_bytes(n, h, k, p):
+    """Algorithmic bytes of the LogFMT entry points: the encoder reads one bf16
+    expert row and the (id, slot) entry per valid entry's row and writes its
+    codes (1 B per channel) and headers (8 B per 128 channels); the LogFMT
+    combine reads those codes and headers per valid entry plus idx + slot +
+    weight per entry, and writes one bf16 output row per token."""
+    payload = h + 8 * (h // 128)
+    return {"encode": p * (2 * h + payload) + 12 * n * k,
+            "combine_logfmt": p * payload + 16 * n * k + 2 * n * h}
+
+
+def time_logfmt(wid, steps, scrub_bytes, say, batch=10):
+    """The LogFMT combine payload on workload ``wid``: the encoder (expert
+    side) and the LogFMT combine, each cold (one launch after an eviction)
+    and back to back, beside the BF16 combine of the same expert outputs in
+    the same run.  Expert outputs are bf16 N(0, 1) in every row."""
+    import torch
+    from combine_ep_layout_02_amd import ep
+    from combine_ep_layout_02_amd import workloads as W
+
+    w = W.WORKLOADS[wid]
+    inp = W.make_inputs(w.scaled(w.num_tokens, 128))  # the routing; no activations needed
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    shape = ep.shape_of(w)
+    N, H, K, E, S = w.num_tokens, w.hidden, w.num_topk, w.num_experts, w.expert_capacity
+    topk_idx = torch.from_numpy(inp["topk_idx"]).to(dev)
+    topk_weights = torch.from_numpy(inp["topk_weights"]).to(dev)
+    buf = ep.allocate(shape, dev, parts=("layout", "combine", "logfmt"))
+    ep.ep_layout(shape, topk_idx, buf["num_tokens_per_rank"], buf["num_tokens_per_expert"],
+                 buf["is_token_in_rank"], buf["expert_slot"], buf["rank_slot"],
+                 buf["expert_offset"], buf["workspace"], buf["status"])
+    g = torch.Generator(device=dev)
+    g.manual_seed(2500 + wid)
+    y = torch.randn((E, S, H), dtype=torch.bfloat16, device=dev, generator=g).view(torch.int16)
+    scrub = torch.ones(scrub_bytes // 4, dtype=torch.float32, device=dev) if scrub_bytes else None
+    scrub_out = torch.zeros((), dtype=torch.float32, device=dev)
+
+    def evict():
+        if scrub is not None:
+            torch.sum(scrub, dim=0, out=scrub_out)
+
+    def encode():
+        ep.ep_logfmt_encode(shape, y, topk_idx, buf["expert_slot"], buf["logfmt_codes"],
+                            buf["logfmt_headers"], buf["status"])
+
+    def combine_logfmt():
+        ep.ep_combine_logfmt(shape, buf["logfmt_codes"], buf["logfmt_headers"], topk_idx,
+                             topk_weights, buf["expert_slot"], buf["combined_x"], buf["status"])
+
+    def combine_bf16():
+        ep.ep_combine(shape, y, topk_idx, topk_weights, buf["expert_slot"], buf["combined_x"],
+                      buf["status"])
+
+    encode()
+    combine_logfmt()
+    torch.cuda.synchronize()
+    if int(buf["status"].item()) != 0:
+        raise RuntimeError(f"device status {int(buf['status'].item())}")
+    P = inp["num_valid"]
+    nb = logfmt_bytes(N, H, K, P)
+    nb["combine_bf16"] = algorithmic_bytes(N, H, K, E, w.num_ranks, P, w.use_fp8)["combine"]
+    out = {"workload": w.name, "bytes": nb,
+           "combine_bytes_saved": nb["combine_bf16"] - nb["combine_logfmt"]}
+    for name, fn in (("encode", encode), ("combine_logfmt", combine_logfmt),
+                     ("combine_bf16", combine_bf16)):
+        say(f"{name} {w.name}: {steps} cold launches, {steps} x {batch} back to back")
+        cold = _timed_cold(fn, steps, evict, stream)
+        b2b = _timed_batches(fn, steps, batch, evict, stream)
+        out[name] = {"us_cold_median": round(cold, 2), "us_back_to_back_mean": round(b2b, 2),
+                     "gbps_back_to_back": round(nb[name] / (b2b * 1e-6) / 1e9, 1),
+                     "frac_of_peak_back_to_back": round(nb[name] / (b2b * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
     torch.cuda.synchronize()
     if int(buf["status"].item()) != 0:
         raise RuntimeError(f"device status {int(buf['status'].item())}")
@@ -1272,7 +1376,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-scale-formats", action="store_true",
                     help="skip the per-variant timings (ep_dispatch per FP8 scale format, "
-                         "ep_combine with the shared expert's bias)")
+                         "ep_combine with the shared expert's bias, the LogFMT payload)")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip the cold steps of the large and skewed workloads")
     ap.add_argument("--no-receive-layouts", action="store_true",
@@ -1355,6 +1459,7 @@ def main():
         "phases_us_with_events_between": prefill["phases"],
         "kernel_avg_us_back_to_back": prefill["kernels"],
         "step_us_warm": prefill["warm_us_per_step"],
+        "warm_steps_by_call_kind": prefill["warm"],
         "bytes_per_step": prefill["bytes"],
         "dispatch_frac_of_peak": round(prefill["bytes"]["dispatch"] / (pack_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
         "gate_60pct_of_peak_us": round(prefill["bytes"]["total"] / (0.6 * PEAK_HBM_GBPS * 1e9) * 1e6, 1),
@@ -1366,6 +1471,8 @@ def main():
             3, min(args.steps, 20), scrub_bytes, say)
         extra["combine_shared_expert_bias_4096x7168"] = time_combine_bias(
             3, min(args.steps, 20), scrub_bytes, say)
+        for wid, key in ((3, "logfmt_combine_4096x7168"), (2, "logfmt_combine_128x7168")):
+            extra[key] = time_logfmt(wid, min(args.steps, 20), scrub_bytes, say)
     if not args.no_other_configs:
         torch.cuda.empty_cache()
         for wid, key in OTHER_CONFIGS.items():
@@ -1385,6 +1492,7 @@ def main():
             "phases_us_with_events_between": decode["phases"],
             "kernel_avg_us_back_to_back": decode["kernels"],
             "step_us_warm": decode["warm_us_per_step"], "bytes_per_step": decode["bytes"],
+            "warm_steps_by_call_kind": decode["warm"],
             "step_through_ep_layout_dispatch": decode["fused"],
         }
     line = {

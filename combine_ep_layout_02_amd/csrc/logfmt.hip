@@ -30,7 +30,10 @@
 // row of a batch of 8 entries before encoding the first, and writes the
 // codes and headers in place of the bf16 row.  The combine loads every
 // row's codes and header of a batch before decoding the first, then runs
-// the combine's k-ordered fp32 FMA chain.
+// the combine's k-ordered fp32 FMA chain.  The decode (a multiply, an add
+// and an exponential per channel) makes the combine compute-bound on one
+// GPU: it reads 42 % fewer bytes than the BF16 combine and takes about as
+// long; the bytes it saves are link bytes when expert outputs cross GPUs.
 #include "ep_device.h"
 #include "ep_internal.h"
 #include "ep_probe.h"
@@ -186,20 +189,34 @@ __global__ __launch_bounds__(kThreads) void logfmt_encode_kernel(
         atomicOr(status, flags);
 }
 
-// Decode one lane's 16 codes and add w * value to acc (ascending channel).
-__device__ __forceinline__ void fma_decoded(float (&acc)[16], float w, const uint4 &c, float lo,
-                                            float hi)
+// Decode one lane's 16 codes and add w * value to acc, ascending channel.
+// When the block's lo >= -126 every decoded value is a normal float and the
+// hardware exponential is used directly (the branch is uniform over the
+// lane's 16 values); otherwise exp2f, which scales subnormal results.
+template <bool NORMAL>
+__device__ __forceinline__ void fma_decoded_lane(float (&acc)[16], float w, const uint4 &c,
+                                                 float lo, float step)
 {
-    const float step = (hi - lo) / 126.0f; // correctly rounded division
     const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const uint32_t code = (cw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
         const uint32_t m = code & 0x7Fu;
         const float d = lo + (float)((int)m - 1) * step;
-        const float mag = m ? exp2f(d) : 0.0f;
-        acc[i] = fmaf(w, (code & 0x80u) ? -mag : mag, acc[i]);
+        const float e = NORMAL ? __builtin_amdgcn_exp2f(d) : exp2f(d);
+        const float mag = m ? e : 0.0f;
+        acc[i] = fmaf(w, __uint_as_float(__float_as_uint(mag) | ((code & 0x80u) << 24)), acc[i]);
     }
+}
+
+__device__ __forceinline__ void fma_decoded(float (&acc)[16], float w, const uint4 &c, float lo,
+                                            float hi)
+{
+    const float step = (hi - lo) / 126.0f; // correctly rounded division
+    if (lo >= -126.0f)
+        fma_decoded_lane<true>(acc, w, c, lo, step);
+    else
+        fma_decoded_lane<false>(acc, w, c, lo, step);
 }
 
 template <int KB, bool BIAS, class Rows>
@@ -218,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void logfmt_combine_kernel(
     const uint32_t t = item / (uint32_t)nchunks;
     const int32_t chunk = (int32_t)(item - t * (uint32_t)nchunks);
     const LfLane l = lf_lane(H, chunk, lane);
-    const int32_t ch = l.active ? l.ch : 0;
+    const int32_t ch = l.active ? l.ch : 0; // lanes past the row end read channel 0 (unused)
     const int32_t g = l.active ? l.g : 0;
     uint4 b0 = make_uint4(0, 0, 0, 0), b1 = make_uint4(0, 0, 0, 0);
     if (BIAS) {

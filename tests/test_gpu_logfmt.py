@@ -187,6 +187,21 @@ def test_logfmt_bias_masked_and_bad_ids(o):
     run_logfmt(o, shape, idx, wts, rows, "bias + masked + bad id", bias=bias)
 
 
+def test_logfmt_pipelined_with_bias(o):
+    """Batches large enough for the pipelined combine (a wave per run of
+    chunks of one token), with a bias, masked entries and a partial last
+    chunk group: 4,096 tokens x 2,560 channels (3 chunks in groups of 4)."""
+    w = W.WORKLOADS[3].scaled(4096, 2560)
+    inp = W.make_inputs(w, seed=77)
+    idx = inp["topk_idx"].copy()
+    rng = np.random.default_rng(78)
+    idx[rng.random(idx.shape) < 0.1] = -1
+    rows = rows_of_kind(rng, int((idx >= 0).sum()), w.hidden, "zeros")
+    bias = W.bf16_bits(rng.standard_normal((w.num_tokens, w.hidden)).astype(np.float32))
+    run_logfmt(o, ep.shape_of(w), idx, inp["topk_weights"], rows, "pipelined + bias",
+               bias=bias, sample_tokens=300)
+
+
 def test_logfmt_full_size_prefill(o):
     """The prefill workload at full size (4,096 x 7,168, top-8 of 256): codes
     and headers of 3,000 sampled rows bit-exact, the combine of 256 sampled
