@@ -655,6 +655,41 @@ def time_copy_ceiling(steps, say):
             "gbps_read_plus_write": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4)}
 
 
+def gpu_clocks():
+    """Current and top shader (sclk) and memory (mclk) clock levels of the
+    GPUs, from the kernel driver's power-management files (each lists the
+    levels in MHz, the current one marked with '*'); when those are not
+    readable, from rocm-smi.  None when neither source answers."""
+    import glob
+    import subprocess
+
+    out = {}
+    for dev_dir in sorted(glob.glob("/sys/class/drm/card*/device")):
+        entry = {}
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            try:
+                with open(os.path.join(dev_dir, name)) as f:
+                    levels = [ln.strip() for ln in f if ln.strip()]
+            except OSError:
+                continue
+            cur = [ln for ln in levels if ln.endswith("*")]
+            mhz = [int(re.findall(r"(\d+)\s*[Mm][Hh]z", ln)[0]) for ln in levels
+                   if re.findall(r"(\d+)\s*[Mm][Hh]z", ln)]
+            entry[name[7:]] = {"current": cur[0] if cur else None, "max_mhz": max(mhz) if mhz else None}
+        if entry:
+            out[dev_dir.split("/")[-2]] = entry
+    if out:
+        return {"source": "/sys/class/drm/*/device/pp_dpm_{sclk,mclk}", "levels": out}
+    try:
+        res = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                             timeout=30)
+        if res.returncode == 0 and res.stdout.strip().startswith("{"):
+            return {"source": "rocm-smi --showclocks --json", "levels": json.loads(res.stdout)}
+    except (OSError, subprocess.SubprocessError, ValueError):
+        pass
+    return None
+
+
 def device_info():
     """The device and software the figures were measured on."""
     import torch
@@ -663,7 +698,7 @@ def device_info():
     return {"name": p.name, "arch": getattr(p, "gcnArchName", ""),
             "compute_units": p.multi_processor_count,
             "memory_gib": round(p.total_memory / 2 ** 30, 1), "hip": torch.version.hip,
-            "torch": torch.__version__}
+            "torch": torch.__version__, "clocks": gpu_clocks()}
 
 
 def time_gating(wid, steps, scrub_bytes, say):

@@ -19,6 +19,7 @@ import contextlib
 import ctypes
 import dataclasses
 import os
+import threading
 from typing import Optional
 
 import torch
@@ -114,6 +115,55 @@ def lib() -> ctypes.CDLL:
     return _LIB
 
 
+# ---- calls, and calls prepared once for re-issue -----------------------------
+_RECORD = threading.local()
+
+
+def _call(name: str, *args) -> int:
+    """Call entry point ``name`` with converted arguments, or, while
+    ``prepare`` records, keep the call instead of making it."""
+    fn = getattr(lib(), name)
+    calls = getattr(_RECORD, "calls", None)
+    if calls is not None:
+        calls.append((fn, args, name))
+        return EP_OK
+    return fn(*args)
+
+
+class Prepared:
+    """One call of an entry point whose arguments were checked and converted
+    once by ``prepare``: calling it issues the same call again (the same
+    pointers and the same stream), without the per-call checks and
+    conversions of the binding, for loops that re-issue one step many times.
+    The tensors it was prepared with are kept alive here; their storage must
+    not be replaced (an in-place resize would leave a stale pointer)."""
+    __slots__ = ("_fn", "_args", "_name", "_keep")
+
+    def __init__(self, fn, args, name, keep):
+        self._fn, self._args, self._name, self._keep = fn, args, name, keep
+
+    def __call__(self) -> None:
+        rc = self._fn(*self._args)
+        if rc != EP_OK:
+            raise EpError(rc, self._name)
+
+
+def prepare(entry, *args, **kwargs) -> Prepared:
+    """``entry`` (one of this module's ep_* functions) with its arguments,
+    checked and converted now, as a ``Prepared`` call.  ``stream`` defaults
+    to torch's current stream at preparation time."""
+    _RECORD.calls = []
+    try:
+        entry(*args, **kwargs)
+        calls = _RECORD.calls
+    finally:
+        _RECORD.calls = None
+    if len(calls) != 1:
+        raise ValueError(f"{getattr(entry, '__name__', entry)} is not a launching entry point")
+    fn, cargs, name = calls[0]
+    return Prepared(fn, cargs, name, (args, kwargs))
+
+
 def make_shape(num_tokens: int, hidden: int, num_topk: int, num_experts: int, num_ranks: int,
                num_max_dispatch_tokens_per_rank: int, expert_capacity: int,
                use_fp8: bool, scale_format: int = EP_SCALE_FP32,
@@ -193,7 +243,7 @@ def ep_layout(shape: ep_shape, topk_idx: torch.Tensor, num_tokens_per_rank: torc
     """Dispatch layout; see ``ep_layout`` in include/ep.h."""
     N, K, E, R = shape.num_tokens, shape.num_topk, shape.num_experts, shape.num_ranks
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib().ep_layout(
+    rc = _call("ep_layout", 
         ctypes.byref(shape), _ptr(topk_idx, "topk_idx", _I64, N * K),
         _ptr(num_tokens_per_rank, "num_tokens_per_rank", _I32, R),
         _ptr(num_tokens_per_expert, "num_tokens_per_expert", _I32, E),
@@ -214,7 +264,7 @@ def ep_layout_noalloc(shape: ep_shape, topk_idx: torch.Tensor, num_tokens_per_ra
     """Dispatch layout with the library's static per-device scratch instead of
     a workspace; see ``ep_layout_noalloc`` in include/ep.h."""
     N, K, E, R = shape.num_tokens, shape.num_topk, shape.num_experts, shape.num_ranks
-    rc = lib().ep_layout_noalloc(
+    rc = _call("ep_layout_noalloc", 
         ctypes.byref(shape), _ptr(topk_idx, "topk_idx", _I64, N * K),
         _ptr(num_tokens_per_rank, "num_tokens_per_rank", _I32, R),
         _ptr(num_tokens_per_expert, "num_tokens_per_expert", _I32, E),
@@ -235,7 +285,7 @@ def ep_dispatch(shape: ep_shape, x: torch.Tensor, topk_idx: torch.Tensor, expert
         shape.expert_capacity
     rows = E * S
     rx_types = _FP8 if shape.use_fp8 else _BF16
-    rc = lib().ep_dispatch(
+    rc = _call("ep_dispatch", 
         ctypes.byref(shape), _ptr(x, "x", _BF16, N * H), _ptr(topk_idx, "topk_idx", _I64, N * K),
         _ptr(expert_slot, "expert_slot", _I32, N * K), _ptr(recv_x, "recv_x", rx_types, rows * H),
         (_ptr(recv_scales, "recv_scales", _STATUS, rows * ((H // 128 + 3) // 4))
@@ -260,7 +310,7 @@ def ep_layout_dispatch(shape: ep_shape, topk_idx: torch.Tensor, x: torch.Tensor,
         shape.num_ranks, shape.expert_capacity
     rows = E * S
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib().ep_layout_dispatch(
+    rc = _call("ep_layout_dispatch", 
         ctypes.byref(shape), _ptr(topk_idx, "topk_idx", _I64, N * K), _ptr(x, "x", _BF16, N * H),
         _ptr(num_tokens_per_rank, "num_tokens_per_rank", _I32, R),
         _ptr(num_tokens_per_expert, "num_tokens_per_expert", _I32, E),
@@ -290,7 +340,7 @@ def ep_dispatch_expand(shape: ep_shape, x: torch.Tensor, topk_idx: torch.Tensor,
     """Dispatch pack into the expand layout; see ``ep_dispatch_expand`` in include/ep.h."""
     N, H, K, E = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts
     T = expand_rows(shape)
-    rc = lib().ep_dispatch_expand(
+    rc = _call("ep_dispatch_expand", 
         ctypes.byref(shape), _ptr(x, "x", _BF16, N * H), _ptr(topk_idx, "topk_idx", _I64, N * K),
         _ptr(expert_slot, "expert_slot", _I32, N * K),
         _ptr(expert_offset, "expert_offset", _I32, E + 1),
@@ -309,7 +359,7 @@ def ep_combine_expand(shape: ep_shape, expert_out: torch.Tensor, topk_idx: torch
                       bias: Optional[torch.Tensor] = None) -> None:
     """Combine from the expand layout; see ``ep_combine_expand`` in include/ep.h."""
     N, H, K, E = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts
-    rc = lib().ep_combine_expand(
+    rc = _call("ep_combine_expand", 
         ctypes.byref(shape), _ptr(expert_out, "expert_out", _BF16, expand_rows(shape) * H),
         _ptr(topk_idx, "topk_idx", _I64, N * K), _ptr(topk_weights, "topk_weights", _F32, N * K),
         _ptr(expert_slot, "expert_slot", _I32, N * K),
@@ -329,7 +379,7 @@ def ep_dispatch_normal(shape: ep_shape, x: torch.Tensor, topk_idx: torch.Tensor,
     """Normal-mode dispatch; see ``ep_dispatch_normal`` in include/ep.h."""
     N, H, K, R = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_ranks
     rows = R * shape.num_max_dispatch_tokens_per_rank
-    rc = lib().ep_dispatch_normal(
+    rc = _call("ep_dispatch_normal", 
         ctypes.byref(shape), _ptr(x, "x", _BF16, N * H), _ptr(topk_idx, "topk_idx", _I64, N * K),
         _ptr(topk_weights, "topk_weights", _F32, N * K), _ptr(rank_slot, "rank_slot", _I32, N * R),
         _ptr(recv_x, "recv_x", _FP8 if shape.use_fp8 else _BF16, rows * H),
@@ -350,7 +400,7 @@ def ep_combine_normal(shape: ep_shape, x: torch.Tensor, rank_slot: torch.Tensor,
     """Normal-mode combine; see ``ep_combine_normal`` in include/ep.h."""
     N, H, K, R = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_ranks
     rows = R * shape.num_max_dispatch_tokens_per_rank
-    rc = lib().ep_combine_normal(
+    rc = _call("ep_combine_normal", 
         ctypes.byref(shape), _ptr(x, "x", _BF16, rows * H), _ptr(rank_slot, "rank_slot", _I32, N * R),
         _ptr(recv_topk_weights, "recv_topk_weights", _F32, rows * K),
         _ptr(bias, "bias", _BF16, N * H), _ptr(combined_x, "combined_x", _BF16, N * H),
@@ -367,7 +417,7 @@ def ep_combine(shape: ep_shape, expert_out: torch.Tensor, topk_idx: torch.Tensor
     """Combine; see ``ep_combine`` in include/ep.h."""
     N, H, K, E, S = shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts, \
         shape.expert_capacity
-    rc = lib().ep_combine(
+    rc = _call("ep_combine", 
         ctypes.byref(shape), _ptr(expert_out, "expert_out", _BF16, E * S * H),
         _ptr(topk_idx, "topk_idx", _I64, N * K), _ptr(topk_weights, "topk_weights", _F32, N * K),
         _ptr(expert_slot, "expert_slot", _I32, N * K), _ptr(bias, "bias", _BF16, N * H),
@@ -383,7 +433,7 @@ def ep_group_limited_topk(shape: ep_shape, num_groups: int, topk_groups: int, ru
     """Group-limited top-k gating under ``rule`` (EP_GATE_MAX_SOFTMAX or
     EP_GATE_SUM_SIGMOID); see ``ep_group_limited_topk`` in include/ep.h."""
     N, E, K = shape.num_tokens, shape.num_experts, shape.num_topk
-    rc = lib().ep_group_limited_topk(
+    rc = _call("ep_group_limited_topk", 
         ctypes.byref(shape), ctypes.c_int32(int(num_groups)), ctypes.c_int32(int(topk_groups)),
         ctypes.c_int32(int(rule)), _ptr(scores, "scores", _F32, N * E), _ptr(topk_idx, "topk_idx", _I64, N * K),
         _ptr(topk_weights, "topk_weights", _F32, N * K), _stream(stream, topk_idx))
@@ -398,7 +448,7 @@ def ep_logfmt_encode(shape: ep_shape, expert_out: torch.Tensor, topk_idx: torch.
     ``ep_logfmt_encode`` in include/ep.h."""
     N, H, K, E, S = (shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts,
                      shape.expert_capacity)
-    rc = lib().ep_logfmt_encode(
+    rc = _call("ep_logfmt_encode", 
         ctypes.byref(shape), _ptr(expert_out, "expert_out", _BF16, E * S * H),
         _ptr(topk_idx, "topk_idx", _I64, N * K), _ptr(expert_slot, "expert_slot", _I32, N * K),
         _ptr(codes, "codes", (torch.uint8,), E * S * H),
@@ -416,7 +466,7 @@ def ep_combine_logfmt(shape: ep_shape, codes: torch.Tensor, headers: torch.Tenso
     include/ep.h."""
     N, H, K, E, S = (shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts,
                      shape.expert_capacity)
-    rc = lib().ep_combine_logfmt(
+    rc = _call("ep_combine_logfmt", 
         ctypes.byref(shape), _ptr(codes, "codes", (torch.uint8,), E * S * H),
         _ptr(headers, "headers", _F32, E * S * (H // 128) * 2),
         _ptr(topk_idx, "topk_idx", _I64, N * K), _ptr(topk_weights, "topk_weights", _F32, N * K),
@@ -431,7 +481,7 @@ def ep_probe_log2_bf16(bits: torch.Tensor, out: torch.Tensor, stream=None) -> No
     """The LogFMT encoder's rounded log2 over an array of bf16 patterns; see
     include/ep_probe.h."""
     n = bits.numel()
-    rc = lib().ep_probe_log2_bf16(_ptr(bits, "bits", _BF16), _ptr(out, "out", _F32, n),
+    rc = _call("ep_probe_log2_bf16", _ptr(bits, "bits", _BF16), _ptr(out, "out", _F32, n),
                                   ctypes.c_int64(n), _stream(stream, bits))
     if rc != EP_OK:
         raise EpError(rc, "ep_probe_log2_bf16")
@@ -441,7 +491,7 @@ def ep_probe_e4m3fn(values: torch.Tensor, out_hw: Optional[torch.Tensor],
                     out_sw: Optional[torch.Tensor], stream=None) -> None:
     """The pack's clamp + FP8 conversion over an array; see include/ep_probe.h."""
     n = values.numel()
-    rc = lib().ep_probe_e4m3fn(_ptr(values, "values", _F32), _ptr(out_hw, "out_hw", _U8, n),
+    rc = _call("ep_probe_e4m3fn", _ptr(values, "values", _F32), _ptr(out_hw, "out_hw", _U8, n),
                                _ptr(out_sw, "out_sw", _U8, n), ctypes.c_int64(n),
                                _stream(stream, values))
     if rc != EP_OK:

@@ -31,9 +31,15 @@
  * Conventions of every entry point:
  *  - Pointers are DEVICE pointers unless the comment says "host".  The caller
  *    allocates and frees every buffer; each must stay valid until the stream
- *    work completes.  The library never allocates, never synchronises the
- *    host and keeps no mutable global state, so calls are reentrant and may be
- *    captured into a HIP graph.
+ *    work completes.  The library never allocates and never synchronises the
+ *    host.  Its only process-wide state: a per-device memo of how many waves
+ *    of each multi-item combine kernel fit on the GPU (a fact about the
+ *    compiled kernel and the device, from the runtime's occupancy query,
+ *    stored atomically on first use), and ep_layout_noalloc's static scratch
+ *    array with its per-device address (looked up at the first call on a
+ *    device).  Neither changes any result.  Calls are reentrant -- except
+ *    ep_layout_noalloc calls that overlap on one GPU, which share its scratch
+ *    -- and may be captured into a HIP graph.
  *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
  *    null stream).  Entry points return EP_OK once the work is enqueued.
  *  - Static errors (bad shape, capacity, null or misaligned pointer, too small

@@ -703,3 +703,50 @@ def test_three_call_api_side_stream_with_workspace(o):
         want, st_c = o.combine(y_or, inp["topk_idx"], inp["topk_weights"], lay["expert_slot"], E, s_or)
         assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), want)
         assert int(handle.status.item()) == 0
+
+
+def test_prepared_calls_match_plain_calls(o):
+    """ep.prepare: the decode step issued three times as prepared calls gives
+    exactly what the plain binding gives (and the oracle); preparing
+    something that launches nothing is refused."""
+    w = W.WORKLOADS[2]
+    inp = W.make_inputs(w, with_expert_rows=True)
+    shape = ep.shape_of(w)
+    d = torch.device("cuda")
+    idx, x = dev(inp["topk_idx"]), dev(inp["x_bits"])
+    wts = dev(inp["topk_weights"])
+    lay = o.layout(inp["topk_idx"], w.num_experts, w.num_ranks)
+    y = place_expert_rows(inp["expert_rows"], inp["topk_idx"], lay["expert_slot"], w.num_experts,
+                          w.expert_capacity, w.hidden)
+    outs = []
+    for kind in ("plain", "prepared"):
+        b = ep.allocate(shape, d)
+        for v in b.values():  # the same fill in both, so unwritten rows compare equal
+            if v is not None:
+                v.view(torch.uint8).fill_(0x5A)
+        b["status"].zero_()
+        args = {
+            "layout": (ep.ep_layout, shape, idx, b["num_tokens_per_rank"], b["num_tokens_per_expert"],
+                       b["is_token_in_rank"], b["expert_slot"], b["rank_slot"], b["expert_offset"],
+                       b["workspace"], b["status"]),
+            "dispatch": (ep.ep_dispatch, shape, x, idx, b["expert_slot"], b["recv_x"], b["recv_scales"],
+                         b["recv_src_idx"], b["status"]),
+            "combine": (ep.ep_combine, shape, y, idx, wts, b["expert_slot"], b["combined_x"],
+                        b["status"]),
+        }
+        if kind == "plain":
+            for fn, *a in args.values():
+                fn(*a)
+        else:
+            calls = [ep.prepare(fn, *a) for fn, *a in args.values()]
+            for _ in range(3):
+                for c in calls:
+                    c()
+        torch.cuda.synchronize()
+        outs.append({k: host(v.view(torch.uint8) if v.dtype == torch.float32 else v)
+                     for k, v in b.items() if v is not None})
+    for k in outs[0]:
+        assert np.array_equal(outs[0][k], outs[1][k]), k
+    assert np.array_equal(outs[1]["expert_slot"], lay["expert_slot"])
+    with pytest.raises(ValueError):
+        ep.prepare(ep.make_shape, 1, 8, 1, 1, 1, 1, 1, False)
