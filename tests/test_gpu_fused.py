@@ -160,6 +160,15 @@ EDGE = [
     ("N=150 K=10 bf16", 150, 520, 10, 64, 8, False, {}),
     ("N=1024 odd K=5 bf16 H=520", 1024, 520, 5, 32, 8, False, dict(mask=0.05)),
     ("N=1025 (layout and pack)", 1025, 1152, 8, 256, 8, True, {}),
+    ("N=1100 K=1", 1100, 256, 1, 32, 8, True, {}),
+    ("N=1200 R=1", 1200, 128, 4, 16, 1, True, {}),
+    ("N=1300 all masked", 1300, 256, 4, 16, 4, True, dict(mask=1.0)),
+    ("N=1500 K=32 E=1024 R=64", 1500, 128, 32, 1024, 64, False, dict(mask=0.1)),
+    ("N=2000 R=E=64 masked", 2000, 256, 6, 64, 64, True, dict(mask=0.2)),
+    ("N=2049 odd K=5 bf16 H=520", 2049, 520, 5, 32, 8, False, dict(mask=0.05)),
+    ("N=3000 repeats K=12 E=8", 3000, 128, 12, 8, 4, True, dict(repeats=True)),
+    ("N=2500 K=16 E=256 R=32", 2500, 256, 16, 256, 32, True, dict(mask=0.1)),
+    ("N=1111 R=64 E=512", 1111, 128, 8, 512, 64, True, dict(mask=0.05)),
     ("N=600 K=1", 600, 256, 1, 32, 8, True, {}),
     ("N=300 all masked", 300, 256, 4, 16, 4, True, dict(mask=1.0)),
     ("K=32 E=1024 R=64", 150, 128, 32, 1024, 64, False, dict(mask=0.1)),
@@ -207,7 +216,7 @@ def test_fused_both_status_bits_in_one_call(o, N):
     assert bits & ep.EP_STATUS_BAD_EXPERT_ID and bits & ep.EP_STATUS_BAD_SLOT, bits
 
 
-@pytest.mark.parametrize("N", [100, 400])
+@pytest.mark.parametrize("N", [100, 400, 1500])
 def test_fused_ids_on_an_8_byte_boundary(o, N):
     """topk_idx at a base that is 8- but not 16-byte aligned: the kernel
     reads ids one at a time instead of two per load."""
@@ -216,7 +225,7 @@ def test_fused_ids_on_an_8_byte_boundary(o, N):
                 topk_offset=1)
 
 
-@pytest.mark.parametrize("N", [120, 500])
+@pytest.mark.parametrize("N", [120, 500, 2000])
 def test_fused_matches_separate_calls_and_expand_offsets(o, N):
     """With an expert alignment, expert_offset follows it exactly as ep_layout's
     (the totals block counts every token at 120 tokens, sums the count
@@ -224,3 +233,23 @@ def test_fused_matches_separate_calls_and_expand_offsets(o, N):
     x, idx = _random(N, 256, 8, 64, 8, seed=21, mask=0.1)
     shape = ep.make_shape(N, 256, 8, 64, 8, N, N, True, expert_alignment=128)
     check_fused(o, shape, x, idx, "expert alignment 128")
+
+
+@pytest.mark.parametrize("fmt", [ep.EP_SCALE_FP32, ep.EP_SCALE_UE8M0], ids=["fp32", "ue8m0"])
+def test_fused_prefill_full_size(o, fmt):
+    """The prefill workload at full size (4,096 tokens x 7,168, group-limited
+    top-8 of 256 experts over 8 ranks): the layout's two kernels and the
+    pack, every output bit-exact."""
+    w = W.WORKLOADS[3]
+    inp = W.make_inputs(w)
+    check_fused(o, ep.shape_of(w, fmt), inp["x_bits"], inp["topk_idx"], f"full {w.name}")
+
+
+def test_fused_skewed_full_size(o):
+    """The skewed workload at full size (4,096 tokens x 4,096, Zipf top-6 of 64
+    experts over 64 ranks, 10 % masked): one rank per expert, every output
+    bit-exact."""
+    w = W.WORKLOADS[5]
+    inp = W.make_inputs(w)
+    check_fused(o, ep.shape_of(w), inp["x_bits"], inp["topk_idx"], f"full {w.name}")
+
