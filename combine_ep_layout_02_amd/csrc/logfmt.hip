@@ -88,50 +88,94 @@ __device__ __forceinline__ LfLane lf_lane(int32_t H, int32_t chunk, int lane)
     return l;
 }
 
+// L of a normal bf16 magnitude (exponent field 1..255): no branch.  A zero
+// magnitude gives a finite value that the caller discards.
+__device__ __forceinline__ float log2_rn_normal(uint32_t mag, const double *T)
+{
+    return (float)((double)((int)(mag >> 7) - 127) + T[mag & 127u]);
+}
+
+// Minimum / maximum over the 8 lanes of a 128-channel block (lanes 8j..8j+7)
+// with DPP moves: swap neighbours (quad permutation 1,0,3,2), swap pairs
+// (2,3,0,1), then mirror the half-row, which pairs each lane of one quad with
+// a lane of the other.
+constexpr int kDppXor1 = 0xB1;       // quad_perm:[1,0,3,2]
+constexpr int kDppXor2 = 0x4E;       // quad_perm:[2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t min8(uint32_t v)
+{
+    v = min(v, dpp<kDppXor1>(v));
+    v = min(v, dpp<kDppXor2>(v));
+    return min(v, dpp<kDppHalfMirror>(v));
+}
+__device__ __forceinline__ uint32_t max8(uint32_t v)
+{
+    v = max(v, dpp<kDppXor1>(v));
+    v = max(v, dpp<kDppXor2>(v));
+    return max(v, dpp<kDppHalfMirror>(v));
+}
+
 // Encode one lane's 16 channels (in0, in1: bf16 pairs) into 16 code bytes,
 // with the block's (lo, hi) from its 8 lanes.  Called by every lane.
+//
+// L is non-decreasing in the magnitude bits, so lo and hi are L of the
+// block's smallest nonzero and largest magnitude: integer min / max over
+// the bits, then two logarithms per lane.  Lanes holding a subnormal take
+// the general logarithm for all 16 channels; the others, almost always all
+// of them, the branch-free one.  With lo <= L <= hi, RN(L - lo) <= hi - lo and
+// inv <= (126 / (hi - lo)) (1 + 2^-24), so q <= 126 + 2^-17 and rint(q) <= 126:
+// the clamp of the code to [1, 127] never acts on a nonzero channel and is
+// left out.  rint(q) is read off RN(q + 1.5 * 2^23), exact for 0 <= q < 2^22
+// (the sum is rounded to an integer, ties to even, as rint does).
 __device__ __forceinline__ void encode_lane(const uint4 &in0, const uint4 &in1, const double *T,
                                             uint4 &codes, float &lo, float &hi)
 {
     const uint32_t w[8] = {in0.x, in0.y, in0.z, in0.w, in1.x, in1.y, in1.z, in1.w};
-    uint32_t h[16];
+    uint32_t mag[16], sgn[16];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        h[2 * i] = w[i] & 0xFFFFu;
-        h[2 * i + 1] = w[i] >> 16;
+        mag[2 * i] = w[i] & 0x7FFFu;
+        mag[2 * i + 1] = (w[i] >> 16) & 0x7FFFu;
+        sgn[2 * i] = (w[i] >> 8) & 0x80u;
+        sgn[2 * i + 1] = (w[i] >> 24) & 0x80u;
     }
-    float l[16];
-    float lmin = __builtin_inff(), lmax = -__builtin_inff();
+    // smallest nonzero magnitude minus one (a zero wraps to the largest
+    // value and drops out), largest magnitude
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const uint32_t mag = h[i] & 0x7FFFu;
-        l[i] = mag ? log2_rn_bf16(mag, T) : 0.0f;
-        if (mag) {
-            lmin = fminf(lmin, l[i]);
-            lmax = fmaxf(lmax, l[i]);
-        }
+        mn = min(mn, mag[i] - 1u);
+        mx = max(mx, mag[i]);
     }
-    lmin = fminf(lmin, __shfl_xor(lmin, 1, 64));
-    lmax = fmaxf(lmax, __shfl_xor(lmax, 1, 64));
-    lmin = fminf(lmin, __shfl_xor(lmin, 2, 64));
-    lmax = fmaxf(lmax, __shfl_xor(lmax, 2, 64));
-    lmin = fminf(lmin, __shfl_xor(lmin, 4, 64));
-    lmax = fmaxf(lmax, __shfl_xor(lmax, 4, 64));
-    const bool any = lmin <= lmax; // a block with no nonzero channel keeps +inf > -inf
-    lo = any ? lmin : 0.0f;
-    hi = any ? lmax : 0.0f;
+    const bool subnormal = mn < 0x7Fu; // a nonzero magnitude below 2^-126
+    mn = min8(mn);
+    mx = max8(mx);
+    const bool any = mx != 0u;
+    lo = any ? log2_rn_bf16(mn + 1u, T) : 0.0f;
+    hi = any ? log2_rn_bf16(mx, T) : 0.0f;
     const float span = hi - lo;
     const float inv = span > 0.0f ? 126.0f / span : 0.0f; // correctly rounded division
+    float l[16];
+    if (subnormal) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            l[i] = log2_rn_bf16(max(mag[i], 1u), T);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            l[i] = log2_rn_normal(mag[i], T);
+    }
     uint32_t out[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const uint32_t mag = h[i] & 0x7FFFu;
-        uint32_t code = 0u;
-        if (mag) {
-            const float q = (l[i] - lo) * inv;
-            const int m = min(max(1 + (int)__builtin_rintf(q), 1), 127);
-            code = ((h[i] >> 8) & 0x80u) | (uint32_t)m;
-        }
+        const float q = (l[i] - lo) * inv;
+        const uint32_t m = __float_as_uint(q + 12582912.0f) - 0x4B3FFFFFu; // 1 + rint(q)
+        const uint32_t code = mag[i] ? (sgn[i] | m) : 0u;
         out[i >> 2] |= code << (8 * (i & 3));
     }
     codes = make_uint4(out[0], out[1], out[2], out[3]);
@@ -170,14 +214,14 @@ __global__ __launch_bounds__(kThreads) void logfmt_encode_kernel(
             a0[b] = load_stream(src);
             a1[b] = load_stream(src + 1);
         }
+        // every row of the batch is encoded (an entry without a row encodes
+        // row 0 and stores nothing), so no row's loads wait inside a branch
 #pragma unroll
         for (int b = 0; b < KB; ++b) {
-            if (row[b] < 0)
-                continue;
             uint4 c;
             float lo, hi;
             encode_lane(a0[b], a1[b], s_T, c, lo, hi);
-            if (l.active) {
+            if (row[b] >= 0 && l.active) {
                 *reinterpret_cast<uint4 *>(codes + (size_t)row[b] * H + l.ch) = c;
                 if ((lane & 7) == 0)
                     *reinterpret_cast<float2 *>(headers + ((size_t)row[b] * l.G + l.g) * 2) =
