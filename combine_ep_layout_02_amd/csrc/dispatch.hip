@@ -19,7 +19,7 @@
 // destination row, the minimum for each layout.
 //
 // FP8 lane map: 8 lanes per 128-channel block, 16 channels (32 bytes of bf16
-// in, 16 bytes of FP8 out) per lane; the block amax is a 3-step xor-shuffle
+// in, 16 bytes of FP8 out) per lane; the block amax is a 3-step DPP
 // reduction over the 8 lanes.  The block scale is a'/448 or, for the
 // power-of-two formats (V1 guide §6.3, round_scale and use_ue8m0), 2^e with e
 // read off the exponent and mantissa bits of a'; the packed UE8M0 word of
@@ -98,9 +98,7 @@ __device__ __forceinline__ Fp8Payload quantize_regs(const uint4 &in0, const uint
 #pragma unroll
     for (int i = 0; i < 16; ++i)
         amax = fmaxf(amax, fabsf(f[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+    amax = fmax8(amax);
     const float ap = fmaxf(amax, 1e-4f);
     Fp8Payload p;
     float inv;

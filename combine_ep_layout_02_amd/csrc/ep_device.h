@@ -19,6 +19,38 @@ __device__ __forceinline__ uint4 load_stream(const uint4 *p)
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Reductions over the 8 lanes of one 128-channel block (lanes 8j..8j+7) with
+// DPP moves instead of LDS permutes: swap neighbours (quad permutation
+// 1,0,3,2), swap pairs (2,3,0,1), then mirror the half-row, which pairs each
+// lane of one quad with a lane of the other.  Every lane ends with the
+// group's result.
+constexpr int kDppXor1 = 0xB1;        // quad_perm:[1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm:[2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t min8(uint32_t v)
+{
+    v = min(v, dpp<kDppXor1>(v));
+    v = min(v, dpp<kDppXor2>(v));
+    return min(v, dpp<kDppHalfMirror>(v));
+}
+__device__ __forceinline__ uint32_t max8(uint32_t v)
+{
+    v = max(v, dpp<kDppXor1>(v));
+    v = max(v, dpp<kDppXor2>(v));
+    return max(v, dpp<kDppHalfMirror>(v));
+}
+__device__ __forceinline__ float fmax8(float v)
+{
+    v = fmaxf(v, __uint_as_float(dpp<kDppXor1>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp<kDppXor2>(__float_as_uint(v))));
+    return fmaxf(v, __uint_as_float(dpp<kDppHalfMirror>(__float_as_uint(v))));
+}
+
 // bf16 bit pattern (low 16 bits of h) -> float: exact widening.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

@@ -24,8 +24,8 @@
 //
 // Work item = one wave on one (token, 1024-channel chunk), as in the pack
 // and the combine; a lane owns 16 channels (32 bytes of bf16, 16 code bytes)
-// and 8 lanes make one 128-channel block, whose min and max take three
-// xor-shuffles.  The encoder takes the token's routed rows (e, slot) -- each
+// and 8 lanes make one 128-channel block, whose min and max take three DPP
+// moves.  The encoder takes the token's routed rows (e, slot) -- each
 // expert output row is referenced by exactly one (token, k) -- loads every
 // row of a batch of 8 entries before encoding the first, and writes the
 // codes and headers in place of the bf16 row.  The combine loads every
@@ -93,31 +93,6 @@ __device__ __forceinline__ LfLane lf_lane(int32_t H, int32_t chunk, int lane)
 __device__ __forceinline__ float log2_rn_normal(uint32_t mag, const double *T)
 {
     return (float)((double)((int)(mag >> 7) - 127) + T[mag & 127u]);
-}
-
-// Minimum / maximum over the 8 lanes of a 128-channel block (lanes 8j..8j+7)
-// with DPP moves: swap neighbours (quad permutation 1,0,3,2), swap pairs
-// (2,3,0,1), then mirror the half-row, which pairs each lane of one quad with
-// a lane of the other.
-constexpr int kDppXor1 = 0xB1;       // quad_perm:[1,0,3,2]
-constexpr int kDppXor2 = 0x4E;       // quad_perm:[2,3,0,1]
-constexpr int kDppHalfMirror = 0x141; // row_half_mirror
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp(uint32_t v)
-{
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
-}
-__device__ __forceinline__ uint32_t min8(uint32_t v)
-{
-    v = min(v, dpp<kDppXor1>(v));
-    v = min(v, dpp<kDppXor2>(v));
-    return min(v, dpp<kDppHalfMirror>(v));
-}
-__device__ __forceinline__ uint32_t max8(uint32_t v)
-{
-    v = max(v, dpp<kDppXor1>(v));
-    v = max(v, dpp<kDppXor2>(v));
-    return max(v, dpp<kDppHalfMirror>(v));
 }
 
 // Encode one lane's 16 channels (in0, in1: bf16 pairs) into 16 code bytes,
