@@ -23,7 +23,9 @@
 // against the correctly rounded value by ep_probe_log2_bf16.
 //
 // Work item = one wave on one (token, 1024-channel chunk), as in the pack
-// and the combine; a lane owns 16 channels (32 bytes of bf16, 16 code bytes)
+// and the combine (large batches run the encoder as a resident grid whose
+// blocks first build L for all 2^15 magnitudes in LDS and then loop over
+// items); a lane owns 16 channels (32 bytes of bf16, 16 code bytes)
 // and 8 lanes make one 128-channel block, whose min and max take three DPP
 // moves.  The encoder takes the token's routed rows (e, slot) -- each
 // expert output row is referenced by exactly one (token, k) -- loads every
@@ -34,6 +36,9 @@
 // and an exponential per channel) makes the combine compute-bound on one
 // GPU: it reads 42 % fewer bytes than the BF16 combine and takes about as
 // long; the bytes it saves are link bytes when expert outputs cross GPUs.
+#include <algorithm>
+#include <atomic>
+
 #include "ep_device.h"
 #include "ep_internal.h"
 #include "ep_probe.h"
@@ -156,6 +161,50 @@ __device__ __forceinline__ void encode_lane(const uint4 &in0, const uint4 &in1, 
     codes = make_uint4(out[0], out[1], out[2], out[3]);
 }
 
+// encode_lane with every logarithm read from a table of L over all 2^15
+// magnitudes (entry 0 unused), the same values log2_rn_bf16 gives.
+__device__ __forceinline__ void encode_lane_table(const uint4 &in0, const uint4 &in1, const float *L,
+                                            uint4 &codes, float &lo, float &hi)
+{
+    const uint32_t w[8] = {in0.x, in0.y, in0.z, in0.w, in1.x, in1.y, in1.z, in1.w};
+    uint32_t mag[16], sgn[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        mag[2 * i] = w[i] & 0x7FFFu;
+        mag[2 * i + 1] = (w[i] >> 16) & 0x7FFFu;
+        sgn[2 * i] = (w[i] >> 8) & 0x80u;
+        sgn[2 * i + 1] = (w[i] >> 24) & 0x80u;
+    }
+    // smallest nonzero magnitude minus one (a zero wraps to the largest
+    // value and drops out), largest magnitude
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        mn = min(mn, mag[i] - 1u);
+        mx = max(mx, mag[i]);
+    }
+    mn = min8(mn);
+    mx = max8(mx);
+    const bool any = mx != 0u;
+    lo = any ? L[mn + 1u] : 0.0f;
+    hi = any ? L[mx] : 0.0f;
+    const float span = hi - lo;
+    const float inv = span > 0.0f ? 126.0f / span : 0.0f; // correctly rounded division
+    float l[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        l[i] = L[mag[i]];
+    uint32_t out[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float q = (l[i] - lo) * inv;
+        const uint32_t m = __float_as_uint(q + 12582912.0f) - 0x4B3FFFFFu; // 1 + rint(q)
+        const uint32_t code = mag[i] ? (sgn[i] | m) : 0u;
+        out[i >> 2] |= code << (8 * (i & 3));
+    }
+    codes = make_uint4(out[0], out[1], out[2], out[3]);
+}
+
 template <int KB, class Rows>
 __global__ __launch_bounds__(kThreads) void logfmt_encode_kernel(
     int32_t N, int32_t H, int32_t K, int32_t E, int32_t nchunks, Rows rows,
@@ -205,6 +254,76 @@ __global__ __launch_bounds__(kThreads) void logfmt_encode_kernel(
         }
     }
     if (flags && status && lane == 0 && chunk == 0)
+        atomicOr(status, flags);
+}
+
+// The encoder for large batches: blocks of 1,024 threads, one per compute
+// unit, each first building L for every bf16 magnitude in LDS (32,768 floats,
+// 128 KiB, from the same T and the same arithmetic as log2_rn_bf16), then
+// looping over work items (wave w of the grid takes items w, w + G, ...).  A
+// channel's logarithm is then one LDS read: the encoder drops from about 20
+// to about 14 instructions per channel.
+constexpr int kTabThreads = 1024;
+constexpr int kTabWaves = kTabThreads / 64;
+constexpr int kMagnitudes = 1 << 15;
+// Below this many work items the per-item encoder is faster: each table
+// block spends a few microseconds building its table first (at 128 tokens x
+// 7,168: 12.5 us per-item against 22.9 us with the table).
+constexpr int64_t kTableMinItems = 4096;
+
+template <int KB, class Rows>
+__global__ __launch_bounds__(kTabThreads) void logfmt_encode_table_kernel(
+    int32_t N, int32_t H, int32_t K, int32_t E, int32_t nchunks, Rows rows,
+    const uint16_t *__restrict__ y, const int64_t *__restrict__ topk_idx,
+    const int32_t *__restrict__ expert_slot, uint8_t *__restrict__ codes,
+    float *__restrict__ headers, uint32_t *status)
+{
+    __shared__ float s_L[kMagnitudes];
+    __shared__ double s_T[128];
+    build_log2_table(s_T);
+    __syncthreads();
+    for (int m = threadIdx.x; m < kMagnitudes; m += kTabThreads)
+        s_L[m] = m ? log2_rn_bf16((uint32_t)m, s_T) : 0.0f;
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t total = (uint32_t)N * (uint32_t)nchunks; // host keeps it < 2^31
+    const uint32_t G = gridDim.x * kTabWaves;
+    uint32_t flags = 0;
+    for (uint32_t item = blockIdx.x * kTabWaves + wave; item < total; item += G) {
+        const uint32_t t = item / (uint32_t)nchunks;
+        const int32_t chunk = (int32_t)(item - t * (uint32_t)nchunks);
+        const LfLane l = lf_lane(H, chunk, lane);
+        const int32_t ch = l.active ? l.ch : 0;
+        const int64_t *idx_t = topk_idx + (size_t)t * K;
+        const int32_t *slot_t = expert_slot + (size_t)t * K;
+        for (int k0 = 0; k0 < K; k0 += KB) {
+            int64_t row[KB];
+            float unused[KB];
+            fetch_entries<KB>(idx_t, slot_t, nullptr, k0, K, E, rows, lane, row, unused, flags);
+            uint4 a0[KB], a1[KB];
+#pragma unroll
+            for (int b = 0; b < KB; ++b) {
+                const uint4 *src =
+                    reinterpret_cast<const uint4 *>(y + (size_t)max(row[b], (int64_t)0) * H + ch);
+                a0[b] = load_stream(src);
+                a1[b] = load_stream(src + 1);
+            }
+#pragma unroll
+            for (int b = 0; b < KB; ++b) {
+                uint4 c;
+                float lo, hi;
+                encode_lane_table(a0[b], a1[b], s_L, c, lo, hi);
+                if (row[b] >= 0 && l.active) {
+                    *reinterpret_cast<uint4 *>(codes + (size_t)row[b] * H + l.ch) = c;
+                    if ((lane & 7) == 0)
+                        *reinterpret_cast<float2 *>(headers + ((size_t)row[b] * l.G + l.g) * 2) =
+                            make_float2(lo, hi);
+                }
+            }
+        }
+    }
+    if (flags && status && lane == 0)
         atomicOr(status, flags);
 }
 
@@ -324,6 +443,29 @@ __global__ __launch_bounds__(kThreads) void log2_probe_kernel(const uint16_t *__
 
 } // namespace
 
+namespace {
+// Compute units of the current device, memoised per device (0 if unknown).
+int compute_units()
+{
+    constexpr int kDevices = 64;
+    static std::atomic<int> known[kDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return 0;
+    if (dev < kDevices) {
+        const int c = known[dev].load(std::memory_order_relaxed);
+        if (c > 0)
+            return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (dev < kDevices)
+        known[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+} // namespace
+
 hipError_t launch_logfmt_encode(const ep_shape &s, const uint16_t *expert_out,
                                 const int64_t *topk_idx, const int32_t *expert_slot,
                                 uint8_t *codes, float *headers, uint32_t *status,
@@ -333,7 +475,17 @@ hipError_t launch_logfmt_encode(const ep_shape &s, const uint16_t *expert_out,
     if (N == 0)
         return hipSuccess;
     const int nchunks = (H + kChunk - 1) / kChunk;
-    const dim3 grid((unsigned)(((int64_t)N * nchunks + kWaves - 1) / kWaves));
+    const int64_t items = (int64_t)N * nchunks;
+    const int cus = compute_units();
+    if (cus > 0 && items >= kTableMinItems) {
+        const int64_t blocks = std::min<int64_t>(cus, (items + kTabWaves - 1) / kTabWaves);
+        hipLaunchKernelGGL((logfmt_encode_table_kernel<kKB, DenseRows>), dim3((unsigned)blocks),
+                           dim3(kTabThreads), 0, stream, N, H, K, E, nchunks,
+                           DenseRows{s.expert_capacity}, expert_out, topk_idx, expert_slot, codes,
+                           headers, status);
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)((items + kWaves - 1) / kWaves));
     hipLaunchKernelGGL((logfmt_encode_kernel<kKB, DenseRows>), grid, dim3(kThreads), 0, stream, N, H,
                        K, E, nchunks, DenseRows{s.expert_capacity}, expert_out, topk_idx,
                        expert_slot, codes, headers, status);

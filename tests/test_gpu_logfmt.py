@@ -188,9 +188,9 @@ def test_logfmt_bias_masked_and_bad_ids(o):
 
 
 def test_logfmt_pipelined_with_bias(o):
-    """Batches large enough for the pipelined combine (a wave per run of
-    chunks of one token), with a bias, masked entries and a partial last
-    chunk group: 4,096 tokens x 2,560 channels (3 chunks in groups of 4)."""
+    """A batch large enough for the table encoder (4,096 tokens x 2,560
+    channels: 12,288 items), with a bias, masked entries and a partial last
+    chunk (2,560 = 2 x 1,024 + 512)."""
     w = W.WORKLOADS[3].scaled(4096, 2560)
     inp = W.make_inputs(w, seed=77)
     idx = inp["topk_idx"].copy()
@@ -200,6 +200,21 @@ def test_logfmt_pipelined_with_bias(o):
     bias = W.bf16_bits(rng.standard_normal((w.num_tokens, w.hidden)).astype(np.float32))
     run_logfmt(o, ep.shape_of(w), idx, inp["topk_weights"], rows, "pipelined + bias",
                bias=bias, sample_tokens=300)
+
+
+@pytest.mark.parametrize("kind", ["wide", "extremes", "zeros"])
+def test_logfmt_table_encoder_special_values(o, kind):
+    """Rows spanning 2^-60..2^60, rows scaled to subnormal and huge
+    magnitudes, and rows with zero channels and whole zero or constant
+    blocks, at a batch (2,048 tokens x 2,048 channels: 4,096 items) that
+    takes the table encoder: codes and headers bit-exact, as the per-item
+    encoder's are on the small cases."""
+    w = W.WORKLOADS[3].scaled(2048, 2048)
+    inp = W.make_inputs(w, seed=91)
+    rng = np.random.default_rng(92)
+    rows = rows_of_kind(rng, inp["num_valid"], w.hidden, kind)
+    run_logfmt(o, ep.shape_of(w), inp["topk_idx"], inp["topk_weights"], rows,
+               f"table encoder {kind}", sample_tokens=300)
 
 
 def test_logfmt_full_size_prefill(o):
