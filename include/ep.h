@@ -32,12 +32,12 @@
  *  - Pointers are DEVICE pointers unless the comment says "host".  The caller
  *    allocates and frees every buffer; each must stay valid until the stream
  *    work completes.  The library never allocates and never synchronises the
- *    host.  Its only process-wide state: a per-device memo of how many waves
- *    of each multi-item combine kernel fit on the GPU (a fact about the
- *    compiled kernel and the device, from the runtime's occupancy query,
- *    stored atomically on first use), and ep_layout_noalloc's static scratch
- *    array with its per-device address (looked up at the first call on a
- *    device).  Neither changes any result.  Calls are reentrant -- except
+ *    host.  Its only process-wide state: per-device memos of how many waves
+ *    of each multi-item combine kernel fit on the GPU and of the device's
+ *    compute units (facts about the compiled kernels and the device, from the
+ *    runtime's queries, stored atomically on first use), and
+ *    ep_layout_noalloc's static scratch array with its per-device address
+ *    (looked up at the first call on a device).  None changes any result.  Calls are reentrant -- except
  *    ep_layout_noalloc calls that overlap on one GPU, which share its scratch
  *    -- and may be captured into a HIP graph.
  *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
