@@ -187,7 +187,7 @@ def test_logfmt_bias_masked_and_bad_ids(o):
     run_logfmt(o, shape, idx, wts, rows, "bias + masked + bad id", bias=bias)
 
 
-def test_logfmt_pipelined_with_bias(o):
+def test_logfmt_large_batch_with_bias(o):
     """A batch large enough for the table encoder (4,096 tokens x 2,560
     channels: 12,288 items), with a bias, masked entries and a partial last
     chunk (2,560 = 2 x 1,024 + 512)."""
@@ -198,7 +198,7 @@ def test_logfmt_pipelined_with_bias(o):
     idx[rng.random(idx.shape) < 0.1] = -1
     rows = rows_of_kind(rng, int((idx >= 0).sum()), w.hidden, "zeros")
     bias = W.bf16_bits(rng.standard_normal((w.num_tokens, w.hidden)).astype(np.float32))
-    run_logfmt(o, ep.shape_of(w), idx, inp["topk_weights"], rows, "pipelined + bias",
+    run_logfmt(o, ep.shape_of(w), idx, inp["topk_weights"], rows, "large batch + bias",
                bias=bias, sample_tokens=300)
 
 
