@@ -162,45 +162,69 @@ __device__ __forceinline__ void encode_lane(const uint4 &in0, const uint4 &in1, 
 }
 
 // encode_lane with every logarithm read from a table of L over all 2^15
-// magnitudes (entry 0 unused), the same values log2_rn_bf16 gives.
+// magnitudes (entry 0 unused), the same values log2_rn_bf16 gives, and the
+// integer work done on packed halves or four bytes at a time:
+//  - magnitudes stay packed two per word; the block's smallest nonzero
+//    magnitude (minus one, a zero wrapping to 0xFFFF) and largest come from
+//    packed 16-bit min / max;
+//  - rint(q) is the low byte of RN(q + 1.5 * 2^23) (q <= 126 + 2^-17 on a
+//    nonzero channel); v_perm_b32 gathers the low bytes of four of them
+//    into one word, and masking each byte to 7 bits keeps the garbage of
+//    zero channels from carrying when 1 is added to every byte;
+//  - the sign bytes and the nonzero masks come from bits 15 and 31 of the
+//    input words (and of magnitude + 0x7FFF per half) with v_perm_b32's
+//    sign-replicating selectors.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2 halves(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
+__device__ __forceinline__ uint32_t word(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+// v_perm_b32 selectors: result byte i takes selector byte i; 0..3 pick a
+// byte of the second operand, 4..7 of the first, 8 / 9 / 10 / 11 give 0xFF
+// or 0x00 by bit 15 / 31 of the second / first operand, 12 gives 0x00.
+constexpr uint32_t kPermLowBytes01 = 0x0C0C0400u; // b0 of second, b0 of first -> bytes 0, 1
+constexpr uint32_t kPermLowBytes23 = 0x04000C0Cu; // b0 of second, b0 of first -> bytes 2, 3
+constexpr uint32_t kPermHalfSigns = 0x0B0A0908u;  // bits 15, 31 of second, then of first
+
 __device__ __forceinline__ void encode_lane_table(const uint4 &in0, const uint4 &in1, const float *L,
-                                            uint4 &codes, float &lo, float &hi)
+                                                  uint4 &codes, float &lo, float &hi)
 {
     const uint32_t w[8] = {in0.x, in0.y, in0.z, in0.w, in1.x, in1.y, in1.z, in1.w};
-    uint32_t mag[16], sgn[16];
+    uint32_t m2[8];
+    u16x2 mnv = {0xFFFF, 0xFFFF}, mxv = {0, 0};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        mag[2 * i] = w[i] & 0x7FFFu;
-        mag[2 * i + 1] = (w[i] >> 16) & 0x7FFFu;
-        sgn[2 * i] = (w[i] >> 8) & 0x80u;
-        sgn[2 * i + 1] = (w[i] >> 24) & 0x80u;
+        m2[i] = w[i] & 0x7FFF7FFFu;
+        const u16x2 v = halves(m2[i]);
+        mnv = __builtin_elementwise_min(mnv, v - (u16x2)(1));
+        mxv = __builtin_elementwise_max(mxv, v);
     }
-    // smallest nonzero magnitude minus one (a zero wraps to the largest
-    // value and drops out), largest magnitude
-    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        mn = min(mn, mag[i] - 1u);
-        mx = max(mx, mag[i]);
-    }
+    uint32_t mn = min((uint32_t)mnv.x, (uint32_t)mnv.y);
+    uint32_t mx = max((uint32_t)mxv.x, (uint32_t)mxv.y);
     mn = min8(mn);
     mx = max8(mx);
     const bool any = mx != 0u;
-    lo = any ? L[mn + 1u] : 0.0f;
+    lo = any ? L[(mn + 1u) & 0x7FFFu] : 0.0f;
     hi = any ? L[mx] : 0.0f;
     const float span = hi - lo;
     const float inv = span > 0.0f ? 126.0f / span : 0.0f; // correctly rounded division
-    float l[16];
+    uint32_t out[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-        l[i] = L[mag[i]];
-    uint32_t out[4] = {0u, 0u, 0u, 0u};
+    for (int j = 0; j < 4; ++j) {
+        // channels 4j .. 4j+3: the low and high halves of words 2j, 2j+1
+        uint32_t t[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float q = (l[i] - lo) * inv;
-        const uint32_t m = __float_as_uint(q + 12582912.0f) - 0x4B3FFFFFu; // 1 + rint(q)
-        const uint32_t code = mag[i] ? (sgn[i] | m) : 0u;
-        out[i >> 2] |= code << (8 * (i & 3));
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t m = m2[2 * j + (e >> 1)];
+            const uint32_t mag = (e & 1) ? m >> 16 : m & 0xFFFFu;
+            const float q = (L[mag] - lo) * inv;
+            t[e] = __float_as_uint(q + 12582912.0f);
+        }
+        const uint32_t r = (__builtin_amdgcn_perm(t[1], t[0], kPermLowBytes01) |
+                            __builtin_amdgcn_perm(t[3], t[2], kPermLowBytes23)) & 0x7F7F7F7Fu;
+        const uint32_t sgn = __builtin_amdgcn_perm(w[2 * j + 1], w[2 * j], kPermHalfSigns) & 0x80808080u;
+        const uint32_t nz = __builtin_amdgcn_perm(word(halves(m2[2 * j + 1]) + (u16x2)(0x7FFF)),
+                                                  word(halves(m2[2 * j]) + (u16x2)(0x7FFF)),
+                                                  kPermHalfSigns);
+        out[j] = ((r + 0x01010101u) | sgn) & nz;
     }
     codes = make_uint4(out[0], out[1], out[2], out[3]);
 }
