@@ -301,6 +301,20 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
             e[1].record(stream)
         torch.cuda.synchronize()
         fused["back_to_back"] = [e[0].elapsed_time(e[1]) * 1e3 / batch for e in evs]
+        # whole steps (ep_layout_dispatch, then ep_combine) back to back, warm
+        # (a few untimed steps first, so the GPU is busy when timing starts)
+        e = new_events(2)
+        for _ in range(5):
+            layout_dispatch()
+            combine()
+        torch.cuda.synchronize()
+        e[0].record(stream)
+        for _ in range(steps):
+            layout_dispatch()
+            combine()
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        fused["warm_us_per_step"] = round(e[0].elapsed_time(e[1]) * 1e3 / steps, 2)
 
     say(f"workload {w.name}: the step captured in a HIP graph, {steps} replays")
     graph = torch.cuda.CUDAGraph()
@@ -331,6 +345,9 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
     for kind, fns in (("prepared", (layout, dispatch, combine)),
                       ("plain", (plain["layout"], plain["dispatch"], plain["combine"]))):
         e = new_events(2)
+        for _ in range(5):
+            for fn in fns:
+                fn()
         torch.cuda.synchronize()
         e[0].record(stream)
         h0 = time.perf_counter()
@@ -371,7 +388,8 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
             "layout_dispatch_us_cold": stats(fused["layout_dispatch"],
                                              nbytes["layout"] + nbytes["dispatch"]),
             "layout_dispatch_us_back_to_back": stats(fused["back_to_back"],
-                                                     nbytes["layout"] + nbytes["dispatch"])},
+                                                     nbytes["layout"] + nbytes["dispatch"]),
+            "step_us_warm": fused["warm_us_per_step"]},
         "wall_cold_s": wall_cold,
         "inputs": inp,
     }
