@@ -617,6 +617,207 @@ __global__ __launch_bounds__(THREADS) void layout_pack_kernel(
     }
 }
 
+// Sum over each group of G consecutive lanes (G a power of two up to 64),
+// every lane of the group ending with it: DPP moves within 8 lanes and the
+// 16-lane row, cross-row steps by lane permutes.
+template <int G>
+__device__ __forceinline__ int group_sum(int v)
+{
+    if (G >= 2)
+        v += (int)dpp<kDppXor1>((uint32_t)v);
+    if (G >= 4)
+        v += (int)dpp<kDppXor2>((uint32_t)v);
+    if (G >= 8)
+        v += (int)dpp<kDppHalfMirror>((uint32_t)v);
+    if (G >= 16)
+        v += __shfl_xor(v, 8, 64);
+    if (G >= 32)
+        v += __shfl_xor(v, 16, 64);
+    if (G >= 64)
+        v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// The pack of ep_layout_dispatch above kFusedCountedMaxTokens tokens: the
+// layout left each entry's rank within its 256-token block (local_slot) and
+// one histogram row per block; an entry's slot is its local slot plus the
+// counts of its expert in every earlier block.  One block per token (block 0
+// sums every histogram row into the totals and writes the offset scan):
+//  1. every wave loads x of its first two chunks;
+//  2. wave 0 computes the token's rows once: a group of 64 / KB lanes takes
+//     entry k of a batch, each lane a share of the earlier blocks' rows, and
+//     a reduction within the group gives the prefix; the same for the column
+//     of the entry's rank.  It writes the token's expert_slot row, its rank
+//     rows and recv_src_idx, and leaves the rows in LDS;
+//  3. after one barrier, wave w quantises chunks w, w + 4, ... once and stores
+//     each to every row, as pack_kernel does.
+template <int KB, int SF, bool FP8>
+__global__ __launch_bounds__(kThreads) void pack_local_kernel(
+    int32_t N, int32_t H, int32_t K, int32_t E, int32_t R, int32_t S, int32_t A, int32_t nchunks,
+    int32_t tpb, int32_t B, int32_t stride, const int32_t *__restrict__ hist,
+    const int32_t *__restrict__ local_slot, const int32_t *__restrict__ local_rank,
+    const uint16_t *__restrict__ x, const int64_t *__restrict__ topk_idx,
+    int32_t *__restrict__ num_tokens_per_rank, int32_t *__restrict__ num_tokens_per_expert,
+    uint8_t *__restrict__ is_token_in_rank, int32_t *__restrict__ expert_slot,
+    int32_t *__restrict__ rank_slot, int32_t *__restrict__ expert_offset, void *__restrict__ recv_x,
+    void *__restrict__ recv_scales, int32_t *__restrict__ recv_src_idx, uint32_t *status)
+{
+    static_assert(KB == 1 || KB == 2 || KB == 4 || KB == 8, "KB divides the wave");
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (blockIdx.x == 0) {
+        // totals: column sums of all B rows, then the counts and the scan
+        __shared__ int32_t s_tot[EP_MAX_EXPERTS + EP_MAX_RANKS];
+        const int W = E + R;
+        for (int c = threadIdx.x; c < W; c += kThreads) {
+            int sum = 0;
+            for (int r = 0; r < B; ++r)
+                sum += hist[(size_t)r * stride + c];
+            s_tot[c] = sum;
+            if (c < E)
+                num_tokens_per_expert[c] = sum;
+            else
+                num_tokens_per_rank[c - E] = sum;
+        }
+        __syncthreads();
+        if (wave == 0 && expert_offset) {
+            const int per = (E + 63) / 64;
+            const int first = lane * per;
+            int local = 0;
+            for (int i = 0; i < per; ++i)
+                if (first + i < E)
+                    local += (s_tot[first + i] + A - 1) / A * A;
+            int incl = local;
+            for (int off = 1; off < 64; off <<= 1) {
+                const int up = __shfl_up(incl, off, 64);
+                if (lane >= off)
+                    incl += up;
+            }
+            int run = incl - local;
+            for (int i = 0; i < per; ++i) {
+                if (first + i < E) {
+                    expert_offset[first + i] = run;
+                    run += (s_tot[first + i] + A - 1) / A * A;
+                }
+            }
+            if (lane == 63)
+                expert_offset[E] = incl;
+        }
+        return;
+    }
+    __shared__ int64_t s_row[EP_MAX_TOPK];
+    const uint32_t t = blockIdx.x - 1; // host launches N + 1 blocks
+    const uint16_t *x_row = x + (size_t)t * H;
+
+    // 1. x of this wave's first two chunks
+    uint4 xr[2][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        xr[c][0] = make_uint4(0, 0, 0, 0);
+        xr[c][1] = make_uint4(0, 0, 0, 0);
+        const int chunk = wave + c * kWaves;
+        if (chunk < nchunks)
+            load_chunk<FP8>(x_row, H, chunk, lane, xr[c][0], xr[c][1]);
+    }
+
+    // 2. the token's rows and layout rows (wave 0)
+    if (wave == 0) {
+        constexpr int G = 64 / KB;
+        const int blk = (int)(t / (uint32_t)tpb); // earlier blocks: 0 .. blk-1
+        const int kq = lane / G;
+        const int m = lane & (G - 1);
+        const uint32_t magic = rank_magic(E / R);
+        uint32_t flags = 0;
+        int32_t my_local = -1, my_before = 0; // lane r < R: rank r
+        const int64_t *idx_t = topk_idx + (size_t)t * K;
+        const int32_t *ls_t = local_slot + (size_t)t * K;
+        const int32_t *lr_t = local_rank + (size_t)t * K;
+        for (int k0 = 0; k0 < K; k0 += KB) {
+            const int kk = min(k0 + kq, K - 1);
+            const bool in_k = k0 + kq < K;
+            const int64_t id = idx_t[kk];
+            const int32_t ls = ls_t[kk];
+            const int32_t lr0 = lr_t[kk];
+            const bool routed = in_k && id >= 0 && id < (int64_t)E;
+            const int32_t e32 = routed ? (int32_t)id : 0;
+            const int32_t rk = routed ? rank_of(e32, magic) : 0;
+            int acc = 0, racc = 0;
+            if (routed) {
+                for (int r = m; r < blk; r += G) {
+                    acc += hist[(size_t)r * stride + e32];
+                    racc += hist[(size_t)r * stride + E + rk];
+                }
+            }
+            acc = group_sum<G>(acc);
+            racc = group_sum<G>(racc);
+            const int32_t slot = ls + acc;
+            const bool slot_ok = routed && slot < S;
+            const int64_t rr = slot_ok ? (int64_t)e32 * S + slot : -1;
+            const bool head = m == 0; // one lane per entry
+            if (__ballot(head && in_k && id != -1 && !routed))
+                flags |= EP_STATUS_BAD_EXPERT_ID;
+            if (__ballot(head && routed && !slot_ok))
+                flags |= EP_STATUS_BAD_SLOT;
+            if (head && in_k) {
+                expert_slot[(size_t)t * K + k0 + kq] = routed ? slot : -1;
+                s_row[k0 + kq] = rr;
+                if (rr >= 0)
+                    recv_src_idx[rr] = (int32_t)t;
+            }
+            const int32_t lr = routed ? lr0 : -1;
+#pragma unroll
+            for (int bb = 0; bb < KB; ++bb) {
+                const int32_t rk_b = __builtin_amdgcn_readlane(routed ? rk : -1, bb * G);
+                const int32_t lr_b = __builtin_amdgcn_readlane(lr, bb * G);
+                const int32_t before_b = __builtin_amdgcn_readlane(racc, bb * G);
+                if (rk_b == lane && lr_b >= 0) {
+                    my_local = lr_b;
+                    my_before = before_b;
+                }
+            }
+        }
+        if (lane < R) {
+            rank_slot[(size_t)t * R + lane] = my_local >= 0 ? my_local + my_before : -1;
+            is_token_in_rank[(size_t)t * R + lane] = my_local >= 0 ? 1 : 0;
+        }
+        if (flags && status && lane == 0)
+            atomicOr(status, flags);
+    }
+    __syncthreads();
+
+    // 3. pack: the first two chunks are loaded; later ones load here
+    for (int chunk = wave, c = 0; chunk < nchunks; chunk += kWaves, ++c) {
+        uint4 in0 = make_uint4(0, 0, 0, 0), in1 = make_uint4(0, 0, 0, 0);
+        if (c == 0) {
+            in0 = xr[0][0];
+            in1 = xr[0][1];
+        } else if (c == 1) {
+            in0 = xr[1][0];
+            in1 = xr[1][1];
+        } else {
+            load_chunk<FP8>(x_row, H, chunk, lane, in0, in1);
+        }
+        Fp8Lane fl;
+        Fp8Payload p;
+        Bf16Lane bl;
+        if (FP8) {
+            fl = fp8_lane(H, chunk, lane);
+            p = quantize_regs<SF>(in0, in1, fl, lane);
+        } else {
+            bl = bf16_lane(H, chunk, lane);
+        }
+        for (int k = 0; k < K; ++k) {
+            const int64_t row = s_row[k];
+            if (row < 0)
+                continue;
+            if (FP8)
+                store_fp8<SF>(p, fl, lane, row, H, static_cast<uint8_t *>(recv_x), recv_scales);
+            else
+                store_bf16(in0, in1, bl, row, H, static_cast<uint16_t *>(recv_x));
+        }
+    }
+}
+
 int batch_of(int K) { return K == 1 ? 1 : K == 2 ? 2 : K <= 4 ? 4 : 8; }
 
 // Launch of the per-expert / expand pack for every (batch, scale format,
@@ -723,6 +924,51 @@ hipError_t launch_layout_dispatch(const ep_shape &s, const LayoutPlan &plan, con
 #undef EP_FUSED_SF
 #undef EP_FUSED_T
 #undef EP_FUSED
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_local(const ep_shape &s, const LayoutPlan &plan, const LocalWorkspace &ws,
+                                 const uint16_t *x, const int64_t *topk_idx,
+                                 int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+                                 uint8_t *is_token_in_rank, int32_t *expert_slot,
+                                 int32_t *rank_slot, int32_t *expert_offset, void *recv_x,
+                                 void *recv_scales, int32_t *recv_src_idx, uint32_t *status,
+                                 hipStream_t stream)
+{
+    const int N = s.num_tokens, H = s.hidden, K = s.num_topk, E = s.num_experts;
+    const int R = s.num_ranks, S = s.expert_capacity, A = expert_alignment(s);
+    if (N == 0)
+        return hipSuccess;
+    const int nchunks = (H + kChunk - 1) / kChunk;
+    const dim3 grid((unsigned)(N + 1)); // block 0: totals; block t + 1: token t
+    const int kb = batch_of(K);
+#define EP_LOCAL(KB, SF, FP8)                                                                      \
+    hipLaunchKernelGGL((pack_local_kernel<KB, SF, FP8>), grid, dim3(kThreads), 0, stream, N, H, K, \
+                       E, R, S, A, nchunks, plan.tokens_per_block, plan.num_blocks,                \
+                       plan.hist_stride, ws.hist, ws.local_slot, ws.local_rank, x, topk_idx,       \
+                       num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank, expert_slot,  \
+                       rank_slot, expert_offset, recv_x, recv_scales, recv_src_idx, status)
+#define EP_LOCAL_KB(SF, FP8)                                                                       \
+    do {                                                                                           \
+        if (kb == 1)                                                                               \
+            EP_LOCAL(1, SF, FP8);                                                                  \
+        else if (kb == 2)                                                                          \
+            EP_LOCAL(2, SF, FP8);                                                                  \
+        else if (kb == 4)                                                                          \
+            EP_LOCAL(4, SF, FP8);                                                                  \
+        else                                                                                       \
+            EP_LOCAL(8, SF, FP8);                                                                  \
+    } while (0)
+    if (!s.use_fp8)
+        EP_LOCAL_KB(EP_SCALE_FP32, false);
+    else if (s.scale_format == EP_SCALE_POW2)
+        EP_LOCAL_KB(EP_SCALE_POW2, true);
+    else if (s.scale_format == EP_SCALE_UE8M0)
+        EP_LOCAL_KB(EP_SCALE_UE8M0, true);
+    else
+        EP_LOCAL_KB(EP_SCALE_FP32, true);
+#undef EP_LOCAL_KB
+#undef EP_LOCAL
     return hipGetLastError();
 }
 

@@ -178,7 +178,7 @@ int ep_query_sizes(const ep_shape *s, ep_sizes *out)
     out->expert_offset = (E + 1) * sizeof(int32_t);
     ep::LayoutPlan plan;
     ep::plan_layout(*s, &plan);
-    out->layout_workspace = plan.workspace_bytes;
+    out->layout_workspace = ep::layout_dispatch_workspace(*s, plan);
     const size_t M = s->num_max_dispatch_tokens_per_rank;
     const size_t scale_row = !s->use_fp8 ? 0
                              : s->scale_format == EP_SCALE_UE8M0 ? ((G + 3) / 4) * sizeof(uint32_t)
@@ -296,7 +296,8 @@ int ep_layout_dispatch(const ep_shape *s, const int64_t *topk_idx, const uint16_
         return EP_ERR_ALIGN;
     ep::LayoutPlan plan;
     ep::plan_layout(*s, &plan);
-    if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+    const size_t need = ep::layout_dispatch_workspace(*s, plan);
+    if (need > 0 && (!workspace || workspace_bytes < need))
         return EP_ERR_WORKSPACE;
     if (has_tokens) {
         if (!x || !recv_x || !recv_src_idx)
@@ -309,7 +310,8 @@ int ep_layout_dispatch(const ep_shape *s, const int64_t *topk_idx, const uint16_
     }
     const hipStream_t st = static_cast<hipStream_t>(stream);
     // up to 256 tokens one kernel; up to 1,024 the layout's count kernel and
-    // then one kernel for the rest; above that the layout and the pack
+    // then one kernel for the rest; above that the layout's local ranking
+    // and the pack that adds each token's prefix over the earlier blocks
     const int N = s->num_tokens;
     int32_t *ws = static_cast<int32_t *>(workspace);
     hipError_t err;
@@ -326,12 +328,13 @@ int ep_layout_dispatch(const ep_shape *s, const int64_t *topk_idx, const uint16_
                                              rank_slot, expert_offset, recv_x, recv_scales,
                                              recv_src_idx, status, st);
     } else {
-        err = ep::launch_layout(*s, plan, topk_idx, num_tokens_per_rank, num_tokens_per_expert,
-                                is_token_in_rank, expert_slot, rank_slot, expert_offset, ws, status,
-                                st);
+        const ep::LocalWorkspace lw = ep::local_workspace(workspace, plan, *s);
+        err = ep::launch_layout_local(*s, plan, topk_idx, lw, status, st);
         if (err == hipSuccess)
-            err = ep::launch_dispatch(*s, x, topk_idx, expert_slot, recv_x, recv_scales,
-                                      recv_src_idx, status, st);
+            err = ep::launch_dispatch_local(*s, plan, lw, x, topk_idx, num_tokens_per_rank,
+                                            num_tokens_per_expert, is_token_in_rank, expert_slot,
+                                            rank_slot, expert_offset, recv_x, recv_scales,
+                                            recv_src_idx, status, st);
     }
     return err == hipSuccess ? EP_OK : EP_ERR_HIP;
 }

@@ -66,6 +66,51 @@ hipError_t launch_layout_count(const ep_shape &s, const LayoutPlan &plan, const 
 // layout's second kernel.
 constexpr int kFusedMaxTokens = 256;
 constexpr int kFusedCountedMaxTokens = 1024;
+
+// ep_layout_dispatch above kFusedCountedMaxTokens: the layout ranks each
+// 256-token block on its own (launch_layout_local), then the pack adds each
+// token's prefix over the earlier blocks (launch_dispatch_local).  Workspace:
+// the histogram rows [B][hist_stride], then local slots and local rank slots
+// [N][K] each.
+struct LocalWorkspace {
+    int32_t *hist;       // [B][hist_stride]
+    int32_t *local_slot; // [N][K]
+    int32_t *local_rank; // [N][K]
+};
+
+inline LocalWorkspace local_workspace(void *ws, const LayoutPlan &plan, const ep_shape &s)
+{
+    LocalWorkspace w;
+    w.hist = static_cast<int32_t *>(ws);
+    w.local_slot = w.hist + (size_t)plan.num_blocks * plan.hist_stride;
+    w.local_rank = w.local_slot + (size_t)s.num_tokens * s.num_topk;
+    return w;
+}
+
+inline size_t local_workspace_bytes(const LayoutPlan &plan, const ep_shape &s)
+{
+    return sizeof(int32_t) * ((size_t)plan.num_blocks * plan.hist_stride +
+                              2 * (size_t)s.num_tokens * s.num_topk);
+}
+
+// Workspace bytes ep_layout_dispatch needs for a shape (at least what
+// ep_layout needs).
+inline size_t layout_dispatch_workspace(const ep_shape &s, const LayoutPlan &plan)
+{
+    return s.num_tokens <= kFusedCountedMaxTokens ? plan.workspace_bytes
+                                                  : local_workspace_bytes(plan, s);
+}
+
+hipError_t launch_layout_local(const ep_shape &s, const LayoutPlan &plan, const int64_t *topk_idx,
+                               const LocalWorkspace &ws, uint32_t *status, hipStream_t stream);
+
+hipError_t launch_dispatch_local(const ep_shape &s, const LayoutPlan &plan, const LocalWorkspace &ws,
+                                 const uint16_t *x, const int64_t *topk_idx,
+                                 int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+                                 uint8_t *is_token_in_rank, int32_t *expert_slot,
+                                 int32_t *rank_slot, int32_t *expert_offset, void *recv_x,
+                                 void *recv_scales, int32_t *recv_src_idx, uint32_t *status,
+                                 hipStream_t stream);
 hipError_t launch_layout_dispatch(const ep_shape &s, const LayoutPlan &plan, const int32_t *hist,
                                   const uint16_t *x, const int64_t *topk_idx,
                                   int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,

@@ -464,6 +464,149 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
     }
 }
 
+// Local ranking: the first launch of ep_layout_dispatch above
+// kFusedCountedMaxTokens tokens.  Each 256-token block ranks its own entries
+// exactly as the assign kernel does, but against its own tokens only:
+// local_slot[t, k] is the entry's rank among the block's entries with the
+// same expert, local_rank[t, k] the token's rank among the block's tokens
+// sent to the rank of expert k (-1 for a masked entry), and the block's
+// histogram row (its entries per expert, repeats included, and its tokens
+// per rank) goes to `hist`.  No block reads another block's output: the pack
+// that follows adds each token's prefix over the earlier blocks' rows.
+template <int KMAX>
+__global__ __launch_bounds__(kThreads) void layout_local_kernel(
+    int32_t N, int32_t K, int32_t E, int32_t R, int32_t L, int32_t stride,
+    const int64_t *__restrict__ topk_idx, int32_t *__restrict__ hist,
+    int32_t *__restrict__ local_slot, int32_t *__restrict__ local_rank, uint32_t *status)
+{
+    extern __shared__ __align__(16) char lds_raw[];
+    const int W = E + R;
+    uint64_t *s_bm = reinterpret_cast<uint64_t *>(lds_raw);                  // [kGroups][W]
+    int32_t *s_wb = reinterpret_cast<int32_t *>(s_bm + (size_t)kGroups * W); // [kGroups][W]
+    int32_t *s_tot = s_wb + (size_t)kGroups * W;                             // [W]
+    int32_t *s_misc = s_tot + W;                                             // [8]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int g = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int b = blockIdx.x;
+    const int64_t t = (int64_t)b * kThreads + tid;
+
+    int32_t e[KMAX];
+    uint32_t bad = 0;
+    load_token<KMAX>(topk_idx, t, N, K, E, e, bad);
+    for (int i = tid; i < kGroups * W; i += kThreads)
+        s_bm[i] = 0ull;
+    if (tid < 8)
+        s_misc[tid] = 0;
+
+    const uint32_t magic = rank_magic(L);
+    int occ[KMAX];
+    int rk[KMAX];
+    int maxocc = 0;
+    uint64_t ranks = 0;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        occ[k] = 0;
+#pragma unroll
+        for (int k2 = 0; k2 < k; ++k2)
+            occ[k] += (e[k] >= 0 && e[k2] == e[k]) ? 1 : 0;
+        maxocc = max(maxocc, occ[k]);
+        rk[k] = e[k] >= 0 ? rank_of(e[k], magic) : 0;
+        if (e[k] >= 0)
+            ranks |= 1ull << rk[k];
+    }
+    __syncthreads(); // LDS cleared
+
+    // layer-0 bitmaps (first occurrences) and rank words, bit = lane
+    uint64_t *my_words = s_bm + (size_t)g * W;
+    const uint64_t bit = 1ull << lane;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+        if (e[k] >= 0 && occ[k] == 0)
+            atomicOr((unsigned long long *)&my_words[e[k]], (unsigned long long)bit);
+    if (R <= kBallotRanks) {
+        for (int r = 0; r < R; ++r) {
+            const uint64_t m = __ballot((ranks >> r) & 1ull);
+            if (lane == 0)
+                my_words[E + r] = m;
+        }
+    } else {
+        for (uint64_t m = ranks; m; m &= m - 1)
+            atomicOr((unsigned long long *)&my_words[E + __builtin_ctzll(m)], (unsigned long long)bit);
+    }
+    if (maxocc > 0)
+        atomicMax(&s_misc[0], maxocc);
+    if (bad)
+        atomicOr(&s_misc[1], 1);
+    __syncthreads();
+
+    // wave bases within the block; past the last wave, the block's count
+    for (int c = tid; c < W; c += kThreads) {
+        int run = 0;
+#pragma unroll
+        for (int g2 = 0; g2 < kGroups; ++g2) {
+            s_wb[g2 * W + c] = run;
+            run += __popcll(s_bm[g2 * W + c]);
+        }
+        s_tot[c] = run;
+    }
+    __syncthreads();
+
+    const int32_t *my_base = s_wb + (size_t)g * W;
+    const uint64_t below = bits_below(lane);
+    int pre[KMAX];
+    int lr[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        pre[k] = e[k] >= 0 ? my_base[e[k]] + __popcll(my_words[e[k]] & below) + occ[k] : 0;
+        lr[k] = e[k] >= 0 ? my_base[E + rk[k]] + __popcll(my_words[E + rk[k]] & below) : -1;
+    }
+
+    // repeated experts: one more bitmap layer per occurrence index, each also
+    // counted in the block's expert columns
+    const int layers = s_misc[0] + 1;
+    for (int layer = 1; layer < layers; ++layer) {
+        __syncthreads();
+        for (int i = tid; i < kGroups * W; i += kThreads)
+            s_bm[i] = 0ull;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (e[k] >= 0 && occ[k] == layer)
+                atomicOr((unsigned long long *)&my_words[e[k]], (unsigned long long)bit);
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (e[k] >= 0)
+                pre[k] += prefix_in_block(&s_bm[e[k]], W, g, lane);
+        for (int i = tid; i < E; i += kThreads) {
+            int c = 0;
+            for (int g2 = 0; g2 < kGroups; ++g2)
+                c += __popcll(s_bm[g2 * W + i]);
+            s_tot[i] += c;
+        }
+    }
+
+    if (t < N) {
+        int32_t *ls = local_slot + t * K;
+        int32_t *lrk = local_rank + t * K;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (k < K) {
+                ls[k] = e[k] >= 0 ? pre[k] : -1;
+                lrk[k] = lr[k];
+            }
+        }
+    }
+    __syncthreads(); // s_tot complete
+    int32_t *row = hist + (size_t)b * stride;
+    for (int c = tid; c < stride; c += kThreads)
+        row[c] = c < W ? s_tot[c] : 0;
+    if (tid == 0 && status && s_misc[1])
+        atomicOr(status, EP_STATUS_BAD_EXPERT_ID);
+}
+
 } // namespace
 
 bool plan_layout(const ep_shape &s, LayoutPlan *plan)
@@ -527,6 +670,26 @@ hipError_t launch_layout_count(const ep_shape &s, const LayoutPlan &plan, const 
     else
         hipLaunchKernelGGL(layout_count_kernel<EP_MAX_TOPK>, dim3(B), dim3(kThreads), count_lds,
                            stream, N, K, E, R, E / R, plan.hist_stride, topk_idx, workspace);
+    return hipGetLastError();
+}
+
+hipError_t launch_layout_local(const ep_shape &s, const LayoutPlan &plan, const int64_t *topk_idx,
+                               const LocalWorkspace &ws, uint32_t *status, hipStream_t stream)
+{
+    const int N = s.num_tokens, K = s.num_topk, E = s.num_experts, R = s.num_ranks;
+    if (N == 0)
+        return hipSuccess;
+#define EP_LOCAL_LAUNCH(KMAX)                                                                      \
+    hipLaunchKernelGGL(layout_local_kernel<KMAX>, dim3(plan.num_blocks), dim3(kThreads),           \
+                       plan.lds_bytes, stream, N, K, E, R, E / R, plan.hist_stride, topk_idx,      \
+                       ws.hist, ws.local_slot, ws.local_rank, status)
+    if (K <= 8)
+        EP_LOCAL_LAUNCH(8);
+    else if (K <= 16)
+        EP_LOCAL_LAUNCH(16);
+    else
+        EP_LOCAL_LAUNCH(EP_MAX_TOPK);
+#undef EP_LOCAL_LAUNCH
     return hipGetLastError();
 }
 

@@ -92,7 +92,7 @@ extern "C" {
 #define EP_MAX_ALIGNMENT 1024 /* expert_alignment */
 #define EP_MAX_GROUPS 64      /* num_groups of ep_group_limited_topk */
 /* Bytes of the static per-device scratch of ep_layout_noalloc (1 MiB):
- * enough for ep_sizes.layout_workspace of up to 253,952 tokens at E = 256,
+ * enough for ep_layout's histograms of up to 253,952 tokens at E = 256,
  * R = 8, or 61,440 tokens at E = 1024, R = 64. */
 #define EP_NOALLOC_SCRATCH_BYTES (1u << 20)
 
@@ -142,7 +142,7 @@ typedef struct {
     size_t expert_slot;           /* N*K*4                                            */
     size_t rank_slot;             /* N*R*4                                            */
     size_t expert_offset;         /* (E+1)*4                                          */
-    size_t layout_workspace;      /* scratch for ep_layout (0: none needed)           */
+    size_t layout_workspace;      /* scratch for ep_layout(_dispatch) (0: none)       */
     /* normal mode (ep_dispatch_normal / ep_combine_normal), M rows per rank: */
     size_t recv_x_normal;         /* R*M*H (FP8) or R*M*H*2 (BF16)                    */
     size_t recv_scales_normal;    /* R*M*(H/128)*4, R*M*ceil(H/512)*4 (UE8M0), or 0   */
@@ -189,9 +189,11 @@ int ep_query_sizes(const ep_shape *shape, ep_sizes *out);
  * expert_slot is the handle that ep_dispatch and ep_combine take ([V1] §5.2(4):
  * the handle holds the routing metadata and can be reused while the routing is
  * unchanged).
- * workspace: device scratch of at least ep_sizes.layout_workspace bytes,
- *   16-byte aligned, owned by the caller, contents irrelevant on entry and
- *   meaningless after; NULL allowed when that size is 0.  Calls sharing one
+ * workspace: device scratch of at least ep_sizes.layout_workspace bytes (the
+ *   size ep_layout_dispatch needs; ep_layout uses its first B * round_up(E +
+ *   R, 4) * 4 bytes, B = ceil(N / 256), none when B == 1), 16-byte aligned,
+ *   owned by the caller, contents irrelevant on entry and meaningless after;
+ *   NULL allowed when ep_layout needs none.  Calls sharing one
  *   workspace must be ordered on one stream.
  * status: nullable device word (see conventions). */
 int ep_layout(const ep_shape *shape, const int64_t *topk_idx, int32_t *num_tokens_per_rank,
@@ -212,7 +214,8 @@ int ep_layout(const ep_shape *shape, const int64_t *topk_idx, int32_t *num_token
  * race and must be serialised by the caller.  Nothing in it needs clearing:
  * each call writes every histogram row before it reads one.
  * Returns EP_ERR_SCRATCH, before anything is enqueued, when the shape needs
- * more than EP_NOALLOC_SCRATCH_BYTES (ep_sizes.layout_workspace says how much),
+ * more than EP_NOALLOC_SCRATCH_BYTES (it needs B * round_up(E + R, 4) * 4
+ * bytes, B = ceil(N / 256), none when B == 1),
  * and EP_ERR_HIP when the device address cannot be looked up. */
 int ep_layout_noalloc(const ep_shape *shape, const int64_t *topk_idx,
                       int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
@@ -255,9 +258,16 @@ int ep_dispatch(const ep_shape *shape, const uint16_t *x, const int64_t *topk_id
  * counts, so the pack needs no separate layout pass.  From 257 to 1,024
  * tokens the layout's per-block histogram kernel runs first, and each
  * token's block adds the histograms of the blocks before its own to its
- * count of the earlier tokens of its block.  Above 1,024 tokens it runs the
- * two ordinary launches.  Above 256 tokens the layout's workspace is needed
- * (NULL with workspace_bytes 0 is allowed up to 256 tokens). */
+ * count of the earlier tokens of its block.  Above 1,024 tokens it is two
+ * launches: each 256-token block ranks its own entries (each entry's rank
+ * among the block's entries with its expert, each token's among the block's
+ * tokens sent to a rank) and writes its histogram row; then one block per
+ * token adds the counts of the earlier blocks to its local ranks, writes the
+ * token's layout rows and packs it, while one more block sums every row into
+ * the totals and the offset scan.  Above 256 tokens it needs a workspace of
+ * ep_sizes.layout_workspace bytes (which covers ep_layout's too; above 1,024
+ * tokens it also holds the local ranks, 8 * N * K bytes); NULL with
+ * workspace_bytes 0 is allowed up to 256 tokens. */
 int ep_layout_dispatch(const ep_shape *shape, const int64_t *topk_idx, const uint16_t *x,
                        int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
                        uint8_t *is_token_in_rank, int32_t *expert_slot, int32_t *rank_slot,

@@ -62,9 +62,12 @@ def test_query_sizes_match_the_receive_geometry(wid):
     assert sz["combined_x"] == N * H * 2
     assert sz["is_token_in_rank"] == N * R and sz["rank_slot"] == N * R * 4
     assert sz["expert_slot"] == N * K * 4 and sz["expert_offset"] == (E + 1) * 4
+    # ep_layout's histogram rows, one per 256 tokens; above 1,024 tokens
+    # ep_layout_dispatch also keeps local slots and local rank slots [N, K]
     blocks = -(-N // 256)
     stride = -(-(E + R) // 4) * 4
-    assert sz["layout_workspace"] == (blocks * stride * 4 if blocks > 1 else 0)
+    rows = blocks * stride * 4 if blocks > 1 else 0
+    assert sz["layout_workspace"] == (rows if N <= 1024 else rows + 2 * N * K * 4)
 
 
 @pytest.mark.parametrize("hidden", [128, 512, 640, 7168])

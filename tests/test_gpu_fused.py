@@ -6,8 +6,10 @@ FP8 byte, scale, BF16 row and recv_src_idx bit-exact, rows past each expert's
 count still poisoned, and the status word equal to the oracle's layout and
 pack bits together.  Up to 256 tokens the call is one fused launch; up to
 1,024 the layout's count kernel and one fused launch that adds the earlier
-count blocks' histograms; above that the ordinary layout and pack.  The cases
-step across both boundaries."""
+count blocks' histograms; above that a kernel that ranks each 256-token block
+on its own and a pack (one block per token) that adds the earlier blocks'
+counts.  The cases step across both boundaries; the workspace starts
+poisoned."""
 import numpy as np
 import pytest
 import torch
@@ -159,7 +161,7 @@ EDGE = [
     ("N=1000 K=16 E=256 R=32", 1000, 256, 16, 256, 32, True, dict(mask=0.1)),
     ("N=150 K=10 bf16", 150, 520, 10, 64, 8, False, {}),
     ("N=1024 odd K=5 bf16 H=520", 1024, 520, 5, 32, 8, False, dict(mask=0.05)),
-    ("N=1025 (layout and pack)", 1025, 1152, 8, 256, 8, True, {}),
+    ("N=1025 (local ranks and pack)", 1025, 1152, 8, 256, 8, True, {}),
     ("N=1100 K=1", 1100, 256, 1, 32, 8, True, {}),
     ("N=1200 R=1", 1200, 128, 4, 16, 1, True, {}),
     ("N=1300 all masked", 1300, 256, 4, 16, 4, True, dict(mask=1.0)),
@@ -206,7 +208,8 @@ def test_fused_capacity_overflow_and_bad_ids(o, N):
 def test_fused_both_status_bits_in_one_call(o, N):
     """Bad ids and entries past the capacity in the same call: both status
     bits are set, by blocks that may run on different XCDs (one launch at
-    150 tokens, the count-kernel form at 700, layout and pack at 1,100)."""
+    150 tokens, the count-kernel form at 700, the large-batch form at
+    1,100)."""
     H, K, E, R = 256, 12, 8, 4
     x, idx = _random(N, H, K, E, R, seed=N, repeats=True)
     rng = np.random.default_rng(N + 1)
@@ -238,8 +241,8 @@ def test_fused_matches_separate_calls_and_expand_offsets(o, N):
 @pytest.mark.parametrize("fmt", [ep.EP_SCALE_FP32, ep.EP_SCALE_UE8M0], ids=["fp32", "ue8m0"])
 def test_fused_prefill_full_size(o, fmt):
     """The prefill workload at full size (4,096 tokens x 7,168, group-limited
-    top-8 of 256 experts over 8 ranks): the layout's two kernels and the
-    pack, every output bit-exact."""
+    top-8 of 256 experts over 8 ranks): the large-batch form, every output
+    bit-exact."""
     w = W.WORKLOADS[3]
     inp = W.make_inputs(w)
     check_fused(o, ep.shape_of(w, fmt), inp["x_bits"], inp["topk_idx"], f"full {w.name}")

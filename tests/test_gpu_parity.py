@@ -445,8 +445,8 @@ def test_hip_graph_capture_and_replay(o, fused, num_tokens, hidden):
     """The path is capturable (no allocation, no host sync, no memset): one
     capture of layout + dispatch + combine (the first two as separate calls or
     as one ep_layout_dispatch; at 600 tokens that is the layout's count kernel
-    and one fused kernel, at 2,048 the layout's two kernels and the pack),
-    replayed several times with eager work in between
+    and one fused kernel, at 2,048 the local ranking and the prefix-adding
+    pack), replayed several times with eager work in between
     and a new routing copied into the captured input, each replay checked
     against an eager run and the oracle."""
     w = W.WORKLOADS[2].scaled(num_tokens, hidden)
