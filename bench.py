@@ -100,10 +100,12 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
     """Times the path on workload ``wid``.  Passes (each of ``steps``
     iterations, an untimed cache eviction before each iteration):
 
-    cold    : events only before ep_layout and after ep_combine -> the value;
-    graph   : the same step captured once in a HIP graph and replayed;
-    phases  : an event between phases as well (each event record delays the
-              next launch by a few us, so these phase times are upper bounds);
+    cold    : the step is ep_layout_dispatch then ep_combine, events only
+              before and after it -> the value;
+    three   : the same step as ep_layout, ep_dispatch, ep_combine;
+    graph   : the step captured once in a HIP graph and replayed;
+    phases  : an event between the two calls as well (each event record
+              delays the next launch by a few us: upper bounds);
     kernels : ``batch`` back-to-back launches of one entry point between two
               events -> average launch duration per entry point (the roofline);
     warm    : ``steps`` steps back to back, no eviction, two events overall.
@@ -191,6 +193,9 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
 
     say(f"workload {w.name}: {warmup} warmup steps")
     for _ in range(warmup):
+        layout_dispatch()
+        combine()
+        evict()
         layout()
         dispatch()
         combine()
@@ -198,6 +203,18 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
     torch.cuda.synchronize()
     if int(buf["status"].item()) != 0:
         raise RuntimeError(f"device status {int(buf['status'].item())} during warmup")
+
+    # the step: ep_layout_dispatch, then ep_combine (the library's one-call
+    # layout and pack; its outputs are exactly those of ep_layout and
+    # ep_dispatch); the same step as three calls is timed alongside
+    def step():
+        layout_dispatch()
+        combine()
+
+    def step_three_calls():
+        layout()
+        dispatch()
+        combine()
 
     say(f"workload {w.name}: {steps} timed steps, cache evicted before each")
     evs = [new_events(2) for _ in range(steps)]
@@ -208,15 +225,23 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
     for e in evs:
         evict()
         e[0].record(stream)
-        layout()
-        dispatch()
-        combine()
+        step()
         e[1].record(stream)
     torch.cuda.synchronize()
     wall_cold = time.perf_counter() - t0
     gc.enable()
     cold = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
     say(f"workload {w.name}: cold step times (us): " + " ".join(f"{v:.1f}" for v in cold))
+
+    say(f"workload {w.name}: {steps} timed steps as three calls")
+    evs = [new_events(2) for _ in range(steps)]
+    for e in evs:
+        evict()
+        e[0].record(stream)
+        step_three_calls()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    cold_three = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
 
     # The step without the latency an event marker adds before the next
     # launch: (eviction + step) minus (eviction alone), each between two
@@ -231,9 +256,7 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
         e[1].record(stream)
         e[2].record(stream)
         evict()
-        layout()
-        dispatch()
-        combine()
+        step()
         e[3].record(stream)
     torch.cuda.synchronize()
     evict_only = statistics.median([e[0].elapsed_time(e[1]) * 1e3 for e in evs])
@@ -242,25 +265,23 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
            "eviction_plus_step_us_median": round(evict_step, 2),
            "step_us": round(evict_step - evict_only, 2)}
 
-    say(f"workload {w.name}: {steps} steps with an event between phases")
-    evs = [new_events(4) for _ in range(steps)]
+    say(f"workload {w.name}: {steps} steps with an event between the two calls")
+    evs = [new_events(3) for _ in range(steps)]
     for e in evs:
         evict()
         e[0].record(stream)
-        layout()
+        layout_dispatch()
         e[1].record(stream)
-        dispatch()
-        e[2].record(stream)
         combine()
-        e[3].record(stream)
+        e[2].record(stream)
     torch.cuda.synchronize()
-    phases = {"layout": [e[0].elapsed_time(e[1]) * 1e3 for e in evs],
-              "dispatch": [e[1].elapsed_time(e[2]) * 1e3 for e in evs],
-              "combine": [e[2].elapsed_time(e[3]) * 1e3 for e in evs]}
+    phases = {"layout_dispatch": [e[0].elapsed_time(e[1]) * 1e3 for e in evs],
+              "combine": [e[1].elapsed_time(e[2]) * 1e3 for e in evs]}
 
     say(f"workload {w.name}: {batch} back-to-back launches per entry point, {steps} times")
     kernels = {}
-    for name, fn in (("layout", layout), ("dispatch", dispatch), ("combine", combine)):
+    for name, fn in (("layout", layout), ("dispatch", dispatch),
+                     ("layout_dispatch", layout_dispatch), ("combine", combine)):
         evs = [new_events(2) for _ in range(steps)]
         for e in evs:
             evict()
@@ -271,63 +292,16 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
         torch.cuda.synchronize()
         kernels[name] = [e[0].elapsed_time(e[1]) * 1e3 / batch for e in evs]
 
-    fused = None
-    if w.num_tokens <= FUSED_MAX_TOKENS:
-        # the one-launch layout + dispatch entry point, then the combine
-        say(f"workload {w.name}: {steps} cold steps through ep_layout_dispatch")
-        evs = [new_events(2) for _ in range(steps)]
-        for e in evs:
-            evict()
-            e[0].record(stream)
-            layout_dispatch()
-            combine()
-            e[1].record(stream)
-        torch.cuda.synchronize()
-        fused = {"step": [e[0].elapsed_time(e[1]) * 1e3 for e in evs]}
-        evs = [new_events(2) for _ in range(steps)]
-        for e in evs:
-            evict()
-            e[0].record(stream)
-            layout_dispatch()
-            e[1].record(stream)
-        torch.cuda.synchronize()
-        fused["layout_dispatch"] = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
-        evs = [new_events(2) for _ in range(steps)]
-        for e in evs:
-            evict()
-            e[0].record(stream)
-            for _ in range(batch):
-                layout_dispatch()
-            e[1].record(stream)
-        torch.cuda.synchronize()
-        fused["back_to_back"] = [e[0].elapsed_time(e[1]) * 1e3 / batch for e in evs]
-        # whole steps (ep_layout_dispatch, then ep_combine) back to back, warm
-        # (a few untimed steps first, so the GPU is busy when timing starts)
-        e = new_events(2)
-        for _ in range(5):
-            layout_dispatch()
-            combine()
-        torch.cuda.synchronize()
-        e[0].record(stream)
-        for _ in range(steps):
-            layout_dispatch()
-            combine()
-        e[1].record(stream)
-        torch.cuda.synchronize()
-        fused["warm_us_per_step"] = round(e[0].elapsed_time(e[1]) * 1e3 / steps, 2)
-
     say(f"workload {w.name}: the step captured in a HIP graph, {steps} replays")
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(stream)
     with torch.cuda.stream(side):
-        plain["layout"]()
-        plain["dispatch"]()
+        plain["layout_dispatch"]()
         plain["combine"]()
     stream.wait_stream(side)
     with torch.cuda.graph(graph):
-        plain["layout"]()
-        plain["dispatch"]()
+        plain["layout_dispatch"]()
         plain["combine"]()
     torch.cuda.synchronize()
     evs = [new_events(2) for _ in range(steps)]
@@ -342,10 +316,11 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
 
     say(f"workload {w.name}: {steps} steps back to back (warm), prepared and plain calls")
     warm = {}
-    for kind, fns in (("prepared", (layout, dispatch, combine)),
-                      ("plain", (plain["layout"], plain["dispatch"], plain["combine"]))):
+    for kind, fns in (("prepared", (layout_dispatch, combine)),
+                      ("prepared_three_calls", (layout, dispatch, combine)),
+                      ("plain_three_calls", (plain["layout"], plain["dispatch"], plain["combine"]))):
         e = new_events(2)
-        for _ in range(5):
+        for _ in range(5):  # untimed, so the GPU is busy when timing starts
             for fn in fns:
                 fn()
         torch.cuda.synchronize()
@@ -374,22 +349,19 @@ def run_workload(wid, steps, warmup, scrub_bytes, say, batch=10):
                 "us_p10": round(percentile(v, 10), 2), "us_p90": round(percentile(v, 90), 2),
                 "gbps_median": round(b / (med * 1e-6) / 1e9, 1)}
 
+    nb_ld = nbytes["layout"] + nbytes["dispatch"]
+    entry_bytes = {"layout": nbytes["layout"], "dispatch": nbytes["dispatch"],
+                   "layout_dispatch": nb_ld, "combine": nbytes["combine"]}
     return {
         "workload": w, "bytes": nbytes, "num_valid": P,
         "cold": stats(cold, nbytes["total"]),
+        "cold_three_calls": stats(cold_three, nbytes["total"]),
         "graph_cold": stats(graph_cold, nbytes["total"]),
         "cold_net_of_marker": dict(net, gbps=round(nbytes["total"] / (net["step_us"] * 1e-6) / 1e9, 1)),
-        "phases": {k: stats(v, nbytes[k]) for k, v in phases.items()},
-        "kernels": {k: stats(v, nbytes[k]) for k, v in kernels.items()},
+        "phases": {k: stats(v, entry_bytes[k]) for k, v in phases.items()},
+        "kernels": {k: stats(v, entry_bytes[k]) for k, v in kernels.items()},
         "warm_us_per_step": round(warm_us, 2),
         "warm": warm,
-        "fused": None if fused is None else {
-            "step_us_cold": stats(fused["step"], nbytes["total"]),
-            "layout_dispatch_us_cold": stats(fused["layout_dispatch"],
-                                             nbytes["layout"] + nbytes["dispatch"]),
-            "layout_dispatch_us_back_to_back": stats(fused["back_to_back"],
-                                                     nbytes["layout"] + nbytes["dispatch"]),
-            "step_us_warm": fused["warm_us_per_step"]},
         "wall_cold_s": wall_cold,
         "inputs": inp,
     }
@@ -562,9 +534,10 @@ def time_receive_layouts(wid, steps, scrub_bytes, say, alignment=128, batch=10):
 
 
 def time_config(wid, steps, warmup, scrub_bytes, say, allocations=1):
-    """The whole step (layout + dispatch + combine) on another workload, cold
-    (eviction before each step, two events around it): median and mean us,
-    and algorithmic GB/s at the mean, against the 60 % of peak bar.
+    """The whole step (ep_layout_dispatch, then ep_combine) on another
+    workload, cold (eviction before each step, two events around it): median
+    and mean us, and algorithmic GB/s at the mean, against the 60 % of peak
+    bar; the median of the same step as three calls beside it.
 
     With allocations > 1 the receive buffer and the expert outputs are freed
     and allocated again that many times in all, and the median step of each
@@ -597,18 +570,30 @@ def time_config(wid, steps, warmup, scrub_bytes, say, allocations=1):
         if scrub is not None:
             torch.sum(scrub, dim=0, out=scrub_out)
 
+    def combine():
+        ep.ep_combine(shape, y, topk_idx, topk_weights, buf["expert_slot"], buf["combined_x"],
+                      buf["status"])
+
     def step():
+        # the bench's step: ep_layout_dispatch, then ep_combine
+        ep.ep_layout_dispatch(shape, topk_idx, x, buf["num_tokens_per_rank"],
+                              buf["num_tokens_per_expert"], buf["is_token_in_rank"],
+                              buf["expert_slot"], buf["rank_slot"], buf["expert_offset"],
+                              buf["workspace"], buf["recv_x"], buf["recv_scales"],
+                              buf["recv_src_idx"], buf["status"])
+        combine()
+
+    def step_three_calls():
         ep.ep_layout(shape, topk_idx, buf["num_tokens_per_rank"], buf["num_tokens_per_expert"],
                      buf["is_token_in_rank"], buf["expert_slot"], buf["rank_slot"],
                      buf["expert_offset"], buf["workspace"], buf["status"])
         ep.ep_dispatch(shape, x, topk_idx, buf["expert_slot"], buf["recv_x"], buf["recv_scales"],
                        buf["recv_src_idx"], buf["status"])
-        ep.ep_combine(shape, y, topk_idx, topk_weights, buf["expert_slot"], buf["combined_x"],
-                      buf["status"])
+        combine()
 
-    def cold_steps():
+    def cold_steps(fn=step):
         for _ in range(warmup):
-            step()
+            fn()
             evict()
         torch.cuda.synchronize()
         times = []
@@ -616,7 +601,7 @@ def time_config(wid, steps, warmup, scrub_bytes, say, allocations=1):
         for _ in range(steps):
             evict()
             e0.record(stream)
-            step()
+            fn()
             e1.record(stream)
             torch.cuda.synchronize()
             times.append(e0.elapsed_time(e1) * 1e3)
@@ -626,6 +611,8 @@ def time_config(wid, steps, warmup, scrub_bytes, say, allocations=1):
 
     say(f"workload {w.name}: {steps} cold steps")
     times = cold_steps()
+    say(f"workload {w.name}: {steps} cold steps as three calls")
+    three = cold_steps(step_three_calls)
     by_allocation = [round(statistics.median(times), 2)]
     for a in range(1, allocations):
         # the same shapes and contents in newly allocated memory
@@ -645,7 +632,8 @@ def time_config(wid, steps, warmup, scrub_bytes, say, allocations=1):
     out = {"us_median": round(statistics.median(times), 2), "us_mean": round(mean, 2),
            "bytes": nb, "gbps_at_mean": round(nb / (mean * 1e-6) / 1e9, 1),
            "frac_of_peak": round(nb / (mean * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
-           "bar_60pct_us": round(nb / (0.6 * PEAK_HBM_GBPS * 1e9) * 1e6, 1)}
+           "bar_60pct_us": round(nb / (0.6 * PEAK_HBM_GBPS * 1e9) * 1e6, 1),
+           "us_median_three_calls": round(statistics.median(three), 2)}
     if allocations > 1:
         out["us_median_by_allocation"] = by_allocation
         out["frac_of_peak_by_allocation"] = [round(nb / (u * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)
@@ -1100,10 +1088,12 @@ def _grid_threads(n, h, kind):
     wave per (token, 1024-channel chunk), four waves per block; the layout
     kernels one lane per token, 256 tokens per block, and the assign kernel
     one more block (the totals) when there are several token blocks."""
-    if kind in ("layout_count", "layout_assign"):
+    if kind in ("layout_count", "layout_assign", "layout_local"):
         blocks = max(1, -(-n // 256))
         extra = 1 if kind == "layout_assign" and blocks > 1 else 0
         return (blocks + extra) * 256
+    if kind == "pack_local":  # one block per token plus the totals block
+        return (n + 1) * 256
     if kind == "fused":  # one block per token plus the totals block: 512 threads up to
         # 256 tokens, 256 threads above
         return (n + 1) * (512 if n <= 256 else 256)
@@ -1170,15 +1160,20 @@ def summarize_headline_profiles(out_dir):
         # instantiation of pack_kernel on dense rows
         # the prefill combine runs the multi-item kernel (more items than one
         # round of resident waves covers), the decode combine the one-item one
-        for kname, kind, phase, short in (("combine_multi_kernel", "any", "combine", "combine"),
-                                          ("combine_kernel", "combine", "combine", "combine"),
-                                          ("pack_kernel", "pack", "dispatch", "pack_fp8"),
-                                          ("layout_assign_kernel", "layout_assign", "layout",
-                                           "layout_assign"),
-                                          ("layout_count_kernel", "layout_count", "layout",
-                                           "layout_count"),
-                                          ("layout_pack_kernel", "fused", "layout_dispatch",
-                                           "layout_pack")):
+        nb = dict(nb, layout_dispatch=nb["layout"] + nb["dispatch"])
+        # (kernel, grid kind, entry point, summary name, counter summary?);
+        # the bench's step runs ep_layout_dispatch (local ranks + the pack of
+        # local_kernel at prefill, the one-launch layout_pack_kernel at
+        # decode), the per-entry passes run the three ordinary calls
+        for kname, kind, phase, short, with_pmc in (
+                ("combine_multi_kernel", "any", "combine", "combine", True),
+                ("combine_kernel", "combine", "combine", "combine", True),
+                ("pack_kernel", "pack", "dispatch", "pack_fp8", True),
+                ("pack_local_kernel", "pack_local", "layout_dispatch", "pack_local_fp8", True),
+                ("layout_local_kernel", "layout_local", "layout_dispatch", "layout_local", False),
+                ("layout_assign_kernel", "layout_assign", "layout", "layout_assign", False),
+                ("layout_count_kernel", "layout_count", "layout", "layout_count", False),
+                ("layout_pack_kernel", "fused", "layout_dispatch", "layout_pack", False)):
             grid = None if kind == "any" else str(_grid_threads(w.num_tokens, w.hidden, kind))
             if grid is None:  # the workload's launches of this kernel, whatever their grid
                 mine = [r for r in trace if r["Kernel_Name"] == kname]
@@ -1191,10 +1186,7 @@ def summarize_headline_profiles(out_dir):
             if not durs:
                 continue
             ex = traced["extra"] if wid == 3 else traced["extra"]["decode_128x7168"]
-            if phase == "layout_dispatch":
-                same_run = ex["step_through_ep_layout_dispatch"]["layout_dispatch_us_back_to_back"]
-            else:
-                same_run = ex["kernel_avg_us_back_to_back"][phase]
+            same_run = ex["kernel_avg_us_back_to_back"][phase]
             lines = [
                 f"# {kname}, workload {w.name}",
                 f"# N={w.num_tokens} H={w.hidden} K={w.num_topk} E={w.num_experts} R={w.num_ranks} "
@@ -1213,13 +1205,13 @@ def summarize_headline_profiles(out_dir):
             if wid == 3:
                 lines += [f"algorithmic_bytes_per_launch ({phase} entry point): {nb[phase]}",
                           f"achieved_GBps_at_trace_avg: {nb[phase] / statistics.fmean(durs) / 1e3:.1f}"
-                          if phase != "layout" else "achieved_GBps_at_trace_avg: n/a (two kernels)"]
+                          if with_pmc else "achieved_GBps_at_trace_avg: n/a (one of two kernels)"]
             lines += ["", "## rocprofv3 --stats (all kernels of the run, both workloads)", stats_txt]
             path = os.path.join(PROFILES, f"{short}_{w.name}_trace.txt")
             with open(path, "w") as f:
                 f.write("\n".join(lines) + "\n")
             written.append(path)
-            if wid != 3 or phase == "layout":
+            if wid != 3 or not with_pmc:
                 continue
             per = {}
             for c in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -1293,7 +1285,12 @@ def summarize_config_profiles(out_dir):
         for c, rs in pmc.items():
             top = max(float(r["Counter_Value"]) for r in rs if "copyBuffer" in r["Kernel_Name"])
             cal[c] = (top, (512 << 20) / 1024.0 / top)
-        kernels = [("layout_count_kernel", "layout_count", "layout"),
+        nb = dict(nb, layout_dispatch=nb["layout"] + nb["dispatch"])
+        # the step's kernels (ep_layout_dispatch: local ranks, then the pack
+        # that adds the prefix; ep_combine), then those of the three calls
+        kernels = [("layout_local_kernel", "layout_local", "layout"),
+                   ("pack_local_kernel", "pack_local", "layout_dispatch"),
+                   ("layout_count_kernel", "layout_count", "layout"),
                    ("layout_assign_kernel", "layout_assign", "layout"),
                    ("pack_kernel", "pack", "dispatch"),
                    ("combine_kernel", "combine", "combine"),
@@ -1324,6 +1321,9 @@ def summarize_config_profiles(out_dir):
             if phase != "layout":
                 lines += [f"algorithmic_bytes_per_launch ({phase} entry point): {nb[phase]}",
                           f"achieved_GBps_at_trace_median: {nb[phase] / med / 1e3:.1f}"]
+            elif kname == "layout_local_kernel":
+                lines += [f"algorithmic_bytes_per_launch (layout outputs; the kernel writes local ranks "
+                          f"that the pack completes): {nb['layout']}"]
             else:
                 lines += [f"algorithmic_bytes_per_launch (layout entry point, both kernels): {nb['layout']}"]
             if len(pmc) == 2 and phase != "layout":
@@ -1535,7 +1535,9 @@ def main():
     }
     pack_us = prefill["kernels"]["dispatch"]["us_mean"]
     extra = {
+        "step": "ep_layout_dispatch then ep_combine (cold: the Infinity Cache evicted before each)",
         "step_us_cold": prefill["cold"],
+        "step_us_cold_three_calls": prefill["cold_three_calls"],
         "step_us_cold_hip_graph": prefill["graph_cold"],
         "step_cold_net_of_event_marker": prefill["cold_net_of_marker"],
         "phases_us_with_events_between": prefill["phases"],
@@ -1570,13 +1572,13 @@ def main():
         extra["copy_2GiB_context"] = time_copy_ceiling(min(args.steps, 20), say)
     if decode is not None:
         extra["decode_128x7168"] = {
-            "step_us_cold": decode["cold"], "step_us_cold_hip_graph": decode["graph_cold"],
+            "step_us_cold": decode["cold"], "step_us_cold_three_calls": decode["cold_three_calls"],
+            "step_us_cold_hip_graph": decode["graph_cold"],
             "step_cold_net_of_event_marker": decode["cold_net_of_marker"],
             "phases_us_with_events_between": decode["phases"],
             "kernel_avg_us_back_to_back": decode["kernels"],
             "step_us_warm": decode["warm_us_per_step"], "bytes_per_step": decode["bytes"],
             "warm_steps_by_call_kind": decode["warm"],
-            "step_through_ep_layout_dispatch": decode["fused"],
         }
     line = {
         "metric": "dispatch+combine achieved HBM GB/s (4096 tok x hidden 7168, FP8 dispatch, BF16 combine)",
