@@ -29,6 +29,9 @@
 // fixed order, so the fp32 sum is the same chain on every run (deterministic,
 // no atomics).
 //
+// Entries come in batches of 1, 2, 4, 6 or 8 (the smallest that holds K, or
+// 8): with K = 5 or 6 no lane of a batch of 8 loads a row only to drop it.
+//
 // When one round of resident waves would not cover every item but 14 rounds
 // would (K <= 8; e.g. 4,096 tokens of 7,168 channels), the top-k combine
 // instead runs a grid that is resident all at once, 8 or 14 items per wave,
@@ -216,21 +219,20 @@ __device__ __forceinline__ RawEntries load_raw_entries(const int64_t *__restrict
     return RawEntries{topk_idx[at], expert_slot[at], topk_weights[at]};
 }
 
-// A grid of G waves small enough to be resident all at once (K <= 8: one
-// batch of entries per item).  Wave w takes items w, w + G, ... < total,
+// A grid of G waves small enough to be resident all at once (K <= KB, KB 6
+// or 8: one batch of entries per item).  Wave w takes items w, w + G, ... < total,
 // keeps their outputs in registers and stores them after its last item:
 // HBM loses bandwidth when reads and writes interleave, and with every wave
 // reading first and writing last the writes come as one burst at the end.
 // The next item's entries are loaded while the current item's rows are in
 // flight.  The arithmetic per item is that of combine_kernel.
-template <bool BIAS, class Rows, int ITEMS>
+template <bool BIAS, class Rows, int ITEMS, int KB>
 __global__ __launch_bounds__(kThreads) void combine_multi_kernel(
     int32_t N, int32_t H, int32_t K, int32_t E, int32_t nchunks, Rows rows,
     const uint16_t *__restrict__ y, const int64_t *__restrict__ topk_idx,
     const float *__restrict__ topk_weights, const int32_t *__restrict__ expert_slot,
     const uint16_t *__restrict__ bias, uint16_t *__restrict__ out, uint32_t *status)
 {
-    constexpr int KB = 8;
     const int lane = threadIdx.x & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t w = blockIdx.x * kWaves + wave;
@@ -445,14 +447,14 @@ hipError_t launch_topk_combine_kb(const ep_shape &s, const Rows &rows, const uin
     const int N = s.num_tokens, H = s.hidden, K = s.num_topk, E = s.num_experts;
     const int nchunks = (H + kChunk - 1) / kChunk;
     const int64_t items = (int64_t)N * nchunks;
-    // several items per wave for 4 < K <= 8 when one round of resident waves
-    // of the one-item kernel does not cover every item
+    // several items per wave for 4 < K <= 8 (batches of 6 or 8) when one
+    // round of resident waves of the one-item kernel does not cover every item
     int per_wave = 1;
-    if constexpr (KB == 8) {
-        if (K <= 8 && items > resident_waves<combine_kernel<KB, BIAS, Rows>>()) {
-            if (items <= 8 * resident_waves<combine_multi_kernel<BIAS, Rows, 8>>())
+    if constexpr (KB == 8 || KB == 6) {
+        if (K <= KB && items > resident_waves<combine_kernel<KB, BIAS, Rows>>()) {
+            if (items <= 8 * resident_waves<combine_multi_kernel<BIAS, Rows, 8, KB>>())
                 per_wave = 8;
-            else if (items <= kMaxItems * resident_waves<combine_multi_kernel<BIAS, Rows, kMaxItems>>())
+            else if (items <= kMaxItems * resident_waves<combine_multi_kernel<BIAS, Rows, kMaxItems, KB>>())
                 per_wave = kMaxItems;
         }
     }
@@ -461,13 +463,13 @@ hipError_t launch_topk_combine_kb(const ep_shape &s, const Rows &rows, const uin
 #define EP_COMBINE_ARGS                                                                            \
     grid, dim3(kThreads), 0, stream, N, H, K, E, nchunks, rows, expert_out, topk_idx,              \
         topk_weights, expert_slot, bias, combined_x, status
-    if constexpr (KB == 8) {
+    if constexpr (KB == 8 || KB == 6) {
         if (per_wave == 8) {
-            hipLaunchKernelGGL((combine_multi_kernel<BIAS, Rows, 8>), EP_COMBINE_ARGS);
+            hipLaunchKernelGGL((combine_multi_kernel<BIAS, Rows, 8, KB>), EP_COMBINE_ARGS);
             return hipGetLastError();
         }
         if (per_wave == kMaxItems) {
-            hipLaunchKernelGGL((combine_multi_kernel<BIAS, Rows, kMaxItems>), EP_COMBINE_ARGS);
+            hipLaunchKernelGGL((combine_multi_kernel<BIAS, Rows, kMaxItems, KB>), EP_COMBINE_ARGS);
             return hipGetLastError();
         }
     }
@@ -490,7 +492,7 @@ hipError_t launch_topk_combine(const ep_shape &s, const Rows &rows, const uint16
                                            expert_slot, bias, combined_x, status, stream)
 #define EP_COMBINE_BIAS(BIAS)                                                                      \
     (K == 1 ? EP_COMBINE_KB(1, BIAS)                                                               \
-            : K == 2 ? EP_COMBINE_KB(2, BIAS) : K <= 4 ? EP_COMBINE_KB(4, BIAS) : EP_COMBINE_KB(8, BIAS))
+            : K == 2 ? EP_COMBINE_KB(2, BIAS) : K <= 4 ? EP_COMBINE_KB(4, BIAS) : K <= 6 ? EP_COMBINE_KB(6, BIAS) : EP_COMBINE_KB(8, BIAS))
     return bias ? EP_COMBINE_BIAS(true) : EP_COMBINE_BIAS(false);
 #undef EP_COMBINE_BIAS
 #undef EP_COMBINE_KB
