@@ -43,6 +43,18 @@ constexpr int kBallotRanks = 16;
 
 __device__ __forceinline__ uint64_t bits_below(int bit) { return (1ull << bit) - 1ull; }
 
+// Number of entries of `e` among the block's tokens before this lane's token
+// (same layer): lower bits of this wave's word plus the earlier waves' words.
+__device__ __forceinline__ int prefix_in_block(const uint64_t *words, int stride, int g, int lane)
+{
+    int cnt = __popcll(words[g * stride] & bits_below(lane));
+#pragma unroll
+    for (int g2 = 0; g2 < kGroups - 1; ++g2)
+        if (g2 < g)
+            cnt += __popcll(words[g2 * stride]);
+    return cnt;
+}
+
 template <int KMAX>
 __global__ __launch_bounds__(kThreads) void layout_count_kernel(
     int32_t N, int32_t K, int32_t E, int32_t R, int32_t L, int32_t stride,
@@ -89,16 +101,6 @@ __host__ __device__ inline size_t assign_lds_bytes(int E, int R)
     // [E + R], misc [8]
     return sizeof(uint64_t) * (size_t)kGroups * (E + R) + sizeof(int32_t) * (size_t)kGroups * (E + R) +
            sizeof(int32_t) * (size_t)(E + R) + sizeof(int32_t) * 8;
-}
-
-// Number of entries of `e` among the block's tokens before this lane's token
-// (same layer): lower bits of this wave's word plus the earlier waves' words.
-__device__ __forceinline__ int prefix_in_block(const uint64_t *words, int stride, int g, int lane)
-{
-    int cnt = __popcll(words[g * stride] & bits_below(lane));
-    for (int g2 = 0; g2 < g; ++g2)
-        cnt += __popcll(words[g2 * stride]);
-    return cnt;
 }
 
 // Rows of expert queue with c entries under expert alignment A >= 1 (the
@@ -467,12 +469,13 @@ __global__ __launch_bounds__(kThreads) void layout_assign_kernel(
 // Local ranking: the first launch of ep_layout_dispatch above
 // kFusedCountedMaxTokens tokens.  Each 256-token block ranks its own entries
 // exactly as the assign kernel does, but against its own tokens only:
-// local_slot[t, k] is the entry's rank among the block's entries with the
+// local_slot[t, k] is entry (t, k)'s rank among the block's entries with the
 // same expert, local_rank[t, k] the token's rank among the block's tokens
-// sent to the rank of expert k (-1 for a masked entry), and the block's
-// histogram row (its entries per expert, repeats included, and its tokens
-// per rank) goes to `hist`.  No block reads another block's output: the pack
-// that follows adds each token's prefix over the earlier blocks' rows.
+// sent to the rank of expert k (-1 for a masked entry), and hist row b
+// (stride ints) gets the block's entries per expert, repeats included, then
+// its tokens per rank, then zeros.  No block reads another block's output:
+// the pack that follows adds each token's prefix over the earlier blocks'
+// rows.
 template <int KMAX>
 __global__ __launch_bounds__(kThreads) void layout_local_kernel(
     int32_t N, int32_t K, int32_t E, int32_t R, int32_t L, int32_t stride,
@@ -480,6 +483,7 @@ __global__ __launch_bounds__(kThreads) void layout_local_kernel(
     int32_t *__restrict__ local_slot, int32_t *__restrict__ local_rank, uint32_t *status)
 {
     extern __shared__ __align__(16) char lds_raw[];
+    const int b = blockIdx.x;
     const int W = E + R;
     uint64_t *s_bm = reinterpret_cast<uint64_t *>(lds_raw);                  // [kGroups][W]
     int32_t *s_wb = reinterpret_cast<int32_t *>(s_bm + (size_t)kGroups * W); // [kGroups][W]
@@ -489,7 +493,6 @@ __global__ __launch_bounds__(kThreads) void layout_local_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int g = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int b = blockIdx.x;
     const int64_t t = (int64_t)b * kThreads + tid;
 
     int32_t e[KMAX];
@@ -553,14 +556,19 @@ __global__ __launch_bounds__(kThreads) void layout_local_kernel(
     }
     __syncthreads();
 
+    // layer 0: each entry's slot and rank slot go out at once; a repeat
+    // layer (rare) adds to the stored slot, so no per-entry array stays live
     const int32_t *my_base = s_wb + (size_t)g * W;
     const uint64_t below = bits_below(lane);
-    int pre[KMAX];
-    int lr[KMAX];
+    const bool own = t < N;
+    int32_t *ls = local_slot + (own ? t : 0) * K;
+    int32_t *lrk = local_rank + (own ? t : 0) * K;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
-        pre[k] = e[k] >= 0 ? my_base[e[k]] + __popcll(my_words[e[k]] & below) + occ[k] : 0;
-        lr[k] = e[k] >= 0 ? my_base[E + rk[k]] + __popcll(my_words[E + rk[k]] & below) : -1;
+        if (own && k < K) {
+            ls[k] = e[k] >= 0 ? my_base[e[k]] + __popcll(my_words[e[k]] & below) + occ[k] : -1;
+            lrk[k] = e[k] >= 0 ? my_base[E + rk[k]] + __popcll(my_words[E + rk[k]] & below) : -1;
+        }
     }
 
     // repeated experts: one more bitmap layer per occurrence index, each also
@@ -578,25 +586,13 @@ __global__ __launch_bounds__(kThreads) void layout_local_kernel(
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
-            if (e[k] >= 0)
-                pre[k] += prefix_in_block(&s_bm[e[k]], W, g, lane);
+            if (own && k < K && e[k] >= 0)
+                ls[k] += prefix_in_block(&s_bm[e[k]], W, g, lane);
         for (int i = tid; i < E; i += kThreads) {
             int c = 0;
             for (int g2 = 0; g2 < kGroups; ++g2)
                 c += __popcll(s_bm[g2 * W + i]);
             s_tot[i] += c;
-        }
-    }
-
-    if (t < N) {
-        int32_t *ls = local_slot + t * K;
-        int32_t *lrk = local_rank + t * K;
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-            if (k < K) {
-                ls[k] = e[k] >= 0 ? pre[k] : -1;
-                lrk[k] = lr[k];
-            }
         }
     }
     __syncthreads(); // s_tot complete
@@ -606,6 +602,7 @@ __global__ __launch_bounds__(kThreads) void layout_local_kernel(
     if (tid == 0 && status && s_misc[1])
         atomicOr(status, EP_STATUS_BAD_EXPERT_ID);
 }
+
 
 } // namespace
 

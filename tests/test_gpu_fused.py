@@ -38,10 +38,11 @@ def oracle_capacity(counts, S):
     return S if top > S else max(1, top)
 
 
-def run_fused(shape, x_bits, topk_idx, topk_offset=0):
-    """One ep_layout_dispatch call on poisoned outputs.  With topk_offset > 0
-    the ids sit that many int64 into their buffer (an 8-byte aligned base that
-    is not 16-byte aligned when the offset is odd)."""
+def launch_fused(shape, x_bits, topk_idx, topk_offset=0, workspace=None):
+    """Enqueue one ep_layout_dispatch call on poisoned outputs (a poisoned
+    workspace of its own unless one is given).  With topk_offset > 0 the ids
+    sit that many int64 into their buffer (an 8-byte aligned base that is not
+    16-byte aligned when the offset is odd)."""
     N, H, K, E, R, S = (shape.num_tokens, shape.hidden, shape.num_topk, shape.num_experts,
                         shape.num_ranks, shape.expert_capacity)
     full = lambda n, v, dt: torch.full((n,), v, dtype=dt, device="cuda")
@@ -56,7 +57,8 @@ def run_fused(shape, x_bits, topk_idx, topk_offset=0):
         "expert_offset": full(E + 1, POISON_I32, torch.int32),
     }
     need = ep.ep_query_sizes(shape)["layout_workspace"]
-    workspace = full(-(-need // 4), POISON_I32, torch.int32) if need else None
+    if workspace is None and need:
+        workspace = full(-(-need // 4), POISON_I32, torch.int32)
     if shape.use_fp8:
         recv_x = torch.full((E, S, H), POISON_X8, dtype=torch.uint8, device="cuda")
         recv_scales = torch.full((E, S, ep.scale_row_elems(shape)), POISON_SCALE_BITS,
@@ -72,16 +74,25 @@ def run_fused(shape, x_bits, topk_idx, topk_offset=0):
     ep.ep_layout_dispatch(shape, ids_dev, x, out["num_tokens_per_rank"], out["num_tokens_per_expert"],
                           out["is_token_in_rank"], out["expert_slot"], out["rank_slot"],
                           out["expert_offset"], workspace, recv_x, recv_scales, recv_src_idx, status)
-    torch.cuda.synchronize()
     return out, recv_x, recv_scales, recv_src_idx, status
 
 
-def check_fused(o, shape, x_bits, topk_idx, name, topk_offset=0):
+def run_fused(shape, x_bits, topk_idx, topk_offset=0, workspace=None):
+    res = launch_fused(shape, x_bits, topk_idx, topk_offset, workspace)
+    torch.cuda.synchronize()
+    return res
+
+
+def check_fused(o, shape, x_bits, topk_idx, name, topk_offset=0, workspace=None, result=None):
+    """Every output of one call against the oracle; `result` is a call
+    already made (launch_fused, then a synchronize), else one is made here."""
     N, H, E, R, S = shape.num_tokens, shape.hidden, shape.num_experts, shape.num_ranks, \
         shape.expert_capacity
     say(f"ep_layout_dispatch {name} N={N} H={H} K={shape.num_topk} E={E} R={R} S={S} "
         f"fp8={shape.use_fp8} scale_format={shape.scale_format}")
-    out, recv_x, recv_scales, recv_src_idx, status = run_fused(shape, x_bits, topk_idx, topk_offset)
+    if result is None:
+        result = run_fused(shape, x_bits, topk_idx, topk_offset, workspace)
+    out, recv_x, recv_scales, recv_src_idx, status = result
     lay = o.layout(topk_idx, E, R, alignment=max(shape.expert_alignment, 1))
     for key in LAYOUT_KEYS:
         got = host(out[key])
@@ -256,3 +267,42 @@ def test_fused_skewed_full_size(o):
     inp = W.make_inputs(w)
     check_fused(o, ep.shape_of(w), inp["x_bits"], inp["topk_idx"], f"full {w.name}")
 
+
+
+def test_fused_one_workspace_call_after_call(o):
+    """One workspace, poisoned once and never cleared, serves an ep_layout
+    call (its histogram rows), then ep_layout_dispatch at 3,000, 1,500 and
+    3,000 tokens with new routings (local ranks, histogram rows and the pack
+    that reads them), the last two enqueued back to back with no wait
+    between: no call depends on what an earlier one left in the workspace.
+    Every call is bit-exact and its status clean."""
+    H, K, E, R = 512, 8, 64, 8
+    big = ep.make_shape(3000, H, K, E, R, 3000, 3000, True)
+    need = ep.ep_query_sizes(big)["layout_workspace"]
+    ws = torch.full((-(-need // 4),), POISON_I32, dtype=torch.int32, device="cuda")
+    x, idx = _random(3000, H, K, E, R, seed=41)
+    lay_out = {k: torch.empty(n, dtype=dt, device="cuda") for k, n, dt in (
+        ("num_tokens_per_rank", R, torch.int32), ("num_tokens_per_expert", E, torch.int32),
+        ("is_token_in_rank", 3000 * R, torch.uint8), ("expert_slot", 3000 * K, torch.int32),
+        ("rank_slot", 3000 * R, torch.int32), ("expert_offset", E + 1, torch.int32))}
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    say("ep_layout N=3000 into the shared workspace")
+    ep.ep_layout(big, dev(idx), lay_out["num_tokens_per_rank"], lay_out["num_tokens_per_expert"],
+                 lay_out["is_token_in_rank"].view(3000, R), lay_out["expert_slot"].view(3000, K),
+                 lay_out["rank_slot"].view(3000, R), lay_out["expert_offset"], ws, st)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(lay_out["expert_slot"]).reshape(3000, K),
+                          o.layout(idx, E, R)["expert_slot"])
+    check_fused(o, big, x, idx, "first call on the shared workspace", workspace=ws)
+    n = 1500
+    x2, idx2 = _random(n, H, K, E, R, seed=42, mask=0.05)
+    check_fused(o, ep.make_shape(n, H, K, E, R, n, n, True), x2, idx2,
+                "smaller call on the shared workspace", workspace=ws)
+    x3, idx3 = _random(3000, H, K, E, R, seed=43)
+    x4, idx4 = _random(3000, H, K, E, R, seed=44, mask=0.1)
+    say("two calls enqueued back to back on the shared workspace")
+    r3 = launch_fused(big, x3, idx3, workspace=ws)
+    r4 = launch_fused(big, x4, idx4, workspace=ws)
+    torch.cuda.synchronize()
+    check_fused(o, big, x3, idx3, "back to back, first", result=r3)
+    check_fused(o, big, x4, idx4, "back to back, second", result=r4)

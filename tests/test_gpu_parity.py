@@ -603,8 +603,10 @@ def test_two_streams_and_two_host_threads(o):
     for r in runs:
         for k in keys:  # rows past each expert's count are never written
             r["buf"][k].fill_(-1)
+        torch.cuda.synchronize()  # the fills (current stream) before the step (its own stream)
         step(r)
         alone.append(snap(r))
+        assert int(r["buf"]["status"].item()) == 0
         for k in keys:
             r["buf"][k].fill_(-1)
     torch.cuda.synchronize()
