@@ -3,12 +3,15 @@
 The library runs one wave per (token, chunk) item when one round of resident
 waves covers every item, and otherwise a grid that is resident all at once
 with 8 or 14 items per wave, whose outputs are stored after the wave's last
-read.  Which one runs depends on the batch size and on the occupancy the
-device reports, so these sizes (H = 7,168, top-8 of 256 experts) step across
-both boundaries on an MI355X.  Each size is compared with the oracle element
-by element, with masked entries, out-of-range ids and, on two sizes, the
-epilogue bias; bit-identical is expected (the tolerance of the other combine
-tests is the bar) and the status bits must match.
+read; a batch larger than 14 items per resident wave is split into equal
+token ranges, one such launch each.  Which one runs depends on the batch size
+and on the occupancy the device reports, so these sizes (H = 7,168, top-8 of
+256 experts; the split sizes with 16 experts to keep the expert buffer small,
+one with top-6) step across every boundary on an MI355X.  Each size is
+compared with the oracle element by element, with masked entries,
+out-of-range ids and, on three sizes, the epilogue bias; bit-identical is
+expected (the tolerance of the other combine tests is the bar) and the
+status bits must match.
 """
 import numpy as np
 import pytest
@@ -21,8 +24,9 @@ from gpu_helpers import LayoutRun, place_expert_rows, run_combine, say
 
 pytestmark = pytest.mark.gpu
 
-SIZES = [700, 800, 1500, 2600, 3000, 3600, 4100]
-WITH_BIAS = (800, 3000)
+SIZES = [(700, 8, 256), (800, 8, 256), (1500, 8, 256), (2600, 8, 256), (3000, 8, 256),
+         (3600, 8, 256), (4100, 8, 256), (9000, 8, 16), (12000, 6, 16)]
+WITH_BIAS = (800, 3000, 9000)
 
 
 @pytest.fixture(scope="module")
@@ -30,9 +34,9 @@ def o():
     return oracle.get()
 
 
-@pytest.mark.parametrize("N", SIZES)
-def test_combine_across_batch_sizes(o, N):
-    H, K, E, R = 7168, 8, 256, 8
+@pytest.mark.parametrize("N,K,E", SIZES, ids=[f"{n}-top{k}-of-{e}" for n, k, e in SIZES])
+def test_combine_across_batch_sizes(o, N, K, E):
+    H, R = 7168, 8
     rng = np.random.default_rng(N)
     idx = np.argsort(rng.random((N, E), dtype=np.float32), axis=1)[:, :K].astype(np.int64)
     idx[rng.random((N, K)) < 0.05] = -1
