@@ -1295,21 +1295,12 @@ def summarize_config_profiles(out_dir):
                    ("pack_kernel", "pack", "dispatch"),
                    ("combine_kernel", "combine", "combine"),
                    ("combine_multi_kernel", "combine", "combine")]
-        # every step makes one combine call; above one resident round of
-        # multi-item waves that call is several launches on equal token
-        # ranges, back to back: their durations are summed per call
-        calls = sum(1 for r in trace if r["Kernel_Name"] in ("pack_local_kernel", "pack_kernel"))
         for kname, short, phase in kernels:
-            mine = sorted((r for r in trace if r["Kernel_Name"] == kname),
-                          key=lambda r: int(r["Start_Timestamp"]))
-            durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in mine]
+            durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
+                    if r["Kernel_Name"] == kname]
             if not durs:
                 continue
-            per_call = 1
-            if phase == "combine" and calls and len(durs) > calls and len(durs) % calls == 0:
-                per_call = len(durs) // calls
-                durs = [sum(durs[i:i + per_call]) for i in range(0, len(durs), per_call)]
-            grids = sorted({r["Grid_Size_X"] for r in mine})
+            grids = sorted({r["Grid_Size_X"] for r in trace if r["Kernel_Name"] == kname})
             med = statistics.median(durs)
             lines = [
                 f"# {kname}, workload {w.name} (cold steps: an eviction read of 1 GiB before each)",
@@ -1320,12 +1311,7 @@ def summarize_config_profiles(out_dir):
                 "",
                 "## rocprofv3 kernel trace (kernel-only durations of every dispatch in the run)",
                 f"command: {PROFILE_COMMANDS['configs_trace'].replace('${WID}', str(wid))}",
-                f"dispatches: {len(mine)}",
-            ]
-            if per_call > 1:
-                lines += [f"launches_per_call: {per_call} (equal token ranges, back to back); the "
-                          "figures below are per call, each the sum of its launches"]
-            lines += [
+                f"dispatches: {len(durs)}",
                 f"avg_us: {statistics.fmean(durs):.2f}",
                 f"median_us: {med:.2f}",
                 f"min_us: {min(durs):.2f}  max_us: {max(durs):.2f}",
@@ -1346,7 +1332,6 @@ def summarize_config_profiles(out_dir):
                     per[c] = statistics.median(float(r["Counter_Value"]) for r in rs
                                                if r["Kernel_Name"] == kname)
                 hbm = (per["FETCH_SIZE"] * cal["FETCH_SIZE"][1] + per["WRITE_SIZE"] * cal["WRITE_SIZE"][1]) * 1024
-                hbm *= per_call  # equal ranges: the median launch times the launches of a call
                 lines += [
                     "",
                     "## HBM traffic from rocprofv3 counters (one run per counter)",
@@ -1358,7 +1343,7 @@ def summarize_config_profiles(out_dir):
                     f"  WRITE_SIZE on the copy: {cal['WRITE_SIZE'][0]:.0f} KiB -> factor {cal['WRITE_SIZE'][1]:.4f}",
                     f"FETCH_SIZE_KiB_per_dispatch (median): {per['FETCH_SIZE']:.0f}",
                     f"WRITE_SIZE_KiB_per_dispatch (median): {per['WRITE_SIZE']:.0f}",
-                    f"hbm_bytes_per_{'call' if per_call > 1 else 'launch'}: {hbm:.0f}",
+                    f"hbm_bytes_per_launch: {hbm:.0f}",
                     f"traffic_over_algorithmic: {hbm / nb[phase]:.4f}",
                 ]
             path = os.path.join(PROFILES, f"{short}_{w.name}.txt")

@@ -38,7 +38,6 @@
 // and each wave stores its outputs after its last read: HBM loses bandwidth
 // when reads and writes interleave, and this moves the writes towards the
 // end.  Same arithmetic per item.  Larger batches run the one-item kernel.
-#include <algorithm>
 #include <atomic>
 
 #include "ep_device.h"
@@ -407,11 +406,9 @@ __global__ __launch_bounds__(kThreads) void combine_normal_kernel(
 }
 
 // Items per wave for the top-k combine: 1 (a wave per item) when one round of
-// resident waves covers every item; otherwise the smallest instantiated count
-// whose grid is resident all at once (occupancy of that instantiation times
-// the compute units).  A batch with more items than kMaxItems per resident
-// wave is split into equal token ranges, one launch each, so that every
-// launch keeps the reads-first order of the multi-item kernel.
+// resident waves covers every item or when more than kMaxItems per wave would
+// be needed; otherwise the smallest instantiated count whose grid is resident
+// all at once (occupancy of that instantiation times the compute units).
 constexpr int kMaxItems = 14;
 
 // Waves of KERNEL that fit on the current device at once (occupancy of its
@@ -441,23 +438,15 @@ int64_t resident_waves()
     return w;
 }
 
-// Tokens [t0, t0 + N) of the batch in one launch.
 template <int KB, bool BIAS, class Rows>
-hipError_t launch_topk_combine_range(const ep_shape &s, int N, int64_t t0, const Rows &rows,
-                                     const uint16_t *expert_out, const int64_t *topk_idx,
-                                     const float *topk_weights, const int32_t *expert_slot,
-                                     const uint16_t *bias, uint16_t *combined_x, uint32_t *status,
-                                     hipStream_t stream)
+hipError_t launch_topk_combine_kb(const ep_shape &s, const Rows &rows, const uint16_t *expert_out,
+                                  const int64_t *topk_idx, const float *topk_weights,
+                                  const int32_t *expert_slot, const uint16_t *bias,
+                                  uint16_t *combined_x, uint32_t *status, hipStream_t stream)
 {
-    const int H = s.hidden, K = s.num_topk, E = s.num_experts;
+    const int N = s.num_tokens, H = s.hidden, K = s.num_topk, E = s.num_experts;
     const int nchunks = (H + kChunk - 1) / kChunk;
     const int64_t items = (int64_t)N * nchunks;
-    topk_idx += t0 * K;
-    topk_weights += t0 * K;
-    expert_slot += t0 * K;
-    combined_x += t0 * H;
-    if (BIAS)
-        bias += t0 * H;
     // several items per wave for 4 < K <= 8 (batches of 6 or 8) when one
     // round of resident waves of the one-item kernel does not cover every item
     int per_wave = 1;
@@ -487,35 +476,6 @@ hipError_t launch_topk_combine_range(const ep_shape &s, int N, int64_t t0, const
     hipLaunchKernelGGL((combine_kernel<KB, BIAS, Rows>), EP_COMBINE_ARGS);
 #undef EP_COMBINE_ARGS
     return hipGetLastError();
-}
-
-template <int KB, bool BIAS, class Rows>
-hipError_t launch_topk_combine_kb(const ep_shape &s, const Rows &rows, const uint16_t *expert_out,
-                                  const int64_t *topk_idx, const float *topk_weights,
-                                  const int32_t *expert_slot, const uint16_t *bias,
-                                  uint16_t *combined_x, uint32_t *status, hipStream_t stream)
-{
-    const int N = s.num_tokens, K = s.num_topk;
-    const int64_t nchunks = (s.hidden + kChunk - 1) / kChunk;
-    int64_t per = N; // tokens per launch
-    if constexpr (KB == 8 || KB == 6) {
-        // tokens one round of resident kMaxItems-item waves covers; equal
-        // parts of at most that many (ceil(N / ceil(N / m)) <= m)
-        const int64_t m =
-            kMaxItems * resident_waves<combine_multi_kernel<BIAS, Rows, kMaxItems, KB>>() / nchunks;
-        if (K <= KB && m > 0 && N > m) {
-            const int64_t parts = (N + m - 1) / m;
-            per = (N + parts - 1) / parts;
-        }
-    }
-    for (int64_t t0 = 0; t0 < N; t0 += per) {
-        const hipError_t err = launch_topk_combine_range<KB, BIAS, Rows>(
-            s, (int)std::min<int64_t>(per, N - t0), t0, rows, expert_out, topk_idx, topk_weights,
-            expert_slot, bias, combined_x, status, stream);
-        if (err != hipSuccess)
-            return err;
-    }
-    return hipSuccess;
 }
 
 template <class Rows>

@@ -3,11 +3,11 @@
 The library runs one wave per (token, chunk) item when one round of resident
 waves covers every item, and otherwise a grid that is resident all at once
 with 8 or 14 items per wave, whose outputs are stored after the wave's last
-read; a batch larger than 14 items per resident wave is split into equal
-token ranges, one such launch each.  Which one runs depends on the batch size
-and on the occupancy the device reports, so these sizes (H = 7,168, top-8 of
-256 experts; the split sizes with 16 experts to keep the expert buffer small,
-one with top-6) step across every boundary on an MI355X.  Each size is
+read; past 14 items per resident wave it goes back to one wave per item.
+Which one runs depends on the batch size and on the occupancy the device
+reports, so these sizes (H = 7,168, top-8 of 256 experts; the two largest
+with 16 experts to keep the expert buffer small, one with top-6) step across
+every boundary on an MI355X.  Each size is
 compared with the oracle element by element, with masked entries,
 out-of-range ids and, on three sizes, the epilogue bias; bit-identical is
 expected (the tolerance of the other combine tests is the bar) and the
