@@ -249,7 +249,8 @@ def test_fused_matches_separate_calls_and_expand_offsets(o, N):
     check_fused(o, shape, x, idx, "expert alignment 128")
 
 
-@pytest.mark.parametrize("fmt", [ep.EP_SCALE_FP32, ep.EP_SCALE_UE8M0], ids=["fp32", "ue8m0"])
+@pytest.mark.parametrize("fmt", [ep.EP_SCALE_FP32, ep.EP_SCALE_POW2, ep.EP_SCALE_UE8M0],
+                         ids=["fp32", "pow2", "ue8m0"])
 def test_fused_prefill_full_size(o, fmt):
     """The prefill workload at full size (4,096 tokens x 7,168, group-limited
     top-8 of 256 experts over 8 ranks): the large-batch form, every output
@@ -257,6 +258,16 @@ def test_fused_prefill_full_size(o, fmt):
     w = W.WORKLOADS[3]
     inp = W.make_inputs(w)
     check_fused(o, ep.shape_of(w, fmt), inp["x_bits"], inp["topk_idx"], f"full {w.name}")
+
+
+def test_fused_large_full_size(o):
+    """The large workload at full size (16,384 tokens x 7,168 BF16, top-6 of
+    256 experts over 8 ranks, a 60 GB receive buffer): 64 ranking blocks, and
+    a pack whose last tokens add 63 earlier blocks' counts; every output
+    bit-exact."""
+    w = W.WORKLOADS[4]
+    inp = W.make_inputs(w)
+    check_fused(o, ep.shape_of(w), inp["x_bits"], inp["topk_idx"], f"full {w.name}")
 
 
 def test_fused_skewed_full_size(o):
