@@ -641,17 +641,21 @@ __device__ __forceinline__ int group_sum(int v)
 // The pack of ep_layout_dispatch above kFusedCountedMaxTokens tokens: the
 // layout left each entry's rank within its 256-token block (local_slot) and
 // one histogram row per block; an entry's slot is its local slot plus the
-// counts of its expert in every earlier block.  One block per token (block 0
-// sums every histogram row into the totals and writes the offset scan):
-//  1. every wave loads x of its first two chunks;
-//  2. wave 0 computes the token's rows once: a group of 64 / KB lanes takes
-//     entry k of a batch, each lane a share of the earlier blocks' rows, and
-//     a reduction within the group gives the prefix; the same for the column
-//     of the entry's rank.  It writes the token's expert_slot row, its rank
-//     rows and recv_src_idx, and leaves the rows in LDS;
-//  3. after one barrier, wave w quantises chunks w, w + 4, ... once and stores
-//     each to every row, as pack_kernel does.
-template <int KB, int SF, bool FP8>
+// counts of its expert in every earlier block.  Each block packs T tokens
+// (T = 2 when a token has at most kWaves chunks, so every wave still gets two
+// chunks; otherwise 1); block 0 sums every histogram row into the totals and
+// writes the offset scan.  Item j of a block is chunk j mod nchunks of its
+// token j / nchunks:
+//  1. every wave loads x of its first two items;
+//  2. wave q < T computes the rows of the block's token q once: a group of
+//     64 / KB lanes takes entry k of a batch, each lane a share of the earlier
+//     blocks' rows, and a reduction within the group gives the prefix; the
+//     same for the column of the entry's rank.  It writes the token's
+//     expert_slot row, its rank rows and recv_src_idx, and leaves the rows in
+//     LDS;
+//  3. after one barrier, wave w quantises items w, w + 4, ... once and stores
+//     each to every row of its token, as pack_kernel does.
+template <int KB, int SF, bool FP8, int T>
 __global__ __launch_bounds__(kThreads) void pack_local_kernel(
     int32_t N, int32_t H, int32_t K, int32_t E, int32_t R, int32_t S, int32_t A, int32_t nchunks,
     int32_t tpb, int32_t B, int32_t stride, const int32_t *__restrict__ hist,
@@ -705,23 +709,28 @@ __global__ __launch_bounds__(kThreads) void pack_local_kernel(
         }
         return;
     }
-    __shared__ int64_t s_row[EP_MAX_TOPK];
-    const uint32_t t = blockIdx.x - 1; // host launches N + 1 blocks
-    const uint16_t *x_row = x + (size_t)t * H;
+    static_assert(T >= 1 && T <= kWaves, "a wave per token's rows");
+    __shared__ int64_t s_row[T][EP_MAX_TOPK];
+    const uint32_t t0 = (blockIdx.x - 1) * (uint32_t)T; // host launches 1 + ceil(N / T) blocks
+    const int tokens = min(T, N - (int)t0);
+    const int items = tokens * nchunks;
 
-    // 1. x of this wave's first two chunks
+    // 1. x of this wave's first two items
     uint4 xr[2][2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         xr[c][0] = make_uint4(0, 0, 0, 0);
         xr[c][1] = make_uint4(0, 0, 0, 0);
-        const int chunk = wave + c * kWaves;
-        if (chunk < nchunks)
-            load_chunk<FP8>(x_row, H, chunk, lane, xr[c][0], xr[c][1]);
+        const int j = wave + c * kWaves;
+        if (j < items) {
+            const int q = T == 1 ? 0 : j / nchunks;
+            load_chunk<FP8>(x + (size_t)(t0 + q) * H, H, j - q * nchunks, lane, xr[c][0], xr[c][1]);
+        }
     }
 
-    // 2. the token's rows and layout rows (wave 0)
-    if (wave == 0) {
+    // 2. each token's rows and layout rows (wave q for token q)
+    if (wave < tokens) {
+        const uint32_t t = t0 + wave;
         constexpr int G = 64 / KB;
         const int blk = (int)(t / (uint32_t)tpb); // earlier blocks: 0 .. blk-1
         const int kq = lane / G;
@@ -760,7 +769,7 @@ __global__ __launch_bounds__(kThreads) void pack_local_kernel(
                 flags |= EP_STATUS_BAD_SLOT;
             if (head && in_k) {
                 expert_slot[(size_t)t * K + k0 + kq] = routed ? slot : -1;
-                s_row[k0 + kq] = rr;
+                s_row[wave][k0 + kq] = rr;
                 if (rr >= 0)
                     recv_src_idx[rr] = (int32_t)t;
             }
@@ -785,8 +794,10 @@ __global__ __launch_bounds__(kThreads) void pack_local_kernel(
     }
     __syncthreads();
 
-    // 3. pack: the first two chunks are loaded; later ones load here
-    for (int chunk = wave, c = 0; chunk < nchunks; chunk += kWaves, ++c) {
+    // 3. pack: the first two items are loaded; later ones load here
+    for (int j = wave, c = 0; j < items; j += kWaves, ++c) {
+        const int q = T == 1 ? 0 : j / nchunks;
+        const int chunk = j - q * nchunks;
         uint4 in0 = make_uint4(0, 0, 0, 0), in1 = make_uint4(0, 0, 0, 0);
         if (c == 0) {
             in0 = xr[0][0];
@@ -795,7 +806,7 @@ __global__ __launch_bounds__(kThreads) void pack_local_kernel(
             in0 = xr[1][0];
             in1 = xr[1][1];
         } else {
-            load_chunk<FP8>(x_row, H, chunk, lane, in0, in1);
+            load_chunk<FP8>(x + (size_t)(t0 + q) * H, H, chunk, lane, in0, in1);
         }
         Fp8Lane fl;
         Fp8Payload p;
@@ -807,7 +818,7 @@ __global__ __launch_bounds__(kThreads) void pack_local_kernel(
             bl = bf16_lane(H, chunk, lane);
         }
         for (int k = 0; k < K; ++k) {
-            const int64_t row = s_row[k];
+            const int64_t row = s_row[q][k];
             if (row < 0)
                 continue;
             if (FP8)
@@ -940,14 +951,24 @@ hipError_t launch_dispatch_local(const ep_shape &s, const LayoutPlan &plan, cons
     if (N == 0)
         return hipSuccess;
     const int nchunks = (H + kChunk - 1) / kChunk;
-    const dim3 grid((unsigned)(N + 1)); // block 0: totals; block t + 1: token t
+    // two tokens per block when a token has no more chunks than a block has
+    // waves (each wave then still packs two chunks), else one
+    const int T = nchunks <= kWaves ? 2 : 1;
+    const dim3 grid((unsigned)(1 + (N + T - 1) / T)); // block 0: totals
     const int kb = batch_of(K);
-#define EP_LOCAL(KB, SF, FP8)                                                                      \
-    hipLaunchKernelGGL((pack_local_kernel<KB, SF, FP8>), grid, dim3(kThreads), 0, stream, N, H, K, \
-                       E, R, S, A, nchunks, plan.tokens_per_block, plan.num_blocks,                \
+#define EP_LOCAL_T(KB, SF, FP8, TT)                                                                \
+    hipLaunchKernelGGL((pack_local_kernel<KB, SF, FP8, TT>), grid, dim3(kThreads), 0, stream, N,   \
+                       H, K, E, R, S, A, nchunks, plan.tokens_per_block, plan.num_blocks,          \
                        plan.hist_stride, ws.hist, ws.local_slot, ws.local_rank, x, topk_idx,       \
                        num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank, expert_slot,  \
                        rank_slot, expert_offset, recv_x, recv_scales, recv_src_idx, status)
+#define EP_LOCAL(KB, SF, FP8)                                                                      \
+    do {                                                                                           \
+        if (T == 2)                                                                                \
+            EP_LOCAL_T(KB, SF, FP8, 2);                                                            \
+        else                                                                                       \
+            EP_LOCAL_T(KB, SF, FP8, 1);                                                            \
+    } while (0)
 #define EP_LOCAL_KB(SF, FP8)                                                                       \
     do {                                                                                           \
         if (kb == 1)                                                                               \
@@ -969,6 +990,7 @@ hipError_t launch_dispatch_local(const ep_shape &s, const LayoutPlan &plan, cons
         EP_LOCAL_KB(EP_SCALE_FP32, true);
 #undef EP_LOCAL_KB
 #undef EP_LOCAL
+#undef EP_LOCAL_T
     return hipGetLastError();
 }
 
