@@ -35,6 +35,9 @@ def noalloc_layout(shape, topk_idx_dev, stream=None):
         "expert_offset": full(E + 1, POISON_I32, torch.int32),
     }
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    if stream is not None:
+        # the fills above ran on the current stream: order them before the call
+        stream.wait_stream(torch.cuda.current_stream())
     ep.ep_layout_noalloc(shape, topk_idx_dev, out["num_tokens_per_rank"],
                          out["num_tokens_per_expert"], out["is_token_in_rank"], out["expert_slot"],
                          out["rank_slot"], out["expert_offset"], status, stream=stream)
@@ -74,8 +77,6 @@ def test_noalloc_matches_ep_layout_call_after_call(stream_kind):
         say(f"ep_layout_noalloc workload {wid} N={n} K={shape.num_topk} E={shape.num_experts} "
             f"R={shape.num_ranks} scratch bytes used {need} stream {stream_kind}")
         idx_dev = dev(idx)
-        if stream is not None:
-            stream.wait_stream(torch.cuda.current_stream())
         got = noalloc_layout(shape, idx_dev, stream=stream)
         ref = LayoutRun(shape, idx).numpy()  # ep_layout with a poisoned caller workspace
         want = o.layout(idx, shape.num_experts, shape.num_ranks)
