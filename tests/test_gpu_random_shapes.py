@@ -10,7 +10,9 @@ checked with the bar of its own tests: integer outputs, FP8 bytes and scales
 bit-exact, combines bit-identical to the oracle.  The shapes are small enough
 for the oracle to finish in seconds and step across the library's block and
 launch boundaries (256 and 1,024 tokens, 1,024-channel chunks, K of 8, 16
-and 32)."""
+and 32); the last 16 cases draw N from 1,025 to 4,097 tokens, odd counts
+included, where ep_layout_dispatch ranks 256-token blocks and packs one or
+two tokens per block."""
 import numpy as np
 import pytest
 
@@ -24,7 +26,8 @@ from test_gpu_receive_layouts import check_expand, check_normal
 
 pytestmark = pytest.mark.gpu
 
-CASES = 24
+CASES = 40
+FIRST_LARGE = 24  # cases from here on draw the larger batches
 
 
 @pytest.fixture(scope="module")
@@ -34,7 +37,10 @@ def o():
 
 def draw(seed):
     rng = np.random.default_rng(5000 + seed)
-    N = int(rng.choice([0, 1, 37, 129, 256, 257, 511, 700, 1024, 1025, 1300]))
+    if seed < FIRST_LARGE:
+        N = int(rng.choice([0, 1, 37, 129, 256, 257, 511, 700, 1024, 1025, 1300]))
+    else:
+        N = int(rng.choice([1025, 1537, 2049, 2560, 3001, 4097]))
     fp8 = bool(rng.random() < 0.6)
     H = int(128 * rng.integers(1, 13)) if fp8 else int(8 * rng.integers(1, 200))
     E = int(rng.choice([4, 8, 16, 32, 64, 256, 1024]))
