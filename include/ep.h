@@ -262,9 +262,9 @@ int ep_dispatch(const ep_shape *shape, const uint16_t *x, const int64_t *topk_id
  * launches: each 256-token block ranks its own entries (each entry's rank
  * among the block's entries with its expert, each token's among the block's
  * tokens sent to a rank) and writes its histogram row; then one block per
- * token adds the counts of the earlier blocks to its local ranks, writes the
- * token's layout rows and packs it, while one more block sums every row into
- * the totals and the offset scan.  Above 256 tokens it needs a workspace of
+ * token (per two tokens when hidden <= 4,096) adds the counts of the earlier
+ * blocks to its local ranks, writes the token's layout rows and packs it,
+ * while one more block sums every row into the totals and the offset scan.  Above 256 tokens it needs a workspace of
  * ep_sizes.layout_workspace bytes (which covers ep_layout's too; above 1,024
  * tokens it also holds the local ranks, 8 * N * K bytes); NULL with
  * workspace_bytes 0 is allowed up to 256 tokens. */
